@@ -1,0 +1,256 @@
+"""Benchmark: one Medusa decoding step on one MI355X.
+
+Workload (default): Vicuna-7B-shaped single step, bf16 -- hidden 4096, vocab
+32000, 5 Medusa heads (W1 4096x4096 + bias, W2 32000x4096), sparse 64-node
+tree, one attention layer of 32 heads x 128 over a 2048-token KV cache,
+greedy acceptance and accepted-path compaction.  Synthetic seeded inputs,
+resident in HBM before timing starts.
+
+A step = medusa_resid_silu + medusa_vocab_topk (the heads) -> medusa_build_tree
+-> tree_attention_verify -> medusa_base_greedy -> medusa_accept.
+
+Prints one JSON line (see the design doc for the fields).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+METRIC = "Medusa steps/sec + tree-verify tokens/sec (64-node tree, 7B shape), % of HBM roofline"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload index (2: 7B sparse-64, 3: dense-256, 4: batched)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="replay the step as a captured HIP graph")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the Medusa step here is a single-GPU path "
+              "(see DESIGN.md for how it would shard); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import medusa_inputs as mi
+    import speculative_decoding_medusa_amd as M
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cfg = mi.config(args.config)
+    dt_str = cfg.dtype
+    t0 = time.time()
+    heads = mi.gen_heads(cfg)
+    att = mi.gen_attention(cfg)
+    root = mi.gen_root_tokens(cfg)
+    gen_s = time.time() - t0
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16 else torch.from_numpy(a)
+        return t.cuda()
+
+    d = {k: dev(v) for k, v in {**heads, **att}.items()}
+    root_d = dev(root)
+    B, K, H, V, N, topk = cfg.B, cfg.K, cfg.H, cfg.V, cfg.N, cfg.topk
+    parent, rank = cfg.tree.arrays()
+    tree = M.Tree(parent, rank, K, topk)
+    wdt = M.BF16 if dt_str == "bf16" else M.F32
+    z = torch.empty(B, K, H, device="cuda")
+    ti = torch.empty(B, K, topk, dtype=torch.int32, device="cuda")
+    tv = torch.empty(B, K, topk, device="cuda")
+    ws_v = torch.empty(M.vocab_topk_workspace_size(B, H, V, K, topk, wdt), dtype=torch.uint8, device="cuda")
+    tok = torch.empty(B, N, dtype=torch.int32, device="cuda")
+    pos = torch.empty_like(tok)
+    o = torch.empty_like(d["q"])
+    ws_a = torch.empty(M.tree_attention_workspace_size(tree, B, cfg.nH, cfg.D, max(cfg.P), wdt), dtype=torch.uint8,
+                       device="cuda")
+    g = torch.empty(B * N, dtype=torch.int32, device="cuda")
+    ws_g = torch.empty(M.base_greedy_workspace_size(B * N, H, V, wdt), dtype=torch.uint8, device="cuda")
+    al = torch.empty(B, dtype=torch.int32, device="cuda")
+    an = torch.empty(B, tree.max_depth + 1, dtype=torch.int32, device="cuda")
+    ot = torch.empty_like(an)
+    ncl = torch.empty(B, dtype=torch.int32, device="cuda")
+    maxP = max(cfg.P)
+
+    def step():
+        M.medusa_resid_silu(d["h"], d["W1"], d["b1"], z)
+        M.medusa_vocab_topk(z, d["W2"], topk, ti, tv, ws=ws_v)
+        M.medusa_build_tree(tree, ti, root_d, d["cache_len"], tok, pos)
+        M.tree_attention_verify(d["q"], d["k_tree"], d["v_tree"], d["k_cache"], d["v_cache"], d["cache_len"], maxP,
+                                tree, o, ws=ws_a)
+        M.medusa_base_greedy(o, d["lm_head"], g, ws=ws_g)
+        M.medusa_accept(tree, tok, g.view(B, N), al, an, ot, d["cache_len"], ncl, k_cache=d["k_cache"],
+                        v_cache=d["v_cache"])
+
+    run = step
+    graph = None
+    if args.graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for _ in range(3):
+                step()
+        torch.cuda.current_stream().wait_stream(s)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        run = graph.replay
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+
+    # timed region: K steps between two synchronisations
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    w0 = time.perf_counter()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # per-kernel durations: the same K steps again, every launch bracketed by
+    # HIP events on the stream it runs on
+    M.profiler_reset()
+    M.profiler_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    prof = M.profiler_collect()
+    M.profiler_enable(False)
+    kern_us = {k: 1e3 * ms / n for k, (n, ms) in prof.items()}
+
+    def stage(*names):
+        return sum(kern_us.get(n, 0.0) for n in names)
+
+    st = {
+        "heads_resid_silu": stage("resid_silu_gemv"),
+        "heads_vocab_topk": stage("vocab_proj_topk", "topk_merge") * 1.0,
+        "build_tree": stage("build_tree"),
+        "tree_attention": stage("tree_attn_split", "tree_attn_combine", "tree_attn_mfma"),
+        "base_greedy": stage("rmsnorm_rows", "lm_head_argmax", "argmax_merge") +
+        (kern_us.get("vocab_proj_topk", 0.0) * 0),
+        "accept_compact": stage("accept_compact"),
+    }
+    # the base-greedy stage also launches vocab_proj_topk/topk_merge when it
+    # runs on the GEMV path; split those launches out by their counts
+    n_vt = prof.get("vocab_proj_topk", (0, 0.0))[0] / max(args.steps, 1)
+    if n_vt > 1:
+        per = prof["vocab_proj_topk"][1] / prof["vocab_proj_topk"][0] * 1e3
+        per_m = prof["topk_merge"][1] / prof["topk_merge"][0] * 1e3
+        st["heads_vocab_topk"] = per + per_m
+        st["base_greedy"] += (n_vt - 1) * (per + per_m)
+
+    # roofline of the dominant kernel: the vocabulary projection of the heads
+    itemsize = 2 if dt_str == "bf16" else 4
+    w2_bytes = K * V * H * itemsize
+    z_bytes = B * K * H * 4
+    algo_bytes = w2_bytes + z_bytes + B * K * topk * 8
+    vt_calls, vt_ms = prof["vocab_proj_topk"]
+    # one launch of the heads' projection per step (greedy launches, if any, read lm_head instead)
+    vt_us = kern_us["vocab_proj_topk"] if n_vt <= 1 else per
+    achieved = algo_bytes / (vt_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "vocab_proj_topk",
+                "bytes_per_launch": algo_bytes, "avg_us": round(vt_us, 2)}
+
+    t_verify_us = st["tree_attention"]
+    result = {
+        "metric": METRIC,
+        "value": round(1000.0 / ms_step, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt_str,
+        "data": "synthetic (seeded Philox inputs, random-init weights)",
+        "config": {"workload": cfg.name, "batch": B, "hidden": H, "vocab": V, "medusa_heads": K, "topk": topk,
+                   "tree_nodes": N, "attn_heads": cfg.nH, "head_dim": cfg.D, "kv_cache_len": list(cfg.P),
+                   "graph": bool(args.graph)},
+        "tree_verify_tokens_per_s": round(B * N / (t_verify_us * 1e-6), 1) if t_verify_us > 0 else None,
+        "stages_us": {k: round(v, 2) for k, v in st.items()},
+        "kernels_us": {k: round(v, 2) for k, v in kern_us.items()},
+        "wall_ms_per_step": round(1e3 * wall / args.steps, 4),
+        "roofline": roofline,
+        "input_gen_s": round(gen_s, 2),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, heads, att, root)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(cfg, heads, att, root):
+    """The float64 oracle on the host cores, on a bounded sample of the same
+    step, scaled to steps/s: one of the K heads (x K), 4 of the attention
+    heads (x nH/4), 8 of the B*N greedy rows (lm_head is widened once; the
+    per-row product is scaled x B*N/8)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    dt = cfg.dtype
+    t = {}
+    t0 = time.perf_counter()
+    h = oracle.widen(heads["h"], dt)
+    W1 = oracle.widen(heads["W1"][:1], dt)
+    b1 = oracle.widen(heads["b1"][:1], dt)
+    W2 = oracle.widen(heads["W2"][:1], dt)
+    logits, _ = oracle.medusa_heads(h, W1, b1, W2)
+    oracle.topk(logits, cfg.topk)
+    t["heads"] = (time.perf_counter() - t0) * cfg.K
+    del W1, W2
+    nh = min(4, cfg.nH)
+    parent, rank = cfg.tree.arrays()
+    t0 = time.perf_counter()
+    w = {k: oracle.widen(att[k], dt) for k in ("q", "k_tree", "v_tree", "k_cache", "v_cache")}
+    kv_sel = slice(0, max(1, nh * cfg.nKV // cfg.nH))
+    o = oracle.tree_attention(w["q"][:, :, :nh], w["k_tree"][:, :, kv_sel], w["v_tree"][:, :, kv_sel],
+                              w["k_cache"][:, kv_sel], w["v_cache"][:, kv_sel], att["cache_len"], parent,
+                              1.0 / np.sqrt(cfg.D))
+    t["attention"] = (time.perf_counter() - t0) * cfg.nH / nh
+    t0 = time.perf_counter()
+    lm = oracle.widen(heads["lm_head"], dt)
+    t_widen = time.perf_counter() - t0
+    rows = np.random.default_rng(0).normal(0, 1, (8, cfg.H))
+    t0 = time.perf_counter()
+    oracle.base_greedy(rows, lm, 1e-6, dt == "bf16")
+    t["base_greedy"] = t_widen + (time.perf_counter() - t0) * cfg.B * cfg.N / 8
+    del lm
+    tok = np.zeros((cfg.B, cfg.N), dtype=np.int32)
+    t0 = time.perf_counter()
+    for b in range(cfg.B):
+        L, path, _ = oracle.accept(parent, tok[b], np.ones(cfg.N, dtype=np.int32))
+    t["accept"] = time.perf_counter() - t0
+    total = sum(t.values())
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": round(1.0 / total, 5), "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 NumPy oracle: 1 of {cfg.K} heads, {nh} of {cfg.nH} attention heads, 8 of "
+                      f"{cfg.B * cfg.N} greedy rows, each stage timed and scaled linearly to the full step",
+            "stage_s": {k: round(v, 3) for k, v in t.items()},
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,208 @@
+/*
+ * medusa.h -- C ABI of one Medusa decoding step on an AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The calls follow the method as the "Medusa Heads" glossary page
+ * (Ultralytics; Arabic and Portuguese editions carry the same text) states it:
+ *   - section on how the heads predict later tokens: K heads read the same last
+ *     hidden state h; head k is one feed-forward layer with SiLU and a residual
+ *     connection, then a projection to the vocabulary
+ *     (medusa_resid_silu, medusa_vocab_topk, medusa_heads_forward);
+ *   - section on tree attention and acceptance: the heads' top guesses form a
+ *     Cartesian candidate tree (medusa_tree_create, medusa_build_tree); every
+ *     candidate is verified in one pass in which each token sees only its tree
+ *     ancestors (tree_attention_verify); under greedy decoding a candidate is
+ *     accepted when it equals the base model's top choice
+ *     (medusa_base_greedy), the longest accepted branch is kept and its state
+ *     is handed to the next round (medusa_accept, which also compacts the
+ *     accepted branch's keys/values in the cache).
+ * The accepted-tokens-plus-one accounting (a correction or bonus token every
+ * round) follows the speculative-decoding e-book "Giai ma dau co: doan truoc
+ * roi kiem mot luot", section on why a round always yields k + 1 tokens.
+ *
+ * Conventions
+ *   - Every pointer is a device pointer unless marked "host".
+ *   - Every compute call is asynchronous on `stream` (a hipStream_t passed as
+ *     void*; NULL = the default stream) and returns a medusa_status.  All
+ *     arguments are validated on the host before anything is enqueued; on an
+ *     error nothing is enqueued and medusa_last_error() describes it.
+ *   - The caller owns every buffer.  Scratch memory comes from a caller
+ *     workspace `ws` of at least the size the matching *_workspace_size()
+ *     returns; the compute calls never allocate.  The workspace must not be
+ *     shared by calls that may run concurrently.
+ *   - dtype MEDUSA_F32: float32 storage.  MEDUSA_BF16: bfloat16 storage
+ *     (uint16 bit patterns).  Accumulation is always float32.
+ *   - Row-major layouts; weights use the [out][in] layout of a linear layer.
+ *   - Top-k and argmax order: larger value first, lower index first among
+ *     equal values; decisions are taken on the float32 accumulators.
+ */
+#ifndef MEDUSA_H
+#define MEDUSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MEDUSA_OK = 0,
+    MEDUSA_EINVAL = 1,        /* null pointer, bad shape, bad tree spec, sizes too small */
+    MEDUSA_EUNSUPPORTED = 2,  /* valid request outside the implemented envelope */
+    MEDUSA_EHIP = 3           /* a HIP runtime call or kernel launch failed */
+} medusa_status;
+
+typedef enum { MEDUSA_F32 = 0, MEDUSA_BF16 = 1 } medusa_dtype;
+
+/* Opaque candidate-tree topology (library-owned; device copy inside). */
+typedef struct medusa_tree medusa_tree;
+
+/* Thread-local description of the last error on this thread ("" if none). */
+const char* medusa_last_error(void);
+const char* medusa_version(void);
+
+/* Implementation limits. */
+#define MEDUSA_MAX_TREE_NODES 256
+#define MEDUSA_MAX_TOPK 16
+#define MEDUSA_MAX_DEPTH 16
+#define MEDUSA_MAX_BATCH 8
+
+/* ---------------------------------------------------------------------------
+ * Step a1 -- residual-SiLU block of every head (heads page, section on how the
+ * heads predict later tokens):  z[b][k][:] = h[b] + SiLU(W1_k h[b] + b1_k).
+ *   h  [B][H] (dt), w1 [K][H][H] (dt, [out][in]), b1 [K][H] (dt)
+ *   z  [B][K][H] float32 (output)
+ * Limits: 1 <= B <= 8, H % 8 == 0, H <= 8192.
+ * ------------------------------------------------------------------------- */
+medusa_status medusa_resid_silu(const void* h, const void* w1, const void* b1,
+                                int B, int H, int K, medusa_dtype dt,
+                                float* z, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Step a2 -- vocabulary projection and per-head top-k (heads page: projection
+ * to the vocabulary; tree section: the heads' top guesses).
+ *   z        [B][K][H] float32: head k's input for sequence b
+ *   w2       [K][V][H] (dt): head k's projection (no bias)
+ *   logits   [B][K][V] float32, optional (NULL: not written)
+ *   topk_idx [B][K][topk] int32, topk_val [B][K][topk] float32 (outputs)
+ * Limits: 1 <= topk <= min(16, V), 1 <= B <= 8, H % 8 == 0, H <= 8192.
+ * ------------------------------------------------------------------------- */
+size_t medusa_vocab_topk_workspace_size(int B, int H, int V, int K, int topk, medusa_dtype dt);
+medusa_status medusa_vocab_topk(const float* z, const void* w2,
+                                int B, int H, int V, int K, int topk, medusa_dtype dt,
+                                float* logits, int32_t* topk_idx, float* topk_val,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Steps a1 + a2 in one call: the K Medusa heads on the last hidden state.
+ *   w1 == NULL and b1 == NULL: z_k = h for every head (plain projection, e.g.
+ *   the base model's lm_head with K = 1).  Workspace holds z and the top-k
+ *   partials.  Other arguments as above.
+ * ------------------------------------------------------------------------- */
+size_t medusa_heads_workspace_size(int B, int H, int V, int K, int topk, medusa_dtype dt);
+medusa_status medusa_heads_forward(const void* h, const void* w1, const void* b1, const void* w2,
+                                   int B, int H, int V, int K, int topk, medusa_dtype dt,
+                                   float* logits, int32_t* topk_idx, float* topk_val,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Step a3 -- candidate tree (tree section: Cartesian product of the heads'
+ * top guesses, sharing prefixes).
+ *
+ * medusa_tree_create: host arrays parent[N], rank[N] in breadth-first order.
+ *   Node 0 is the root (parent[0] = -1, the token the base model already
+ *   chose); node i > 0 has 0 <= parent[i] < i and carries the rank[i]-th token
+ *   (0 <= rank[i] < topk) of head depth(i) (1 <= depth(i) <= K).  Siblings
+ *   must have distinct ranks.  1 <= N <= 256.  Uploads the spec and the
+ *   ancestor bitmask to the current device (allocates; not for hot loops).
+ * medusa_build_tree: node_tok[b][i] = root_tok[b] for i = 0, else
+ *   topk_idx[b][depth(i)-1][rank[i]];  node_pos[b][i] = cache_len[b] + depth(i);
+ *   anc_mask (optional) [N][W] uint64, W = ceil(N/64): bit j of word j/64 of
+ *   row i is set iff node j is node i or an ancestor of i.
+ * ------------------------------------------------------------------------- */
+medusa_status medusa_tree_create(const int32_t* parent, const int32_t* rank, int N, int K, int topk,
+                                 medusa_tree** out);
+void medusa_tree_destroy(medusa_tree* tree);
+int medusa_tree_num_nodes(const medusa_tree* tree);
+int medusa_tree_max_depth(const medusa_tree* tree);
+/* host copy of the ancestor bitmask, [N][ceil(N/64)] */
+medusa_status medusa_tree_mask_host(const medusa_tree* tree, uint64_t* mask, size_t words);
+
+medusa_status medusa_build_tree(const medusa_tree* tree, const int32_t* topk_idx,
+                                const int32_t* root_tok, const int32_t* cache_len, int B, int K, int topk,
+                                int32_t* node_tok, int32_t* node_pos, uint64_t* anc_mask, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Step a4 -- tree-masked attention (tree section: all candidates appended in
+ * one pass; each token sees only its ancestors -- and itself).
+ *   q [B][N][nH][D], k_tree / v_tree [B][N][nKV][D] (dt)
+ *   k_cache / v_cache [B][nKV][Lmax][D] (dt): slots < cache_len[b] are the
+ *     prefix; this call also writes the tree keys/values to slots
+ *     cache_len[b] .. cache_len[b]+N-1.
+ *   out [B][N][nH][D] (dt): o = sum_j softmax_j(scale * q.k_j) v_j over the
+ *     prefix and the node's ancestors-or-self; query head h reads KV head
+ *     h / (nH / nKV).
+ *   max_cache_len (host): an upper bound of cache_len[] (sizes the launch).
+ * Limits: D in {64, 128}; nH % nKV == 0; cache_len[b] + N <= Lmax.
+ * ------------------------------------------------------------------------- */
+size_t tree_attention_workspace_size(const medusa_tree* tree, int B, int nH, int D,
+                                     int max_cache_len, medusa_dtype dt);
+medusa_status tree_attention_verify(const void* q, const void* k_tree, const void* v_tree,
+                                    void* k_cache, void* v_cache, const int32_t* cache_len,
+                                    int max_cache_len, const medusa_tree* tree,
+                                    int B, int nH, int nKV, int D, int Lmax, float scale,
+                                    medusa_dtype dt, void* out, void* ws, size_t ws_bytes,
+                                    void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Step a5 -- the base model's greedy choice after every tree node (tree
+ * section: greedy acceptance compares with the model's top choice).
+ *   x [R][H] (dt): one row per node; n = x * rsqrt(mean(x^2) + eps) (unit
+ *   weight), rounded to bf16 when dt is BF16; greedy[r] = argmax_v
+ *   (lm_head[v] . n_r), lower index first among equal values.
+ *   lm_head [V][H] (dt); greedy [R] int32; logits [R][V] float32 optional.
+ * Limits: H % 8 == 0, H <= 8192, R >= 1.
+ * ------------------------------------------------------------------------- */
+size_t medusa_base_greedy_workspace_size(int R, int H, int V, medusa_dtype dt);
+medusa_status medusa_base_greedy(const void* x, const void* lm_head, int R, int H, int V, float eps,
+                                 medusa_dtype dt, int32_t* greedy, float* logits,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Steps a6 + a7 -- longest accepted branch and its KV hand-off (tree section:
+ * keep the longest branch the model accepts; its final state feeds the heads
+ * next round; e-book: a round yields the accepted tokens plus one).
+ *   node_tok, greedy [B][N] int32 (greedy[b][i]: base choice after node i)
+ *   accept_len [B]: L = depth of the deepest node whose whole chain matches
+ *   accept_nodes [B][Dmax+1]: node ids of the accepted path (root first),
+ *     -1 after position L;  Dmax = the tree's maximum depth
+ *   out_tokens [B][Dmax+1]: the L accepted tokens then greedy[path[L]]
+ *     (the correction/bonus token, next round's root), -1 after position L
+ *   cache_len [B] (in) / new_cache_len [B] (out) = cache_len + L + 1
+ *   k_cache / v_cache (optional, both or neither): n_layers caches, layer l
+ *     at base + l * layer_stride_elems, each [B][nKV][Lmax][D] (dt); for
+ *     d = 1..L slot cache_len+d receives slot cache_len+path[d] (all sources
+ *     read before any write).
+ * ------------------------------------------------------------------------- */
+medusa_status medusa_accept(const medusa_tree* tree, const int32_t* node_tok, const int32_t* greedy,
+                            int B, int32_t* accept_len, int32_t* accept_nodes, int32_t* out_tokens,
+                            const int32_t* cache_len, int32_t* new_cache_len,
+                            void* k_cache, void* v_cache, int n_layers, int64_t layer_stride_elems,
+                            int nKV, int D, int Lmax, medusa_dtype dt, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Kernel timing: while enabled, every kernel launch of the library is
+ * bracketed by HIP events on its stream.  medusa_profiler_collect waits for
+ * the recorded events and folds them into per-kernel totals; ..._stat reads
+ * entry i (0 <= i < count) of those totals.
+ * ------------------------------------------------------------------------- */
+medusa_status medusa_profiler_enable(int on);
+medusa_status medusa_profiler_reset(void);
+int medusa_profiler_collect(void);
+medusa_status medusa_profiler_stat(int i, char* name, size_t name_len, int64_t* calls, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MEDUSA_H */

@@ -1,0 +1,273 @@
+"""Python binding of libmedusa.so, the HIP (gfx950) implementation of one
+Medusa decoding step.
+
+Argument marshalling only: torch tensors supply device memory and the current
+HIP stream; every step of the path runs in the library's kernels.  The
+functions carry the names of the C entry points declared in
+include/medusa.h.  There is no fallback: if the library is missing, importing
+this package fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmedusa.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m speculative_decoding_medusa_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
+F32, BF16 = 0, 1
+
+_vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_SIGS = {
+    "medusa_last_error": ([], ctypes.c_char_p),
+    "medusa_version": ([], ctypes.c_char_p),
+    "medusa_resid_silu": ([_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp], _i32),
+    "medusa_vocab_topk_workspace_size": ([_i32, _i32, _i32, _i32, _i32, _i32], _sz),
+    "medusa_vocab_topk": ([_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
+    "medusa_heads_workspace_size": ([_i32, _i32, _i32, _i32, _i32, _i32], _sz),
+    "medusa_heads_forward": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz,
+                              _vp], _i32),
+    "medusa_tree_create": ([_vp, _vp, _i32, _i32, _i32, ctypes.POINTER(_vp)], _i32),
+    "medusa_tree_destroy": ([_vp], None),
+    "medusa_tree_num_nodes": ([_vp], _i32),
+    "medusa_tree_max_depth": ([_vp], _i32),
+    "medusa_tree_mask_host": ([_vp, _vp, _sz], _i32),
+    "medusa_build_tree": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp], _i32),
+    "tree_attention_workspace_size": ([_vp, _i32, _i32, _i32, _i32, _i32], _sz),
+    "tree_attention_verify": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                               _vp, _vp, _sz, _vp], _i32),
+    "medusa_base_greedy_workspace_size": ([_i32, _i32, _i32, _i32], _sz),
+    "medusa_base_greedy": ([_vp, _vp, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
+    "medusa_accept": ([_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32,
+                       _vp], _i32),
+    "medusa_profiler_enable": ([_i32], _i32),
+    "medusa_profiler_reset": ([], _i32),
+    "medusa_profiler_collect": ([], _i32),
+    "medusa_profiler_stat": ([_i32, ctypes.c_char_p, _sz, ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double)],
+                             _i32),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = _res
+
+
+class MedusaError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed with status {status}: {_lib.medusa_last_error().decode()}")
+
+
+def _check(fn, st):
+    if st != OK:
+        raise MedusaError(fn, st)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dt(t) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ws(nbytes: int, device, ws):
+    if ws is None:
+        ws = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    assert ws.numel() * ws.element_size() >= nbytes, "workspace too small"
+    return ws
+
+
+def version() -> str:
+    return _lib.medusa_version().decode()
+
+
+# ---------------------------------------------------------------------------
+# a1 / a2
+# ---------------------------------------------------------------------------
+
+def medusa_resid_silu(h, w1, b1, z, stream=None):
+    K, H, _ = w1.shape
+    B = h.shape[0]
+    _check("medusa_resid_silu", _lib.medusa_resid_silu(_p(h), _p(w1), _p(b1), B, H, K, _dt(w1), _p(z),
+                                                       _stream(stream)))
+    return z
+
+
+def vocab_topk_workspace_size(B, H, V, K, topk, dt):
+    return _lib.medusa_vocab_topk_workspace_size(B, H, V, K, topk, dt)
+
+
+def medusa_vocab_topk(z, w2, topk, topk_idx, topk_val, logits=None, ws=None, stream=None):
+    K, V, H = w2.shape
+    B = z.shape[0]
+    dt = _dt(w2)
+    need = vocab_topk_workspace_size(B, H, V, K, topk, dt)
+    ws = _ws(need, z.device, ws)
+    _check("medusa_vocab_topk", _lib.medusa_vocab_topk(_p(z), _p(w2), B, H, V, K, topk, dt, _p(logits),
+                                                       _p(topk_idx), _p(topk_val), _p(ws),
+                                                       ws.numel() * ws.element_size(), _stream(stream)))
+    return topk_idx, topk_val
+
+
+def heads_workspace_size(B, H, V, K, topk, dt):
+    return _lib.medusa_heads_workspace_size(B, H, V, K, topk, dt)
+
+
+def medusa_heads_forward(h, w1, b1, w2, topk, topk_idx, topk_val, logits=None, ws=None, stream=None):
+    K, V, H = w2.shape
+    B = h.shape[0]
+    dt = _dt(w2)
+    need = heads_workspace_size(B, H, V, K, topk, dt)
+    ws = _ws(need, h.device, ws)
+    _check("medusa_heads_forward", _lib.medusa_heads_forward(
+        _p(h), _p(w1), _p(b1), _p(w2), B, H, V, K, topk, dt, _p(logits), _p(topk_idx), _p(topk_val), _p(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
+    return topk_idx, topk_val
+
+
+# ---------------------------------------------------------------------------
+# a3
+# ---------------------------------------------------------------------------
+
+class Tree:
+    """Owner of a medusa_tree handle (topology uploaded to the current device)."""
+
+    def __init__(self, parent, rank, K: int, topk: int):
+        import numpy as np
+        self._parent = np.ascontiguousarray(parent, dtype=np.int32)
+        self._rank = np.ascontiguousarray(rank, dtype=np.int32)
+        h = ctypes.c_void_p()
+        _check("medusa_tree_create", _lib.medusa_tree_create(
+            self._parent.ctypes.data, self._rank.ctypes.data, len(self._parent), K, topk, ctypes.byref(h)))
+        self.handle = h
+        self.N = _lib.medusa_tree_num_nodes(h)
+        self.max_depth = _lib.medusa_tree_max_depth(h)
+        self.W = (self.N + 63) // 64
+
+    def mask_host(self):
+        import numpy as np
+        m = np.zeros((self.N, self.W), dtype=np.uint64)
+        _check("medusa_tree_mask_host", _lib.medusa_tree_mask_host(self.handle, m.ctypes.data, m.size))
+        return m
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value:
+            _lib.medusa_tree_destroy(h)
+            self.handle = None
+
+
+def medusa_build_tree(tree: Tree, topk_idx, root_tok, cache_len, node_tok, node_pos, anc_mask=None, stream=None):
+    B, K, topk = topk_idx.shape
+    _check("medusa_build_tree", _lib.medusa_build_tree(
+        tree.handle, _p(topk_idx), _p(root_tok), _p(cache_len), B, K, topk, _p(node_tok), _p(node_pos),
+        _p(anc_mask), _stream(stream)))
+    return node_tok, node_pos
+
+
+# ---------------------------------------------------------------------------
+# a4
+# ---------------------------------------------------------------------------
+
+def tree_attention_workspace_size(tree: Tree, B, nH, D, max_cache_len, dt):
+    return _lib.tree_attention_workspace_size(tree.handle, B, nH, D, max_cache_len, dt)
+
+
+def tree_attention_verify(q, k_tree, v_tree, k_cache, v_cache, cache_len, max_cache_len: int, tree: Tree, out,
+                          scale=None, ws=None, stream=None):
+    B, N, nH, D = q.shape
+    nKV = k_tree.shape[2]
+    Lmax = k_cache.shape[2]
+    dt = _dt(q)
+    if scale is None:
+        scale = 1.0 / (D ** 0.5)
+    need = tree_attention_workspace_size(tree, B, nH, D, max_cache_len, dt)
+    ws = _ws(need, q.device, ws)
+    _check("tree_attention_verify", _lib.tree_attention_verify(
+        _p(q), _p(k_tree), _p(v_tree), _p(k_cache), _p(v_cache), _p(cache_len), int(max_cache_len), tree.handle,
+        B, nH, nKV, D, Lmax, float(scale), dt, _p(out), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# a5
+# ---------------------------------------------------------------------------
+
+def base_greedy_workspace_size(R, H, V, dt):
+    return _lib.medusa_base_greedy_workspace_size(R, H, V, dt)
+
+
+def medusa_base_greedy(x, lm_head, greedy, eps=1e-6, logits=None, ws=None, stream=None):
+    V, H = lm_head.shape
+    R = x.numel() // H
+    dt = _dt(lm_head)
+    need = base_greedy_workspace_size(R, H, V, dt)
+    ws = _ws(need, x.device, ws)
+    _check("medusa_base_greedy", _lib.medusa_base_greedy(
+        _p(x), _p(lm_head), R, H, V, float(eps), dt, _p(greedy), _p(logits), _p(ws), ws.numel() * ws.element_size(),
+        _stream(stream)))
+    return greedy
+
+
+# ---------------------------------------------------------------------------
+# a6 + a7
+# ---------------------------------------------------------------------------
+
+def medusa_accept(tree: Tree, node_tok, greedy, accept_len, accept_nodes, out_tokens, cache_len, new_cache_len,
+                  k_cache=None, v_cache=None, stream=None):
+    """k_cache / v_cache: None, or [layers][B][nKV][Lmax][D] / [B][nKV][Lmax][D] tensors."""
+    B = node_tok.shape[0]
+    n_layers, nKV, D, Lmax, stride, dt = 0, 0, 0, 0, 0, F32
+    if k_cache is not None:
+        kc = k_cache if k_cache.dim() == 5 else k_cache.unsqueeze(0)
+        n_layers, _, nKV, Lmax, D = kc.shape
+        stride = kc.stride(0)
+        dt = _dt(kc)
+    _check("medusa_accept", _lib.medusa_accept(
+        tree.handle, _p(node_tok), _p(greedy), B, _p(accept_len), _p(accept_nodes), _p(out_tokens), _p(cache_len),
+        _p(new_cache_len), _p(k_cache), _p(v_cache), n_layers, stride, nKV, D, Lmax, dt, _stream(stream)))
+    return accept_len
+
+
+# ---------------------------------------------------------------------------
+# kernel timing
+# ---------------------------------------------------------------------------
+
+def profiler_enable(on: bool = True):
+    _lib.medusa_profiler_enable(1 if on else 0)
+
+
+def profiler_reset():
+    _lib.medusa_profiler_reset()
+
+
+def profiler_collect() -> dict:
+    """{kernel name: (launches, total milliseconds)} since the last reset."""
+    n = _lib.medusa_profiler_collect()
+    out = {}
+    for i in range(n):
+        name = ctypes.create_string_buffer(128)
+        calls = ctypes.c_int64()
+        ms = ctypes.c_double()
+        _check("medusa_profiler_stat", _lib.medusa_profiler_stat(i, name, 128, ctypes.byref(calls), ctypes.byref(ms)))
+        out[name.value.decode()] = (calls.value, ms.value)
+    return out

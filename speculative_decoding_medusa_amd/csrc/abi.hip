@@ -1,0 +1,482 @@
+// C ABI of the Medusa step library: argument validation, workspace carving,
+// tree objects, kernel timing.  Every check runs on the host before anything
+// is enqueued.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/medusa.h"
+#include "common.hpp"
+#include "tree.hpp"
+
+namespace medusa {
+
+// launchers (kernel files)
+void launch_resid_silu(const void* h, const void* w1, const void* b1, int B, int H, int K, bool bf16, float* z,
+                       hipStream_t s);
+void launch_vocab_topk(const float* z, const void* w2, int B, int H, int V, int K, int topk, bool bf16,
+                       float* logits, int32_t* topk_idx, float* topk_val, float* cv, int* ci, hipStream_t s);
+int vocab_topk_groups(int V, int K);
+void launch_build_tree(const TreeDev& t, const int32_t* topk_idx, int K, int topk, const int32_t* root_tok,
+                       const int32_t* cache_len, int B, int32_t* node_tok, int32_t* node_pos, uint64_t* anc_mask,
+                       hipStream_t s);
+void launch_tree_attention(const void* q, const void* k_tree, const void* v_tree, void* k_cache, void* v_cache,
+                           const int32_t* cache_len, int max_cache_len, const TreeDev& t, int B, int nH, int nKV,
+                           int D, int Lmax, float scale, bool bf16, void* out, float* part_o, float* part_ml,
+                           hipStream_t s);
+size_t attn_workspace_bytes(int B, int nH, int N, int D, int max_cache_len);
+void attn_carve(int B, int nH, int N, int D, int max_cache_len, void* ws, float** part_o, float** part_ml);
+size_t greedy_workspace_bytes(int R, int H, int V);
+void launch_base_greedy(const void* x, const void* lm_head, int R, int H, int V, float eps, bool bf16,
+                        int32_t* greedy, float* logits, void* ws, hipStream_t s);
+void launch_accept(const TreeDev& t, const int32_t* node_tok, const int32_t* greedy, int B, int32_t* accept_len,
+                   int32_t* accept_nodes, int32_t* out_tokens, const int32_t* cache_len, int32_t* new_cache_len,
+                   void* k_cache, void* v_cache, int n_layers, int64_t layer_stride, int nKV, int D, int Lmax,
+                   bool bf16, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// errors
+// ---------------------------------------------------------------------------
+static thread_local std::string g_err;
+void set_error(const std::string& msg) { g_err = msg; }
+
+struct Fail {
+    medusa_status st;
+};
+
+static void failf(medusa_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    set_error(buf);
+    throw Fail{st};
+}
+#define REQUIRE(cond, ...) \
+    do {                   \
+        if (!(cond)) failf(MEDUSA_EINVAL, __VA_ARGS__); \
+    } while (0)
+#define SUPPORT(cond, ...) \
+    do {                   \
+        if (!(cond)) failf(MEDUSA_EUNSUPPORTED, __VA_ARGS__); \
+    } while (0)
+
+static medusa_status finish_launches(const char* what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        set_error(std::string(what) + ": " + hipGetErrorString(e));
+        return MEDUSA_EHIP;
+    }
+    return MEDUSA_OK;
+}
+
+template <typename F>
+static medusa_status guarded(const char* what, F&& f) {
+    g_err.clear();
+    try {
+        f();
+    } catch (const Fail& x) {
+        return x.st;
+    }
+    return finish_launches(what);
+}
+
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// ---------------------------------------------------------------------------
+// kernel timing
+// ---------------------------------------------------------------------------
+struct ProfRec {
+    const char* name;
+    hipEvent_t a, b;
+};
+struct ProfStat {
+    int64_t calls = 0;
+    double ms = 0.0;
+};
+static std::mutex g_prof_mu;
+static bool g_prof_on = false;
+static std::vector<ProfRec> g_prof_pending;
+static std::vector<hipEvent_t> g_prof_pool;
+static std::map<std::string, ProfStat> g_prof_stats;
+static std::vector<std::pair<std::string, ProfStat>> g_prof_snapshot;
+static thread_local const char* g_prof_name = nullptr;
+static thread_local hipEvent_t g_prof_a = nullptr;
+
+static hipEvent_t prof_event() {
+    if (!g_prof_pool.empty()) {
+        hipEvent_t e = g_prof_pool.back();
+        g_prof_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    hipEventCreate(&e);
+    return e;
+}
+
+void prof_before(const char* name, hipStream_t s) {
+    if (!g_prof_on) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_name = name;
+    g_prof_a = prof_event();
+    hipEventRecord(g_prof_a, s);
+}
+
+void prof_after(hipStream_t s) {
+    if (!g_prof_on || g_prof_a == nullptr) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    hipEvent_t b = prof_event();
+    hipEventRecord(b, s);
+    g_prof_pending.push_back({g_prof_name, g_prof_a, b});
+    g_prof_a = nullptr;
+}
+
+}  // namespace medusa
+
+using namespace medusa;
+
+struct medusa_tree {
+    TreeDev t;
+};
+
+extern "C" {
+
+const char* medusa_last_error(void) { return g_err.c_str(); }
+const char* medusa_version(void) { return "medusa-mi355x 0.1 (gfx950)"; }
+
+// ---------------------------------------------------------------------------
+// a1 / a2
+// ---------------------------------------------------------------------------
+static void check_heads_shape(int B, int H, int K, medusa_dtype dt) {
+    REQUIRE(dt == MEDUSA_F32 || dt == MEDUSA_BF16, "dtype must be MEDUSA_F32 or MEDUSA_BF16");
+    REQUIRE(B >= 1 && K >= 1 && H >= 1, "B, H and K must be positive (B=%d H=%d K=%d)", B, H, K);
+    SUPPORT(B <= MEDUSA_MAX_BATCH, "B=%d exceeds %d", B, MEDUSA_MAX_BATCH);
+    SUPPORT(H % 8 == 0 && H <= 8192, "H=%d must be a multiple of 8 and <= 8192", H);
+    SUPPORT((size_t)((B <= 1) ? 1 : (B <= 2) ? 2 : (B <= 4) ? 4 : 8) * H * 4 <= 160 * 1024,
+            "B*H too large for the LDS-staged right-hand sides");
+}
+
+medusa_status medusa_resid_silu(const void* h, const void* w1, const void* b1, int B, int H, int K,
+                                medusa_dtype dt, float* z, void* stream) {
+    return guarded("medusa_resid_silu", [&] {
+        check_heads_shape(B, H, K, dt);
+        REQUIRE(h && w1 && b1 && z, "null pointer argument");
+        launch_resid_silu(h, w1, b1, B, H, K, dt == MEDUSA_BF16, z, (hipStream_t)stream);
+    });
+}
+
+size_t medusa_vocab_topk_workspace_size(int B, int H, int V, int K, int topk, medusa_dtype dt) {
+    (void)H; (void)dt;
+    if (B < 1 || V < 1 || K < 1 || topk < 1) return 0;
+    const size_t G = (size_t)vocab_topk_groups(V, K);
+    return align256((size_t)B * K * G * topk * 4) * 2;
+}
+
+static void carve_vocab_ws(void* ws, int B, int V, int K, int topk, float** cv, int** ci) {
+    const size_t G = (size_t)vocab_topk_groups(V, K);
+    const size_t one = align256((size_t)B * K * G * topk * 4);
+    *cv = (float*)ws;
+    *ci = (int*)((char*)ws + one);
+}
+
+static void check_vocab(int B, int H, int V, int K, int topk, medusa_dtype dt) {
+    check_heads_shape(B, H, K, dt);
+    REQUIRE(V >= 1, "V must be positive");
+    REQUIRE(topk >= 1 && topk <= V, "topk=%d must be in [1, V]", topk);
+    SUPPORT(topk <= MEDUSA_MAX_TOPK, "topk=%d exceeds %d", topk, MEDUSA_MAX_TOPK);
+}
+
+medusa_status medusa_vocab_topk(const float* z, const void* w2, int B, int H, int V, int K, int topk,
+                                medusa_dtype dt, float* logits, int32_t* topk_idx, float* topk_val, void* ws,
+                                size_t ws_bytes, void* stream) {
+    return guarded("medusa_vocab_topk", [&] {
+        check_vocab(B, H, V, K, topk, dt);
+        REQUIRE(z && w2 && topk_idx && topk_val && ws, "null pointer argument");
+        const size_t need = medusa_vocab_topk_workspace_size(B, H, V, K, topk, dt);
+        REQUIRE(ws_bytes >= need, "workspace too small: %zu < %zu", ws_bytes, need);
+        float* cv;
+        int* ci;
+        carve_vocab_ws(ws, B, V, K, topk, &cv, &ci);
+        launch_vocab_topk(z, w2, B, H, V, K, topk, dt == MEDUSA_BF16, logits, topk_idx, topk_val, cv, ci,
+                          (hipStream_t)stream);
+    });
+}
+
+size_t medusa_heads_workspace_size(int B, int H, int V, int K, int topk, medusa_dtype dt) {
+    if (B < 1 || H < 1 || V < 1 || K < 1 || topk < 1) return 0;
+    return align256((size_t)B * K * H * 4) + medusa_vocab_topk_workspace_size(B, H, V, K, topk, dt);
+}
+
+// z = h for every head (lm_head mode)
+__global__ void broadcast_h_kernel(const void* h, int B, int H, int K, int bf16, float* z) {
+    const size_t n = (size_t)B * K * H;
+    for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
+        const size_t b = e / ((size_t)K * H), j = e % H;
+        z[e] = bf16 ? bf16_to_f32(((const bf16_t*)h)[b * H + j]) : ((const float*)h)[b * H + j];
+    }
+}
+
+medusa_status medusa_heads_forward(const void* h, const void* w1, const void* b1, const void* w2, int B, int H,
+                                   int V, int K, int topk, medusa_dtype dt, float* logits, int32_t* topk_idx,
+                                   float* topk_val, void* ws, size_t ws_bytes, void* stream) {
+    return guarded("medusa_heads_forward", [&] {
+        check_vocab(B, H, V, K, topk, dt);
+        REQUIRE(h && w2 && topk_idx && topk_val && ws, "null pointer argument");
+        REQUIRE((w1 == nullptr) == (b1 == nullptr), "w1 and b1 must both be given or both be NULL");
+        const size_t need = medusa_heads_workspace_size(B, H, V, K, topk, dt);
+        REQUIRE(ws_bytes >= need, "workspace too small: %zu < %zu", ws_bytes, need);
+        float* z = (float*)ws;
+        void* vws = (char*)ws + align256((size_t)B * K * H * 4);
+        hipStream_t s = (hipStream_t)stream;
+        if (w1)
+            launch_resid_silu(h, w1, b1, B, H, K, dt == MEDUSA_BF16, z, s);
+        else
+            MEDUSA_LAUNCH("broadcast_h", broadcast_h_kernel, dim3(64), dim3(256), 0, s, h, B, H, K,
+                          dt == MEDUSA_BF16 ? 1 : 0, z);
+        float* cv;
+        int* ci;
+        carve_vocab_ws(vws, B, V, K, topk, &cv, &ci);
+        launch_vocab_topk(z, w2, B, H, V, K, topk, dt == MEDUSA_BF16, logits, topk_idx, topk_val, cv, ci, s);
+    });
+}
+
+// ---------------------------------------------------------------------------
+// a3 tree
+// ---------------------------------------------------------------------------
+medusa_status medusa_tree_create(const int32_t* parent, const int32_t* rank, int N, int K, int topk,
+                                 medusa_tree** out) {
+    g_err.clear();
+    try {
+        REQUIRE(parent && rank && out, "null pointer argument");
+        REQUIRE(N >= 1, "N must be >= 1");
+        SUPPORT(N <= MEDUSA_MAX_TREE_NODES, "N=%d exceeds %d", N, MEDUSA_MAX_TREE_NODES);
+        REQUIRE(K >= 1 && topk >= 1, "K and topk must be >= 1");
+        SUPPORT(topk <= MEDUSA_MAX_TOPK, "topk=%d exceeds %d", topk, MEDUSA_MAX_TOPK);
+        REQUIRE(parent[0] == -1, "parent[0] must be -1 (root)");
+        TreeDev t;
+        t.N = N;
+        t.W = (N + 63) / 64;
+        t.K = K;
+        t.topk = topk;
+        t.h_parent.assign(parent, parent + N);
+        t.h_rank.assign(N, 0);
+        t.h_depth.assign(N, 0);
+        std::vector<uint32_t> seen((size_t)N * ((topk + 31) / 32), 0u);
+        for (int i = 1; i < N; ++i) {
+            const int p = parent[i];
+            REQUIRE(p >= 0 && p < i, "parent[%d]=%d must satisfy 0 <= parent < index", i, p);
+            REQUIRE(rank[i] >= 0 && rank[i] < topk, "rank[%d]=%d must be in [0, topk=%d)", i, rank[i], topk);
+            t.h_depth[i] = t.h_depth[p] + 1;
+            t.h_rank[i] = rank[i];
+            REQUIRE(t.h_depth[i] <= K, "node %d has depth %d > K=%d", i, t.h_depth[i], K);
+            SUPPORT(t.h_depth[i] <= MEDUSA_MAX_DEPTH, "node %d depth exceeds %d", i, MEDUSA_MAX_DEPTH);
+            uint32_t& w = seen[(size_t)p * ((topk + 31) / 32) + rank[i] / 32];
+            REQUIRE(!(w & (1u << (rank[i] % 32))), "node %d repeats rank %d under parent %d", i, rank[i], p);
+            w |= 1u << (rank[i] % 32);
+            if (t.h_depth[i] > t.max_depth) t.max_depth = t.h_depth[i];
+            if (rank[i] > t.max_rank) t.max_rank = rank[i];
+        }
+        t.h_mask.assign((size_t)N * t.W, 0ull);
+        for (int i = 0; i < N; ++i)
+            for (int j = i; j >= 0; j = j > 0 ? t.h_parent[j] : -1) t.h_mask[(size_t)i * t.W + j / 64] |= 1ull << (j % 64);
+        // upload
+        hipError_t e = hipSuccess;
+        auto up = [&](void** dst, const void* src, size_t bytes) {
+            if (e != hipSuccess) return;
+            e = hipMalloc(dst, bytes);
+            if (e == hipSuccess) e = hipMemcpy(*dst, src, bytes, hipMemcpyHostToDevice);
+        };
+        up((void**)&t.parent, t.h_parent.data(), N * sizeof(int));
+        up((void**)&t.depth, t.h_depth.data(), N * sizeof(int));
+        up((void**)&t.rank, t.h_rank.data(), N * sizeof(int));
+        up((void**)&t.mask, t.h_mask.data(), t.h_mask.size() * sizeof(uint64_t));
+        if (e != hipSuccess) {
+            hipFree(t.parent); hipFree(t.depth); hipFree(t.rank); hipFree(t.mask);
+            set_error(std::string("medusa_tree_create: ") + hipGetErrorString(e));
+            return MEDUSA_EHIP;
+        }
+        medusa_tree* obj = new medusa_tree;
+        obj->t = std::move(t);
+        *out = obj;
+    } catch (const Fail& x) {
+        return x.st;
+    }
+    return MEDUSA_OK;
+}
+
+void medusa_tree_destroy(medusa_tree* tree) {
+    if (!tree) return;
+    hipFree(tree->t.parent);
+    hipFree(tree->t.depth);
+    hipFree(tree->t.rank);
+    hipFree(tree->t.mask);
+    delete tree;
+}
+
+int medusa_tree_num_nodes(const medusa_tree* tree) { return tree ? tree->t.N : 0; }
+int medusa_tree_max_depth(const medusa_tree* tree) { return tree ? tree->t.max_depth : 0; }
+
+medusa_status medusa_tree_mask_host(const medusa_tree* tree, uint64_t* mask, size_t words) {
+    g_err.clear();
+    if (!tree || !mask) { set_error("null pointer argument"); return MEDUSA_EINVAL; }
+    if (words < tree->t.h_mask.size()) { set_error("mask buffer too small"); return MEDUSA_EINVAL; }
+    memcpy(mask, tree->t.h_mask.data(), tree->t.h_mask.size() * sizeof(uint64_t));
+    return MEDUSA_OK;
+}
+
+medusa_status medusa_build_tree(const medusa_tree* tree, const int32_t* topk_idx, const int32_t* root_tok,
+                                const int32_t* cache_len, int B, int K, int topk, int32_t* node_tok,
+                                int32_t* node_pos, uint64_t* anc_mask, void* stream) {
+    return guarded("medusa_build_tree", [&] {
+        REQUIRE(tree && topk_idx && root_tok && cache_len && node_tok && node_pos, "null pointer argument");
+        REQUIRE(B >= 1, "B must be >= 1");
+        REQUIRE(K >= tree->t.max_depth, "K=%d is smaller than the tree depth %d", K, tree->t.max_depth);
+        REQUIRE(topk > tree->t.max_rank, "topk=%d does not cover rank %d", topk, tree->t.max_rank);
+        launch_build_tree(tree->t, topk_idx, K, topk, root_tok, cache_len, B, node_tok, node_pos, anc_mask,
+                          (hipStream_t)stream);
+    });
+}
+
+// ---------------------------------------------------------------------------
+// a4 tree attention
+// ---------------------------------------------------------------------------
+size_t tree_attention_workspace_size(const medusa_tree* tree, int B, int nH, int D, int max_cache_len,
+                                     medusa_dtype dt) {
+    (void)dt;
+    if (!tree || B < 1 || nH < 1 || D < 1 || max_cache_len < 0) return 0;
+    return attn_workspace_bytes(B, nH, tree->t.N, D, max_cache_len);
+}
+
+medusa_status tree_attention_verify(const void* q, const void* k_tree, const void* v_tree, void* k_cache,
+                                    void* v_cache, const int32_t* cache_len, int max_cache_len,
+                                    const medusa_tree* tree, int B, int nH, int nKV, int D, int Lmax, float scale,
+                                    medusa_dtype dt, void* out, void* ws, size_t ws_bytes, void* stream) {
+    return guarded("tree_attention_verify", [&] {
+        REQUIRE(tree && q && k_tree && v_tree && k_cache && v_cache && cache_len && out && ws,
+                "null pointer argument");
+        REQUIRE(dt == MEDUSA_F32 || dt == MEDUSA_BF16, "bad dtype");
+        REQUIRE(B >= 1 && nH >= 1 && nKV >= 1 && nH % nKV == 0, "need nH %% nKV == 0 (nH=%d nKV=%d)", nH, nKV);
+        SUPPORT(D == 64 || D == 128, "D=%d not in {64, 128}", D);
+        REQUIRE(max_cache_len >= 0 && max_cache_len + tree->t.N <= Lmax,
+                "max_cache_len + N = %d exceeds Lmax = %d", max_cache_len + tree->t.N, Lmax);
+        const size_t need = tree_attention_workspace_size(tree, B, nH, D, max_cache_len, dt);
+        REQUIRE(ws_bytes >= need, "workspace too small: %zu < %zu", ws_bytes, need);
+        float* part_o;
+        float* part_ml;
+        attn_carve(B, nH, tree->t.N, D, max_cache_len, ws, &part_o, &part_ml);
+        launch_tree_attention(q, k_tree, v_tree, k_cache, v_cache, cache_len, max_cache_len, tree->t, B, nH, nKV, D,
+                              Lmax, scale, dt == MEDUSA_BF16, out, part_o, part_ml, (hipStream_t)stream);
+    });
+}
+
+// ---------------------------------------------------------------------------
+// a5 base greedy
+// ---------------------------------------------------------------------------
+size_t medusa_base_greedy_workspace_size(int R, int H, int V, medusa_dtype dt) {
+    (void)dt;
+    if (R < 1 || H < 1 || V < 1) return 0;
+    return greedy_workspace_bytes(R, H, V);
+}
+
+medusa_status medusa_base_greedy(const void* x, const void* lm_head, int R, int H, int V, float eps,
+                                 medusa_dtype dt, int32_t* greedy, float* logits, void* ws, size_t ws_bytes,
+                                 void* stream) {
+    return guarded("medusa_base_greedy", [&] {
+        REQUIRE(x && lm_head && greedy && ws, "null pointer argument");
+        REQUIRE(dt == MEDUSA_F32 || dt == MEDUSA_BF16, "bad dtype");
+        REQUIRE(R >= 1 && V >= 1 && H >= 1, "R, H, V must be positive");
+        SUPPORT(H % 8 == 0 && H <= 8192, "H=%d must be a multiple of 8 and <= 8192", H);
+        REQUIRE(eps >= 0.f, "eps must be >= 0");
+        const size_t need = medusa_base_greedy_workspace_size(R, H, V, dt);
+        REQUIRE(ws_bytes >= need, "workspace too small: %zu < %zu", ws_bytes, need);
+        launch_base_greedy(x, lm_head, R, H, V, eps, dt == MEDUSA_BF16, greedy, logits, ws, (hipStream_t)stream);
+    });
+}
+
+// ---------------------------------------------------------------------------
+// a6 + a7 accept and compaction
+// ---------------------------------------------------------------------------
+medusa_status medusa_accept(const medusa_tree* tree, const int32_t* node_tok, const int32_t* greedy, int B,
+                            int32_t* accept_len, int32_t* accept_nodes, int32_t* out_tokens,
+                            const int32_t* cache_len, int32_t* new_cache_len, void* k_cache, void* v_cache,
+                            int n_layers, int64_t layer_stride_elems, int nKV, int D, int Lmax, medusa_dtype dt,
+                            void* stream) {
+    return guarded("medusa_accept", [&] {
+        REQUIRE(tree && node_tok && greedy && accept_len && accept_nodes && out_tokens && cache_len &&
+                    new_cache_len,
+                "null pointer argument");
+        REQUIRE(B >= 1, "B must be >= 1");
+        REQUIRE((k_cache == nullptr) == (v_cache == nullptr), "k_cache and v_cache must both be given or both NULL");
+        if (k_cache) {
+            REQUIRE(dt == MEDUSA_F32 || dt == MEDUSA_BF16, "bad dtype");
+            REQUIRE(n_layers >= 1 && nKV >= 1 && D >= 1 && Lmax >= tree->t.N, "bad cache shape");
+            SUPPORT(D <= 128, "D=%d exceeds 128", D);
+            REQUIRE(layer_stride_elems >= (int64_t)B * nKV * Lmax * D || n_layers == 1,
+                    "layer stride smaller than one layer's cache");
+        }
+        launch_accept(tree->t, node_tok, greedy, B, accept_len, accept_nodes, out_tokens, cache_len, new_cache_len,
+                      k_cache, v_cache, n_layers, layer_stride_elems, nKV, D, Lmax, dt == MEDUSA_BF16,
+                      (hipStream_t)stream);
+    });
+}
+
+// ---------------------------------------------------------------------------
+// profiler
+// ---------------------------------------------------------------------------
+medusa_status medusa_profiler_enable(int on) {
+    g_prof_on = on != 0;
+    return MEDUSA_OK;
+}
+
+medusa_status medusa_profiler_reset(void) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    for (auto& r : g_prof_pending) {
+        hipEventSynchronize(r.b);
+        g_prof_pool.push_back(r.a);
+        g_prof_pool.push_back(r.b);
+    }
+    g_prof_pending.clear();
+    g_prof_stats.clear();
+    g_prof_snapshot.clear();
+    return MEDUSA_OK;
+}
+
+int medusa_profiler_collect(void) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    for (auto& r : g_prof_pending) {
+        hipEventSynchronize(r.b);
+        float ms = 0.f;
+        hipEventElapsedTime(&ms, r.a, r.b);
+        ProfStat& st = g_prof_stats[r.name];
+        st.calls += 1;
+        st.ms += ms;
+        g_prof_pool.push_back(r.a);
+        g_prof_pool.push_back(r.b);
+    }
+    g_prof_pending.clear();
+    g_prof_snapshot.assign(g_prof_stats.begin(), g_prof_stats.end());
+    return (int)g_prof_snapshot.size();
+}
+
+medusa_status medusa_profiler_stat(int i, char* name, size_t name_len, int64_t* calls, double* total_ms) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (i < 0 || i >= (int)g_prof_snapshot.size()) {
+        set_error("profiler index out of range");
+        return MEDUSA_EINVAL;
+    }
+    if (name && name_len) {
+        strncpy(name, g_prof_snapshot[i].first.c_str(), name_len - 1);
+        name[name_len - 1] = 0;
+    }
+    if (calls) *calls = g_prof_snapshot[i].second.calls;
+    if (total_ms) *total_ms = g_prof_snapshot[i].second.ms;
+    return MEDUSA_OK;
+}
+
+}  // extern "C"

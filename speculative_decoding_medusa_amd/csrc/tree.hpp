@@ -1,0 +1,24 @@
+// Device-resident candidate-tree topology.
+#pragma once
+#include <stdint.h>
+
+#include <vector>
+
+namespace medusa {
+
+struct TreeDev {
+    int N = 0;          // nodes (root included)
+    int W = 0;          // 64-bit mask words per row, ceil(N / 64)
+    int K = 0;          // heads the tree was declared for
+    int topk = 0;       // top-k the tree was declared for
+    int max_depth = 0;  // deepest node
+    int max_rank = 0;   // largest rank used
+    int* parent = nullptr;     // device [N]
+    int* depth = nullptr;      // device [N]
+    int* rank = nullptr;       // device [N]
+    uint64_t* mask = nullptr;  // device [N][W]
+    std::vector<int> h_parent, h_depth, h_rank;
+    std::vector<uint64_t> h_mask;
+};
+
+}  // namespace medusa

@@ -1,0 +1,157 @@
+"""Helpers shared by the tests and the golden-value script.
+
+* ``enforce_gaps``: make every integer decision of a workload robust: the
+  oracle's consecutive gaps among each head's top-(k+1) logits, and between
+  each node's best two base logits, must be at least ``gap``.  Violations are
+  removed by redrawing the lower-ranked row of W2 (or lm_head) from its own
+  stream (an "override"), which changes no other input.
+* ``widen_inputs``: the float64 view of generated inputs the oracle consumes.
+* device helpers (only used by GPU tests).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import medusa_inputs as mi
+import oracle
+
+GAP = 1e-2
+
+
+def widen_inputs(cfg, heads, att, root_tok):
+    dt = cfg.dtype
+    x = {k: oracle.widen(v, dt) for k, v in heads.items()}
+    for k in ("k_cache", "v_cache", "q", "k_tree", "v_tree"):
+        x[k] = oracle.widen(att[k], dt)
+    x["cache_len"] = np.asarray(att["cache_len"])
+    x["root_tok"] = np.asarray(root_tok)
+    return x
+
+
+def _oracle_z(cfg, heads):
+    dt = cfg.dtype
+    h = oracle.widen(heads["h"], dt)
+    z = np.empty((cfg.B, cfg.K, cfg.H))
+    for k in range(cfg.K):
+        W1 = oracle.widen(heads["W1"][k], dt)
+        b1 = oracle.widen(heads["b1"][k], dt)
+        z[:, k] = h + oracle.silu(h @ W1.T + b1)
+    return z
+
+
+def _row_logits(W, rows, z, dt):
+    return oracle.widen(W[rows], dt) @ z.T  # [rows][B]
+
+
+def _top(lg, n):
+    order = np.lexsort((np.arange(lg.shape[0]), -oracle.round_f32(lg)))
+    return order[:n]
+
+
+def enforce_heads_gap(cfg, heads, overrides, gap=GAP, max_iter=200):
+    """Redraw W2 rows until every (b, head) has top-(k+1) gaps >= gap."""
+    dt = cfg.dtype
+    z = _oracle_z(cfg, heads)
+    logits = np.empty((cfg.K, cfg.V, cfg.B))
+    for k in range(cfg.K):
+        for r0 in range(0, cfg.V, 8192):
+            logits[k, r0:r0 + 8192] = _row_logits(heads["W2"][k], slice(r0, r0 + 8192), z[:, k], dt)
+    for _ in range(max_iter):
+        bad = []
+        for k in range(cfg.K):
+            for b in range(cfg.B):
+                lg = logits[k, :, b]
+                top = _top(lg, cfg.topk + 1)
+                for j in range(cfg.topk):
+                    if lg[top[j]] - lg[top[j + 1]] < gap:
+                        bad.append((k, int(top[j + 1])))
+                        break
+        if not bad:
+            return logits, z
+        for k, row in sorted(set(bad)):
+            o = {"tensor": "W2", "head": k, "row": row, "serial": len(overrides)}
+            overrides.append(o)
+            mi.apply_overrides(cfg, heads, [o])
+            logits[k, row] = _row_logits(heads["W2"][k], [row], z[:, k], dt)[0]
+    raise RuntimeError("heads gap enforcement did not converge")
+
+
+def node_hidden(cfg, att):
+    """Oracle attention output per node, rounded like the boundary's output
+    type, flattened to [B*N][nH*D]."""
+    dt = cfg.dtype
+    parent, _ = cfg.tree.arrays()
+    w = {k: oracle.widen(att[k], dt) for k in ("q", "k_tree", "v_tree", "k_cache", "v_cache")}
+    scale = float(np.float32(1.0 / np.sqrt(cfg.D)))
+    o = oracle.tree_attention(w["q"], w["k_tree"], w["v_tree"], w["k_cache"], w["v_cache"], att["cache_len"],
+                              parent, scale)
+    if dt == "bf16":
+        o = oracle.round_bf16(o)
+    return o
+
+
+def enforce_greedy_gap(cfg, heads, o, overrides, eps=1e-6, gap=GAP, max_iter=200):
+    """Redraw lm_head rows until every node's best two base logits differ by >= gap.
+    ``o``: node hidden rows (any shape ending in H)."""
+    dt = cfg.dtype
+    rows = o.reshape(-1, cfg.H)
+    n = oracle.rmsnorm(rows, eps)
+    if dt == "bf16":
+        n = oracle.round_bf16(n)
+    logits = np.empty((cfg.V, n.shape[0]))
+    for r0 in range(0, cfg.V, 8192):
+        logits[r0:r0 + 8192] = oracle.widen(heads["lm_head"][r0:r0 + 8192], dt) @ n.T
+    for _ in range(max_iter):
+        bad = set()
+        for r in range(n.shape[0]):
+            top = _top(logits[:, r], 2)
+            if logits[top[0], r] - logits[top[1], r] < gap:
+                bad.add(int(top[1]))
+        if not bad:
+            return logits.T
+        for row in sorted(bad):
+            ov = {"tensor": "lm_head", "row": row, "serial": len(overrides)}
+            overrides.append(ov)
+            mi.apply_overrides(cfg, heads, [ov])
+            logits[row] = oracle.widen(heads["lm_head"][row], dt) @ n.T
+    raise RuntimeError("greedy gap enforcement did not converge")
+
+
+def make_workload(cfg, overrides=None, enforce=True):
+    """Generate every input of a workload; apply (or compute) gap overrides."""
+    heads = mi.gen_heads(cfg)
+    att = mi.gen_attention(cfg)
+    root = mi.gen_root_tokens(cfg)
+    if overrides is not None:
+        mi.apply_overrides(cfg, heads, overrides)
+        return heads, att, root, list(overrides)
+    ov = []
+    if enforce:
+        enforce_heads_gap(cfg, heads, ov)
+        o = node_hidden(cfg, att)
+        enforce_greedy_gap(cfg, heads, o, ov)
+    return heads, att, root, ov
+
+
+# ---------------------------------------------------------------------------
+# device helpers
+# ---------------------------------------------------------------------------
+
+def dev(arr, dtype_str=None):
+    import torch
+    a = np.ascontiguousarray(arr)
+    if a.dtype == np.uint16:
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(a)
+    return t.cuda()
+
+
+def host_f64(t):
+    import torch
+    return t.detach().float().cpu().numpy().astype(np.float64) if t.dtype == torch.bfloat16 else \
+        t.detach().cpu().numpy().astype(np.float64)
+
+
+def tol(dtype_str):
+    return 1e-4 if dtype_str == "f32" else 2e-2

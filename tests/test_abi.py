@@ -1,0 +1,107 @@
+"""The C-ABI library loads on a machine without a GPU, exports every function
+include/medusa.h declares, and rejects bad arguments on the host before any
+GPU work (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "medusa.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "return")))
+
+
+@pytest.fixture(scope="module")
+def M():
+    import speculative_decoding_medusa_amd as M
+    return M
+
+
+def test_header_declares_the_step_calls():
+    names = _declared()
+    for n in ["medusa_heads_forward", "medusa_build_tree", "tree_attention_verify", "medusa_accept",
+              "medusa_resid_silu", "medusa_vocab_topk", "medusa_base_greedy", "medusa_tree_create"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(M):
+    for n in _declared():
+        assert hasattr(M._lib, n), f"libmedusa.so does not export {n}"
+
+
+def test_binding_names_match_the_abi(M):
+    for n in ["medusa_resid_silu", "medusa_vocab_topk", "medusa_heads_forward", "medusa_build_tree",
+              "tree_attention_verify", "medusa_base_greedy", "medusa_accept"]:
+        assert callable(getattr(M, n))
+
+
+def _tree(M, parent, rank, N=None, K=5, topk=4):
+    p = np.asarray(parent, dtype=np.int32)
+    r = np.asarray(rank, dtype=np.int32)
+    h = ctypes.c_void_p()
+    st = M._lib.medusa_tree_create(p.ctypes.data, r.ctypes.data, len(p) if N is None else N, K, topk,
+                                   ctypes.byref(h))
+    return st, M._lib.medusa_last_error().decode()
+
+
+@pytest.mark.parametrize("parent,rank,kw,err", [
+    ([0, 0], [0, 0], {}, "parent[0]"),
+    ([-1, 1], [0, 0], {}, "parent"),
+    ([-1, 0, 0], [0, 1, 1], {}, "repeats rank"),
+    ([-1, 0], [0, 4], {}, "rank"),
+    ([-1, 0, 1, 2], [0, 0, 0, 0], {"K": 2}, "depth"),
+    ([-1], [0], {"N": 0}, "N must be"),
+])
+def test_tree_spec_errors(M, parent, rank, kw, err):
+    st, msg = _tree(M, parent, rank, **kw)
+    assert st == M.EINVAL and err in msg
+
+
+def test_tree_too_large_is_unsupported(M):
+    parent = [-1] + [0] * 300
+    st, msg = _tree(M, parent, list(range(301)), topk=16)
+    assert st in (M.EUNSUPPORTED, M.EINVAL)
+
+
+def test_heads_argument_errors(M):
+    L = M._lib
+    st = L.medusa_heads_forward(None, None, None, None, 1, 4096, 32000, 5, 4, M.BF16, None, None, None, None, 0, None)
+    assert st == M.EINVAL and "null" in L.medusa_last_error().decode()
+    d = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    st = L.medusa_vocab_topk(d, d, 1, 4096, 32000, 5, 0, M.BF16, None, d, d, d, 1 << 30, None)
+    assert st == M.EINVAL and "topk" in L.medusa_last_error().decode()
+    st = L.medusa_vocab_topk(d, d, 1, 4096, 32000, 5, 17, M.BF16, None, d, d, d, 1 << 30, None)
+    assert st == M.EUNSUPPORTED
+    st = L.medusa_vocab_topk(d, d, 9, 4096, 32000, 5, 4, M.BF16, None, d, d, d, 1 << 30, None)
+    assert st == M.EUNSUPPORTED
+    st = L.medusa_vocab_topk(d, d, 1, 4100, 32000, 5, 4, M.BF16, None, d, d, d, 1 << 30, None)
+    assert st == M.EUNSUPPORTED
+    st = L.medusa_vocab_topk(d, d, 1, 4096, 32000, 5, 4, M.BF16, None, d, d, d, 10, None)
+    assert st == M.EINVAL and "workspace" in L.medusa_last_error().decode()
+    st = L.medusa_heads_forward(d, d, None, d, 1, 4096, 32000, 5, 4, M.BF16, None, d, d, d, 1 << 30, None)
+    assert st == M.EINVAL and "both" in L.medusa_last_error().decode()
+    st = L.medusa_resid_silu(d, d, d, 1, 4096, 5, 7, d, None)
+    assert st == M.EINVAL
+
+
+def test_workspace_sizes_are_positive(M):
+    L = M._lib
+    assert L.medusa_heads_workspace_size(1, 4096, 32000, 5, 4, M.BF16) >= 5 * 4096 * 4
+    assert L.medusa_vocab_topk_workspace_size(8, 4096, 128256, 5, 4, M.BF16) > 0
+    assert L.medusa_base_greedy_workspace_size(64, 4096, 32000, M.BF16) >= 64 * 4096 * 4
+    assert L.medusa_heads_workspace_size(0, 4096, 32000, 5, 4, M.BF16) == 0
+
+
+def test_profiler_without_launches(M):
+    M.profiler_enable(True)
+    M.profiler_reset()
+    assert M.profiler_collect() == {}
+    M.profiler_enable(False)

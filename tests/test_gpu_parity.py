@@ -1,0 +1,271 @@
+"""GPU parity: every C-ABI call against the float64 oracle on the same seeded
+inputs.  Integers (top-k ids, tree tokens/positions/masks, greedy ids,
+accepted lengths/paths/tokens, compacted caches) must match exactly; floats
+within 1e-4 (float32 workloads) or 2e-2 (bf16 workloads, fp32 accumulation).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import medusa_inputs as mi
+import oracle
+from medusa_testlib import dev, enforce_greedy_gap, enforce_heads_gap, host_f64, make_workload, tol
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def M():
+    import speculative_decoding_medusa_amd as M
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return M
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def _cfg(name, dtype, B, H, V, K, topk, tree, nH=4, nKV=4, D=64, P=(128,), seed=100):
+    return mi.custom_config(name, dtype, B, H, V, K, topk, tree, nH, nKV, D, P, seed)
+
+
+HEAD_CASES = [
+    ("c1", lambda: mi.config(1)),
+    ("bf16_h1024_v5003_b1", lambda: _cfg("m1", "bf16", 1, 1024, 5003, 3, 4, mi.tiny_tree(), seed=101)),
+    ("bf16_h512_v3001_b3_k6", lambda: _cfg("m2", "bf16", 3, 512, 3001, 2, 6, mi.tiny_tree(), seed=102)),
+    ("f32_h256_v777_b2_k5", lambda: _cfg("m3", "f32", 2, 256, 777, 3, 5, mi.tiny_tree(), seed=103)),
+    ("bf16_h2048_v4000_b8", lambda: _cfg("m4", "bf16", 8, 2048, 4000, 2, 4, mi.tiny_tree(), seed=104)),
+]
+
+
+@pytest.mark.parametrize("name,mk", HEAD_CASES, ids=[c[0] for c in HEAD_CASES])
+def test_heads_parity(M, name, mk):
+    cfg = mk()
+    _say("heads", name)
+    heads = mi.gen_heads(cfg)
+    ov = []
+    logits_ref, z_ref = enforce_heads_gap(cfg, heads, ov)   # [K][V][B], [B][K][H]
+    logits_ref = np.transpose(logits_ref, (2, 0, 1))
+    idx_ref, val_ref = oracle.topk(logits_ref, cfg.topk)
+    h, W1, b1, W2 = (dev(heads[k]) for k in ("h", "W1", "b1", "W2"))
+    B, K, V, H, k = cfg.B, cfg.K, cfg.V, cfg.H, cfg.topk
+    z = torch.empty(B, K, H, device="cuda")
+    M.medusa_resid_silu(h, W1, b1, z)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(host_f64(z), z_ref, rtol=0, atol=tol(cfg.dtype))
+    logits = torch.empty(B, K, V, device="cuda")
+    ti = torch.empty(B, K, k, dtype=torch.int32, device="cuda")
+    tv = torch.empty(B, K, k, device="cuda")
+    M.medusa_heads_forward(h, W1, b1, W2, k, ti, tv, logits=logits)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(host_f64(logits), logits_ref, rtol=0, atol=tol(cfg.dtype))
+    assert np.array_equal(ti.cpu().numpy(), idx_ref)
+    np.testing.assert_allclose(host_f64(tv), val_ref, rtol=0, atol=tol(cfg.dtype))
+    # the two-call form (a1 then a2) gives the same bits as the fused call
+    ti2 = torch.empty_like(ti)
+    tv2 = torch.empty_like(tv)
+    M.medusa_vocab_topk(z, W2, k, ti2, tv2)
+    torch.cuda.synchronize()
+    assert torch.equal(ti, ti2) and torch.equal(tv, tv2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_zero_init_heads_reproduce_lm_head_bitwise(M, dtype):
+    # heads page sketch: W1 = 0, b1 = 0, W2 = copy of lm_head => every head's
+    # logits equal lm_head(h) exactly
+    _say("zero-init", dtype)
+    H, V, K = (256, 1000, 3) if dtype == "f32" else (4096, 32000, 5)
+    cfg = _cfg("zi", dtype, 1, H, V, K, 4, mi.tiny_tree(), seed=105)
+    lm = mi.normal((V, H), cfg.seed, mi.S_LM_HEAD, 0.02, dtype)
+    h = dev(mi.normal((1, H), cfg.seed, mi.S_H, 1.0, dtype))
+    lm_d = dev(lm)
+    W2 = lm_d.unsqueeze(0).repeat(K, 1, 1).contiguous()
+    W1 = torch.zeros(K, H, H, dtype=lm_d.dtype, device="cuda")
+    b1 = torch.zeros(K, H, dtype=lm_d.dtype, device="cuda")
+    lg = torch.empty(1, K, V, device="cuda")
+    ti = torch.empty(1, K, 4, dtype=torch.int32, device="cuda")
+    tv = torch.empty(1, K, 4, device="cuda")
+    M.medusa_heads_forward(h, W1, b1, W2, 4, ti, tv, logits=lg)
+    base = torch.empty(1, 1, V, device="cuda")
+    bi = torch.empty(1, 1, 4, dtype=torch.int32, device="cuda")
+    bv = torch.empty(1, 1, 4, device="cuda")
+    M.medusa_heads_forward(h, None, None, lm_d.unsqueeze(0).contiguous(), 4, bi, bv, logits=base)
+    torch.cuda.synchronize()
+    assert [bool(torch.equal(lg[:, k], base[:, 0])) for k in range(K)] == [True] * K
+    assert all(torch.equal(ti[:, k], bi[:, 0]) for k in range(K))
+
+
+@pytest.mark.parametrize("tree,K,topk,B", [(mi.tiny_tree(), 3, 3, 1), (mi.sparse_tree(64), 5, 4, 8),
+                                           (mi.dense_tree(256), 5, 3, 2), (mi.chain_tree(7), 7, 1, 3)])
+def test_build_tree_exact(M, tree, K, topk, B):
+    _say("build_tree", tree.name, B)
+    r = np.random.default_rng(7)
+    tk = np.stack([np.stack([r.choice(50000, topk, replace=False) for _ in range(K)]) for _ in range(B)]).astype(np.int32)
+    root = r.integers(0, 50000, B).astype(np.int32)
+    P = r.integers(0, 5000, B).astype(np.int32)
+    parent, rank = tree.arrays()
+    t = M.Tree(parent, rank, K, topk)
+    tok = torch.empty(B, tree.n, dtype=torch.int32, device="cuda")
+    pos = torch.empty_like(tok)
+    mask = torch.zeros(tree.n, t.W, dtype=torch.int64, device="cuda")
+    M.medusa_build_tree(t, dev(tk), dev(root), dev(P), tok, pos, anc_mask=mask)
+    torch.cuda.synchronize()
+    tok_ref, pos_ref, mask_ref = oracle.build_tree(parent, rank, tk, root, P)
+    assert np.array_equal(tok.cpu().numpy(), tok_ref)
+    assert np.array_equal(pos.cpu().numpy(), pos_ref)
+    m = mask.cpu().numpy().view(np.uint64)
+    bits = np.zeros((tree.n, tree.n), dtype=bool)
+    for i in range(tree.n):
+        for j in range(tree.n):
+            bits[i, j] = (int(m[i, j // 64]) >> (j % 64)) & 1
+    assert np.array_equal(bits, mask_ref)
+    assert np.array_equal(t.mask_host(), m)
+
+
+ATT_CASES = [
+    ("c1", lambda: mi.config(1)),
+    ("bf16_sparse64_h4_d128_p300", lambda: _cfg("a1", "bf16", 1, 512, 10, 5, 4, mi.sparse_tree(64), 4, 4, 128, (300,), 201)),
+    ("bf16_tiny_gqa_d64_b2", lambda: _cfg("a2", "bf16", 2, 256, 10, 3, 3, mi.tiny_tree(), 4, 2, 64, (100, 257), 202)),
+    ("f32_chain9_d128_p0", lambda: _cfg("a3", "f32", 1, 256, 10, 9, 1, mi.chain_tree(9), 2, 2, 128, (0,), 203)),
+    ("bf16_dense256_h2_d128_p1000", lambda: _cfg("a4", "bf16", 1, 256, 10, 5, 3, mi.dense_tree(256), 2, 2, 128, (1000,), 204)),
+    ("bf16_sparse64_b3_ragged", lambda: _cfg("a5", "bf16", 3, 256, 10, 5, 4, mi.sparse_tree(64), 2, 1, 128, (1, 777, 2049), 205)),
+]
+
+
+@pytest.mark.parametrize("name,mk", ATT_CASES, ids=[c[0] for c in ATT_CASES])
+def test_tree_attention_parity(M, name, mk):
+    cfg = mk()
+    _say("attention", name)
+    att = mi.gen_attention(cfg)
+    parent, rank = cfg.tree.arrays()
+    t = M.Tree(parent, rank, cfg.K, cfg.topk)
+    q, kt, vt, kc, vc = (dev(att[k]) for k in ("q", "k_tree", "v_tree", "k_cache", "v_cache"))
+    kc0, vc0 = kc.clone(), vc.clone()
+    cl = dev(att["cache_len"])
+    out = torch.empty_like(q)
+    M.tree_attention_verify(q, kt, vt, kc, vc, cl, max(cfg.P), t, out)
+    torch.cuda.synchronize()
+    w = {k: oracle.widen(att[k], cfg.dtype) for k in ("q", "k_tree", "v_tree", "k_cache", "v_cache")}
+    scale = float(np.float32(1.0 / np.sqrt(cfg.D)))
+    ref = oracle.tree_attention(w["q"], w["k_tree"], w["v_tree"], w["k_cache"], w["v_cache"], att["cache_len"],
+                                parent, scale)
+    np.testing.assert_allclose(host_f64(out), ref, rtol=0, atol=tol(cfg.dtype))
+    # the tree's keys/values now sit at slots P..P+N-1; every other slot is untouched
+    kc_ref = kc0.clone()
+    vc_ref = vc0.clone()
+    for b, P in enumerate(cfg.P):
+        kc_ref[b, :, P:P + cfg.N] = kt[b].transpose(0, 1)
+        vc_ref[b, :, P:P + cfg.N] = vt[b].transpose(0, 1)
+    assert torch.equal(kc, kc_ref) and torch.equal(vc, vc_ref)
+
+
+GREEDY_CASES = [
+    ("f32_r9_v1000", "f32", 9, 256, 1000),
+    ("bf16_r64_h1024_v5000", "bf16", 64, 1024, 5000),
+    ("bf16_r13_h4096_v3001", "bf16", 13, 4096, 3001),
+]
+
+
+@pytest.mark.parametrize("name,dtype,R,H,V", GREEDY_CASES, ids=[c[0] for c in GREEDY_CASES])
+def test_base_greedy_parity(M, name, dtype, R, H, V):
+    _say("base_greedy", name)
+    cfg = _cfg("g", dtype, 1, H, V, 1, 1, mi.tiny_tree(), seed=300 + R)
+    heads = {"lm_head": mi.normal((V, H), cfg.seed, mi.S_LM_HEAD, 0.02, dtype)}
+    x = mi.normal((R, H), cfg.seed, mi.S_TEST, 1.0, dtype)
+    xw = oracle.widen(x, dtype)
+    ov = []
+    enforce_greedy_gap(cfg, heads, xw, ov)
+    g_ref, lg_ref = oracle.base_greedy(xw, oracle.widen(heads["lm_head"], dtype), 1e-6, dtype == "bf16")
+    g = torch.empty(R, dtype=torch.int32, device="cuda")
+    lg = torch.empty(R, V, device="cuda")
+    M.medusa_base_greedy(dev(x), dev(heads["lm_head"]), g, eps=1e-6, logits=lg)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(host_f64(lg), lg_ref, rtol=0, atol=tol(dtype))
+    assert np.array_equal(g.cpu().numpy(), g_ref)
+
+
+def _planted_greedy(tree, tk, tok, truth):
+    """greedy[i] = head (d+1)'s token of the true rank at depth d+1 (or a
+    token outside the top-k)."""
+    parent, _ = tree.arrays()
+    depth = np.asarray(tree.depth)
+    B, N = tok.shape
+    K, k = tk.shape[1], tk.shape[2]
+    g = np.zeros((B, N), dtype=np.int32)
+    for b in range(B):
+        for i in range(N):
+            d = depth[i]
+            if d < K:
+                R = truth[b, d]
+                g[b, i] = tk[b, d, R] if R < k else 999999
+            else:
+                g[b, i] = 123456 + i
+    return g
+
+
+@pytest.mark.parametrize("tree,K,topk", [(mi.tiny_tree(), 2, 3), (mi.sparse_tree(64), 5, 4),
+                                         (mi.dense_tree(256), 5, 3), (mi.chain_tree(5), 5, 1)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_accept_and_compaction_exact(M, tree, K, topk, dtype):
+    _say("accept", tree.name, dtype)
+    B, nKV, D, layers = 8, 2, 64, 3
+    parent, rank = tree.arrays()
+    r = np.random.default_rng(11)
+    tk = np.stack([np.stack([r.choice(30000, topk, replace=False) for _ in range(K)]) for _ in range(B)]).astype(np.int32)
+    root = r.integers(0, 30000, B).astype(np.int32)
+    P = r.integers(0, 300, B).astype(np.int32)
+    tok, _, _ = oracle.build_tree(parent, rank, tk, root, P)
+    pr = np.array([mi.rank_prior(0.8, j) for j in range(topk)] + [0.0])
+    pr[-1] = 1 - pr[:-1].sum()
+    truth = r.choice(topk + 1, size=(B, K), p=pr)
+    truth[0] = 0  # sequence 0 accepts its deepest rank-0 chain
+    g = _planted_greedy(tree, tk, tok, truth)
+    Lmax = int(P.max()) + tree.n + 5
+    cache_k = mi.normal((layers, B, nKV, Lmax, D), 50, mi.S_TEST + 1, 1.0, dtype)
+    cache_v = mi.normal((layers, B, nKV, Lmax, D), 50, mi.S_TEST + 2, 1.0, dtype)
+    t = M.Tree(parent, rank, K, topk)
+    kc, vc = dev(cache_k), dev(cache_v)
+    Dm = t.max_depth
+    al = torch.empty(B, dtype=torch.int32, device="cuda")
+    an = torch.empty(B, Dm + 1, dtype=torch.int32, device="cuda")
+    ot = torch.empty(B, Dm + 1, dtype=torch.int32, device="cuda")
+    ncl = torch.empty(B, dtype=torch.int32, device="cuda")
+    M.medusa_accept(t, dev(tok), dev(g), al, an, ot, dev(P), ncl, k_cache=kc, v_cache=vc)
+    torch.cuda.synchronize()
+    kc_h = kc.cpu()
+    vc_h = vc.cpu()
+    ck = torch.from_numpy(cache_k.view(np.int16)).view(torch.bfloat16) if dtype == "bf16" else torch.from_numpy(cache_k)
+    cv = torch.from_numpy(cache_v.view(np.int16)).view(torch.bfloat16) if dtype == "bf16" else torch.from_numpy(cache_v)
+    for b in range(B):
+        L, path, toks = oracle.accept(parent, tok[b], g[b])
+        assert al[b].item() == L
+        assert an[b].cpu().numpy().tolist() == path.tolist() + [-1] * (Dm - L)
+        assert ot[b].cpu().numpy().tolist() == toks.tolist() + [-1] * (Dm - L)
+        assert ncl[b].item() == P[b] + L + 1
+        for src, got in ((ck, kc_h), (cv, vc_h)):
+            ref, _ = oracle.compact_kv(src[:, b].float().numpy(), int(P[b]), path)
+            assert np.array_equal(got[:, b].float().numpy(), ref)
+    assert al[0].item() == Dm if tree.name != "tiny_2x3" else al[0].item() == 2
+
+
+def test_accept_without_caches(M):
+    tree = mi.sparse_tree(64)
+    parent, rank = tree.arrays()
+    _say("accept-no-cache")
+    t = M.Tree(parent, rank, 5, 4)
+    tk = np.arange(5 * 4, dtype=np.int32).reshape(1, 5, 4) + 100
+    tok, _, _ = oracle.build_tree(parent, rank, tk, np.array([1]), np.array([10]))
+    g = _planted_greedy(tree, tk, tok, np.array([[1, 0, 2, 0, 0]]))
+    al = torch.empty(1, dtype=torch.int32, device="cuda")
+    an = torch.empty(1, 6, dtype=torch.int32, device="cuda")
+    ot = torch.empty(1, 6, dtype=torch.int32, device="cuda")
+    ncl = torch.empty(1, dtype=torch.int32, device="cuda")
+    M.medusa_accept(t, dev(tok), dev(g), al, an, ot, dev(np.array([10], np.int32)), ncl)
+    torch.cuda.synchronize()
+    L, path, toks = oracle.accept(parent, tok[0], g[0])
+    assert al.item() == L and ncl.item() == 10 + L + 1
+    assert an[0, :L + 1].cpu().numpy().tolist() == path.tolist()
+    assert ot[0, :L + 1].cpu().numpy().tolist() == toks.tolist()
