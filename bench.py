@@ -143,30 +143,21 @@ def main():
 
     st = {
         "heads_resid_silu": stage("resid_silu_gemv"),
-        "heads_vocab_topk": stage("vocab_proj_topk", "topk_merge") * 1.0,
+        "heads_vocab_topk": stage("vocab_proj_topk", "topk_merge"),
         "build_tree": stage("build_tree"),
-        "tree_attention": stage("tree_attn_split", "tree_attn_combine", "tree_attn_mfma"),
+        "tree_attention": stage("tree_attn_split", "tree_attn_combine"),
         "base_greedy": stage("rmsnorm_rows", "lm_head_argmax", "argmax_merge") +
-        (kern_us.get("vocab_proj_topk", 0.0) * 0),
+        prof.get("lm_head_gemv", (0, 0.0))[1] * 1e3 / max(args.steps, 1) +
+        prof.get("lm_head_gemv_merge", (0, 0.0))[1] * 1e3 / max(args.steps, 1),
         "accept_compact": stage("accept_compact"),
     }
-    # the base-greedy stage also launches vocab_proj_topk/topk_merge when it
-    # runs on the GEMV path; split those launches out by their counts
-    n_vt = prof.get("vocab_proj_topk", (0, 0.0))[0] / max(args.steps, 1)
-    if n_vt > 1:
-        per = prof["vocab_proj_topk"][1] / prof["vocab_proj_topk"][0] * 1e3
-        per_m = prof["topk_merge"][1] / prof["topk_merge"][0] * 1e3
-        st["heads_vocab_topk"] = per + per_m
-        st["base_greedy"] += (n_vt - 1) * (per + per_m)
 
     # roofline of the dominant kernel: the vocabulary projection of the heads
     itemsize = 2 if dt_str == "bf16" else 4
     w2_bytes = K * V * H * itemsize
     z_bytes = B * K * H * 4
     algo_bytes = w2_bytes + z_bytes + B * K * topk * 8
-    vt_calls, vt_ms = prof["vocab_proj_topk"]
-    # one launch of the heads' projection per step (greedy launches, if any, read lm_head instead)
-    vt_us = kern_us["vocab_proj_topk"] if n_vt <= 1 else per
+    vt_us = kern_us["vocab_proj_topk"]
     achieved = algo_bytes / (vt_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "vocab_proj_topk",

@@ -31,7 +31,7 @@ void launch_tree_attention(const void* q, const void* k_tree, const void* v_tree
                            hipStream_t s);
 size_t attn_workspace_bytes(int B, int nH, int N, int D, int max_cache_len);
 void attn_carve(int B, int nH, int N, int D, int max_cache_len, void* ws, float** part_o, float** part_ml);
-size_t greedy_workspace_bytes(int R, int H, int V);
+size_t greedy_workspace_bytes(int R, int H, int V, bool bf16);
 void launch_base_greedy(const void* x, const void* lm_head, int R, int H, int V, float eps, bool bf16,
                         int32_t* greedy, float* logits, void* ws, hipStream_t s);
 void launch_accept(const TreeDev& t, const int32_t* node_tok, const int32_t* greedy, int B, int32_t* accept_len,
@@ -379,9 +379,8 @@ medusa_status tree_attention_verify(const void* q, const void* k_tree, const voi
 // a5 base greedy
 // ---------------------------------------------------------------------------
 size_t medusa_base_greedy_workspace_size(int R, int H, int V, medusa_dtype dt) {
-    (void)dt;
     if (R < 1 || H < 1 || V < 1) return 0;
-    return greedy_workspace_bytes(R, H, V);
+    return greedy_workspace_bytes(R, H, V, dt == MEDUSA_BF16);
 }
 
 medusa_status medusa_base_greedy(const void* x, const void* lm_head, int R, int H, int V, float eps,

@@ -262,21 +262,27 @@ void launch_resid_silu(const void* h, const void* w1, const void* b1, int B, int
                                         z, nullptr, nullptr, 0, s, "resid_silu_gemv");
 }
 
-void launch_vocab_topk(const float* z, const void* w2, int B, int H, int V, int K, int topk, bool bf16,
-                       float* logits, int32_t* topk_idx, float* topk_val, float* cv, int* ci,
-                       hipStream_t s) {
+void launch_vocab_topk_named(const float* z, const void* w2, int B, int H, int V, int K, int topk, bool bf16,
+                             float* logits, int32_t* topk_idx, float* topk_val, float* cv, int* ci, hipStream_t s,
+                             const char* gemv_name, const char* merge_name) {
     const int rpw = rows_per_wg_for(V, K, 1024);
     const int G = (V + rpw - 1) / rpw;
     const int PER = bf16 ? 8 : 4;
     const int NB = pick_nb(B), CPL = pick_cpl(H / PER);
     if (bf16)
         launch_gemv_nb<bf16_t, EPI_TOPK>(NB, CPL, z, (const bf16_t*)w2, nullptr, B, H, V, K, rpw, G, logits,
-                                         cv, ci, topk, s, "vocab_proj_topk");
+                                         cv, ci, topk, s, gemv_name);
     else
         launch_gemv_nb<float, EPI_TOPK>(NB, CPL, z, (const float*)w2, nullptr, B, H, V, K, rpw, G, logits, cv,
-                                        ci, topk, s, "vocab_proj_topk");
-    MEDUSA_LAUNCH("topk_merge", topk_merge_kernel, dim3(B * K), dim3(64), 0, s, cv, ci, G * topk, topk,
+                                        ci, topk, s, gemv_name);
+    MEDUSA_LAUNCH(merge_name, topk_merge_kernel, dim3(B * K), dim3(64), 0, s, cv, ci, G * topk, topk,
                   topk_idx, topk_val);
+}
+
+void launch_vocab_topk(const float* z, const void* w2, int B, int H, int V, int K, int topk, bool bf16,
+                       float* logits, int32_t* topk_idx, float* topk_val, float* cv, int* ci, hipStream_t s) {
+    launch_vocab_topk_named(z, w2, B, H, V, K, topk, bf16, logits, topk_idx, topk_val, cv, ci, s,
+                            "vocab_proj_topk", "topk_merge");
 }
 
 }  // namespace medusa

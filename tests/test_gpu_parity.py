@@ -166,6 +166,9 @@ GREEDY_CASES = [
     ("f32_r9_v1000", "f32", 9, 256, 1000),
     ("bf16_r64_h1024_v5000", "bf16", 64, 1024, 5000),
     ("bf16_r13_h4096_v3001", "bf16", 13, 4096, 3001),
+    ("bf16_r100_h1024_v2000", "bf16", 100, 1024, 2000),     # 128-node MFMA tiles
+    ("bf16_r200_h512_v1537", "bf16", 200, 512, 1537),       # 256-node MFMA tiles, 2nd tile ragged
+    ("bf16_r5_h520_v999_gemv", "bf16", 5, 520, 999),        # H not a multiple of the MFMA k-chunk
 ]
 
 
