@@ -145,7 +145,7 @@ def main():
         "heads_resid_silu": stage("resid_silu_gemv"),
         "heads_vocab_topk": stage("vocab_proj_topk", "topk_merge"),
         "build_tree": stage("build_tree"),
-        "tree_attention": stage("tree_attn_split", "tree_attn_combine"),
+        "tree_attention": stage("tree_attn_split", "tree_attn_mfma", "tree_attn_combine"),
         "base_greedy": stage("rmsnorm_rows", "lm_head_argmax", "argmax_merge") +
         prof.get("lm_head_gemv", (0, 0.0))[1] * 1e3 / max(args.steps, 1) +
         prof.get("lm_head_gemv_merge", (0, 0.0))[1] * 1e3 / max(args.steps, 1),

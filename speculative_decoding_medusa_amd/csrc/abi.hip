@@ -29,8 +29,9 @@ void launch_tree_attention(const void* q, const void* k_tree, const void* v_tree
                            const int32_t* cache_len, int max_cache_len, const TreeDev& t, int B, int nH, int nKV,
                            int D, int Lmax, float scale, bool bf16, void* out, float* part_o, float* part_ml,
                            hipStream_t s);
-size_t attn_workspace_bytes(int B, int nH, int N, int D, int max_cache_len);
-void attn_carve(int B, int nH, int N, int D, int max_cache_len, void* ws, float** part_o, float** part_ml);
+size_t attn_workspace_bytes(int B, int nH, int N, int D, int max_cache_len, bool bf16);
+void attn_carve(int B, int nH, int N, int D, int max_cache_len, bool bf16, void* ws, float** part_o,
+                float** part_ml);
 size_t greedy_workspace_bytes(int R, int H, int V, bool bf16);
 void launch_base_greedy(const void* x, const void* lm_head, int R, int H, int V, float eps, bool bf16,
                         int32_t* greedy, float* logits, void* ws, hipStream_t s);
@@ -348,9 +349,8 @@ medusa_status medusa_build_tree(const medusa_tree* tree, const int32_t* topk_idx
 // ---------------------------------------------------------------------------
 size_t tree_attention_workspace_size(const medusa_tree* tree, int B, int nH, int D, int max_cache_len,
                                      medusa_dtype dt) {
-    (void)dt;
     if (!tree || B < 1 || nH < 1 || D < 1 || max_cache_len < 0) return 0;
-    return attn_workspace_bytes(B, nH, tree->t.N, D, max_cache_len);
+    return attn_workspace_bytes(B, nH, tree->t.N, D, max_cache_len, dt == MEDUSA_BF16);
 }
 
 medusa_status tree_attention_verify(const void* q, const void* k_tree, const void* v_tree, void* k_cache,
@@ -369,7 +369,7 @@ medusa_status tree_attention_verify(const void* q, const void* k_tree, const voi
         REQUIRE(ws_bytes >= need, "workspace too small: %zu < %zu", ws_bytes, need);
         float* part_o;
         float* part_ml;
-        attn_carve(B, nH, tree->t.N, D, max_cache_len, ws, &part_o, &part_ml);
+        attn_carve(B, nH, tree->t.N, D, max_cache_len, dt == MEDUSA_BF16, ws, &part_o, &part_ml);
         launch_tree_attention(q, k_tree, v_tree, k_cache, v_cache, cache_len, max_cache_len, tree->t, B, nH, nKV, D,
                               Lmax, scale, dt == MEDUSA_BF16, out, part_o, part_ml, (hipStream_t)stream);
     });

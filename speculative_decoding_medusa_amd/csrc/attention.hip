@@ -166,19 +166,242 @@ __global__ __launch_bounds__(D) void tree_attn_combine_kernel(const float* __res
     Elem<T>::store(out, (((size_t)b * N + i) * nH + h) * D + c, acc / L);
 }
 
-int attn_splits(int B, int nH, int N, int max_total) {
-    const int qblocks = (N + ATT_QB - 1) / ATT_QB;
-    const int base = B * nH * qblocks;
-    int S = (1024 + base - 1) / base;
-    const int max_s = (max_total + ATT_TK - 1) / ATT_TK;
-    if (S > max_s) S = max_s;
-    if (S < 1) S = 1;
-    return S;
+// ---------------------------------------------------------------------------
+// bf16 MFMA variant.  The same split-KV decomposition, with the contractions
+// on v_mfma_f32_16x16x32_bf16 in transposed form so that no register data has
+// to move between lanes:
+//   S^T[key][q] = K . Q^T   (A = K tile rows from LDS, B = the wave's Q rows
+//                            held in registers for the whole kernel);
+//   the output layout gives each lane 4 consecutive keys of one query per
+//   16-key block, exactly the 8 values the next product needs as its B
+//   operand, so P^T never leaves the lane;
+//   O^T[d][q] += V^T . P^T (A = V^T from an LDS tile stored transposed,
+//                            [d][key]; the contraction runs over the keys in a
+//                            fixed permuted order, the same for both operands).
+// The online-softmax state of query q lives in the 4 lanes that hold column q.
+// Tiles of 64 keys are staged in LDS by the whole workgroup, the next tile
+// prefetched into registers while the current one is consumed.
+// ---------------------------------------------------------------------------
+constexpr int MF_TK = 64;
+
+template <int D, int WAVES, int QBW>
+__global__ __launch_bounds__(WAVES * 64) void tree_attn_mfma_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_tree, const bf16_t* __restrict__ v_tree,
+    bf16_t* __restrict__ k_cache, bf16_t* __restrict__ v_cache, const int32_t* __restrict__ cache_len,
+    const uint64_t* __restrict__ mask, int N, int W, int nH, int nKV, int Lmax, int max_cache_len,
+    float scale_log2, int KPS, float* __restrict__ part_o, float* __restrict__ part_ml) {
+    constexpr int NT = WAVES * 64;
+    constexpr int TK = MF_TK;
+    constexpr int KB = TK / 16;     // 16-key blocks per tile
+    constexpr int DK = D / 32;      // k-steps of S over the head dimension
+    constexpr int DB = D / 16;      // 16-row blocks of O^T
+    constexpr int CH = TK * D / 8;  // 16-byte chunks per tile per tensor
+    constexpr int PT = CH / NT;     // chunks per thread
+    constexpr int DC = D / 8;       // chunks per key row
+    __shared__ __attribute__((aligned(16))) bf16_t Ks[TK][D + 8];
+    __shared__ __attribute__((aligned(16))) bf16_t Vt[D][TK + 8];
+
+    const int bh = blockIdx.x;
+    const int b = bh / nH, h = bh - b * nH;
+    const int grp = nH / nKV;
+    const int kvh = h / grp;
+    const int S = gridDim.y;
+    const int s = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, lk = lane >> 4;
+    const int P = max(0, min(cache_len[b], max_cache_len));
+    const int total = P + N;
+
+    if (s == 0 && h % grp == 0) {
+        for (int e = tid; e < N * DC; e += NT) {
+            const int t = e / DC, c = e - t * DC;
+            const size_t src = (((size_t)b * N + t) * nKV + kvh) * D + c * 8;
+            const size_t dst = (((size_t)b * nKV + kvh) * Lmax + P + t) * D + c * 8;
+            *(u32x4*)(k_cache + dst) = *(const u32x4*)(k_tree + src);
+            *(u32x4*)(v_cache + dst) = *(const u32x4*)(v_tree + src);
+        }
+    }
+
+    // this lane's queries (column lr of each of its 16-query blocks)
+    u32x4 qf[QBW][DK];
+    uint64_t mrow[QBW][4];
+    int qidx[QBW];
+#pragma unroll
+    for (int qb = 0; qb < QBW; ++qb) {
+        const int qi = (wave * QBW + qb) * 16 + lr;
+        qidx[qb] = qi;
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks)
+            qf[qb][ks] = qi < N ? *(const u32x4*)(q + (((size_t)b * N + qi) * nH + h) * D + ks * 32 + lk * 8)
+                                : (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) mrow[qb][w] = (qi < N && w < W) ? mask[(size_t)qi * W + w] : 0ull;
+    }
+
+    f32x4 o[QBW][DB];
+    float m[QBW], l[QBW];
+#pragma unroll
+    for (int qb = 0; qb < QBW; ++qb) {
+        m[qb] = -INFINITY;
+        l[qb] = 0.f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[qb][db] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+
+    const int k_begin = s * KPS;
+    const int k_end = min(total, k_begin + KPS);
+    const size_t cache_row0 = ((size_t)b * nKV + kvh) * Lmax;
+
+    u32x4 kreg[PT], vreg[PT];
+    auto load_tile = [&](int t0) {
+#pragma unroll
+        for (int e = 0; e < PT; ++e) {
+            const int c = tid + e * NT;
+            const int key = c / DC, dc = c - key * DC;
+            const int j = t0 + key;
+            if (j < k_end) {
+                const size_t off = j < P ? (cache_row0 + j) * D + dc * 8
+                                         : (((size_t)b * N + (j - P)) * nKV + kvh) * D + dc * 8;
+                kreg[e] = *(const u32x4*)((j < P ? k_cache : k_tree) + off);
+                vreg[e] = *(const u32x4*)((j < P ? v_cache : v_tree) + off);
+            } else {
+                kreg[e] = (u32x4){0u, 0u, 0u, 0u};
+                vreg[e] = (u32x4){0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int e = 0; e < PT; ++e) {
+            const int c = tid + e * NT;
+            const int key = c / DC, dc = c - key * DC;
+            *(u32x4*)(&Ks[key][dc * 8]) = kreg[e];
+            const uint32_t w4[4] = {vreg[e].x, vreg[e].y, vreg[e].z, vreg[e].w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                Vt[dc * 8 + 2 * u][key] = (bf16_t)(w4[u] & 0xFFFFu);
+                Vt[dc * 8 + 2 * u + 1][key] = (bf16_t)(w4[u] >> 16);
+            }
+        }
+    };
+
+    if (k_begin < k_end) load_tile(k_begin);
+    for (int t0 = k_begin; t0 < k_end; t0 += TK) {
+        __syncthreads();
+        store_tile();
+        __syncthreads();
+        if (t0 + TK < k_end) load_tile(t0 + TK);
+#pragma unroll
+        for (int qb = 0; qb < QBW; ++qb) {
+            f32x4 st[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                st[kb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < DK; ++ks) {
+                    const u32x4 a = *(const u32x4*)(&Ks[kb * 16 + lr][ks * 32 + lk * 8]);
+                    st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                                     __builtin_bit_cast(bf16x8, qf[qb][ks]), st[kb],
+                                                                     0, 0, 0);
+                }
+            }
+            // scale, mask (prefix: visible; tree key t: ancestor bit), tile max
+            const int qi = qidx[qb];
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = t0 + kb * 16 + lk * 4 + r;
+                    bool vis = j < k_end && qi < N;
+                    if (vis && j >= P) {
+                        const int t = j - P;
+                        const int w = t >> 6;
+                        const uint64_t word = w == 0 ? mrow[qb][0] : w == 1 ? mrow[qb][1] : w == 2 ? mrow[qb][2]
+                                                                                              : mrow[qb][3];
+                        vis = (word >> (t & 63)) & 1ull;
+                    }
+                    const float x = vis ? st[kb][r] * scale_log2 : -INFINITY;
+                    st[kb][r] = x;
+                    tmax = fmaxf(tmax, x);
+                }
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+            const float m_new = fmaxf(m[qb], tmax);
+            const bool live = m_new != -INFINITY;
+            const float alpha = live ? exp2f(m[qb] - m_new) : 1.f;
+            float psum = 0.f;
+            uint32_t pk[KB][2];  // bf16 pairs of P^T
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                float p4[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    p4[r] = live ? exp2f(st[kb][r] - m_new) : 0.f;
+                    psum += p4[r];
+                }
+                pk[kb][0] = (uint32_t)f32_to_bf16(p4[0]) | ((uint32_t)f32_to_bf16(p4[1]) << 16);
+                pk[kb][1] = (uint32_t)f32_to_bf16(p4[2]) | ((uint32_t)f32_to_bf16(p4[3]) << 16);
+            }
+            psum += __shfl_xor(psum, 16, 64);
+            psum += __shfl_xor(psum, 32, 64);
+            l[qb] = l[qb] * alpha + psum;
+            m[qb] = m_new;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
+#pragma unroll
+            for (int k2 = 0; k2 < TK / 32; ++k2) {
+                const u32x4 bp = (u32x4){pk[2 * k2][0], pk[2 * k2][1], pk[2 * k2 + 1][0], pk[2 * k2 + 1][1]};
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const uint2 lo = *(const uint2*)(&Vt[db * 16 + lr][k2 * 32 + lk * 4]);
+                    const uint2 hi = *(const uint2*)(&Vt[db * 16 + lr][k2 * 32 + 16 + lk * 4]);
+                    const u32x4 av = (u32x4){lo.x, lo.y, hi.x, hi.y};
+                    o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                                        __builtin_bit_cast(bf16x8, bp), o[qb][db], 0,
+                                                                        0, 0);
+                }
+            }
+        }
+    }
+
+    // O^T block db: lane holds d = db*16 + 4*lk + r of query column lr
+#pragma unroll
+    for (int qb = 0; qb < QBW; ++qb) {
+        const int qi = qidx[qb];
+        if (qi < N) {
+            const size_t pr = ((size_t)bh * S + s) * N + qi;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                *(f32x4*)(part_o + pr * D + db * 16 + lk * 4) = o[qb][db];
+            if (lk == 0) { part_ml[pr * 2] = m[qb]; part_ml[pr * 2 + 1] = l[qb]; }
+        }
+    }
 }
 
-int attn_keys_per_split(int S, int max_total) {
+struct AttnPlan {
+    bool mfma;
+    int S;    // splits of the key range
+    int KPS;  // keys per split
+};
+
+static AttnPlan attn_plan(bool bf16, int B, int nH, int N, int max_total) {
+    AttnPlan p;
+    p.mfma = bf16 && N <= MEDUSA_MAX_NODES_DEV;
+    const int unit = p.mfma ? 32 : ATT_TK;
+    const int qblocks = p.mfma ? 1 : (N + ATT_QB - 1) / ATT_QB;
+    const int base = B * nH * qblocks;
+    const int target = p.mfma ? 512 : 1024;
+    int S = (target + base - 1) / base;
+    const int max_s = (max_total + unit - 1) / unit;
+    if (S > max_s) S = max_s;
+    if (S < 1) S = 1;
     int kps = (max_total + S - 1) / S;
-    return ((kps + ATT_TK - 1) / ATT_TK) * ATT_TK;
+    kps = ((kps + unit - 1) / unit) * unit;
+    p.KPS = kps;
+    p.S = (max_total + kps - 1) / kps;
+    return p;
 }
 
 void launch_tree_attention(const void* q, const void* k_tree, const void* v_tree, void* k_cache, void* v_cache,
@@ -186,16 +409,36 @@ void launch_tree_attention(const void* q, const void* k_tree, const void* v_tree
                            int nKV, int D, int Lmax, float scale, bool bf16, void* out, float* part_o,
                            float* part_ml, hipStream_t s) {
     const int N = t.N;
-    const int max_total = max_cache_len + N;
-    const int S = attn_splits(B, nH, N, max_total);
-    const int KPS = attn_keys_per_split(S, max_total);
-    const dim3 grid(B * nH, S, (N + ATT_QB - 1) / ATT_QB);
+    const AttnPlan pl = attn_plan(bf16, B, nH, N, max_cache_len + N);
     const float scale_log2 = scale * 1.4426950408889634f;
+    if (pl.mfma) {
+        const bf16_t *Q = (const bf16_t*)q, *KT = (const bf16_t*)k_tree, *VT = (const bf16_t*)v_tree;
+        bf16_t *KC = (bf16_t*)k_cache, *VC = (bf16_t*)v_cache;
+#define MEDUSA_MF(DD, WV, QB)                                                                                   \
+    MEDUSA_LAUNCH("tree_attn_mfma", (tree_attn_mfma_kernel<DD, WV, QB>), dim3(B * nH, pl.S), dim3(WV * 64), 0, s, \
+                  Q, KT, VT, KC, VC, cache_len, t.mask, N, t.W, nH, nKV, Lmax, max_cache_len, scale_log2, pl.KPS,   \
+                  part_o, part_ml)
+        if (D == 64) {
+            if (N <= 64) MEDUSA_MF(64, 4, 1); else if (N <= 128) MEDUSA_MF(64, 4, 2); else MEDUSA_MF(64, 8, 2);
+        } else {
+            if (N <= 64) MEDUSA_MF(128, 4, 1); else if (N <= 128) MEDUSA_MF(128, 4, 2); else MEDUSA_MF(128, 8, 2);
+        }
+#undef MEDUSA_MF
+        if (D == 64)
+            MEDUSA_LAUNCH("tree_attn_combine", (tree_attn_combine_kernel<bf16_t, 64>), dim3(N, B * nH), dim3(64), 0,
+                          s, part_o, part_ml, pl.S, N, nH, (bf16_t*)out);
+        else
+            MEDUSA_LAUNCH("tree_attn_combine", (tree_attn_combine_kernel<bf16_t, 128>), dim3(N, B * nH), dim3(128),
+                          0, s, part_o, part_ml, pl.S, N, nH, (bf16_t*)out);
+        return;
+    }
+    const dim3 grid(B * nH, pl.S, (N + ATT_QB - 1) / ATT_QB);
+    const int S = pl.S, KPS = pl.KPS;
 #define MEDUSA_ATT(T, DD)                                                                                   \
     do {                                                                                                    \
         MEDUSA_LAUNCH("tree_attn_split", (tree_attn_valu_kernel<T, DD>), grid, dim3(ATT_THREADS), 0, s,     \
                       (const T*)q, (const T*)k_tree, (const T*)v_tree, (T*)k_cache, (T*)v_cache, cache_len, \
-                      t.mask, N, t.W, nH, nKV, Lmax, max_cache_len, scale_log2, KPS, part_o, part_ml);                     \
+                      t.mask, N, t.W, nH, nKV, Lmax, max_cache_len, scale_log2, KPS, part_o, part_ml);      \
         MEDUSA_LAUNCH("tree_attn_combine", (tree_attn_combine_kernel<T, DD>), dim3(N, B * nH), dim3(DD), 0, \
                       s, part_o, part_ml, S, N, nH, (T*)out);                                               \
     } while (0)
@@ -207,14 +450,15 @@ void launch_tree_attention(const void* q, const void* k_tree, const void* v_tree
 #undef MEDUSA_ATT
 }
 
-size_t attn_workspace_bytes(int B, int nH, int N, int D, int max_cache_len) {
-    const int S = attn_splits(B, nH, N, max_cache_len + N);
+size_t attn_workspace_bytes(int B, int nH, int N, int D, int max_cache_len, bool bf16) {
+    const int S = attn_plan(bf16, B, nH, N, max_cache_len + N).S;
     const size_t rows = (size_t)B * nH * S * N;
     return (rows * D * sizeof(float) + 255) / 256 * 256 + rows * 2 * sizeof(float);
 }
 
-void attn_carve(int B, int nH, int N, int D, int max_cache_len, void* ws, float** part_o, float** part_ml) {
-    const int S = attn_splits(B, nH, N, max_cache_len + N);
+void attn_carve(int B, int nH, int N, int D, int max_cache_len, bool bf16, void* ws, float** part_o,
+                float** part_ml) {
+    const int S = attn_plan(bf16, B, nH, N, max_cache_len + N).S;
     const size_t rows = (size_t)B * nH * S * N;
     *part_o = (float*)ws;
     *part_ml = (float*)((char*)ws + (rows * D * sizeof(float) + 255) / 256 * 256);
