@@ -21,14 +21,16 @@ void launch_resid_silu(const void* h, const void* w1, const void* b1, int B, int
                        hipStream_t s);
 void launch_vocab_topk(const float* z, const void* w2, int B, int H, int V, int K, int topk, bool bf16,
                        float* logits, int32_t* topk_idx, float* topk_val, float* cv, int* ci, hipStream_t s);
-int vocab_topk_groups(int V, int K);
+int vocab_topk_groups(int B, int V, int K);
+size_t vocab_topk_lds_bytes(int B, int H, int V, int K);
+size_t resid_silu_lds_bytes(int B, int H);
 void launch_build_tree(const TreeDev& t, const int32_t* topk_idx, int K, int topk, const int32_t* root_tok,
                        const int32_t* cache_len, int B, int32_t* node_tok, int32_t* node_pos, uint64_t* anc_mask,
                        hipStream_t s);
 void launch_tree_attention(const void* q, const void* k_tree, const void* v_tree, void* k_cache, void* v_cache,
                            const int32_t* cache_len, int max_cache_len, const TreeDev& t, int B, int nH, int nKV,
                            int D, int Lmax, float scale, bool bf16, void* out, float* part_o, float* part_ml,
-                           hipStream_t s);
+                           hipStream_t s, int target_wg = 0);
 size_t attn_workspace_bytes(int B, int nH, int N, int D, int max_cache_len, bool bf16);
 void attn_carve(int B, int nH, int N, int D, int max_cache_len, bool bf16, void* ws, float** part_o,
                 float** part_ml);
@@ -159,8 +161,7 @@ static void check_heads_shape(int B, int H, int K, medusa_dtype dt) {
     REQUIRE(B >= 1 && K >= 1 && H >= 1, "B, H and K must be positive (B=%d H=%d K=%d)", B, H, K);
     SUPPORT(B <= MEDUSA_MAX_BATCH, "B=%d exceeds %d", B, MEDUSA_MAX_BATCH);
     SUPPORT(H % 8 == 0 && H <= 8192, "H=%d must be a multiple of 8 and <= 8192", H);
-    SUPPORT((size_t)((B <= 1) ? 1 : (B <= 2) ? 2 : (B <= 4) ? 4 : 8) * H * 4 <= 160 * 1024,
-            "B*H too large for the LDS-staged right-hand sides");
+    SUPPORT(resid_silu_lds_bytes(B, H) <= 160 * 1024, "B*H too large for the LDS-staged right-hand sides");
 }
 
 medusa_status medusa_resid_silu(const void* h, const void* w1, const void* b1, int B, int H, int K,
@@ -175,12 +176,12 @@ medusa_status medusa_resid_silu(const void* h, const void* w1, const void* b1, i
 size_t medusa_vocab_topk_workspace_size(int B, int H, int V, int K, int topk, medusa_dtype dt) {
     (void)H; (void)dt;
     if (B < 1 || V < 1 || K < 1 || topk < 1) return 0;
-    const size_t G = (size_t)vocab_topk_groups(V, K);
+    const size_t G = (size_t)vocab_topk_groups(B, V, K);
     return align256((size_t)B * K * G * topk * 4) * 2;
 }
 
 static void carve_vocab_ws(void* ws, int B, int V, int K, int topk, float** cv, int** ci) {
-    const size_t G = (size_t)vocab_topk_groups(V, K);
+    const size_t G = (size_t)vocab_topk_groups(B, V, K);
     const size_t one = align256((size_t)B * K * G * topk * 4);
     *cv = (float*)ws;
     *ci = (int*)((char*)ws + one);
@@ -191,6 +192,7 @@ static void check_vocab(int B, int H, int V, int K, int topk, medusa_dtype dt) {
     REQUIRE(V >= 1, "V must be positive");
     REQUIRE(topk >= 1 && topk <= V, "topk=%d must be in [1, V]", topk);
     SUPPORT(topk <= MEDUSA_MAX_TOPK, "topk=%d exceeds %d", topk, MEDUSA_MAX_TOPK);
+    SUPPORT(vocab_topk_lds_bytes(B, H, V, K) <= 160 * 1024, "B*H too large for the LDS-staged right-hand sides");
 }
 
 medusa_status medusa_vocab_topk(const float* z, const void* w2, int B, int H, int V, int K, int topk,

@@ -144,24 +144,51 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attn_valu_kernel(
 }
 
 // out[b][i][h][:] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
+// The S (m, l) pairs are read in parallel into LDS first; the partial rows are
+// then summed four splits at a time (independent loads in flight).
+constexpr int ATT_MAX_SPLITS = 1024;
+
 template <typename T, int D>
 __global__ __launch_bounds__(D) void tree_attn_combine_kernel(const float* __restrict__ part_o,
                                                               const float* __restrict__ part_ml, int S, int N,
                                                               int nH, T* __restrict__ out) {
+    __shared__ float ms[ATT_MAX_SPLITS];
+    __shared__ float ls[ATT_MAX_SPLITS];
+    __shared__ float red[D / 64];
     const int i = blockIdx.x;
     const int bh = blockIdx.y;
     const int b = bh / nH, h = bh - b * nH;
     const int c = threadIdx.x;
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, part_ml[(((size_t)bh * S + s) * N + i) * 2]);
-    float L = 0.f, acc = 0.f;
-    for (int s = 0; s < S; ++s) {
+    float mloc = -INFINITY;
+    for (int s = c; s < S; s += D) {
         const size_t pr = ((size_t)bh * S + s) * N + i;
-        const float ms = part_ml[pr * 2];
-        if (ms == -INFINITY) continue;
-        const float f = exp2f(ms - M);
-        L += f * part_ml[pr * 2 + 1];
-        acc += f * part_o[pr * D + c];
+        ms[s] = part_ml[pr * 2];
+        ls[s] = part_ml[pr * 2 + 1];
+        mloc = fmaxf(mloc, ms[s]);
+    }
+    mloc = wave_max(mloc);
+    if ((c & 63) == 0) red[c >> 6] = mloc;
+    __syncthreads();
+    float M = red[0];
+#pragma unroll
+    for (int w = 1; w < D / 64; ++w) M = fmaxf(M, red[w]);
+    float L = 0.f, acc = 0.f;
+    for (int s0 = 0; s0 < S; s0 += 4) {
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int s = s0 + u;
+            v[u] = (s < S && ms[s] != -INFINITY) ? part_o[(((size_t)bh * S + s) * N + i) * D + c] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int s = s0 + u;
+            if (s < S && ms[s] != -INFINITY) {
+                const float f = exp2f(ms[s] - M);
+                L += f * ls[s];
+                acc += f * v[u];
+            }
+        }
     }
     Elem<T>::store(out, (((size_t)b * N + i) * nH + h) * D + c, acc / L);
 }
@@ -199,7 +226,7 @@ __global__ __launch_bounds__(WAVES * 64) void tree_attn_mfma_kernel(
     constexpr int PT = CH / NT;     // chunks per thread
     constexpr int DC = D / 8;       // chunks per key row
     __shared__ __attribute__((aligned(16))) bf16_t Ks[TK][D + 8];
-    __shared__ __attribute__((aligned(16))) bf16_t Vt[D][TK + 8];
+    __shared__ __attribute__((aligned(16))) bf16_t Vt[D][TK + 4];  // 136-byte rows: 4-way write conflicts at most
 
     const int bh = blockIdx.x;
     const int b = bh / nH, h = bh - b * nH;
@@ -253,45 +280,73 @@ __global__ __launch_bounds__(WAVES * 64) void tree_attn_mfma_kernel(
     const int k_end = min(total, k_begin + KPS);
     const size_t cache_row0 = ((size_t)b * nKV + kvh) * Lmax;
 
-    u32x4 kreg[PT], vreg[PT];
-    auto load_tile = [&](int t0) {
+    // Tile loads: thread t owns KPT consecutive keys (group t / DC) and the
+    // 16-byte column chunk t % DC of each, so 16 lanes read one 256-byte key
+    // row contiguously.  K goes to LDS row-major; V is transposed in
+    // registers (v_perm_b32 pairs the same column of two keys) and written as
+    // KPT-key runs of each column row of Vt.
+    constexpr int KPT = PT;  // keys per thread per tile
+    const int kg = tid / DC, dc = tid - (tid / DC) * DC;
+    // Register ring of RING tiles: a workgroup's first RING tiles are all in
+    // flight before the first is consumed, and each consumed slot is refilled
+    // with the tile RING ahead.  Loads complete in issue order, so waiting for
+    // the oldest slot never waits for a younger one.
+    constexpr int RING = QBW == 1 ? 3 : 1;
+    u32x4 kreg[RING][KPT], vreg[RING][KPT];
+    auto load_tile = [&](u32x4(&kr)[KPT], u32x4(&vr)[KPT], int t0) {
 #pragma unroll
-        for (int e = 0; e < PT; ++e) {
-            const int c = tid + e * NT;
-            const int key = c / DC, dc = c - key * DC;
-            const int j = t0 + key;
+        for (int e = 0; e < KPT; ++e) {
+            const int j = t0 + kg * KPT + e;
             if (j < k_end) {
-                const size_t off = j < P ? (cache_row0 + j) * D + dc * 8
-                                         : (((size_t)b * N + (j - P)) * nKV + kvh) * D + dc * 8;
-                kreg[e] = *(const u32x4*)((j < P ? k_cache : k_tree) + off);
-                vreg[e] = *(const u32x4*)((j < P ? v_cache : v_tree) + off);
+                if (j < P) {
+                    const size_t off = (cache_row0 + j) * D + dc * 8;
+                    kr[e] = ld_stream(k_cache + off);
+                    vr[e] = ld_stream(v_cache + off);
+                } else {
+                    const size_t off = (((size_t)b * N + (j - P)) * nKV + kvh) * D + dc * 8;
+                    kr[e] = *(const u32x4*)(k_tree + off);
+                    vr[e] = *(const u32x4*)(v_tree + off);
+                }
             } else {
-                kreg[e] = (u32x4){0u, 0u, 0u, 0u};
-                vreg[e] = (u32x4){0u, 0u, 0u, 0u};
+                kr[e] = (u32x4){0u, 0u, 0u, 0u};
+                vr[e] = (u32x4){0u, 0u, 0u, 0u};
             }
         }
     };
-    auto store_tile = [&]() {
+    // K -> LDS row-major; V transposed in registers (v_perm_b32 pairs the same
+    // column of two keys) and written as KPT-key runs of each row of Vt.
+    auto store_tile = [&](const u32x4(&kr)[KPT], const u32x4(&vr)[KPT]) {
 #pragma unroll
-        for (int e = 0; e < PT; ++e) {
-            const int c = tid + e * NT;
-            const int key = c / DC, dc = c - key * DC;
-            *(u32x4*)(&Ks[key][dc * 8]) = kreg[e];
-            const uint32_t w4[4] = {vreg[e].x, vreg[e].y, vreg[e].z, vreg[e].w};
+        for (int e = 0; e < KPT; ++e) *(u32x4*)(&Ks[kg * KPT + e][dc * 8]) = kr[e];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                Vt[dc * 8 + 2 * u][key] = (bf16_t)(w4[u] & 0xFFFFu);
-                Vt[dc * 8 + 2 * u + 1][key] = (bf16_t)(w4[u] >> 16);
-            }
+        for (int i = 0; i < 8; ++i) {  // column dc * 8 + i
+            const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+            uint32_t w[KPT / 2 > 0 ? KPT / 2 : 1];
+#pragma unroll
+            for (int e = 0; e + 1 < KPT; e += 2)
+                w[e / 2] = __builtin_amdgcn_perm(vr[e + 1][i >> 1], vr[e][i >> 1], sel);
+            bf16_t* dst = &Vt[dc * 8 + i][kg * KPT];
+            if (KPT == 4) *(uint2*)dst = (uint2){w[0], w[1]};
+            else if (KPT == 2) *(uint32_t*)dst = w[0];
+            else *dst = (bf16_t)((i & 1) ? (vr[0][i >> 1] >> 16) : (vr[0][i >> 1] & 0xFFFFu));
         }
     };
-
-    if (k_begin < k_end) load_tile(k_begin);
-    for (int t0 = k_begin; t0 < k_end; t0 += TK) {
-        __syncthreads();
-        store_tile();
-        __syncthreads();
-        if (t0 + TK < k_end) load_tile(t0 + TK);
+#pragma unroll
+    for (int u = 0; u < RING; ++u)
+        if (k_begin + u * TK < k_end) load_tile(kreg[u], vreg[u], k_begin + u * TK);
+    for (int tb = k_begin; tb < k_end; tb += RING * TK) {
+#pragma unroll
+        for (int u = 0; u < RING; ++u) {
+            const int t0 = tb + u * TK;
+            if (t0 < k_end) {
+                __syncthreads();
+                store_tile(kreg[u], vreg[u]);
+                __syncthreads();
+                if (t0 + RING * TK < k_end) load_tile(kreg[u], vreg[u], t0 + RING * TK);
+                {  // compute tile t0 (written inline: a lambda here made the compiler spill)
+        // tiles entirely inside the prefix and the split need no masking
+        // (padded query columns are never written out)
+        const bool plain = QBW == 1 && t0 + TK <= P && t0 + TK <= k_end;
 #pragma unroll
         for (int qb = 0; qb < QBW; ++qb) {
             f32x4 st[KB];
@@ -309,30 +364,40 @@ __global__ __launch_bounds__(WAVES * 64) void tree_attn_mfma_kernel(
             // scale, mask (prefix: visible; tree key t: ancestor bit), tile max
             const int qi = qidx[qb];
             float tmax = -INFINITY;
+            if (plain) {
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+                for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = t0 + kb * 16 + lk * 4 + r;
-                    bool vis = j < k_end && qi < N;
-                    if (vis && j >= P) {
-                        const int t = j - P;
-                        const int w = t >> 6;
-                        const uint64_t word = w == 0 ? mrow[qb][0] : w == 1 ? mrow[qb][1] : w == 2 ? mrow[qb][2]
-                                                                                              : mrow[qb][3];
-                        vis = (word >> (t & 63)) & 1ull;
+                    for (int r = 0; r < 4; ++r) {
+                        st[kb][r] *= scale_log2;
+                        tmax = fmaxf(tmax, st[kb][r]);
                     }
-                    const float x = vis ? st[kb][r] * scale_log2 : -INFINITY;
-                    st[kb][r] = x;
-                    tmax = fmaxf(tmax, x);
-                }
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = t0 + kb * 16 + lk * 4 + r;
+                        bool vis = j < k_end && qi < N;
+                        if (vis && j >= P) {
+                            const int t = j - P;
+                            const int w = t >> 6;
+                            const uint64_t word = w == 0 ? mrow[qb][0] : w == 1 ? mrow[qb][1]
+                                                                      : w == 2 ? mrow[qb][2] : mrow[qb][3];
+                            vis = (word >> (t & 63)) & 1ull;
+                        }
+                        const float x = vis ? st[kb][r] * scale_log2 : -INFINITY;
+                        st[kb][r] = x;
+                        tmax = fmaxf(tmax, x);
+                    }
+            }
             tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
             const float m_new = fmaxf(m[qb], tmax);
             const bool live = m_new != -INFINITY;
             const float alpha = live ? exp2f(m[qb] - m_new) : 1.f;
             float psum = 0.f;
-            uint32_t pk[KB][2];  // bf16 pairs of P^T
+            uint32_t pk[KB][2];  // bf16 pairs of P^T (round to nearest even)
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 float p4[4];
@@ -341,8 +406,8 @@ __global__ __launch_bounds__(WAVES * 64) void tree_attn_mfma_kernel(
                     p4[r] = live ? exp2f(st[kb][r] - m_new) : 0.f;
                     psum += p4[r];
                 }
-                pk[kb][0] = (uint32_t)f32_to_bf16(p4[0]) | ((uint32_t)f32_to_bf16(p4[1]) << 16);
-                pk[kb][1] = (uint32_t)f32_to_bf16(p4[2]) | ((uint32_t)f32_to_bf16(p4[3]) << 16);
+                pk[kb][0] = pack_bf16x2(p4[0], p4[1]);
+                pk[kb][1] = pack_bf16x2(p4[2], p4[3]);
             }
             psum += __shfl_xor(psum, 16, 64);
             psum += __shfl_xor(psum, 32, 64);
@@ -362,6 +427,9 @@ __global__ __launch_bounds__(WAVES * 64) void tree_attn_mfma_kernel(
                                                                         __builtin_bit_cast(bf16x8, bp), o[qb][db], 0,
                                                                         0, 0);
                 }
+            }
+        }
+                    }
             }
         }
     }
@@ -386,16 +454,21 @@ struct AttnPlan {
     int KPS;  // keys per split
 };
 
-static AttnPlan attn_plan(bool bf16, int B, int nH, int N, int max_total) {
+// Workgroups the split of the key range aims at (MFMA path / vector-ALU path).
+constexpr int ATT_MFMA_TARGET_WG = 256;
+constexpr int ATT_VALU_TARGET_WG = 1024;
+
+static AttnPlan attn_plan(bool bf16, int B, int nH, int N, int max_total, int target_wg = 0) {
     AttnPlan p;
     p.mfma = bf16 && N <= MEDUSA_MAX_NODES_DEV;
     const int unit = p.mfma ? 32 : ATT_TK;
     const int qblocks = p.mfma ? 1 : (N + ATT_QB - 1) / ATT_QB;
     const int base = B * nH * qblocks;
-    const int target = p.mfma ? 512 : 1024;
+    const int target = target_wg > 0 ? target_wg : p.mfma ? ATT_MFMA_TARGET_WG : ATT_VALU_TARGET_WG;
     int S = (target + base - 1) / base;
     const int max_s = (max_total + unit - 1) / unit;
     if (S > max_s) S = max_s;
+    if (S > ATT_MAX_SPLITS) S = ATT_MAX_SPLITS;
     if (S < 1) S = 1;
     int kps = (max_total + S - 1) / S;
     kps = ((kps + unit - 1) / unit) * unit;
@@ -407,9 +480,9 @@ static AttnPlan attn_plan(bool bf16, int B, int nH, int N, int max_total) {
 void launch_tree_attention(const void* q, const void* k_tree, const void* v_tree, void* k_cache, void* v_cache,
                            const int32_t* cache_len, int max_cache_len, const TreeDev& t, int B, int nH,
                            int nKV, int D, int Lmax, float scale, bool bf16, void* out, float* part_o,
-                           float* part_ml, hipStream_t s) {
+                           float* part_ml, hipStream_t s, int target_wg) {
     const int N = t.N;
-    const AttnPlan pl = attn_plan(bf16, B, nH, N, max_cache_len + N);
+    const AttnPlan pl = attn_plan(bf16, B, nH, N, max_cache_len + N, target_wg);
     const float scale_log2 = scale * 1.4426950408889634f;
     if (pl.mfma) {
         const bf16_t *Q = (const bf16_t*)q, *KT = (const bf16_t*)k_tree, *VT = (const bf16_t*)v_tree;

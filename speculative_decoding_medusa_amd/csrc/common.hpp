@@ -22,6 +22,12 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 
+// One 16-byte load of data that is streamed once per call (weights, KV
+// cache): non-temporal, so it does not displace reused lines from the caches.
+__device__ __forceinline__ u32x4 ld_stream(const void* p) {
+    return __builtin_nontemporal_load((const u32x4*)p);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
@@ -32,6 +38,14 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
     if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (bf16_t)((u >> 16) | 0x40u);
     u += 0x7FFFu + ((u >> 16) & 1u);
     return (bf16_t)(u >> 16);
+}
+
+// Two floats -> packed bf16 pair (low half = lo), round to nearest even, in
+// one v_cvt_pk_bf16_f32.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 template <typename T> struct Elem;

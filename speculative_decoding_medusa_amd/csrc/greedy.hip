@@ -5,13 +5,15 @@
 // bf16: the product of the node rows with lm_head is a dense contraction
 // (64-512 rows share every lm_head byte), so it runs on MFMA
 // (v_mfma_f32_16x16x32_bf16) with the argmax fused into the epilogue:
-//   grid (ceil(V / 128), ceil(R / NODES)); 4 waves per workgroup, each wave
-//   owns 32 vocabulary rows (two 16-row MFMA blocks) against NODES node rows.
+//   grid (ceil(V / 64), ceil(R / NODES)); 4 waves per workgroup, each wave
+//   owns 16 vocabulary rows (one 16-row MFMA block) against NODES node rows,
+//   so the 32000-row vocabulary gives 500 workgroups (about two per CU).
 //   lm_head fragments stream from HBM straight into registers (each lane
 //   reads 16 contiguous bytes; 4 lanes cover 64 contiguous bytes of a row),
-//   prefetched one LDS chunk ahead; the node rows are staged in LDS in
-//   k-chunks shared by the 4 waves.  Each workgroup writes, per node, its best
-//   (value, index); a merge kernel reduces them.
+//   non-temporal, up to three k-chunks ahead; the node rows are staged in LDS in
+//   k-chunks shared by the 4 waves (double-buffered, one barrier per chunk).
+//   Each workgroup writes, per node, its best (value, index); a merge kernel
+//   reduces them.
 // float32: the vector-ALU GEMV of the heads (one pass per 8 rows).
 #include "common.hpp"
 
@@ -42,17 +44,29 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const T* __restrict__
 }
 
 constexpr int LMH_WAVES = 4;
-constexpr int LMH_VB = 2;                          // 16-row vocabulary blocks per wave
+constexpr int LMH_VB = 1;                          // 16-row vocabulary blocks per wave
 constexpr int LMH_ROWS = LMH_WAVES * LMH_VB * 16;  // vocabulary rows per workgroup
 
 template <int NBLK>
 struct LmhCfg {
     static constexpr int NODES = NBLK * 16;
-    static constexpr int KC = NBLK <= 4 ? 256 : NBLK <= 8 ? 128 : 64;  // k per LDS chunk
-    static constexpr int KS = KC / 32;                                 // MFMA k-steps per chunk
-    static constexpr int LDW = KC + 8;                                 // padded LDS row (bf16)
+    // k per chunk and ring depth (measured on 64 x 4096 x 32000: 256-wide
+    // chunks two deep beat 128-wide chunks three deep); larger node tiles use
+    // narrower chunks so a node stage stays at 8192 elements
+    static constexpr int KC = NBLK <= 4 ? 256 : 512 / NBLK;
+    static constexpr int KS = KC / 32;                 // MFMA k-steps per chunk
+    static constexpr int LDW = KC + 8;                 // padded LDS row (bf16)
+    static constexpr int NPT = NODES * KC / 8 / 256;   // 16-byte node pieces per thread per chunk
+    static constexpr int D = NBLK <= 4 ? 2 : 3;        // chunks in flight per register ring
 };
 
+// Pipeline (one barrier per chunk): step c issues the node rows and then the
+// lm_head fragments of chunk c + D - 1 into register rings, runs chunk c's
+// MFMAs from LDS stage c & 1, publishes the node rows of chunk c + 1 into the
+// other LDS stage, and synchronises.  Node loads are issued before the
+// lm_head loads of the same step: vector-memory loads complete in issue
+// order, so waiting for a chunk's node rows never waits for younger lm_head
+// fragments, and about two chunks of lm_head stay in flight at all times.
 template <int NBLK>
 __global__ __launch_bounds__(256) void lm_head_argmax_kernel(const bf16_t* __restrict__ n,  // [R][H]
                                                              const bf16_t* __restrict__ W,  // [V][H]
@@ -60,7 +74,8 @@ __global__ __launch_bounds__(256) void lm_head_argmax_kernel(const bf16_t* __res
                                                              int* __restrict__ cand_idx,  // [R][G]
                                                              float* __restrict__ logits) {
     using C = LmhCfg<NBLK>;
-    __shared__ __attribute__((aligned(16))) bf16_t ns[C::NODES][C::LDW];
+    constexpr int D = C::D;
+    __shared__ __attribute__((aligned(16))) bf16_t ns[2][C::NODES][C::LDW];
     __shared__ float red_v[LMH_WAVES][C::NODES];
     __shared__ int red_i[LMH_WAVES][C::NODES];
 
@@ -87,39 +102,38 @@ __global__ __launch_bounds__(256) void lm_head_argmax_kernel(const bf16_t* __res
     }
 
     const int nchunk = H / C::KC;  // host guarantees H % KC == 0
-    constexpr int NCH = C::NODES * C::KC / 8 / 256;  // 16-byte node chunks per thread per LDS chunk
-    u32x4 abuf[2][C::KS][LMH_VB];
-    u32x4 nreg[NCH];
-    auto load_a = [&](u32x4(&dst)[C::KS][LMH_VB], int kc) {
+    u32x4 aring[D][C::KS][LMH_VB];
+    u32x4 nring[D][C::NPT];
+    auto load_a = [&](u32x4(&dst)[C::KS][LMH_VB], int c) {
 #pragma unroll
         for (int s = 0; s < C::KS; ++s)
 #pragma unroll
             for (int a = 0; a < LMH_VB; ++a)
-                dst[s][a] = wvalid[a] ? *(const u32x4*)(wrow[a] + kc + s * 32) : (u32x4){0u, 0u, 0u, 0u};
+                dst[s][a] = wvalid[a] ? ld_stream(wrow[a] + c * C::KC + s * 32) : (u32x4){0u, 0u, 0u, 0u};
     };
-    auto load_n = [&](int kc) {
+    auto load_n = [&](u32x4(&dst)[C::NPT], int c) {
 #pragma unroll
-        for (int e = 0; e < NCH; ++e) {
-            const int c = tid + e * 256;
-            const int r = c / (C::KC / 8), k8 = c - r * (C::KC / 8);
+        for (int e = 0; e < C::NPT; ++e) {
+            const int p = tid + e * 256;
+            const int r = p / (C::KC / 8), k8 = p - r * (C::KC / 8);
             const int node = node0 + r;
-            nreg[e] = node < R ? *(const u32x4*)(n + (size_t)node * H + kc + k8 * 8) : (u32x4){0u, 0u, 0u, 0u};
+            dst[e] = node < R ? *(const u32x4*)(n + (size_t)node * H + c * C::KC + k8 * 8) : (u32x4){0u, 0u, 0u, 0u};
         }
     };
-    auto store_n = [&]() {
+    auto store_n = [&](const u32x4(&src)[C::NPT], int stage) {
 #pragma unroll
-        for (int e = 0; e < NCH; ++e) {
-            const int c = tid + e * 256;
-            const int r = c / (C::KC / 8), k8 = c - r * (C::KC / 8);
-            *(u32x4*)(&ns[r][k8 * 8]) = nreg[e];
+        for (int e = 0; e < C::NPT; ++e) {
+            const int p = tid + e * 256;
+            const int r = p / (C::KC / 8), k8 = p - r * (C::KC / 8);
+            *(u32x4*)(&ns[stage][r][k8 * 8]) = src[e];
         }
     };
-    auto compute = [&](const u32x4(&src)[C::KS][LMH_VB]) {
+    auto compute = [&](const u32x4(&src)[C::KS][LMH_VB], int stage) {
 #pragma unroll
         for (int s = 0; s < C::KS; ++s) {
 #pragma unroll
             for (int b = 0; b < NBLK; ++b) {
-                const u32x4 bv = *(const u32x4*)(&ns[b * 16 + lr][s * 32 + lk * 8]);
+                const u32x4 bv = *(const u32x4*)(&ns[stage][b * 16 + lr][s * 32 + lk * 8]);
 #pragma unroll
                 for (int a = 0; a < LMH_VB; ++a)
                     acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, src[s][a]),
@@ -128,24 +142,29 @@ __global__ __launch_bounds__(256) void lm_head_argmax_kernel(const bf16_t* __res
             }
         }
     };
-    // chunk c: publish the node rows loaded one chunk earlier, issue the loads
-    // of chunk c+1 (lm_head and node rows), then run chunk c's MFMAs
-    auto step = [&](int c, const u32x4(&cur)[C::KS][LMH_VB], u32x4(&nxt)[C::KS][LMH_VB]) {
-        __syncthreads();
-        store_n();
-        __syncthreads();
-        if (c + 1 < nchunk) {
-            load_n((c + 1) * C::KC);
-            load_a(nxt, (c + 1) * C::KC);
-        }
-        compute(cur);
-    };
 
-    load_n(0);
-    load_a(abuf[0], 0);
-    for (int c = 0; c < nchunk; c += 2) {
-        step(c, abuf[0], abuf[1]);
-        if (c + 1 < nchunk) step(c + 1, abuf[1], abuf[0]);
+#pragma unroll
+    for (int u = 0; u < D - 1; ++u)
+        if (u < nchunk) {
+            load_n(nring[u], u);
+            load_a(aring[u], u);
+        }
+    store_n(nring[0], 0);
+    __syncthreads();
+    for (int c0 = 0; c0 < nchunk; c0 += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            const int c = c0 + u;  // ring slot of chunk c is c % D == u
+            if (c < nchunk) {
+                if (c + D - 1 < nchunk) {
+                    load_n(nring[(u + D - 1) % D], c + D - 1);
+                    load_a(aring[(u + D - 1) % D], c + D - 1);
+                }
+                compute(aring[u], c & 1);
+                if (c + 1 < nchunk) store_n(nring[(u + 1) % D], (c + 1) & 1);
+                __syncthreads();
+            }
+        }
     }
 
     // epilogue: lane holds rows vw + a*16 + 4*lk + r of node column b*16 + lr
@@ -207,10 +226,17 @@ __global__ __launch_bounds__(64) void argmax_merge_kernel(const float* __restric
 void launch_vocab_topk_named(const float* z, const void* w2, int B, int H, int V, int K, int topk, bool bf16,
                              float* logits, int32_t* topk_idx, float* topk_val, float* cv, int* ci, hipStream_t s,
                              const char* gemv_name, const char* merge_name);
-int vocab_topk_groups(int V, int K);
+int vocab_topk_groups(int B, int V, int K);
+
+// workgroups of the float32 GEMV path over any chunk of <= 8 rows
+static int gemv_groups_max(int V) {
+    int g = 0;
+    for (int nb = 1; nb <= 8; ++nb) g = vocab_topk_groups(nb, V, 1) > g ? vocab_topk_groups(nb, V, 1) : g;
+    return g;
+}
 
 static int lmh_nblk(int R) { return R <= 64 ? 4 : R <= 128 ? 8 : 16; }
-static int lmh_kc(int nblk) { return nblk <= 4 ? 256 : nblk <= 8 ? 128 : 64; }
+static int lmh_kc(int nblk) { return nblk <= 4 ? 256 : 512 / nblk; }
 
 static bool use_mfma(bool bf16, int H, int R) { return bf16 && H % lmh_kc(lmh_nblk(R)) == 0; }
 
@@ -221,7 +247,7 @@ size_t greedy_workspace_bytes(int R, int H, int V, bool bf16) {
         const size_t G = (V + LMH_ROWS - 1) / LMH_ROWS;
         return a256((size_t)R * H * 2) + a256((size_t)R * G * 4) * 2;
     }
-    const int G = vocab_topk_groups(V, 1);
+    const int G = gemv_groups_max(V);
     return a256((size_t)R * H * 4) + a256((size_t)8 * G * 4) * 2 + a256((size_t)R * 4);
 }
 
@@ -252,7 +278,7 @@ void launch_base_greedy(const void* x, const void* lm_head, int R, int H, int V,
     }
     float* n = (float*)p;
     p += a256((size_t)R * H * 4);
-    const int G = vocab_topk_groups(V, 1);
+    const int G = gemv_groups_max(V);
     float* cv = (float*)p;
     int* ci = (int*)(p + a256((size_t)8 * G * 4));
     p += a256((size_t)8 * G * 4) * 2;

@@ -7,24 +7,51 @@
 // the MFMA ridge.
 //
 // Layout of the work: grid (G, K); workgroup g of head k owns a contiguous
-// block of rows; its 4 waves take groups of R consecutive rows in turn, so
-// each wave visits its rows in increasing order.  A lane owns 16-byte chunks
+// block of rows; its waves take groups of R consecutive rows in turn, so each
+// wave visits its rows in increasing order.  A lane owns 16-byte chunks
 // c*64 + lane of a row (fully coalesced 1 KiB per wave per load), multiplies
 // them with the right-hand sides staged once per workgroup in LDS as fp32,
 // and the 64 partial sums are combined with an xor butterfly whose result is
 // bitwise identical in every lane.  The reduction order depends only on the
 // row length, so the projection of a given z is bitwise reproducible.
+//
+// The weight loads are non-temporal: every weight byte is read once per call,
+// so it should not displace reused lines (z, the candidates) from the caches.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace medusa {
 
 enum { EPI_SILU = 0, EPI_TOPK = 1 };
 
-constexpr int GEMV_THREADS = 256;
-constexpr int GEMV_WAVES = GEMV_THREADS / 64;
+// Upper bound of the rows one workgroup owns (sizes the row-value LDS array).
+constexpr int GEMV_MAX_ROWS_PER_WG = 512;
 
-template <typename WT, int NB, int CPL, int R, int EPI>
-__global__ __launch_bounds__(GEMV_THREADS) void gemv_rows_kernel(
+// Sorted register list of the best TK (value, index) pairs, best first.
+template <int TK>
+__device__ __forceinline__ void sorted_insert(float (&lv)[TK], int (&li)[TK], float v, int i) {
+    if (!better(v, i, lv[TK - 1], li[TK - 1])) return;
+    lv[TK - 1] = v;
+    li[TK - 1] = i;
+#pragma unroll
+    for (int t = TK - 1; t > 0; --t) {
+        if (better(lv[t], li[t], lv[t - 1], li[t - 1])) {
+            const float tv = lv[t]; lv[t] = lv[t - 1]; lv[t - 1] = tv;
+            const int ti = li[t]; li[t] = li[t - 1]; li[t - 1] = ti;
+        }
+    }
+}
+template <int TK>
+__device__ __forceinline__ void sorted_pop(float (&lv)[TK], int (&li)[TK]) {
+#pragma unroll
+    for (int u = 0; u < TK - 1; ++u) { lv[u] = lv[u + 1]; li[u] = li[u + 1]; }
+    lv[TK - 1] = -INFINITY;
+    li[TK - 1] = 0x7FFFFFFF;
+}
+
+template <typename WT, int NB, int CPL, int R, int EPI, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void gemv_rows_kernel(
     const void* __restrict__ xsrc,   // SILU: h [B][H] (WT);  TOPK: z [B][K][H] fp32
     const WT* __restrict__ W,        // [K][nrows][H]
     const WT* __restrict__ bias,     // SILU: b1 [K][H]
@@ -32,7 +59,12 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_rows_kernel(
     float* __restrict__ out,         // SILU: z [B][K][H];  TOPK: logits [B][K][nrows] or null
     float* __restrict__ cand_val,    // TOPK: [B][K][G][topk]
     int* __restrict__ cand_idx, int topk) {
-    extern __shared__ float xs[];    // [NB][H] fp32
+    // The right-hand sides and the row values live in separate LDS arrays, so
+    // the compiler knows the row-value stores never touch x and can keep x in
+    // registers across the row loop.
+    extern __shared__ __attribute__((aligned(16))) float xs[];  // [NB][H] fp32
+    __shared__ float rowv[EPI == EPI_TOPK ? NB * GEMV_MAX_ROWS_PER_WG : 1];  // TOPK: [NB][rows_per_wg]
+    constexpr int NT = WAVES * 64;
     constexpr int PER = Elem<WT>::PER16;
     const int k = blockIdx.y;
     const int g = blockIdx.x;
@@ -40,15 +72,30 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_rows_kernel(
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
 
-    // Stage the right-hand sides (fp32) in LDS; padded batch slots are zero.
-    for (int i = threadIdx.x; i < NB * H; i += GEMV_THREADS) {
-        const int b = i / H, j = i - b * H;
-        float v = 0.f;
-        if (b < B) {
-            if (EPI == EPI_SILU) v = Elem<WT>::load((const WT*)xsrc, (size_t)b * H + j);
-            else v = ((const float*)xsrc)[((size_t)b * K + k) * H + j];
+    // Stage the right-hand sides (fp32) in LDS with 16-byte loads; padded
+    // batch slots are zero.  H % 8 == 0, so a chunk never straddles two rows.
+    {
+        constexpr int XE = EPI == EPI_SILU ? Elem<WT>::PER16 : 4;  // elements per 16-byte chunk of x
+        const int cpr = H / XE;                                    // chunks per right-hand side
+        for (int i = threadIdx.x; i < NB * cpr; i += NT) {
+            const int b = i / cpr, j = (i - b * cpr) * XE;
+            float v[XE];
+            if (b < B) {
+                if (EPI == EPI_SILU) {
+                    Elem<WT>::expand(*(const u32x4*)((const WT*)xsrc + (size_t)b * H + j), v);
+                } else {
+                    const f32x4 q = *(const f32x4*)((const float*)xsrc + ((size_t)b * K + k) * H + j);
+#pragma unroll
+                    for (int t = 0; t < XE; ++t) v[t] = q[t];
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < XE; ++t) v[t] = 0.f;
+            }
+#pragma unroll
+            for (int t = 0; t < XE; t += 4)
+                *(f32x4*)(xs + b * H + j + t) = (f32x4){v[t], v[t + 1], v[t + 2], v[t + 3]};
         }
-        xs[i] = v;
     }
     __syncthreads();
 
@@ -57,15 +104,19 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_rows_kernel(
     const int row1 = min(nrows, row0 + rows_per_wg);
     const WT* Wk = W + (size_t)k * nrows * H;
 
-    // Per-wave top-k list, lane j < topk holds rank j of sequence b.
-    float tv[NB];
-    int ti[NB];
-    float kth[NB];
+    // Rows of H = CPL * 64 * PER elements and whole row groups take the
+    // unchecked paths: the checks are wave-uniform, so the common case runs
+    // without per-lane execution masks around every load and FMA block.
+    const bool full_rows = nchunks == CPL * 64;
+    auto load_rows = [&](u32x4(&wv)[R][CPL], int rb) {
+        if (full_rows && rb + R <= row1) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) { tv[b] = -INFINITY; ti[b] = 0x7FFFFFFF; kth[b] = -INFINITY; }
-
-    for (int rb = row0 + wave * R; rb < row1; rb += GEMV_WAVES * R) {
-        u32x4 wv[R][CPL];
+            for (int j = 0; j < R; ++j)
+#pragma unroll
+                for (int c = 0; c < CPL; ++c)
+                    wv[j][c] = ld_stream(Wk + (size_t)(rb + j) * H + (size_t)(c * 64 + lane) * PER);
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < R; ++j) {
             const int row = rb + j;
@@ -73,20 +124,18 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_rows_kernel(
             for (int c = 0; c < CPL; ++c) {
                 const int ci = c * 64 + lane;
                 if (row < row1 && ci < nchunks)
-                    wv[j][c] = *(const u32x4*)(Wk + (size_t)row * H + (size_t)ci * PER);
+                    wv[j][c] = ld_stream(Wk + (size_t)row * H + (size_t)ci * PER);
                 else
                     wv[j][c] = (u32x4){0u, 0u, 0u, 0u};
             }
         }
-        float acc[R][NB];
-#pragma unroll
-        for (int j = 0; j < R; ++j)
-#pragma unroll
-            for (int b = 0; b < NB; ++b) acc[j][b] = 0.f;
+    };
+    auto dot = [&](auto checked, const u32x4(&wv)[R][CPL], float(&acc)[R][NB]) {
+        constexpr bool CHECKED = decltype(checked)::value;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             const int ci = c * 64 + lane;
-            if (ci < nchunks) {
+            if (!CHECKED || ci < nchunks) {
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
                     float xv[PER];
@@ -105,6 +154,15 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_rows_kernel(
                 }
             }
         }
+    };
+    auto process = [&](const u32x4(&wv)[R][CPL], int rb) {
+        float acc[R][NB];
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) acc[j][b] = 0.f;
+        if (full_rows) dot(std::false_type{}, wv, acc);
+        else dot(std::true_type{}, wv, acc);
 #pragma unroll
         for (int j = 0; j < R; ++j) {
             const int row = rb + j;
@@ -118,79 +176,94 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_rows_kernel(
                         const float s = pre / (1.f + __expf(-pre));
                         out[((size_t)b * K + k) * H + row] = xs[b * H + row] + s;
                     }
-                } else {
-                    if (out != nullptr && lane == 0) out[((size_t)b * K + k) * nrows + row] = v;
-                    if (v > kth[b]) {
-                        const bool gt = lane < topk && v > tv[b];
-                        const uint64_t m = __ballot(gt);
-                        const int p = __ffsll((unsigned long long)m) - 1;
-                        const float upv = __shfl_up(tv[b], 1, 64);
-                        const int upi = __shfl_up(ti[b], 1, 64);
-                        if (lane > p && lane < topk) { tv[b] = upv; ti[b] = upi; }
-                        if (lane == p) { tv[b] = v; ti[b] = row; }
-                        kth[b] = __shfl(tv[b], topk - 1, 64);
-                    }
+                } else if (lane == 0) {
+                    rowv[b * rows_per_wg + (row - row0)] = v;
+                    if (out != nullptr) out[((size_t)b * K + k) * nrows + row] = v;
                 }
             }
         }
+    };
+
+    for (int rb = row0 + wave * R; rb < row1; rb += WAVES * R) {
+        u32x4 wv[R][CPL];
+        load_rows(wv, rb);
+        process(wv, rb);
     }
 
     if (EPI == EPI_TOPK) {
-        // Merge the 4 per-wave sorted lists into the workgroup's top-k.
-        __shared__ float sv[GEMV_WAVES][NB][MEDUSA_MAX_TOPK_DEV];
-        __shared__ int si[GEMV_WAVES][NB][MEDUSA_MAX_TOPK_DEV];
-        if (lane < topk) {
-#pragma unroll
-            for (int b = 0; b < NB; ++b) { sv[wave][b][lane] = tv[b]; si[wave][b][lane] = ti[b]; }
-        }
+        // The workgroup's top-k of each sequence: wave w takes sequences
+        // w, w + WAVES, ...  Each lane keeps a sorted register list of the rows
+        // it scans; the wave then extracts the winners rank by rank.
         __syncthreads();
-        if (threadIdx.x < B) {
-            const int b = threadIdx.x;
-            int head[GEMV_WAVES] = {0, 0, 0, 0};
+        const int nr = row1 - row0;
+        for (int b = wave; b < B; b += WAVES) {
+            float lv[MEDUSA_MAX_TOPK_DEV];
+            int li[MEDUSA_MAX_TOPK_DEV];
+#pragma unroll
+            for (int t = 0; t < MEDUSA_MAX_TOPK_DEV; ++t) { lv[t] = -INFINITY; li[t] = 0x7FFFFFFF; }
+            for (int r = lane; r < nr; r += 64) sorted_insert<MEDUSA_MAX_TOPK_DEV>(lv, li, rowv[b * rows_per_wg + r], row0 + r);
             const size_t base = (((size_t)b * K + k) * G + g) * topk;
             for (int t = 0; t < topk; ++t) {
-                int best = 0;
-                for (int w = 1; w < GEMV_WAVES; ++w)
-                    if (better(sv[w][b][head[w]], si[w][b][head[w]], sv[best][b][head[best]],
-                               si[best][b][head[best]]))
-                        best = w;
-                cand_val[base + t] = sv[best][b][head[best]];
-                cand_idx[base + t] = si[best][b][head[best]];
-                if (head[best] < topk - 1) ++head[best];
-                else sv[best][b][head[best]] = -INFINITY, si[best][b][head[best]] = 0x7FFFFFFF;
+                float bv = lv[0];
+                int bi = li[0];
+                wave_argmax(bv, bi);
+                if (lane == 0) { cand_val[base + t] = bv; cand_idx[base + t] = bi; }
+                if (lv[0] == bv && li[0] == bi) sorted_pop<MEDUSA_MAX_TOPK_DEV>(lv, li);
             }
         }
     }
 }
 
-// Final merge: per (b, k) pick the top-k of G * topk workgroup candidates.
-// All candidate indices are distinct rows, so "strictly after the previous
-// winner in (value desc, index asc) order" identifies the next one.
-__global__ __launch_bounds__(64) void topk_merge_kernel(const float* __restrict__ cand_val,
-                                                        const int* __restrict__ cand_idx, int M,
-                                                        int topk, int32_t* __restrict__ topk_idx,
-                                                        float* __restrict__ topk_val) {
+// Final merge: per (b, k) the top-k of the G * topk workgroup candidates.
+// Each thread keeps a sorted register list of the best TK candidates it reads
+// (loads issued four at a time); the block then extracts the winners one rank
+// at a time: block-wide argmax of the threads' list heads, the winning thread
+// pops its head.  Candidate rows are distinct (padding entries rank last), so
+// the (value desc, index asc) order is total.
+template <int TK>
+__global__ __launch_bounds__(256) void topk_merge_kernel(const float* __restrict__ cand_val,
+                                                         const int* __restrict__ cand_idx, int M, int topk,
+                                                         int32_t* __restrict__ topk_idx,
+                                                         float* __restrict__ topk_val) {
+    __shared__ float wv_s[4];
+    __shared__ int wi_s[4];
     const int bk = blockIdx.x;
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float* cv = cand_val + (size_t)bk * M;
     const int* ci = cand_idx + (size_t)bk * M;
-    float pv = INFINITY;
-    int pi = -1;
+    float lv[TK];
+    int li[TK];
+#pragma unroll
+    for (int t = 0; t < TK; ++t) { lv[t] = -INFINITY; li[t] = 0x7FFFFFFF; }
+    for (int m0 = tid; m0 < M; m0 += 4 * 256) {
+        float v[4];
+        int i[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int m = m0 + u * 256;
+            v[u] = m < M ? cv[m] : -INFINITY;
+            i[u] = m < M ? ci[m] : 0x7FFFFFFF;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sorted_insert<TK>(lv, li, v[u], i[u]);
+    }
     for (int t = 0; t < topk; ++t) {
-        float bv = -INFINITY;
-        int bi = 0x7FFFFFFF;
-        for (int m = lane; m < M; m += 64) {
-            const float v = cv[m];
-            const int i = ci[m];
-            if (better(pv, pi, v, i) && better(v, i, bv, bi)) { bv = v; bi = i; }
-        }
+        float bv = lv[0];
+        int bi = li[0];
         wave_argmax(bv, bi);
-        if (lane == 0) {
-            topk_idx[(size_t)bk * topk + t] = bi;
-            topk_val[(size_t)bk * topk + t] = bv;
+        if (lane == 0) { wv_s[wave] = bv; wi_s[wave] = bi; }
+        __syncthreads();
+        float gv = wv_s[0];
+        int gi = wi_s[0];
+#pragma unroll
+        for (int w = 1; w < 4; ++w)
+            if (better(wv_s[w], wi_s[w], gv, gi)) { gv = wv_s[w]; gi = wi_s[w]; }
+        if (tid == 0) {
+            topk_idx[(size_t)bk * topk + t] = gi;
+            topk_val[(size_t)bk * topk + t] = gv;
         }
-        pv = bv;
-        pi = bi;
+        if (lv[0] == gv && li[0] == gi) sorted_pop<TK>(lv, li);  // the owner pops its head
+        __syncthreads();
     }
 }
 
@@ -203,27 +276,65 @@ static int pick_cpl(int nchunks) {
     return c <= 1 ? 1 : c <= 2 ? 2 : c <= 4 ? 4 : c <= 8 ? 8 : 16;
 }
 
-constexpr int GEMV_R = 2;
+// Launch shape of one GEMV: rows per workgroup and the number of workgroups
+// per head.  Rows per workgroup are a multiple of the rows one pass of the
+// waves covers, sized so that the launch has about `target` workgroups.
+struct GemvPlan {
+    int rows_per_wg;
+    int G;
+};
 
-template <typename WT, int NB, int CPL, int EPI>
-static void launch_gemv_t(const void* x, const WT* W, const WT* bias, int B, int H, int nrows, int K,
-                          int rows_per_wg, int G, float* out, float* cv, int* ci, int topk,
-                          hipStream_t s, const char* name) {
-    auto kern = gemv_rows_kernel<WT, NB, CPL, GEMV_R, EPI>;
-    const size_t shmem = (size_t)NB * H * sizeof(float);
-    if (shmem > 65536) hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-    MEDUSA_LAUNCH(name, kern, dim3(G, K), dim3(GEMV_THREADS), shmem, s, x, W, bias, B, H, nrows, K,
-                  rows_per_wg, out, cv, ci, topk);
+static GemvPlan gemv_plan(int nrows, int K, int target, int quantum) {
+    long long total = (long long)nrows * K;
+    long long r = (total + target - 1) / target;
+    r = ((r + quantum - 1) / quantum) * quantum;
+    if (r < quantum) r = quantum;
+    if (r > nrows) r = ((nrows + quantum - 1) / quantum) * quantum;
+    if (r > GEMV_MAX_ROWS_PER_WG) r = GEMV_MAX_ROWS_PER_WG;
+    return GemvPlan{(int)r, (int)((nrows + r - 1) / r)};
 }
 
-template <typename WT, int EPI>
+// LDS of one workgroup: the fp32 right-hand sides (dynamic) and, for the
+// top-k epilogue, the statically sized row-value array.
+static size_t gemv_dyn_lds_bytes(int NB, int H) { return (size_t)NB * H * sizeof(float); }
+static size_t gemv_lds_bytes(int NB, int H, bool topk) {
+    return gemv_dyn_lds_bytes(NB, H) + (topk ? (size_t)NB * GEMV_MAX_ROWS_PER_WG * sizeof(float) : 0);
+}
+
+template <typename WT, int NB, int CPL, int R, int EPI, int WAVES>
+static void launch_gemv_t(const void* x, const WT* W, const WT* bias, int B, int H, int nrows, int K,
+                          const GemvPlan& pl, float* out, float* cv, int* ci, int topk, hipStream_t s,
+                          const char* name) {
+    auto kern = gemv_rows_kernel<WT, NB, CPL, R, EPI, WAVES>;
+    const size_t shmem = gemv_dyn_lds_bytes(NB, H);
+    // allow the largest dynamic LDS that fits beside the static arrays (once per instantiation)
+    static const bool lds_ok = [&] {
+        const size_t stat = EPI == EPI_TOPK ? (size_t)NB * GEMV_MAX_ROWS_PER_WG * sizeof(float) : 0;
+        return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   (int)(160 * 1024 - stat - 1024)) == hipSuccess;
+    }();
+    (void)lds_ok;
+    MEDUSA_LAUNCH(name, kern, dim3(pl.G, K), dim3(WAVES * 64), shmem, s, x, W, bias, B, H, nrows, K,
+                  pl.rows_per_wg, out, cv, ci, topk);
+}
+
+// Production shapes (measured on the 7B head shapes, 20480 and 160000 rows of
+// 4096 bf16): the residual-SiLU block runs 4 waves x 4 rows per step on about
+// 512 workgroups (2 rows per step above two right-hand sides, to bound
+// registers); the vocabulary projection 8 waves x 2 rows per step on about
+// 2048 workgroups.
+constexpr int SILU_WAVES = 4, SILU_TARGET_WG = 512;
+constexpr int TOPK_R = 2, TOPK_WAVES = 8, TOPK_TARGET_WG = 2048;
+static int silu_r(int NB) { return NB <= 2 ? 4 : 2; }
+
+template <typename WT, int EPI, int R, int WAVES>
 static void launch_gemv_nb(int NB, int CPL, const void* x, const WT* W, const WT* bias, int B, int H,
-                           int nrows, int K, int rows_per_wg, int G, float* out, float* cv, int* ci,
-                           int topk, hipStream_t s, const char* name) {
-#define MEDUSA_GEMV_CASE(nb, cpl)                                                                  \
-    if (NB == nb && CPL == cpl)                                                                    \
-        return launch_gemv_t<WT, nb, cpl, EPI>(x, W, bias, B, H, nrows, K, rows_per_wg, G, out, cv, \
-                                               ci, topk, s, name);
+                           int nrows, int K, const GemvPlan& pl, float* out, float* cv, int* ci, int topk,
+                           hipStream_t s, const char* name) {
+#define MEDUSA_GEMV_CASE(nb, cpl)                                                                          \
+    if (NB == nb && CPL == cpl)                                                                            \
+        return launch_gemv_t<WT, nb, cpl, R, EPI, WAVES>(x, W, bias, B, H, nrows, K, pl, out, cv, ci, topk, s, \
+                                                         name);
 #define MEDUSA_GEMV_NB(nb) \
     MEDUSA_GEMV_CASE(nb, 1) MEDUSA_GEMV_CASE(nb, 2) MEDUSA_GEMV_CASE(nb, 4) MEDUSA_GEMV_CASE(nb, 8) MEDUSA_GEMV_CASE(nb, 16)
     MEDUSA_GEMV_NB(1) MEDUSA_GEMV_NB(2) MEDUSA_GEMV_NB(4) MEDUSA_GEMV_NB(8)
@@ -231,52 +342,66 @@ static void launch_gemv_nb(int NB, int CPL, const void* x, const WT* W, const WT
 #undef MEDUSA_GEMV_CASE
 }
 
-// rows per workgroup: a multiple of the rows one pass of the 4 waves covers,
-// sized so that the whole launch has about `target` workgroups.
-static int rows_per_wg_for(int nrows, int K, int target) {
-    const int quantum = GEMV_WAVES * GEMV_R;
-    long long total = (long long)nrows * K;
-    long long r = (total + target - 1) / target;
-    r = ((r + quantum - 1) / quantum) * quantum;
-    if (r < quantum) r = quantum;
-    if (r > nrows) r = ((nrows + quantum - 1) / quantum) * quantum;
-    return (int)r;
+static GemvPlan topk_plan(int V, int K, int NB) {
+    (void)NB;
+    return gemv_plan(V, K, TOPK_TARGET_WG, TOPK_WAVES * TOPK_R);
 }
 
-int vocab_topk_groups(int V, int K) {
-    const int rpw = rows_per_wg_for(V, K, 1024);
-    return (V + rpw - 1) / rpw;
+int vocab_topk_groups(int B, int V, int K) { return topk_plan(V, K, pick_nb(B)).G; }
+
+size_t vocab_topk_lds_bytes(int B, int H, int V, int K) {
+    const int NB = pick_nb(B);
+    (void)V; (void)K;
+    return gemv_lds_bytes(NB, H, true);
 }
+
+size_t resid_silu_lds_bytes(int B, int H) { return gemv_lds_bytes(pick_nb(B), H, false); }
 
 void launch_resid_silu(const void* h, const void* w1, const void* b1, int B, int H, int K, bool bf16,
                        float* z, hipStream_t s) {
-    const int rpw = rows_per_wg_for(H, K, 1024);
-    const int G = (H + rpw - 1) / rpw;
     const int PER = bf16 ? 8 : 4;
     const int NB = pick_nb(B), CPL = pick_cpl(H / PER);
-    if (bf16)
-        launch_gemv_nb<bf16_t, EPI_SILU>(NB, CPL, h, (const bf16_t*)w1, (const bf16_t*)b1, B, H, H, K, rpw,
-                                         G, z, nullptr, nullptr, 0, s, "resid_silu_gemv");
+    const int R = silu_r(NB);
+    const GemvPlan pl = gemv_plan(H, K, SILU_TARGET_WG, SILU_WAVES * R);
+#define MEDUSA_SILU_GO(RR)                                                                                         \
+    do {                                                                                                           \
+        if (bf16)                                                                                                  \
+            launch_gemv_nb<bf16_t, EPI_SILU, RR, SILU_WAVES>(NB, CPL, h, (const bf16_t*)w1, (const bf16_t*)b1, B, H, \
+                                                            H, K, pl, z, nullptr, nullptr, 0, s, "resid_silu_gemv"); \
+        else                                                                                                       \
+            launch_gemv_nb<float, EPI_SILU, RR, SILU_WAVES>(NB, CPL, h, (const float*)w1, (const float*)b1, B, H, H, \
+                                                           K, pl, z, nullptr, nullptr, 0, s, "resid_silu_gemv");    \
+    } while (0)
+    if (R == 4) MEDUSA_SILU_GO(4); else MEDUSA_SILU_GO(2);
+#undef MEDUSA_SILU_GO
+}
+
+void launch_topk_merge(const float* cv, const int* ci, int BK, int M, int topk, int32_t* topk_idx,
+                       float* topk_val, hipStream_t s, const char* merge_name) {
+    if (topk <= 4)
+        MEDUSA_LAUNCH(merge_name, topk_merge_kernel<4>, dim3(BK), dim3(256), 0, s, cv, ci, M, topk, topk_idx,
+                      topk_val);
+    else if (topk <= 8)
+        MEDUSA_LAUNCH(merge_name, topk_merge_kernel<8>, dim3(BK), dim3(256), 0, s, cv, ci, M, topk, topk_idx,
+                      topk_val);
     else
-        launch_gemv_nb<float, EPI_SILU>(NB, CPL, h, (const float*)w1, (const float*)b1, B, H, H, K, rpw, G,
-                                        z, nullptr, nullptr, 0, s, "resid_silu_gemv");
+        MEDUSA_LAUNCH(merge_name, topk_merge_kernel<16>, dim3(BK), dim3(256), 0, s, cv, ci, M, topk, topk_idx,
+                      topk_val);
 }
 
 void launch_vocab_topk_named(const float* z, const void* w2, int B, int H, int V, int K, int topk, bool bf16,
                              float* logits, int32_t* topk_idx, float* topk_val, float* cv, int* ci, hipStream_t s,
                              const char* gemv_name, const char* merge_name) {
-    const int rpw = rows_per_wg_for(V, K, 1024);
-    const int G = (V + rpw - 1) / rpw;
     const int PER = bf16 ? 8 : 4;
     const int NB = pick_nb(B), CPL = pick_cpl(H / PER);
+    const GemvPlan pl = topk_plan(V, K, NB);
     if (bf16)
-        launch_gemv_nb<bf16_t, EPI_TOPK>(NB, CPL, z, (const bf16_t*)w2, nullptr, B, H, V, K, rpw, G, logits,
-                                         cv, ci, topk, s, gemv_name);
+        launch_gemv_nb<bf16_t, EPI_TOPK, TOPK_R, TOPK_WAVES>(NB, CPL, z, (const bf16_t*)w2, nullptr, B, H, V, K, pl,
+                                                             logits, cv, ci, topk, s, gemv_name);
     else
-        launch_gemv_nb<float, EPI_TOPK>(NB, CPL, z, (const float*)w2, nullptr, B, H, V, K, rpw, G, logits, cv,
-                                        ci, topk, s, gemv_name);
-    MEDUSA_LAUNCH(merge_name, topk_merge_kernel, dim3(B * K), dim3(64), 0, s, cv, ci, G * topk, topk,
-                  topk_idx, topk_val);
+        launch_gemv_nb<float, EPI_TOPK, TOPK_R, TOPK_WAVES>(NB, CPL, z, (const float*)w2, nullptr, B, H, V, K, pl,
+                                                            logits, cv, ci, topk, s, gemv_name);
+    launch_topk_merge(cv, ci, B * K, pl.G * topk, topk, topk_idx, topk_val, s, merge_name);
 }
 
 void launch_vocab_topk(const float* z, const void* w2, int B, int H, int V, int K, int topk, bool bf16,
