@@ -155,3 +155,67 @@ def host_f64(t):
 
 def tol(dtype_str):
     return 1e-4 if dtype_str == "f32" else 2e-2
+
+
+# ---------------------------------------------------------------------------
+# one whole step on the GPU, in the call sequence and launch shapes bench.py
+# times (the same C-ABI calls with the same arguments)
+# ---------------------------------------------------------------------------
+
+def run_step_gpu(M, cfg, heads, att, root):
+    """Upload the workload, run resid_silu -> vocab_topk -> build_tree ->
+    tree_attention_verify -> base_greedy -> accept (with compaction) once and
+    return host copies of every output."""
+    import torch
+    d = {k: dev(v) for k, v in {**heads, **att}.items()}
+    B, K, H, V, N, topk = cfg.B, cfg.K, cfg.H, cfg.V, cfg.N, cfg.topk
+    parent, rank = cfg.tree.arrays()
+    tree = M.Tree(parent, rank, K, topk)
+    wdt = M.BF16 if cfg.dtype == "bf16" else M.F32
+    z = torch.empty(B, K, H, device="cuda")
+    ti = torch.empty(B, K, topk, dtype=torch.int32, device="cuda")
+    tv = torch.empty(B, K, topk, device="cuda")
+    ws_v = torch.empty(M.vocab_topk_workspace_size(B, H, V, K, topk, wdt), dtype=torch.uint8, device="cuda")
+    tok = torch.empty(B, N, dtype=torch.int32, device="cuda")
+    pos = torch.empty_like(tok)
+    o = torch.empty_like(d["q"])
+    maxP = max(cfg.P)
+    ws_a = torch.empty(M.tree_attention_workspace_size(tree, B, cfg.nH, cfg.D, maxP, wdt), dtype=torch.uint8,
+                       device="cuda")
+    g = torch.empty(B * N, dtype=torch.int32, device="cuda")
+    ws_g = torch.empty(M.base_greedy_workspace_size(B * N, H, V, wdt), dtype=torch.uint8, device="cuda")
+    al = torch.empty(B, dtype=torch.int32, device="cuda")
+    an = torch.empty(B, tree.max_depth + 1, dtype=torch.int32, device="cuda")
+    ot = torch.empty_like(an)
+    ncl = torch.empty(B, dtype=torch.int32, device="cuda")
+    M.medusa_resid_silu(d["h"], d["W1"], d["b1"], z)
+    M.medusa_vocab_topk(z, d["W2"], topk, ti, tv, ws=ws_v)
+    M.medusa_build_tree(tree, ti, dev(root), d["cache_len"], tok, pos)
+    M.tree_attention_verify(d["q"], d["k_tree"], d["v_tree"], d["k_cache"], d["v_cache"], d["cache_len"], maxP, tree, o,
+                            ws=ws_a)
+    M.medusa_base_greedy(o, d["lm_head"], g, ws=ws_g)
+    M.medusa_accept(tree, tok, g.view(B, N), al, an, ot, d["cache_len"], ncl, k_cache=d["k_cache"],
+                    v_cache=d["v_cache"])
+    torch.cuda.synchronize()
+    out = dict(z=host_f64(z), topk_idx=ti.cpu().numpy(), topk_val=host_f64(tv), node_tok=tok.cpu().numpy(),
+               node_pos=pos.cpu().numpy(), o=host_f64(o), greedy=g.view(B, N).cpu().numpy(),
+               accept_len=al.cpu().numpy(), accept_nodes=an.cpu().numpy(), out_tokens=ot.cpu().numpy(),
+               new_cache_len=ncl.cpu().numpy(), k_cache=d["k_cache"], v_cache=d["v_cache"])
+    del d
+    return out
+
+
+def oracle_attention_seqs(cfg, att, seqs):
+    """Oracle tree attention for every node and head of the listed sequences,
+    rounded like the boundary's output type: {b: o[N][nH][D]}."""
+    dt = cfg.dtype
+    parent, _ = cfg.tree.arrays()
+    scale = float(np.float32(1.0 / np.sqrt(cfg.D)))
+    res = {}
+    for b in seqs:
+        sl = slice(b, b + 1)
+        w = {k: oracle.widen(att[k][sl], dt) for k in ("q", "k_tree", "v_tree", "k_cache", "v_cache")}
+        o = oracle.tree_attention(w["q"], w["k_tree"], w["v_tree"], w["k_cache"], w["v_cache"],
+                                  np.asarray(att["cache_len"])[sl], parent, scale)[0]
+        res[b] = oracle.round_bf16(o) if dt == "bf16" else o
+    return res
