@@ -1,0 +1,95 @@
+"""The whole step captured in a HIP graph: every replay must reproduce the
+eager step bit for bit (the kernels are deterministic).  Replays are separated
+by eager work and synchronisations, and every replay is checked."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import medusa_inputs as mi
+from medusa_testlib import dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def test_step_graph_replays_match_eager():
+    import speculative_decoding_medusa_amd as M
+    _say("graph step")
+    cfg = mi.custom_config("graph", "bf16", 2, 1024, 5003, 5, 4, mi.sparse_tree(64), 8, 8, 128, (300, 517), 401)
+    heads = mi.gen_heads(cfg)
+    att = mi.gen_attention(cfg)
+    root = mi.gen_root_tokens(cfg)
+    d = {k: dev(v) for k, v in {**heads, **att}.items()}
+    kc0, vc0 = d["k_cache"].clone(), d["v_cache"].clone()
+    B, K, H, V, N, topk = cfg.B, cfg.K, cfg.H, cfg.V, cfg.N, cfg.topk
+    parent, rank = cfg.tree.arrays()
+    tree = M.Tree(parent, rank, K, topk)
+    wdt = M.BF16
+    bufs = dict(
+        z=torch.empty(B, K, H, device="cuda"),
+        ti=torch.empty(B, K, topk, dtype=torch.int32, device="cuda"),
+        tv=torch.empty(B, K, topk, device="cuda"),
+        tok=torch.empty(B, N, dtype=torch.int32, device="cuda"),
+        pos=torch.empty(B, N, dtype=torch.int32, device="cuda"),
+        o=torch.empty_like(d["q"]),
+        g=torch.empty(B * N, dtype=torch.int32, device="cuda"),
+        al=torch.empty(B, dtype=torch.int32, device="cuda"),
+        an=torch.empty(B, tree.max_depth + 1, dtype=torch.int32, device="cuda"),
+        ot=torch.empty(B, tree.max_depth + 1, dtype=torch.int32, device="cuda"),
+        ncl=torch.empty(B, dtype=torch.int32, device="cuda"),
+    )
+    maxP = max(cfg.P)
+    ws_v = torch.empty(M.vocab_topk_workspace_size(B, H, V, K, topk, wdt), dtype=torch.uint8, device="cuda")
+    ws_a = torch.empty(M.tree_attention_workspace_size(tree, B, cfg.nH, cfg.D, maxP, wdt), dtype=torch.uint8,
+                       device="cuda")
+    ws_g = torch.empty(M.base_greedy_workspace_size(B * N, H, V, wdt), dtype=torch.uint8, device="cuda")
+    root_d = dev(root)
+
+    def step():
+        b = bufs
+        M.medusa_resid_silu(d["h"], d["W1"], d["b1"], b["z"])
+        M.medusa_vocab_topk(b["z"], d["W2"], topk, b["ti"], b["tv"], ws=ws_v)
+        M.medusa_build_tree(tree, b["ti"], root_d, d["cache_len"], b["tok"], b["pos"])
+        M.tree_attention_verify(d["q"], d["k_tree"], d["v_tree"], d["k_cache"], d["v_cache"], d["cache_len"], maxP,
+                                tree, b["o"], ws=ws_a)
+        M.medusa_base_greedy(b["o"], d["lm_head"], b["g"], ws=ws_g)
+        M.medusa_accept(tree, b["tok"], b["g"].view(B, N), b["al"], b["an"], b["ot"], d["cache_len"], b["ncl"],
+                        k_cache=d["k_cache"], v_cache=d["v_cache"])
+
+    def snapshot():
+        torch.cuda.synchronize()
+        s = {k: v.clone() for k, v in bufs.items()}
+        s["k_cache"] = d["k_cache"].clone()
+        s["v_cache"] = d["v_cache"].clone()
+        return s
+
+    step()
+    ref = snapshot()
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(4):
+        # clobber every output and restore the caches with eager work between replays
+        for v in bufs.values():
+            v.fill_(7 if v.dtype == torch.int32 else -3)
+        d["k_cache"].copy_(kc0)
+        d["v_cache"].copy_(vc0)
+        torch.cuda.synchronize()
+        graph.replay()
+        got = snapshot()
+        for k in ref:
+            assert torch.equal(got[k], ref[k]), f"replay {rep}: {k} differs from the eager step"
+    _say("replays ok")
