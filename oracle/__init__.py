@@ -24,9 +24,16 @@ Sources, cited by page title and section (the pages are public web text):
 Every function below states the passage it follows.  Where the pages are silent
 the reading taken is named in the docstring (and listed in the design doc).
 
+The tree-verify pass through a Llama-shaped decoder (``decoder.py``) follows
+the same section: the verify pass is the base model's forward pass over all
+candidates with the ancestor mask.
+
 Parity status: every function here is pinned by a ``-m "not gpu"`` test against
-something other than itself (printed values, closed forms, special cases or
-brute force); see tests/test_oracle_*.py.
+something other than itself (printed values, closed forms, special cases,
+brute force, or an independent implementation: the decoder against Hugging
+Face transformers' Llama run causally on every branch); see
+tests/test_oracle_*.py.
 """
 from .medusa import *  # noqa: F401,F403
 from .cost import *    # noqa: F401,F403
+from .decoder import *  # noqa: F401,F403
