@@ -192,6 +192,57 @@ medusa_status medusa_accept(const medusa_tree* tree, const int32_t* node_tok, co
                             int nKV, int D, int Lmax, medusa_dtype dt, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Step a8 -- the tree-verify forward pass through a Llama-shaped decoder
+ * ("Medusa Heads" glossary, section on tree attention and acceptance: every
+ * candidate is appended to the input of one forward pass of the base model,
+ * each token attending only to its tree ancestors).  The decoder internals are
+ * not on the pages; this is the standard pre-norm Llama layer:
+ *   n = RMSNorm(x); q, k = RoPE(W_q n), RoPE(W_k n) at position node_pos;
+ *   v = W_v n; o = tree attention of q over the layer's cache prefix plus the
+ *   node's ancestors-or-self (the tree keys/values are written to cache slots
+ *   cache_len .. cache_len + N - 1 of the layer, as tree_attention_verify
+ *   does); x += W_o o; n' = RMSNorm(x); x += W_down (SiLU(W_gate n') *
+ *   (W_up n')); after the last layer greedy = argmax_v lm_head[v] .
+ *   RMSNorm(x), lower index first among equal values.
+ *   RMSNorm: unit weight, x * rsqrt(mean(x^2) + rms_eps).  RoPE rotates the
+ *   pair (i, i + D/2) of every head by node_pos * rope_base^(-2i/D).
+ *   x starts as embedding[node_tok] and is kept in float32; the normalised
+ *   rows, q/k/v, the attention output and the SwiGLU product are rounded to
+ *   bf16 (nearest even) before they enter the next product.
+ * Arguments (bf16 only; device pointers unless noted):
+ *   layers (host array [n_layers]): weights in the [out][in] layout, bf16:
+ *     wq [nH*D][H], wk and wv [nKV*D][H], wo [H][nH*D], w_gate and w_up [F][H],
+ *     w_down [H][F];  embedding and lm_head [V][H];
+ *   node_tok, node_pos [B][N] int32 (medusa_build_tree's outputs; token ids
+ *     outside [0, V) read row 0 of the embedding);  cache_len [B];
+ *   k_cache / v_cache: n_layers caches, layer l at base + l * layer_stride_elems,
+ *     each [B][nKV][Lmax][D];
+ *   greedy [B][N] int32 (output); hidden [B][N][H] float32, optional: the
+ *     final normalised rows (bf16 values) that lm_head scores.
+ * Limits: H == nH * D, D in {64, 128}, H and F multiples of 256 (of
+ *   512 / ceil(B*N/16) above 64 nodes), B*N <= 256, H <= 16384.
+ *   The workspace must not be shared by calls that may run concurrently.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+    const void* wq;
+    const void* wk;
+    const void* wv;
+    const void* wo;
+    const void* w_gate;
+    const void* w_up;
+    const void* w_down;
+} medusa_layer_weights;
+
+size_t medusa_decoder_workspace_size(const medusa_tree* tree, int B, int H, int nH, int nKV, int D, int F, int V,
+                                     int max_cache_len);
+medusa_status medusa_decoder_verify(const medusa_layer_weights* layers, int n_layers, const void* embedding,
+                                    const void* lm_head, const medusa_tree* tree, const int32_t* node_tok,
+                                    const int32_t* node_pos, const int32_t* cache_len, int max_cache_len,
+                                    void* k_cache, void* v_cache, int64_t layer_stride_elems, int B, int H, int nH,
+                                    int nKV, int D, int F, int V, int Lmax, float rms_eps, float rope_base,
+                                    int32_t* greedy, float* hidden, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Kernel timing: while enabled, every kernel launch of the library is
  * bracketed by HIP events on its stream.  medusa_profiler_collect waits for
  * the recorded events and folds them into per-kernel totals; ..._stat reads

@@ -48,6 +48,9 @@ _SIGS = {
     "medusa_base_greedy": ([_vp, _vp, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
     "medusa_accept": ([_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32,
                        _vp], _i32),
+    "medusa_decoder_workspace_size": ([_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32], _sz),
+    "medusa_decoder_verify": ([_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
+                               _i32, _i32, _i32, _i32, _f32, _f32, _vp, _vp, _vp, _sz, _vp], _i32),
     "medusa_profiler_enable": ([_i32], _i32),
     "medusa_profiler_reset": ([], _i32),
     "medusa_profiler_collect": ([], _i32),
@@ -246,6 +249,40 @@ def medusa_accept(tree: Tree, node_tok, greedy, accept_len, accept_nodes, out_to
         tree.handle, _p(node_tok), _p(greedy), B, _p(accept_len), _p(accept_nodes), _p(out_tokens), _p(cache_len),
         _p(new_cache_len), _p(k_cache), _p(v_cache), n_layers, stride, nKV, D, Lmax, dt, _stream(stream)))
     return accept_len
+
+
+# ---------------------------------------------------------------------------
+# a8
+# ---------------------------------------------------------------------------
+
+class LayerWeights(ctypes.Structure):
+    """medusa_layer_weights: device pointers of one decoder layer's matrices."""
+    _fields_ = [(n, ctypes.c_void_p) for n in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")]
+
+
+def decoder_workspace_size(tree: Tree, B, H, nH, nKV, D, F, V, max_cache_len):
+    return _lib.medusa_decoder_workspace_size(tree.handle, B, H, nH, nKV, D, F, V, max_cache_len)
+
+
+def medusa_decoder_verify(layers, embedding, lm_head, tree: Tree, node_tok, node_pos, cache_len, max_cache_len: int,
+                          k_cache, v_cache, nH: int, greedy, hidden=None, rms_eps=1e-6, rope_base=10000.0, ws=None,
+                          stream=None):
+    """layers: list of dicts of bf16 tensors (wq, wk, wv, wo, w_gate, w_up, w_down);
+    k_cache / v_cache: [layers][B][nKV][Lmax][D] bf16."""
+    n_layers, B, nKV, Lmax, D = k_cache.shape
+    V, H = embedding.shape
+    F = layers[0]["w_gate"].shape[0]
+    arr = (LayerWeights * len(layers))()
+    for i, W in enumerate(layers):
+        arr[i] = LayerWeights(*[W[n].data_ptr() for n in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")])
+    need = decoder_workspace_size(tree, B, H, nH, nKV, D, F, V, max_cache_len)
+    ws = _ws(need, embedding.device, ws)
+    _check("medusa_decoder_verify", _lib.medusa_decoder_verify(
+        ctypes.cast(arr, ctypes.c_void_p), len(layers), _p(embedding), _p(lm_head), tree.handle, _p(node_tok),
+        _p(node_pos), _p(cache_len), int(max_cache_len), _p(k_cache), _p(v_cache), k_cache.stride(0), B, H, nH, nKV,
+        D, F, V, Lmax, float(rms_eps), float(rope_base), _p(greedy), _p(hidden), _p(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
+    return greedy
 
 
 # ---------------------------------------------------------------------------

@@ -42,6 +42,16 @@ void launch_accept(const TreeDev& t, const int32_t* node_tok, const int32_t* gre
                    void* k_cache, void* v_cache, int n_layers, int64_t layer_stride, int nKV, int D, int Lmax,
                    bool bf16, hipStream_t s);
 
+struct LayerPtrs {
+    const bf16_t *wq, *wk, *wv, *wo, *w_gate, *w_up, *w_down;
+};
+size_t decoder_workspace_bytes(int B, int N, int H, int nH, int nKV, int D, int F, int V, int max_cache_len);
+void launch_decoder_verify(const LayerPtrs* layers, int n_layers, const bf16_t* E, const bf16_t* lm_head,
+                           const TreeDev& t, const int32_t* node_tok, const int32_t* node_pos,
+                           const int32_t* cache_len, int max_cache_len, bf16_t* k_cache, bf16_t* v_cache,
+                           int64_t layer_stride, int B, int H, int nH, int nKV, int D, int F, int V, int Lmax,
+                           float eps, float rope_base, int32_t* greedy, float* hidden, void* ws, hipStream_t s);
+
 // ---------------------------------------------------------------------------
 // errors
 // ---------------------------------------------------------------------------
@@ -424,6 +434,56 @@ medusa_status medusa_accept(const medusa_tree* tree, const int32_t* node_tok, co
         launch_accept(tree->t, node_tok, greedy, B, accept_len, accept_nodes, out_tokens, cache_len, new_cache_len,
                       k_cache, v_cache, n_layers, layer_stride_elems, nKV, D, Lmax, dt == MEDUSA_BF16,
                       (hipStream_t)stream);
+    });
+}
+
+// ---------------------------------------------------------------------------
+// a8 decoder verify
+// ---------------------------------------------------------------------------
+size_t medusa_decoder_workspace_size(const medusa_tree* tree, int B, int H, int nH, int nKV, int D, int F, int V,
+                                     int max_cache_len) {
+    if (!tree || B < 1 || H < 1 || nH < 1 || nKV < 1 || D < 1 || F < 1 || V < 1 || max_cache_len < 0) return 0;
+    return decoder_workspace_bytes(B, tree->t.N, H, nH, nKV, D, F, V, max_cache_len);
+}
+
+medusa_status medusa_decoder_verify(const medusa_layer_weights* layers, int n_layers, const void* embedding,
+                                    const void* lm_head, const medusa_tree* tree, const int32_t* node_tok,
+                                    const int32_t* node_pos, const int32_t* cache_len, int max_cache_len,
+                                    void* k_cache, void* v_cache, int64_t layer_stride_elems, int B, int H, int nH,
+                                    int nKV, int D, int F, int V, int Lmax, float rms_eps, float rope_base,
+                                    int32_t* greedy, float* hidden, void* ws, size_t ws_bytes, void* stream) {
+    return guarded("medusa_decoder_verify", [&] {
+        REQUIRE(layers && embedding && lm_head && tree && node_tok && node_pos && cache_len && k_cache && v_cache &&
+                    greedy && ws,
+                "null pointer argument");
+        REQUIRE(n_layers >= 1 && B >= 1 && H >= 1 && nH >= 1 && nKV >= 1 && D >= 1 && F >= 1 && V >= 1,
+                "sizes must be positive");
+        REQUIRE(nH % nKV == 0, "need nH %% nKV == 0 (nH=%d nKV=%d)", nH, nKV);
+        SUPPORT(H == nH * D, "H=%d must equal nH*D=%d", H, nH * D);
+        SUPPORT(D == 64 || D == 128, "D=%d not in {64, 128}", D);
+        const int R = B * tree->t.N;
+        SUPPORT(R <= MEDUSA_MAX_TREE_NODES, "B*N=%d exceeds %d", R, MEDUSA_MAX_TREE_NODES);
+        const int kc = R <= 64 ? 256 : R <= 128 ? 64 : 32;
+        SUPPORT(H % kc == 0 && F % kc == 0, "H=%d and F=%d must be multiples of %d", H, F, kc);
+        SUPPORT(H <= 16384, "H=%d exceeds 16384", H);
+        REQUIRE(rms_eps >= 0.f && rope_base > 1.f, "need rms_eps >= 0 and rope_base > 1");
+        REQUIRE(max_cache_len >= 0 && max_cache_len + tree->t.N <= Lmax,
+                "max_cache_len + N = %d exceeds Lmax = %d", max_cache_len + tree->t.N, Lmax);
+        REQUIRE(layer_stride_elems >= (int64_t)B * nKV * Lmax * D || n_layers == 1,
+                "layer stride smaller than one layer's cache");
+        std::vector<LayerPtrs> L((size_t)n_layers);
+        for (int l = 0; l < n_layers; ++l) {
+            const medusa_layer_weights& w = layers[l];
+            REQUIRE(w.wq && w.wk && w.wv && w.wo && w.w_gate && w.w_up && w.w_down, "layer %d: null weight", l);
+            L[l] = LayerPtrs{(const bf16_t*)w.wq, (const bf16_t*)w.wk, (const bf16_t*)w.wv, (const bf16_t*)w.wo,
+                             (const bf16_t*)w.w_gate, (const bf16_t*)w.w_up, (const bf16_t*)w.w_down};
+        }
+        const size_t need = medusa_decoder_workspace_size(tree, B, H, nH, nKV, D, F, V, max_cache_len);
+        REQUIRE(ws_bytes >= need, "workspace too small: %zu < %zu", ws_bytes, need);
+        launch_decoder_verify(L.data(), n_layers, (const bf16_t*)embedding, (const bf16_t*)lm_head, tree->t, node_tok,
+                              node_pos, cache_len, max_cache_len, (bf16_t*)k_cache, (bf16_t*)v_cache,
+                              layer_stride_elems, B, H, nH, nKV, D, F, V, Lmax, rms_eps, rope_base, greedy, hidden, ws,
+                              (hipStream_t)stream);
     });
 }
 

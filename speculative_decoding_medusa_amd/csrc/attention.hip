@@ -195,19 +195,24 @@ __global__ __launch_bounds__(D) void tree_attn_combine_kernel(const float* __res
 
 // ---------------------------------------------------------------------------
 // bf16 MFMA variant.  The same split-KV decomposition, with the contractions
-// on v_mfma_f32_16x16x32_bf16 in transposed form so that no register data has
-// to move between lanes:
-//   S^T[key][q] = K . Q^T   (A = K tile rows from LDS, B = the wave's Q rows
-//                            held in registers for the whole kernel);
+// on MFMA in transposed form so that no register data has to move between
+// lanes:
+//   S^T[key][q] = K . Q^T   (v_mfma_f32_16x16x32_bf16; A = K tile rows from
+//                            LDS, B = the wave's Q rows held in registers for
+//                            the whole kernel);
 //   the output layout gives each lane 4 consecutive keys of one query per
 //   16-key block, exactly the 8 values the next product needs as its B
 //   operand, so P^T never leaves the lane;
-//   O^T[d][q] += V^T . P^T (A = V^T from an LDS tile stored transposed,
-//                            [d][key]; the contraction runs over the keys in a
-//                            fixed permuted order, the same for both operands).
+//   O^T[d][q] += V^T . P^T (v_mfma_f32_16x16x32_f16; A = V^T from an LDS tile
+//                            stored transposed, [d][key], widened to fp16; B =
+//                            the probabilities rounded to fp16, whose 11-bit
+//                            significand keeps the weighted sum 8x closer to
+//                            the exact one than bf16 would; the contraction
+//                            runs over the keys in a fixed permuted order, the
+//                            same for both operands).
 // The online-softmax state of query q lives in the 4 lanes that hold column q.
-// Tiles of 64 keys are staged in LDS by the whole workgroup, the next tile
-// prefetched into registers while the current one is consumed.
+// Tiles of 64 keys are staged in LDS by the whole workgroup, up to three tiles
+// in flight in a register ring.
 // ---------------------------------------------------------------------------
 constexpr int MF_TK = 64;
 
@@ -226,7 +231,7 @@ __global__ __launch_bounds__(WAVES * 64) void tree_attn_mfma_kernel(
     constexpr int PT = CH / NT;     // chunks per thread
     constexpr int DC = D / 8;       // chunks per key row
     __shared__ __attribute__((aligned(16))) bf16_t Ks[TK][D + 8];
-    __shared__ __attribute__((aligned(16))) bf16_t Vt[D][TK + 4];  // 136-byte rows: 4-way write conflicts at most
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[D][TK + 4];  // fp16 bits; 136-byte rows: 4-way write conflicts at most
 
     const int bh = blockIdx.x;
     const int b = bh / nH, h = bh - b * nH;
@@ -313,22 +318,26 @@ __global__ __launch_bounds__(WAVES * 64) void tree_attn_mfma_kernel(
             }
         }
     };
-    // K -> LDS row-major; V transposed in registers (v_perm_b32 pairs the same
-    // column of two keys) and written as KPT-key runs of each row of Vt.
+    // K -> LDS row-major (bf16); V widened to fp16 (exact for every bf16 value
+    // of magnitude >= 2^-14; smaller ones move by < 2^-25), transposed in
+    // registers and written as KPT-key runs of each row of Vt.
     auto store_tile = [&](const u32x4(&kr)[KPT], const u32x4(&vr)[KPT]) {
 #pragma unroll
         for (int e = 0; e < KPT; ++e) *(u32x4*)(&Ks[kg * KPT + e][dc * 8]) = kr[e];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {  // column dc * 8 + i
-            const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-            uint32_t w[KPT / 2 > 0 ? KPT / 2 : 1];
+            float f[KPT];
 #pragma unroll
-            for (int e = 0; e + 1 < KPT; e += 2)
-                w[e / 2] = __builtin_amdgcn_perm(vr[e + 1][i >> 1], vr[e][i >> 1], sel);
-            bf16_t* dst = &Vt[dc * 8 + i][kg * KPT];
-            if (KPT == 4) *(uint2*)dst = (uint2){w[0], w[1]};
-            else if (KPT == 2) *(uint32_t*)dst = w[0];
-            else *dst = (bf16_t)((i & 1) ? (vr[0][i >> 1] >> 16) : (vr[0][i >> 1] & 0xFFFFu));
+            for (int e = 0; e < KPT; ++e)
+                f[e] = (i & 1) ? bf16_hi(vr[e][i >> 1]) : bf16_lo(vr[e][i >> 1]);
+            uint16_t* dst = &Vt[dc * 8 + i][kg * KPT];
+            if (KPT == 4) {
+                *(uint2*)dst = (uint2){pack_f16x2(f[0], f[1]), pack_f16x2(f[2 % KPT], f[3 % KPT])};
+            } else if (KPT == 2) {
+                *(uint32_t*)dst = pack_f16x2(f[0], f[1 % KPT]);
+            } else {
+                *dst = (uint16_t)(pack_f16x2(f[0], 0.f) & 0xFFFFu);
+            }
         }
     };
 #pragma unroll
@@ -397,7 +406,7 @@ __global__ __launch_bounds__(WAVES * 64) void tree_attn_mfma_kernel(
             const bool live = m_new != -INFINITY;
             const float alpha = live ? exp2f(m[qb] - m_new) : 1.f;
             float psum = 0.f;
-            uint32_t pk[KB][2];  // bf16 pairs of P^T (round to nearest even)
+            uint32_t pk[KB][2];  // fp16 pairs of P^T (round to nearest even)
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 float p4[4];
@@ -406,8 +415,8 @@ __global__ __launch_bounds__(WAVES * 64) void tree_attn_mfma_kernel(
                     p4[r] = live ? exp2f(st[kb][r] - m_new) : 0.f;
                     psum += p4[r];
                 }
-                pk[kb][0] = pack_bf16x2(p4[0], p4[1]);
-                pk[kb][1] = pack_bf16x2(p4[2], p4[3]);
+                pk[kb][0] = pack_f16x2(p4[0], p4[1]);
+                pk[kb][1] = pack_f16x2(p4[2], p4[3]);
             }
             psum += __shfl_xor(psum, 16, 64);
             psum += __shfl_xor(psum, 32, 64);
@@ -423,9 +432,9 @@ __global__ __launch_bounds__(WAVES * 64) void tree_attn_mfma_kernel(
                     const uint2 lo = *(const uint2*)(&Vt[db * 16 + lr][k2 * 32 + lk * 4]);
                     const uint2 hi = *(const uint2*)(&Vt[db * 16 + lr][k2 * 32 + 16 + lk * 4]);
                     const u32x4 av = (u32x4){lo.x, lo.y, hi.x, hi.y};
-                    o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                                        __builtin_bit_cast(bf16x8, bp), o[qb][db], 0,
-                                                                        0, 0);
+                    o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av),
+                                                                       __builtin_bit_cast(f16x8, bp), o[qb][db], 0,
+                                                                       0, 0);
                 }
             }
         }

@@ -48,6 +48,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
+// Two floats -> packed fp16 pair (low half = lo), round to nearest even, in
+// one v_cvt_pk_f16_f32.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
     static constexpr int PER16 = 4;  // elements per 16-byte chunk

@@ -1,0 +1,278 @@
+// The tree-verify forward pass through a Llama-shaped decoder: every tree
+// token runs through every layer at once, each attending to the layer's KV
+// prefix plus its own tree ancestors, and the base model's greedy choice is
+// taken after every node.
+//
+// Per layer (pre-norm): n = bf16(RMSNorm(x)); [q|k|v] = n W_qkv^T with RoPE
+// on q and k at position cache_len + depth; o = tree attention (which also
+// writes the tree keys/values into the layer's cache slots P..P+N-1);
+// x += o W_o^T; n' = bf16(RMSNorm(x)); a = bf16(SiLU(n' W_gate^T) * (n' W_up^T));
+// x += a W_down^T.  The residual stream x is float32; RMSNorm has unit
+// weight.  After the last layer: greedy = argmax lm_head . bf16(RMSNorm(x)).
+//
+// The projections are skinny products (R = B*N <= 256 node rows against
+// 4096-22016 weight rows): the weight matrix streams once from HBM through
+// skinny_mfma_kernel, split along the contraction so that every matrix
+// launches about 512 workgroups; each split writes fp32 partial sums and a
+// small epilogue kernel adds them and applies RoPE, the residual or SwiGLU.
+#include <algorithm>
+
+#include "common.hpp"
+#include "skinny_mfma.hpp"
+#include "tree.hpp"
+
+namespace medusa {
+
+void launch_tree_attention(const void* q, const void* k_tree, const void* v_tree, void* k_cache, void* v_cache,
+                           const int32_t* cache_len, int max_cache_len, const TreeDev& t, int B, int nH,
+                           int nKV, int D, int Lmax, float scale, bool bf16, void* out, float* part_o,
+                           float* part_ml, hipStream_t s, int target_wg);
+size_t attn_workspace_bytes(int B, int nH, int N, int D, int max_cache_len, bool bf16);
+void attn_carve(int B, int nH, int N, int D, int max_cache_len, bool bf16, void* ws, float** part_o,
+                float** part_ml);
+size_t lm_head_greedy_workspace_bytes(int R, int H, int V);
+void launch_lm_head_greedy(const bf16_t* n, const bf16_t* lm_head, int R, int H, int V, int32_t* greedy,
+                           void* ws, hipStream_t s);
+
+// x[r][:] = embedding[tok[r]] (fp32); ids outside [0, V) read row 0.
+__global__ __launch_bounds__(256) void embed_rows_kernel(const int32_t* __restrict__ tok, const bf16_t* __restrict__ E,
+                                                         int H, int V, float* __restrict__ x) {
+    const int r = blockIdx.x;
+    int t = tok[r];
+    if (t < 0 || t >= V) t = 0;
+    const bf16_t* e = E + (size_t)t * H;
+    for (int j = threadIdx.x * 8; j < H; j += 256 * 8) {
+        float v[8];
+        Elem<bf16_t>::expand(*(const u32x4*)(e + j), v);
+        *(f32x4*)(x + (size_t)r * H + j) = (f32x4){v[0], v[1], v[2], v[3]};
+        *(f32x4*)(x + (size_t)r * H + j + 4) = (f32x4){v[4], v[5], v[6], v[7]};
+    }
+}
+
+// n[r][:] = bf16(x[r][:] * rsqrt(mean(x[r]^2) + eps)), x fp32.
+__global__ __launch_bounds__(256) void rmsnorm_f32_bf16_kernel(const float* __restrict__ x, int H, float eps,
+                                                               bf16_t* __restrict__ n) {
+    __shared__ float red[4];
+    const int r = blockIdx.x;
+    const float* xr = x + (size_t)r * H;
+    float ss = 0.f;
+    for (int j = threadIdx.x * 4; j < H; j += 256 * 4) {
+        const f32x4 v = *(const f32x4*)(xr + j);
+        ss = fmaf(v.x, v.x, ss);
+        ss = fmaf(v.y, v.y, ss);
+        ss = fmaf(v.z, v.z, ss);
+        ss = fmaf(v.w, v.w, ss);
+    }
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float rs = rsqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)H + eps);
+    for (int j = threadIdx.x * 4; j < H; j += 256 * 4) {
+        const f32x4 v = *(const f32x4*)(xr + j);
+        *(uint2*)(n + (size_t)r * H + j) = (uint2){(uint32_t)f32_to_bf16(v.x * rs) | ((uint32_t)f32_to_bf16(v.y * rs) << 16),
+                                                   (uint32_t)f32_to_bf16(v.z * rs) | ((uint32_t)f32_to_bf16(v.w * rs) << 16)};
+    }
+}
+
+// out[e] = float(in[e])
+__global__ __launch_bounds__(256) void widen_bf16_kernel(const bf16_t* __restrict__ in, size_t n, float* __restrict__ out) {
+    for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x)
+        out[e] = bf16_to_f32(in[e]);
+}
+
+__device__ __forceinline__ float sum_splits(const float* __restrict__ part, int S, size_t stride, size_t off) {
+    float v = 0.f;
+    for (int s = 0; s < S; ++s) v += part[(size_t)s * stride + off];
+    return v;
+}
+
+// Sum the q|k|v partials of node r, rotate q and k (pair (i, i + D/2) of a
+// head by pos * base^(-2i/D); the angle and its sine and cosine in double),
+// and store bf16 q [R][nH][D], k and v [R][nKV][D].
+__global__ __launch_bounds__(256) void qkv_rope_kernel(const float* __restrict__ part, int S, int R, int nH, int nKV,
+                                                       int D, const int32_t* __restrict__ pos, float log2_base,
+                                                       bf16_t* __restrict__ q, bf16_t* __restrict__ k,
+                                                       bf16_t* __restrict__ v) {
+    const int r = blockIdx.x;
+    const int ncols = (nH + 2 * nKV) * D;
+    const size_t stride = (size_t)R * ncols;
+    const int half = D / 2;
+    const double p = (double)pos[r];
+    for (int e = threadIdx.x; e < (nH + nKV) * half; e += blockDim.x) {
+        const int head = e / half, i = e - head * half;  // heads 0..nH-1 are q, then the nKV k heads
+        const int c0 = head * D + i;
+        const float x1 = sum_splits(part, S, stride, (size_t)r * ncols + c0);
+        const float x2 = sum_splits(part, S, stride, (size_t)r * ncols + c0 + half);
+        const double ang = p * exp2(-2.0 * (double)i / (double)D * (double)log2_base);
+        double sn, cs;
+        sincos(ang, &sn, &cs);
+        const float c = (float)cs, sg = (float)sn;
+        const float y1 = x1 * c - x2 * sg;
+        const float y2 = x2 * c + x1 * sg;
+        bf16_t* dst = head < nH ? q + ((size_t)r * nH + head) * D : k + ((size_t)r * nKV + (head - nH)) * D;
+        dst[i] = f32_to_bf16(y1);
+        dst[i + half] = f32_to_bf16(y2);
+    }
+    for (int e = threadIdx.x; e < nKV * D; e += blockDim.x) {
+        const float x = sum_splits(part, S, stride, (size_t)r * ncols + (nH + nKV) * D + e);
+        v[(size_t)r * nKV * D + e] = f32_to_bf16(x);
+    }
+}
+
+// x[e] += sum of the S partials of element e (x and each partial [R][H]).
+__global__ __launch_bounds__(256) void residual_add_kernel(const float* __restrict__ part, int S, size_t n,
+                                                           float* __restrict__ x) {
+    for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x)
+        x[e] += sum_splits(part, S, n, e);
+}
+
+// a[r][c] = bf16(SiLU(g) * u) with g = column c and u = column F + c of the
+// summed gate|up partials [R][2F].
+__global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ part, int S, int R, int F,
+                                                     bf16_t* __restrict__ a) {
+    const size_t n = (size_t)R * F;
+    const size_t stride = (size_t)R * 2 * F;
+    for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
+        const size_t r = e / F, c = e - r * F;
+        const float g = sum_splits(part, S, stride, r * 2 * F + c);
+        const float u = sum_splits(part, S, stride, r * 2 * F + F + c);
+        a[e] = f32_to_bf16(g / (1.f + __expf(-g)) * u);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+struct GemmSplit {
+    int S;    // splits of the contraction
+    int cps;  // k-chunks per split
+};
+
+// about 512 workgroups per product, at most 16 splits, whole k-chunks
+static GemmSplit gemm_split(int R, int K, int ncols) {
+    const int nblk = lmh_nblk(R);
+    const int nchunk = K / lmh_kc(nblk);
+    const long long tiles = (long long)((ncols + LMH_ROWS - 1) / LMH_ROWS) * ((R + nblk * 16 - 1) / (nblk * 16));
+    int S = (int)((512 + tiles - 1) / tiles);
+    if (S > 16) S = 16;
+    if (S > nchunk) S = nchunk;
+    if (S < 1) S = 1;
+    const int cps = (nchunk + S - 1) / S;
+    return GemmSplit{(nchunk + cps - 1) / cps, cps};
+}
+
+static void launch_skinny_partial(const bf16_t* n, const WeightRows& w, int R, int K, int ncols, const GemmSplit& sp,
+                                  float* part, hipStream_t s, const char* name) {
+    const int nblk = lmh_nblk(R);
+    const dim3 grid((ncols + LMH_ROWS - 1) / LMH_ROWS, (R + nblk * 16 - 1) / (nblk * 16), sp.S);
+    if (nblk == 4)
+        MEDUSA_LAUNCH(name, (skinny_mfma_kernel<4, SKINNY_PARTIAL>), grid, dim3(256), 0, s, n, w, R, K, ncols, sp.cps,
+                      nullptr, nullptr, part);
+    else if (nblk == 8)
+        MEDUSA_LAUNCH(name, (skinny_mfma_kernel<8, SKINNY_PARTIAL>), grid, dim3(256), 0, s, n, w, R, K, ncols, sp.cps,
+                      nullptr, nullptr, part);
+    else
+        MEDUSA_LAUNCH(name, (skinny_mfma_kernel<16, SKINNY_PARTIAL>), grid, dim3(256), 0, s, n, w, R, K, ncols, sp.cps,
+                      nullptr, nullptr, part);
+}
+
+static size_t a256(size_t x) { return (x + 255) / 256 * 256; }
+
+struct DecoderWs {
+    float* x;
+    bf16_t *n, *q, *kt, *vt, *o, *a;
+    float* part;
+    float *att_o, *att_ml;
+    void* greedy_ws;
+};
+
+static size_t partial_floats(int R, int H, int nH, int nKV, int D, int F) {
+    size_t m = 0;
+    const int qkv = (nH + 2 * nKV) * D;
+    const GemmSplit a = gemm_split(R, H, qkv), b = gemm_split(R, nH * D, H), c = gemm_split(R, H, 2 * F),
+                    d = gemm_split(R, F, H);
+    m = std::max(m, (size_t)a.S * R * qkv);
+    m = std::max(m, (size_t)b.S * R * H);
+    m = std::max(m, (size_t)c.S * R * 2 * F);
+    m = std::max(m, (size_t)d.S * R * H);
+    return m;
+}
+
+size_t decoder_workspace_bytes(int B, int N, int H, int nH, int nKV, int D, int F, int V, int max_cache_len) {
+    const size_t R = (size_t)B * N;
+    return a256(R * H * 4) + a256(R * H * 2) + a256(R * nH * D * 2) + 2 * a256(R * nKV * D * 2) + a256(R * H * 2) +
+           a256(R * F * 2) + a256(partial_floats((int)R, H, nH, nKV, D, F) * 4) +
+           a256(attn_workspace_bytes(B, nH, N, D, max_cache_len, true)) + a256(lm_head_greedy_workspace_bytes((int)R, H, V));
+}
+
+static DecoderWs carve(void* ws, int B, int N, int H, int nH, int nKV, int D, int F, int max_cache_len) {
+    const size_t R = (size_t)B * N;
+    char* p = (char*)ws;
+    DecoderWs w;
+    w.x = (float*)p; p += a256(R * H * 4);
+    w.n = (bf16_t*)p; p += a256(R * H * 2);
+    w.q = (bf16_t*)p; p += a256(R * nH * D * 2);
+    w.kt = (bf16_t*)p; p += a256(R * nKV * D * 2);
+    w.vt = (bf16_t*)p; p += a256(R * nKV * D * 2);
+    w.o = (bf16_t*)p; p += a256(R * H * 2);
+    w.a = (bf16_t*)p; p += a256(R * F * 2);
+    w.part = (float*)p; p += a256(partial_floats((int)R, H, nH, nKV, D, F) * 4);
+    attn_carve(B, nH, N, D, max_cache_len, true, p, &w.att_o, &w.att_ml);
+    p += a256(attn_workspace_bytes(B, nH, N, D, max_cache_len, true));
+    w.greedy_ws = p;
+    return w;
+}
+
+struct LayerPtrs {
+    const bf16_t *wq, *wk, *wv, *wo, *w_gate, *w_up, *w_down;
+};
+
+void launch_decoder_verify(const LayerPtrs* layers, int n_layers, const bf16_t* E, const bf16_t* lm_head,
+                           const TreeDev& t, const int32_t* node_tok, const int32_t* node_pos,
+                           const int32_t* cache_len, int max_cache_len, bf16_t* k_cache, bf16_t* v_cache,
+                           int64_t layer_stride, int B, int H, int nH, int nKV, int D, int F, int V, int Lmax,
+                           float eps, float rope_base, int32_t* greedy, float* hidden, void* ws, hipStream_t s) {
+    const int N = t.N;
+    const int R = B * N;
+    const DecoderWs w = carve(ws, B, N, H, nH, nKV, D, F, max_cache_len);
+    const int qkv = (nH + 2 * nKV) * D;
+    const GemmSplit sp_qkv = gemm_split(R, H, qkv), sp_o = gemm_split(R, nH * D, H),
+                    sp_gu = gemm_split(R, H, 2 * F), sp_d = gemm_split(R, F, H);
+    const float scale = 1.0f / sqrtf((float)D);
+    const float log2_base = log2f(rope_base);
+    const int ew_blocks = 1024;
+
+    MEDUSA_LAUNCH("embed_rows", embed_rows_kernel, dim3(R), dim3(256), 0, s, node_tok, E, H, V, w.x);
+    for (int l = 0; l < n_layers; ++l) {
+        const LayerPtrs& L = layers[l];
+        bf16_t* kc = k_cache + (size_t)l * layer_stride;
+        bf16_t* vc = v_cache + (size_t)l * layer_stride;
+        MEDUSA_LAUNCH("rmsnorm_f32", rmsnorm_f32_bf16_kernel, dim3(R), dim3(256), 0, s, w.x, H, eps, w.n);
+        launch_skinny_partial(w.n, WeightRows{L.wq, L.wk, L.wv, nH * D, nKV * D}, R, H, qkv, sp_qkv, w.part, s,
+                              "dec_gemm_qkv");
+        MEDUSA_LAUNCH("qkv_rope", qkv_rope_kernel, dim3(R), dim3(256), 0, s, w.part, sp_qkv.S, R, nH, nKV, D, node_pos,
+                      log2_base, w.q, w.kt, w.vt);
+        launch_tree_attention(w.q, w.kt, w.vt, kc, vc, cache_len, max_cache_len, t, B, nH, nKV, D, Lmax, scale, true,
+                              w.o, w.att_o, w.att_ml, s, 0);
+        launch_skinny_partial(w.o, WeightRows{L.wo, nullptr, nullptr, H, 0}, R, nH * D, H, sp_o, w.part, s,
+                              "dec_gemm_o");
+        MEDUSA_LAUNCH("residual_add", residual_add_kernel, dim3(ew_blocks), dim3(256), 0, s, w.part, sp_o.S,
+                      (size_t)R * H, w.x);
+        MEDUSA_LAUNCH("rmsnorm_f32", rmsnorm_f32_bf16_kernel, dim3(R), dim3(256), 0, s, w.x, H, eps, w.n);
+        launch_skinny_partial(w.n, WeightRows{L.w_gate, L.w_up, nullptr, F, F}, R, H, 2 * F, sp_gu, w.part, s,
+                              "dec_gemm_gate_up");
+        MEDUSA_LAUNCH("swiglu", swiglu_kernel, dim3(ew_blocks), dim3(256), 0, s, w.part, sp_gu.S, R, F, w.a);
+        launch_skinny_partial(w.a, WeightRows{L.w_down, nullptr, nullptr, H, 0}, R, F, H, sp_d, w.part, s,
+                              "dec_gemm_down");
+        MEDUSA_LAUNCH("residual_add", residual_add_kernel, dim3(ew_blocks), dim3(256), 0, s, w.part, sp_d.S,
+                      (size_t)R * H, w.x);
+    }
+    MEDUSA_LAUNCH("rmsnorm_f32", rmsnorm_f32_bf16_kernel, dim3(R), dim3(256), 0, s, w.x, H, eps, w.n);
+    launch_lm_head_greedy(w.n, lm_head, R, H, V, greedy, w.greedy_ws, s);
+    if (hidden != nullptr) {
+        // the final normalised rows, widened to fp32
+        MEDUSA_LAUNCH("widen_rows", widen_bf16_kernel, dim3(ew_blocks), dim3(256), 0, s, w.n, (size_t)R * H, hidden);
+    }
+}
+
+}  // namespace medusa

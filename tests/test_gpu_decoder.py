@@ -1,0 +1,150 @@
+"""GPU parity of the tree-verify pass through the Llama-shaped decoder
+(medusa_decoder_verify) against the float64 decoder oracle on the same seeded
+inputs.
+
+Checked: the greedy choice after every node (bit-exact; lm_head rows are
+redrawn until every node's best two scores differ by >= 1e-2), the final
+normalised rows, and the rotated keys and values every layer writes into its
+cache slots P..P+N-1.
+
+Float bound.  Every layer rounds its normalised rows, q/k/v, attention output
+and SwiGLU product to bf16, and each rounding turns a difference far below
+one bf16 step into a whole step for the values it tips over.  Through stacked
+layers this cascade amplifies any float32-vs-float64 difference: with the
+oracle alone, multiplying the attention output of one full-width layer by
+(1 + 1.5e-4 * noise) -- the relative accuracy the GPU attention measures at --
+changes the residual stream by 0.3% of its RMS and the normalised rows by up
+to 0.031.  The float outputs of this multi-layer pass are therefore checked
+against max(4e-2, two bf16 steps) per element and 1% of the values' RMS for
+the RMS of the difference; the integer decisions stay exact.  Cases span the 64-, 128- and 256-row
+tile shapes of the projections, GQA, ragged cache lengths, and two layers at
+the full Llama-7B width (hidden 4096, 32 x 128 heads, MLP 11008, vocabulary
+32000, 4096-token caches, sparse 64-node tree).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import medusa_inputs as mi
+import oracle
+from medusa_testlib import GAP, dev, host_f64
+
+pytestmark = pytest.mark.gpu
+
+BF16_STEP = 2.0 ** -7
+
+
+def _close(got, ref):
+    np.testing.assert_allclose(got, ref, rtol=2 * BF16_STEP, atol=4e-2)
+    assert np.sqrt(np.mean((got - ref) ** 2)) <= 1e-2 * np.sqrt(np.mean(ref ** 2))
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def _cfg(name, B, H, V, tree, nH, nKV, D, P, seed, layers, ffn):
+    return mi.custom_config(name, "bf16", B, H, V, 5, 4, tree, nH, nKV, D, P, seed, layers=layers, ffn=ffn)
+
+
+CASES = [
+    ("tiny_tree_b2_ragged", lambda: _cfg("d1", 2, 256, 1000, mi.tiny_tree(), 4, 4, 64, (5, 40), 501, 2, 512)),
+    ("sparse24_gqa_3layers", lambda: _cfg("d2", 1, 512, 1500, mi.sparse_tree(24), 8, 2, 64, (100,), 502, 3, 768)),
+    ("rows128_b2_sparse64", lambda: _cfg("d3", 2, 256, 777, mi.sparse_tree(64), 2, 2, 128, (0, 33), 503, 2, 384)),
+    ("rows256_dense256", lambda: _cfg("d4", 1, 512, 3001, mi.dense_tree(256), 8, 8, 64, (64,), 504, 1, 320)),
+    ("full_width_2layers", lambda: _cfg("d5", 1, 4096, 32000, mi.sparse_tree(64), 32, 32, 128, (4096,), 505, 2, 11008)),
+]
+
+
+def _enforce_gap(cfg, lm_head, rows, gap=GAP, max_iter=1000):
+    """Redraw lm_head rows (from their override streams) until every row's
+    best two scores differ by >= gap.  rows: final normalised rows (float64)."""
+    lm = {"lm_head": lm_head}
+    ov = []
+    for _ in range(max_iter):
+        lg = (oracle.widen(lm_head, "bf16") @ rows.T).T
+        lg32 = oracle.round_f32(lg)
+        bad = set()
+        for r in range(lg.shape[0]):
+            top = np.lexsort((np.arange(lg.shape[1]), -lg32[r]))[:2]
+            if lg[r, top[0]] - lg[r, top[1]] < gap:
+                bad.add(int(top[1]))
+        if not bad:
+            return ov
+        for row in sorted(bad):
+            o = {"tensor": "lm_head", "row": row, "serial": len(ov)}
+            ov.append(o)
+            mi.apply_overrides(cfg, lm, [o])
+    raise RuntimeError("greedy gap enforcement did not converge")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,mk", CASES, ids=[c[0] for c in CASES])
+def test_decoder_verify_parity(name, mk):
+    import speculative_decoding_medusa_amd as M
+    cfg = mk()
+    _say("decoder", name, "layers", cfg.layers, "H", cfg.H, "F", cfg.ffn, "N", cfg.N, "P", cfg.P)
+    L, B, N = cfg.layers, cfg.B, cfg.N
+    layers = [mi.gen_layer(cfg, l) for l in range(L)]
+    caches = [mi.gen_layer_cache(cfg, l) for l in range(L)]
+    emb = mi.gen_embedding(cfg)
+    lm_head = mi.normal((cfg.V, cfg.H), cfg.seed, mi.S_LM_HEAD, mi.WEIGHT_SIGMA, "bf16")
+    tok = mi.uniform_int((B, N), cfg.seed, mi.S_TEST + 3, 0, cfg.V - 1)
+    P = np.asarray(cfg.P, dtype=np.int32)
+    parent, rank = cfg.tree.arrays()
+    node_pos = (P[:, None] + np.asarray(cfg.tree.depth, dtype=np.int32)[None, :]).astype(np.int32)
+
+    # oracle (float64, the kernels' bf16 rounding points mirrored)
+    wl = [{m: oracle.widen(W[m], "bf16") for m in W} for W in layers]
+    kc = [oracle.widen(c[0], "bf16") for c in caches]
+    vc = [oracle.widen(c[1], "bf16") for c in caches]
+    ref = oracle.decoder_verify(tok, P, parent, oracle.widen(emb, "bf16"), wl, oracle.widen(lm_head, "bf16"), kc, vc,
+                                cfg.nH, cfg.nKV, bf16=True)
+    del wl
+    ov = _enforce_gap(cfg, lm_head, ref["hidden"].reshape(B * N, cfg.H))
+    g_ref = np.argmax(oracle.round_f32(ref["hidden"].reshape(B * N, -1) @ oracle.widen(lm_head, "bf16").T), axis=1)
+    g_ref = g_ref.reshape(B, N).astype(np.int32)
+    _say("oracle done,", len(ov), "lm_head overrides")
+
+    # GPU
+    d_layers = [{m: dev(W[m]) for m in W} for W in layers]
+    k_cache = torch.stack([dev(c[0]) for c in caches])
+    v_cache = torch.stack([dev(c[1]) for c in caches])
+    tree = M.Tree(parent, rank, cfg.K, cfg.topk)
+    greedy = torch.empty(B, N, dtype=torch.int32, device="cuda")
+    hidden = torch.empty(B, N, cfg.H, device="cuda")
+    M.medusa_decoder_verify(d_layers, dev(emb), dev(lm_head), tree, dev(tok), dev(node_pos), dev(P), int(P.max()),
+                            k_cache, v_cache, cfg.nH, greedy, hidden=hidden)
+    torch.cuda.synchronize()
+
+    assert np.array_equal(greedy.cpu().numpy(), g_ref)
+    _close(host_f64(hidden), ref["hidden"])
+    kh, vh = host_f64(k_cache), host_f64(v_cache)
+    for l in range(L):
+        for b in range(B):
+            got_k = kh[l, b, :, P[b]:P[b] + N].transpose(1, 0, 2)   # [N][nKV][D]
+            got_v = vh[l, b, :, P[b]:P[b] + N].transpose(1, 0, 2)
+            _close(got_k, ref["k_tree"][l][b])
+            _close(got_v, ref["v_tree"][l][b])
+            # the prefix is never written
+            assert np.array_equal(kh[l, b, :, :P[b]], kc[l][b, :, :P[b]])
+    _say("ok")
+
+
+def test_decoder_argument_errors():
+    import speculative_decoding_medusa_amd as M
+    cfg = _cfg("e", 1, 256, 100, mi.tiny_tree(), 4, 4, 64, (5,), 510, 1, 300)   # F not a multiple of 256
+    parent, rank = cfg.tree.arrays()
+    tree = M.Tree(parent, rank, 5, 4)
+    W = {m: torch.zeros(shp, dtype=torch.bfloat16, device="cuda") for m, shp in mi.layer_shapes(cfg).items()}
+    emb = torch.zeros(cfg.V, cfg.H, dtype=torch.bfloat16, device="cuda")
+    kc = torch.zeros(1, 1, 4, cfg.Lmax, 64, dtype=torch.bfloat16, device="cuda")
+    tok = torch.zeros(1, cfg.N, dtype=torch.int32, device="cuda")
+    g = torch.empty_like(tok)
+    with pytest.raises(M.MedusaError) as e:
+        M.medusa_decoder_verify([W], emb, emb, tree, tok, tok, torch.zeros(1, dtype=torch.int32, device="cuda"), 5,
+                                kc, kc.clone(), 4, g)
+    assert e.value.status == M.EUNSUPPORTED
