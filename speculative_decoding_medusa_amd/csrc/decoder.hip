@@ -86,58 +86,104 @@ __device__ __forceinline__ float sum_splits(const float* __restrict__ part, int 
     return v;
 }
 
-// Sum the q|k|v partials of node r, rotate q and k (pair (i, i + D/2) of a
-// head by pos * base^(-2i/D); the angle and its sine and cosine in double),
-// and store bf16 q [R][nH][D], k and v [R][nKV][D].
-__global__ __launch_bounds__(256) void qkv_rope_kernel(const float* __restrict__ part, int S, int R, int nH, int nKV,
-                                                       int D, const int32_t* __restrict__ pos, float log2_base,
-                                                       bf16_t* __restrict__ q, bf16_t* __restrict__ k,
-                                                       bf16_t* __restrict__ v) {
-    const int r = blockIdx.x;
-    const int ncols = (nH + 2 * nKV) * D;
-    const size_t stride = (size_t)R * ncols;
-    const int half = D / 2;
-    const double p = (double)pos[r];
-    for (int e = threadIdx.x; e < (nH + nKV) * half; e += blockDim.x) {
-        const int head = e / half, i = e - head * half;  // heads 0..nH-1 are q, then the nKV k heads
-        const int c0 = head * D + i;
-        const float x1 = sum_splits(part, S, stride, (size_t)r * ncols + c0);
-        const float x2 = sum_splits(part, S, stride, (size_t)r * ncols + c0 + half);
-        const double ang = p * exp2(-2.0 * (double)i / (double)D * (double)log2_base);
-        double sn, cs;
-        sincos(ang, &sn, &cs);
-        const float c = (float)cs, sg = (float)sn;
-        const float y1 = x1 * c - x2 * sg;
-        const float y2 = x2 * c + x1 * sg;
-        bf16_t* dst = head < nH ? q + ((size_t)r * nH + head) * D : k + ((size_t)r * nKV + (head - nH)) * D;
-        dst[i] = f32_to_bf16(y1);
-        dst[i + half] = f32_to_bf16(y2);
-    }
-    for (int e = threadIdx.x; e < nKV * D; e += blockDim.x) {
-        const float x = sum_splits(part, S, stride, (size_t)r * ncols + (nH + nKV) * D + e);
-        v[(size_t)r * nKV * D + e] = f32_to_bf16(x);
+// cs[r][i] = (cos, sin) of the angle pos[r] * base^(-2i/D), computed in double
+// once per verify call (every layer rotates at the same positions).
+__global__ void rope_table_kernel(const int32_t* __restrict__ pos, int D, double log2_base, float2* __restrict__ cs) {
+    const int r = blockIdx.x, half = D / 2;
+    for (int i = threadIdx.x; i < half; i += blockDim.x) {
+        const double ang = (double)pos[r] * exp2(-2.0 * (double)i / (double)D * log2_base);
+        double sn, c;
+        sincos(ang, &sn, &c);
+        cs[(size_t)r * half + i] = make_float2((float)c, (float)sn);
     }
 }
 
-// x[e] += sum of the S partials of element e (x and each partial [R][H]).
-__global__ __launch_bounds__(256) void residual_add_kernel(const float* __restrict__ part, int S, size_t n,
-                                                           float* __restrict__ x) {
-    for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x)
-        x[e] += sum_splits(part, S, n, e);
+// Block (r, head): sum the S partials of node r's q|k|v columns of one head;
+// heads 0..nH-1 (q) and nH..nH+nKV-1 (k) rotate the pair (i, i + D/2) by the
+// table angle; the last nKV heads are v.  Stores bf16 q [R][nH][D], k and v
+// [R][nKV][D].  blockDim = D / 2.
+__global__ __launch_bounds__(64) void qkv_rope_kernel(const float* __restrict__ part, int S, int R, int nH, int nKV,
+                                                      int D, const float2* __restrict__ cs, bf16_t* __restrict__ q,
+                                                      bf16_t* __restrict__ k, bf16_t* __restrict__ v) {
+    const int r = blockIdx.x, head = blockIdx.y, i = threadIdx.x;
+    const int half = D / 2;
+    const int ncols = (nH + 2 * nKV) * D;
+    const size_t stride = (size_t)R * ncols;
+    const size_t c0 = (size_t)r * ncols + (size_t)head * D + i;
+    const float x1 = sum_splits(part, S, stride, c0);
+    const float x2 = sum_splits(part, S, stride, c0 + half);
+    if (head >= nH + nKV) {
+        bf16_t* dst = v + ((size_t)r * nKV + (head - nH - nKV)) * D;
+        dst[i] = f32_to_bf16(x1);
+        dst[i + half] = f32_to_bf16(x2);
+        return;
+    }
+    const float2 t = cs[(size_t)r * half + i];
+    const float y1 = x1 * t.x - x2 * t.y;
+    const float y2 = x2 * t.x + x1 * t.y;
+    bf16_t* dst = head < nH ? q + ((size_t)r * nH + head) * D : k + ((size_t)r * nKV + (head - nH)) * D;
+    dst[i] = f32_to_bf16(y1);
+    dst[i + half] = f32_to_bf16(y2);
+}
+
+// One block per row r: x[r] += sum of the S partials of row r ([S][R][H]),
+// then n[r] = bf16(x[r] * rsqrt(mean(x[r]^2) + eps)).  The row stays in
+// registers between the two passes (H <= 16384 with 512 threads).
+constexpr int RN_THREADS = 512;
+__global__ __launch_bounds__(RN_THREADS) void residual_rmsnorm_kernel(const float* __restrict__ part, int S, int R,
+                                                                      int H, float eps, float* __restrict__ x,
+                                                                      bf16_t* __restrict__ n) {
+    __shared__ float red[RN_THREADS / 64];
+    const int r = blockIdx.x;
+    float* xr = x + (size_t)r * H;
+    const size_t stride = (size_t)R * H;
+    f32x4 xv[8];
+    float ss = 0.f;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int j = (it * RN_THREADS + threadIdx.x) * 4;
+        if (j < H) {
+            f32x4 a = *(const f32x4*)(xr + j);
+            for (int s2 = 0; s2 < S; ++s2) a += *(const f32x4*)(part + (size_t)s2 * stride + (size_t)r * H + j);
+            *(f32x4*)(xr + j) = a;
+            xv[it] = a;
+            ss = fmaf(a.x, a.x, ss);
+            ss = fmaf(a.y, a.y, ss);
+            ss = fmaf(a.z, a.z, ss);
+            ss = fmaf(a.w, a.w, ss);
+        }
+    }
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < RN_THREADS / 64; ++w) tot += red[w];
+    const float rs = rsqrtf(tot / (float)H + eps);
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int j = (it * RN_THREADS + threadIdx.x) * 4;
+        if (j < H) {
+            const f32x4 a = xv[it];
+            *(uint2*)(n + (size_t)r * H + j) =
+                (uint2){(uint32_t)f32_to_bf16(a.x * rs) | ((uint32_t)f32_to_bf16(a.y * rs) << 16),
+                        (uint32_t)f32_to_bf16(a.z * rs) | ((uint32_t)f32_to_bf16(a.w * rs) << 16)};
+        }
+    }
 }
 
 // a[r][c] = bf16(SiLU(g) * u) with g = column c and u = column F + c of the
-// summed gate|up partials [R][2F].
+// summed gate|up partials [S][R][2F].  Grid (ceil(F / 256), R).
 __global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ part, int S, int R, int F,
                                                      bf16_t* __restrict__ a) {
-    const size_t n = (size_t)R * F;
+    const int r = blockIdx.y;
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= F) return;
     const size_t stride = (size_t)R * 2 * F;
-    for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
-        const size_t r = e / F, c = e - r * F;
-        const float g = sum_splits(part, S, stride, r * 2 * F + c);
-        const float u = sum_splits(part, S, stride, r * 2 * F + F + c);
-        a[e] = f32_to_bf16(g / (1.f + __expf(-g)) * u);
-    }
+    const size_t row = (size_t)r * 2 * F;
+    const float g = sum_splits(part, S, stride, row + c);
+    const float u = sum_splits(part, S, stride, row + F + c);
+    a[(size_t)r * F + c] = f32_to_bf16(g / (1.f + __expf(-g)) * u);
 }
 
 // ---------------------------------------------------------------------------
@@ -183,6 +229,7 @@ struct DecoderWs {
     bf16_t *n, *q, *kt, *vt, *o, *a;
     float* part;
     float *att_o, *att_ml;
+    float2* rope;
     void* greedy_ws;
 };
 
@@ -202,7 +249,8 @@ size_t decoder_workspace_bytes(int B, int N, int H, int nH, int nKV, int D, int 
     const size_t R = (size_t)B * N;
     return a256(R * H * 4) + a256(R * H * 2) + a256(R * nH * D * 2) + 2 * a256(R * nKV * D * 2) + a256(R * H * 2) +
            a256(R * F * 2) + a256(partial_floats((int)R, H, nH, nKV, D, F) * 4) +
-           a256(attn_workspace_bytes(B, nH, N, D, max_cache_len, true)) + a256(lm_head_greedy_workspace_bytes((int)R, H, V));
+           a256(attn_workspace_bytes(B, nH, N, D, max_cache_len, true)) + a256(R * (D / 2) * sizeof(float2)) +
+           a256(lm_head_greedy_workspace_bytes((int)R, H, V));
 }
 
 static DecoderWs carve(void* ws, int B, int N, int H, int nH, int nKV, int D, int F, int max_cache_len) {
@@ -219,6 +267,7 @@ static DecoderWs carve(void* ws, int B, int N, int H, int nH, int nKV, int D, in
     w.part = (float*)p; p += a256(partial_floats((int)R, H, nH, nKV, D, F) * 4);
     attn_carve(B, nH, N, D, max_cache_len, true, p, &w.att_o, &w.att_ml);
     p += a256(attn_workspace_bytes(B, nH, N, D, max_cache_len, true));
+    w.rope = (float2*)p; p += a256(R * (D / 2) * sizeof(float2));
     w.greedy_ws = p;
     return w;
 }
@@ -239,35 +288,35 @@ void launch_decoder_verify(const LayerPtrs* layers, int n_layers, const bf16_t* 
     const GemmSplit sp_qkv = gemm_split(R, H, qkv), sp_o = gemm_split(R, nH * D, H),
                     sp_gu = gemm_split(R, H, 2 * F), sp_d = gemm_split(R, F, H);
     const float scale = 1.0f / sqrtf((float)D);
-    const float log2_base = log2f(rope_base);
+    const double log2_base = log2((double)rope_base);
     const int ew_blocks = 1024;
 
     MEDUSA_LAUNCH("embed_rows", embed_rows_kernel, dim3(R), dim3(256), 0, s, node_tok, E, H, V, w.x);
+    MEDUSA_LAUNCH("rope_table", rope_table_kernel, dim3(R), dim3(64), 0, s, node_pos, D, log2_base, w.rope);
+    MEDUSA_LAUNCH("rmsnorm_f32", rmsnorm_f32_bf16_kernel, dim3(R), dim3(256), 0, s, w.x, H, eps, w.n);
     for (int l = 0; l < n_layers; ++l) {
+        // w.n holds bf16(RMSNorm(x)) of the layer input
         const LayerPtrs& L = layers[l];
         bf16_t* kc = k_cache + (size_t)l * layer_stride;
         bf16_t* vc = v_cache + (size_t)l * layer_stride;
-        MEDUSA_LAUNCH("rmsnorm_f32", rmsnorm_f32_bf16_kernel, dim3(R), dim3(256), 0, s, w.x, H, eps, w.n);
         launch_skinny_partial(w.n, WeightRows{L.wq, L.wk, L.wv, nH * D, nKV * D}, R, H, qkv, sp_qkv, w.part, s,
                               "dec_gemm_qkv");
-        MEDUSA_LAUNCH("qkv_rope", qkv_rope_kernel, dim3(R), dim3(256), 0, s, w.part, sp_qkv.S, R, nH, nKV, D, node_pos,
-                      log2_base, w.q, w.kt, w.vt);
+        MEDUSA_LAUNCH("qkv_rope", qkv_rope_kernel, dim3(R, nH + 2 * nKV), dim3(D / 2), 0, s, w.part, sp_qkv.S, R, nH,
+                      nKV, D, w.rope, w.q, w.kt, w.vt);
         launch_tree_attention(w.q, w.kt, w.vt, kc, vc, cache_len, max_cache_len, t, B, nH, nKV, D, Lmax, scale, true,
                               w.o, w.att_o, w.att_ml, s, 0);
         launch_skinny_partial(w.o, WeightRows{L.wo, nullptr, nullptr, H, 0}, R, nH * D, H, sp_o, w.part, s,
                               "dec_gemm_o");
-        MEDUSA_LAUNCH("residual_add", residual_add_kernel, dim3(ew_blocks), dim3(256), 0, s, w.part, sp_o.S,
-                      (size_t)R * H, w.x);
-        MEDUSA_LAUNCH("rmsnorm_f32", rmsnorm_f32_bf16_kernel, dim3(R), dim3(256), 0, s, w.x, H, eps, w.n);
+        MEDUSA_LAUNCH("residual_rmsnorm", residual_rmsnorm_kernel, dim3(R), dim3(RN_THREADS), 0, s, w.part, sp_o.S, R,
+                      H, eps, w.x, w.n);
         launch_skinny_partial(w.n, WeightRows{L.w_gate, L.w_up, nullptr, F, F}, R, H, 2 * F, sp_gu, w.part, s,
                               "dec_gemm_gate_up");
-        MEDUSA_LAUNCH("swiglu", swiglu_kernel, dim3(ew_blocks), dim3(256), 0, s, w.part, sp_gu.S, R, F, w.a);
+        MEDUSA_LAUNCH("swiglu", swiglu_kernel, dim3((F + 255) / 256, R), dim3(256), 0, s, w.part, sp_gu.S, R, F, w.a);
         launch_skinny_partial(w.a, WeightRows{L.w_down, nullptr, nullptr, H, 0}, R, F, H, sp_d, w.part, s,
                               "dec_gemm_down");
-        MEDUSA_LAUNCH("residual_add", residual_add_kernel, dim3(ew_blocks), dim3(256), 0, s, w.part, sp_d.S,
-                      (size_t)R * H, w.x);
+        MEDUSA_LAUNCH("residual_rmsnorm", residual_rmsnorm_kernel, dim3(R), dim3(RN_THREADS), 0, s, w.part, sp_d.S, R,
+                      H, eps, w.x, w.n);
     }
-    MEDUSA_LAUNCH("rmsnorm_f32", rmsnorm_f32_bf16_kernel, dim3(R), dim3(256), 0, s, w.x, H, eps, w.n);
     launch_lm_head_greedy(w.n, lm_head, R, H, V, greedy, w.greedy_ws, s);
     if (hidden != nullptr) {
         // the final normalised rows, widened to fp32

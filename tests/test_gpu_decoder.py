@@ -3,7 +3,7 @@
 inputs.
 
 Checked: the greedy choice after every node (bit-exact; lm_head rows are
-redrawn until every node's best two scores differ by >= 1e-2), the final
+redrawn until every node's best two scores differ by a margin, see below), the final
 normalised rows, and the rotated keys and values every layer writes into its
 cache slots P..P+N-1.
 
@@ -16,7 +16,13 @@ oracle alone, multiplying the attention output of one full-width layer by
 changes the residual stream by 0.3% of its RMS and the normalised rows by up
 to 0.031.  The float outputs of this multi-layer pass are therefore checked
 against max(4e-2, two bf16 steps) per element and 1% of the values' RMS for
-the RMS of the difference; the integer decisions stay exact.  Cases span the 64-, 128- and 256-row
+the RMS of the difference.  The same cascade moves the lm_head scores: at the
+full width over two layers, that 1.5e-4 noise moves them by 0.0069 RMS and
+0.038 at most (scores of RMS 1.28), so a 1e-2 margin between a node's best two
+scores is about one standard deviation of the noise on their difference.  The
+margin enforced for the full-width case is 0.1 (above twice the largest
+measured move); the narrow cases keep 1e-2.  The greedy choices must then
+match exactly.  Cases span the 64-, 128- and 256-row
 tile shapes of the projections, GQA, ragged cache lengths, and two layers at
 the full Llama-7B width (hidden 4096, 32 x 128 heads, MLP 11008, vocabulary
 32000, 4096-token caches, sparse 64-node tree).
@@ -57,15 +63,18 @@ CASES = [
     ("rows256_dense256", lambda: _cfg("d4", 1, 512, 3001, mi.dense_tree(256), 8, 8, 64, (64,), 504, 1, 320)),
     ("full_width_2layers", lambda: _cfg("d5", 1, 4096, 32000, mi.sparse_tree(64), 32, 32, 128, (4096,), 505, 2, 11008)),
 ]
+# margin between each node's best two lm_head scores
+MARGIN = {"full_width_2layers": 0.1}
 
 
 def _enforce_gap(cfg, lm_head, rows, gap=GAP, max_iter=1000):
     """Redraw lm_head rows (from their override streams) until every row's
-    best two scores differ by >= gap.  rows: final normalised rows (float64)."""
+    best two scores differ by >= gap.  rows: final normalised rows (float64).
+    The scores are computed once and updated for the redrawn rows only."""
     lm = {"lm_head": lm_head}
     ov = []
+    lg = rows @ oracle.widen(lm_head, "bf16").T            # [R][V]
     for _ in range(max_iter):
-        lg = (oracle.widen(lm_head, "bf16") @ rows.T).T
         lg32 = oracle.round_f32(lg)
         bad = set()
         for r in range(lg.shape[0]):
@@ -78,6 +87,7 @@ def _enforce_gap(cfg, lm_head, rows, gap=GAP, max_iter=1000):
             o = {"tensor": "lm_head", "row": row, "serial": len(ov)}
             ov.append(o)
             mi.apply_overrides(cfg, lm, [o])
+            lg[:, row] = rows @ oracle.widen(lm_head[row], "bf16")
     raise RuntimeError("greedy gap enforcement did not converge")
 
 
@@ -104,7 +114,7 @@ def test_decoder_verify_parity(name, mk):
     ref = oracle.decoder_verify(tok, P, parent, oracle.widen(emb, "bf16"), wl, oracle.widen(lm_head, "bf16"), kc, vc,
                                 cfg.nH, cfg.nKV, bf16=True)
     del wl
-    ov = _enforce_gap(cfg, lm_head, ref["hidden"].reshape(B * N, cfg.H))
+    ov = _enforce_gap(cfg, lm_head, ref["hidden"].reshape(B * N, cfg.H), gap=MARGIN.get(name, GAP))
     g_ref = np.argmax(oracle.round_f32(ref["hidden"].reshape(B * N, -1) @ oracle.widen(lm_head, "bf16").T), axis=1)
     g_ref = g_ref.reshape(B, N).astype(np.int32)
     _say("oracle done,", len(ov), "lm_head overrides")
