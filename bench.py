@@ -129,7 +129,11 @@ def main():
     ws_a = torch.empty(M.tree_attention_workspace_size(tree, B, cfg.nH, cfg.D, max(cfg.P), wdt), dtype=torch.uint8,
                        device="cuda")
     g = torch.empty(B * N, dtype=torch.int32, device="cuda")
-    ws_g = torch.empty(M.base_greedy_workspace_size(B * N, H, V, wdt), dtype=torch.uint8, device="cuda")
+    # bf16 lm_head in the MFMA product's packed layout (packed once, like a
+    # weight load; the float32 workload keeps the row-major GEMV)
+    lm_layout = M.PACKED if wdt == M.BF16 and H % 64 == 0 else M.ROW_MAJOR
+    lm = M.pack(d.pop("lm_head")) if lm_layout == M.PACKED else d["lm_head"]
+    ws_g = torch.empty(M.base_greedy_workspace_size(B * N, H, V, wdt, lm_layout), dtype=torch.uint8, device="cuda")
     al = torch.empty(B, dtype=torch.int32, device="cuda")
     an = torch.empty(B, tree.max_depth + 1, dtype=torch.int32, device="cuda")
     ot = torch.empty_like(an)
@@ -142,7 +146,7 @@ def main():
         M.medusa_build_tree(tree, ti, root_d, d["cache_len"], tok, pos)
         M.tree_attention_verify(d["q"], d["k_tree"], d["v_tree"], d["k_cache"], d["v_cache"], d["cache_len"], maxP,
                                 tree, o, ws=ws_a)
-        M.medusa_base_greedy(o, d["lm_head"], g, ws=ws_g)
+        M.medusa_base_greedy(o, lm, g, ws=ws_g)
         M.medusa_accept(tree, tok, g.view(B, N), al, an, ot, d["cache_len"], ncl, k_cache=d["k_cache"],
                         v_cache=d["v_cache"])
 
@@ -315,13 +319,14 @@ def bench_decoder(args, cfg):
     v_cache = torch.empty_like(k_cache)
     for l in range(L):
         W = mi.gen_layer(cfg, l)
-        layers.append({m: dev(W[m]) for m in W})
+        layers.append(M.pack_layer({m: dev(W[m]) for m in W}))
         del W
         kc, vc = mi.gen_layer_cache(cfg, l)
         k_cache[l].copy_(dev(kc))
         v_cache[l].copy_(dev(vc))
         del kc, vc
     emb = dev(mi.gen_embedding(cfg))
+    lm_head = M.pack(d.pop("lm_head"))
     root = dev(mi.gen_root_tokens(cfg))
     cache_len = dev(np.asarray(cfg.P, dtype=np.int32))
     gen_s = time.time() - t0
@@ -348,7 +353,7 @@ def bench_decoder(args, cfg):
         M.medusa_resid_silu(d["h"], d["W1"], d["b1"], z)
         M.medusa_vocab_topk(z, d["W2"], topk, ti, tv, ws=ws_v)
         M.medusa_build_tree(tree, ti, root, cache_len, tok, pos)
-        M.medusa_decoder_verify(layers, emb, d["lm_head"], tree, tok, pos, cache_len, maxP, k_cache, v_cache, cfg.nH, g,
+        M.medusa_decoder_verify(layers, emb, lm_head, tree, tok, pos, cache_len, maxP, k_cache, v_cache, cfg.nH, g,
                                 ws=ws_d)
         M.medusa_accept(tree, tok, g, al, an, ot, cache_len, ncl, k_cache=k_cache, v_cache=v_cache)
 

@@ -55,6 +55,10 @@ typedef enum {
 
 typedef enum { MEDUSA_F32 = 0, MEDUSA_BF16 = 1 } medusa_dtype;
 
+/* Layout of a weight matrix [rows][cols]: row-major, or packed by
+ * medusa_pack_rows into the fragment order of the MFMA products. */
+typedef enum { MEDUSA_ROW_MAJOR = 0, MEDUSA_PACKED = 1 } medusa_layout;
+
 /* Opaque candidate-tree topology (library-owned; device copy inside). */
 typedef struct medusa_tree medusa_tree;
 
@@ -156,17 +160,39 @@ medusa_status tree_attention_verify(const void* q, const void* k_tree, const voi
                                     void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Weight packing for the MFMA products (base greedy's lm_head, the decoder's
+ * projections).  Not a step of the method: a layout, applied once when the
+ * weights are loaded.  A packed matrix of `rows` rows and `cols` columns
+ * (bf16) stores row r, column k at element
+ *   ((r / 16) * (cols / 32) + k / 32) * 512 + ((k % 32) / 8 * 16 + r % 16) * 8 + k % 8
+ * (every 16 x 32 tile is one contiguous 1 KB fragment) and occupies
+ * medusa_packed_size(rows, cols) bytes (rows rounded up to 16).
+ *   medusa_pack_rows: src [rows][cols] row-major bf16 (device) -> packed rows
+ *   dst_row0 .. dst_row0 + rows - 1 of dst, a packed matrix of dst_rows rows.
+ *   Several matrices stack into one by packing each at its row offset (the
+ *   decoder's q|k|v and gate|up); the call that ends at dst_rows also zeroes
+ *   the padding rows.  Asynchronous on `stream`; src must stay valid until
+ *   the copy has run.
+ * Limits: cols % 32 == 0.  medusa_packed_size returns 0 for invalid sizes.
+ * ------------------------------------------------------------------------- */
+size_t medusa_packed_size(int rows, int cols);
+medusa_status medusa_pack_rows(const void* src, int rows, int cols, void* dst, int dst_row0, int dst_rows,
+                               void* stream);
+
+/* ---------------------------------------------------------------------------
  * Step a5 -- the base model's greedy choice after every tree node (tree
  * section: greedy acceptance compares with the model's top choice).
  *   x [R][H] (dt): one row per node; n = x * rsqrt(mean(x^2) + eps) (unit
  *   weight), rounded to bf16 when dt is BF16; greedy[r] = argmax_v
  *   (lm_head[v] . n_r), lower index first among equal values.
- *   lm_head [V][H] (dt); greedy [R] int32; logits [R][V] float32 optional.
- * Limits: H % 8 == 0, H <= 8192, R >= 1.
+ *   lm_head [V][H] (dt) in lm_layout: MEDUSA_PACKED (bf16 only; the MFMA
+ *   product) or MEDUSA_ROW_MAJOR (the vector GEMV, any dt);
+ *   greedy [R] int32; logits [R][V] float32 optional.
+ * Limits: H % 8 == 0, H <= 8192, R >= 1; packed: H % 64 == 0.
  * ------------------------------------------------------------------------- */
-size_t medusa_base_greedy_workspace_size(int R, int H, int V, medusa_dtype dt);
-medusa_status medusa_base_greedy(const void* x, const void* lm_head, int R, int H, int V, float eps,
-                                 medusa_dtype dt, int32_t* greedy, float* logits,
+size_t medusa_base_greedy_workspace_size(int R, int H, int V, medusa_dtype dt, medusa_layout lm_layout);
+medusa_status medusa_base_greedy(const void* x, const void* lm_head, medusa_layout lm_layout, int R, int H, int V,
+                                 float eps, medusa_dtype dt, int32_t* greedy, float* logits,
                                  void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
@@ -210,26 +236,25 @@ medusa_status medusa_accept(const medusa_tree* tree, const int32_t* node_tok, co
  *   rows, q/k/v, the attention output and the SwiGLU product are rounded to
  *   bf16 (nearest even) before they enter the next product.
  * Arguments (bf16 only; device pointers unless noted):
- *   layers (host array [n_layers]): weights in the [out][in] layout, bf16:
- *     wq [nH*D][H], wk and wv [nKV*D][H], wo [H][nH*D], w_gate and w_up [F][H],
- *     w_down [H][F];  embedding and lm_head [V][H];
+ *   layers (host array [n_layers]): each layer's weights, [out][in] matrices
+ *     packed by medusa_pack_rows: wqkv = W_q [nH*D][H], W_k and W_v
+ *     [nKV*D][H] stacked in that order ((nH + 2 nKV) D rows); wo [H][nH*D];
+ *     w_gate_up = W_gate and W_up [F][H] stacked (2F rows); w_down [H][F];
+ *   embedding [V][H] row-major;  lm_head [V][H] packed;
  *   node_tok, node_pos [B][N] int32 (medusa_build_tree's outputs; token ids
  *     outside [0, V) read row 0 of the embedding);  cache_len [B];
  *   k_cache / v_cache: n_layers caches, layer l at base + l * layer_stride_elems,
  *     each [B][nKV][Lmax][D];
  *   greedy [B][N] int32 (output); hidden [B][N][H] float32, optional: the
  *     final normalised rows (bf16 values) that lm_head scores.
- * Limits: H == nH * D, D in {64, 128}, H and F multiples of 256 (of
- *   512 / ceil(B*N/16) above 64 nodes), B*N <= 256, H <= 16384.
+ * Limits: H == nH * D, D in {64, 128}, H and F multiples of 64,
+ *   B*N <= 256, H <= 16384.
  *   The workspace must not be shared by calls that may run concurrently.
  * ------------------------------------------------------------------------- */
 typedef struct {
-    const void* wq;
-    const void* wk;
-    const void* wv;
+    const void* wqkv;
     const void* wo;
-    const void* w_gate;
-    const void* w_up;
+    const void* w_gate_up;
     const void* w_down;
 } medusa_layer_weights;
 

@@ -24,6 +24,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
 F32, BF16 = 0, 1
+ROW_MAJOR, PACKED = 0, 1
 
 _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 _SIGS = {
@@ -44,8 +45,10 @@ _SIGS = {
     "tree_attention_workspace_size": ([_vp, _i32, _i32, _i32, _i32, _i32], _sz),
     "tree_attention_verify": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                                _vp, _vp, _sz, _vp], _i32),
-    "medusa_base_greedy_workspace_size": ([_i32, _i32, _i32, _i32], _sz),
-    "medusa_base_greedy": ([_vp, _vp, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
+    "medusa_packed_size": ([_i32, _i32], _sz),
+    "medusa_pack_rows": ([_vp, _i32, _i32, _vp, _i32, _i32, _vp], _i32),
+    "medusa_base_greedy_workspace_size": ([_i32, _i32, _i32, _i32, _i32], _sz),
+    "medusa_base_greedy": ([_vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
     "medusa_accept": ([_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32,
                        _vp], _i32),
     "medusa_decoder_workspace_size": ([_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32], _sz),
@@ -212,22 +215,72 @@ def tree_attention_verify(q, k_tree, v_tree, k_cache, v_cache, cache_len, max_ca
 
 
 # ---------------------------------------------------------------------------
+# weight packing (the MFMA products' layout)
+# ---------------------------------------------------------------------------
+
+class Packed:
+    """A bf16 matrix [rows][cols] in the packed fragment order of
+    medusa_pack_rows; `data` is the device buffer (bf16, padded rows)."""
+
+    def __init__(self, data, rows: int, cols: int):
+        self.data, self.rows, self.cols = data, rows, cols
+
+    @property
+    def shape(self):
+        return (self.rows, self.cols)
+
+    def data_ptr(self):
+        return self.data.data_ptr()
+
+
+def packed_size(rows: int, cols: int) -> int:
+    return _lib.medusa_packed_size(rows, cols)
+
+
+def medusa_pack_rows(src, dst: Packed, dst_row0: int = 0, stream=None):
+    rows, cols = src.shape
+    _check("medusa_pack_rows", _lib.medusa_pack_rows(_p(src), rows, cols, _p(dst.data), int(dst_row0), dst.rows,
+                                                     _stream(stream)))
+    return dst
+
+
+def pack(*mats, stream=None) -> Packed:
+    """Pack bf16 [rows_i][cols] matrices (stacked in the given order) into one
+    packed matrix."""
+    cols = mats[0].shape[1]
+    rows = sum(m.shape[0] for m in mats)
+    nbytes = packed_size(rows, cols)
+    if nbytes == 0:
+        raise MedusaError("medusa_packed_size", EUNSUPPORTED)
+    dst = Packed(torch.empty(nbytes // 2, dtype=torch.bfloat16, device=mats[0].device), rows, cols)
+    r0 = 0
+    for m in mats:
+        assert m.shape[1] == cols and m.dtype == torch.bfloat16 and m.is_contiguous()
+        medusa_pack_rows(m, dst, r0, stream)
+        r0 += m.shape[0]
+    return dst
+
+
+# ---------------------------------------------------------------------------
 # a5
 # ---------------------------------------------------------------------------
 
-def base_greedy_workspace_size(R, H, V, dt):
-    return _lib.medusa_base_greedy_workspace_size(R, H, V, dt)
+def base_greedy_workspace_size(R, H, V, dt, layout=ROW_MAJOR):
+    return _lib.medusa_base_greedy_workspace_size(R, H, V, dt, layout)
 
 
 def medusa_base_greedy(x, lm_head, greedy, eps=1e-6, logits=None, ws=None, stream=None):
+    """lm_head: a row-major [V][H] tensor (vector GEMV) or a Packed bf16
+    matrix (MFMA product)."""
+    layout = PACKED if isinstance(lm_head, Packed) else ROW_MAJOR
     V, H = lm_head.shape
     R = x.numel() // H
-    dt = _dt(lm_head)
-    need = base_greedy_workspace_size(R, H, V, dt)
+    dt = BF16 if layout == PACKED else _dt(lm_head)
+    need = base_greedy_workspace_size(R, H, V, dt, layout)
     ws = _ws(need, x.device, ws)
     _check("medusa_base_greedy", _lib.medusa_base_greedy(
-        _p(x), _p(lm_head), R, H, V, float(eps), dt, _p(greedy), _p(logits), _p(ws), ws.numel() * ws.element_size(),
-        _stream(stream)))
+        _p(x), ctypes.c_void_p(lm_head.data_ptr()), layout, R, H, V, float(eps), dt, _p(greedy), _p(logits), _p(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
     return greedy
 
 
@@ -255,33 +308,43 @@ def medusa_accept(tree: Tree, node_tok, greedy, accept_len, accept_nodes, out_to
 # a8
 # ---------------------------------------------------------------------------
 
+LAYER_MATRICES = ("wqkv", "wo", "w_gate_up", "w_down")
+
+
 class LayerWeights(ctypes.Structure):
-    """medusa_layer_weights: device pointers of one decoder layer's matrices."""
-    _fields_ = [(n, ctypes.c_void_p) for n in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")]
+    """medusa_layer_weights: device pointers of one decoder layer's packed matrices."""
+    _fields_ = [(n, ctypes.c_void_p) for n in LAYER_MATRICES]
+
+
+def pack_layer(W, stream=None):
+    """Row-major bf16 layer weights {wq, wk, wv, wo, w_gate, w_up, w_down}
+    -> the packed matrices medusa_decoder_verify reads."""
+    return {"wqkv": pack(W["wq"], W["wk"], W["wv"], stream=stream), "wo": pack(W["wo"], stream=stream),
+            "w_gate_up": pack(W["w_gate"], W["w_up"], stream=stream), "w_down": pack(W["w_down"], stream=stream)}
 
 
 def decoder_workspace_size(tree: Tree, B, H, nH, nKV, D, F, V, max_cache_len):
     return _lib.medusa_decoder_workspace_size(tree.handle, B, H, nH, nKV, D, F, V, max_cache_len)
 
 
-def medusa_decoder_verify(layers, embedding, lm_head, tree: Tree, node_tok, node_pos, cache_len, max_cache_len: int,
-                          k_cache, v_cache, nH: int, greedy, hidden=None, rms_eps=1e-6, rope_base=10000.0, ws=None,
-                          stream=None):
-    """layers: list of dicts of bf16 tensors (wq, wk, wv, wo, w_gate, w_up, w_down);
-    k_cache / v_cache: [layers][B][nKV][Lmax][D] bf16."""
+def medusa_decoder_verify(layers, embedding, lm_head: Packed, tree: Tree, node_tok, node_pos, cache_len,
+                          max_cache_len: int, k_cache, v_cache, nH: int, greedy, hidden=None, rms_eps=1e-6,
+                          rope_base=10000.0, ws=None, stream=None):
+    """layers: list of pack_layer() dicts; embedding [V][H] bf16 row-major;
+    lm_head Packed [V][H]; k_cache / v_cache: [layers][B][nKV][Lmax][D] bf16."""
     n_layers, B, nKV, Lmax, D = k_cache.shape
     V, H = embedding.shape
-    F = layers[0]["w_gate"].shape[0]
+    F = layers[0]["w_gate_up"].rows // 2
     arr = (LayerWeights * len(layers))()
     for i, W in enumerate(layers):
-        arr[i] = LayerWeights(*[W[n].data_ptr() for n in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")])
+        arr[i] = LayerWeights(*[W[n].data_ptr() for n in LAYER_MATRICES])
     need = decoder_workspace_size(tree, B, H, nH, nKV, D, F, V, max_cache_len)
     ws = _ws(need, embedding.device, ws)
     _check("medusa_decoder_verify", _lib.medusa_decoder_verify(
-        ctypes.cast(arr, ctypes.c_void_p), len(layers), _p(embedding), _p(lm_head), tree.handle, _p(node_tok),
-        _p(node_pos), _p(cache_len), int(max_cache_len), _p(k_cache), _p(v_cache), k_cache.stride(0), B, H, nH, nKV,
-        D, F, V, Lmax, float(rms_eps), float(rope_base), _p(greedy), _p(hidden), _p(ws),
-        ws.numel() * ws.element_size(), _stream(stream)))
+        ctypes.cast(arr, ctypes.c_void_p), len(layers), _p(embedding), ctypes.c_void_p(lm_head.data_ptr()),
+        tree.handle, _p(node_tok), _p(node_pos), _p(cache_len), int(max_cache_len), _p(k_cache), _p(v_cache),
+        k_cache.stride(0), B, H, nH, nKV, D, F, V, Lmax, float(rms_eps), float(rope_base), _p(greedy), _p(hidden),
+        _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return greedy
 
 

@@ -34,8 +34,8 @@ void launch_tree_attention(const void* q, const void* k_tree, const void* v_tree
 size_t attn_workspace_bytes(int B, int nH, int N, int D, int max_cache_len, bool bf16);
 void attn_carve(int B, int nH, int N, int D, int max_cache_len, bool bf16, void* ws, float** part_o,
                 float** part_ml);
-size_t greedy_workspace_bytes(int R, int H, int V, bool bf16);
-void launch_base_greedy(const void* x, const void* lm_head, int R, int H, int V, float eps, bool bf16,
+size_t greedy_workspace_bytes(int R, int H, int V, bool packed);
+void launch_base_greedy(const void* x, const void* lm_head, bool packed, int R, int H, int V, float eps, bool bf16,
                         int32_t* greedy, float* logits, void* ws, hipStream_t s);
 void launch_accept(const TreeDev& t, const int32_t* node_tok, const int32_t* greedy, int B, int32_t* accept_len,
                    int32_t* accept_nodes, int32_t* out_tokens, const int32_t* cache_len, int32_t* new_cache_len,
@@ -43,8 +43,10 @@ void launch_accept(const TreeDev& t, const int32_t* node_tok, const int32_t* gre
                    bool bf16, hipStream_t s);
 
 struct LayerPtrs {
-    const bf16_t *wq, *wk, *wv, *wo, *w_gate, *w_up, *w_down;
+    const bf16_t *wqkv, *wo, *w_gate_up, *w_down;
 };
+size_t packed_elems(int rows, int K);
+void launch_pack_rows(const bf16_t* src, int rows, int K, bf16_t* dst, int dst_row0, int dst_rows, hipStream_t s);
 size_t decoder_workspace_bytes(int B, int N, int H, int nH, int nKV, int D, int F, int V, int max_cache_len);
 void launch_decoder_verify(const LayerPtrs* layers, int n_layers, const bf16_t* E, const bf16_t* lm_head,
                            const TreeDev& t, const int32_t* node_tok, const int32_t* node_pos,
@@ -390,23 +392,50 @@ medusa_status tree_attention_verify(const void* q, const void* k_tree, const voi
 // ---------------------------------------------------------------------------
 // a5 base greedy
 // ---------------------------------------------------------------------------
-size_t medusa_base_greedy_workspace_size(int R, int H, int V, medusa_dtype dt) {
+size_t medusa_base_greedy_workspace_size(int R, int H, int V, medusa_dtype dt, medusa_layout lm_layout) {
     if (R < 1 || H < 1 || V < 1) return 0;
-    return greedy_workspace_bytes(R, H, V, dt == MEDUSA_BF16);
+    (void)dt;
+    return greedy_workspace_bytes(R, H, V, lm_layout == MEDUSA_PACKED);
 }
 
-medusa_status medusa_base_greedy(const void* x, const void* lm_head, int R, int H, int V, float eps,
-                                 medusa_dtype dt, int32_t* greedy, float* logits, void* ws, size_t ws_bytes,
-                                 void* stream) {
+medusa_status medusa_base_greedy(const void* x, const void* lm_head, medusa_layout lm_layout, int R, int H, int V,
+                                 float eps, medusa_dtype dt, int32_t* greedy, float* logits, void* ws,
+                                 size_t ws_bytes, void* stream) {
     return guarded("medusa_base_greedy", [&] {
         REQUIRE(x && lm_head && greedy && ws, "null pointer argument");
         REQUIRE(dt == MEDUSA_F32 || dt == MEDUSA_BF16, "bad dtype");
+        REQUIRE(lm_layout == MEDUSA_ROW_MAJOR || lm_layout == MEDUSA_PACKED, "bad lm_head layout");
         REQUIRE(R >= 1 && V >= 1 && H >= 1, "R, H, V must be positive");
         SUPPORT(H % 8 == 0 && H <= 8192, "H=%d must be a multiple of 8 and <= 8192", H);
+        if (lm_layout == MEDUSA_PACKED) {
+            SUPPORT(dt == MEDUSA_BF16, "a packed lm_head must be bf16");
+            SUPPORT(H % 64 == 0, "H=%d must be a multiple of 64 for a packed lm_head", H);
+        }
         REQUIRE(eps >= 0.f, "eps must be >= 0");
-        const size_t need = medusa_base_greedy_workspace_size(R, H, V, dt);
+        const size_t need = medusa_base_greedy_workspace_size(R, H, V, dt, lm_layout);
         REQUIRE(ws_bytes >= need, "workspace too small: %zu < %zu", ws_bytes, need);
-        launch_base_greedy(x, lm_head, R, H, V, eps, dt == MEDUSA_BF16, greedy, logits, ws, (hipStream_t)stream);
+        launch_base_greedy(x, lm_head, lm_layout == MEDUSA_PACKED, R, H, V, eps, dt == MEDUSA_BF16, greedy, logits, ws,
+                           (hipStream_t)stream);
+    });
+}
+
+// ---------------------------------------------------------------------------
+// weight packing
+// ---------------------------------------------------------------------------
+size_t medusa_packed_size(int rows, int cols) {
+    if (rows < 1 || cols < 1 || cols % 32 != 0) return 0;
+    return packed_elems(rows, cols) * 2;
+}
+
+medusa_status medusa_pack_rows(const void* src, int rows, int cols, void* dst, int dst_row0, int dst_rows,
+                               void* stream) {
+    return guarded("medusa_pack_rows", [&] {
+        REQUIRE(src && dst, "null pointer argument");
+        REQUIRE(rows >= 1 && cols >= 1, "rows and cols must be positive");
+        SUPPORT(cols % 32 == 0, "cols=%d must be a multiple of 32", cols);
+        REQUIRE(dst_row0 >= 0 && (int64_t)dst_row0 + rows <= dst_rows,
+                "rows [%d, %d) do not fit the %d packed rows", dst_row0, dst_row0 + rows, dst_rows);
+        launch_pack_rows((const bf16_t*)src, rows, cols, (bf16_t*)dst, dst_row0, dst_rows, (hipStream_t)stream);
     });
 }
 
@@ -463,8 +492,7 @@ medusa_status medusa_decoder_verify(const medusa_layer_weights* layers, int n_la
         SUPPORT(D == 64 || D == 128, "D=%d not in {64, 128}", D);
         const int R = B * tree->t.N;
         SUPPORT(R <= MEDUSA_MAX_TREE_NODES, "B*N=%d exceeds %d", R, MEDUSA_MAX_TREE_NODES);
-        const int kc = R <= 64 ? 256 : R <= 128 ? 64 : 32;
-        SUPPORT(H % kc == 0 && F % kc == 0, "H=%d and F=%d must be multiples of %d", H, F, kc);
+        SUPPORT(H % 64 == 0 && F % 64 == 0, "H=%d and F=%d must be multiples of 64", H, F);
         SUPPORT(H <= 16384, "H=%d exceeds 16384", H);
         REQUIRE(rms_eps >= 0.f && rope_base > 1.f, "need rms_eps >= 0 and rope_base > 1");
         REQUIRE(max_cache_len >= 0 && max_cache_len + tree->t.N <= Lmax,
@@ -474,9 +502,9 @@ medusa_status medusa_decoder_verify(const medusa_layer_weights* layers, int n_la
         std::vector<LayerPtrs> L((size_t)n_layers);
         for (int l = 0; l < n_layers; ++l) {
             const medusa_layer_weights& w = layers[l];
-            REQUIRE(w.wq && w.wk && w.wv && w.wo && w.w_gate && w.w_up && w.w_down, "layer %d: null weight", l);
-            L[l] = LayerPtrs{(const bf16_t*)w.wq, (const bf16_t*)w.wk, (const bf16_t*)w.wv, (const bf16_t*)w.wo,
-                             (const bf16_t*)w.w_gate, (const bf16_t*)w.w_up, (const bf16_t*)w.w_down};
+            REQUIRE(w.wqkv && w.wo && w.w_gate_up && w.w_down, "layer %d: null weight", l);
+            L[l] = LayerPtrs{(const bf16_t*)w.wqkv, (const bf16_t*)w.wo, (const bf16_t*)w.w_gate_up,
+                             (const bf16_t*)w.w_down};
         }
         const size_t need = medusa_decoder_workspace_size(tree, B, H, nH, nKV, D, F, V, max_cache_len);
         REQUIRE(ws_bytes >= need, "workspace too small: %zu < %zu", ws_bytes, need);

@@ -11,11 +11,13 @@
 // weight.  After the last layer: greedy = argmax lm_head . bf16(RMSNorm(x)).
 //
 // The projections are skinny products (R = B*N <= 256 node rows against
-// 4096-22016 weight rows): the weight matrix streams once from HBM through
-// skinny_mfma_kernel, split along the contraction so that every matrix
-// launches about 512 workgroups; each split writes fp32 partial sums and a
-// small epilogue kernel adds them and applies RoPE, the residual or SwiGLU.
+// 4096-22016 weight rows): the packed weight matrix (q|k|v and gate|up each
+// stacked into one) streams once from HBM through skinny_mfma_kernel, split
+// along the contraction into whole rounds of workgroups over the CUs; each
+// split writes fp32 partial sums and a small epilogue kernel adds them and
+// applies RoPE, the residual (with the next RMSNorm) or SwiGLU.
 #include <algorithm>
+#include <cmath>
 
 #include "common.hpp"
 #include "skinny_mfma.hpp"
@@ -194,20 +196,34 @@ struct GemmSplit {
     int cps;  // k-chunks per split
 };
 
-// about 512 workgroups per product, at most 16 splits, whole k-chunks
+// Splits of the contraction (whole k-chunks each, at most 16).  Every
+// workgroup of a product is resident at once, so a count just past a multiple
+// of the CU count leaves most CUs idle while the last round streams: pick the
+// split count whose workgroups fill their rounds best, discounted 3% per
+// extra split for the partial sums it writes and reads back (measured on the
+// Llama-7B projections with 64 rows: 4, 4, 2 and 4 splits for q|k|v, o,
+// gate|up and down).
+constexpr int GPU_CUS = 256;
 static GemmSplit gemm_split(int R, int K, int ncols) {
     const int nblk = lmh_nblk(R);
     const int nchunk = K / lmh_kc(nblk);
     const long long tiles = (long long)((ncols + LMH_ROWS - 1) / LMH_ROWS) * ((R + nblk * 16 - 1) / (nblk * 16));
-    int S = (int)((512 + tiles - 1) / tiles);
-    if (S > 16) S = 16;
-    if (S > nchunk) S = nchunk;
-    if (S < 1) S = 1;
-    const int cps = (nchunk + S - 1) / S;
-    return GemmSplit{(nchunk + cps - 1) / cps, cps};
+    GemmSplit best{1, nchunk};
+    double best_score = -1.0;
+    for (int S = 1; S <= std::min(16, nchunk); ++S) {
+        const int cps = (nchunk + S - 1) / S;
+        const int se = (nchunk + cps - 1) / cps;  // splits actually used
+        const double rounds = (double)(tiles * se) / GPU_CUS;
+        const double score = rounds / std::ceil(rounds) * (1.0 - 0.03 * (se - 1));
+        if (score > best_score + 1e-9) {
+            best_score = score;
+            best = GemmSplit{se, cps};
+        }
+    }
+    return best;
 }
 
-static void launch_skinny_partial(const bf16_t* n, const WeightRows& w, int R, int K, int ncols, const GemmSplit& sp,
+static void launch_skinny_partial(const bf16_t* n, const bf16_t* w, int R, int K, int ncols, const GemmSplit& sp,
                                   float* part, hipStream_t s, const char* name) {
     const int nblk = lmh_nblk(R);
     const dim3 grid((ncols + LMH_ROWS - 1) / LMH_ROWS, (R + nblk * 16 - 1) / (nblk * 16), sp.S);
@@ -272,8 +288,10 @@ static DecoderWs carve(void* ws, int B, int N, int H, int nH, int nKV, int D, in
     return w;
 }
 
+// packed weights of one layer: q|k|v stacked ((nH + 2 nKV) D rows of H),
+// o (H rows of nH D), gate|up stacked (2F rows of H), down (H rows of F)
 struct LayerPtrs {
-    const bf16_t *wq, *wk, *wv, *wo, *w_gate, *w_up, *w_down;
+    const bf16_t *wqkv, *wo, *w_gate_up, *w_down;
 };
 
 void launch_decoder_verify(const LayerPtrs* layers, int n_layers, const bf16_t* E, const bf16_t* lm_head,
@@ -299,21 +317,17 @@ void launch_decoder_verify(const LayerPtrs* layers, int n_layers, const bf16_t* 
         const LayerPtrs& L = layers[l];
         bf16_t* kc = k_cache + (size_t)l * layer_stride;
         bf16_t* vc = v_cache + (size_t)l * layer_stride;
-        launch_skinny_partial(w.n, WeightRows{L.wq, L.wk, L.wv, nH * D, nKV * D}, R, H, qkv, sp_qkv, w.part, s,
-                              "dec_gemm_qkv");
+        launch_skinny_partial(w.n, L.wqkv, R, H, qkv, sp_qkv, w.part, s, "dec_gemm_qkv");
         MEDUSA_LAUNCH("qkv_rope", qkv_rope_kernel, dim3(R, nH + 2 * nKV), dim3(D / 2), 0, s, w.part, sp_qkv.S, R, nH,
                       nKV, D, w.rope, w.q, w.kt, w.vt);
         launch_tree_attention(w.q, w.kt, w.vt, kc, vc, cache_len, max_cache_len, t, B, nH, nKV, D, Lmax, scale, true,
                               w.o, w.att_o, w.att_ml, s, 0);
-        launch_skinny_partial(w.o, WeightRows{L.wo, nullptr, nullptr, H, 0}, R, nH * D, H, sp_o, w.part, s,
-                              "dec_gemm_o");
+        launch_skinny_partial(w.o, L.wo, R, nH * D, H, sp_o, w.part, s, "dec_gemm_o");
         MEDUSA_LAUNCH("residual_rmsnorm", residual_rmsnorm_kernel, dim3(R), dim3(RN_THREADS), 0, s, w.part, sp_o.S, R,
                       H, eps, w.x, w.n);
-        launch_skinny_partial(w.n, WeightRows{L.w_gate, L.w_up, nullptr, F, F}, R, H, 2 * F, sp_gu, w.part, s,
-                              "dec_gemm_gate_up");
+        launch_skinny_partial(w.n, L.w_gate_up, R, H, 2 * F, sp_gu, w.part, s, "dec_gemm_gate_up");
         MEDUSA_LAUNCH("swiglu", swiglu_kernel, dim3((F + 255) / 256, R), dim3(256), 0, s, w.part, sp_gu.S, R, F, w.a);
-        launch_skinny_partial(w.a, WeightRows{L.w_down, nullptr, nullptr, H, 0}, R, F, H, sp_d, w.part, s,
-                              "dec_gemm_down");
+        launch_skinny_partial(w.a, L.w_down, R, F, H, sp_d, w.part, s, "dec_gemm_down");
         MEDUSA_LAUNCH("residual_rmsnorm", residual_rmsnorm_kernel, dim3(R), dim3(RN_THREADS), 0, s, w.part, sp_d.S, R,
                       H, eps, w.x, w.n);
     }

@@ -2,12 +2,13 @@
 // n_r = x_r * rsqrt(mean(x_r^2) + eps) (bf16-rounded for bf16 weights), then
 // greedy[r] = argmax_v lm_head[v] . n_r  (lower index first among equal values).
 //
-// bf16: the product of the node rows with lm_head is a dense contraction
-// (64-512 rows share every lm_head byte), so it runs on MFMA with the argmax
-// fused into the epilogue (skinny_mfma.hpp; the 32000-row vocabulary gives
-// 500 workgroups, about two per CU).  Each workgroup writes, per node, its
-// best (value, index); a merge kernel reduces them.
-// float32: the vector-ALU GEMV of the heads (one pass per 8 rows).
+// Packed bf16 lm_head: the product of the node rows with lm_head is a dense
+// contraction (64-256 rows share every lm_head byte), so it runs on MFMA with
+// the argmax fused into the epilogue (skinny_mfma.hpp; the 32000-row
+// vocabulary gives 500 workgroups, about two per CU).  Each workgroup writes,
+// per node, its best (value, index); a merge kernel reduces them.
+// Row-major lm_head (float32 or bf16): the vector-ALU GEMV of the heads, one
+// pass per 8 rows.
 #include "common.hpp"
 #include "skinny_mfma.hpp"
 
@@ -66,7 +67,6 @@ static int gemv_groups_max(int V) {
 }
 
 
-static bool use_mfma(bool bf16, int H, int R) { return bf16 && H % lmh_kc(lmh_nblk(R)) == 0; }
 
 static size_t a256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -86,17 +86,16 @@ void launch_lm_head_greedy(const bf16_t* n, const bf16_t* lm_head, int R, int H,
     int* ci = (int*)((char*)ws + a256((size_t)R * G * 4));
     const int nblk = lmh_nblk(R);
     const dim3 grid(G, (R + nblk * 16 - 1) / (nblk * 16));
-    const WeightRows wr{lm_head, nullptr, nullptr, V, 0};
     const int nch = H / lmh_kc(nblk);
     if (nblk == 4)
-        MEDUSA_LAUNCH("lm_head_argmax", (skinny_mfma_kernel<4, SKINNY_ARGMAX>), grid, dim3(256), 0, s, n, wr, R, H, V,
-                      nch, cv, ci, logits);
+        MEDUSA_LAUNCH("lm_head_argmax", (skinny_mfma_kernel<4, SKINNY_ARGMAX>), grid, dim3(256), 0, s, n, lm_head,
+                      R, H, V, nch, cv, ci, logits);
     else if (nblk == 8)
-        MEDUSA_LAUNCH("lm_head_argmax", (skinny_mfma_kernel<8, SKINNY_ARGMAX>), grid, dim3(256), 0, s, n, wr, R, H, V,
-                      nch, cv, ci, logits);
+        MEDUSA_LAUNCH("lm_head_argmax", (skinny_mfma_kernel<8, SKINNY_ARGMAX>), grid, dim3(256), 0, s, n, lm_head,
+                      R, H, V, nch, cv, ci, logits);
     else
-        MEDUSA_LAUNCH("lm_head_argmax", (skinny_mfma_kernel<16, SKINNY_ARGMAX>), grid, dim3(256), 0, s, n, wr, R, H,
-                      V, nch, cv, ci, logits);
+        MEDUSA_LAUNCH("lm_head_argmax", (skinny_mfma_kernel<16, SKINNY_ARGMAX>), grid, dim3(256), 0, s, n, lm_head,
+                      R, H, V, nch, cv, ci, logits);
     MEDUSA_LAUNCH("argmax_merge", argmax_merge_kernel, dim3(R), dim3(64), 0, s, cv, ci, G, greedy);
 }
 
@@ -105,16 +104,18 @@ void launch_lm_head_greedy(const bf16_t* n, const bf16_t* lm_head, int R, int H,
     launch_lm_head_greedy(n, lm_head, R, H, V, greedy, nullptr, ws, s);
 }
 
-size_t greedy_workspace_bytes(int R, int H, int V, bool bf16) {
-    if (use_mfma(bf16, H, R)) return a256((size_t)R * H * 2) + lm_head_greedy_workspace_bytes(R, H, V);
+size_t greedy_workspace_bytes(int R, int H, int V, bool packed) {
+    if (packed) return a256((size_t)R * H * 2) + lm_head_greedy_workspace_bytes(R, H, V);
     const int G = gemv_groups_max(V);
     return a256((size_t)R * H * 4) + a256((size_t)8 * G * 4) * 2 + a256((size_t)R * 4);
 }
 
-void launch_base_greedy(const void* x, const void* lm_head, int R, int H, int V, float eps, bool bf16,
+// packed: bf16 x and packed bf16 lm_head (MFMA);  otherwise row-major lm_head
+// of x's type (GEMV)
+void launch_base_greedy(const void* x, const void* lm_head, bool packed, int R, int H, int V, float eps, bool bf16,
                         int32_t* greedy, float* logits, void* ws, hipStream_t s) {
     char* p = (char*)ws;
-    if (use_mfma(bf16, H, R)) {
+    if (packed) {
         bf16_t* n = (bf16_t*)p;
         p += a256((size_t)R * H * 2);
         MEDUSA_LAUNCH("rmsnorm_rows", (rmsnorm_rows_kernel<bf16_t, bf16_t, false>), dim3(R), dim3(256), 0, s,

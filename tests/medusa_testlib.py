@@ -162,6 +162,16 @@ def tol(dtype_str):
 # times (the same C-ABI calls with the same arguments)
 # ---------------------------------------------------------------------------
 
+def lm_head_arg(M, lm_head):
+    """The lm_head argument of medusa_base_greedy as a step passes it: bf16
+    weights packed for the MFMA product when H allows it (H % 64 == 0), else
+    the row-major tensor (vector GEMV).  Returns (argument, layout)."""
+    import torch
+    if lm_head.dtype == torch.bfloat16 and lm_head.shape[1] % 64 == 0:
+        return M.pack(lm_head), M.PACKED
+    return lm_head, M.ROW_MAJOR
+
+
 def run_step_gpu(M, cfg, heads, att, root):
     """Upload the workload, run resid_silu -> vocab_topk -> build_tree ->
     tree_attention_verify -> base_greedy -> accept (with compaction) once and
@@ -183,7 +193,8 @@ def run_step_gpu(M, cfg, heads, att, root):
     ws_a = torch.empty(M.tree_attention_workspace_size(tree, B, cfg.nH, cfg.D, maxP, wdt), dtype=torch.uint8,
                        device="cuda")
     g = torch.empty(B * N, dtype=torch.int32, device="cuda")
-    ws_g = torch.empty(M.base_greedy_workspace_size(B * N, H, V, wdt), dtype=torch.uint8, device="cuda")
+    lm, layout = lm_head_arg(M, d["lm_head"])
+    ws_g = torch.empty(M.base_greedy_workspace_size(B * N, H, V, wdt, layout), dtype=torch.uint8, device="cuda")
     al = torch.empty(B, dtype=torch.int32, device="cuda")
     an = torch.empty(B, tree.max_depth + 1, dtype=torch.int32, device="cuda")
     ot = torch.empty_like(an)
@@ -193,7 +204,7 @@ def run_step_gpu(M, cfg, heads, att, root):
     M.medusa_build_tree(tree, ti, dev(root), d["cache_len"], tok, pos)
     M.tree_attention_verify(d["q"], d["k_tree"], d["v_tree"], d["k_cache"], d["v_cache"], d["cache_len"], maxP, tree, o,
                             ws=ws_a)
-    M.medusa_base_greedy(o, d["lm_head"], g, ws=ws_g)
+    M.medusa_base_greedy(o, lm, g, ws=ws_g)
     M.medusa_accept(tree, tok, g.view(B, N), al, an, ot, d["cache_len"], ncl, k_cache=d["k_cache"],
                     v_cache=d["v_cache"])
     torch.cuda.synchronize()
@@ -201,7 +212,7 @@ def run_step_gpu(M, cfg, heads, att, root):
                node_pos=pos.cpu().numpy(), o=host_f64(o), greedy=g.view(B, N).cpu().numpy(),
                accept_len=al.cpu().numpy(), accept_nodes=an.cpu().numpy(), out_tokens=ot.cpu().numpy(),
                new_cache_len=ncl.cpu().numpy(), k_cache=d["k_cache"], v_cache=d["v_cache"])
-    del d
+    del d, lm
     return out
 
 

@@ -39,7 +39,8 @@ def test_library_exports_every_declared_symbol(M):
 
 def test_binding_names_match_the_abi(M):
     for n in ["medusa_resid_silu", "medusa_vocab_topk", "medusa_heads_forward", "medusa_build_tree",
-              "tree_attention_verify", "medusa_base_greedy", "medusa_accept"]:
+              "tree_attention_verify", "medusa_base_greedy", "medusa_accept", "medusa_pack_rows",
+              "medusa_decoder_verify"]:
         assert callable(getattr(M, n))
 
 
@@ -96,9 +97,30 @@ def test_workspace_sizes_are_positive(M):
     L = M._lib
     assert L.medusa_heads_workspace_size(1, 4096, 32000, 5, 4, M.BF16) >= 5 * 4096 * 4
     assert L.medusa_vocab_topk_workspace_size(8, 4096, 128256, 5, 4, M.BF16) > 0
-    assert L.medusa_base_greedy_workspace_size(64, 4096, 32000, M.BF16) >= 64 * 4096 * 2  # bf16 normalised rows
-    assert L.medusa_base_greedy_workspace_size(9, 256, 1000, M.F32) >= 9 * 256 * 4
+    assert L.medusa_base_greedy_workspace_size(64, 4096, 32000, M.BF16, M.PACKED) >= 64 * 4096 * 2  # bf16 rows
+    assert L.medusa_base_greedy_workspace_size(9, 256, 1000, M.F32, M.ROW_MAJOR) >= 9 * 256 * 4
     assert L.medusa_heads_workspace_size(0, 4096, 32000, 5, 4, M.BF16) == 0
+
+
+def test_packed_size(M):
+    # rows round up to whole 16-row fragments; cols must be a multiple of 32
+    assert M.packed_size(16, 32) == 16 * 32 * 2
+    assert M.packed_size(17, 64) == 32 * 64 * 2
+    assert M.packed_size(32000, 4096) == 32000 * 4096 * 2
+    assert M.packed_size(16, 48) == 0
+    assert M.packed_size(0, 64) == 0
+
+
+def test_pack_rows_argument_errors(M):
+    L = M._lib
+    d = ctypes.c_void_p(16)
+    assert L.medusa_pack_rows(d, 16, 48, d, 0, 16, None) == M.EUNSUPPORTED       # cols % 32
+    assert L.medusa_pack_rows(d, 16, 64, d, 8, 16, None) == M.EINVAL             # rows do not fit
+    assert L.medusa_pack_rows(None, 16, 64, d, 0, 16, None) == M.EINVAL
+    assert L.medusa_base_greedy(d, d, M.PACKED, 4, 256, 100, 1e-6, M.F32, d, None, d, 1 << 30, None) == \
+        M.EUNSUPPORTED                                                           # packed needs bf16
+    assert L.medusa_base_greedy(d, d, M.PACKED, 4, 264, 100, 1e-6, M.BF16, d, None, d, 1 << 30, None) == \
+        M.EUNSUPPORTED                                                           # H % 64
 
 
 def test_profiler_without_launches(M):

@@ -120,13 +120,13 @@ def test_decoder_verify_parity(name, mk):
     _say("oracle done,", len(ov), "lm_head overrides")
 
     # GPU
-    d_layers = [{m: dev(W[m]) for m in W} for W in layers]
+    d_layers = [M.pack_layer({m: dev(W[m]) for m in W}) for W in layers]
     k_cache = torch.stack([dev(c[0]) for c in caches])
     v_cache = torch.stack([dev(c[1]) for c in caches])
     tree = M.Tree(parent, rank, cfg.K, cfg.topk)
     greedy = torch.empty(B, N, dtype=torch.int32, device="cuda")
     hidden = torch.empty(B, N, cfg.H, device="cuda")
-    M.medusa_decoder_verify(d_layers, dev(emb), dev(lm_head), tree, dev(tok), dev(node_pos), dev(P), int(P.max()),
+    M.medusa_decoder_verify(d_layers, dev(emb), M.pack(dev(lm_head)), tree, dev(tok), dev(node_pos), dev(P), int(P.max()),
                             k_cache, v_cache, cfg.nH, greedy, hidden=hidden)
     torch.cuda.synchronize()
 
@@ -146,15 +146,15 @@ def test_decoder_verify_parity(name, mk):
 
 def test_decoder_argument_errors():
     import speculative_decoding_medusa_amd as M
-    cfg = _cfg("e", 1, 256, 100, mi.tiny_tree(), 4, 4, 64, (5,), 510, 1, 300)   # F not a multiple of 256
+    cfg = _cfg("e", 1, 256, 100, mi.tiny_tree(), 4, 4, 64, (5,), 510, 1, 288)   # F not a multiple of 64
     parent, rank = cfg.tree.arrays()
     tree = M.Tree(parent, rank, 5, 4)
-    W = {m: torch.zeros(shp, dtype=torch.bfloat16, device="cuda") for m, shp in mi.layer_shapes(cfg).items()}
+    W = M.pack_layer({m: torch.zeros(shp, dtype=torch.bfloat16, device="cuda") for m, shp in mi.layer_shapes(cfg).items()})
     emb = torch.zeros(cfg.V, cfg.H, dtype=torch.bfloat16, device="cuda")
     kc = torch.zeros(1, 1, 4, cfg.Lmax, 64, dtype=torch.bfloat16, device="cuda")
     tok = torch.zeros(1, cfg.N, dtype=torch.int32, device="cuda")
     g = torch.empty_like(tok)
     with pytest.raises(M.MedusaError) as e:
-        M.medusa_decoder_verify([W], emb, emb, tree, tok, tok, torch.zeros(1, dtype=torch.int32, device="cuda"), 5,
+        M.medusa_decoder_verify([W], emb, M.pack(emb), tree, tok, tok, torch.zeros(1, dtype=torch.int32, device="cuda"), 5,
                                 kc, kc.clone(), 4, g)
     assert e.value.status == M.EUNSUPPORTED

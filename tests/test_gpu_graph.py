@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import medusa_inputs as mi
-from medusa_testlib import dev
+from medusa_testlib import dev, lm_head_arg
 
 pytestmark = pytest.mark.gpu
 
@@ -48,7 +48,8 @@ def test_step_graph_replays_match_eager():
     ws_v = torch.empty(M.vocab_topk_workspace_size(B, H, V, K, topk, wdt), dtype=torch.uint8, device="cuda")
     ws_a = torch.empty(M.tree_attention_workspace_size(tree, B, cfg.nH, cfg.D, maxP, wdt), dtype=torch.uint8,
                        device="cuda")
-    ws_g = torch.empty(M.base_greedy_workspace_size(B * N, H, V, wdt), dtype=torch.uint8, device="cuda")
+    lm, layout = lm_head_arg(M, d["lm_head"])
+    ws_g = torch.empty(M.base_greedy_workspace_size(B * N, H, V, wdt, layout), dtype=torch.uint8, device="cuda")
     root_d = dev(root)
 
     def step():
@@ -58,7 +59,7 @@ def test_step_graph_replays_match_eager():
         M.medusa_build_tree(tree, b["ti"], root_d, d["cache_len"], b["tok"], b["pos"])
         M.tree_attention_verify(d["q"], d["k_tree"], d["v_tree"], d["k_cache"], d["v_cache"], d["cache_len"], maxP,
                                 tree, b["o"], ws=ws_a)
-        M.medusa_base_greedy(b["o"], d["lm_head"], b["g"], ws=ws_g)
+        M.medusa_base_greedy(b["o"], lm, b["g"], ws=ws_g)
         M.medusa_accept(tree, b["tok"], b["g"].view(B, N), b["al"], b["an"], b["ot"], d["cache_len"], b["ncl"],
                         k_cache=d["k_cache"], v_cache=d["v_cache"])
 

@@ -163,17 +163,19 @@ def test_tree_attention_parity(M, name, mk):
 
 
 GREEDY_CASES = [
-    ("f32_r9_v1000", "f32", 9, 256, 1000),
-    ("bf16_r64_h1024_v5000", "bf16", 64, 1024, 5000),
-    ("bf16_r13_h4096_v3001", "bf16", 13, 4096, 3001),
-    ("bf16_r100_h1024_v2000", "bf16", 100, 1024, 2000),     # 128-node MFMA tiles
-    ("bf16_r200_h512_v1537", "bf16", 200, 512, 1537),       # 256-node MFMA tiles, 2nd tile ragged
-    ("bf16_r5_h520_v999_gemv", "bf16", 5, 520, 999),        # H not a multiple of the MFMA k-chunk
+    ("f32_r9_v1000", "f32", 9, 256, 1000, "rows"),
+    ("bf16_r64_h1024_v5000", "bf16", 64, 1024, 5000, "packed"),
+    ("bf16_r64_h1024_v5000_gemv", "bf16", 64, 1024, 5000, "rows"),
+    ("bf16_r13_h4096_v3001", "bf16", 13, 4096, 3001, "packed"),
+    ("bf16_r100_h1024_v2000", "bf16", 100, 1024, 2000, "packed"),   # 128-node MFMA tiles
+    ("bf16_r200_h512_v1537", "bf16", 200, 512, 1537, "packed"),     # 256-node MFMA tiles, ragged vocabulary
+    ("bf16_r300_h256_v1000", "bf16", 300, 256, 1000, "packed"),     # two 256-node tiles, the second ragged
+    ("bf16_r5_h520_v999_gemv", "bf16", 5, 520, 999, "rows"),        # H not a multiple of the MFMA k-chunk
 ]
 
 
-@pytest.mark.parametrize("name,dtype,R,H,V", GREEDY_CASES, ids=[c[0] for c in GREEDY_CASES])
-def test_base_greedy_parity(M, name, dtype, R, H, V):
+@pytest.mark.parametrize("name,dtype,R,H,V,layout", GREEDY_CASES, ids=[c[0] for c in GREEDY_CASES])
+def test_base_greedy_parity(M, name, dtype, R, H, V, layout):
     _say("base_greedy", name)
     cfg = _cfg("g", dtype, 1, H, V, 1, 1, mi.tiny_tree(), seed=300 + R)
     heads = {"lm_head": mi.normal((V, H), cfg.seed, mi.S_LM_HEAD, 0.02, dtype)}
@@ -184,10 +186,44 @@ def test_base_greedy_parity(M, name, dtype, R, H, V):
     g_ref, lg_ref = oracle.base_greedy(xw, oracle.widen(heads["lm_head"], dtype), 1e-6, dtype == "bf16")
     g = torch.empty(R, dtype=torch.int32, device="cuda")
     lg = torch.empty(R, V, device="cuda")
-    M.medusa_base_greedy(dev(x), dev(heads["lm_head"]), g, eps=1e-6, logits=lg)
+    lm = dev(heads["lm_head"])
+    if layout == "packed":
+        lm = M.pack(lm)
+    M.medusa_base_greedy(dev(x), lm, g, eps=1e-6, logits=lg)
     torch.cuda.synchronize()
     np.testing.assert_allclose(host_f64(lg), lg_ref, rtol=0, atol=tol(dtype))
     assert np.array_equal(g.cpu().numpy(), g_ref)
+
+
+def _pack_layout(W):
+    """Row r, column k of a [rows][K] matrix -> element
+    ((r // 16) * (K // 32) + k // 32) * 512 + ((k % 32) // 8 * 16 + r % 16) * 8 + k % 8
+    of the packed buffer (padding rows zero)."""
+    rows, K = W.shape
+    rp = -(-rows // 16) * 16
+    out = np.zeros(rp * K, dtype=W.dtype)
+    r = np.arange(rows)[:, None]
+    k = np.arange(K)[None, :]
+    idx = ((r // 16) * (K // 32) + k // 32) * 512 + ((k % 32) // 8 * 16 + r % 16) * 8 + k % 8
+    out[idx.ravel()] = W.ravel()
+    return out
+
+
+@pytest.mark.parametrize("shapes", [[(16, 32)], [(37, 64)], [(4096, 96), (1024, 96), (1024, 96)], [(5, 256), (3, 256)]],
+                         ids=["one_block", "ragged_rows", "stacked_qkv", "stacked_ragged"])
+def test_pack_rows_layout(M, shapes):
+    _say("pack_rows", shapes)
+    r = np.random.default_rng(7)
+    mats = [r.integers(0, 1 << 16, size=s, dtype=np.uint16) for s in shapes]
+    want = _pack_layout(np.concatenate(mats))
+    dst = M.Packed(torch.full((M.packed_size(sum(s[0] for s in shapes), shapes[0][1]) // 2,), -1, dtype=torch.int16,
+                              device="cuda"), sum(s[0] for s in shapes), shapes[0][1])
+    r0 = 0
+    for m in mats:
+        M.medusa_pack_rows(torch.from_numpy(m.view(np.int16)).cuda(), dst, r0)
+        r0 += m.shape[0]
+    torch.cuda.synchronize()
+    assert np.array_equal(dst.data.cpu().numpy().view(np.uint16), want)
 
 
 def _planted_greedy(tree, tk, tok, truth):
