@@ -37,16 +37,28 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 # calibration (profiles/medusa_step_hbm_counters__vicuna7b_sparse64.txt).
 # Valid only for the kernel sources they were taken on (sha256 prefix of
 # heads.hip + common.hpp); reported as null after any change to them.
-VOCAB_TRAFFIC = {"sources_sha256_16": "9c703bb2f9bdf3df", "read_bytes": 1311508573, "write_bytes": 128114}
+VOCAB_TRAFFIC = {"sources_sha256_16": "009e083c90dc20a3", "read_bytes": 1311508042, "write_bytes": 128090}
+# the same for the gate|up projection of the 32-layer workload (one layer's
+# launch: 64 x 4096 node rows against 22016 packed weight rows, 2 splits)
+GATE_UP_TRAFFIC = {"sources_sha256_16": "6dbed1afd9b7404d", "read_bytes": 188534752, "write_bytes": 11272642}
+
+
+def _traffic_bytes(rec, sources):
+    """Counter-measured bytes of a kernel, or None once its sources changed."""
+    import hashlib
+    csrc = os.path.join(ROOT, "speculative_decoding_medusa_amd", "csrc")
+    data = b"".join(open(os.path.join(csrc, f), "rb").read() for f in sources)
+    if hashlib.sha256(data).hexdigest()[:16] != rec["sources_sha256_16"]:
+        return None
+    return rec["read_bytes"] + rec["write_bytes"]
 
 
 def vocab_traffic_bytes():
-    import hashlib
-    csrc = os.path.join(ROOT, "speculative_decoding_medusa_amd", "csrc")
-    data = b"".join(open(os.path.join(csrc, f), "rb").read() for f in ("heads.hip", "common.hpp"))
-    if hashlib.sha256(data).hexdigest()[:16] != VOCAB_TRAFFIC["sources_sha256_16"]:
-        return None
-    return VOCAB_TRAFFIC["read_bytes"] + VOCAB_TRAFFIC["write_bytes"]
+    return _traffic_bytes(VOCAB_TRAFFIC, ("heads.hip", "common.hpp"))
+
+
+def gate_up_traffic_bytes():
+    return _traffic_bytes(GATE_UP_TRAFFIC, ("skinny_mfma.hpp", "decoder.hip", "common.hpp"))
 METRIC = "Medusa steps/sec + tree-verify tokens/sec (64-node tree, 7B shape), % of HBM roofline"
 
 
@@ -416,7 +428,8 @@ def bench_decoder(args, cfg):
         "kernels_us_per_step": {k: round(v, 2) for k, v in sorted(per_step_us.items(), key=lambda kv: -kv[1])},
         "wall_ms_per_step": round(1e3 * wall / args.steps, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "dec_gemm_gate_up",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": gate_up_traffic_bytes(),
+                     "kernel": "dec_gemm_gate_up",
                      "bytes_per_launch": gu_bytes, "avg_us": round(gu_us, 2)},
         "input_gen_s": round(gen_s, 2),
     }
