@@ -22,7 +22,7 @@ Sources, cited by page title and section (the pages are public web text):
   acceptance-flag string.
 
 Every function below states the passage it follows.  Where the pages are silent
-the reading taken is named in the docstring (and listed in the design doc).
+the reading taken is named in the docstring.
 
 The tree-verify pass through a Llama-shaped decoder (``decoder.py``) follows
 the same section: the verify pass is the base model's forward pass over all

@@ -8,7 +8,7 @@ decoder, so the verify step of the 32-layer workload runs every tree token
 through every layer with the tree-masked attention of ``tree_attention``.
 
 The pages fix no decoder internals; the layer is the standard Llama shape the
-workload names (readings listed in the design doc):
+workload names (readings taken):
 
 * pre-norm residual blocks: x += Wo . Attn(RoPE(Wq n), RoPE(Wk n), Wv n) with
   n = RMSNorm(x); then x += Wdown . (SiLU(Wgate n') * (Wup n')) with
