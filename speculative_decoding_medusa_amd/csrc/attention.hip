@@ -404,7 +404,9 @@ __global__ __launch_bounds__(WAVES * 64) void tree_attn_mfma_kernel(
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
             const float m_new = fmaxf(m[qb], tmax);
             const bool live = m_new != -INFINITY;
-            const float alpha = live ? exp2f(m[qb] - m_new) : 1.f;
+            // exponents are <= 0: the bare v_exp_f32 (no denormal range fix-up;
+            // results below 2^-126 vanish in the fp16 probabilities anyway)
+            const float alpha = live ? __builtin_amdgcn_exp2f(m[qb] - m_new) : 1.f;
             float psum = 0.f;
             uint32_t pk[KB][2];  // fp16 pairs of P^T (round to nearest even)
 #pragma unroll
@@ -412,7 +414,7 @@ __global__ __launch_bounds__(WAVES * 64) void tree_attn_mfma_kernel(
                 float p4[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    p4[r] = live ? exp2f(st[kb][r] - m_new) : 0.f;
+                    p4[r] = live ? __builtin_amdgcn_exp2f(st[kb][r] - m_new) : 0.f;
                     psum += p4[r];
                 }
                 pk[kb][0] = pack_f16x2(p4[0], p4[1]);
@@ -422,8 +424,12 @@ __global__ __launch_bounds__(WAVES * 64) void tree_attn_mfma_kernel(
             psum += __shfl_xor(psum, 32, 64);
             l[qb] = l[qb] * alpha + psum;
             m[qb] = m_new;
+            // the accumulators live in AGPRs, so a rescale costs three instructions
+            // per element: skip it when no query of the wave raised its max
+            if (__any(alpha != 1.f)) {
 #pragma unroll
-            for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
+                for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
+            }
 #pragma unroll
             for (int k2 = 0; k2 < TK / 32; ++k2) {
                 const u32x4 bp = (u32x4){pk[2 * k2][0], pk[2 * k2][1], pk[2 * k2 + 1][0], pk[2 * k2 + 1][1]};

@@ -192,32 +192,46 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ p
 // host side
 // ---------------------------------------------------------------------------
 struct GemmSplit {
-    int S;    // splits of the contraction
-    int cps;  // k-chunks per split
+    int S;      // splits of the contraction
+    int cps;    // k-chunks per split
+    int waves;  // waves per workgroup (16 weight rows each)
 };
 
-// Splits of the contraction (whole k-chunks each, at most 16).  Every
-// workgroup of a product is resident at once, so a count just past a multiple
-// of the CU count leaves most CUs idle while the last round streams: pick the
-// split count whose workgroups fill their rounds best, discounted 3% per
-// extra split for the partial sums it writes and reads back (measured on the
-// Llama-7B projections with 64 rows: 4, 4, 2 and 4 splits for q|k|v, o,
-// gate|up and down).
+// Workgroup shape and splits of the contraction (whole k-chunks each, at most
+// 16), measured on the Llama-7B projections with 64 node rows:
+// * wide products (>= 8192 weight rows) stream best from 8-wave workgroups
+//   with as few splits as keep >= 160 workgroups in flight -- more waves per
+//   CU keep more weight bytes in flight, and every split costs a round trip
+//   of fp32 partial sums (q|k|v: 2 splits, gate|up: 1);
+// * narrow ones (o, down: 4096 rows) need 4-wave workgroups and the split
+//   count whose workgroups fill whole rounds of the 256 CUs best, discounted
+//   3% per extra split (4 splits).
 constexpr int GPU_CUS = 256;
+constexpr int WIDE_PRODUCT_ROWS = 8192;
+constexpr int WIDE_MIN_WG = 160;
 static GemmSplit gemm_split(int R, int K, int ncols) {
     const int nblk = lmh_nblk(R);
     const int nchunk = K / lmh_kc(nblk);
-    const long long tiles = (long long)((ncols + LMH_ROWS - 1) / LMH_ROWS) * ((R + nblk * 16 - 1) / (nblk * 16));
-    GemmSplit best{1, nchunk};
+    const long long node_tiles = (R + nblk * 16 - 1) / (nblk * 16);
+    auto make = [&](int S, int waves) {
+        S = std::max(1, std::min(S, std::min(16, nchunk)));
+        const int cps = (nchunk + S - 1) / S;
+        return GemmSplit{(nchunk + cps - 1) / cps, cps, waves};
+    };
+    if (ncols >= WIDE_PRODUCT_ROWS) {
+        const long long tiles = (long long)((ncols + 16 * 8 - 1) / (16 * 8)) * node_tiles;
+        return make((int)((WIDE_MIN_WG + tiles - 1) / tiles), 8);
+    }
+    const long long tiles = (long long)((ncols + LMH_ROWS - 1) / LMH_ROWS) * node_tiles;
+    GemmSplit best = make(1, LMH_WAVES);
     double best_score = -1.0;
     for (int S = 1; S <= std::min(16, nchunk); ++S) {
-        const int cps = (nchunk + S - 1) / S;
-        const int se = (nchunk + cps - 1) / cps;  // splits actually used
-        const double rounds = (double)(tiles * se) / GPU_CUS;
-        const double score = rounds / std::ceil(rounds) * (1.0 - 0.03 * (se - 1));
+        const GemmSplit g = make(S, LMH_WAVES);
+        const double rounds = (double)(tiles * g.S) / GPU_CUS;
+        const double score = rounds / std::ceil(rounds) * (1.0 - 0.03 * (g.S - 1));
         if (score > best_score + 1e-9) {
             best_score = score;
-            best = GemmSplit{se, cps};
+            best = g;
         }
     }
     return best;
@@ -226,16 +240,20 @@ static GemmSplit gemm_split(int R, int K, int ncols) {
 static void launch_skinny_partial(const bf16_t* n, const bf16_t* w, int R, int K, int ncols, const GemmSplit& sp,
                                   float* part, hipStream_t s, const char* name) {
     const int nblk = lmh_nblk(R);
-    const dim3 grid((ncols + LMH_ROWS - 1) / LMH_ROWS, (R + nblk * 16 - 1) / (nblk * 16), sp.S);
-    if (nblk == 4)
-        MEDUSA_LAUNCH(name, (skinny_mfma_kernel<4, SKINNY_PARTIAL>), grid, dim3(256), 0, s, n, w, R, K, ncols, sp.cps,
-                      nullptr, nullptr, part);
-    else if (nblk == 8)
-        MEDUSA_LAUNCH(name, (skinny_mfma_kernel<8, SKINNY_PARTIAL>), grid, dim3(256), 0, s, n, w, R, K, ncols, sp.cps,
-                      nullptr, nullptr, part);
-    else
-        MEDUSA_LAUNCH(name, (skinny_mfma_kernel<16, SKINNY_PARTIAL>), grid, dim3(256), 0, s, n, w, R, K, ncols, sp.cps,
-                      nullptr, nullptr, part);
+    const dim3 grid((ncols + 16 * sp.waves - 1) / (16 * sp.waves), (R + nblk * 16 - 1) / (nblk * 16), sp.S);
+#define SKINNY_PARTIAL_LAUNCH(NB, WV)                                                                              \
+    MEDUSA_LAUNCH(name, (skinny_mfma_kernel<NB, SKINNY_PARTIAL, WV>), grid, dim3(WV * 64), 0, s, n, w, R, K, ncols, \
+                  sp.cps, nullptr, nullptr, part)
+    if (sp.waves == 8) {
+        if (nblk == 4) SKINNY_PARTIAL_LAUNCH(4, 8);
+        else if (nblk == 8) SKINNY_PARTIAL_LAUNCH(8, 8);
+        else SKINNY_PARTIAL_LAUNCH(16, 8);
+    } else {
+        if (nblk == 4) SKINNY_PARTIAL_LAUNCH(4, 4);
+        else if (nblk == 8) SKINNY_PARTIAL_LAUNCH(8, 4);
+        else SKINNY_PARTIAL_LAUNCH(16, 4);
+    }
+#undef SKINNY_PARTIAL_LAUNCH
 }
 
 static size_t a256(size_t x) { return (x + 255) / 256 * 256; }

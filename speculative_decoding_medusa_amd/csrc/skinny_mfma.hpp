@@ -10,10 +10,10 @@
 // v_mfma_f32_16x16x32_bf16 sits in a wave (lane l: row l % 16, k = 8 (l / 16)
 // .. +7), so every weight load of a wave is one coalesced 1 KB read.
 //
-// Grid (ceil(V / 64), ceil(R / NODES), splits); 4 waves per workgroup, each
-// wave owns one 16-row block against NODES node rows.  Weight fragments stream
+// Grid (ceil(V / (16 WAVES)), ceil(R / NODES), splits); WAVES waves per
+// workgroup, each owning one 16-row block against NODES node rows.  Weight fragments stream
 // into registers (non-temporal) up to D - 1 k-chunks ahead; the node rows are
-// staged in LDS in k-chunks shared by the 4 waves (double-buffered, one
+// staged in LDS in k-chunks shared by the waves (double-buffered, one
 // barrier per chunk).  Every load is issued unconditionally -- rows past the
 // end read a clamped valid row whose results the epilogue discards -- so the
 // compiler can count outstanding loads exactly and wait for each chunk alone.
@@ -34,10 +34,10 @@ constexpr int PACK_FRAG = PACK_ROWS * PACK_K;      // elements per fragment (1 K
 inline int lmh_nblk(int R) { return R <= 64 ? 4 : R <= 128 ? 8 : 16; }
 inline int lmh_kc(int nblk) { return nblk <= 8 ? 64 : 32; }
 
-constexpr int LMH_WAVES = 4;
+constexpr int LMH_WAVES = 4;                       // waves per workgroup of the products
 constexpr int LMH_ROWS = LMH_WAVES * PACK_ROWS;    // weight rows per workgroup
 
-template <int NBLK>
+template <int NBLK, int WAVES = LMH_WAVES>
 struct LmhCfg {
     static constexpr int NODES = NBLK * 16;
     // k per chunk and register-ring depth (measured on 64 x 4096 x 32000:
@@ -46,9 +46,10 @@ struct LmhCfg {
     static constexpr int KC = NBLK <= 8 ? 64 : 32;
     static constexpr int KS = KC / PACK_K;             // MFMA k-steps per chunk
     static constexpr int LDW = KC + 8;                 // padded LDS row (bf16): conflict-free B reads
-    static constexpr int NPT = NODES * KC / 8 / 256;   // 16-byte node pieces per thread per chunk
+    static constexpr int NT = WAVES * 64;
+    static constexpr int NPT = NODES * KC / 8 / NT;    // 16-byte node pieces per thread per chunk
     static constexpr int D = NBLK <= 4 ? 4 : 3;        // chunks in flight per register ring
-    static_assert(NPT * 256 * 8 == NODES * KC, "node stage must split evenly over 256 threads");
+    static_assert(NPT * NT * 8 == NODES * KC, "node stage must split evenly over the threads");
 };
 
 // Pipeline (one barrier per chunk): step c issues the node rows and then the
@@ -58,25 +59,26 @@ struct LmhCfg {
 // loads go out before the weight loads of the same step: vector-memory loads
 // complete in issue order, so waiting for a chunk's node rows never waits for
 // younger weight fragments.
-template <int NBLK, int EPI>
-__global__ __launch_bounds__(256) void skinny_mfma_kernel(const bf16_t* __restrict__ n,   // [R][K] node rows
+template <int NBLK, int EPI, int WAVES = LMH_WAVES>
+__global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* __restrict__ n,   // [R][K] node rows
                                                           const bf16_t* __restrict__ Wp,  // packed, V rows of K
                                                           int R, int K, int V, int chunks_per_split,
                                                           float* __restrict__ cand_val,
                                                           int* __restrict__ cand_idx,  // ARGMAX: [R][G]
                                                           float* __restrict__ out) {
     // ARGMAX: out = optional logits [R][V];  PARTIAL: out = [splits][R][V]
-    using C = LmhCfg<NBLK>;
+    using C = LmhCfg<NBLK, WAVES>;
     constexpr int D = C::D;
+    constexpr int NT = C::NT;
     __shared__ __attribute__((aligned(16))) bf16_t ns[2][C::NODES][C::LDW];
-    __shared__ float red_v[LMH_WAVES][EPI == SKINNY_ARGMAX ? C::NODES : 1];
-    __shared__ int red_i[LMH_WAVES][EPI == SKINNY_ARGMAX ? C::NODES : 1];
+    __shared__ float red_v[WAVES][EPI == SKINNY_ARGMAX ? C::NODES : 1];
+    __shared__ int red_i[WAVES][EPI == SKINNY_ARGMAX ? C::NODES : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int G = gridDim.x;
     const int node0 = blockIdx.y * C::NODES;
-    const int rb = blockIdx.x * LMH_WAVES + wave;     // this wave's 16-row block
+    const int rb = blockIdx.x * WAVES + wave;         // this wave's 16-row block
     const int vw = rb * PACK_ROWS;                    // its first weight row
     const int lr = lane & 15, lk = lane >> 4;         // row / k-group within a 16x16x32 tile
     const int nrb = (V + PACK_ROWS - 1) / PACK_ROWS;
@@ -93,7 +95,7 @@ __global__ __launch_bounds__(256) void skinny_mfma_kernel(const bf16_t* __restri
     int k8p[C::NPT];
 #pragma unroll
     for (int e = 0; e < C::NPT; ++e) {
-        const int p = tid + e * 256;
+        const int p = tid + e * NT;
         const int r = p / (C::KC / 8);
         k8p[e] = p - r * (C::KC / 8);
         nrow[e] = n + (size_t)min(node0 + r, R - 1) * K;
@@ -115,7 +117,7 @@ __global__ __launch_bounds__(256) void skinny_mfma_kernel(const bf16_t* __restri
     auto store_n = [&](const u32x4(&src)[C::NPT], int stage) {
 #pragma unroll
         for (int e = 0; e < C::NPT; ++e) {
-            const int r = (tid + e * 256) / (C::KC / 8);
+            const int r = (tid + e * NT) / (C::KC / 8);
             *(u32x4*)(&ns[stage][r][k8p[e] * 8]) = src[e];
         }
     };
@@ -194,11 +196,11 @@ __global__ __launch_bounds__(256) void skinny_mfma_kernel(const bf16_t* __restri
         if (lane < 16) { red_v[wave][b * 16 + lane] = bv; red_i[wave][b * 16 + lane] = bi; }
     }
     __syncthreads();
-    for (int j = tid; j < C::NODES; j += 256) {
+    for (int j = tid; j < C::NODES; j += NT) {
         float bv = red_v[0][j];
         int bi = red_i[0][j];
 #pragma unroll
-        for (int w = 1; w < LMH_WAVES; ++w)
+        for (int w = 1; w < WAVES; ++w)
             if (better(red_v[w][j], red_i[w][j], bv, bi)) { bv = red_v[w][j]; bi = red_i[w][j]; }
         const int node = node0 + j;
         if (node < R) {
