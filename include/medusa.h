@@ -167,17 +167,20 @@ medusa_status tree_attention_verify(const void* q, const void* k_tree, const voi
  *   ((r / 16) * (cols / 32) + k / 32) * 512 + ((k % 32) / 8 * 16 + r % 16) * 8 + k % 8
  * (every 16 x 32 tile is one contiguous 1 KB fragment) and occupies
  * medusa_packed_size(rows, cols) bytes (rows rounded up to 16).
- *   medusa_pack_rows: src [rows][cols] row-major bf16 (device) -> packed rows
- *   dst_row0 .. dst_row0 + rows - 1 of dst, a packed matrix of dst_rows rows.
- *   Several matrices stack into one by packing each at its row offset (the
- *   decoder's q|k|v and gate|up); the call that ends at dst_rows also zeroes
- *   the padding rows.  Asynchronous on `stream`; src must stay valid until
- *   the copy has run.
+ *   medusa_pack_rows: src [rows][cols] row-major bf16 (device) -> rows of dst,
+ *   a packed matrix of dst_rows rows.  interleave == 1: source row i goes to
+ *   packed row dst_row0 + i, so several matrices stack into one by packing
+ *   each at its row offset (the decoder's q|k|v); the call that ends at
+ *   dst_rows also zeroes the padding rows.  interleave == n > 1: source row i
+ *   goes to packed row dst_row0 + (i / 16) * 16 n + i % 16, so n matrices
+ *   packed with dst_row0 = 0, 16, .. 16 (n - 1) alternate in blocks of 16
+ *   rows (the decoder's gate|up; rows and dst_row0 multiples of 16).
+ *   Asynchronous on `stream`; src must stay valid until the copy has run.
  * Limits: cols % 32 == 0.  medusa_packed_size returns 0 for invalid sizes.
  * ------------------------------------------------------------------------- */
 size_t medusa_packed_size(int rows, int cols);
 medusa_status medusa_pack_rows(const void* src, int rows, int cols, void* dst, int dst_row0, int dst_rows,
-                               void* stream);
+                               int interleave, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Step a5 -- the base model's greedy choice after every tree node (tree
@@ -239,7 +242,9 @@ medusa_status medusa_accept(const medusa_tree* tree, const int32_t* node_tok, co
  *   layers (host array [n_layers]): each layer's weights, [out][in] matrices
  *     packed by medusa_pack_rows: wqkv = W_q [nH*D][H], W_k and W_v
  *     [nKV*D][H] stacked in that order ((nH + 2 nKV) D rows); wo [H][nH*D];
- *     w_gate_up = W_gate and W_up [F][H] stacked (2F rows); w_down [H][F];
+ *     w_gate_up = W_gate and W_up [F][H] interleaved in blocks of 16 rows
+ *     (interleave 2: gate rows 16j.. at packed block 2j, up rows at 2j + 1);
+ *     w_down [H][F];
  *   embedding [V][H] row-major;  lm_head [V][H] packed;
  *   node_tok, node_pos [B][N] int32 (medusa_build_tree's outputs; token ids
  *     outside [0, V) read row 0 of the embedding);  cache_len [B];

@@ -46,7 +46,7 @@ _SIGS = {
     "tree_attention_verify": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                                _vp, _vp, _sz, _vp], _i32),
     "medusa_packed_size": ([_i32, _i32], _sz),
-    "medusa_pack_rows": ([_vp, _i32, _i32, _vp, _i32, _i32, _vp], _i32),
+    "medusa_pack_rows": ([_vp, _i32, _i32, _vp, _i32, _i32, _i32, _vp], _i32),
     "medusa_base_greedy_workspace_size": ([_i32, _i32, _i32, _i32, _i32], _sz),
     "medusa_base_greedy": ([_vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
     "medusa_accept": ([_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32,
@@ -237,16 +237,17 @@ def packed_size(rows: int, cols: int) -> int:
     return _lib.medusa_packed_size(rows, cols)
 
 
-def medusa_pack_rows(src, dst: Packed, dst_row0: int = 0, stream=None):
+def medusa_pack_rows(src, dst: Packed, dst_row0: int = 0, interleave: int = 1, stream=None):
     rows, cols = src.shape
     _check("medusa_pack_rows", _lib.medusa_pack_rows(_p(src), rows, cols, _p(dst.data), int(dst_row0), dst.rows,
-                                                     _stream(stream)))
+                                                     int(interleave), _stream(stream)))
     return dst
 
 
-def pack(*mats, stream=None) -> Packed:
-    """Pack bf16 [rows_i][cols] matrices (stacked in the given order) into one
-    packed matrix."""
+def pack(*mats, interleave: bool = False, stream=None) -> Packed:
+    """Pack bf16 [rows_i][cols] matrices into one packed matrix: stacked in the
+    given order, or (interleave) alternating in blocks of 16 rows (equal row
+    counts, multiples of 16)."""
     cols = mats[0].shape[1]
     rows = sum(m.shape[0] for m in mats)
     nbytes = packed_size(rows, cols)
@@ -254,10 +255,13 @@ def pack(*mats, stream=None) -> Packed:
         raise MedusaError("medusa_packed_size", EUNSUPPORTED)
     dst = Packed(torch.empty(nbytes // 2, dtype=torch.bfloat16, device=mats[0].device), rows, cols)
     r0 = 0
-    for m in mats:
+    for i, m in enumerate(mats):
         assert m.shape[1] == cols and m.dtype == torch.bfloat16 and m.is_contiguous()
-        medusa_pack_rows(m, dst, r0, stream)
-        r0 += m.shape[0]
+        if interleave:
+            medusa_pack_rows(m, dst, 16 * i, len(mats), stream)
+        else:
+            medusa_pack_rows(m, dst, r0, 1, stream)
+            r0 += m.shape[0]
     return dst
 
 
@@ -320,7 +324,8 @@ def pack_layer(W, stream=None):
     """Row-major bf16 layer weights {wq, wk, wv, wo, w_gate, w_up, w_down}
     -> the packed matrices medusa_decoder_verify reads."""
     return {"wqkv": pack(W["wq"], W["wk"], W["wv"], stream=stream), "wo": pack(W["wo"], stream=stream),
-            "w_gate_up": pack(W["w_gate"], W["w_up"], stream=stream), "w_down": pack(W["w_down"], stream=stream)}
+            "w_gate_up": pack(W["w_gate"], W["w_up"], interleave=True, stream=stream),
+            "w_down": pack(W["w_down"], stream=stream)}
 
 
 def decoder_workspace_size(tree: Tree, B, H, nH, nKV, D, F, V, max_cache_len):

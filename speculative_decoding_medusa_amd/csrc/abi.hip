@@ -46,7 +46,8 @@ struct LayerPtrs {
     const bf16_t *wqkv, *wo, *w_gate_up, *w_down;
 };
 size_t packed_elems(int rows, int K);
-void launch_pack_rows(const bf16_t* src, int rows, int K, bf16_t* dst, int dst_row0, int dst_rows, hipStream_t s);
+void launch_pack_rows(const bf16_t* src, int rows, int K, bf16_t* dst, int dst_row0, int dst_rows, int inter,
+                      hipStream_t s);
 size_t decoder_workspace_bytes(int B, int N, int H, int nH, int nKV, int D, int F, int V, int max_cache_len);
 void launch_decoder_verify(const LayerPtrs* layers, int n_layers, const bf16_t* E, const bf16_t* lm_head,
                            const TreeDev& t, const int32_t* node_tok, const int32_t* node_pos,
@@ -428,14 +429,23 @@ size_t medusa_packed_size(int rows, int cols) {
 }
 
 medusa_status medusa_pack_rows(const void* src, int rows, int cols, void* dst, int dst_row0, int dst_rows,
-                               void* stream) {
+                               int interleave, void* stream) {
     return guarded("medusa_pack_rows", [&] {
         REQUIRE(src && dst, "null pointer argument");
         REQUIRE(rows >= 1 && cols >= 1, "rows and cols must be positive");
         SUPPORT(cols % 32 == 0, "cols=%d must be a multiple of 32", cols);
-        REQUIRE(dst_row0 >= 0 && (int64_t)dst_row0 + rows <= dst_rows,
-                "rows [%d, %d) do not fit the %d packed rows", dst_row0, dst_row0 + rows, dst_rows);
-        launch_pack_rows((const bf16_t*)src, rows, cols, (bf16_t*)dst, dst_row0, dst_rows, (hipStream_t)stream);
+        REQUIRE(interleave >= 1, "interleave must be >= 1");
+        if (interleave == 1) {
+            REQUIRE(dst_row0 >= 0 && (int64_t)dst_row0 + rows <= dst_rows,
+                    "rows [%d, %d) do not fit the %d packed rows", dst_row0, dst_row0 + rows, dst_rows);
+        } else {
+            REQUIRE(rows % 16 == 0 && dst_row0 % 16 == 0 && dst_row0 >= 0 && dst_row0 < 16 * interleave,
+                    "interleaved packing needs rows and dst_row0 multiples of 16, dst_row0 < 16 * interleave");
+            REQUIRE((int64_t)dst_row0 + (int64_t)(rows / 16 - 1) * 16 * interleave + 16 <= dst_rows,
+                    "interleaved rows do not fit the %d packed rows", dst_rows);
+        }
+        launch_pack_rows((const bf16_t*)src, rows, cols, (bf16_t*)dst, dst_row0, dst_rows, interleave,
+                         (hipStream_t)stream);
     });
 }
 

@@ -174,8 +174,10 @@ __global__ __launch_bounds__(RN_THREADS) void residual_rmsnorm_kernel(const floa
     }
 }
 
-// a[r][c] = bf16(SiLU(g) * u) with g = column c and u = column F + c of the
-// summed gate|up partials [S][R][2F].  Grid (ceil(F / 256), R).
+// a[r][c] = bf16(SiLU(g) * u) from the summed gate|up partials [S][R][2F],
+// whose columns interleave gate and up in blocks of 16: g at column
+// 32 (c / 16) + c % 16, u 16 columns later.  Grid (ceil(F / 256), R).  (An
+// unsplit gate|up product applies this in its own epilogue instead.)
 __global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ part, int S, int R, int F,
                                                      bf16_t* __restrict__ a) {
     const int r = blockIdx.y;
@@ -183,8 +185,9 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ p
     if (c >= F) return;
     const size_t stride = (size_t)R * 2 * F;
     const size_t row = (size_t)r * 2 * F;
-    const float g = sum_splits(part, S, stride, row + c);
-    const float u = sum_splits(part, S, stride, row + F + c);
+    const size_t gc = row + (size_t)(c / 16) * 32 + c % 16;
+    const float g = sum_splits(part, S, stride, gc);
+    const float u = sum_splits(part, S, stride, gc + 16);
     a[(size_t)r * F + c] = f32_to_bf16(g / (1.f + __expf(-g)) * u);
 }
 
@@ -256,6 +259,27 @@ static void launch_skinny_partial(const bf16_t* n, const bf16_t* w, int R, int K
 #undef SKINNY_PARTIAL_LAUNCH
 }
 
+// unsplit gate|up product with the SwiGLU epilogue: a = bf16(SiLU(g) * u)
+static void launch_skinny_swiglu(const bf16_t* n, const bf16_t* w, int R, int K, int F, const GemmSplit& sp, bf16_t* a,
+                                 hipStream_t s) {
+    const int nblk = lmh_nblk(R);
+    const dim3 grid((2 * F + 16 * sp.waves - 1) / (16 * sp.waves), (R + nblk * 16 - 1) / (nblk * 16), 1);
+    float* out = (float*)a;
+#define SKINNY_SWIGLU_LAUNCH(NB, WV)                                                                             \
+    MEDUSA_LAUNCH("dec_gemm_gate_up", (skinny_mfma_kernel<NB, SKINNY_SWIGLU, WV>), grid, dim3(WV * 64), 0, s, n, w, \
+                  R, K, 2 * F, sp.cps, nullptr, nullptr, out)
+    if (sp.waves == 8) {
+        if (nblk == 4) SKINNY_SWIGLU_LAUNCH(4, 8);
+        else if (nblk == 8) SKINNY_SWIGLU_LAUNCH(8, 8);
+        else SKINNY_SWIGLU_LAUNCH(16, 8);
+    } else {
+        if (nblk == 4) SKINNY_SWIGLU_LAUNCH(4, 4);
+        else if (nblk == 8) SKINNY_SWIGLU_LAUNCH(8, 4);
+        else SKINNY_SWIGLU_LAUNCH(16, 4);
+    }
+#undef SKINNY_SWIGLU_LAUNCH
+}
+
 static size_t a256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct DecoderWs {
@@ -307,7 +331,8 @@ static DecoderWs carve(void* ws, int B, int N, int H, int nH, int nKV, int D, in
 }
 
 // packed weights of one layer: q|k|v stacked ((nH + 2 nKV) D rows of H),
-// o (H rows of nH D), gate|up stacked (2F rows of H), down (H rows of F)
+// o (H rows of nH D), gate|up interleaved in 16-row blocks (2F rows of H),
+// down (H rows of F)
 struct LayerPtrs {
     const bf16_t *wqkv, *wo, *w_gate_up, *w_down;
 };
@@ -343,8 +368,13 @@ void launch_decoder_verify(const LayerPtrs* layers, int n_layers, const bf16_t* 
         launch_skinny_partial(w.o, L.wo, R, nH * D, H, sp_o, w.part, s, "dec_gemm_o");
         MEDUSA_LAUNCH("residual_rmsnorm", residual_rmsnorm_kernel, dim3(R), dim3(RN_THREADS), 0, s, w.part, sp_o.S, R,
                       H, eps, w.x, w.n);
-        launch_skinny_partial(w.n, L.w_gate_up, R, H, 2 * F, sp_gu, w.part, s, "dec_gemm_gate_up");
-        MEDUSA_LAUNCH("swiglu", swiglu_kernel, dim3((F + 255) / 256, R), dim3(256), 0, s, w.part, sp_gu.S, R, F, w.a);
+        if (sp_gu.S == 1) {
+            launch_skinny_swiglu(w.n, L.w_gate_up, R, H, F, sp_gu, w.a, s);
+        } else {
+            launch_skinny_partial(w.n, L.w_gate_up, R, H, 2 * F, sp_gu, w.part, s, "dec_gemm_gate_up");
+            MEDUSA_LAUNCH("swiglu", swiglu_kernel, dim3((F + 255) / 256, R), dim3(256), 0, s, w.part, sp_gu.S, R, F,
+                          w.a);
+        }
         launch_skinny_partial(w.a, L.w_down, R, F, H, sp_d, w.part, s, "dec_gemm_down");
         MEDUSA_LAUNCH("residual_rmsnorm", residual_rmsnorm_kernel, dim3(R), dim3(RN_THREADS), 0, s, w.part, sp_d.S, R,
                       H, eps, w.x, w.n);

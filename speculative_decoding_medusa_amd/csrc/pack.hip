@@ -5,7 +5,9 @@
 // i.e. every 16 x 32 tile is one contiguous 1 KB fragment in the lane order of
 // the A operand of v_mfma_f32_16x16x32_bf16.  A packed matrix of `rows` rows
 // holds ceil(rows / 16) * 16 * K elements; several row-major matrices can be
-// packed into one (stacked along the rows) by packing each at its row offset.
+// packed into one, stacked along the rows (each at its row offset) or
+// interleaved in blocks of 16 rows (block j of matrix m at packed block
+// j * n + m, for n matrices).
 #include <algorithm>
 
 #include "common.hpp"
@@ -16,10 +18,12 @@ namespace medusa {
 size_t packed_elems(int rows, int K) { return (size_t)((rows + PACK_ROWS - 1) / PACK_ROWS) * PACK_ROWS * K; }
 
 // One thread per 8-element piece: reads src row-major (coalesced), writes the
-// piece to its fragment slot.  Rows i >= rows (the padding of the last
-// fragment row block, written only when this call ends the matrix) get zeros.
+// piece to its fragment slot.  Source row i goes to packed row
+// dst_row0 + (i / 16) * 16 * inter + i % 16.  Rows i >= rows (the padding of
+// the last fragment row block, written only when a plain call ends the
+// matrix) get zeros.
 __global__ __launch_bounds__(256) void pack_rows_kernel(const bf16_t* __restrict__ src, int rows, int rows_out, int K,
-                                                        bf16_t* __restrict__ dst, int dst_row0) {
+                                                        bf16_t* __restrict__ dst, int dst_row0, int inter) {
     const size_t per_row = (size_t)K / 8;
     const size_t total = (size_t)rows_out * per_row;
     const int ksteps = K / PACK_K;
@@ -27,18 +31,19 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const bf16_t* __restrict
         const int i = (int)(p / per_row);
         const int k8 = (int)(p - (size_t)i * per_row);
         const u32x4 v = i < rows ? *(const u32x4*)(src + (size_t)i * K + (size_t)k8 * 8) : (u32x4){0u, 0u, 0u, 0u};
-        const int r = dst_row0 + i;
+        const int r = dst_row0 + (i / PACK_ROWS) * PACK_ROWS * inter + i % PACK_ROWS;
         const size_t frag = (size_t)(r / PACK_ROWS) * ksteps + k8 / 4;
         *(u32x4*)(dst + frag * PACK_FRAG + ((k8 & 3) * PACK_ROWS + r % PACK_ROWS) * 8) = v;
     }
 }
 
-void launch_pack_rows(const bf16_t* src, int rows, int K, bf16_t* dst, int dst_row0, int dst_rows, hipStream_t s) {
+void launch_pack_rows(const bf16_t* src, int rows, int K, bf16_t* dst, int dst_row0, int dst_rows, int inter,
+                      hipStream_t s) {
     const int end = dst_row0 + rows;
-    const int rows_out = end == dst_rows ? (int)(packed_elems(dst_rows, K) / K) - dst_row0 : rows;
+    const int rows_out = inter == 1 && end == dst_rows ? (int)(packed_elems(dst_rows, K) / K) - dst_row0 : rows;
     const size_t total = (size_t)rows_out * (K / 8);
     const int blocks = (int)std::min<size_t>((total + 255) / 256, 8192);
-    MEDUSA_LAUNCH("pack_rows", pack_rows_kernel, dim3(blocks), dim3(256), 0, s, src, rows, rows_out, K, dst, dst_row0);
+    MEDUSA_LAUNCH("pack_rows", pack_rows_kernel, dim3(blocks), dim3(256), 0, s, src, rows, rows_out, K, dst, dst_row0, inter);
 }
 
 }  // namespace medusa

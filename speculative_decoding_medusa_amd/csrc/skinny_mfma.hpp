@@ -23,7 +23,10 @@
 
 namespace medusa {
 
-enum { SKINNY_ARGMAX = 0, SKINNY_PARTIAL = 1 };
+// ARGMAX: per-workgroup argmax candidates (base greedy);  PARTIAL: fp32 sums
+// per contraction split;  SWIGLU (unsplit gate|up with gate and up rows
+// interleaved in 16-row blocks): bf16(SiLU(gate) * up)
+enum { SKINNY_ARGMAX = 0, SKINNY_PARTIAL = 1, SKINNY_SWIGLU = 2 };
 
 // packed fragment geometry
 constexpr int PACK_ROWS = 16;                      // rows per fragment
@@ -66,13 +69,15 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
                                                           float* __restrict__ cand_val,
                                                           int* __restrict__ cand_idx,  // ARGMAX: [R][G]
                                                           float* __restrict__ out) {
-    // ARGMAX: out = optional logits [R][V];  PARTIAL: out = [splits][R][V]
+    // ARGMAX: out = optional logits [R][V];  PARTIAL: out = [splits][R][V];
+    // SWIGLU: out = bf16 [R][V / 2]
     using C = LmhCfg<NBLK, WAVES>;
     constexpr int D = C::D;
     constexpr int NT = C::NT;
     __shared__ __attribute__((aligned(16))) bf16_t ns[2][C::NODES][C::LDW];
     __shared__ float red_v[WAVES][EPI == SKINNY_ARGMAX ? C::NODES : 1];
     __shared__ int red_i[WAVES][EPI == SKINNY_ARGMAX ? C::NODES : 1];
+    __shared__ f32x4 xup[EPI == SKINNY_SWIGLU ? WAVES / 2 : 1][EPI == SKINNY_SWIGLU ? NBLK : 1][64];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -156,6 +161,31 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
     }
 
     // epilogue: lane holds rows vw + 4*lk + r of node column b*16 + lr
+    if (EPI == SKINNY_SWIGLU) {
+        // waves 2j (gate rows) and 2j + 1 (up rows) hold the same 16 output
+        // columns in the same lane layout; the up wave hands its sums over
+        static_assert(WAVES % 2 == 0, "gate and up blocks pair up within a workgroup");
+        if (wave & 1) {
+#pragma unroll
+            for (int b = 0; b < NBLK; ++b) xup[wave >> 1][b][lane] = acc[b];
+        }
+        __syncthreads();
+        if (wave & 1) return;
+        const int F = V / 2;
+        const int c0 = (rb >> 1) * PACK_ROWS + lk * 4;  // this lane's 4 output columns
+        bf16_t* a = (bf16_t*)out;
+#pragma unroll
+        for (int b = 0; b < NBLK; ++b) {
+            const int node = node0 + b * 16 + lr;
+            if (node >= R || c0 >= F) continue;
+            const f32x4 g = acc[b], u = xup[wave >> 1][b][lane];
+            float y[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) y[r] = g[r] / (1.f + __expf(-g[r])) * u[r];
+            *(uint2*)(a + (size_t)node * F + c0) = (uint2){pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+        }
+        return;
+    }
     if (EPI == SKINNY_PARTIAL) {
         float* part = out + (size_t)blockIdx.z * R * V;
         const int v0 = vw + lk * 4;

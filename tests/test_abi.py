@@ -114,9 +114,12 @@ def test_packed_size(M):
 def test_pack_rows_argument_errors(M):
     L = M._lib
     d = ctypes.c_void_p(16)
-    assert L.medusa_pack_rows(d, 16, 48, d, 0, 16, None) == M.EUNSUPPORTED       # cols % 32
-    assert L.medusa_pack_rows(d, 16, 64, d, 8, 16, None) == M.EINVAL             # rows do not fit
-    assert L.medusa_pack_rows(None, 16, 64, d, 0, 16, None) == M.EINVAL
+    assert L.medusa_pack_rows(d, 16, 48, d, 0, 16, 1, None) == M.EUNSUPPORTED    # cols % 32
+    assert L.medusa_pack_rows(d, 16, 64, d, 8, 16, 1, None) == M.EINVAL          # rows do not fit
+    assert L.medusa_pack_rows(None, 16, 64, d, 0, 16, 1, None) == M.EINVAL
+    assert L.medusa_pack_rows(d, 24, 64, d, 0, 48, 2, None) == M.EINVAL          # interleave: rows % 16
+    assert L.medusa_pack_rows(d, 32, 64, d, 32, 64, 2, None) == M.EINVAL         # interleave: dst_row0 < 32
+    assert L.medusa_pack_rows(d, 32, 64, d, 16, 48, 2, None) == M.EINVAL         # interleave: rows do not fit
     assert L.medusa_base_greedy(d, d, M.PACKED, 4, 256, 100, 1e-6, M.F32, d, None, d, 1 << 30, None) == \
         M.EUNSUPPORTED                                                           # packed needs bf16
     assert L.medusa_base_greedy(d, d, M.PACKED, 4, 264, 100, 1e-6, M.BF16, d, None, d, 1 << 30, None) == \

@@ -209,19 +209,31 @@ def _pack_layout(W):
     return out
 
 
-@pytest.mark.parametrize("shapes", [[(16, 32)], [(37, 64)], [(4096, 96), (1024, 96), (1024, 96)], [(5, 256), (3, 256)]],
-                         ids=["one_block", "ragged_rows", "stacked_qkv", "stacked_ragged"])
-def test_pack_rows_layout(M, shapes):
-    _say("pack_rows", shapes)
+@pytest.mark.parametrize("shapes,inter", [([(16, 32)], 1), ([(37, 64)], 1), ([(4096, 96), (1024, 96), (1024, 96)], 1),
+                                          ([(5, 256), (3, 256)], 1), ([(64, 64), (64, 64)], 2),
+                                          ([(32, 96), (32, 96), (32, 96)], 3)],
+                         ids=["one_block", "ragged_rows", "stacked_qkv", "stacked_ragged", "gate_up_interleaved",
+                              "three_interleaved"])
+def test_pack_rows_layout(M, shapes, inter):
+    _say("pack_rows", shapes, inter)
     r = np.random.default_rng(7)
     mats = [r.integers(0, 1 << 16, size=s, dtype=np.uint16) for s in shapes]
-    want = _pack_layout(np.concatenate(mats))
-    dst = M.Packed(torch.full((M.packed_size(sum(s[0] for s in shapes), shapes[0][1]) // 2,), -1, dtype=torch.int16,
-                              device="cuda"), sum(s[0] for s in shapes), shapes[0][1])
+    if inter == 1:
+        logical = np.concatenate(mats)
+    else:  # 16-row blocks of the matrices alternate: A[0:16], B[0:16], .., A[16:32], ..
+        logical = np.concatenate([m[j:j + 16] for j in range(0, shapes[0][0], 16) for m in mats])
+    want = _pack_layout(logical)
+    rows = sum(s[0] for s in shapes)
+    dst = M.Packed(torch.full((M.packed_size(rows, shapes[0][1]) // 2,), -1, dtype=torch.int16, device="cuda"),
+                   rows, shapes[0][1])
     r0 = 0
-    for m in mats:
-        M.medusa_pack_rows(torch.from_numpy(m.view(np.int16)).cuda(), dst, r0)
-        r0 += m.shape[0]
+    for i, m in enumerate(mats):
+        src = torch.from_numpy(m.view(np.int16)).cuda()
+        if inter == 1:
+            M.medusa_pack_rows(src, dst, r0)
+            r0 += m.shape[0]
+        else:
+            M.medusa_pack_rows(src, dst, 16 * i, inter)
     torch.cuda.synchronize()
     assert np.array_equal(dst.data.cpu().numpy().view(np.uint16), want)
 
