@@ -291,7 +291,7 @@ def cpu_baseline(cfg, heads, att, root):
     t_widen = time.perf_counter() - t0
     rows = np.random.default_rng(0).normal(0, 1, (8, cfg.H))
     t0 = time.perf_counter()
-    oracle.base_greedy(rows, lm, 1e-6, dt == "bf16")
+    oracle.base_greedy(rows, lm, 1e-6)
     t["base_greedy"] = t_widen + (time.perf_counter() - t0) * cfg.B * cfg.N / 8
     del lm
     tok = np.zeros((cfg.B, cfg.N), dtype=np.int32)
@@ -483,7 +483,7 @@ def cpu_baseline_decoder(cfg, heads):
     del Wl, W, kc, vc
     t0 = time.perf_counter()
     lm = oracle.widen(heads["lm_head"], dt)
-    oracle.base_greedy(r.normal(0, 1, (8, cfg.H)), lm, 1e-6, True)
+    oracle.base_greedy(r.normal(0, 1, (8, cfg.H)), lm, 1e-6)
     t["lm_head"] = (time.perf_counter() - t0) * cfg.B * cfg.N / 8
     total = sum(t.values())
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])

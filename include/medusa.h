@@ -186,11 +186,13 @@ medusa_status medusa_pack_rows(const void* src, int rows, int cols, void* dst, i
  * Step a5 -- the base model's greedy choice after every tree node (tree
  * section: greedy acceptance compares with the model's top choice).
  *   x [R][H] (dt): one row per node; n = x * rsqrt(mean(x^2) + eps) (unit
- *   weight), rounded to bf16 when dt is BF16; greedy[r] = argmax_v
- *   (lm_head[v] . n_r), lower index first among equal values.
- *   lm_head [V][H] (dt) in lm_layout: MEDUSA_PACKED (bf16 only; the MFMA
- *   product) or MEDUSA_ROW_MAJOR (the vector GEMV, any dt);
- *   greedy [R] int32; logits [R][V] float32 optional.
+ *   weight); greedy[r] = argmax_v (lm_head[v] . n_r), lower index first among
+ *   equal values; logits [R][V] = lm_head . n (float32, optional).
+ *   lm_head [V][H] (dt) in lm_layout: MEDUSA_PACKED (bf16 only) runs the MFMA
+ *   product on the bf16 rows x and applies the positive factor
+ *   rsqrt(mean(x^2) + eps) to the float32 scores (it does not move the
+ *   argmax); MEDUSA_ROW_MAJOR (any dt) forms n in float32 for the vector GEMV.
+ *   greedy [R] int32.
  * Limits: H % 8 == 0, H <= 8192, R >= 1; packed: H % 64 == 0.
  * ------------------------------------------------------------------------- */
 size_t medusa_base_greedy_workspace_size(int R, int H, int V, medusa_dtype dt, medusa_layout lm_layout);

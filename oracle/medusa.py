@@ -198,21 +198,20 @@ def rmsnorm(x, eps):
     return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
 
 
-def base_greedy(o_rows, lm_head, eps, bf16_operand: bool):
+def base_greedy(o_rows, lm_head, eps):
     """Greedy decoding accepts a candidate when it equals the base model's top
     choice [MH-tree]; this is that top choice after each tree node.
 
     Reading: with synthetic attention outputs standing in for the backbone,
     the node's hidden state is RMSNorm(o) (unit weight) and its scores are
-    lm_head . RMSNorm(o).  In bf16 workloads the normalised row is rounded to
-    bf16 (the operand precision of the product); the argmax is taken on the
-    float32-rounded scores, lower index first among equal values.
+    lm_head . RMSNorm(o); the normalised row is not rounded (RMSNorm with unit
+    weight is a positive factor per row, so the top choice is that of
+    lm_head . o).  The argmax is taken on the float32-rounded scores, lower
+    index first among equal values.
 
     o_rows [R][H]; lm_head [V][H] -> greedy [R] int32, logits [R][V]
     """
     n = rmsnorm(o_rows, eps)
-    if bf16_operand:
-        n = round_bf16(n)
     logits = n @ lm_head.T
     lg = round_f32(logits)
     g = np.empty(lg.shape[0], dtype=np.int32)
@@ -298,7 +297,7 @@ def medusa_step(x: dict, parent, rank, topk_k: int, dtype: str, eps: float = 1e-
     if bf:
         o = round_bf16(o)
     B, N = node_tok.shape
-    g, node_logits = base_greedy(o.reshape(B * N, -1), x["lm_head"], eps, bf)
+    g, node_logits = base_greedy(o.reshape(B * N, -1), x["lm_head"], eps)
     g = g.reshape(B, N)
     kc, vc = write_tree_kv(x["k_cache"], x["v_cache"], x["k_tree"], x["v_tree"], x["cache_len"])
     res = dict(logits=logits, z=z, topk_idx=tk_idx, topk_val=tk_val, node_tok=node_tok,

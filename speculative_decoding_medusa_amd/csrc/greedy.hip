@@ -1,23 +1,26 @@
 // Base model's greedy choice after every tree node (step a5):
-// n_r = x_r * rsqrt(mean(x_r^2) + eps) (bf16-rounded for bf16 weights), then
+// n_r = x_r * rsqrt(mean(x_r^2) + eps) (unit weight), then
 // greedy[r] = argmax_v lm_head[v] . n_r  (lower index first among equal values).
 //
 // Packed bf16 lm_head: the product of the node rows with lm_head is a dense
 // contraction (64-256 rows share every lm_head byte), so it runs on MFMA with
 // the argmax fused into the epilogue (skinny_mfma.hpp; the 32000-row
-// vocabulary gives 500 workgroups, about two per CU).  Each workgroup writes,
-// per node, its best (value, index); a merge kernel reduces them.
-// Row-major lm_head (float32 or bf16): the vector-ALU GEMV of the heads, one
-// pass per 8 rows.
+// vocabulary gives 250 8-wave workgroups).  RMSNorm with unit weight is a
+// positive factor per row, so the product runs on the bf16 rows x themselves
+// and the argmax is that of lm_head . x; the factor is applied only to the
+// logits when they are asked for.  Each workgroup writes, per node, its best
+// (value, index); a merge kernel reduces them.
+// Row-major lm_head (float32 or bf16): the vector-ALU GEMV of the heads on the
+// float32 normalised rows, one pass per 8 rows.
 #include "common.hpp"
 #include "skinny_mfma.hpp"
 
 namespace medusa {
 
-// One block per row; writes n (float32 for the GEMV path, bf16 for MFMA).
-template <typename T, typename OUT, bool ROUND_BF16>
+// One block per row; writes n = x * rsqrt(mean(x^2) + eps) in float32.
+template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const T* __restrict__ x, int H, float eps,
-                                                           OUT* __restrict__ n) {
+                                                           float* __restrict__ n) {
     __shared__ float red[4];
     const int r = blockIdx.x;
     const T* xr = x + (size_t)r * H;
@@ -31,11 +34,24 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const T* __restrict__
     __syncthreads();
     const float tot = (red[0] + red[1]) + (red[2] + red[3]);
     const float rs = rsqrtf(tot / (float)H + eps);
+    for (int j = threadIdx.x; j < H; j += 256) n[(size_t)r * H + j] = Elem<T>::load(xr, j) * rs;
+}
+
+// rs[r] = rsqrt(mean(x_r^2) + eps): the RMSNorm factor of each row (for the
+// logits of the MFMA path).  One block of 256 threads per row.
+__global__ __launch_bounds__(256) void row_rscale_kernel(const bf16_t* __restrict__ x, int H, float eps,
+                                                         float* __restrict__ rs) {
+    __shared__ float red[4];
+    const bf16_t* xr = x + (size_t)blockIdx.x * H;
+    float ss = 0.f;
     for (int j = threadIdx.x; j < H; j += 256) {
-        float v = Elem<T>::load(xr, j) * rs;
-        if (ROUND_BF16) v = bf16_to_f32(f32_to_bf16(v));
-        Elem<OUT>::store(n, (size_t)r * H + j, v);
+        const float v = bf16_to_f32(xr[j]);
+        ss = fmaf(v, v, ss);
     }
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    if (threadIdx.x == 0) rs[blockIdx.x] = rsqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)H + eps);
 }
 
 // greedy[r] = best of the G workgroup candidates of row r
@@ -85,7 +101,7 @@ size_t lm_head_greedy_workspace_bytes(int R, int H, int V) {
 }
 
 void launch_lm_head_greedy(const bf16_t* n, const bf16_t* lm_head, int R, int H, int V, int32_t* greedy,
-                           float* logits, void* ws, hipStream_t s) {
+                           float* logits, const float* row_scale, void* ws, hipStream_t s) {
     const int G = lmh_groups(V);
     float* cv = (float*)ws;
     int* ci = (int*)((char*)ws + a256((size_t)R * G * 4));
@@ -94,7 +110,7 @@ void launch_lm_head_greedy(const bf16_t* n, const bf16_t* lm_head, int R, int H,
     const int nch = H / lmh_kc(nblk);
 #define LMH_LAUNCH(NB, WV)                                                                                        \
     MEDUSA_LAUNCH("lm_head_argmax", (skinny_mfma_kernel<NB, SKINNY_ARGMAX, WV>), grid, dim3(WV * 64), 0, s, n, \
-                  lm_head, R, H, V, nch, cv, ci, logits)
+                  lm_head, R, H, V, nch, cv, ci, logits, row_scale)
     if (lmh_waves(V) == 8) {
         if (nblk == 4) LMH_LAUNCH(4, 8);
         else if (nblk == 8) LMH_LAUNCH(8, 8);
@@ -110,11 +126,11 @@ void launch_lm_head_greedy(const bf16_t* n, const bf16_t* lm_head, int R, int H,
 
 void launch_lm_head_greedy(const bf16_t* n, const bf16_t* lm_head, int R, int H, int V, int32_t* greedy, void* ws,
                            hipStream_t s) {
-    launch_lm_head_greedy(n, lm_head, R, H, V, greedy, nullptr, ws, s);
+    launch_lm_head_greedy(n, lm_head, R, H, V, greedy, nullptr, nullptr, ws, s);
 }
 
 size_t greedy_workspace_bytes(int R, int H, int V, bool packed) {
-    if (packed) return a256((size_t)R * H * 2) + lm_head_greedy_workspace_bytes(R, H, V);
+    if (packed) return a256((size_t)R * 4) + lm_head_greedy_workspace_bytes(R, H, V);
     const int G = gemv_groups_max(V);
     return a256((size_t)R * H * 4) + a256((size_t)8 * G * 4) * 2 + a256((size_t)R * 4);
 }
@@ -125,11 +141,13 @@ void launch_base_greedy(const void* x, const void* lm_head, bool packed, int R, 
                         int32_t* greedy, float* logits, void* ws, hipStream_t s) {
     char* p = (char*)ws;
     if (packed) {
-        bf16_t* n = (bf16_t*)p;
-        p += a256((size_t)R * H * 2);
-        MEDUSA_LAUNCH("rmsnorm_rows", (rmsnorm_rows_kernel<bf16_t, bf16_t, false>), dim3(R), dim3(256), 0, s,
-                      (const bf16_t*)x, H, eps, n);
-        launch_lm_head_greedy(n, (const bf16_t*)lm_head, R, H, V, greedy, logits, p, s);
+        float* rs = nullptr;
+        if (logits != nullptr) {
+            rs = (float*)p;
+            MEDUSA_LAUNCH("row_rscale", row_rscale_kernel, dim3(R), dim3(256), 0, s, (const bf16_t*)x, H, eps, rs);
+        }
+        p += a256((size_t)R * 4);
+        launch_lm_head_greedy((const bf16_t*)x, (const bf16_t*)lm_head, R, H, V, greedy, logits, rs, p, s);
         return;
     }
     float* n = (float*)p;
@@ -140,11 +158,11 @@ void launch_base_greedy(const void* x, const void* lm_head, bool packed, int R, 
     p += a256((size_t)8 * G * 4) * 2;
     float* gval = (float*)p;
     if (bf16)
-        MEDUSA_LAUNCH("rmsnorm_rows", (rmsnorm_rows_kernel<bf16_t, float, true>), dim3(R), dim3(256), 0, s,
-                      (const bf16_t*)x, H, eps, n);
+        MEDUSA_LAUNCH("rmsnorm_rows", rmsnorm_rows_kernel<bf16_t>, dim3(R), dim3(256), 0, s, (const bf16_t*)x, H, eps,
+                      n);
     else
-        MEDUSA_LAUNCH("rmsnorm_rows", (rmsnorm_rows_kernel<float, float, false>), dim3(R), dim3(256), 0, s,
-                      (const float*)x, H, eps, n);
+        MEDUSA_LAUNCH("rmsnorm_rows", rmsnorm_rows_kernel<float>, dim3(R), dim3(256), 0, s, (const float*)x, H, eps,
+                      n);
     for (int r0 = 0; r0 < R; r0 += 8) {
         const int nb = R - r0 < 8 ? R - r0 : 8;
         launch_vocab_topk_named(n + (size_t)r0 * H, lm_head, nb, H, V, 1, 1, bf16,

@@ -68,9 +68,11 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
                                                           int R, int K, int V, int chunks_per_split,
                                                           float* __restrict__ cand_val,
                                                           int* __restrict__ cand_idx,  // ARGMAX: [R][G]
-                                                          float* __restrict__ out) {
-    // ARGMAX: out = optional logits [R][V];  PARTIAL: out = [splits][R][V];
-    // SWIGLU: out = bf16 [R][V / 2]
+                                                          float* __restrict__ out,
+                                                          const float* __restrict__ row_scale = nullptr) {
+    // ARGMAX: out = optional logits [R][V], each node row's scores times
+    // row_scale[node] when given (a positive factor: the argmax is that of the
+    // unscaled scores);  PARTIAL: out = [splits][R][V];  SWIGLU: out = bf16 [R][V / 2]
     using C = LmhCfg<NBLK, WAVES>;
     constexpr int D = C::D;
     constexpr int NT = C::NT;
@@ -208,12 +210,13 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
         float bv = -INFINITY;
         int bi = 0x7FFFFFFF;
         const int node = node0 + b * 16 + lr;
+        const float sc = (out != nullptr && row_scale != nullptr && node < R) ? row_scale[node] : 1.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int v = vw + lk * 4 + r;
             const float x = acc[b][r];
             if (v < V) {
-                if (out != nullptr && node < R) out[(size_t)node * V + v] = x;
+                if (out != nullptr && node < R) out[(size_t)node * V + v] = x * sc;
                 if (better(x, v, bv, bi)) { bv = x; bi = v; }
             }
         }

@@ -96,8 +96,6 @@ def enforce_greedy_gap(cfg, heads, o, overrides, eps=1e-6, gap=GAP, max_iter=200
     dt = cfg.dtype
     rows = o.reshape(-1, cfg.H)
     n = oracle.rmsnorm(rows, eps)
-    if dt == "bf16":
-        n = oracle.round_bf16(n)
     logits = np.empty((cfg.V, n.shape[0]))
     for r0 in range(0, cfg.V, 8192):
         logits[r0:r0 + 8192] = oracle.widen(heads["lm_head"][r0:r0 + 8192], dt) @ n.T

@@ -97,7 +97,8 @@ def test_workspace_sizes_are_positive(M):
     L = M._lib
     assert L.medusa_heads_workspace_size(1, 4096, 32000, 5, 4, M.BF16) >= 5 * 4096 * 4
     assert L.medusa_vocab_topk_workspace_size(8, 4096, 128256, 5, 4, M.BF16) > 0
-    assert L.medusa_base_greedy_workspace_size(64, 4096, 32000, M.BF16, M.PACKED) >= 64 * 4096 * 2  # bf16 rows
+    # packed: row factors + per-workgroup (value, index) candidates of every row
+    assert L.medusa_base_greedy_workspace_size(64, 4096, 32000, M.BF16, M.PACKED) >= 64 * 4 + 2 * 64 * 250 * 4
     assert L.medusa_base_greedy_workspace_size(9, 256, 1000, M.F32, M.ROW_MAJOR) >= 9 * 256 * 4
     assert L.medusa_heads_workspace_size(0, 4096, 32000, 5, 4, M.BF16) == 0
 

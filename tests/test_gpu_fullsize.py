@@ -68,7 +68,7 @@ def test_full_step(M, c):
         np.testing.assert_allclose(got["o"][b], o_ref[b], rtol=0, atol=tol(cfg.dtype))
         if lm is None:
             lm = oracle.widen(heads["lm_head"], cfg.dtype)
-        g_ref, _ = oracle.base_greedy(o_ref[b].reshape(cfg.N, cfg.H), lm, 1e-6, cfg.dtype == "bf16")
+        g_ref, _ = oracle.base_greedy(o_ref[b].reshape(cfg.N, cfg.H), lm, 1e-6)
         assert np.array_equal(got["greedy"][b], g_ref)
         L, path, toks = oracle.accept(parent, tok_ref[b], g_ref)
         Dm = got["accept_nodes"].shape[1] - 1

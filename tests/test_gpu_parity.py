@@ -183,7 +183,7 @@ def test_base_greedy_parity(M, name, dtype, R, H, V, layout):
     xw = oracle.widen(x, dtype)
     ov = []
     enforce_greedy_gap(cfg, heads, xw, ov)
-    g_ref, lg_ref = oracle.base_greedy(xw, oracle.widen(heads["lm_head"], dtype), 1e-6, dtype == "bf16")
+    g_ref, lg_ref = oracle.base_greedy(xw, oracle.widen(heads["lm_head"], dtype), 1e-6)
     g = torch.empty(R, dtype=torch.int32, device="cuda")
     lg = torch.empty(R, V, device="cuda")
     lm = dev(heads["lm_head"])

@@ -123,23 +123,28 @@ def test_base_greedy_brute_force_and_rmsnorm():
     r = np.random.default_rng(8)
     o = r.normal(0, 1, (6, 32))
     lm = r.normal(0, 0.02, (50, 32))
-    for bf in (False, True):
-        g, logits = oracle.base_greedy(o, lm, 1e-6, bf)
-        n = oracle.rmsnorm(o, 1e-6)
-        if bf:
-            n = torch.from_numpy(n).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
-        ref = torch.from_numpy(n) @ torch.from_numpy(lm).T
-        np.testing.assert_allclose(logits, ref.numpy(), rtol=1e-12, atol=1e-13)
-        for row in range(6):
-            lg = logits[row].astype(np.float32)
-            best = max(range(50), key=lambda j: (lg[j], -j))
-            assert g[row] == best
+    g, logits = oracle.base_greedy(o, lm, 1e-6)
+    # RMS of each row by a plain loop, then the scores through torch
+    n = np.stack([row / np.sqrt(sum(float(x) * float(x) for x in row) / len(row) + 1e-6) for row in o])
+    ref = torch.from_numpy(n) @ torch.from_numpy(lm).T
+    np.testing.assert_allclose(logits, ref.numpy(), rtol=1e-12, atol=1e-13)
+    for row in range(6):
+        lg = logits[row].astype(np.float32)
+        best = max(range(50), key=lambda j: (lg[j], -j))
+        assert g[row] == best
+    # unit-weight RMSNorm is a positive factor per row: the top choice is that of lm_head . o, and
+    # scaling a row by any positive constant changes nothing
+    raw = o @ lm.T
+    assert np.array_equal(g, np.argmax(raw, axis=1))
+    g2, _ = oracle.base_greedy(o * np.array([[3.0], [0.01], [7.5], [1.0], [250.0], [0.5]]), lm, 0.0)
+    g0, _ = oracle.base_greedy(o, lm, 0.0)
+    assert np.array_equal(g2, g0)
     # RMSNorm: unit mean square (up to eps), scale invariant
     n = oracle.rmsnorm(o, 0.0)
     np.testing.assert_allclose((n * n).mean(1), 1.0, rtol=1e-13)
     np.testing.assert_allclose(oracle.rmsnorm(o * 37.0, 0.0), n, rtol=1e-13)
     # ties go to the lower index
-    g, _ = oracle.base_greedy(np.ones((1, 4)), np.ones((5, 4)), 1e-6, False)
+    g, _ = oracle.base_greedy(np.ones((1, 4)), np.ones((5, 4)), 1e-6)
     assert g[0] == 0
 
 
