@@ -39,8 +39,9 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 # heads.hip + common.hpp); reported as null after any change to them.
 VOCAB_TRAFFIC = {"sources_sha256_16": "009e083c90dc20a3", "read_bytes": 1311508042, "write_bytes": 128090}
 # the same for the gate|up projection of the 32-layer workload (one layer's
-# launch: 64 x 4096 node rows against 22016 packed weight rows, 2 splits)
-GATE_UP_TRAFFIC = {"sources_sha256_16": "6dbed1afd9b7404d", "read_bytes": 188534752, "write_bytes": 11272642}
+# launch: 64 x 4096 node rows against 22016 packed weight rows, unsplit, the
+# SwiGLU product written in bf16)
+GATE_UP_TRAFFIC = {"sources_sha256_16": "1d07fdc9042c6638", "read_bytes": 187013933, "write_bytes": 1409242}
 
 
 def _traffic_bytes(rec, sources):
@@ -392,9 +393,10 @@ def bench_decoder(args, cfg):
     per_launch_us = {k: 1e3 * ms / n for k, (n, ms) in prof.items()}
     per_step_us = {k: 1e3 * ms / args.steps for k, (n, ms) in prof.items()}
 
-    # dominant kernel: the gate|up projection (the largest weight stream per launch)
+    # dominant kernel: the gate|up projection (the largest weight stream per
+    # launch): packed weights + node rows in, the bf16 SwiGLU product out
     R = B * N
-    gu_bytes = 2 * cfg.ffn * H * 2 + R * H * 2
+    gu_bytes = 2 * cfg.ffn * H * 2 + R * H * 2 + R * cfg.ffn * 2
     gu_us = per_launch_us["dec_gemm_gate_up"]
     achieved = gu_bytes / (gu_us * 1e-6) / 1e9
     w_layer = sum(int(np.prod(s)) for s in mi.layer_shapes(cfg).values()) * 2
