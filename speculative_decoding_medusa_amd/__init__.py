@@ -177,7 +177,7 @@ class Tree:
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h is not None and h.value:
+        if h is not None and h.value and _lib is not None:  # _lib is gone at interpreter shutdown
             _lib.medusa_tree_destroy(h)
             self.handle = None
 

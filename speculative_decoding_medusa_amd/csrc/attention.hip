@@ -143,352 +143,544 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attn_valu_kernel(
     }
 }
 
-// out[b][i][h][:] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
-// The S (m, l) pairs are read in parallel into LDS first; the partial rows are
-// then summed four splits at a time (independent loads in flight).
-constexpr int ATT_MAX_SPLITS = 1024;
+// out[b][i][h][:] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with
+// M = max_s m_s; a split with m_s = -inf saw no key of query i and adds
+// nothing (its partial row is never summed, so its contents do not matter).
+// One thread per 4 columns of an output row; the partials of 8 splits are
+// loaded together (one memory round trip per 8 splits).
+constexpr int ATT_MERGE_THREADS = 256;
+constexpr int ATT_MERGE_SPLITS = 8;
 
 template <typename T, int D>
-__global__ __launch_bounds__(D) void tree_attn_combine_kernel(const float* __restrict__ part_o,
-                                                              const float* __restrict__ part_ml, int S, int N,
-                                                              int nH, T* __restrict__ out) {
-    __shared__ float ms[ATT_MAX_SPLITS];
-    __shared__ float ls[ATT_MAX_SPLITS];
-    __shared__ float red[D / 64];
-    const int i = blockIdx.x;
+__global__ __launch_bounds__(ATT_MERGE_THREADS) void tree_attn_merge_kernel(const float* __restrict__ part_o,
+                                                                             const float* __restrict__ part_ml,
+                                                                             int S, int N, int nH,
+                                                                             T* __restrict__ out) {
+    constexpr int TPR = D / 4;                       // threads per output row
+    constexpr int RPB = ATT_MERGE_THREADS / TPR;     // rows per workgroup
+    constexpr int SU = ATT_MERGE_SPLITS;
     const int bh = blockIdx.y;
-    const int b = bh / nH, h = bh - b * nH;
-    const int c = threadIdx.x;
-    float mloc = -INFINITY;
-    for (int s = c; s < S; s += D) {
-        const size_t pr = ((size_t)bh * S + s) * N + i;
-        ms[s] = part_ml[pr * 2];
-        ls[s] = part_ml[pr * 2 + 1];
-        mloc = fmaxf(mloc, ms[s]);
-    }
-    mloc = wave_max(mloc);
-    if ((c & 63) == 0) red[c >> 6] = mloc;
-    __syncthreads();
-    float M = red[0];
+    const int i = blockIdx.x * RPB + threadIdx.x / TPR;
+    if (i >= N) return;
+    const int c = (threadIdx.x % TPR) * 4;
+    const size_t row0 = (size_t)bh * S * N + i;      // partial row of split s: row0 + s * N
+    float M = -INFINITY, L = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < S; s0 += SU) {
+        float2 ml[SU];
+        f32x4 o[SU];
 #pragma unroll
-    for (int w = 1; w < D / 64; ++w) M = fmaxf(M, red[w]);
-    float L = 0.f, acc = 0.f;
-    for (int s0 = 0; s0 < S; s0 += 4) {
-        float v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int s = s0 + u;
-            v[u] = (s < S && ms[s] != -INFINITY) ? part_o[(((size_t)bh * S + s) * N + i) * D + c] : 0.f;
+        for (int u = 0; u < SU; ++u) {
+            const size_t r = row0 + (size_t)min(s0 + u, S - 1) * N;
+            ml[u] = *(const float2*)(part_ml + r * 2);
+            o[u] = *(const f32x4*)(part_o + r * D + c);
         }
+        float mx = M;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int s = s0 + u;
-            if (s < S && ms[s] != -INFINITY) {
-                const float f = exp2f(ms[s] - M);
-                L += f * ls[s];
-                acc += f * v[u];
+        for (int u = 0; u < SU; ++u)
+            if (s0 + u < S) mx = fmaxf(mx, ml[u].x);
+        if (mx == -INFINITY) continue;
+        const float r = exp2f(M - mx);  // 0 while nothing has been summed
+        L *= r;
+        acc *= r;
+#pragma unroll
+        for (int u = 0; u < SU; ++u) {
+            if (s0 + u < S && ml[u].x != -INFINITY) {
+                const float f = exp2f(ml[u].x - mx);
+                L += f * ml[u].y;
+                acc += f * o[u];
             }
         }
+        M = mx;
     }
-    Elem<T>::store(out, (((size_t)b * N + i) * nH + h) * D + c, acc / L);
+    const float inv = 1.f / L;
+    const size_t dst = (((size_t)(bh / nH) * N + i) * nH + (bh % nH)) * D + c;
+    if constexpr (sizeof(T) == 2) {
+        *(uint2*)(out + dst) = (uint2){pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+    } else {
+        *(f32x4*)(out + dst) = acc * inv;
+    }
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA variant.  The same split-KV decomposition, with the contractions
-// on MFMA in transposed form so that no register data has to move between
+// bf16 MFMA variant.
+//
+// Work split: a workgroup holds MF_Q = 64 tree queries of one head and one key
+// range.  Ranges 0..S-2 each cover KPS consecutive prefix keys (cache slots);
+// range S-1 is the N tree keys, read from k_tree / v_tree under the ancestor
+// mask.  The tree range's workgroup of query block 0 also copies the tree
+// keys/values into cache slots P..P+N-1 (no other workgroup reads those
+// slots).  For N > 64 the query blocks of one key range get linear workgroup
+// ids 8 apart: workgroups are dealt to the 8 XCDs round-robin, so the blocks
+// land on one XCD and read the range's K/V through the same L2.
+//
+// Inside the workgroup, 8 waves = 2 query halves x 4 key quarters: wave w
+// takes queries 32 (w & 1) .. +31 (two 16-query blocks) against keys
+// 16 (w >> 1) .. +15 of every 64-key tile, and keeps its own online-softmax
+// state; the four key quarters are merged through LDS at the end.
+//
+// Contractions, in transposed form so that no register data moves between
 // lanes:
-//   S^T[key][q] = K . Q^T   (v_mfma_f32_16x16x32_bf16; A = K tile rows from
-//                            LDS, B = the wave's Q rows held in registers for
-//                            the whole kernel);
-//   the output layout gives each lane 4 consecutive keys of one query per
-//   16-key block, exactly the 8 values the next product needs as its B
-//   operand, so P^T never leaves the lane;
-//   O^T[d][q] += V^T . P^T (v_mfma_f32_16x16x32_f16; A = V^T from an LDS tile
-//                            stored transposed, [d][key], widened to fp16; B =
-//                            the probabilities rounded to fp16, whose 11-bit
-//                            significand keeps the weighted sum 8x closer to
-//                            the exact one than bf16 would; the contraction
-//                            runs over the keys in a fixed permuted order, the
-//                            same for both operands).
-// The online-softmax state of query q lives in the 4 lanes that hold column q.
-// Tiles of 64 keys are staged in LDS by the whole workgroup, up to three tiles
-// in flight in a register ring.
+//   S^T[key][q]  = K . Q^T  (v_mfma_f32_16x16x32_bf16; A = the wave's 16 keys
+//                            x 32 dims from the LDS K tile, B = the query
+//                            block's Q fragment, held in registers);
+//   O^T[d][q]   += V^T . P^T (v_mfma_f32_16x16x32_bf16 over the wave's 16
+//                            keys twice: each probability is split into a
+//                            bf16 head and a bf16 remainder, so the product
+//                            carries 17 significant bits of P; the lane's B
+//                            fragment is the heads and remainders of exactly
+//                            the 4 keys its S^T output holds; A = V^T of
+//                            those keys, repeated, read from the row-major
+//                            LDS V tile by ds_read_b64_tr_b16, which
+//                            transposes 4 x 4 blocks of 16-bit values across
+//                            lanes).
+// Softmax in base 2 against a lazily raised reference M: a query's M (and so
+// O and l) changes only when a tile's score exceeds it by more than 2^8, so
+// probabilities stay <= 256 and almost every tile skips the rescale; O / l is
+// the same for any reference.  The state of query q lives in the 4 lanes that
+// hold its column.
+//
+// Pipeline: K/V tiles of 64 keys go from HBM straight into a ring of
+// MF_STAGES LDS stages with global_load_lds_dwordx4 (lane l of a wave writes
+// bytes 16 l .. 16 l + 15 of a 1 KB block), three tiles ahead of the one
+// being computed.  Each wave waits only for its own loads of the current
+// tile (an explicit vmcnt that leaves the loads of the younger requested
+// tiles in flight), then one barrier per tile publishes the tile and frees
+// the stage the next load overwrites.  No tile past the range is requested;
+// rows of the last tile past the range are clamped to its last row (their
+// scores are masked).  Within a
+// stage a row's 16-byte chunks are XOR-swizzled by a function of the row, so
+// the K fragment reads (16 rows, one chunk) and the transposing V reads (4
+// rows, two chunks) hit distinct LDS banks.  The first tiles are requested
+// before the sequence's cache length is read (clamped to the host bound
+// max_cache_len, so they stay in bounds).
 // ---------------------------------------------------------------------------
-constexpr int MF_TK = 64;
+constexpr int MF_TK = 64;       // keys per tile
+constexpr int MF_Q = 64;        // tree queries per workgroup
+constexpr int MF_THREADS = 512;
+constexpr int MF_STAGES = 4;
+constexpr float MF_LAZY = 8.f;  // log2 of the largest probability before a rescale
 
-template <int D, int WAVES, int QBW>
-__global__ __launch_bounds__(WAVES * 64) void tree_attn_mfma_kernel(
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One 16-byte global -> LDS load per lane: lane l writes LDS bytes
+// lds_addr + 16 l .. + 15 (lds_addr wave-uniform).  Issued from asm, so the
+// compiler does not model these loads: the explicit vmcnt waits below alone
+// order them with the LDS reads, and no load the compiler does model is in
+// flight while they are (the compiler would otherwise count its own waits
+// without them, which only over-waits, but could not place the tile waits).
+// M0 is saved and restored around the load.
+__device__ __forceinline__ void mf_dma16(const void* src, const void* lds_dst) {
+    const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds_dst);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(a)
+        : "memory");
+}
+
+// 4 bf16 values of V^T from the row-major V tile (see the lane layout above).
+__device__ __forceinline__ i16x4 ds_read_tr16(const char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+}
+
+// XOR swizzle of the 16-byte chunks of LDS row r (DC chunks per row).
+template <int DC> __device__ __forceinline__ int mf_swz(int r) {
+    if constexpr (DC == 16) return ((r << 1) & 14) | ((r >> 3) & 1);
+    else return ((r << 1) & 6) | ((r >> 2) & 1);
+}
+
+// This wave's loads of the current tile are done (the `younger` loads
+// issued after them may still be in flight) and its LDS reads of the
+// previous tile too; then the workgroup barrier.  s_waitcnt immediate:
+// vmcnt = younger, expcnt = 7 (no wait), lgkmcnt = 0.  The compiler fences
+// keep every memory access on its side of the barrier.
+template <int younger> __device__ __forceinline__ void mf_tile_barrier() {
+    static_assert(younger < 16, "vmcnt field");
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x70 | younger);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// Every load of this wave into LDS has landed (vmcnt = 0, lgkmcnt = 15).
+__device__ __forceinline__ void mf_loads_landed() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <int D>
+__global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_tree, const bf16_t* __restrict__ v_tree,
     bf16_t* __restrict__ k_cache, bf16_t* __restrict__ v_cache, const int32_t* __restrict__ cache_len,
     const uint64_t* __restrict__ mask, int N, int W, int nH, int nKV, int Lmax, int max_cache_len,
-    float scale_log2, int KPS, float* __restrict__ part_o, float* __restrict__ part_ml) {
-    constexpr int NT = WAVES * 64;
+    float scale_log2, int KPS, int S, int QB, int BH, float* __restrict__ part_o, float* __restrict__ part_ml) {
     constexpr int TK = MF_TK;
-    constexpr int KB = TK / 16;     // 16-key blocks per tile
-    constexpr int DK = D / 32;      // k-steps of S over the head dimension
-    constexpr int DB = D / 16;      // 16-row blocks of O^T
-    constexpr int CH = TK * D / 8;  // 16-byte chunks per tile per tensor
-    constexpr int PT = CH / NT;     // chunks per thread
-    constexpr int DC = D / 8;       // chunks per key row
-    __shared__ __attribute__((aligned(16))) bf16_t Ks[TK][D + 8];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[D][TK + 4];  // fp16 bits; 136-byte rows: 4-way write conflicts at most
+    constexpr int DK = D / 32;                   // k-steps of S^T over the head dimension
+    constexpr int DB = D / 16;                   // 16-row blocks of O^T
+    constexpr int DC = D / 8;                    // 16-byte chunks per key row
+    constexpr int ROWB = D * 2;                  // bytes per key row
+    constexpr int TILE_B = TK * ROWB;            // bytes of one K (or V) tile
+    constexpr int STAGE_B = 2 * TILE_B;          // K tile, then V tile
+    constexpr int BLKS = 2 * TILE_B / 1024;      // 1 KB load blocks per stage
+    constexpr int NLD = BLKS / (MF_THREADS / 64);  // loads per wave per tile
+    static_assert(NLD >= 1 && NLD * (MF_THREADS / 64) == BLKS && (BLKS / 2) % NLD == 0, "load split");
+    constexpr int QBLKS = MF_Q * ROWB / 1024;       // 1 KB load blocks of the query block
+    constexpr int NQLD = QBLKS / (MF_THREADS / 64); // query loads per wave
+    static_assert(NQLD >= 1 && NQLD * (MF_THREADS / 64) == QBLKS, "query load split");
+    // after the key loop the stages hold the states of four waves for the
+    // merge of the key quarters: O^T fragments + (M, l) per lane
+    constexpr int MERGE_WAVE_F = 2 * DB * 64 * 4 + 2 * 64 * 2;
+    static_assert(MERGE_WAVE_F * 4 <= STAGE_B && MF_STAGES == 4, "merge area: one wave state per stage");
+    // four separate arrays, so the compiler can tell a stage being read from
+    // the stages the loads in flight write to
+    __shared__ __attribute__((aligned(1024))) char lds0[STAGE_B];
+    __shared__ __attribute__((aligned(1024))) char lds1[STAGE_B];
+    __shared__ __attribute__((aligned(1024))) char lds2[STAGE_B];
+    __shared__ __attribute__((aligned(1024))) char lds3[STAGE_B];
+    auto stage_ptr = [&](int u) -> char* { return u == 0 ? lds0 : u == 1 ? lds1 : u == 2 ? lds2 : lds3; };
+    __shared__ __attribute__((aligned(1024))) char qlds[MF_Q * ROWB];  // the block's queries (swizzled rows)
 
-    const int bh = blockIdx.x;
+    const int Lid = blockIdx.x;
+    const int qblk = (Lid >> 3) % QB;
+    const int unit = (Lid & 7) + 8 * (Lid / (8 * QB));
+    if (unit >= BH * S) return;
+    const int bh = unit % BH, s = unit / BH;
     const int b = bh / nH, h = bh - b * nH;
     const int grp = nH / nKV;
     const int kvh = h / grp;
-    const int S = gridDim.y;
-    const int s = blockIdx.y;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const bool tree = s == S - 1;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lk = lane >> 4;
-    const int P = max(0, min(cache_len[b], max_cache_len));
-    const int total = P + N;
+    const int kq = wave >> 1, qh = wave & 1;  // key quarter, query half
+    const size_t cache_row0 = ((size_t)b * nKV + kvh) * Lmax;
+    const size_t prow = ((size_t)bh * S + s) * N;  // partial rows of this (head, range)
 
-    if (s == 0 && h % grp == 0) {
-        for (int e = tid; e < N * DC; e += NT) {
-            const int t = e / DC, c = e - t * DC;
-            const size_t src = (((size_t)b * N + t) * nKV + kvh) * D + c * 8;
-            const size_t dst = (((size_t)b * nKV + kvh) * Lmax + P + t) * D + c * 8;
-            *(u32x4*)(k_cache + dst) = *(const u32x4*)(k_tree + src);
-            *(u32x4*)(v_cache + dst) = *(const u32x4*)(v_tree + src);
+    // key range: rows j = 0 .. at kbase / vbase + j * stride elements; rows
+    // up to nspec - 1 are always in bounds, the first nkeys are the range
+    const bf16_t* kbase;
+    const bf16_t* vbase;
+    int nspec, stride, k0 = 0;
+    if (tree) {
+        const size_t o = (size_t)b * N * nKV * D + (size_t)kvh * D;
+        kbase = k_tree + o;
+        vbase = v_tree + o;
+        nspec = N;
+        stride = nKV * D;
+    } else {
+        k0 = s * KPS;
+        const size_t o = (cache_row0 + k0) * D;
+        kbase = k_cache + o;
+        vbase = v_cache + o;
+        nspec = max(1, min(KPS, max_cache_len - k0));
+        stride = D;
+    }
+
+    // the lane's queries (a padded query, qi >= N, computes with the last
+    // query's data and is never written) and, in the tree range, their
+    // ancestor rows (words past W are never used: the range has W tiles),
+    // loaded and waited for before any load into LDS is issued
+    int qidx[2];
+    uint64_t mrow[2][4] = {{~0ull, ~0ull, ~0ull, ~0ull}, {~0ull, ~0ull, ~0ull, ~0ull}};
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) qidx[qb] = qblk * MF_Q + qh * 32 + qb * 16 + lr;
+    if (tree) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) mrow[qb][w] = mask[(size_t)min(qidx[qb], N - 1) * W + min(w, W - 1)];
+        mf_loads_landed();
+    }
+    // the query block -> LDS: row r is query min(qblk * 64 + r, N - 1)
+#pragma unroll
+    for (int j = 0; j < NQLD; ++j) {
+        const int unit16 = (wave * NQLD + j) * 64 + lane;
+        const int r = unit16 / DC;
+        const int c = (unit16 % DC) ^ mf_swz<DC>(r);
+        const int qc = min(qblk * MF_Q + r, N - 1);
+        mf_dma16(q + (((size_t)b * N + qc) * nH + h) * D + c * 8, qlds + (wave * NQLD + j) * 1024);
+    }
+
+    // tile loads: wave w moves 1 KB blocks w * NLD .. w * NLD + NLD - 1 of a
+    // stage (the first half of the blocks is the K tile); lane l writes the
+    // 16-byte unit (block, l): row lrow[j], physical chunk -> logical chunk
+    const bool ld_v = wave * NLD >= BLKS / 2;
+    const char* gsrc = (const char*)(ld_v ? vbase : kbase);
+    int lrow[NLD];
+    uint32_t lcol[NLD];  // byte offset of the logical chunk within the row
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+        const int unit16 = ((wave * NLD + j) % (BLKS / 2)) * 64 + lane;  // 16-byte unit within the tile
+        lrow[j] = unit16 / DC;
+        lcol[j] = (uint32_t)(((unit16 % DC) ^ mf_swz<DC>(lrow[j])) * 16);
+    }
+    auto issue = [&](int stage, int i) {
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) {
+            const int row = min(i * TK + lrow[j], nspec - 1);
+            const char* src = gsrc + (size_t)row * stride * 2 + lcol[j];
+            mf_dma16(src, stage_ptr(stage) + (wave * NLD + j) * 1024);
         }
-    }
+    };
+    // the first three tiles of the range as far as it can reach (the true
+    // size is known only after the cache length is read)
+    const int nt_spec = (nspec + TK - 1) / TK;
+    issue(0, 0);
+    if (nt_spec > 1) issue(1, 1);
+    if (nt_spec > 2) issue(2, 2);
 
-    // this lane's queries (column lr of each of its 16-query blocks)
-    u32x4 qf[QBW][DK];
-    uint64_t mrow[QBW][4];
-    int qidx[QBW];
-#pragma unroll
-    for (int qb = 0; qb < QBW; ++qb) {
-        const int qi = (wave * QBW + qb) * 16 + lr;
-        qidx[qb] = qi;
-#pragma unroll
-        for (int ks = 0; ks < DK; ++ks)
-            qf[qb][ks] = qi < N ? *(const u32x4*)(q + (((size_t)b * N + qi) * nH + h) * D + ks * 32 + lk * 8)
-                                : (u32x4){0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int w = 0; w < 4; ++w) mrow[qb][w] = (qi < N && w < W) ? mask[(size_t)qi * W + w] : 0ull;
+    // the sequence's prefix length decides the range's true size
+    const int P = max(0, min(cache_len[b], max_cache_len));
+    const int nkeys = tree ? N : min(KPS, P - k0);
+    if (nkeys <= 0) {  // a range past this sequence's prefix: empty partials
+        if (tid < MF_Q) {
+            const int i = qblk * MF_Q + tid;
+            if (i < N) {
+                part_ml[(prow + i) * 2] = -INFINITY;
+                part_ml[(prow + i) * 2 + 1] = 0.f;
+            }
+        }
+        mf_loads_landed();  // no load into LDS outlives the workgroup
+        return;
     }
+    const int ntiles = (nkeys + TK - 1) / TK;
+    // tile t has been requested iff t < ntiles, or t < 3 and t < nt_spec
+    auto requested = [&](int t) { return t < ntiles || (t < 3 && t < nt_spec); };
+    u32x4 qf[2][DK];  // read from LDS after the first tile barrier
 
-    f32x4 o[QBW][DB];
-    float m[QBW], l[QBW];
+    // per-lane LDS byte offsets (within a stage) of the K and V^T fragments
+    const int krow = kq * 16 + lr;
+    uint32_t koff[DK];
 #pragma unroll
-    for (int qb = 0; qb < QBW; ++qb) {
-        m[qb] = -INFINITY;
-        l[qb] = 0.f;
+    for (int ks = 0; ks < DK; ++ks) koff[ks] = krow * ROWB + (((ks * 4 + lk) ^ mf_swz<DC>(krow)) * 16);
+    const int vrow = kq * 16 + lk * 4 + (lr >> 2);
+    uint32_t voff[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+        voff[db] = TILE_B + vrow * ROWB + (((db * 2 + ((lr & 3) >> 1)) ^ mf_swz<DC>(vrow)) * 16) + (lr & 1) * 8;
+
+    f32x4 o[2][DB];
+    float Mq[2], l[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        Mq[qb] = -3.402823466e38f;  // reference (scaled, base 2); finite so that M - M' never is inf - inf
+        l[qb] = 0.f;                // this lane's share of the query's sum
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[qb][db] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
 
-    const int k_begin = s * KPS;
-    const int k_end = min(total, k_begin + KPS);
-    const size_t cache_row0 = ((size_t)b * nKV + kvh) * Lmax;
-
-    // Tile loads: thread t owns KPT consecutive keys (group t / DC) and the
-    // 16-byte column chunk t % DC of each, so 16 lanes read one 256-byte key
-    // row contiguously.  K goes to LDS row-major; V is transposed in
-    // registers (v_perm_b32 pairs the same column of two keys) and written as
-    // KPT-key runs of each column row of Vt.
-    constexpr int KPT = PT;  // keys per thread per tile
-    const int kg = tid / DC, dc = tid - (tid / DC) * DC;
-    // Register ring of RING tiles: a workgroup's first RING tiles are all in
-    // flight before the first is consumed, and each consumed slot is refilled
-    // with the tile RING ahead.  Loads complete in issue order, so waiting for
-    // the oldest slot never waits for a younger one.
-    constexpr int RING = QBW == 1 ? 3 : 1;
-    u32x4 kreg[RING][KPT], vreg[RING][KPT];
-    auto load_tile = [&](u32x4(&kr)[KPT], u32x4(&vr)[KPT], int t0) {
+    for (int tb = 0; tb < ntiles; tb += MF_STAGES) {
 #pragma unroll
-        for (int e = 0; e < KPT; ++e) {
-            const int j = t0 + kg * KPT + e;
-            if (j < k_end) {
-                if (j < P) {
-                    const size_t off = (cache_row0 + j) * D + dc * 8;
-                    kr[e] = ld_stream(k_cache + off);
-                    vr[e] = ld_stream(v_cache + off);
-                } else {
-                    const size_t off = (((size_t)b * N + (j - P)) * nKV + kvh) * D + dc * 8;
-                    kr[e] = *(const u32x4*)(k_tree + off);
-                    vr[e] = *(const u32x4*)(v_tree + off);
-                }
-            } else {
-                kr[e] = (u32x4){0u, 0u, 0u, 0u};
-                vr[e] = (u32x4){0u, 0u, 0u, 0u};
-            }
-        }
-    };
-    // K -> LDS row-major (bf16); V widened to fp16 (exact for every bf16 value
-    // of magnitude >= 2^-14; smaller ones move by < 2^-25), transposed in
-    // registers and written as KPT-key runs of each row of Vt.
-    auto store_tile = [&](const u32x4(&kr)[KPT], const u32x4(&vr)[KPT]) {
+        for (int u = 0; u < MF_STAGES; ++u) {
+            const int i = tb + u;
+            if (i < ntiles) {
+                // wait for tile i: the younger requests are those of tiles i+1, i+2
+                if (requested(i + 2)) mf_tile_barrier<2 * NLD>();
+                else if (requested(i + 1)) mf_tile_barrier<NLD>();
+                else mf_tile_barrier<0>();
+                if (i + 3 < ntiles) issue((u + 3) % MF_STAGES, i + 3);
+                if (i == 0) {
 #pragma unroll
-        for (int e = 0; e < KPT; ++e) *(u32x4*)(&Ks[kg * KPT + e][dc * 8]) = kr[e];
+                    for (int qb = 0; qb < 2; ++qb) {
+                        const int r = qh * 32 + qb * 16 + lr;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {  // column dc * 8 + i
-            float f[KPT];
-#pragma unroll
-            for (int e = 0; e < KPT; ++e)
-                f[e] = (i & 1) ? bf16_hi(vr[e][i >> 1]) : bf16_lo(vr[e][i >> 1]);
-            uint16_t* dst = &Vt[dc * 8 + i][kg * KPT];
-            if (KPT == 4) {
-                *(uint2*)dst = (uint2){pack_f16x2(f[0], f[1]), pack_f16x2(f[2 % KPT], f[3 % KPT])};
-            } else if (KPT == 2) {
-                *(uint32_t*)dst = pack_f16x2(f[0], f[1 % KPT]);
-            } else {
-                *dst = (uint16_t)(pack_f16x2(f[0], 0.f) & 0xFFFFu);
-            }
-        }
-    };
-#pragma unroll
-    for (int u = 0; u < RING; ++u)
-        if (k_begin + u * TK < k_end) load_tile(kreg[u], vreg[u], k_begin + u * TK);
-    for (int tb = k_begin; tb < k_end; tb += RING * TK) {
-#pragma unroll
-        for (int u = 0; u < RING; ++u) {
-            const int t0 = tb + u * TK;
-            if (t0 < k_end) {
-                __syncthreads();
-                store_tile(kreg[u], vreg[u]);
-                __syncthreads();
-                if (t0 + RING * TK < k_end) load_tile(kreg[u], vreg[u], t0 + RING * TK);
-                {  // compute tile t0 (written inline: a lambda here made the compiler spill)
-        // tiles entirely inside the prefix and the split need no masking
-        // (padded query columns are never written out)
-        const bool plain = QBW == 1 && t0 + TK <= P && t0 + TK <= k_end;
-#pragma unroll
-        for (int qb = 0; qb < QBW; ++qb) {
-            f32x4 st[KB];
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                st[kb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < DK; ++ks) {
-                    const u32x4 a = *(const u32x4*)(&Ks[kb * 16 + lr][ks * 32 + lk * 8]);
-                    st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                                     __builtin_bit_cast(bf16x8, qf[qb][ks]), st[kb],
-                                                                     0, 0, 0);
-                }
-            }
-            // scale, mask (prefix: visible; tree key t: ancestor bit), tile max
-            const int qi = qidx[qb];
-            float tmax = -INFINITY;
-            if (plain) {
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        st[kb][r] *= scale_log2;
-                        tmax = fmaxf(tmax, st[kb][r]);
+                        for (int ks = 0; ks < DK; ++ks)
+                            qf[qb][ks] = *(const u32x4*)(qlds + r * ROWB + (((ks * 4 + lk) ^ mf_swz<DC>(r)) * 16));
                     }
-            } else {
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int j = t0 + kb * 16 + lk * 4 + r;
-                        bool vis = j < k_end && qi < N;
-                        if (vis && j >= P) {
-                            const int t = j - P;
-                            const int w = t >> 6;
-                            const uint64_t word = w == 0 ? mrow[qb][0] : w == 1 ? mrow[qb][1]
-                                                                      : w == 2 ? mrow[qb][2] : mrow[qb][3];
-                            vis = (word >> (t & 63)) & 1ull;
-                        }
-                        const float x = vis ? st[kb][r] * scale_log2 : -INFINITY;
-                        st[kb][r] = x;
-                        tmax = fmaxf(tmax, x);
-                    }
-            }
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-            const float m_new = fmaxf(m[qb], tmax);
-            const bool live = m_new != -INFINITY;
-            // exponents are <= 0: the bare v_exp_f32 (no denormal range fix-up;
-            // results below 2^-126 vanish in the fp16 probabilities anyway)
-            const float alpha = live ? __builtin_amdgcn_exp2f(m[qb] - m_new) : 1.f;
-            float psum = 0.f;
-            uint32_t pk[KB][2];  // fp16 pairs of P^T (round to nearest even)
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                float p4[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    p4[r] = live ? __builtin_amdgcn_exp2f(st[kb][r] - m_new) : 0.f;
-                    psum += p4[r];
                 }
-                pk[kb][0] = pack_f16x2(p4[0], p4[1]);
-                pk[kb][1] = pack_f16x2(p4[2], p4[3]);
-            }
-            psum += __shfl_xor(psum, 16, 64);
-            psum += __shfl_xor(psum, 32, 64);
-            l[qb] = l[qb] * alpha + psum;
-            m[qb] = m_new;
-            // the accumulators live in AGPRs, so a rescale costs three instructions
-            // per element: skip it when no query of the wave raised its max
-            if (__any(alpha != 1.f)) {
+                const char* st = stage_ptr(u);
+                u32x4 ka[DK];
 #pragma unroll
-                for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
-            }
-#pragma unroll
-            for (int k2 = 0; k2 < TK / 32; ++k2) {
-                const u32x4 bp = (u32x4){pk[2 * k2][0], pk[2 * k2][1], pk[2 * k2 + 1][0], pk[2 * k2 + 1][1]};
+                for (int ks = 0; ks < DK; ++ks) ka[ks] = *(const u32x4*)(st + koff[ks]);
+                u32x4 va[DB];  // the 4 keys' V^T values, repeated in both halves
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    const uint2 lo = *(const uint2*)(&Vt[db * 16 + lr][k2 * 32 + lk * 4]);
-                    const uint2 hi = *(const uint2*)(&Vt[db * 16 + lr][k2 * 32 + 16 + lk * 4]);
-                    const u32x4 av = (u32x4){lo.x, lo.y, hi.x, hi.y};
-                    o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av),
-                                                                       __builtin_bit_cast(f16x8, bp), o[qb][db], 0,
-                                                                       0, 0);
+                    const uint2 v = __builtin_bit_cast(uint2, ds_read_tr16(st + voff[db]));
+                    va[db] = (u32x4){v.x, v.y, v.x, v.y};
                 }
-            }
-        }
+                const bool masked = tree || (i + 1) * TK > nkeys;
+                const int kk0 = kq * 16 + lk * 4;  // the lane's first key within the tile
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+                    f32x4 sc = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < DK; ++ks)
+                        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[ks]),
+                                                                     __builtin_bit_cast(bf16x8, qf[qb][ks]), sc, 0, 0,
+                                                                     0);
+                    // mask: keys past the range; in the tree range, non-ancestors
+                    if (masked) {
+                        const uint64_t word = !tree ? ~0ull : i == 0 ? mrow[qb][0] : i == 1 ? mrow[qb][1]
+                                                                       : i == 2 ? mrow[qb][2] : mrow[qb][3];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const bool vis = i * TK + kk0 + r < nkeys && ((word >> (kk0 + r)) & 1ull);
+                            sc[r] = vis ? sc[r] : -INFINITY;
+                        }
                     }
+                    const float lm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+                    if (__any(lm * scale_log2 > Mq[qb] + MF_LAZY)) {
+                        // raise the reference of the queries that need it (the
+                        // tile max over the query's 4 lanes decides, so they agree)
+                        float t = fmaxf(lm, __shfl_xor(lm, 16, 64));
+                        t = fmaxf(t, __shfl_xor(t, 32, 64));
+                        const float tc = t * scale_log2;
+                        const float Mn = tc > Mq[qb] + MF_LAZY ? tc : Mq[qb];
+                        const float alpha = __builtin_amdgcn_exp2f(Mq[qb] - Mn);  // exactly 1 when unchanged
+                        Mq[qb] = Mn;
+                        l[qb] *= alpha;
+#pragma unroll
+                        for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
+                    }
+                    // probabilities (bare v_exp_f32: arguments <= 8, masked ones -inf)
+                    const float nm = -Mq[qb];
+                    float p4[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        p4[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], scale_log2, nm));
+                        l[qb] += p4[r];
+                    }
+                    // p = head + remainder, both bf16 (17 significant bits
+                    // together): k-slots 0..3 of the lane's B fragment carry the
+                    // heads of its 4 keys, slots 4..7 the remainders, and the A
+                    // fragment repeats the 4 keys' V^T values in both halves
+                    const uint32_t h01 = pack_bf16x2(p4[0], p4[1]), h23 = pack_bf16x2(p4[2], p4[3]);
+                    const uint32_t r01 = pack_bf16x2(p4[0] - bf16_lo(h01), p4[1] - bf16_hi(h01));
+                    const uint32_t r23 = pack_bf16x2(p4[2] - bf16_lo(h23), p4[3] - bf16_hi(h23));
+                    const u32x4 pb = (u32x4){h01, h23, r01, r23};
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+                        o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va[db]),
+                                                                            __builtin_bit_cast(bf16x8, pb), o[qb][db],
+                                                                            0, 0, 0);
+                }
             }
         }
     }
 
-    // O^T block db: lane holds d = db*16 + 4*lk + r of query column lr
+    // per-query sums over the 4 lanes of the query
 #pragma unroll
-    for (int qb = 0; qb < QBW; ++qb) {
-        const int qi = qidx[qb];
-        if (qi < N) {
-            const size_t pr = ((size_t)bh * S + s) * N + qi;
+    for (int qb = 0; qb < 2; ++qb) {
+        l[qb] += __shfl_xor(l[qb], 16, 64);
+        l[qb] += __shfl_xor(l[qb], 32, 64);
+    }
+    // the stages become the merge area once no tile load is in flight
+    mf_loads_landed();
+    // merge the key quarters: quarters 2, 3 into 0, 1, then 1 into 0 (the
+    // state of source slot k sits in stage k)
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
-                *(f32x4*)(part_o + pr * D + db * 16 + lk * 4) = o[qb][db];
-            if (lk == 0) { part_ml[pr * 2] = m[qb]; part_ml[pr * 2 + 1] = l[qb]; }
+    for (int step = 0; step < 2; ++step) {
+        const int lo = step == 0 ? 2 : 1;   // source quarters lo .. 2 lo - 1 merge into quarters 0 .. lo - 1
+        __syncthreads();                     // the stages (or the previous step's area) are free
+        if (kq >= lo && kq < 2 * lo) {
+            float* w = (float*)stage_ptr((kq - lo) * 2 + qh);
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+                for (int db = 0; db < DB; ++db) *(f32x4*)(w + ((qb * DB + db) * 64 + lane) * 4) = o[qb][db];
+                *(float2*)(w + 2 * DB * 64 * 4 + (qb * 64 + lane) * 2) = (float2){Mq[qb], l[qb]};
+            }
+        }
+        __syncthreads();
+        if (kq < lo) {
+            const float* w = (const float*)stage_ptr(kq * 2 + qh);
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const float2 ml = *(const float2*)(w + 2 * DB * 64 * 4 + (qb * 64 + lane) * 2);
+                const float Mn = fmaxf(Mq[qb], ml.x);
+                const float fa = __builtin_amdgcn_exp2f(Mq[qb] - Mn), fb = __builtin_amdgcn_exp2f(ml.x - Mn);
+                Mq[qb] = Mn;
+                l[qb] = l[qb] * fa + ml.y * fb;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    o[qb][db] = o[qb][db] * fa + *(const f32x4*)(w + ((qb * DB + db) * 64 + lane) * 4) * fb;
+            }
+        }
+    }
+    // key quarter 0 writes the partial: O^T block db, lane holds
+    // d = db * 16 + 4 * lk + r of query column lr
+    if (kq == 0) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            if (qidx[qb] < N) {
+                const size_t r = prow + qidx[qb];
+#pragma unroll
+                for (int db = 0; db < DB; ++db) *(f32x4*)(part_o + r * D + db * 16 + lk * 4) = o[qb][db];
+                if (lk == 0) {
+                    part_ml[r * 2] = l[qb] > 0.f ? Mq[qb] : -INFINITY;
+                    part_ml[r * 2 + 1] = l[qb];
+                }
+            }
+        }
+    }
+    // tree keys/values -> cache slots P..P+N-1 (one writer per KV head)
+    if (tree && qblk == 0 && h % grp == 0) {
+        for (int e = tid; e < N * DC; e += MF_THREADS) {
+            const int t = e / DC, c = e - t * DC;
+            const size_t src = (size_t)t * stride + c * 8;
+            const size_t dst = (cache_row0 + P + t) * D + c * 8;
+            *(u32x4*)(k_cache + dst) = *(const u32x4*)(kbase + src);
+            *(u32x4*)(v_cache + dst) = *(const u32x4*)(vbase + src);
         }
     }
 }
 
 struct AttnPlan {
     bool mfma;
-    int S;    // splits of the key range
-    int KPS;  // keys per split
+    int S;    // partial slots per (head, query): key ranges
+    int KPS;  // keys per range (MFMA: prefix keys per range; the tree keys are one more range)
+    int QB;   // query blocks per head (MFMA)
 };
 
-// Workgroups the split of the key range aims at (MFMA path / vector-ALU path).
+// Workgroups the key-range split aims at: the MFMA path fills one round of
+// the 256 CUs (one 8-wave workgroup per CU), the vector-ALU path several.
 constexpr int ATT_MFMA_TARGET_WG = 256;
+constexpr int ATT_MFMA_MAX_RANGE = 2816;
 constexpr int ATT_VALU_TARGET_WG = 1024;
 
-static AttnPlan attn_plan(bool bf16, int B, int nH, int N, int max_total, int target_wg = 0) {
+static AttnPlan attn_plan(bool bf16, int B, int nH, int N, int max_cache_len, int target_wg = 0) {
     AttnPlan p;
     p.mfma = bf16 && N <= MEDUSA_MAX_NODES_DEV;
-    const int unit = p.mfma ? 32 : ATT_TK;
-    const int qblocks = p.mfma ? 1 : (N + ATT_QB - 1) / ATT_QB;
-    const int base = B * nH * qblocks;
-    const int target = target_wg > 0 ? target_wg : p.mfma ? ATT_MFMA_TARGET_WG : ATT_VALU_TARGET_WG;
+    if (p.mfma) {
+        // as many prefix ranges as fit beside the tree range in the target,
+        // but no range longer than ATT_MFMA_MAX_RANGE keys (a longer chain of
+        // tiles in one workgroup costs more than the extra partials), each a
+        // whole number of 64-key tiles (measured: 7 ranges of 320 keys for
+        // 32 heads x 2048 keys, 2 of 2048 for 4 query blocks x 32 heads x
+        // 4096 keys, 3 of 2752 for 8 x 32 heads up to 8192 keys)
+        p.QB = (N + MF_Q - 1) / MF_Q;
+        const int target = target_wg > 0 ? target_wg : ATT_MFMA_TARGET_WG;
+        const int units = B * nH * p.QB;
+        int Sp = target / units - 1;
+        const int by_len = (max_cache_len + ATT_MFMA_MAX_RANGE - 1) / ATT_MFMA_MAX_RANGE;
+        if (Sp < by_len) Sp = by_len;
+        if (Sp < 1) Sp = 1;
+        long long kps = ((long long)max_cache_len + Sp - 1) / Sp;
+        if (kps < MF_TK) kps = MF_TK;
+        kps = (kps + MF_TK - 1) / MF_TK * MF_TK;
+        p.KPS = (int)kps;
+        p.S = (int)((max_cache_len + kps - 1) / kps) + 1;
+        return p;
+    }
+    const int max_total = max_cache_len + N;
+    const int base = B * nH * ((N + ATT_QB - 1) / ATT_QB);
+    const int target = target_wg > 0 ? target_wg : ATT_VALU_TARGET_WG;
     int S = (target + base - 1) / base;
-    const int max_s = (max_total + unit - 1) / unit;
+    const int max_s = (max_total + ATT_TK - 1) / ATT_TK;
     if (S > max_s) S = max_s;
-    if (S > ATT_MAX_SPLITS) S = ATT_MAX_SPLITS;
     if (S < 1) S = 1;
     int kps = (max_total + S - 1) / S;
-    kps = ((kps + unit - 1) / unit) * unit;
+    kps = ((kps + ATT_TK - 1) / ATT_TK) * ATT_TK;
     p.KPS = kps;
     p.S = (max_total + kps - 1) / kps;
+    p.QB = 1;
     return p;
 }
 
@@ -497,56 +689,53 @@ void launch_tree_attention(const void* q, const void* k_tree, const void* v_tree
                            int nKV, int D, int Lmax, float scale, bool bf16, void* out, float* part_o,
                            float* part_ml, hipStream_t s, int target_wg) {
     const int N = t.N;
-    const AttnPlan pl = attn_plan(bf16, B, nH, N, max_cache_len + N, target_wg);
+    const AttnPlan pl = attn_plan(bf16, B, nH, N, max_cache_len, target_wg);
     const float scale_log2 = scale * 1.4426950408889634f;
     if (pl.mfma) {
         const bf16_t *Q = (const bf16_t*)q, *KT = (const bf16_t*)k_tree, *VT = (const bf16_t*)v_tree;
         bf16_t *KC = (bf16_t*)k_cache, *VC = (bf16_t*)v_cache;
-#define MEDUSA_MF(DD, WV, QB)                                                                                   \
-    MEDUSA_LAUNCH("tree_attn_mfma", (tree_attn_mfma_kernel<DD, WV, QB>), dim3(B * nH, pl.S), dim3(WV * 64), 0, s, \
-                  Q, KT, VT, KC, VC, cache_len, t.mask, N, t.W, nH, nKV, Lmax, max_cache_len, scale_log2, pl.KPS,   \
-                  part_o, part_ml)
-        if (D == 64) {
-            if (N <= 64) MEDUSA_MF(64, 4, 1); else if (N <= 128) MEDUSA_MF(64, 4, 2); else MEDUSA_MF(64, 8, 2);
-        } else {
-            if (N <= 64) MEDUSA_MF(128, 4, 1); else if (N <= 128) MEDUSA_MF(128, 4, 2); else MEDUSA_MF(128, 8, 2);
-        }
+        const int units = B * nH * pl.S;
+        const dim3 grid((unsigned)(((units + 7) / 8) * 8 * pl.QB));
+#define MEDUSA_MF(DD)                                                                                        \
+    MEDUSA_LAUNCH("tree_attn_mfma", (tree_attn_mfma_kernel<DD>), grid, dim3(MF_THREADS), 0, s, Q, KT, VT,     \
+                  KC, VC, cache_len, t.mask, N, t.W, nH, nKV, Lmax, max_cache_len, scale_log2, pl.KPS, pl.S,  \
+                  pl.QB, B * nH, part_o, part_ml)
+        if (D == 64) MEDUSA_MF(64); else MEDUSA_MF(128);
 #undef MEDUSA_MF
-        if (D == 64)
-            MEDUSA_LAUNCH("tree_attn_combine", (tree_attn_combine_kernel<bf16_t, 64>), dim3(N, B * nH), dim3(64), 0,
-                          s, part_o, part_ml, pl.S, N, nH, (bf16_t*)out);
-        else
-            MEDUSA_LAUNCH("tree_attn_combine", (tree_attn_combine_kernel<bf16_t, 128>), dim3(N, B * nH), dim3(128),
-                          0, s, part_o, part_ml, pl.S, N, nH, (bf16_t*)out);
-        return;
-    }
-    const dim3 grid(B * nH, pl.S, (N + ATT_QB - 1) / ATT_QB);
-    const int S = pl.S, KPS = pl.KPS;
-#define MEDUSA_ATT(T, DD)                                                                                   \
-    do {                                                                                                    \
-        MEDUSA_LAUNCH("tree_attn_split", (tree_attn_valu_kernel<T, DD>), grid, dim3(ATT_THREADS), 0, s,     \
-                      (const T*)q, (const T*)k_tree, (const T*)v_tree, (T*)k_cache, (T*)v_cache, cache_len, \
-                      t.mask, N, t.W, nH, nKV, Lmax, max_cache_len, scale_log2, KPS, part_o, part_ml);      \
-        MEDUSA_LAUNCH("tree_attn_combine", (tree_attn_combine_kernel<T, DD>), dim3(N, B * nH), dim3(DD), 0, \
-                      s, part_o, part_ml, S, N, nH, (T*)out);                                               \
-    } while (0)
-    if (bf16) {
-        if (D == 64) MEDUSA_ATT(bf16_t, 64); else MEDUSA_ATT(bf16_t, 128);
     } else {
-        if (D == 64) MEDUSA_ATT(float, 64); else MEDUSA_ATT(float, 128);
-    }
+        const dim3 grid(B * nH, pl.S, (N + ATT_QB - 1) / ATT_QB);
+#define MEDUSA_ATT(T, DD)                                                                                   \
+    MEDUSA_LAUNCH("tree_attn_split", (tree_attn_valu_kernel<T, DD>), grid, dim3(ATT_THREADS), 0, s,         \
+                  (const T*)q, (const T*)k_tree, (const T*)v_tree, (T*)k_cache, (T*)v_cache, cache_len,     \
+                  t.mask, N, t.W, nH, nKV, Lmax, max_cache_len, scale_log2, pl.KPS, part_o, part_ml)
+        if (bf16) {
+            if (D == 64) MEDUSA_ATT(bf16_t, 64); else MEDUSA_ATT(bf16_t, 128);
+        } else {
+            if (D == 64) MEDUSA_ATT(float, 64); else MEDUSA_ATT(float, 128);
+        }
 #undef MEDUSA_ATT
+    }
+#define MEDUSA_MERGE(T, DD)                                                                                  \
+    MEDUSA_LAUNCH("tree_attn_merge", (tree_attn_merge_kernel<T, DD>),                                        \
+                  dim3((N + ATT_MERGE_THREADS / (DD / 4) - 1) / (ATT_MERGE_THREADS / (DD / 4)), B * nH),     \
+                  dim3(ATT_MERGE_THREADS), 0, s, part_o, part_ml, pl.S, N, nH, (T*)out)
+    if (bf16) {
+        if (D == 64) MEDUSA_MERGE(bf16_t, 64); else MEDUSA_MERGE(bf16_t, 128);
+    } else {
+        if (D == 64) MEDUSA_MERGE(float, 64); else MEDUSA_MERGE(float, 128);
+    }
+#undef MEDUSA_MERGE
 }
 
 size_t attn_workspace_bytes(int B, int nH, int N, int D, int max_cache_len, bool bf16) {
-    const int S = attn_plan(bf16, B, nH, N, max_cache_len + N).S;
+    const int S = attn_plan(bf16, B, nH, N, max_cache_len).S;
     const size_t rows = (size_t)B * nH * S * N;
     return (rows * D * sizeof(float) + 255) / 256 * 256 + rows * 2 * sizeof(float);
 }
 
 void attn_carve(int B, int nH, int N, int D, int max_cache_len, bool bf16, void* ws, float** part_o,
                 float** part_ml) {
-    const int S = attn_plan(bf16, B, nH, N, max_cache_len + N).S;
+    const int S = attn_plan(bf16, B, nH, N, max_cache_len).S;
     const size_t rows = (size_t)B * nH * S * N;
     *part_o = (float*)ws;
     *part_ml = (float*)((char*)ws + (rows * D * sizeof(float) + 255) / 256 * 256);
