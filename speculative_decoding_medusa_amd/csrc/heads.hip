@@ -318,33 +318,50 @@ static void launch_gemv_t(const void* x, const WT* W, const WT* bias, int B, int
                   pl.rows_per_wg, out, cv, ci, topk);
 }
 
-// Production shapes (measured on the 7B head shapes, 20480 and 160000 rows of
-// 4096 bf16): the residual-SiLU block runs 4 waves x 4 rows per step on about
-// 512 workgroups (2 rows per step above two right-hand sides, to bound
-// registers); the vocabulary projection 8 waves x 2 rows per step on about
-// 2048 workgroups.
-constexpr int SILU_WAVES = 4, SILU_TARGET_WG = 512;
-constexpr int TOPK_R = 2, TOPK_WAVES = 8, TOPK_TARGET_WG = 2048;
-static int silu_r(int NB) { return NB <= 2 ? 4 : 2; }
+// Production shapes, measured on the 7B head shapes (W1: 5 x 4096 rows, W2:
+// 5 x 32000 and 5 x 128256 rows, of 4096 bf16).  One right-hand side streams
+// the weights (4 waves x 4 rows per step on ~512 workgroups for W1, 8 waves x
+// 2 rows on ~2048 for W2).  With 8 right-hand sides the kernel is bound by
+// the vector ALUs and the LDS reads of the right-hand sides, which more rows
+// per step amortise: 8 waves x 4 rows on ~256 workgroups for W1 (111 us
+// against 235 with 2 rows), 4 waves x 8 rows on ~1024 for W2 (2.32 ms against
+// 3.64).
+struct GemvShape {
+    int R, WAVES, target;
+};
+static GemvShape silu_shape(int NB) { return NB <= 2 ? GemvShape{4, 4, 512} : GemvShape{4, 8, 256}; }
+static GemvShape topk_shape(int NB) {
+    return NB <= 2 ? GemvShape{2, 8, 2048} : NB <= 4 ? GemvShape{4, 4, 1024} : GemvShape{8, 4, 1024};
+}
 
-template <typename WT, int EPI, int R, int WAVES>
-static void launch_gemv_nb(int NB, int CPL, const void* x, const WT* W, const WT* bias, int B, int H,
-                           int nrows, int K, const GemvPlan& pl, float* out, float* cv, int* ci, int topk,
-                           hipStream_t s, const char* name) {
-#define MEDUSA_GEMV_CASE(nb, cpl)                                                                          \
-    if (NB == nb && CPL == cpl)                                                                            \
-        return launch_gemv_t<WT, nb, cpl, R, EPI, WAVES>(x, W, bias, B, H, nrows, K, pl, out, cv, ci, topk, s, \
+// Dispatch on the chunks per lane of one right-hand-side width NB.
+template <typename WT, int NB, int EPI, int R, int WAVES>
+static void launch_gemv_cpl(int CPL, const void* x, const WT* W, const WT* bias, int B, int H, int nrows, int K,
+                            const GemvPlan& pl, float* out, float* cv, int* ci, int topk, hipStream_t s,
+                            const char* name) {
+#define MEDUSA_GEMV_CASE(cpl)                                                                               \
+    if (CPL == cpl)                                                                                         \
+        return launch_gemv_t<WT, NB, cpl, R, EPI, WAVES>(x, W, bias, B, H, nrows, K, pl, out, cv, ci, topk, s, \
                                                          name);
-#define MEDUSA_GEMV_NB(nb) \
-    MEDUSA_GEMV_CASE(nb, 1) MEDUSA_GEMV_CASE(nb, 2) MEDUSA_GEMV_CASE(nb, 4) MEDUSA_GEMV_CASE(nb, 8) MEDUSA_GEMV_CASE(nb, 16)
-    MEDUSA_GEMV_NB(1) MEDUSA_GEMV_NB(2) MEDUSA_GEMV_NB(4) MEDUSA_GEMV_NB(8)
-#undef MEDUSA_GEMV_NB
+    MEDUSA_GEMV_CASE(1) MEDUSA_GEMV_CASE(2) MEDUSA_GEMV_CASE(4) MEDUSA_GEMV_CASE(8) MEDUSA_GEMV_CASE(16)
 #undef MEDUSA_GEMV_CASE
 }
 
+// Dispatch on NB among the widths NBS (the widths a launch shape serves).
+template <typename WT, int EPI, int R, int WAVES, int... NBS>
+static void launch_gemv_nb(int NB, int CPL, const void* x, const WT* W, const WT* bias, int B, int H,
+                           int nrows, int K, const GemvPlan& pl, float* out, float* cv, int* ci, int topk,
+                           hipStream_t s, const char* name) {
+    (void)((NB == NBS ? (launch_gemv_cpl<WT, NBS, EPI, R, WAVES>(CPL, x, W, bias, B, H, nrows, K, pl, out, cv, ci,
+                                                                  topk, s, name),
+                         true)
+                      : false) ||
+           ...);
+}
+
 static GemvPlan topk_plan(int V, int K, int NB) {
-    (void)NB;
-    return gemv_plan(V, K, TOPK_TARGET_WG, TOPK_WAVES * TOPK_R);
+    const GemvShape sh = topk_shape(NB);
+    return gemv_plan(V, K, sh.target, sh.WAVES * sh.R);
 }
 
 int vocab_topk_groups(int B, int V, int K) { return topk_plan(V, K, pick_nb(B)).G; }
@@ -361,18 +378,20 @@ void launch_resid_silu(const void* h, const void* w1, const void* b1, int B, int
                        float* z, hipStream_t s) {
     const int PER = bf16 ? 8 : 4;
     const int NB = pick_nb(B), CPL = pick_cpl(H / PER);
-    const int R = silu_r(NB);
-    const GemvPlan pl = gemv_plan(H, K, SILU_TARGET_WG, SILU_WAVES * R);
-#define MEDUSA_SILU_GO(RR)                                                                                         \
-    do {                                                                                                           \
-        if (bf16)                                                                                                  \
-            launch_gemv_nb<bf16_t, EPI_SILU, RR, SILU_WAVES>(NB, CPL, h, (const bf16_t*)w1, (const bf16_t*)b1, B, H, \
-                                                            H, K, pl, z, nullptr, nullptr, 0, s, "resid_silu_gemv"); \
-        else                                                                                                       \
-            launch_gemv_nb<float, EPI_SILU, RR, SILU_WAVES>(NB, CPL, h, (const float*)w1, (const float*)b1, B, H, H, \
-                                                           K, pl, z, nullptr, nullptr, 0, s, "resid_silu_gemv");    \
+    const GemvShape sh = silu_shape(NB);
+    const GemvPlan pl = gemv_plan(H, K, sh.target, sh.WAVES * sh.R);
+#define MEDUSA_SILU_GO(RR, WV, ...)                                                                            \
+    do {                                                                                                       \
+        if (bf16)                                                                                              \
+            launch_gemv_nb<bf16_t, EPI_SILU, RR, WV, __VA_ARGS__>(NB, CPL, h, (const bf16_t*)w1, (const bf16_t*)b1, \
+                                                                 B, H, H, K, pl, z, nullptr, nullptr, 0, s,      \
+                                                                 "resid_silu_gemv");                             \
+        else                                                                                                   \
+            launch_gemv_nb<float, EPI_SILU, RR, WV, __VA_ARGS__>(NB, CPL, h, (const float*)w1, (const float*)b1, B, \
+                                                                H, H, K, pl, z, nullptr, nullptr, 0, s,          \
+                                                                "resid_silu_gemv");                              \
     } while (0)
-    if (R == 4) MEDUSA_SILU_GO(4); else MEDUSA_SILU_GO(2);
+    if (sh.WAVES == 4) MEDUSA_SILU_GO(4, 4, 1, 2); else MEDUSA_SILU_GO(4, 8, 4, 8);
 #undef MEDUSA_SILU_GO
 }
 
@@ -394,13 +413,19 @@ void launch_vocab_topk_named(const float* z, const void* w2, int B, int H, int V
                              const char* gemv_name, const char* merge_name) {
     const int PER = bf16 ? 8 : 4;
     const int NB = pick_nb(B), CPL = pick_cpl(H / PER);
+    const GemvShape sh = topk_shape(NB);
     const GemvPlan pl = topk_plan(V, K, NB);
-    if (bf16)
-        launch_gemv_nb<bf16_t, EPI_TOPK, TOPK_R, TOPK_WAVES>(NB, CPL, z, (const bf16_t*)w2, nullptr, B, H, V, K, pl,
-                                                             logits, cv, ci, topk, s, gemv_name);
-    else
-        launch_gemv_nb<float, EPI_TOPK, TOPK_R, TOPK_WAVES>(NB, CPL, z, (const float*)w2, nullptr, B, H, V, K, pl,
-                                                            logits, cv, ci, topk, s, gemv_name);
+#define MEDUSA_TOPK_GO(RR, WV, ...)                                                                               \
+    do {                                                                                                          \
+        if (bf16)                                                                                                 \
+            launch_gemv_nb<bf16_t, EPI_TOPK, RR, WV, __VA_ARGS__>(NB, CPL, z, (const bf16_t*)w2, nullptr, B, H, V, K, \
+                                                                 pl, logits, cv, ci, topk, s, gemv_name);          \
+        else                                                                                                      \
+            launch_gemv_nb<float, EPI_TOPK, RR, WV, __VA_ARGS__>(NB, CPL, z, (const float*)w2, nullptr, B, H, V, K,  \
+                                                                pl, logits, cv, ci, topk, s, gemv_name);           \
+    } while (0)
+    if (sh.R == 2) MEDUSA_TOPK_GO(2, 8, 1, 2); else if (sh.R == 4) MEDUSA_TOPK_GO(4, 4, 4); else MEDUSA_TOPK_GO(8, 4, 8);
+#undef MEDUSA_TOPK_GO
     launch_topk_merge(cv, ci, B * K, pl.G * topk, topk, topk_idx, topk_val, s, merge_name);
 }
 
