@@ -37,11 +37,11 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 # calibration (profiles/medusa_step_hbm_counters__vicuna7b_sparse64.txt).
 # Valid only for the kernel sources they were taken on (sha256 prefix of
 # heads.hip + common.hpp); reported as null after any change to them.
-VOCAB_TRAFFIC = {"sources_sha256_16": "009e083c90dc20a3", "read_bytes": 1311508042, "write_bytes": 128090}
+VOCAB_TRAFFIC = {"sources_sha256_16": "048b28c1d5af0dd6", "read_bytes": 1311518018, "write_bytes": 128138}
 # the same for the gate|up projection of the 32-layer workload (one layer's
 # launch: 64 x 4096 node rows against 22016 packed weight rows, unsplit, the
 # SwiGLU product written in bf16)
-GATE_UP_TRAFFIC = {"sources_sha256_16": "1d07fdc9042c6638", "read_bytes": 187013933, "write_bytes": 1409242}
+GATE_UP_TRAFFIC = {"sources_sha256_16": "1d07fdc9042c6638", "read_bytes": 187009641, "write_bytes": 1409318}
 
 
 def _traffic_bytes(rec, sources):
@@ -211,7 +211,7 @@ def main():
         "heads_resid_silu": stage("resid_silu_gemv"),
         "heads_vocab_topk": stage("vocab_proj_topk", "topk_merge"),
         "build_tree": stage("build_tree"),
-        "tree_attention": stage("tree_attn_split", "tree_attn_mfma", "tree_attn_combine"),
+        "tree_attention": stage("tree_attn_split", "tree_attn_mfma", "tree_attn_merge"),
         "base_greedy": stage("rmsnorm_rows", "lm_head_argmax", "argmax_merge") +
         prof.get("lm_head_gemv", (0, 0.0))[1] * 1e3 / max(args.steps, 1) +
         prof.get("lm_head_gemv_merge", (0, 0.0))[1] * 1e3 / max(args.steps, 1),

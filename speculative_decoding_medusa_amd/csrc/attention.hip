@@ -1,17 +1,19 @@
 // Tree-masked attention (step a4): every tree node attends to the cache
 // prefix plus its own ancestors-or-self.
 //
-// Split-KV layout: grid (B * nH, S, query blocks).  Split s of sequence b
-// covers keys [s * KPS, (s+1) * KPS) of the key space "prefix (cache_len[b]
-// keys) followed by the N tree keys"; tree keys come straight from k_tree /
-// v_tree and are visible to query i only where bit j of its ancestor row is
-// set.  Each split keeps an online-softmax state (running max m, running sum l,
-// unnormalised output) in base-2 exponent form, written as a partial; a
-// combine kernel rescales and sums the partials.  Split 0 / query block 0 of
-// every KV head also copies the tree keys/values into cache slots
+// Both variants split the key space "prefix (cache_len[b] keys) followed by
+// the N tree keys" into ranges; tree keys come straight from k_tree / v_tree
+// and are visible to query i only where bit j of its ancestor row is set.
+// Each range keeps an online-softmax state (reference m, sum l, unnormalised
+// output) in base-2 exponent form, written as a partial, and
+// tree_attn_merge_kernel rescales and sums the partials.  One workgroup per
+// KV head also copies the tree keys/values into cache slots
 // cache_len .. cache_len + N - 1.
 //
-// This is the vector-ALU variant (float32 or bf16 storage, float32 math).
+// First the vector-ALU variant (float32 storage): grid (B * nH, S, query
+// blocks of 16); range s covers keys [s * KPS, (s+1) * KPS) of the key space;
+// split 0 / query block 0 writes the cache slots.  The bf16 MFMA variant
+// follows the merge kernel.
 #include "common.hpp"
 #include "tree.hpp"
 
