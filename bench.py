@@ -37,7 +37,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 # calibration (profiles/medusa_step_hbm_counters__vicuna7b_sparse64.txt).
 # Valid only for the kernel sources they were taken on (sha256 prefix of
 # heads.hip + common.hpp); reported as null after any change to them.
-VOCAB_TRAFFIC = {"sources_sha256_16": "048b28c1d5af0dd6", "read_bytes": 1311518018, "write_bytes": 128138}
+VOCAB_TRAFFIC = {"sources_sha256_16": "882a53cfb293a163", "read_bytes": 1311511587, "write_bytes": 128106}
 # the same for the gate|up projection of the 32-layer workload (one layer's
 # launch: 64 x 4096 node rows against 22016 packed weight rows, unsplit, the
 # SwiGLU product written in bf16)
@@ -135,7 +135,13 @@ def main():
     z = torch.empty(B, K, H, device="cuda")
     ti = torch.empty(B, K, topk, dtype=torch.int32, device="cuda")
     tv = torch.empty(B, K, topk, device="cuda")
-    ws_v = torch.empty(M.vocab_topk_workspace_size(B, H, V, K, topk, wdt), dtype=torch.uint8, device="cuda")
+    # from 4 sequences on, W2 in the packed layout of the MFMA vocabulary
+    # product (packed once, like a weight load); fewer sequences stream the
+    # row-major W2 through the vector-ALU GEMV
+    w2_layout = M.PACKED if B >= 4 and wdt == M.BF16 and H % 256 == 0 else M.ROW_MAJOR
+    w2 = M.pack_heads(d.pop("W2")) if w2_layout == M.PACKED else d["W2"]
+    ws_v = torch.empty(M.vocab_topk_workspace_size(B, H, V, K, topk, wdt, w2_layout), dtype=torch.uint8,
+                       device="cuda")
     tok = torch.empty(B, N, dtype=torch.int32, device="cuda")
     pos = torch.empty_like(tok)
     o = torch.empty_like(d["q"])
@@ -155,7 +161,7 @@ def main():
 
     def step():
         M.medusa_resid_silu(d["h"], d["W1"], d["b1"], z)
-        M.medusa_vocab_topk(z, d["W2"], topk, ti, tv, ws=ws_v)
+        M.medusa_vocab_topk(z, w2, topk, ti, tv, ws=ws_v)
         M.medusa_build_tree(tree, ti, root_d, d["cache_len"], tok, pos)
         M.tree_attention_verify(d["q"], d["k_tree"], d["v_tree"], d["k_cache"], d["v_cache"], d["cache_len"], maxP,
                                 tree, o, ws=ws_a)
@@ -209,7 +215,7 @@ def main():
 
     st = {
         "heads_resid_silu": stage("resid_silu_gemv"),
-        "heads_vocab_topk": stage("vocab_proj_topk", "topk_merge"),
+        "heads_vocab_topk": stage("vocab_proj_topk", "split_rows", "vocab_proj_topk_mfma", "topk_merge"),
         "build_tree": stage("build_tree"),
         "tree_attention": stage("tree_attn_split", "tree_attn_mfma", "tree_attn_merge"),
         "base_greedy": stage("rmsnorm_rows", "lm_head_argmax", "argmax_merge") +
@@ -223,10 +229,14 @@ def main():
     w2_bytes = K * V * H * itemsize
     z_bytes = B * K * H * 4
     algo_bytes = w2_bytes + z_bytes + B * K * topk * 8
-    vt_us = kern_us["vocab_proj_topk"]
+    # (the GEMV over row-major W2, or the MFMA product over packed W2 from 4
+    # sequences on; the stored counter traffic is the GEMV's)
+    vt_name = "vocab_proj_topk" if w2_layout == M.ROW_MAJOR else "vocab_proj_topk_mfma"
+    vt_us = kern_us[vt_name]
     achieved = algo_bytes / (vt_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": vocab_traffic_bytes(), "kernel": "vocab_proj_topk",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": vocab_traffic_bytes() if w2_layout == M.ROW_MAJOR else None, "kernel": vt_name,
                 "bytes_per_launch": algo_bytes, "avg_us": round(vt_us, 2)}
 
     t_verify_us = st["tree_attention"]

@@ -87,13 +87,23 @@ medusa_status medusa_resid_silu(const void* h, const void* w1, const void* b1,
  * Step a2 -- vocabulary projection and per-head top-k (heads page: projection
  * to the vocabulary; tree section: the heads' top guesses).
  *   z        [B][K][H] float32: head k's input for sequence b
- *   w2       [K][V][H] (dt): head k's projection (no bias)
+ *   w2       head k's projection (no bias), laid out as w2_layout says:
+ *            MEDUSA_ROW_MAJOR: [K][V][H] (dt), streamed by a vector-ALU GEMV
+ *            (every weight byte meets B <= 8 inputs);
+ *            MEDUSA_PACKED (bf16 only, H a multiple of 256): K packed
+ *            matrices of V rows x H columns back to back, each
+ *            medusa_packed_size(V, H) bytes (medusa_pack_rows of head k at
+ *            byte offset k * medusa_packed_size(V, H)), streamed through
+ *            MFMA with z entering as a bf16 head plus a bf16 remainder (17
+ *            significant bits); the faster choice from B = 4 on.
  *   logits   [B][K][V] float32, optional (NULL: not written)
- *   topk_idx [B][K][topk] int32, topk_val [B][K][topk] float32 (outputs)
+ *   topk_idx [B][K][topk] int32, topk_val [B][K][topk] float32 (outputs);
+ *            ties keep the lower index.
  * Limits: 1 <= topk <= min(16, V), 1 <= B <= 8, H % 8 == 0, H <= 8192.
  * ------------------------------------------------------------------------- */
-size_t medusa_vocab_topk_workspace_size(int B, int H, int V, int K, int topk, medusa_dtype dt);
-medusa_status medusa_vocab_topk(const float* z, const void* w2,
+size_t medusa_vocab_topk_workspace_size(int B, int H, int V, int K, int topk, medusa_dtype dt,
+                                        medusa_layout w2_layout);
+medusa_status medusa_vocab_topk(const float* z, const void* w2, medusa_layout w2_layout,
                                 int B, int H, int V, int K, int topk, medusa_dtype dt,
                                 float* logits, int32_t* topk_idx, float* topk_val,
                                 void* ws, size_t ws_bytes, void* stream);
@@ -104,8 +114,10 @@ medusa_status medusa_vocab_topk(const float* z, const void* w2,
  *   the base model's lm_head with K = 1).  Workspace holds z and the top-k
  *   partials.  Other arguments as above.
  * ------------------------------------------------------------------------- */
-size_t medusa_heads_workspace_size(int B, int H, int V, int K, int topk, medusa_dtype dt);
+size_t medusa_heads_workspace_size(int B, int H, int V, int K, int topk, medusa_dtype dt,
+                                   medusa_layout w2_layout);
 medusa_status medusa_heads_forward(const void* h, const void* w1, const void* b1, const void* w2,
+                                   medusa_layout w2_layout,
                                    int B, int H, int V, int K, int topk, medusa_dtype dt,
                                    float* logits, int32_t* topk_idx, float* topk_val,
                                    void* ws, size_t ws_bytes, void* stream);

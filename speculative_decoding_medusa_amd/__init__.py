@@ -31,10 +31,10 @@ _SIGS = {
     "medusa_last_error": ([], ctypes.c_char_p),
     "medusa_version": ([], ctypes.c_char_p),
     "medusa_resid_silu": ([_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp], _i32),
-    "medusa_vocab_topk_workspace_size": ([_i32, _i32, _i32, _i32, _i32, _i32], _sz),
-    "medusa_vocab_topk": ([_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
-    "medusa_heads_workspace_size": ([_i32, _i32, _i32, _i32, _i32, _i32], _sz),
-    "medusa_heads_forward": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz,
+    "medusa_vocab_topk_workspace_size": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32], _sz),
+    "medusa_vocab_topk": ([_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
+    "medusa_heads_workspace_size": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32], _sz),
+    "medusa_heads_forward": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz,
                               _vp], _i32),
     "medusa_tree_create": ([_vp, _vp, _i32, _i32, _i32, ctypes.POINTER(_vp)], _i32),
     "medusa_tree_destroy": ([_vp], None),
@@ -118,35 +118,45 @@ def medusa_resid_silu(h, w1, b1, z, stream=None):
     return z
 
 
-def vocab_topk_workspace_size(B, H, V, K, topk, dt):
-    return _lib.medusa_vocab_topk_workspace_size(B, H, V, K, topk, dt)
+def vocab_topk_workspace_size(B, H, V, K, topk, dt, layout=ROW_MAJOR):
+    return _lib.medusa_vocab_topk_workspace_size(B, H, V, K, topk, dt, layout)
+
+
+def _w2_args(w2):
+    """(layout, dtype) of a head projection: a [K][V][H] tensor or the
+    packed heads of pack_heads."""
+    if isinstance(w2, Packed):
+        return PACKED, BF16
+    return ROW_MAJOR, _dt(w2)
 
 
 def medusa_vocab_topk(z, w2, topk, topk_idx, topk_val, logits=None, ws=None, stream=None):
+    """w2: [K][V][H] (row-major) or the result of pack_heads (packed, MFMA)."""
     K, V, H = w2.shape
     B = z.shape[0]
-    dt = _dt(w2)
-    need = vocab_topk_workspace_size(B, H, V, K, topk, dt)
+    layout, dt = _w2_args(w2)
+    need = vocab_topk_workspace_size(B, H, V, K, topk, dt, layout)
     ws = _ws(need, z.device, ws)
-    _check("medusa_vocab_topk", _lib.medusa_vocab_topk(_p(z), _p(w2), B, H, V, K, topk, dt, _p(logits),
+    _check("medusa_vocab_topk", _lib.medusa_vocab_topk(_p(z), _p(w2), layout, B, H, V, K, topk, dt, _p(logits),
                                                        _p(topk_idx), _p(topk_val), _p(ws),
                                                        ws.numel() * ws.element_size(), _stream(stream)))
     return topk_idx, topk_val
 
 
-def heads_workspace_size(B, H, V, K, topk, dt):
-    return _lib.medusa_heads_workspace_size(B, H, V, K, topk, dt)
+def heads_workspace_size(B, H, V, K, topk, dt, layout=ROW_MAJOR):
+    return _lib.medusa_heads_workspace_size(B, H, V, K, topk, dt, layout)
 
 
 def medusa_heads_forward(h, w1, b1, w2, topk, topk_idx, topk_val, logits=None, ws=None, stream=None):
+    """w2: [K][V][H] (row-major) or the result of pack_heads (packed, MFMA)."""
     K, V, H = w2.shape
     B = h.shape[0]
-    dt = _dt(w2)
-    need = heads_workspace_size(B, H, V, K, topk, dt)
+    layout, dt = _w2_args(w2)
+    need = heads_workspace_size(B, H, V, K, topk, dt, layout)
     ws = _ws(need, h.device, ws)
     _check("medusa_heads_forward", _lib.medusa_heads_forward(
-        _p(h), _p(w1), _p(b1), _p(w2), B, H, V, K, topk, dt, _p(logits), _p(topk_idx), _p(topk_val), _p(ws),
-        ws.numel() * ws.element_size(), _stream(stream)))
+        _p(h), _p(w1), _p(b1), _p(w2), layout, B, H, V, K, topk, dt, _p(logits), _p(topk_idx), _p(topk_val),
+        _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return topk_idx, topk_val
 
 
@@ -220,14 +230,15 @@ def tree_attention_verify(q, k_tree, v_tree, k_cache, v_cache, cache_len, max_ca
 
 class Packed:
     """A bf16 matrix [rows][cols] in the packed fragment order of
-    medusa_pack_rows; `data` is the device buffer (bf16, padded rows)."""
+    medusa_pack_rows; `data` is the device buffer (bf16, padded rows).  With
+    heads = K, K such matrices back to back (shape (K, rows, cols))."""
 
-    def __init__(self, data, rows: int, cols: int):
-        self.data, self.rows, self.cols = data, rows, cols
+    def __init__(self, data, rows: int, cols: int, heads: int = 0):
+        self.data, self.rows, self.cols, self.heads = data, rows, cols, heads
 
     @property
     def shape(self):
-        return (self.rows, self.cols)
+        return (self.heads, self.rows, self.cols) if self.heads else (self.rows, self.cols)
 
     def data_ptr(self):
         return self.data.data_ptr()
@@ -263,6 +274,22 @@ def pack(*mats, interleave: bool = False, stream=None) -> Packed:
             medusa_pack_rows(m, dst, r0, 1, stream)
             r0 += m.shape[0]
     return dst
+
+
+def pack_heads(w2, stream=None) -> Packed:
+    """Pack the heads' projections w2 [K][V][H] (bf16) for medusa_vocab_topk /
+    medusa_heads_forward: head k's packed matrix at byte offset
+    k * medusa_packed_size(V, H)."""
+    K, V, H = w2.shape
+    assert w2.dtype == torch.bfloat16 and w2.is_contiguous()
+    one = packed_size(V, H)
+    if one == 0:
+        raise MedusaError("medusa_packed_size", EUNSUPPORTED)
+    data = torch.empty(K * one // 2, dtype=torch.bfloat16, device=w2.device)
+    for k in range(K):
+        dst = Packed(data[k * one // 2:(k + 1) * one // 2], V, H)
+        medusa_pack_rows(w2[k], dst, 0, 1, stream)
+    return Packed(data, V, H, heads=K)
 
 
 # ---------------------------------------------------------------------------

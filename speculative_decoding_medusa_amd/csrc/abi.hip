@@ -23,6 +23,10 @@ void launch_vocab_topk(const float* z, const void* w2, int B, int H, int V, int 
                        float* logits, int32_t* topk_idx, float* topk_val, float* cv, int* ci, hipStream_t s);
 int vocab_topk_groups(int B, int V, int K);
 size_t vocab_topk_lds_bytes(int B, int H, int V, int K);
+int vocab_topk_packed_kc();
+size_t vocab_topk_packed_ws_bytes(int B, int H, int V, int K, int topk);
+void launch_vocab_topk_packed(const float* z, const void* w2p, int B, int H, int V, int K, int topk, float* logits,
+                              int32_t* topk_idx, float* topk_val, void* ws, hipStream_t s);
 size_t resid_silu_lds_bytes(int B, int H);
 void launch_build_tree(const TreeDev& t, const int32_t* topk_idx, int K, int topk, const int32_t* root_tok,
                        const int32_t* cache_len, int B, int32_t* node_tok, int32_t* node_pos, uint64_t* anc_mask,
@@ -186,9 +190,11 @@ medusa_status medusa_resid_silu(const void* h, const void* w1, const void* b1, i
     });
 }
 
-size_t medusa_vocab_topk_workspace_size(int B, int H, int V, int K, int topk, medusa_dtype dt) {
-    (void)H; (void)dt;
-    if (B < 1 || V < 1 || K < 1 || topk < 1) return 0;
+size_t medusa_vocab_topk_workspace_size(int B, int H, int V, int K, int topk, medusa_dtype dt,
+                                        medusa_layout w2_layout) {
+    (void)dt;
+    if (B < 1 || H < 1 || V < 1 || K < 1 || topk < 1) return 0;
+    if (w2_layout == MEDUSA_PACKED) return vocab_topk_packed_ws_bytes(B, H, V, K, topk);
     const size_t G = (size_t)vocab_topk_groups(B, V, K);
     return align256((size_t)B * K * G * topk * 4) * 2;
 }
@@ -200,33 +206,49 @@ static void carve_vocab_ws(void* ws, int B, int V, int K, int topk, float** cv, 
     *ci = (int*)((char*)ws + one);
 }
 
-static void check_vocab(int B, int H, int V, int K, int topk, medusa_dtype dt) {
+static void check_vocab(int B, int H, int V, int K, int topk, medusa_dtype dt, medusa_layout w2_layout) {
     check_heads_shape(B, H, K, dt);
     REQUIRE(V >= 1, "V must be positive");
     REQUIRE(topk >= 1 && topk <= V, "topk=%d must be in [1, V]", topk);
     SUPPORT(topk <= MEDUSA_MAX_TOPK, "topk=%d exceeds %d", topk, MEDUSA_MAX_TOPK);
-    SUPPORT(vocab_topk_lds_bytes(B, H, V, K) <= 160 * 1024, "B*H too large for the LDS-staged right-hand sides");
+    REQUIRE(w2_layout == MEDUSA_ROW_MAJOR || w2_layout == MEDUSA_PACKED, "w2_layout must be ROW_MAJOR or PACKED");
+    if (w2_layout == MEDUSA_PACKED) {
+        SUPPORT(dt == MEDUSA_BF16, "a packed w2 must be bf16");
+        SUPPORT(H % vocab_topk_packed_kc() == 0, "packed w2: H=%d must be a multiple of %d", H,
+                vocab_topk_packed_kc());
+    } else {
+        SUPPORT(vocab_topk_lds_bytes(B, H, V, K) <= 160 * 1024, "B*H too large for the LDS-staged right-hand sides");
+    }
 }
 
-medusa_status medusa_vocab_topk(const float* z, const void* w2, int B, int H, int V, int K, int topk,
-                                medusa_dtype dt, float* logits, int32_t* topk_idx, float* topk_val, void* ws,
-                                size_t ws_bytes, void* stream) {
+static void run_vocab_topk(const float* z, const void* w2, medusa_layout w2_layout, int B, int H, int V, int K,
+                           int topk, medusa_dtype dt, float* logits, int32_t* topk_idx, float* topk_val, void* ws,
+                           hipStream_t s) {
+    if (w2_layout == MEDUSA_PACKED) {
+        launch_vocab_topk_packed(z, w2, B, H, V, K, topk, logits, topk_idx, topk_val, ws, s);
+        return;
+    }
+    float* cv;
+    int* ci;
+    carve_vocab_ws(ws, B, V, K, topk, &cv, &ci);
+    launch_vocab_topk(z, w2, B, H, V, K, topk, dt == MEDUSA_BF16, logits, topk_idx, topk_val, cv, ci, s);
+}
+
+medusa_status medusa_vocab_topk(const float* z, const void* w2, medusa_layout w2_layout, int B, int H, int V, int K,
+                                int topk, medusa_dtype dt, float* logits, int32_t* topk_idx, float* topk_val,
+                                void* ws, size_t ws_bytes, void* stream) {
     return guarded("medusa_vocab_topk", [&] {
-        check_vocab(B, H, V, K, topk, dt);
+        check_vocab(B, H, V, K, topk, dt, w2_layout);
         REQUIRE(z && w2 && topk_idx && topk_val && ws, "null pointer argument");
-        const size_t need = medusa_vocab_topk_workspace_size(B, H, V, K, topk, dt);
+        const size_t need = medusa_vocab_topk_workspace_size(B, H, V, K, topk, dt, w2_layout);
         REQUIRE(ws_bytes >= need, "workspace too small: %zu < %zu", ws_bytes, need);
-        float* cv;
-        int* ci;
-        carve_vocab_ws(ws, B, V, K, topk, &cv, &ci);
-        launch_vocab_topk(z, w2, B, H, V, K, topk, dt == MEDUSA_BF16, logits, topk_idx, topk_val, cv, ci,
-                          (hipStream_t)stream);
+        run_vocab_topk(z, w2, w2_layout, B, H, V, K, topk, dt, logits, topk_idx, topk_val, ws, (hipStream_t)stream);
     });
 }
 
-size_t medusa_heads_workspace_size(int B, int H, int V, int K, int topk, medusa_dtype dt) {
+size_t medusa_heads_workspace_size(int B, int H, int V, int K, int topk, medusa_dtype dt, medusa_layout w2_layout) {
     if (B < 1 || H < 1 || V < 1 || K < 1 || topk < 1) return 0;
-    return align256((size_t)B * K * H * 4) + medusa_vocab_topk_workspace_size(B, H, V, K, topk, dt);
+    return align256((size_t)B * K * H * 4) + medusa_vocab_topk_workspace_size(B, H, V, K, topk, dt, w2_layout);
 }
 
 // z = h for every head (lm_head mode)
@@ -238,14 +260,15 @@ __global__ void broadcast_h_kernel(const void* h, int B, int H, int K, int bf16,
     }
 }
 
-medusa_status medusa_heads_forward(const void* h, const void* w1, const void* b1, const void* w2, int B, int H,
-                                   int V, int K, int topk, medusa_dtype dt, float* logits, int32_t* topk_idx,
-                                   float* topk_val, void* ws, size_t ws_bytes, void* stream) {
+medusa_status medusa_heads_forward(const void* h, const void* w1, const void* b1, const void* w2,
+                                   medusa_layout w2_layout, int B, int H, int V, int K, int topk, medusa_dtype dt,
+                                   float* logits, int32_t* topk_idx, float* topk_val, void* ws, size_t ws_bytes,
+                                   void* stream) {
     return guarded("medusa_heads_forward", [&] {
-        check_vocab(B, H, V, K, topk, dt);
+        check_vocab(B, H, V, K, topk, dt, w2_layout);
         REQUIRE(h && w2 && topk_idx && topk_val && ws, "null pointer argument");
         REQUIRE((w1 == nullptr) == (b1 == nullptr), "w1 and b1 must both be given or both be NULL");
-        const size_t need = medusa_heads_workspace_size(B, H, V, K, topk, dt);
+        const size_t need = medusa_heads_workspace_size(B, H, V, K, topk, dt, w2_layout);
         REQUIRE(ws_bytes >= need, "workspace too small: %zu < %zu", ws_bytes, need);
         float* z = (float*)ws;
         void* vws = (char*)ws + align256((size_t)B * K * H * 4);
@@ -255,10 +278,7 @@ medusa_status medusa_heads_forward(const void* h, const void* w1, const void* b1
         else
             MEDUSA_LAUNCH("broadcast_h", broadcast_h_kernel, dim3(64), dim3(256), 0, s, h, B, H, K,
                           dt == MEDUSA_BF16 ? 1 : 0, z);
-        float* cv;
-        int* ci;
-        carve_vocab_ws(vws, B, V, K, topk, &cv, &ci);
-        launch_vocab_topk(z, w2, B, H, V, K, topk, dt == MEDUSA_BF16, logits, topk_idx, topk_val, cv, ci, s);
+        run_vocab_topk(z, w2, w2_layout, B, H, V, K, topk, dt, logits, topk_idx, topk_val, vws, s);
     });
 }
 

@@ -107,6 +107,28 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
     }
 }
 
+// Sorted register list of the best TK (value, index) pairs, best first.
+template <int TK>
+__device__ __forceinline__ void sorted_insert(float (&lv)[TK], int (&li)[TK], float v, int i) {
+    if (!better(v, i, lv[TK - 1], li[TK - 1])) return;
+    lv[TK - 1] = v;
+    li[TK - 1] = i;
+#pragma unroll
+    for (int t = TK - 1; t > 0; --t) {
+        if (better(lv[t], li[t], lv[t - 1], li[t - 1])) {
+            const float tv = lv[t]; lv[t] = lv[t - 1]; lv[t - 1] = tv;
+            const int ti = li[t]; li[t] = li[t - 1]; li[t - 1] = ti;
+        }
+    }
+}
+template <int TK>
+__device__ __forceinline__ void sorted_pop(float (&lv)[TK], int (&li)[TK]) {
+#pragma unroll
+    for (int u = 0; u < TK - 1; ++u) { lv[u] = lv[u + 1]; li[u] = li[u + 1]; }
+    lv[TK - 1] = -INFINITY;
+    li[TK - 1] = 0x7FFFFFFF;
+}
+
 }  // namespace medusa
 
 // ---------------------------------------------------------------------------

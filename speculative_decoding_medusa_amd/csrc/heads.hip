@@ -20,6 +20,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "skinny_mfma.hpp"
 
 namespace medusa {
 
@@ -27,28 +28,6 @@ enum { EPI_SILU = 0, EPI_TOPK = 1 };
 
 // Upper bound of the rows one workgroup owns (sizes the row-value LDS array).
 constexpr int GEMV_MAX_ROWS_PER_WG = 512;
-
-// Sorted register list of the best TK (value, index) pairs, best first.
-template <int TK>
-__device__ __forceinline__ void sorted_insert(float (&lv)[TK], int (&li)[TK], float v, int i) {
-    if (!better(v, i, lv[TK - 1], li[TK - 1])) return;
-    lv[TK - 1] = v;
-    li[TK - 1] = i;
-#pragma unroll
-    for (int t = TK - 1; t > 0; --t) {
-        if (better(lv[t], li[t], lv[t - 1], li[t - 1])) {
-            const float tv = lv[t]; lv[t] = lv[t - 1]; lv[t - 1] = tv;
-            const int ti = li[t]; li[t] = li[t - 1]; li[t - 1] = ti;
-        }
-    }
-}
-template <int TK>
-__device__ __forceinline__ void sorted_pop(float (&lv)[TK], int (&li)[TK]) {
-#pragma unroll
-    for (int u = 0; u < TK - 1; ++u) { lv[u] = lv[u + 1]; li[u] = li[u + 1]; }
-    lv[TK - 1] = -INFINITY;
-    li[TK - 1] = 0x7FFFFFFF;
-}
 
 template <typename WT, int NB, int CPL, int R, int EPI, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void gemv_rows_kernel(
@@ -427,6 +406,57 @@ void launch_vocab_topk_named(const float* z, const void* w2, int B, int H, int V
     if (sh.R == 2) MEDUSA_TOPK_GO(2, 8, 1, 2); else if (sh.R == 4) MEDUSA_TOPK_GO(4, 4, 4); else MEDUSA_TOPK_GO(8, 4, 8);
 #undef MEDUSA_TOPK_GO
     launch_topk_merge(cv, ci, B * K, pl.G * topk, topk, topk_idx, topk_val, s, merge_name);
+}
+
+// ---------------------------------------------------------------------------
+// Vocabulary projection over packed W2 on MFMA (several sequences): every
+// weight byte feeds 2 B scores, so the vector-ALU GEMV above is bound by its
+// FMAs and by its LDS reads of z from B = 4 on; the MFMA product streams the
+// packed weights at HBM speed.  z enters as a bf16 head and a bf16 remainder
+// (17 significant bits, against the fp32 z: the scores stay within a few
+// units of 2^-17 of the fp32 ones): node rows 0..7 of matrix k are the heads
+// of sequences 0..7, rows 8..15 the remainders (absent sequences zero), and
+// the epilogue adds the two columns of a sequence.
+// ---------------------------------------------------------------------------
+constexpr int VT_WAVES = 4;  // waves per workgroup: 64 weight rows
+
+// z [B][K][H] fp32 -> zs [K][16][H] bf16
+__global__ __launch_bounds__(256) void split_rows_kernel(const float* __restrict__ z, int B, int K, int H,
+                                                         bf16_t* __restrict__ zs) {
+    const size_t n = (size_t)K * 8 * H;  // (k, b < 8, j)
+    for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
+        const int j = (int)(e % H);
+        const int b = (int)((e / H) % 8);
+        const int k = (int)(e / ((size_t)8 * H));
+        const float x = b < B ? z[((size_t)b * K + k) * H + j] : 0.f;
+        const bf16_t hi = f32_to_bf16(x);
+        zs[((size_t)k * 16 + b) * H + j] = hi;
+        zs[((size_t)k * 16 + 8 + b) * H + j] = f32_to_bf16(x - bf16_to_f32(hi));
+    }
+}
+
+int vocab_topk_packed_groups(int V) { return (V + 16 * VT_WAVES - 1) / (16 * VT_WAVES); }
+int vocab_topk_packed_kc() { return LmhCfg<1, VT_WAVES>::KC; }
+
+static size_t a256h(size_t n) { return (n + 255) / 256 * 256; }
+size_t vocab_topk_packed_ws_bytes(int B, int H, int V, int K, int topk) {
+    const size_t cand = (size_t)B * K * vocab_topk_packed_groups(V) * topk;
+    return a256h((size_t)K * 16 * H * 2) + 2 * a256h(cand * 4);
+}
+
+void launch_vocab_topk_packed(const float* z, const void* w2p, int B, int H, int V, int K, int topk, float* logits,
+                              int32_t* topk_idx, float* topk_val, void* ws, hipStream_t s) {
+    const int G = vocab_topk_packed_groups(V);
+    const size_t cand = (size_t)B * K * G * topk;
+    bf16_t* zs = (bf16_t*)ws;
+    float* cv = (float*)((char*)ws + a256h((size_t)K * 16 * H * 2));
+    int* ci = (int*)((char*)cv + a256h(cand * 4));
+    MEDUSA_LAUNCH("split_rows", split_rows_kernel, dim3(256), dim3(256), 0, s, z, B, K, H, zs);
+    const long long w_stride = (long long)((V + PACK_ROWS - 1) / PACK_ROWS) * PACK_ROWS * H;
+    MEDUSA_LAUNCH("vocab_proj_topk_mfma", (skinny_mfma_kernel<1, SKINNY_TOPK, VT_WAVES>), dim3(G, K),
+                  dim3(VT_WAVES * 64), 0, s, zs, (const bf16_t*)w2p, 16, H, V, H / LmhCfg<1, VT_WAVES>::KC, cv, ci,
+                  logits, nullptr, topk, B, (long long)16 * H, w_stride);
+    launch_topk_merge(cv, ci, B * K, G * topk, topk, topk_idx, topk_val, s, "topk_merge");
 }
 
 void launch_vocab_topk(const float* z, const void* w2, int B, int H, int V, int K, int topk, bool bf16,

@@ -1,8 +1,9 @@
 // Skinny bf16 matrix products on MFMA: R <= 256 node rows (the tree tokens)
 // times V weight rows of length K, the weights streamed from HBM once.  Used
 // for the base model's lm_head over the tree nodes (argmax fused into the
-// epilogue) and for the decoder layer's projections (split over the
-// contraction, fp32 partial sums per split).
+// epilogue), for the decoder layer's projections (split over the
+// contraction, fp32 partial sums per split), and for the heads' vocabulary
+// projection of up to 8 sequences (per-head top-k fused into the epilogue).
 //
 // Weights are read in the packed fragment order (pack.hip): for every block
 // of 16 rows and every 32-wide step of the contraction, the 16 x 32 tile is
@@ -25,8 +26,11 @@ namespace medusa {
 
 // ARGMAX: per-workgroup argmax candidates (base greedy);  PARTIAL: fp32 sums
 // per contraction split;  SWIGLU (unsplit gate|up with gate and up rows
-// interleaved in 16-row blocks): bf16(SiLU(gate) * up)
-enum { SKINNY_ARGMAX = 0, SKINNY_PARTIAL = 1, SKINNY_SWIGLU = 2 };
+// interleaved in 16-row blocks): bf16(SiLU(gate) * up);  TOPK (16 node rows:
+// rows 0..7 the bf16 heads of up to 8 sequences' inputs, rows 8..15 their
+// bf16 remainders; one weight matrix per grid row y): per-workgroup top-k
+// candidates of each sequence
+enum { SKINNY_ARGMAX = 0, SKINNY_PARTIAL = 1, SKINNY_SWIGLU = 2, SKINNY_TOPK = 3 };
 
 // packed fragment geometry
 constexpr int PACK_ROWS = 16;                      // rows per fragment
@@ -43,15 +47,16 @@ constexpr int LMH_ROWS = LMH_WAVES * PACK_ROWS;    // weight rows per workgroup
 template <int NBLK, int WAVES = LMH_WAVES>
 struct LmhCfg {
     static constexpr int NODES = NBLK * 16;
+    static constexpr int NT = WAVES * 64;
     // k per chunk and register-ring depth (measured on 64 x 4096 x 32000:
     // 64-wide chunks four deep beat 128 three deep and 256 two deep); 256
-    // node rows use 32-wide chunks so the node ring stays small
-    static constexpr int KC = NBLK <= 8 ? 64 : 32;
+    // node rows use 32-wide chunks so the node ring stays small; 16 node rows
+    // use chunks wide enough that every thread stages one 16-byte piece
+    static constexpr int KC = NBLK == 1 ? NT / 2 : NBLK <= 8 ? 64 : 32;
     static constexpr int KS = KC / PACK_K;             // MFMA k-steps per chunk
     static constexpr int LDW = KC + 8;                 // padded LDS row (bf16): conflict-free B reads
-    static constexpr int NT = WAVES * 64;
     static constexpr int NPT = NODES * KC / 8 / NT;    // 16-byte node pieces per thread per chunk
-    static constexpr int D = NBLK <= 4 ? 4 : 3;        // chunks in flight per register ring
+    static constexpr int D = NBLK == 1 && WAVES > 4 ? 3 : NBLK <= 4 ? 4 : 3;  // chunks in flight per ring
     static_assert(NPT * NT * 8 == NODES * KC, "node stage must split evenly over the threads");
 };
 
@@ -69,10 +74,15 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
                                                           float* __restrict__ cand_val,
                                                           int* __restrict__ cand_idx,  // ARGMAX: [R][G]
                                                           float* __restrict__ out,
-                                                          const float* __restrict__ row_scale = nullptr) {
+                                                          const float* __restrict__ row_scale = nullptr,
+                                                          int topk = 0, int nseq = 0, long long n_stride = 0,
+                                                          long long w_stride = 0) {
     // ARGMAX: out = optional logits [R][V], each node row's scores times
     // row_scale[node] when given (a positive factor: the argmax is that of the
-    // unscaled scores);  PARTIAL: out = [splits][R][V];  SWIGLU: out = bf16 [R][V / 2]
+    // unscaled scores);  PARTIAL: out = [splits][R][V];  SWIGLU: out = bf16 [R][V / 2];
+    // TOPK: grid row y is matrix y (node rows at n + y n_stride, weights at
+    // Wp + y w_stride); out = optional logits [nseq][gridDim.y][V];
+    // candidates [nseq][gridDim.y][G][topk]
     using C = LmhCfg<NBLK, WAVES>;
     constexpr int D = C::D;
     constexpr int NT = C::NT;
@@ -80,11 +90,17 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
     __shared__ float red_v[WAVES][EPI == SKINNY_ARGMAX ? C::NODES : 1];
     __shared__ int red_i[WAVES][EPI == SKINNY_ARGMAX ? C::NODES : 1];
     __shared__ f32x4 xup[EPI == SKINNY_SWIGLU ? WAVES / 2 : 1][EPI == SKINNY_SWIGLU ? NBLK : 1][64];
+    __shared__ float tkv[EPI == SKINNY_TOPK ? WAVES * PACK_ROWS : 1][8];  // TOPK: the workgroup's rows x sequences
+    static_assert(EPI != SKINNY_TOPK || NBLK == 1, "top-k epilogue: 16 node rows");
+    if (EPI == SKINNY_TOPK) {
+        n += (size_t)blockIdx.y * n_stride;
+        Wp += (size_t)blockIdx.y * w_stride;
+    }
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int G = gridDim.x;
-    const int node0 = blockIdx.y * C::NODES;
+    const int node0 = EPI == SKINNY_TOPK ? 0 : blockIdx.y * C::NODES;
     const int rb = blockIdx.x * WAVES + wave;         // this wave's 16-row block
     const int vw = rb * PACK_ROWS;                    // its first weight row
     const int lr = lane & 15, lk = lane >> 4;         // row / k-group within a 16x16x32 tile
@@ -185,6 +201,43 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
 #pragma unroll
             for (int r = 0; r < 4; ++r) y[r] = g[r] / (1.f + __expf(-g[r])) * u[r];
             *(uint2*)(a + (size_t)node * F + c0) = (uint2){pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+        }
+        return;
+    }
+    if (EPI == SKINNY_TOPK) {
+        // lane (lr, lk) holds rows vw + 4 lk + r of node column lr; sequence
+        // b's score adds its remainder column b + 8, held by lane lr ^ 8
+        const int nm = gridDim.y, m = blockIdx.y;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float x = acc[0][r] + __shfl_xor(acc[0][r], 8, 64);
+            const int v = vw + lk * 4 + r;
+            if (lr < 8) {
+                tkv[wave * PACK_ROWS + lk * 4 + r][lr] = v < V ? x : -INFINITY;
+                if (out != nullptr && lr < nseq && v < V) out[((size_t)lr * nm + m) * V + v] = x;
+            }
+        }
+        __syncthreads();
+        // each wave takes sequences wave, wave + WAVES, ...: every lane keeps a
+        // sorted list of the rows it scans, then the wave extracts the winners
+        constexpr int ROWS = WAVES * PACK_ROWS;
+        for (int b = wave; b < nseq; b += WAVES) {
+            float lv[MEDUSA_MAX_TOPK_DEV];
+            int li[MEDUSA_MAX_TOPK_DEV];
+#pragma unroll
+            for (int t = 0; t < MEDUSA_MAX_TOPK_DEV; ++t) { lv[t] = -INFINITY; li[t] = 0x7FFFFFFF; }
+            for (int r = lane; r < ROWS; r += 64) {
+                const int v = blockIdx.x * ROWS + r;
+                if (v < V) sorted_insert<MEDUSA_MAX_TOPK_DEV>(lv, li, tkv[r][b], v);
+            }
+            const size_t base = (((size_t)b * nm + m) * G + blockIdx.x) * topk;
+            for (int t = 0; t < topk; ++t) {
+                float bv = lv[0];
+                int bi = li[0];
+                wave_argmax(bv, bi);
+                if (lane == 0) { cand_val[base + t] = bv; cand_idx[base + t] = bi; }
+                if (lv[0] == bv && li[0] == bi) sorted_pop<MEDUSA_MAX_TOPK_DEV>(lv, li);
+            }
         }
         return;
     }

@@ -170,6 +170,15 @@ def lm_head_arg(M, lm_head):
     return lm_head, M.ROW_MAJOR
 
 
+def w2_arg(M, W2, B):
+    """The heads' projection as a step passes it: packed for the MFMA product
+    from 4 sequences on (bf16, H % 256 == 0), else the row-major tensor."""
+    import torch
+    if B >= 4 and W2.dtype == torch.bfloat16 and W2.shape[2] % 256 == 0:
+        return M.pack_heads(W2)
+    return W2
+
+
 def run_step_gpu(M, cfg, heads, att, root):
     """Upload the workload, run resid_silu -> vocab_topk -> build_tree ->
     tree_attention_verify -> base_greedy -> accept (with compaction) once and
@@ -183,7 +192,10 @@ def run_step_gpu(M, cfg, heads, att, root):
     z = torch.empty(B, K, H, device="cuda")
     ti = torch.empty(B, K, topk, dtype=torch.int32, device="cuda")
     tv = torch.empty(B, K, topk, device="cuda")
-    ws_v = torch.empty(M.vocab_topk_workspace_size(B, H, V, K, topk, wdt), dtype=torch.uint8, device="cuda")
+    w2 = w2_arg(M, d["W2"], B)
+    w2_layout = M.PACKED if isinstance(w2, M.Packed) else M.ROW_MAJOR
+    ws_v = torch.empty(M.vocab_topk_workspace_size(B, H, V, K, topk, wdt, w2_layout), dtype=torch.uint8,
+                       device="cuda")
     tok = torch.empty(B, N, dtype=torch.int32, device="cuda")
     pos = torch.empty_like(tok)
     o = torch.empty_like(d["q"])
@@ -198,7 +210,7 @@ def run_step_gpu(M, cfg, heads, att, root):
     ot = torch.empty_like(an)
     ncl = torch.empty(B, dtype=torch.int32, device="cuda")
     M.medusa_resid_silu(d["h"], d["W1"], d["b1"], z)
-    M.medusa_vocab_topk(z, d["W2"], topk, ti, tv, ws=ws_v)
+    M.medusa_vocab_topk(z, w2, topk, ti, tv, ws=ws_v)
     M.medusa_build_tree(tree, ti, dev(root), d["cache_len"], tok, pos)
     M.tree_attention_verify(d["q"], d["k_tree"], d["v_tree"], d["k_cache"], d["v_cache"], d["cache_len"], maxP, tree, o,
                             ws=ws_a)
@@ -210,7 +222,7 @@ def run_step_gpu(M, cfg, heads, att, root):
                node_pos=pos.cpu().numpy(), o=host_f64(o), greedy=g.view(B, N).cpu().numpy(),
                accept_len=al.cpu().numpy(), accept_nodes=an.cpu().numpy(), out_tokens=ot.cpu().numpy(),
                new_cache_len=ncl.cpu().numpy(), k_cache=d["k_cache"], v_cache=d["v_cache"])
-    del d, lm
+    del d, lm, w2
     return out
 
 

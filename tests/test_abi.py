@@ -74,33 +74,43 @@ def test_tree_too_large_is_unsupported(M):
 
 def test_heads_argument_errors(M):
     L = M._lib
-    st = L.medusa_heads_forward(None, None, None, None, 1, 4096, 32000, 5, 4, M.BF16, None, None, None, None, 0, None)
+    st = L.medusa_heads_forward(None, None, None, None, M.ROW_MAJOR, 1, 4096, 32000, 5, 4, M.BF16, None, None, None, None, 0, None)
     assert st == M.EINVAL and "null" in L.medusa_last_error().decode()
     d = ctypes.c_void_p(16)  # never dereferenced: validation fails first
-    st = L.medusa_vocab_topk(d, d, 1, 4096, 32000, 5, 0, M.BF16, None, d, d, d, 1 << 30, None)
+    st = L.medusa_vocab_topk(d, d, M.ROW_MAJOR, 1, 4096, 32000, 5, 0, M.BF16, None, d, d, d, 1 << 30, None)
     assert st == M.EINVAL and "topk" in L.medusa_last_error().decode()
-    st = L.medusa_vocab_topk(d, d, 1, 4096, 32000, 5, 17, M.BF16, None, d, d, d, 1 << 30, None)
+    st = L.medusa_vocab_topk(d, d, M.ROW_MAJOR, 1, 4096, 32000, 5, 17, M.BF16, None, d, d, d, 1 << 30, None)
     assert st == M.EUNSUPPORTED
-    st = L.medusa_vocab_topk(d, d, 9, 4096, 32000, 5, 4, M.BF16, None, d, d, d, 1 << 30, None)
+    st = L.medusa_vocab_topk(d, d, M.ROW_MAJOR, 9, 4096, 32000, 5, 4, M.BF16, None, d, d, d, 1 << 30, None)
     assert st == M.EUNSUPPORTED
-    st = L.medusa_vocab_topk(d, d, 1, 4100, 32000, 5, 4, M.BF16, None, d, d, d, 1 << 30, None)
+    st = L.medusa_vocab_topk(d, d, M.ROW_MAJOR, 1, 4100, 32000, 5, 4, M.BF16, None, d, d, d, 1 << 30, None)
     assert st == M.EUNSUPPORTED
-    st = L.medusa_vocab_topk(d, d, 1, 4096, 32000, 5, 4, M.BF16, None, d, d, d, 10, None)
+    st = L.medusa_vocab_topk(d, d, M.ROW_MAJOR, 1, 4096, 32000, 5, 4, M.BF16, None, d, d, d, 10, None)
     assert st == M.EINVAL and "workspace" in L.medusa_last_error().decode()
-    st = L.medusa_heads_forward(d, d, None, d, 1, 4096, 32000, 5, 4, M.BF16, None, d, d, d, 1 << 30, None)
+    st = L.medusa_heads_forward(d, d, None, d, M.ROW_MAJOR, 1, 4096, 32000, 5, 4, M.BF16, None, d, d, d, 1 << 30, None)
     assert st == M.EINVAL and "both" in L.medusa_last_error().decode()
     st = L.medusa_resid_silu(d, d, d, 1, 4096, 5, 7, d, None)
     assert st == M.EINVAL
+    # packed w2: bf16 only, H a multiple of 256, a known layout
+    st = L.medusa_vocab_topk(d, d, M.PACKED, 8, 256, 1000, 5, 4, M.F32, None, d, d, d, 1 << 30, None)
+    assert st == M.EUNSUPPORTED and "bf16" in L.medusa_last_error().decode()
+    st = L.medusa_vocab_topk(d, d, M.PACKED, 8, 4104, 1000, 5, 4, M.BF16, None, d, d, d, 1 << 30, None)
+    assert st == M.EUNSUPPORTED and "multiple" in L.medusa_last_error().decode()
+    st = L.medusa_vocab_topk(d, d, 7, 8, 4096, 1000, 5, 4, M.BF16, None, d, d, d, 1 << 30, None)
+    assert st == M.EINVAL and "layout" in L.medusa_last_error().decode()
 
 
 def test_workspace_sizes_are_positive(M):
     L = M._lib
-    assert L.medusa_heads_workspace_size(1, 4096, 32000, 5, 4, M.BF16) >= 5 * 4096 * 4
-    assert L.medusa_vocab_topk_workspace_size(8, 4096, 128256, 5, 4, M.BF16) > 0
+    assert L.medusa_heads_workspace_size(1, 4096, 32000, 5, 4, M.BF16, M.ROW_MAJOR) >= 5 * 4096 * 4
+    assert L.medusa_vocab_topk_workspace_size(8, 4096, 128256, 5, 4, M.BF16, M.ROW_MAJOR) > 0
+    # packed: the bf16 head/remainder rows of every head + per-workgroup top-k candidates
+    assert (L.medusa_vocab_topk_workspace_size(8, 4096, 128256, 5, 4, M.BF16, M.PACKED)
+            >= 5 * 16 * 4096 * 2 + 2 * 8 * 5 * 1002 * 4 * 4)
     # packed: row factors + per-workgroup (value, index) candidates of every row
     assert L.medusa_base_greedy_workspace_size(64, 4096, 32000, M.BF16, M.PACKED) >= 64 * 4 + 2 * 64 * 250 * 4
     assert L.medusa_base_greedy_workspace_size(9, 256, 1000, M.F32, M.ROW_MAJOR) >= 9 * 256 * 4
-    assert L.medusa_heads_workspace_size(0, 4096, 32000, 5, 4, M.BF16) == 0
+    assert L.medusa_heads_workspace_size(0, 4096, 32000, 5, 4, M.BF16, M.ROW_MAJOR) == 0
 
 
 def test_packed_size(M):

@@ -32,25 +32,34 @@ def _cfg(name, dtype, B, H, V, K, topk, tree, nH=4, nKV=4, D=64, P=(128,), seed=
     return mi.custom_config(name, dtype, B, H, V, K, topk, tree, nH, nKV, D, P, seed)
 
 
+# (name, workload, layout of W2: row-major GEMV or packed MFMA product)
 HEAD_CASES = [
-    ("c1", lambda: mi.config(1)),
-    ("bf16_h1024_v5003_b1", lambda: _cfg("m1", "bf16", 1, 1024, 5003, 3, 4, mi.tiny_tree(), seed=101)),
-    ("bf16_h512_v3001_b3_k6", lambda: _cfg("m2", "bf16", 3, 512, 3001, 2, 6, mi.tiny_tree(), seed=102)),
-    ("f32_h256_v777_b2_k5", lambda: _cfg("m3", "f32", 2, 256, 777, 3, 5, mi.tiny_tree(), seed=103)),
-    ("bf16_h2048_v4000_b8", lambda: _cfg("m4", "bf16", 8, 2048, 4000, 2, 4, mi.tiny_tree(), seed=104)),
+    ("c1", lambda: mi.config(1), "rows"),
+    ("bf16_h1024_v5003_b1", lambda: _cfg("m1", "bf16", 1, 1024, 5003, 3, 4, mi.tiny_tree(), seed=101), "rows"),
+    ("bf16_h512_v3001_b3_k6", lambda: _cfg("m2", "bf16", 3, 512, 3001, 2, 6, mi.tiny_tree(), seed=102), "rows"),
+    ("f32_h256_v777_b2_k5", lambda: _cfg("m3", "f32", 2, 256, 777, 3, 5, mi.tiny_tree(), seed=103), "rows"),
+    ("bf16_h2048_v4000_b8", lambda: _cfg("m4", "bf16", 8, 2048, 4000, 2, 4, mi.tiny_tree(), seed=104), "rows"),
+    # packed W2 (MFMA): 8, 3 and 1 sequences; vocabularies not a multiple of
+    # the 128 rows of a workgroup; top-16
+    ("packed_h2048_v4000_b8", lambda: _cfg("m4", "bf16", 8, 2048, 4000, 2, 4, mi.tiny_tree(), seed=104), "packed"),
+    ("packed_h512_v3001_b3_k6", lambda: _cfg("m2", "bf16", 3, 512, 3001, 2, 6, mi.tiny_tree(), seed=102), "packed"),
+    ("packed_h1024_v5003_b1_k16", lambda: _cfg("m5", "bf16", 1, 1024, 5003, 3, 16, mi.tiny_tree(), seed=106),
+     "packed"),
 ]
 
 
-@pytest.mark.parametrize("name,mk", HEAD_CASES, ids=[c[0] for c in HEAD_CASES])
-def test_heads_parity(M, name, mk):
+@pytest.mark.parametrize("name,mk,layout", HEAD_CASES, ids=[c[0] for c in HEAD_CASES])
+def test_heads_parity(M, name, mk, layout):
     cfg = mk()
-    _say("heads", name)
+    _say("heads", name, layout)
     heads = mi.gen_heads(cfg)
     ov = []
     logits_ref, z_ref = enforce_heads_gap(cfg, heads, ov)   # [K][V][B], [B][K][H]
     logits_ref = np.transpose(logits_ref, (2, 0, 1))
     idx_ref, val_ref = oracle.topk(logits_ref, cfg.topk)
     h, W1, b1, W2 = (dev(heads[k]) for k in ("h", "W1", "b1", "W2"))
+    if layout == "packed":
+        W2 = M.pack_heads(W2)
     B, K, V, H, k = cfg.B, cfg.K, cfg.V, cfg.H, cfg.topk
     z = torch.empty(B, K, H, device="cuda")
     M.medusa_resid_silu(h, W1, b1, z)
@@ -72,11 +81,13 @@ def test_heads_parity(M, name, mk):
     assert torch.equal(ti, ti2) and torch.equal(tv, tv2)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "bf16_packed"])
 def test_zero_init_heads_reproduce_lm_head_bitwise(M, dtype):
     # heads page sketch: W1 = 0, b1 = 0, W2 = copy of lm_head => every head's
     # logits equal lm_head(h) exactly
     _say("zero-init", dtype)
+    packed = dtype.endswith("_packed")
+    dtype = dtype.replace("_packed", "")
     H, V, K = (256, 1000, 3) if dtype == "f32" else (4096, 32000, 5)
     cfg = _cfg("zi", dtype, 1, H, V, K, 4, mi.tiny_tree(), seed=105)
     lm = mi.normal((V, H), cfg.seed, mi.S_LM_HEAD, 0.02, dtype)
@@ -88,11 +99,14 @@ def test_zero_init_heads_reproduce_lm_head_bitwise(M, dtype):
     lg = torch.empty(1, K, V, device="cuda")
     ti = torch.empty(1, K, 4, dtype=torch.int32, device="cuda")
     tv = torch.empty(1, K, 4, device="cuda")
+    lm_w2 = lm_d.unsqueeze(0).contiguous()
+    if packed:
+        W2, lm_w2 = M.pack_heads(W2), M.pack_heads(lm_w2)
     M.medusa_heads_forward(h, W1, b1, W2, 4, ti, tv, logits=lg)
     base = torch.empty(1, 1, V, device="cuda")
     bi = torch.empty(1, 1, 4, dtype=torch.int32, device="cuda")
     bv = torch.empty(1, 1, 4, device="cuda")
-    M.medusa_heads_forward(h, None, None, lm_d.unsqueeze(0).contiguous(), 4, bi, bv, logits=base)
+    M.medusa_heads_forward(h, None, None, lm_w2, 4, bi, bv, logits=base)
     torch.cuda.synchronize()
     assert [bool(torch.equal(lg[:, k], base[:, 0])) for k in range(K)] == [True] * K
     assert all(torch.equal(ti[:, k], bi[:, 0]) for k in range(K))
