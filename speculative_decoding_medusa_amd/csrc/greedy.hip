@@ -89,36 +89,53 @@ static size_t a256(size_t x) { return (x + 255) / 256 * 256; }
 // greedy[r] = argmax_v lm_head[v] . n[r] for bf16 rows n already normalised
 // (MFMA product with the fused argmax, then the merge of the workgroups'
 // candidates).  Workspace: the candidates.
-// Vocabularies of >= 8192 rows stream from 8-wave workgroups (more weight
-// bytes in flight per CU: 64 x 4096 x 32000 takes 45.7 us against 48.7 us
-// with 4 waves); smaller ones keep 4 waves for more workgroups.
-static int lmh_waves(int V) { return V >= 8192 ? 8 : 4; }
-static int lmh_groups(int V) { return (V + 16 * lmh_waves(V) - 1) / (16 * lmh_waves(V)); }
+// Launch shape (measured, 4096-wide rows): up to 64 node rows, vocabularies
+// of >= 8192 rows stream from 8-wave workgroups with one 16-row weight block
+// per wave (64 x 32000: 45.6 us against 50.0 with 4 waves).  From 128 node
+// rows on the products are bound by the LDS reads of the node fragments, so
+// each wave takes two weight blocks (a fragment read feeds two products):
+// 256 x 128256 in 280 us against 363, 512 x 128256 in 574 against 717; 8
+// waves unless that leaves fewer than 256 workgroups (256 x 32000: 4 waves,
+// 110 us against 126).
+struct LmhShape {
+    int waves, rb;
+};
+static LmhShape lmh_shape(int R, int V) {
+    const int nblk = lmh_nblk(R);
+    if (nblk < 8) return {V >= 8192 ? 8 : 4, 1};
+    const int tiles = (R + nblk * 16 - 1) / (nblk * 16);
+    return {(V + 255) / 256 * tiles >= 256 ? 8 : 4, 2};
+}
+static int lmh_groups(int R, int V) {
+    const LmhShape sh = lmh_shape(R, V);
+    const int rows = 16 * sh.waves * sh.rb;
+    return (V + rows - 1) / rows;
+}
 
 size_t lm_head_greedy_workspace_bytes(int R, int H, int V) {
     (void)H;
-    return a256((size_t)R * lmh_groups(V) * 4) * 2;
+    return a256((size_t)R * lmh_groups(R, V) * 4) * 2;
 }
 
 void launch_lm_head_greedy(const bf16_t* n, const bf16_t* lm_head, int R, int H, int V, int32_t* greedy,
                            float* logits, const float* row_scale, void* ws, hipStream_t s) {
-    const int G = lmh_groups(V);
+    const int G = lmh_groups(R, V);
     float* cv = (float*)ws;
     int* ci = (int*)((char*)ws + a256((size_t)R * G * 4));
     const int nblk = lmh_nblk(R);
     const dim3 grid(G, (R + nblk * 16 - 1) / (nblk * 16));
     const int nch = H / lmh_kc(nblk);
-#define LMH_LAUNCH(NB, WV)                                                                                        \
-    MEDUSA_LAUNCH("lm_head_argmax", (skinny_mfma_kernel<NB, SKINNY_ARGMAX, WV>), grid, dim3(WV * 64), 0, s, n, \
-                  lm_head, R, H, V, nch, cv, ci, logits, row_scale)
-    if (lmh_waves(V) == 8) {
-        if (nblk == 4) LMH_LAUNCH(4, 8);
-        else if (nblk == 8) LMH_LAUNCH(8, 8);
-        else LMH_LAUNCH(16, 8);
+#define LMH_LAUNCH(NB, WV, RBL)                                                                                 \
+    MEDUSA_LAUNCH("lm_head_argmax", (skinny_mfma_kernel<NB, SKINNY_ARGMAX, WV, RBL>), grid, dim3(WV * 64), 0, s, \
+                  n, lm_head, R, H, V, nch, cv, ci, logits, row_scale)
+    if (lmh_shape(R, V).waves == 8) {
+        if (nblk == 4) LMH_LAUNCH(4, 8, 1);
+        else if (nblk == 8) LMH_LAUNCH(8, 8, 2);
+        else LMH_LAUNCH(16, 8, 2);
     } else {
-        if (nblk == 4) LMH_LAUNCH(4, 4);
-        else if (nblk == 8) LMH_LAUNCH(8, 4);
-        else LMH_LAUNCH(16, 4);
+        if (nblk == 4) LMH_LAUNCH(4, 4, 1);
+        else if (nblk == 8) LMH_LAUNCH(8, 4, 2);
+        else LMH_LAUNCH(16, 4, 2);
     }
 #undef LMH_LAUNCH
     MEDUSA_LAUNCH("argmax_merge", argmax_merge_kernel, dim3(R), dim3(64), 0, s, cv, ci, G, greedy);

@@ -67,7 +67,10 @@ struct LmhCfg {
 // loads go out before the weight loads of the same step: vector-memory loads
 // complete in issue order, so waiting for a chunk's node rows never waits for
 // younger weight fragments.
-template <int NBLK, int EPI, int WAVES = LMH_WAVES>
+// RB (ARGMAX only): 16-row weight blocks per wave; every node fragment read
+// from LDS then feeds RB products, which halves the LDS traffic per product
+// at RB = 2 (the bound of the 128- and 256-node tiles).
+template <int NBLK, int EPI, int WAVES = LMH_WAVES, int RB = 1>
 __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* __restrict__ n,   // [R][K] node rows
                                                           const bf16_t* __restrict__ Wp,  // packed, V rows of K
                                                           int R, int K, int V, int chunks_per_split,
@@ -92,6 +95,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
     __shared__ f32x4 xup[EPI == SKINNY_SWIGLU ? WAVES / 2 : 1][EPI == SKINNY_SWIGLU ? NBLK : 1][64];
     __shared__ float tkv[EPI == SKINNY_TOPK ? WAVES * PACK_ROWS : 1][8];  // TOPK: the workgroup's rows x sequences
     static_assert(EPI != SKINNY_TOPK || NBLK == 1, "top-k epilogue: 16 node rows");
+    static_assert(RB == 1 || EPI == SKINNY_ARGMAX, "several row blocks per wave: argmax epilogue only");
     if (EPI == SKINNY_TOPK) {
         n += (size_t)blockIdx.y * n_stride;
         Wp += (size_t)blockIdx.y * w_stride;
@@ -101,17 +105,19 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
     const int lane = tid & 63, wave = tid >> 6;
     const int G = gridDim.x;
     const int node0 = EPI == SKINNY_TOPK ? 0 : blockIdx.y * C::NODES;
-    const int rb = blockIdx.x * WAVES + wave;         // this wave's 16-row block
+    const int rb = (blockIdx.x * WAVES + wave) * RB;  // this wave's first 16-row block
     const int vw = rb * PACK_ROWS;                    // its first weight row
     const int lr = lane & 15, lk = lane >> 4;         // row / k-group within a 16x16x32 tile
     const int nrb = (V + PACK_ROWS - 1) / PACK_ROWS;
     const int ksteps = K / PACK_K;
 
-    f32x4 acc[NBLK];
+    f32x4 acc[RB * NBLK];  // row block j, node block b: acc[j * NBLK + b]
 #pragma unroll
-    for (int b = 0; b < NBLK; ++b) acc[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < RB * NBLK; ++b) acc[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    const bf16_t* wb = Wp + (size_t)min(rb, nrb - 1) * ksteps * PACK_FRAG + lane * 8;
+    const bf16_t* wb[RB];
+#pragma unroll
+    for (int j = 0; j < RB; ++j) wb[j] = Wp + (size_t)min(rb + j, nrb - 1) * ksteps * PACK_FRAG + lane * 8;
 
     // the node row of each of this thread's pieces is the same in every chunk
     const bf16_t* nrow[C::NPT];
@@ -127,11 +133,14 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
     // this workgroup's k-range: chunks [c_lo, c_lo + nchunk), nchunk >= 1
     const int c_lo = blockIdx.z * chunks_per_split;
     const int nchunk = min(K / C::KC - c_lo, chunks_per_split);  // host guarantees K % KC == 0
-    u32x4 aring[D][C::KS];
+    u32x4 aring[D][C::KS * RB];
     u32x4 nring[D][C::NPT];
-    auto load_a = [&](u32x4(&dst)[C::KS], int c) {
+    auto load_a = [&](u32x4(&dst)[C::KS * RB], int c) {
 #pragma unroll
-        for (int s = 0; s < C::KS; ++s) dst[s] = ld_stream(wb + (size_t)((c_lo + c) * C::KS + s) * PACK_FRAG);
+        for (int s = 0; s < C::KS; ++s)
+#pragma unroll
+            for (int j = 0; j < RB; ++j)
+                dst[s * RB + j] = ld_stream(wb[j] + (size_t)((c_lo + c) * C::KS + s) * PACK_FRAG);
     };
     auto load_n = [&](u32x4(&dst)[C::NPT], int c) {
 #pragma unroll
@@ -167,9 +176,11 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
 #pragma unroll
                     for (int b = 0; b < NBLK; ++b) {
                         const u32x4 bv = *(const u32x4*)(&ns[stage][b * 16 + lr][s * 32 + lk * 8]);
-                        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, aring[u][s]),
-                                                                         __builtin_bit_cast(bf16x8, bv), acc[b], 0, 0,
-                                                                         0);
+#pragma unroll
+                        for (int j = 0; j < RB; ++j)
+                            acc[j * NBLK + b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8, aring[u][s * RB + j]), __builtin_bit_cast(bf16x8, bv),
+                                acc[j * NBLK + b], 0, 0, 0);
                     }
             }
             // the other stage was last read before the previous barrier
@@ -265,14 +276,16 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
         const int node = node0 + b * 16 + lr;
         const float sc = (out != nullptr && row_scale != nullptr && node < R) ? row_scale[node] : 1.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int v = vw + lk * 4 + r;
-            const float x = acc[b][r];
-            if (v < V) {
-                if (out != nullptr && node < R) out[(size_t)node * V + v] = x * sc;
-                if (better(x, v, bv, bi)) { bv = x; bi = v; }
+        for (int j = 0; j < RB; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int v = vw + j * PACK_ROWS + lk * 4 + r;
+                const float x = acc[j * NBLK + b][r];
+                if (v < V) {
+                    if (out != nullptr && node < R) out[(size_t)node * V + v] = x * sc;
+                    if (better(x, v, bv, bi)) { bv = x; bi = v; }
+                }
             }
-        }
 #pragma unroll
         for (int m = 16; m <= 32; m <<= 1) {
             const float ov = __shfl_xor(bv, m, 64);
