@@ -135,10 +135,11 @@ def main():
     z = torch.empty(B, K, H, device="cuda")
     ti = torch.empty(B, K, topk, dtype=torch.int32, device="cuda")
     tv = torch.empty(B, K, topk, device="cuda")
-    # from 4 sequences on, W2 in the packed layout of the MFMA vocabulary
-    # product (packed once, like a weight load); fewer sequences stream the
-    # row-major W2 through the vector-ALU GEMV
+    # from 4 sequences on, W1 and W2 in the packed layout of the MFMA head
+    # products (packed once, like a weight load); fewer sequences stream the
+    # row-major weights through the vector-ALU GEMVs
     w2_layout = M.PACKED if B >= 4 and wdt == M.BF16 and H % 256 == 0 else M.ROW_MAJOR
+    w1 = M.pack_heads(d.pop("W1")) if w2_layout == M.PACKED else d["W1"]
     w2 = M.pack_heads(d.pop("W2")) if w2_layout == M.PACKED else d["W2"]
     ws_v = torch.empty(M.vocab_topk_workspace_size(B, H, V, K, topk, wdt, w2_layout), dtype=torch.uint8,
                        device="cuda")
@@ -160,7 +161,7 @@ def main():
     maxP = max(cfg.P)
 
     def step():
-        M.medusa_resid_silu(d["h"], d["W1"], d["b1"], z)
+        M.medusa_resid_silu(d["h"], w1, d["b1"], z)
         M.medusa_vocab_topk(z, w2, topk, ti, tv, ws=ws_v)
         M.medusa_build_tree(tree, ti, root_d, d["cache_len"], tok, pos)
         M.tree_attention_verify(d["q"], d["k_tree"], d["v_tree"], d["k_cache"], d["v_cache"], d["cache_len"], maxP,
@@ -214,7 +215,7 @@ def main():
         return sum(kern_us.get(n, 0.0) for n in names)
 
     st = {
-        "heads_resid_silu": stage("resid_silu_gemv"),
+        "heads_resid_silu": stage("resid_silu_gemv", "resid_silu_mfma"),
         "heads_vocab_topk": stage("vocab_proj_topk", "split_rows", "vocab_proj_topk_mfma", "topk_merge"),
         "build_tree": stage("build_tree"),
         "tree_attention": stage("tree_attn_split", "tree_attn_mfma", "tree_attn_merge"),

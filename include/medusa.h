@@ -75,11 +75,17 @@ const char* medusa_version(void);
 /* ---------------------------------------------------------------------------
  * Step a1 -- residual-SiLU block of every head (heads page, section on how the
  * heads predict later tokens):  z[b][k][:] = h[b] + SiLU(W1_k h[b] + b1_k).
- *   h  [B][H] (dt), w1 [K][H][H] (dt, [out][in]), b1 [K][H] (dt)
+ *   h  [B][H] (dt), b1 [K][H] (dt)
+ *   w1 head k's square matrix ([out][in]), laid out as w1_layout says:
+ *      MEDUSA_ROW_MAJOR: [K][H][H] (dt), streamed by a vector-ALU GEMV;
+ *      MEDUSA_PACKED (bf16 only, H a multiple of 128): K packed H x H
+ *      matrices back to back (head k at byte offset k * medusa_packed_size(H,
+ *      H)), streamed through MFMA with the bf16 h rows as exact operands;
+ *      the faster choice from B = 4 on.
  *   z  [B][K][H] float32 (output)
  * Limits: 1 <= B <= 8, H % 8 == 0, H <= 8192.
  * ------------------------------------------------------------------------- */
-medusa_status medusa_resid_silu(const void* h, const void* w1, const void* b1,
+medusa_status medusa_resid_silu(const void* h, const void* w1, medusa_layout w1_layout, const void* b1,
                                 int B, int H, int K, medusa_dtype dt,
                                 float* z, void* stream);
 
@@ -111,13 +117,14 @@ medusa_status medusa_vocab_topk(const float* z, const void* w2, medusa_layout w2
 /* ---------------------------------------------------------------------------
  * Steps a1 + a2 in one call: the K Medusa heads on the last hidden state.
  *   w1 == NULL and b1 == NULL: z_k = h for every head (plain projection, e.g.
- *   the base model's lm_head with K = 1).  Workspace holds z and the top-k
- *   partials.  Other arguments as above.
+ *   the base model's lm_head with K = 1).  `layout` applies to w1 and w2
+ *   alike.  Workspace holds z and the top-k partials.  Other arguments as
+ *   above.
  * ------------------------------------------------------------------------- */
 size_t medusa_heads_workspace_size(int B, int H, int V, int K, int topk, medusa_dtype dt,
                                    medusa_layout w2_layout);
 medusa_status medusa_heads_forward(const void* h, const void* w1, const void* b1, const void* w2,
-                                   medusa_layout w2_layout,
+                                   medusa_layout layout,
                                    int B, int H, int V, int K, int topk, medusa_dtype dt,
                                    float* logits, int32_t* topk_idx, float* topk_val,
                                    void* ws, size_t ws_bytes, void* stream);

@@ -30,7 +30,7 @@ _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctyp
 _SIGS = {
     "medusa_last_error": ([], ctypes.c_char_p),
     "medusa_version": ([], ctypes.c_char_p),
-    "medusa_resid_silu": ([_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp], _i32),
+    "medusa_resid_silu": ([_vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _vp, _vp], _i32),
     "medusa_vocab_topk_workspace_size": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32], _sz),
     "medusa_vocab_topk": ([_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
     "medusa_heads_workspace_size": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32], _sz),
@@ -111,9 +111,11 @@ def version() -> str:
 # ---------------------------------------------------------------------------
 
 def medusa_resid_silu(h, w1, b1, z, stream=None):
+    """w1: [K][H][H] (row-major) or the result of pack_heads (packed, MFMA)."""
     K, H, _ = w1.shape
     B = h.shape[0]
-    _check("medusa_resid_silu", _lib.medusa_resid_silu(_p(h), _p(w1), _p(b1), B, H, K, _dt(w1), _p(z),
+    layout, dt = _w_args(w1)
+    _check("medusa_resid_silu", _lib.medusa_resid_silu(_p(h), _p(w1), layout, _p(b1), B, H, K, dt, _p(z),
                                                        _stream(stream)))
     return z
 
@@ -122,19 +124,19 @@ def vocab_topk_workspace_size(B, H, V, K, topk, dt, layout=ROW_MAJOR):
     return _lib.medusa_vocab_topk_workspace_size(B, H, V, K, topk, dt, layout)
 
 
-def _w2_args(w2):
-    """(layout, dtype) of a head projection: a [K][V][H] tensor or the
-    packed heads of pack_heads."""
-    if isinstance(w2, Packed):
+def _w_args(w):
+    """(layout, dtype) of a head weight: a [K][rows][H] tensor or the packed
+    heads of pack_heads."""
+    if isinstance(w, Packed):
         return PACKED, BF16
-    return ROW_MAJOR, _dt(w2)
+    return ROW_MAJOR, _dt(w)
 
 
 def medusa_vocab_topk(z, w2, topk, topk_idx, topk_val, logits=None, ws=None, stream=None):
     """w2: [K][V][H] (row-major) or the result of pack_heads (packed, MFMA)."""
     K, V, H = w2.shape
     B = z.shape[0]
-    layout, dt = _w2_args(w2)
+    layout, dt = _w_args(w2)
     need = vocab_topk_workspace_size(B, H, V, K, topk, dt, layout)
     ws = _ws(need, z.device, ws)
     _check("medusa_vocab_topk", _lib.medusa_vocab_topk(_p(z), _p(w2), layout, B, H, V, K, topk, dt, _p(logits),
@@ -148,10 +150,13 @@ def heads_workspace_size(B, H, V, K, topk, dt, layout=ROW_MAJOR):
 
 
 def medusa_heads_forward(h, w1, b1, w2, topk, topk_idx, topk_val, logits=None, ws=None, stream=None):
-    """w2: [K][V][H] (row-major) or the result of pack_heads (packed, MFMA)."""
+    """w1, w2: [K][H][H], [K][V][H] (row-major), or both the results of
+    pack_heads (packed, MFMA; w1 may be None either way)."""
     K, V, H = w2.shape
     B = h.shape[0]
-    layout, dt = _w2_args(w2)
+    if w1 is not None:
+        assert isinstance(w1, Packed) == isinstance(w2, Packed), "w1 and w2 must share one layout"
+    layout, dt = _w_args(w2)
     need = heads_workspace_size(B, H, V, K, topk, dt, layout)
     ws = _ws(need, h.device, ws)
     _check("medusa_heads_forward", _lib.medusa_heads_forward(
@@ -277,9 +282,10 @@ def pack(*mats, interleave: bool = False, stream=None) -> Packed:
 
 
 def pack_heads(w2, stream=None) -> Packed:
-    """Pack the heads' projections w2 [K][V][H] (bf16) for medusa_vocab_topk /
+    """Pack per-head matrices [K][rows][H] (bf16; the heads' W2 [K][V][H] or
+    W1 [K][H][H]) for medusa_vocab_topk / medusa_resid_silu /
     medusa_heads_forward: head k's packed matrix at byte offset
-    k * medusa_packed_size(V, H)."""
+    k * medusa_packed_size(rows, H)."""
     K, V, H = w2.shape
     assert w2.dtype == torch.bfloat16 and w2.is_contiguous()
     one = packed_size(V, H)

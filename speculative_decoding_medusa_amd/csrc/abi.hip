@@ -24,6 +24,9 @@ void launch_vocab_topk(const float* z, const void* w2, int B, int H, int V, int 
 int vocab_topk_groups(int B, int V, int K);
 size_t vocab_topk_lds_bytes(int B, int H, int V, int K);
 int vocab_topk_packed_kc();
+int resid_silu_packed_kc();
+void launch_resid_silu_packed(const void* h, const void* w1p, const void* b1, int B, int H, int K, float* z,
+                              hipStream_t s);
 size_t vocab_topk_packed_ws_bytes(int B, int H, int V, int K, int topk);
 void launch_vocab_topk_packed(const float* z, const void* w2p, int B, int H, int V, int K, int topk, float* logits,
                               int32_t* topk_idx, float* topk_val, void* ws, hipStream_t s);
@@ -181,12 +184,30 @@ static void check_heads_shape(int B, int H, int K, medusa_dtype dt) {
     SUPPORT(resid_silu_lds_bytes(B, H) <= 160 * 1024, "B*H too large for the LDS-staged right-hand sides");
 }
 
-medusa_status medusa_resid_silu(const void* h, const void* w1, const void* b1, int B, int H, int K,
-                                medusa_dtype dt, float* z, void* stream) {
+static void check_w1_layout(int H, medusa_dtype dt, medusa_layout w1_layout) {
+    REQUIRE(w1_layout == MEDUSA_ROW_MAJOR || w1_layout == MEDUSA_PACKED, "w1_layout must be ROW_MAJOR or PACKED");
+    if (w1_layout == MEDUSA_PACKED) {
+        SUPPORT(dt == MEDUSA_BF16, "a packed w1 must be bf16");
+        SUPPORT(H % resid_silu_packed_kc() == 0, "packed w1: H=%d must be a multiple of %d", H,
+                resid_silu_packed_kc());
+    }
+}
+
+static void run_resid_silu(const void* h, const void* w1, medusa_layout w1_layout, const void* b1, int B, int H,
+                           int K, medusa_dtype dt, float* z, hipStream_t s) {
+    if (w1_layout == MEDUSA_PACKED)
+        launch_resid_silu_packed(h, w1, b1, B, H, K, z, s);
+    else
+        launch_resid_silu(h, w1, b1, B, H, K, dt == MEDUSA_BF16, z, s);
+}
+
+medusa_status medusa_resid_silu(const void* h, const void* w1, medusa_layout w1_layout, const void* b1, int B,
+                                int H, int K, medusa_dtype dt, float* z, void* stream) {
     return guarded("medusa_resid_silu", [&] {
         check_heads_shape(B, H, K, dt);
+        check_w1_layout(H, dt, w1_layout);
         REQUIRE(h && w1 && b1 && z, "null pointer argument");
-        launch_resid_silu(h, w1, b1, B, H, K, dt == MEDUSA_BF16, z, (hipStream_t)stream);
+        run_resid_silu(h, w1, w1_layout, b1, B, H, K, dt, z, (hipStream_t)stream);
     });
 }
 
@@ -261,11 +282,13 @@ __global__ void broadcast_h_kernel(const void* h, int B, int H, int K, int bf16,
 }
 
 medusa_status medusa_heads_forward(const void* h, const void* w1, const void* b1, const void* w2,
-                                   medusa_layout w2_layout, int B, int H, int V, int K, int topk, medusa_dtype dt,
+                                   medusa_layout layout, int B, int H, int V, int K, int topk, medusa_dtype dt,
                                    float* logits, int32_t* topk_idx, float* topk_val, void* ws, size_t ws_bytes,
                                    void* stream) {
+    const medusa_layout w2_layout = layout;
     return guarded("medusa_heads_forward", [&] {
         check_vocab(B, H, V, K, topk, dt, w2_layout);
+        if (w1) check_w1_layout(H, dt, layout);
         REQUIRE(h && w2 && topk_idx && topk_val && ws, "null pointer argument");
         REQUIRE((w1 == nullptr) == (b1 == nullptr), "w1 and b1 must both be given or both be NULL");
         const size_t need = medusa_heads_workspace_size(B, H, V, K, topk, dt, w2_layout);
@@ -274,7 +297,7 @@ medusa_status medusa_heads_forward(const void* h, const void* w1, const void* b1
         void* vws = (char*)ws + align256((size_t)B * K * H * 4);
         hipStream_t s = (hipStream_t)stream;
         if (w1)
-            launch_resid_silu(h, w1, b1, B, H, K, dt == MEDUSA_BF16, z, s);
+            run_resid_silu(h, w1, layout, b1, B, H, K, dt, z, s);
         else
             MEDUSA_LAUNCH("broadcast_h", broadcast_h_kernel, dim3(64), dim3(256), 0, s, h, B, H, K,
                           dt == MEDUSA_BF16 ? 1 : 0, z);

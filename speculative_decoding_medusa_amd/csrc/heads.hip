@@ -459,6 +459,24 @@ void launch_vocab_topk_packed(const float* z, const void* w2p, int B, int H, int
     launch_topk_merge(cv, ci, B * K, G * topk, topk, topk_idx, topk_val, s, "topk_merge");
 }
 
+// Residual-SiLU block over packed W1 on MFMA (several sequences): the bf16
+// hidden states are the node rows (exact, no split), grid (H / 64, K), one
+// packed H x H matrix per grid row; the epilogue adds the bias, applies SiLU
+// and the residual.
+constexpr int SILU_MF_WAVES = 4;
+
+int resid_silu_packed_kc() { return LmhCfg<1, SILU_MF_WAVES>::KC; }
+
+void launch_resid_silu_packed(const void* h, const void* w1p, const void* b1, int B, int H, int K, float* z,
+                              hipStream_t s) {
+    const int G = (H + 16 * SILU_MF_WAVES - 1) / (16 * SILU_MF_WAVES);
+    const long long w_stride = (long long)((H + PACK_ROWS - 1) / PACK_ROWS) * PACK_ROWS * H;
+    MEDUSA_LAUNCH("resid_silu_mfma", (skinny_mfma_kernel<1, SKINNY_SILU, SILU_MF_WAVES>), dim3(G, K),
+                  dim3(SILU_MF_WAVES * 64), 0, s, (const bf16_t*)h, (const bf16_t*)w1p, B, H, H,
+                  H / LmhCfg<1, SILU_MF_WAVES>::KC, nullptr, nullptr, z, nullptr, 0, 0, 0LL, w_stride,
+                  (const bf16_t*)b1);
+}
+
 void launch_vocab_topk(const float* z, const void* w2, int B, int H, int V, int K, int topk, bool bf16,
                        float* logits, int32_t* topk_idx, float* topk_val, float* cv, int* ci, hipStream_t s) {
     launch_vocab_topk_named(z, w2, B, H, V, K, topk, bf16, logits, topk_idx, topk_val, cv, ci, s,

@@ -29,8 +29,10 @@ namespace medusa {
 // interleaved in 16-row blocks): bf16(SiLU(gate) * up);  TOPK (16 node rows:
 // rows 0..7 the bf16 heads of up to 8 sequences' inputs, rows 8..15 their
 // bf16 remainders; one weight matrix per grid row y): per-workgroup top-k
-// candidates of each sequence
-enum { SKINNY_ARGMAX = 0, SKINNY_PARTIAL = 1, SKINNY_SWIGLU = 2, SKINNY_TOPK = 3 };
+// candidates of each sequence;  SILU (node rows: the R <= 16 sequences'
+// bf16 hidden states; one weight matrix per grid row y): the residual-SiLU
+// block z[b][y][row] = h[b][row] + SiLU(score + bias[y][row])
+enum { SKINNY_ARGMAX = 0, SKINNY_PARTIAL = 1, SKINNY_SWIGLU = 2, SKINNY_TOPK = 3, SKINNY_SILU = 4 };
 
 // packed fragment geometry
 constexpr int PACK_ROWS = 16;                      // rows per fragment
@@ -79,7 +81,8 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
                                                           float* __restrict__ out,
                                                           const float* __restrict__ row_scale = nullptr,
                                                           int topk = 0, int nseq = 0, long long n_stride = 0,
-                                                          long long w_stride = 0) {
+                                                          long long w_stride = 0,
+                                                          const bf16_t* __restrict__ bias = nullptr) {
     // ARGMAX: out = optional logits [R][V], each node row's scores times
     // row_scale[node] when given (a positive factor: the argmax is that of the
     // unscaled scores);  PARTIAL: out = [splits][R][V];  SWIGLU: out = bf16 [R][V / 2];
@@ -94,9 +97,9 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
     __shared__ int red_i[WAVES][EPI == SKINNY_ARGMAX ? C::NODES : 1];
     __shared__ f32x4 xup[EPI == SKINNY_SWIGLU ? WAVES / 2 : 1][EPI == SKINNY_SWIGLU ? NBLK : 1][64];
     __shared__ float tkv[EPI == SKINNY_TOPK ? WAVES * PACK_ROWS : 1][8];  // TOPK: the workgroup's rows x sequences
-    static_assert(EPI != SKINNY_TOPK || NBLK == 1, "top-k epilogue: 16 node rows");
+    static_assert((EPI != SKINNY_TOPK && EPI != SKINNY_SILU) || NBLK == 1, "top-k / SiLU epilogue: 16 node rows");
     static_assert(RB == 1 || EPI == SKINNY_ARGMAX, "several row blocks per wave: argmax epilogue only");
-    if (EPI == SKINNY_TOPK) {
+    if (EPI == SKINNY_TOPK || EPI == SKINNY_SILU) {
         n += (size_t)blockIdx.y * n_stride;
         Wp += (size_t)blockIdx.y * w_stride;
     }
@@ -104,7 +107,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int G = gridDim.x;
-    const int node0 = EPI == SKINNY_TOPK ? 0 : blockIdx.y * C::NODES;
+    const int node0 = (EPI == SKINNY_TOPK || EPI == SKINNY_SILU) ? 0 : blockIdx.y * C::NODES;
     const int rb = (blockIdx.x * WAVES + wave) * RB;  // this wave's first 16-row block
     const int vw = rb * PACK_ROWS;                    // its first weight row
     const int lr = lane & 15, lk = lane >> 4;         // row / k-group within a 16x16x32 tile
@@ -212,6 +215,23 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
 #pragma unroll
             for (int r = 0; r < 4; ++r) y[r] = g[r] / (1.f + __expf(-g[r])) * u[r];
             *(uint2*)(a + (size_t)node * F + c0) = (uint2){pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+        }
+        return;
+    }
+    if (EPI == SKINNY_SILU) {
+        // lane (lr, lk) holds output rows vw + 4 lk + r of sequence lr (node
+        // rows past R are clamped copies; their columns are not written)
+        const int nm = gridDim.y, m = blockIdx.y;
+        if (lr < R) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int v = vw + lk * 4 + r;
+                if (v < V) {
+                    const float pre = acc[0][r] + bf16_to_f32(bias[(size_t)m * V + v]);
+                    const float sl = pre / (1.f + __expf(-pre));
+                    out[((size_t)lr * nm + m) * V + v] = bf16_to_f32(n[(size_t)lr * K + v]) + sl;
+                }
+            }
         }
         return;
     }

@@ -170,13 +170,14 @@ def lm_head_arg(M, lm_head):
     return lm_head, M.ROW_MAJOR
 
 
-def w2_arg(M, W2, B):
-    """The heads' projection as a step passes it: packed for the MFMA product
-    from 4 sequences on (bf16, H % 256 == 0), else the row-major tensor."""
+def head_weights_arg(M, W1, W2, B):
+    """The heads' W1 and W2 as a step passes them: packed for the MFMA
+    products from 4 sequences on (bf16, H % 256 == 0), else the row-major
+    tensors (vector-ALU GEMVs)."""
     import torch
     if B >= 4 and W2.dtype == torch.bfloat16 and W2.shape[2] % 256 == 0:
-        return M.pack_heads(W2)
-    return W2
+        return M.pack_heads(W1), M.pack_heads(W2)
+    return W1, W2
 
 
 def run_step_gpu(M, cfg, heads, att, root):
@@ -192,7 +193,7 @@ def run_step_gpu(M, cfg, heads, att, root):
     z = torch.empty(B, K, H, device="cuda")
     ti = torch.empty(B, K, topk, dtype=torch.int32, device="cuda")
     tv = torch.empty(B, K, topk, device="cuda")
-    w2 = w2_arg(M, d["W2"], B)
+    w1, w2 = head_weights_arg(M, d["W1"], d["W2"], B)
     w2_layout = M.PACKED if isinstance(w2, M.Packed) else M.ROW_MAJOR
     ws_v = torch.empty(M.vocab_topk_workspace_size(B, H, V, K, topk, wdt, w2_layout), dtype=torch.uint8,
                        device="cuda")
@@ -209,7 +210,7 @@ def run_step_gpu(M, cfg, heads, att, root):
     an = torch.empty(B, tree.max_depth + 1, dtype=torch.int32, device="cuda")
     ot = torch.empty_like(an)
     ncl = torch.empty(B, dtype=torch.int32, device="cuda")
-    M.medusa_resid_silu(d["h"], d["W1"], d["b1"], z)
+    M.medusa_resid_silu(d["h"], w1, d["b1"], z)
     M.medusa_vocab_topk(z, w2, topk, ti, tv, ws=ws_v)
     M.medusa_build_tree(tree, ti, dev(root), d["cache_len"], tok, pos)
     M.tree_attention_verify(d["q"], d["k_tree"], d["v_tree"], d["k_cache"], d["v_cache"], d["cache_len"], maxP, tree, o,
@@ -222,7 +223,7 @@ def run_step_gpu(M, cfg, heads, att, root):
                node_pos=pos.cpu().numpy(), o=host_f64(o), greedy=g.view(B, N).cpu().numpy(),
                accept_len=al.cpu().numpy(), accept_nodes=an.cpu().numpy(), out_tokens=ot.cpu().numpy(),
                new_cache_len=ncl.cpu().numpy(), k_cache=d["k_cache"], v_cache=d["v_cache"])
-    del d, lm, w2
+    del d, lm, w1, w2
     return out
 
 

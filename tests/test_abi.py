@@ -89,8 +89,12 @@ def test_heads_argument_errors(M):
     assert st == M.EINVAL and "workspace" in L.medusa_last_error().decode()
     st = L.medusa_heads_forward(d, d, None, d, M.ROW_MAJOR, 1, 4096, 32000, 5, 4, M.BF16, None, d, d, d, 1 << 30, None)
     assert st == M.EINVAL and "both" in L.medusa_last_error().decode()
-    st = L.medusa_resid_silu(d, d, d, 1, 4096, 5, 7, d, None)
+    st = L.medusa_resid_silu(d, d, M.ROW_MAJOR, d, 1, 4096, 5, 7, d, None)
     assert st == M.EINVAL
+    st = L.medusa_resid_silu(d, d, M.PACKED, d, 8, 4104, 5, M.BF16, d, None)
+    assert st == M.EUNSUPPORTED and "multiple" in L.medusa_last_error().decode()
+    st = L.medusa_resid_silu(d, d, M.PACKED, d, 8, 4096, 5, M.F32, d, None)
+    assert st == M.EUNSUPPORTED and "bf16" in L.medusa_last_error().decode()
     # packed w2: bf16 only, H a multiple of 256, a known layout
     st = L.medusa_vocab_topk(d, d, M.PACKED, 8, 256, 1000, 5, 4, M.F32, None, d, d, d, 1 << 30, None)
     assert st == M.EUNSUPPORTED and "bf16" in L.medusa_last_error().decode()

@@ -59,7 +59,7 @@ def test_heads_parity(M, name, mk, layout):
     idx_ref, val_ref = oracle.topk(logits_ref, cfg.topk)
     h, W1, b1, W2 = (dev(heads[k]) for k in ("h", "W1", "b1", "W2"))
     if layout == "packed":
-        W2 = M.pack_heads(W2)
+        W1, W2 = M.pack_heads(W1), M.pack_heads(W2)
     B, K, V, H, k = cfg.B, cfg.K, cfg.V, cfg.H, cfg.topk
     z = torch.empty(B, K, H, device="cuda")
     M.medusa_resid_silu(h, W1, b1, z)
@@ -101,7 +101,7 @@ def test_zero_init_heads_reproduce_lm_head_bitwise(M, dtype):
     tv = torch.empty(1, K, 4, device="cuda")
     lm_w2 = lm_d.unsqueeze(0).contiguous()
     if packed:
-        W2, lm_w2 = M.pack_heads(W2), M.pack_heads(lm_w2)
+        W1, W2, lm_w2 = M.pack_heads(W1), M.pack_heads(W2), M.pack_heads(lm_w2)
     M.medusa_heads_forward(h, W1, b1, W2, 4, ti, tv, logits=lg)
     base = torch.empty(1, 1, V, device="cuda")
     bi = torch.empty(1, 1, 4, dtype=torch.int32, device="cuda")
