@@ -146,6 +146,10 @@ ATT_CASES = [
     ("f32_chain9_d128_p0", lambda: _cfg("a3", "f32", 1, 256, 10, 9, 1, mi.chain_tree(9), 2, 2, 128, (0,), 203)),
     ("bf16_dense256_h2_d128_p1000", lambda: _cfg("a4", "bf16", 1, 256, 10, 5, 3, mi.dense_tree(256), 2, 2, 128, (1000,), 204)),
     ("bf16_sparse64_b3_ragged", lambda: _cfg("a5", "bf16", 3, 256, 10, 5, 4, mi.sparse_tree(64), 2, 1, 128, (1, 777, 2049), 205)),
+    # no prefix at all: the tree range is the only key range
+    ("bf16_sparse64_p0", lambda: _cfg("a6", "bf16", 1, 256, 10, 5, 4, mi.sparse_tree(64), 4, 4, 128, (0,), 206)),
+    # four query blocks of 64 at D = 64, GQA, two sequences
+    ("bf16_dense256_d64_gqa_b2", lambda: _cfg("a7", "bf16", 2, 256, 10, 5, 3, mi.dense_tree(256), 4, 2, 64, (70, 513), 207)),
 ]
 
 
