@@ -182,9 +182,11 @@ medusa_status tree_attention_verify(const void* q, const void* k_tree, const voi
  * Weight packing for the MFMA products (base greedy's lm_head, the decoder's
  * projections).  Not a step of the method: a layout, applied once when the
  * weights are loaded.  A packed matrix of `rows` rows and `cols` columns
- * (bf16) stores row r, column k at element
- *   ((r / 16) * (cols / 32) + k / 32) * 512 + ((k % 32) / 8 * 16 + r % 16) * 8 + k % 8
- * (every 16 x 32 tile is one contiguous 1 KB fragment) and occupies
+ * (bf16), NRB = ceil(rows / 16) blocks of 16 rows, stores row r, column k at
+ * element
+ *   ((k / 32) * NRB + r / 16) * 512 + ((k % 32) / 8 * 16 + r % 16) * 8 + k % 8
+ * (every 16 x 32 tile is one contiguous 1 KB fragment; the fragments of one
+ * 32-wide k-step are contiguous over all row blocks) and occupies
  * medusa_packed_size(rows, cols) bytes (rows rounded up to 16).
  *   medusa_pack_rows: src [rows][cols] row-major bf16 (device) -> rows of dst,
  *   a packed matrix of dst_rows rows.  interleave == 1: source row i goes to

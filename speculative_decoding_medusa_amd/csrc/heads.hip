@@ -43,6 +43,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_rows_kernel(
     // registers across the row loop.
     extern __shared__ __attribute__((aligned(16))) float xs[];  // [NB][H] fp32
     __shared__ float rowv[EPI == EPI_TOPK ? NB * GEMV_MAX_ROWS_PER_WG : 1];  // TOPK: [NB][rows_per_wg]
+    __shared__ float bsh[EPI == EPI_SILU ? GEMV_MAX_ROWS_PER_WG : 1];         // SILU: the rows' biases
     constexpr int NT = WAVES * 64;
     constexpr int PER = Elem<WT>::PER16;
     const int k = blockIdx.y;
@@ -50,33 +51,6 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_rows_kernel(
     const int G = gridDim.x;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-
-    // Stage the right-hand sides (fp32) in LDS with 16-byte loads; padded
-    // batch slots are zero.  H % 8 == 0, so a chunk never straddles two rows.
-    {
-        constexpr int XE = EPI == EPI_SILU ? Elem<WT>::PER16 : 4;  // elements per 16-byte chunk of x
-        const int cpr = H / XE;                                    // chunks per right-hand side
-        for (int i = threadIdx.x; i < NB * cpr; i += NT) {
-            const int b = i / cpr, j = (i - b * cpr) * XE;
-            float v[XE];
-            if (b < B) {
-                if (EPI == EPI_SILU) {
-                    Elem<WT>::expand(*(const u32x4*)((const WT*)xsrc + (size_t)b * H + j), v);
-                } else {
-                    const f32x4 q = *(const f32x4*)((const float*)xsrc + ((size_t)b * K + k) * H + j);
-#pragma unroll
-                    for (int t = 0; t < XE; ++t) v[t] = q[t];
-                }
-            } else {
-#pragma unroll
-                for (int t = 0; t < XE; ++t) v[t] = 0.f;
-            }
-#pragma unroll
-            for (int t = 0; t < XE; t += 4)
-                *(f32x4*)(xs + b * H + j + t) = (f32x4){v[t], v[t + 1], v[t + 2], v[t + 3]};
-        }
-    }
-    __syncthreads();
 
     const int nchunks = H / PER;
     const int row0 = g * rows_per_wg;
@@ -109,6 +83,42 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_rows_kernel(
             }
         }
     };
+
+    // The first weight rows of every wave are requested before the
+    // right-hand sides are staged, so the stream starts at once.
+    const int rb_first = row0 + wave * R;
+    u32x4 wv[R][CPL];
+    if (rb_first < row1) load_rows(wv, rb_first);
+
+    // Stage the right-hand sides (fp32) in LDS with 16-byte loads; padded
+    // batch slots are zero.  H % 8 == 0, so a chunk never straddles two rows.
+    // The SiLU epilogue's biases of this workgroup's rows go to LDS as well.
+    if (EPI == EPI_SILU)
+        for (int i = threadIdx.x; i < row1 - row0; i += NT) bsh[i] = Elem<WT>::load(bias, (size_t)k * H + row0 + i);
+    {
+        constexpr int XE = EPI == EPI_SILU ? Elem<WT>::PER16 : 4;  // elements per 16-byte chunk of x
+        const int cpr = H / XE;                                    // chunks per right-hand side
+        for (int i = threadIdx.x; i < NB * cpr; i += NT) {
+            const int b = i / cpr, j = (i - b * cpr) * XE;
+            float v[XE];
+            if (b < B) {
+                if (EPI == EPI_SILU) {
+                    Elem<WT>::expand(*(const u32x4*)((const WT*)xsrc + (size_t)b * H + j), v);
+                } else {
+                    const f32x4 q = *(const f32x4*)((const float*)xsrc + ((size_t)b * K + k) * H + j);
+#pragma unroll
+                    for (int t = 0; t < XE; ++t) v[t] = q[t];
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < XE; ++t) v[t] = 0.f;
+            }
+#pragma unroll
+            for (int t = 0; t < XE; t += 4)
+                *(f32x4*)(xs + b * H + j + t) = (f32x4){v[t], v[t + 1], v[t + 2], v[t + 3]};
+        }
+    }
+    __syncthreads();
     auto dot = [&](auto checked, const u32x4(&wv)[R][CPL], float(&acc)[R][NB]) {
         constexpr bool CHECKED = decltype(checked)::value;
 #pragma unroll
@@ -151,7 +161,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_rows_kernel(
                 if (row >= row1 || b >= B) continue;
                 if (EPI == EPI_SILU) {
                     if (lane == 0) {
-                        const float pre = v + Elem<WT>::load(bias, (size_t)k * H + row);
+                        const float pre = v + bsh[row - row0];
                         const float s = pre / (1.f + __expf(-pre));
                         out[((size_t)b * K + k) * H + row] = xs[b * H + row] + s;
                     }
@@ -163,9 +173,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_rows_kernel(
         }
     };
 
-    for (int rb = row0 + wave * R; rb < row1; rb += WAVES * R) {
-        u32x4 wv[R][CPL];
-        load_rows(wv, rb);
+    for (int rb = rb_first; rb < row1; rb += WAVES * R) {
+        if (rb != rb_first) load_rows(wv, rb);
         process(wv, rb);
     }
 
@@ -273,11 +282,15 @@ static GemvPlan gemv_plan(int nrows, int K, int target, int quantum) {
     return GemvPlan{(int)r, (int)((nrows + r - 1) / r)};
 }
 
-// LDS of one workgroup: the fp32 right-hand sides (dynamic) and, for the
-// top-k epilogue, the statically sized row-value array.
+// LDS of one workgroup: the fp32 right-hand sides (dynamic) and the
+// statically sized arrays: the row values (top-k epilogue) or the row biases
+// (SiLU epilogue).
 static size_t gemv_dyn_lds_bytes(int NB, int H) { return (size_t)NB * H * sizeof(float); }
+static size_t gemv_static_lds_bytes(int NB, bool topk) {
+    return (size_t)(topk ? NB : 1) * GEMV_MAX_ROWS_PER_WG * sizeof(float);
+}
 static size_t gemv_lds_bytes(int NB, int H, bool topk) {
-    return gemv_dyn_lds_bytes(NB, H) + (topk ? (size_t)NB * GEMV_MAX_ROWS_PER_WG * sizeof(float) : 0);
+    return gemv_dyn_lds_bytes(NB, H) + gemv_static_lds_bytes(NB, topk);
 }
 
 template <typename WT, int NB, int CPL, int R, int EPI, int WAVES>
@@ -288,7 +301,7 @@ static void launch_gemv_t(const void* x, const WT* W, const WT* bias, int B, int
     const size_t shmem = gemv_dyn_lds_bytes(NB, H);
     // allow the largest dynamic LDS that fits beside the static arrays (once per instantiation)
     static const bool lds_ok = [&] {
-        const size_t stat = EPI == EPI_TOPK ? (size_t)NB * GEMV_MAX_ROWS_PER_WG * sizeof(float) : 0;
+        const size_t stat = gemv_static_lds_bytes(NB, EPI == EPI_TOPK);
         return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                    (int)(160 * 1024 - stat - 1024)) == hipSuccess;
     }();
@@ -298,9 +311,11 @@ static void launch_gemv_t(const void* x, const WT* W, const WT* bias, int B, int
 }
 
 // Production shapes, measured on the 7B head shapes (W1: 5 x 4096 rows, W2:
-// 5 x 32000 and 5 x 128256 rows, of 4096 bf16).  One right-hand side streams
-// the weights (4 waves x 4 rows per step on ~512 workgroups for W1, 8 waves x
-// 2 rows on ~2048 for W2).  With 8 right-hand sides the kernel is bound by
+// 5 x 32000 and 5 x 128256 rows, of 4096 bf16) with the caches flushed
+// between launches.  One right-hand side streams the weights: 4 waves x 1 row
+// per step on ~2048 workgroups for W1 (29.3 us against 32.4 with 4 rows on
+// ~512: small workgroups balance over the CUs), 8 waves x 2 rows on ~2048 for
+// W2.  With 8 right-hand sides the kernel is bound by
 // the vector ALUs and the LDS reads of the right-hand sides, which more rows
 // per step amortise: 8 waves x 4 rows on ~256 workgroups for W1 (111 us
 // against 235 with 2 rows), 4 waves x 8 rows on ~1024 for W2 (2.32 ms against
@@ -308,7 +323,7 @@ static void launch_gemv_t(const void* x, const WT* W, const WT* bias, int B, int
 struct GemvShape {
     int R, WAVES, target;
 };
-static GemvShape silu_shape(int NB) { return NB <= 2 ? GemvShape{4, 4, 512} : GemvShape{4, 8, 256}; }
+static GemvShape silu_shape(int NB) { return NB <= 2 ? GemvShape{1, 4, 2048} : GemvShape{4, 8, 256}; }
 static GemvShape topk_shape(int NB) {
     return NB <= 2 ? GemvShape{2, 8, 2048} : NB <= 4 ? GemvShape{4, 4, 1024} : GemvShape{8, 4, 1024};
 }
@@ -370,7 +385,7 @@ void launch_resid_silu(const void* h, const void* w1, const void* b1, int B, int
                                                                 H, H, K, pl, z, nullptr, nullptr, 0, s,          \
                                                                 "resid_silu_gemv");                              \
     } while (0)
-    if (sh.WAVES == 4) MEDUSA_SILU_GO(4, 4, 1, 2); else MEDUSA_SILU_GO(4, 8, 4, 8);
+    if (sh.WAVES == 4) MEDUSA_SILU_GO(1, 4, 1, 2); else MEDUSA_SILU_GO(4, 8, 4, 8);
 #undef MEDUSA_SILU_GO
 }
 

@@ -9,7 +9,9 @@
 // of 16 rows and every 32-wide step of the contraction, the 16 x 32 tile is
 // one contiguous 1 KB fragment laid out exactly as the A operand of
 // v_mfma_f32_16x16x32_bf16 sits in a wave (lane l: row l % 16, k = 8 (l / 16)
-// .. +7), so every weight load of a wave is one coalesced 1 KB read.
+// .. +7), so every weight load of a wave is one coalesced 1 KB read; the
+// fragments of one k-step lie side by side over all row blocks, so a wave's
+// consecutive fragments are one k-step of the whole matrix apart.
 //
 // Grid (ceil(V / (16 WAVES)), ceil(R / NODES), splits); WAVES waves per
 // workgroup, each owning one 16-row block against NODES node rows.  Weight fragments stream
@@ -112,7 +114,6 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
     const int vw = rb * PACK_ROWS;                    // its first weight row
     const int lr = lane & 15, lk = lane >> 4;         // row / k-group within a 16x16x32 tile
     const int nrb = (V + PACK_ROWS - 1) / PACK_ROWS;
-    const int ksteps = K / PACK_K;
 
     f32x4 acc[RB * NBLK];  // row block j, node block b: acc[j * NBLK + b]
 #pragma unroll
@@ -120,7 +121,8 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
 
     const bf16_t* wb[RB];
 #pragma unroll
-    for (int j = 0; j < RB; ++j) wb[j] = Wp + (size_t)min(rb + j, nrb - 1) * ksteps * PACK_FRAG + lane * 8;
+    for (int j = 0; j < RB; ++j) wb[j] = Wp + (size_t)min(rb + j, nrb - 1) * PACK_FRAG + lane * 8;
+    const size_t kstride = (size_t)nrb * PACK_FRAG;  // elements from one k-step's fragment to the next
 
     // the node row of each of this thread's pieces is the same in every chunk
     const bf16_t* nrow[C::NPT];
@@ -143,7 +145,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
         for (int s = 0; s < C::KS; ++s)
 #pragma unroll
             for (int j = 0; j < RB; ++j)
-                dst[s * RB + j] = ld_stream(wb[j] + (size_t)((c_lo + c) * C::KS + s) * PACK_FRAG);
+                dst[s * RB + j] = ld_stream(wb[j] + (size_t)((c_lo + c) * C::KS + s) * kstride);
     };
     auto load_n = [&](u32x4(&dst)[C::NPT], int c) {
 #pragma unroll

@@ -214,15 +214,15 @@ def test_base_greedy_parity(M, name, dtype, R, H, V, layout):
 
 
 def _pack_layout(W):
-    """Row r, column k of a [rows][K] matrix -> element
-    ((r // 16) * (K // 32) + k // 32) * 512 + ((k % 32) // 8 * 16 + r % 16) * 8 + k % 8
+    """Row r, column k of a [rows][K] matrix of NRB = ceil(rows / 16) row blocks
+    -> element ((k // 32) * NRB + r // 16) * 512 + ((k % 32) // 8 * 16 + r % 16) * 8 + k % 8
     of the packed buffer (padding rows zero)."""
     rows, K = W.shape
-    rp = -(-rows // 16) * 16
-    out = np.zeros(rp * K, dtype=W.dtype)
+    nrb = -(-rows // 16)
+    out = np.zeros(nrb * 16 * K, dtype=W.dtype)
     r = np.arange(rows)[:, None]
     k = np.arange(K)[None, :]
-    idx = ((r // 16) * (K // 32) + k // 32) * 512 + ((k % 32) // 8 * 16 + r % 16) * 8 + k % 8
+    idx = ((k // 32) * nrb + r // 16) * 512 + ((k % 32) // 8 * 16 + r % 16) * 8 + k % 8
     out[idx.ravel()] = W.ravel()
     return out
 
