@@ -201,40 +201,37 @@ struct GemmSplit {
 };
 
 // Workgroup shape and splits of the contraction (whole k-chunks each, at most
-// 16), measured on the Llama-7B projections with 64 node rows:
-// * wide products (>= 8192 weight rows) stream best from 8-wave workgroups
-//   with as few splits as keep >= 160 workgroups in flight -- more waves per
-//   CU keep more weight bytes in flight, and every split costs a round trip
-//   of fp32 partial sums (q|k|v: 2 splits, gate|up: 1);
-// * narrow ones (o, down: 4096 rows) need 4-wave workgroups and the split
-//   count whose workgroups fill whole rounds of the 256 CUs best, discounted
-//   3% per extra split (4 splits).
+// 16), from a cost model measured on the Llama-7B projections with 64 node
+// rows: a product runs one workgroup per CU per round, so it takes about
+// rounds x (16-row weight blocks per workgroup) x (k-chunks per split), and
+// every split beyond the first costs ~3% more (its fp32 partial sums).  Over
+// 4, 6 and 8 waves per workgroup this picks q|k|v (768 blocks): 6 waves x 2
+// splits = 256 workgroups (23.4 us against 25.2 with 8 waves, which leave 64
+// CUs idle); gate|up (1376 blocks, unsplit for the SwiGLU epilogue): 6 waves,
+// 230 workgroups (37.2 us against 40.0 with 8 waves on 172 CUs); o and down
+// (256 blocks): 4 waves x 4 splits.  A split gate|up also needs its own SwiGLU
+// kernel: split_extra = 50 (about 5 us in the same units) is added to its cost,
+// so only narrow gate|up products with long rows split.
 constexpr int GPU_CUS = 256;
-constexpr int WIDE_PRODUCT_ROWS = 8192;
-constexpr int WIDE_MIN_WG = 160;
-static GemmSplit gemm_split(int R, int K, int ncols) {
+constexpr double GATE_UP_SPLIT_EXTRA = 50.0;
+static GemmSplit gemm_split(int R, int K, int ncols, double split_extra = 0.0) {
     const int nblk = lmh_nblk(R);
     const int nchunk = K / lmh_kc(nblk);
     const long long node_tiles = (R + nblk * 16 - 1) / (nblk * 16);
-    auto make = [&](int S, int waves) {
-        S = std::max(1, std::min(S, std::min(16, nchunk)));
-        const int cps = (nchunk + S - 1) / S;
-        return GemmSplit{(nchunk + cps - 1) / cps, cps, waves};
-    };
-    if (ncols >= WIDE_PRODUCT_ROWS) {
-        const long long tiles = (long long)((ncols + 16 * 8 - 1) / (16 * 8)) * node_tiles;
-        return make((int)((WIDE_MIN_WG + tiles - 1) / tiles), 8);
-    }
-    const long long tiles = (long long)((ncols + LMH_ROWS - 1) / LMH_ROWS) * node_tiles;
-    GemmSplit best = make(1, LMH_WAVES);
-    double best_score = -1.0;
-    for (int S = 1; S <= std::min(16, nchunk); ++S) {
-        const GemmSplit g = make(S, LMH_WAVES);
-        const double rounds = (double)(tiles * g.S) / GPU_CUS;
-        const double score = rounds / std::ceil(rounds) * (1.0 - 0.03 * (g.S - 1));
-        if (score > best_score + 1e-9) {
-            best_score = score;
-            best = g;
+    const long long nrb = (ncols + 15) / 16;
+    GemmSplit best{1, nchunk, LMH_WAVES};
+    double best_cost = -1.0;
+    for (int waves : {4, 6, 8}) {
+        for (int S = 1; S <= std::min(16, nchunk); ++S) {
+            const int cps = (nchunk + S - 1) / S;
+            const int Se = (nchunk + cps - 1) / cps;
+            const long long wgs = (nrb + waves - 1) / waves * node_tiles * Se;
+            const long long rounds = (wgs + GPU_CUS - 1) / GPU_CUS;
+            const double cost = (double)rounds * waves * cps * (1.0 + 0.03 * (Se - 1)) + (Se > 1 ? split_extra : 0.0);
+            if (best_cost < 0 || cost < best_cost - 1e-9) {
+                best_cost = cost;
+                best = GemmSplit{Se, cps, waves};
+            }
         }
     }
     return best;
@@ -251,6 +248,10 @@ static void launch_skinny_partial(const bf16_t* n, const bf16_t* w, int R, int K
         if (nblk == 4) SKINNY_PARTIAL_LAUNCH(4, 8);
         else if (nblk == 8) SKINNY_PARTIAL_LAUNCH(8, 8);
         else SKINNY_PARTIAL_LAUNCH(16, 8);
+    } else if (sp.waves == 6) {
+        if (nblk == 4) SKINNY_PARTIAL_LAUNCH(4, 6);
+        else if (nblk == 8) SKINNY_PARTIAL_LAUNCH(8, 6);
+        else SKINNY_PARTIAL_LAUNCH(16, 6);
     } else {
         if (nblk == 4) SKINNY_PARTIAL_LAUNCH(4, 4);
         else if (nblk == 8) SKINNY_PARTIAL_LAUNCH(8, 4);
@@ -272,6 +273,10 @@ static void launch_skinny_swiglu(const bf16_t* n, const bf16_t* w, int R, int K,
         if (nblk == 4) SKINNY_SWIGLU_LAUNCH(4, 8);
         else if (nblk == 8) SKINNY_SWIGLU_LAUNCH(8, 8);
         else SKINNY_SWIGLU_LAUNCH(16, 8);
+    } else if (sp.waves == 6) {
+        if (nblk == 4) SKINNY_SWIGLU_LAUNCH(4, 6);
+        else if (nblk == 8) SKINNY_SWIGLU_LAUNCH(8, 6);
+        else SKINNY_SWIGLU_LAUNCH(16, 6);
     } else {
         if (nblk == 4) SKINNY_SWIGLU_LAUNCH(4, 4);
         else if (nblk == 8) SKINNY_SWIGLU_LAUNCH(8, 4);
@@ -294,8 +299,8 @@ struct DecoderWs {
 static size_t partial_floats(int R, int H, int nH, int nKV, int D, int F) {
     size_t m = 0;
     const int qkv = (nH + 2 * nKV) * D;
-    const GemmSplit a = gemm_split(R, H, qkv), b = gemm_split(R, nH * D, H), c = gemm_split(R, H, 2 * F),
-                    d = gemm_split(R, F, H);
+    const GemmSplit a = gemm_split(R, H, qkv), b = gemm_split(R, nH * D, H),
+                    c = gemm_split(R, H, 2 * F, GATE_UP_SPLIT_EXTRA), d = gemm_split(R, F, H);
     m = std::max(m, (size_t)a.S * R * qkv);
     m = std::max(m, (size_t)b.S * R * H);
     m = std::max(m, (size_t)c.S * R * 2 * F);
@@ -347,7 +352,7 @@ void launch_decoder_verify(const LayerPtrs* layers, int n_layers, const bf16_t* 
     const DecoderWs w = carve(ws, B, N, H, nH, nKV, D, F, max_cache_len);
     const int qkv = (nH + 2 * nKV) * D;
     const GemmSplit sp_qkv = gemm_split(R, H, qkv), sp_o = gemm_split(R, nH * D, H),
-                    sp_gu = gemm_split(R, H, 2 * F), sp_d = gemm_split(R, F, H);
+                    sp_gu = gemm_split(R, H, 2 * F, GATE_UP_SPLIT_EXTRA), sp_d = gemm_split(R, F, H);
     const float scale = 1.0f / sqrtf((float)D);
     const double log2_base = log2((double)rope_base);
     const int ew_blocks = 1024;

@@ -59,9 +59,10 @@ struct LmhCfg {
     static constexpr int KC = NBLK == 1 ? NT / 2 : NBLK <= 8 ? 64 : 32;
     static constexpr int KS = KC / PACK_K;             // MFMA k-steps per chunk
     static constexpr int LDW = KC + 8;                 // padded LDS row (bf16): conflict-free B reads
-    static constexpr int NPT = NODES * KC / 8 / NT;    // 16-byte node pieces per thread per chunk
+    static constexpr int PIECES = NODES * KC / 8;           // 16-byte node pieces per chunk
+    static constexpr int NPT = (PIECES + NT - 1) / NT;     // per thread (the last round may be partial)
+    static constexpr bool EVEN = NPT * NT == PIECES;
     static constexpr int D = NBLK == 1 && WAVES > 4 ? 3 : NBLK <= 4 ? 4 : 3;  // chunks in flight per ring
-    static_assert(NPT * NT * 8 == NODES * KC, "node stage must split evenly over the threads");
 };
 
 // Pipeline (one barrier per chunk): step c issues the node rows and then the
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
     int k8p[C::NPT];
 #pragma unroll
     for (int e = 0; e < C::NPT; ++e) {
-        const int p = tid + e * NT;
+        const int p = min(tid + e * NT, C::PIECES - 1);  // past the stage: re-read the last piece, not stored
         const int r = p / (C::KC / 8);
         k8p[e] = p - r * (C::KC / 8);
         nrow[e] = n + (size_t)min(node0 + r, R - 1) * K;
@@ -154,8 +155,8 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
     auto store_n = [&](const u32x4(&src)[C::NPT], int stage) {
 #pragma unroll
         for (int e = 0; e < C::NPT; ++e) {
-            const int r = (tid + e * NT) / (C::KC / 8);
-            *(u32x4*)(&ns[stage][r][k8p[e] * 8]) = src[e];
+            const int p = tid + e * NT;
+            if (C::EVEN || p < C::PIECES) *(u32x4*)(&ns[stage][p / (C::KC / 8)][k8p[e] * 8]) = src[e];
         }
     };
 

@@ -23,7 +23,8 @@ scores is about one standard deviation of the noise on their difference.  The
 margin enforced for the full-width case is 0.1 (above twice the largest
 measured move); the narrow cases keep 1e-2.  The greedy choices must then
 match exactly.  Cases span the 64-, 128- and 256-row
-tile shapes of the projections, GQA, ragged cache lengths, and two layers at
+tile shapes of the projections, GQA, ragged cache lengths, a gate|up product
+split over its contraction, and two layers at
 the full Llama-7B width (hidden 4096, 32 x 128 heads, MLP 11008, vocabulary
 32000, 4096-token caches, sparse 64-node tree).
 """
@@ -62,6 +63,9 @@ CASES = [
     ("rows128_b2_sparse64", lambda: _cfg("d3", 2, 256, 777, mi.sparse_tree(64), 2, 2, 128, (0, 33), 503, 2, 384)),
     ("rows256_dense256", lambda: _cfg("d4", 1, 512, 3001, mi.dense_tree(256), 8, 8, 64, (64,), 504, 1, 320)),
     ("full_width_2layers", lambda: _cfg("d5", 1, 4096, 32000, mi.sparse_tree(64), 32, 32, 128, (4096,), 505, 2, 11008)),
+    # a narrow MLP under long rows: the gate|up product splits its contraction
+    # (fp32 partial sums, then the separate SwiGLU kernel)
+    ("split_gate_up_h2048_f128", lambda: _cfg("d6", 1, 2048, 1000, mi.sparse_tree(24), 16, 16, 128, (64,), 506, 1, 128)),
 ]
 # margin between each node's best two lm_head scores
 MARGIN = {"full_width_2layers": 0.1}
