@@ -61,10 +61,18 @@ __global__ __launch_bounds__(64) void argmax_merge_kernel(const float* __restric
     const int r = blockIdx.x;
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
-    for (int g = threadIdx.x; g < G; g += 64) {
-        const float v = cand_val[(size_t)r * G + g];
-        const int i = cand_idx[(size_t)r * G + g];
-        if (better(v, i, bv, bi)) { bv = v; bi = i; }
+    for (int g0 = threadIdx.x; g0 < G; g0 += 4 * 64) {  // four loads in flight per thread
+        float v[4];
+        int i[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int g = g0 + u * 64;
+            v[u] = g < G ? cand_val[(size_t)r * G + g] : -INFINITY;
+            i[u] = g < G ? cand_idx[(size_t)r * G + g] : 0x7FFFFFFF;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (better(v[u], i[u], bv, bi)) { bv = v[u]; bi = i[u]; }
     }
     wave_argmax(bv, bi);
     if (threadIdx.x == 0) greedy[r] = bi;

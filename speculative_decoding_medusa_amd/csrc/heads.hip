@@ -204,7 +204,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_rows_kernel(
 
 // Final merge: per (b, k) the top-k of the G * topk workgroup candidates.
 // Each thread keeps a sorted register list of the best TK candidates it reads
-// (loads issued four at a time); the block then extracts the winners one rank
+// (loads issued eight at a time: one round for up to 2048 candidates); the block then extracts the winners one rank
 // at a time: block-wide argmax of the threads' list heads, the winning thread
 // pops its head.  Candidate rows are distinct (padding entries rank last), so
 // the (value desc, index asc) order is total.
@@ -223,17 +223,17 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(const float* __restrict
     int li[TK];
 #pragma unroll
     for (int t = 0; t < TK; ++t) { lv[t] = -INFINITY; li[t] = 0x7FFFFFFF; }
-    for (int m0 = tid; m0 < M; m0 += 4 * 256) {
-        float v[4];
-        int i[4];
+    for (int m0 = tid; m0 < M; m0 += 8 * 256) {
+        float v[8];
+        int i[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 8; ++u) {
             const int m = m0 + u * 256;
             v[u] = m < M ? cv[m] : -INFINITY;
             i[u] = m < M ? ci[m] : 0x7FFFFFFF;
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) sorted_insert<TK>(lv, li, v[u], i[u]);
+        for (int u = 0; u < 8; ++u) sorted_insert<TK>(lv, li, v[u], i[u]);
     }
     for (int t = 0; t < topk; ++t) {
         float bv = lv[0];

@@ -7,32 +7,47 @@ namespace medusa {
 
 // node_tok[b][i] = root for i = 0, else topk_idx[b][depth-1][rank];
 // node_pos[b][i] = cache_len[b] + depth.  Block b also copies the ancestor
-// mask when b == 0.
+// mask when b == 0.  Every global load is issued before the one barrier:
+// the candidates the tree can use (heads 1 .. max_depth, ranks 0 ..
+// max_rank; at most 16 x 16) are staged in LDS, so no load waits on another.
 __global__ __launch_bounds__(256) void build_tree_kernel(const int* __restrict__ depth,
                                                          const int* __restrict__ rank,
                                                          const uint64_t* __restrict__ mask, int N, int W,
-                                                         const int32_t* __restrict__ topk_idx, int K, int topk,
-                                                         const int32_t* __restrict__ root_tok,
+                                                         int max_depth, int max_rank,
+                                                         const int32_t* __restrict__ topk_idx,
+                                                         int K, int topk, const int32_t* __restrict__ root_tok,
                                                          const int32_t* __restrict__ cache_len,
                                                          int32_t* __restrict__ node_tok,
                                                          int32_t* __restrict__ node_pos,
                                                          uint64_t* __restrict__ anc_mask) {
+    __shared__ int tk[MEDUSA_MAX_DEPTH_DEV * MEDUSA_MAX_TOPK_DEV];
     const int b = blockIdx.x;
-    for (int i = threadIdx.x; i < N; i += blockDim.x) {
-        const int d = depth[i];
-        node_tok[(size_t)b * N + i] =
-            d == 0 ? root_tok[b] : topk_idx[((size_t)b * K + (d - 1)) * topk + rank[i]];
-        node_pos[(size_t)b * N + i] = cache_len[b] + d;
+    const int tid = threadIdx.x;
+    const int cols = max_rank + 1;  // K >= max_depth and topk > max_rank (checked on the host)
+    for (int e = tid; e < max_depth * cols; e += blockDim.x) {
+        const int r = e / cols, c = e - r * cols;
+        tk[e] = topk_idx[((size_t)b * K + r) * topk + c];
     }
+    const int root = root_tok[b];
+    const int P = cache_len[b];
+    // N <= 256 nodes: one per thread
+    const int d = tid < N ? depth[tid] : 0;
+    const int rk = tid < N ? rank[tid] : 0;
     if (b == 0 && anc_mask != nullptr)
-        for (int i = threadIdx.x; i < N * W; i += blockDim.x) anc_mask[i] = mask[i];
+        for (int i = tid; i < N * W; i += blockDim.x) anc_mask[i] = mask[i];
+    __syncthreads();
+    if (tid < N) {
+        node_tok[(size_t)b * N + tid] = d == 0 ? root : tk[(d - 1) * cols + rk];
+        node_pos[(size_t)b * N + tid] = P + d;
+    }
 }
 
 void launch_build_tree(const TreeDev& t, const int32_t* topk_idx, int K, int topk, const int32_t* root_tok,
                        const int32_t* cache_len, int B, int32_t* node_tok, int32_t* node_pos,
                        uint64_t* anc_mask, hipStream_t s) {
     MEDUSA_LAUNCH("build_tree", build_tree_kernel, dim3(B), dim3(256), 0, s, t.depth, t.rank, t.mask, t.N,
-                  t.W, topk_idx, K, topk, root_tok, cache_len, node_tok, node_pos, anc_mask);
+                  t.W, t.max_depth, t.max_rank, topk_idx, K, topk, root_tok, cache_len, node_tok, node_pos,
+                  anc_mask);
 }
 
 // ---------------------------------------------------------------------------
@@ -52,27 +67,39 @@ __global__ __launch_bounds__(256) void accept_compact_kernel(
     const int32_t* __restrict__ cache_len, int32_t* __restrict__ new_cache_len, T* __restrict__ k_cache,
     T* __restrict__ v_cache, int nKV, int D, int Lmax, int64_t layer_stride, int n_slices) {
     __shared__ int s_acc_depth[256];
+    __shared__ int s_par[256], s_tok[256], s_g[256];
     __shared__ int s_path[MEDUSA_MAX_DEPTH_DEV + 1];
     __shared__ int s_L, s_deepest;
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     const int32_t* tok = node_tok + (size_t)b * N;
     const int32_t* g = greedy + (size_t)b * N;
+    const int P = cache_len[b];
 
+    // the sequence's nodes (N <= 256, one per thread) -> LDS in one round of
+    // loads, so the walks below read no global memory
+    int dep = 0;
+    if (tid < N) {
+        s_par[tid] = parent[tid];
+        s_tok[tid] = tok[tid];
+        s_g[tid] = g[tid];
+        dep = depth[tid];
+    }
+    if (tid == 0) { s_L = 0; s_deepest = 0; }
+    __syncthreads();
     // accepted iff every node on the chain to the root matches its parent's choice
     int my = -1;
     if (tid < N) {
         bool ok = true;
         int j = tid;
         while (j > 0) {
-            const int p = parent[j];
-            ok = ok && (tok[j] == g[p]);
+            const int p = s_par[j];
+            ok = ok && (s_tok[j] == s_g[p]);
             j = p;
         }
-        my = ok ? depth[tid] : -1;
+        my = ok ? dep : -1;
     }
-    if (tid < 256) s_acc_depth[tid] = my;
-    if (tid == 0) { s_L = 0; s_deepest = 0; }
+    s_acc_depth[tid] = my;
     __syncthreads();
     // deepest accepted depth, then the lowest node index at that depth
     if (tid == 0) {
@@ -82,18 +109,17 @@ __global__ __launch_bounds__(256) void accept_compact_kernel(
         s_L = L;
         s_deepest = deepest;
         int j = deepest;
-        for (int d = L; d >= 0; --d) { s_path[d] = j; j = d > 0 ? parent[j] : 0; }
+        for (int d = L; d >= 0; --d) { s_path[d] = j; j = d > 0 ? s_par[j] : 0; }
     }
     __syncthreads();
     const int L = s_L;
-    const int P = cache_len[b];
 
     if (blockIdx.y == 0 && tid <= Dmax) {
         const int d = tid;
         const size_t o = (size_t)b * (Dmax + 1) + d;
         if (d <= L) {
             accept_nodes[o] = s_path[d];
-            out_tokens[o] = d < L ? tok[s_path[d + 1]] : g[s_deepest];
+            out_tokens[o] = d < L ? s_tok[s_path[d + 1]] : s_g[s_deepest];
         } else {
             accept_nodes[o] = -1;
             out_tokens[o] = -1;
