@@ -37,3 +37,4 @@ tests/test_oracle_*.py.
 from .medusa import *  # noqa: F401,F403
 from .cost import *    # noqa: F401,F403
 from .decoder import *  # noqa: F401,F403
+from .generate import *  # noqa: F401,F403
