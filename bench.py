@@ -72,6 +72,9 @@ def parse():
                     help="workload index (2: 7B sparse-64, 3: dense-256, 4: batched, 5: 32-layer decoder verify)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay the step as a captured HIP graph")
+    ap.add_argument("--loop", type=int, default=0, metavar="ROUNDS",
+                    help="with --config 5: time ROUNDS rounds of the device-resident generate loop (MedusaLoop), "
+                         "eager and as one captured graph, and print that line instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device-to-device copies of MIB MiB (scale for HBM byte counters)")
     return ap.parse_args()
@@ -112,6 +115,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     cfg = mi.config(args.config)
+    if args.loop:
+        assert cfg.layers, "--loop runs the decoder workload (--config 5)"
+        return bench_loop(args, cfg)
     if cfg.layers:
         return bench_decoder(args, cfg)
     dt_str = cfg.dtype
@@ -448,6 +454,122 @@ def bench_decoder(args, cfg):
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_decoder(cfg, heads)
+    print(json.dumps(result), flush=True)
+
+
+def bench_loop(args, cfg):
+    """ROUNDS rounds of the generate loop on the 32-layer workload: heads ->
+    tree -> decoder verify -> accept with compaction -> hand-off, nothing
+    waiting for the host.  The caches are the workload's; the rounds start
+    (Dmax + 1) * ROUNDS tokens before the workload's prefix length, so every
+    round fits the caches.  Timed eagerly and as one captured graph of all
+    ROUNDS rounds, each from the same initial state."""
+    import numpy as np
+    import torch
+
+    import medusa_inputs as mi
+    import speculative_decoding_medusa_amd as M
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16 else torch.from_numpy(a)
+        return t.cuda()
+
+    R = args.loop
+    B, K, H, N, topk, L = cfg.B, cfg.K, cfg.H, cfg.N, cfg.topk, cfg.layers
+    parent, rank = cfg.tree.arrays()
+    tree = M.Tree(parent, rank, K, topk)
+    P0 = np.asarray(cfg.P, dtype=np.int32) - (tree.max_depth + 1) * R
+    assert P0.min() >= 0, "too many rounds for the workload's prefix"
+    heads = mi.gen_heads(cfg)
+    d = {k: dev(v) for k, v in heads.items()}
+    layers = []
+    k_cache = torch.empty(L, B, cfg.nKV, cfg.Lmax, cfg.D, dtype=torch.bfloat16, device="cuda")
+    v_cache = torch.empty_like(k_cache)
+    for l in range(L):
+        W = mi.gen_layer(cfg, l)
+        layers.append(M.pack_layer({m: dev(W[m]) for m in W}))
+        del W
+        kc, vc = mi.gen_layer_cache(cfg, l)
+        k_cache[l].copy_(dev(kc))
+        v_cache[l].copy_(dev(vc))
+        del kc, vc
+    emb = dev(mi.gen_embedding(cfg))
+    lm_head = M.pack(d.pop("lm_head"))
+    state = dict(cache_len=dev(P0), h=d["h"].clone(), root_tok=dev(mi.gen_root_tokens(cfg)))
+    loop = M.MedusaLoop({"w1": d["W1"], "b1": d["b1"], "w2": d["W2"]}, layers, emb, lm_head, tree, topk, k_cache,
+                        v_cache, cfg.nH, state["cache_len"].clone(), state["h"].clone(), state["root_tok"].clone(),
+                        max_cache_len=int(max(cfg.P)), cap=(tree.max_depth + 1) * R)
+    # only the accepted slots [P0, P0 + R (Dmax + 1)) change: keep them to restore the initial state
+    lo, hi = int(P0.min()), int(max(cfg.P)) + N
+    keep_k, keep_v = k_cache[..., lo:hi, :].clone(), v_cache[..., lo:hi, :].clone()
+
+    def restore():
+        k_cache[..., lo:hi, :].copy_(keep_k)
+        v_cache[..., lo:hi, :].copy_(keep_v)
+        loop.cache_len.copy_(state["cache_len"])
+        loop.h.copy_(state["h"])
+        loop.root_tok.copy_(state["root_tok"])
+        loop.n_tokens.zero_()
+
+    loop.run(min(R, 2))       # warm the launch paths
+    restore()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    loop.run(R)
+    e1.record()
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1)
+    n_eager = loop.n_tokens.cpu().numpy().copy()
+    tokens_eager = loop.tokens.cpu().numpy().copy()
+
+    restore()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        loop.run(R)
+    torch.cuda.synchronize()
+    restore()
+    torch.cuda.synchronize()
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_ms = e0.elapsed_time(e1)
+    n_graph = loop.n_tokens.cpu().numpy()
+    same = bool(np.array_equal(n_graph, n_eager) and np.array_equal(loop.tokens.cpu().numpy(), tokens_eager))
+
+    # tokens per round if the heads' guesses were right with the tree's prior
+    # (rank r at any depth right with probability 0.8 * 0.2^r): 1 + the sum
+    # over candidates of the product of the priors along their path
+    depth = np.zeros(N, dtype=int)
+    prob = np.ones(N)
+    for i in range(1, N):
+        depth[i] = depth[parent[i]] + 1
+        prob[i] = prob[parent[i]] * mi.rank_prior(0.8, int(rank[i]))
+    expected = 1.0 + float(prob[1:].sum())
+    rounds_s = R / (graph_ms * 1e-3)
+    result = {
+        "metric": "Medusa generate rounds/sec (32-layer Llama-7B-shaped decoder, device-resident loop)",
+        "value": round(rounds_s, 2),
+        "unit": "rounds/s",
+        "n_gpus": 1,
+        "rounds": R,
+        "higher_is_better": True,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Philox inputs, random-init weights)",
+        "config": {"workload": cfg.name + "_loop", "batch": B, "tree_nodes": N, "decoder_layers": L,
+                   "start_prefix": P0.tolist(), "max_prefix": [int(p) for p in cfg.P]},
+        "ms_per_round_graph": round(graph_ms / R, 4),
+        "ms_per_round_eager": round(eager_ms / R, 4),
+        "graph_replay_matches_eager": same,
+        "tokens_per_round_measured": round(float(n_graph.sum()) / (B * R), 3),
+        "tokens_per_s_measured": round(float(n_graph.sum()) / (graph_ms * 1e-3), 1),
+        "tokens_per_round_under_tree_prior": round(expected, 3),
+        "tokens_per_s_under_tree_prior": round(B * rounds_s * expected, 1),
+    }
     print(json.dumps(result), flush=True)
 
 

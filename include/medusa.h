@@ -244,6 +244,32 @@ medusa_status medusa_accept(const medusa_tree* tree, const int32_t* node_tok, co
                             int nKV, int D, int Lmax, medusa_dtype dt, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * The loop around the step -- hand-off of the accepted branch to the next
+ * round (tree section: the final state of the longest accepted branch feeds
+ * the heads next round; e-book, section on why a round always yields k + 1
+ * tokens: the extra token the base model chose after the last accepted one).
+ * With L = accept_len[b] and the node path accept_nodes[b] from medusa_accept
+ * (Dmax = the tree's maximum depth):
+ *   root_tok [B] (out) = out_tokens[b][L]: the bonus token, next tree's root;
+ *   h [B][H] (out, dt; bf16 rounds to nearest even) = hidden[b][accept_nodes[b][L]]:
+ *     the final normalised state at the deepest accepted node, which the
+ *     heads read next round (hidden [B][N][H] float32: medusa_decoder_verify's
+ *     optional output);
+ *   tokens [B][cap], n_tokens [B] (optional, both or neither): the round's
+ *     L + 1 tokens out_tokens[b][0..L] are written at tokens[b][n_tokens[b] ..]
+ *     (indices >= cap are dropped) and n_tokens[b] grows by L + 1;
+ *   new_cache_len, cache_len [B] (optional, both or neither): cache_len[b] =
+ *     new_cache_len[b], so the next round reads its prefix length from the
+ *     buffer this round's medusa_accept read (the two may not alias there).
+ * A sequence whose L is outside [0, Dmax] or whose node is outside [0, N) is
+ * left unchanged.  One kernel; no workspace.
+ * ------------------------------------------------------------------------- */
+medusa_status medusa_advance(const medusa_tree* tree, const int32_t* accept_len, const int32_t* accept_nodes,
+                             const int32_t* out_tokens, const float* hidden, int B, int H, medusa_dtype dt,
+                             int32_t* root_tok, void* h, int32_t* tokens, int32_t* n_tokens, int cap,
+                             const int32_t* new_cache_len, int32_t* cache_len, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Step a8 -- the tree-verify forward pass through a Llama-shaped decoder
  * ("Medusa Heads" glossary, section on tree attention and acceptance: every
  * candidate is appended to the input of one forward pass of the base model,

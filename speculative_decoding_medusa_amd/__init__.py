@@ -51,6 +51,7 @@ _SIGS = {
     "medusa_base_greedy": ([_vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
     "medusa_accept": ([_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32,
                        _vp], _i32),
+    "medusa_advance": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp], _i32),
     "medusa_decoder_workspace_size": ([_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32], _sz),
     "medusa_decoder_verify": ([_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
                                _i32, _i32, _i32, _i32, _f32, _f32, _vp, _vp, _vp, _sz, _vp], _i32),
@@ -341,6 +342,20 @@ def medusa_accept(tree: Tree, node_tok, greedy, accept_len, accept_nodes, out_to
     return accept_len
 
 
+def medusa_advance(tree: Tree, accept_len, accept_nodes, out_tokens, hidden, root_tok, h, tokens=None,
+                   n_tokens=None, new_cache_len=None, cache_len=None, stream=None):
+    """Hand the accepted branch to the next round: root_tok <- the bonus token,
+    h <- hidden at the deepest accepted node (in h's dtype), optionally append
+    the round's tokens to tokens [B][cap] at n_tokens and copy new_cache_len
+    into cache_len."""
+    B, H = h.shape
+    cap = tokens.shape[1] if tokens is not None else 0
+    _check("medusa_advance", _lib.medusa_advance(
+        tree.handle, _p(accept_len), _p(accept_nodes), _p(out_tokens), _p(hidden), B, H, _dt(h), _p(root_tok),
+        _p(h), _p(tokens), _p(n_tokens), cap, _p(new_cache_len), _p(cache_len), _stream(stream)))
+    return root_tok
+
+
 # ---------------------------------------------------------------------------
 # a8
 # ---------------------------------------------------------------------------
@@ -409,3 +424,6 @@ def profiler_collect() -> dict:
         _check("medusa_profiler_stat", _lib.medusa_profiler_stat(i, name, 128, ctypes.byref(calls), ctypes.byref(ms)))
         out[name.value.decode()] = (calls.value, ms.value)
     return out
+
+
+from .generate import MedusaLoop  # noqa: E402  (the loop helper builds on the calls above)

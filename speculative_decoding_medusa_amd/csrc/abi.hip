@@ -52,6 +52,10 @@ void launch_accept(const TreeDev& t, const int32_t* node_tok, const int32_t* gre
 struct LayerPtrs {
     const bf16_t *wqkv, *wo, *w_gate_up, *w_down;
 };
+void launch_advance(const TreeDev& t, const int32_t* accept_len, const int32_t* accept_nodes,
+                    const int32_t* out_tokens, const float* hidden, int B, int H, bool bf16, int32_t* root_tok,
+                    void* h, int32_t* tokens, int32_t* n_tokens, int cap, const int32_t* new_cache_len,
+                    int32_t* cache_len, hipStream_t s);
 size_t packed_elems(int rows, int K);
 void launch_pack_rows(const bf16_t* src, int rows, int K, bf16_t* dst, int dst_row0, int dst_rows, int inter,
                       hipStream_t s);
@@ -516,6 +520,26 @@ medusa_status medusa_accept(const medusa_tree* tree, const int32_t* node_tok, co
         launch_accept(tree->t, node_tok, greedy, B, accept_len, accept_nodes, out_tokens, cache_len, new_cache_len,
                       k_cache, v_cache, n_layers, layer_stride_elems, nKV, D, Lmax, dt == MEDUSA_BF16,
                       (hipStream_t)stream);
+    });
+}
+
+// ---------------------------------------------------------------------------
+// hand-off to the next round
+// ---------------------------------------------------------------------------
+medusa_status medusa_advance(const medusa_tree* tree, const int32_t* accept_len, const int32_t* accept_nodes,
+                             const int32_t* out_tokens, const float* hidden, int B, int H, medusa_dtype dt,
+                             int32_t* root_tok, void* h, int32_t* tokens, int32_t* n_tokens, int cap,
+                             const int32_t* new_cache_len, int32_t* cache_len, void* stream) {
+    return guarded("medusa_advance", [&] {
+        REQUIRE(tree && accept_len && accept_nodes && out_tokens && hidden && root_tok && h, "null pointer argument");
+        REQUIRE(B >= 1 && H >= 1, "B and H must be positive (B=%d H=%d)", B, H);
+        REQUIRE(dt == MEDUSA_F32 || dt == MEDUSA_BF16, "bad dtype");
+        REQUIRE((tokens == nullptr) == (n_tokens == nullptr), "tokens and n_tokens must both be given or both NULL");
+        REQUIRE(tokens == nullptr || cap >= 1, "cap=%d must be >= 1 when tokens are appended", cap);
+        REQUIRE((new_cache_len == nullptr) == (cache_len == nullptr),
+                "new_cache_len and cache_len must both be given or both NULL");
+        launch_advance(tree->t, accept_len, accept_nodes, out_tokens, hidden, B, H, dt == MEDUSA_BF16, root_tok, h,
+                       tokens, n_tokens, cap, new_cache_len, cache_len, (hipStream_t)stream);
     });
 }
 

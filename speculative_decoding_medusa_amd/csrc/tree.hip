@@ -180,4 +180,55 @@ void launch_accept(const TreeDev& t, const int32_t* node_tok, const int32_t* gre
                       new_cache_len, (float*)k_cache, (float*)v_cache, nKV, D, Lmax, layer_stride, n_slices);
 }
 
+// ---------------------------------------------------------------------------
+// Hand-off to the next round.  Block b reads sequence b's L and deepest
+// accepted node (uniform over the block), gathers that node's final
+// normalised row into h[b] (converted to T), sets the next root to the bonus
+// token, appends the round's L + 1 tokens to the sequence's output and, when
+// asked, copies the new cache length into the buffer the next round reads.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void advance_kernel(const int32_t* __restrict__ accept_len,
+                                                      const int32_t* __restrict__ accept_nodes,
+                                                      const int32_t* __restrict__ out_tokens,
+                                                      const float* __restrict__ hidden, int N, int Dmax, int H,
+                                                      int32_t* __restrict__ root_tok, T* __restrict__ h,
+                                                      int32_t* __restrict__ tokens, int32_t* __restrict__ n_tokens,
+                                                      int cap, const int32_t* __restrict__ new_cache_len,
+                                                      int32_t* __restrict__ cache_len) {
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int L = accept_len[b];
+    if (L < 0 || L > Dmax) return;  // not a medusa_accept result: leave the sequence unchanged
+    const size_t row = (size_t)b * (Dmax + 1);
+    const int node = accept_nodes[row + L];
+    if (node < 0 || node >= N) return;
+    const float* src = hidden + ((size_t)b * N + node) * H;
+    for (int j = tid; j < H; j += blockDim.x) Elem<T>::store(h, (size_t)b * H + j, src[j]);
+    if (tid == 0) {
+        root_tok[b] = out_tokens[row + L];
+        if (cache_len != nullptr) cache_len[b] = new_cache_len[b];
+    }
+    if (tokens != nullptr) {
+        const int n0 = n_tokens[b];
+        __syncthreads();  // every thread has read n0 before it is advanced
+        if (tid <= L && n0 >= 0 && n0 + tid < cap) tokens[(size_t)b * cap + n0 + tid] = out_tokens[row + tid];
+        if (tid == 0) n_tokens[b] = n0 + L + 1;
+    }
+}
+
+void launch_advance(const TreeDev& t, const int32_t* accept_len, const int32_t* accept_nodes,
+                    const int32_t* out_tokens, const float* hidden, int B, int H, bool bf16, int32_t* root_tok,
+                    void* h, int32_t* tokens, int32_t* n_tokens, int cap, const int32_t* new_cache_len,
+                    int32_t* cache_len, hipStream_t s) {
+    if (bf16)
+        MEDUSA_LAUNCH("advance", advance_kernel<bf16_t>, dim3(B), dim3(256), 0, s, accept_len, accept_nodes,
+                      out_tokens, hidden, t.N, t.max_depth, H, root_tok, (bf16_t*)h, tokens, n_tokens, cap,
+                      new_cache_len, cache_len);
+    else
+        MEDUSA_LAUNCH("advance", advance_kernel<float>, dim3(B), dim3(256), 0, s, accept_len, accept_nodes,
+                      out_tokens, hidden, t.N, t.max_depth, H, root_tok, (float*)h, tokens, n_tokens, cap,
+                      new_cache_len, cache_len);
+}
+
 }  // namespace medusa

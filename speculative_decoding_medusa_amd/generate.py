@@ -1,0 +1,89 @@
+"""Device-resident generate loop around the Medusa step on the Llama-shaped
+decoder.
+
+A round runs the heads on h, builds the candidate tree from their top-k,
+verifies every candidate in one pass through the decoder, keeps the longest
+branch the base model agrees with (compacting every layer's cache) and hands
+that branch to the next round: the bonus token becomes the root and the
+hidden state at the deepest accepted node becomes h ("Medusa Heads" glossary,
+section on tree attention and acceptance; the speculative-decoding e-book,
+section on why a round yields the accepted tokens plus one).  Every round is
+a fixed sequence of library calls on one stream that never waits for the
+host, so a run of rounds can be captured in a HIP graph and replayed.
+
+Only argument marshalling happens here; every step runs in libmedusa.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (Packed, Tree, _ws, decoder_workspace_size, heads_workspace_size, medusa_accept, medusa_advance,
+               medusa_build_tree, medusa_decoder_verify, medusa_heads_forward, ROW_MAJOR, PACKED, BF16, F32)
+
+
+class MedusaLoop:
+    """State and buffers of the loop for B sequences.
+
+    heads: dict(w1, b1, w2) as medusa_heads_forward takes them (row-major
+    tensors or pack_heads results); layers: pack_layer() dicts; embedding
+    [V][H] bf16; lm_head: Packed [V][H]; k_cache, v_cache [layers][B][nKV][Lmax][D]
+    bf16 holding each sequence's prefix; cache_len [B] int32 (device);
+    h [B][H] (the heads' dtype) and root_tok [B] int32: the state the first
+    round starts from.  max_cache_len bounds every prefix length the rounds
+    reach (default Lmax - N: any state the caches can hold).  tokens [B][cap]
+    collects every round's output; n_tokens [B] counts it."""
+
+    def __init__(self, heads, layers, embedding, lm_head: Packed, tree: Tree, topk: int, k_cache, v_cache, nH: int,
+                 cache_len, h, root_tok, max_cache_len: int | None = None, cap: int = 1024, rms_eps: float = 1e-6,
+                 rope_base: float = 10000.0):
+        dev = h.device
+        self.heads, self.layers, self.embedding, self.lm_head, self.tree = heads, layers, embedding, lm_head, tree
+        self.topk, self.nH, self.rms_eps, self.rope_base = topk, nH, rms_eps, rope_base
+        self.k_cache, self.v_cache = k_cache, v_cache
+        self.cache_len, self.h, self.root_tok = cache_len, h, root_tok
+        n_layers, B, nKV, Lmax, D = k_cache.shape
+        N, Dmax = tree.N, tree.max_depth
+        V, H = embedding.shape
+        w2 = heads["w2"]
+        K = w2.heads if isinstance(w2, Packed) else w2.shape[0]
+        self.B, self.N, self.K = B, N, K
+        self.max_cache_len = Lmax - N if max_cache_len is None else int(max_cache_len)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.topk_idx = torch.empty(B, K, topk, **i32)
+        self.topk_val = torch.empty(B, K, topk, dtype=torch.float32, device=dev)
+        self.node_tok = torch.empty(B, N, **i32)
+        self.node_pos = torch.empty(B, N, **i32)
+        self.greedy = torch.empty(B, N, **i32)
+        self.hidden = torch.empty(B, N, H, dtype=torch.float32, device=dev)
+        self.accept_len = torch.empty(B, **i32)
+        self.accept_nodes = torch.empty(B, Dmax + 1, **i32)
+        self.out_tokens = torch.empty(B, Dmax + 1, **i32)
+        self.new_cache_len = torch.empty(B, **i32)
+        self.tokens = torch.full((B, cap), -1, **i32)
+        self.n_tokens = torch.zeros(B, **i32)
+        layout = PACKED if isinstance(w2, Packed) else ROW_MAJOR
+        dt = BF16 if h.dtype == torch.bfloat16 else F32
+        self.ws_heads = _ws(heads_workspace_size(B, H, V, K, topk, dt, layout), dev, None)
+        F = layers[0]["w_gate_up"].rows // 2
+        self.ws_dec = _ws(decoder_workspace_size(tree, B, H, nH, nKV, D, F, V, self.max_cache_len), dev, None)
+
+    def round(self, stream=None):
+        """One round on `stream` (torch's current stream if None)."""
+        hd = self.heads
+        medusa_heads_forward(self.h, hd.get("w1"), hd.get("b1"), hd["w2"], self.topk, self.topk_idx, self.topk_val,
+                             ws=self.ws_heads, stream=stream)
+        medusa_build_tree(self.tree, self.topk_idx, self.root_tok, self.cache_len, self.node_tok, self.node_pos,
+                          stream=stream)
+        medusa_decoder_verify(self.layers, self.embedding, self.lm_head, self.tree, self.node_tok, self.node_pos,
+                              self.cache_len, self.max_cache_len, self.k_cache, self.v_cache, self.nH, self.greedy,
+                              hidden=self.hidden, rms_eps=self.rms_eps, rope_base=self.rope_base, ws=self.ws_dec,
+                              stream=stream)
+        medusa_accept(self.tree, self.node_tok, self.greedy, self.accept_len, self.accept_nodes, self.out_tokens,
+                      self.cache_len, self.new_cache_len, k_cache=self.k_cache, v_cache=self.v_cache, stream=stream)
+        medusa_advance(self.tree, self.accept_len, self.accept_nodes, self.out_tokens, self.hidden, self.root_tok,
+                       self.h, tokens=self.tokens, n_tokens=self.n_tokens, new_cache_len=self.new_cache_len,
+                       cache_len=self.cache_len, stream=stream)
+
+    def run(self, rounds: int, stream=None):
+        for _ in range(rounds):
+            self.round(stream)
