@@ -207,19 +207,26 @@ __global__ __launch_bounds__(ATT_MERGE_THREADS) void tree_attn_merge_kernel(cons
 // ---------------------------------------------------------------------------
 // bf16 MFMA variant.
 //
-// Work split: a workgroup holds MF_Q = 64 tree queries of one head and one key
-// range.  Ranges 0..S-2 each cover KPS consecutive prefix keys (cache slots);
-// range S-1 is the N tree keys, read from k_tree / v_tree under the ancestor
-// mask.  The tree range's workgroup of query block 0 also copies the tree
-// keys/values into cache slots P..P+N-1 (no other workgroup reads those
-// slots).  For N > 64 the query blocks of one key range get linear workgroup
-// ids 8 apart: workgroups are dealt to the 8 XCDs round-robin, so the blocks
-// land on one XCD and read the range's K/V through the same L2.
+// Work split: a workgroup holds the tree queries of one head (a block of QW =
+// 32 QG of them) against one key range.  Ranges 0..S-2 each cover KPS
+// consecutive prefix keys (cache slots); range S-1 is the N tree keys, read
+// from k_tree / v_tree under the ancestor mask.  The tree range's workgroup of
+// query block 0 also copies the tree keys/values into cache slots P..P+N-1
+// (no other workgroup reads those slots).  With several query blocks per head
+// the blocks of one key range get linear workgroup ids 8 apart: workgroups are
+// dealt to the 8 XCDs round-robin, so the blocks land on one XCD and read the
+// range's K/V through the same L2.
 //
-// Inside the workgroup, 8 waves = 2 query halves x 4 key quarters: wave w
-// takes queries 32 (w & 1) .. +31 (two 16-query blocks) against keys
-// 16 (w >> 1) .. +15 of every 64-key tile, and keeps its own online-softmax
-// state; the four key quarters are merged through LDS at the end.
+// Inside the workgroup, 8 waves = QG query groups x KG = 8 / QG key groups:
+// wave w takes queries 32 (w % QG) .. +31 (two 16-query blocks) against the
+// KW = 64 / KG keys 16 (w / QG) NKB .. of every 64-key tile (NKB = KW / 16
+// blocks of 16 keys), keeps its own online-softmax state, and the key groups
+// are merged through LDS at the end.  Up to 64 tree nodes QG = 2 (64 queries,
+// 4 key groups of 16 keys); up to 128 QG = 4; up to 256 QG = 8 (every wave
+// against the whole tile, no merge): a wide tree then shares each K/V tile,
+// its barrier and its loads among all its queries instead of re-streaming
+// the range once per 64 queries, and each wave has 4x the independent
+// products per tile.
 //
 // Contractions, in transposed form so that no register data moves between
 // lanes:
@@ -237,7 +244,7 @@ __global__ __launch_bounds__(ATT_MERGE_THREADS) void tree_attn_merge_kernel(cons
 //                            transposes 4 x 4 blocks of 16-bit values across
 //                            lanes).
 // Softmax in base 2 against a lazily raised reference M: a query's M (and so
-// O and l) changes only when a tile's score exceeds it by more than 2^8, so
+// O and l) changes only when a key block's score exceeds it by more than 2^8, so
 // probabilities stay <= 256 and almost every tile skips the rescale; O / l is
 // the same for any reference.  The state of query q lives in the 4 lanes that
 // hold its column.
@@ -255,10 +262,13 @@ __global__ __launch_bounds__(ATT_MERGE_THREADS) void tree_attn_merge_kernel(cons
 // the K fragment reads (16 rows, one chunk) and the transposing V reads (4
 // rows, two chunks) hit distinct LDS banks.  The first tiles are requested
 // before the sequence's cache length is read (clamped to the host bound
-// max_cache_len, so they stay in bounds).
+// max_cache_len, so they stay in bounds).  The 64-query variant stages its
+// queries in LDS with the same loads; the wider ones load each wave's query
+// fragments straight into registers once the first tiles are requested.
 // ---------------------------------------------------------------------------
 constexpr int MF_TK = 64;       // keys per tile
-constexpr int MF_Q = 64;        // tree queries per workgroup
+// query groups of a workgroup (32 queries each) for an N-node tree
+__host__ __device__ constexpr int mf_qg(int N) { return N <= 64 ? 2 : N <= 128 ? 4 : 8; }
 constexpr int MF_THREADS = 512;
 constexpr int MF_STAGES = 4;
 constexpr float MF_LAZY = 8.f;  // log2 of the largest probability before a rescale
@@ -318,13 +328,18 @@ __device__ __forceinline__ void mf_loads_landed() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <int D>
+template <int D, int QG>
 __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_tree, const bf16_t* __restrict__ v_tree,
     bf16_t* __restrict__ k_cache, bf16_t* __restrict__ v_cache, const int32_t* __restrict__ cache_len,
     const uint64_t* __restrict__ mask, int N, int W, int nH, int nKV, int Lmax, int max_cache_len,
     float scale_log2, int KPS, int S, int QB, int BH, float* __restrict__ part_o, float* __restrict__ part_ml) {
     constexpr int TK = MF_TK;
+    constexpr int KG = 8 / QG;                   // key groups
+    constexpr int KW = TK / KG;                  // keys per wave per tile
+    constexpr int NKB = KW / 16;                 // 16-key blocks per wave per tile
+    constexpr int QW = 32 * QG;                  // queries per workgroup
+    constexpr bool QLDS = QG == 2;               // queries staged in LDS (else straight into registers)
     constexpr int DK = D / 32;                   // k-steps of S^T over the head dimension
     constexpr int DB = D / 16;                   // 16-row blocks of O^T
     constexpr int DC = D / 8;                    // 16-byte chunks per key row
@@ -333,14 +348,16 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
     constexpr int STAGE_B = 2 * TILE_B;          // K tile, then V tile
     constexpr int BLKS = 2 * TILE_B / 1024;      // 1 KB load blocks per stage
     constexpr int NLD = BLKS / (MF_THREADS / 64);  // loads per wave per tile
+    static_assert(QG == 2 || QG == 4 || QG == 8, "query groups");
     static_assert(NLD >= 1 && NLD * (MF_THREADS / 64) == BLKS && (BLKS / 2) % NLD == 0, "load split");
-    constexpr int QBLKS = MF_Q * ROWB / 1024;       // 1 KB load blocks of the query block
-    constexpr int NQLD = QBLKS / (MF_THREADS / 64); // query loads per wave
+    constexpr int QBLKS = QLDS ? QW * ROWB / 1024 : 8;  // 1 KB load blocks of the query block
+    constexpr int NQLD = QBLKS / (MF_THREADS / 64);     // query loads per wave
     static_assert(NQLD >= 1 && NQLD * (MF_THREADS / 64) == QBLKS, "query load split");
-    // after the key loop the stages hold the states of four waves for the
-    // merge of the key quarters: O^T fragments + (M, l) per lane
+    // after the key loop the stages hold the states of the key groups' waves
+    // for their merge: O^T fragments + (M, l) per lane, one wave per stage
     constexpr int MERGE_WAVE_F = 2 * DB * 64 * 4 + 2 * 64 * 2;
-    static_assert(MERGE_WAVE_F * 4 <= STAGE_B && MF_STAGES == 4, "merge area: one wave state per stage");
+    static_assert(MERGE_WAVE_F * 4 <= STAGE_B && MF_STAGES == 4 && (KG / 2) * QG <= MF_STAGES,
+                  "merge area: one wave state per stage");
     // four separate arrays, so the compiler can tell a stage being read from
     // the stages the loads in flight write to
     __shared__ __attribute__((aligned(1024))) char lds0[STAGE_B];
@@ -348,7 +365,7 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
     __shared__ __attribute__((aligned(1024))) char lds2[STAGE_B];
     __shared__ __attribute__((aligned(1024))) char lds3[STAGE_B];
     auto stage_ptr = [&](int u) -> char* { return u == 0 ? lds0 : u == 1 ? lds1 : u == 2 ? lds2 : lds3; };
-    __shared__ __attribute__((aligned(1024))) char qlds[MF_Q * ROWB];  // the block's queries (swizzled rows)
+    __shared__ __attribute__((aligned(1024))) char qlds[QLDS ? QW * ROWB : 1024];  // the block's queries (swizzled rows)
 
     const int Lid = blockIdx.x;
     const int qblk = (Lid >> 3) % QB;
@@ -361,7 +378,7 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
     const bool tree = s == S - 1;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lk = lane >> 4;
-    const int kq = wave >> 1, qh = wave & 1;  // key quarter, query half
+    const int kq = wave / QG, qh = wave % QG;  // key group, query group
     const size_t cache_row0 = ((size_t)b * nKV + kvh) * Lmax;
     const size_t prow = ((size_t)bh * S + s) * N;  // partial rows of this (head, range)
 
@@ -386,13 +403,15 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
     }
 
     // the lane's queries (a padded query, qi >= N, computes with the last
-    // query's data and is never written) and, in the tree range, their
-    // ancestor rows (words past W are never used: the range has W tiles),
-    // loaded and waited for before any load into LDS is issued
+    // query's data and is never written)
     int qidx[2];
-    uint64_t mrow[2][4] = {{~0ull, ~0ull, ~0ull, ~0ull}, {~0ull, ~0ull, ~0ull, ~0ull}};
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) qidx[qb] = qblk * MF_Q + qh * 32 + qb * 16 + lr;
+    for (int qb = 0; qb < 2; ++qb) qidx[qb] = qblk * QW + qh * 32 + qb * 16 + lr;
+    u32x4 qf[2][DK];  // QLDS: read from LDS after the first tile barrier; else loaded below
+    // in the tree range, the queries' ancestor rows (words past W are never
+    // used: the range has W tiles), waited for before any load into LDS is
+    // issued
+    uint64_t mrow[2][4] = {{~0ull, ~0ull, ~0ull, ~0ull}, {~0ull, ~0ull, ~0ull, ~0ull}};
     if (tree) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
@@ -400,14 +419,16 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
             for (int w = 0; w < 4; ++w) mrow[qb][w] = mask[(size_t)min(qidx[qb], N - 1) * W + min(w, W - 1)];
         mf_loads_landed();
     }
-    // the query block -> LDS: row r is query min(qblk * 64 + r, N - 1)
+    // the query block -> LDS: row r is query min(qblk * QW + r, N - 1)
+    if constexpr (QLDS) {
 #pragma unroll
-    for (int j = 0; j < NQLD; ++j) {
-        const int unit16 = (wave * NQLD + j) * 64 + lane;
-        const int r = unit16 / DC;
-        const int c = (unit16 % DC) ^ mf_swz<DC>(r);
-        const int qc = min(qblk * MF_Q + r, N - 1);
-        mf_dma16(q + (((size_t)b * N + qc) * nH + h) * D + c * 8, qlds + (wave * NQLD + j) * 1024);
+        for (int j = 0; j < NQLD; ++j) {
+            const int unit16 = (wave * NQLD + j) * 64 + lane;
+            const int r = unit16 / DC;
+            const int c = (unit16 % DC) ^ mf_swz<DC>(r);
+            const int qc = min(qblk * QW + r, N - 1);
+            mf_dma16(q + (((size_t)b * N + qc) * nH + h) * D + c * 8, qlds + (wave * NQLD + j) * 1024);
+        }
     }
 
     // tile loads: wave w moves 1 KB blocks w * NLD .. w * NLD + NLD - 1 of a
@@ -442,8 +463,8 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
     const int P = max(0, min(cache_len[b], max_cache_len));
     const int nkeys = tree ? N : min(KPS, P - k0);
     if (nkeys <= 0) {  // a range past this sequence's prefix: empty partials
-        if (tid < MF_Q) {
-            const int i = qblk * MF_Q + tid;
+        if (tid < QW) {
+            const int i = qblk * QW + tid;
             if (i < N) {
                 part_ml[(prow + i) * 2] = -INFINITY;
                 part_ml[(prow + i) * 2 + 1] = 0.f;
@@ -452,17 +473,31 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
         mf_loads_landed();  // no load into LDS outlives the workgroup
         return;
     }
+    if constexpr (!QLDS) {
+        // the wave's query fragments straight into registers, behind the
+        // first tiles' loads; waiting for all of them costs little more
+        // than the wait for tile 0 that follows anyway, and after a full
+        // vmcnt wait no compiler-placed wait for these loads remains
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const bf16_t* qrow = q + (((size_t)b * N + min(qidx[qb], N - 1)) * nH + h) * D;
+#pragma unroll
+            for (int ks = 0; ks < DK; ++ks) qf[qb][ks] = *(const u32x4*)(qrow + (ks * 4 + lk) * 8);
+        }
+        mf_loads_landed();
+    }
     const int ntiles = (nkeys + TK - 1) / TK;
     // tile t has been requested iff t < ntiles, or t < 3 and t < nt_spec
     auto requested = [&](int t) { return t < ntiles || (t < 3 && t < nt_spec); };
-    u32x4 qf[2][DK];  // read from LDS after the first tile barrier
 
     // per-lane LDS byte offsets (within a stage) of the K and V^T fragments
-    const int krow = kq * 16 + lr;
+    // of key block 0; block kb is kb * 16 rows further (the swizzle of a row
+    // depends only on its row within 16)
+    const int krow = kq * KW + lr;
     uint32_t koff[DK];
 #pragma unroll
     for (int ks = 0; ks < DK; ++ks) koff[ks] = krow * ROWB + (((ks * 4 + lk) ^ mf_swz<DC>(krow)) * 16);
-    const int vrow = kq * 16 + lk * 4 + (lr >> 2);
+    const int vrow = kq * KW + lk * 4 + (lr >> 2);
     uint32_t voff[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -488,80 +523,90 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
                 else if (requested(i + 1)) mf_tile_barrier<NLD>();
                 else mf_tile_barrier<0>();
                 if (i + 3 < ntiles) issue((u + 3) % MF_STAGES, i + 3);
-                if (i == 0) {
+                if constexpr (QLDS) {
+                    if (i == 0) {
 #pragma unroll
-                    for (int qb = 0; qb < 2; ++qb) {
-                        const int r = qh * 32 + qb * 16 + lr;
+                        for (int qb = 0; qb < 2; ++qb) {
+                            const int r = qh * 32 + qb * 16 + lr;
 #pragma unroll
-                        for (int ks = 0; ks < DK; ++ks)
-                            qf[qb][ks] = *(const u32x4*)(qlds + r * ROWB + (((ks * 4 + lk) ^ mf_swz<DC>(r)) * 16));
+                            for (int ks = 0; ks < DK; ++ks)
+                                qf[qb][ks] = *(const u32x4*)(qlds + r * ROWB + (((ks * 4 + lk) ^ mf_swz<DC>(r)) * 16));
+                        }
                     }
                 }
                 const char* st = stage_ptr(u);
-                u32x4 ka[DK];
-#pragma unroll
-                for (int ks = 0; ks < DK; ++ks) ka[ks] = *(const u32x4*)(st + koff[ks]);
-                u32x4 va[DB];  // the 4 keys' V^T values, repeated in both halves
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const uint2 v = __builtin_bit_cast(uint2, ds_read_tr16(st + voff[db]));
-                    va[db] = (u32x4){v.x, v.y, v.x, v.y};
-                }
                 const bool masked = tree || (i + 1) * TK > nkeys;
-                const int kk0 = kq * 16 + lk * 4;  // the lane's first key within the tile
+                // one 16-key block at a time: S^T, mask, reference, then O^T
+                // (the online softmax takes its keys in any grouping); not
+                // unrolled, so the blocks do not compete for registers
+#pragma unroll 1
+                for (int kb = 0; kb < NKB; ++kb) {
+                    u32x4 ka[DK];
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
-                    f32x4 sc = (f32x4){0.f, 0.f, 0.f, 0.f};
+                    for (int ks = 0; ks < DK; ++ks) ka[ks] = *(const u32x4*)(st + koff[ks] + kb * 16 * ROWB);
+                    const int kk0 = kq * KW + kb * 16 + lk * 4;  // the lane's first key of the block
+                    u32x4 pb[2];
 #pragma unroll
-                    for (int ks = 0; ks < DK; ++ks)
-                        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[ks]),
-                                                                     __builtin_bit_cast(bf16x8, qf[qb][ks]), sc, 0, 0,
-                                                                     0);
-                    // mask: keys past the range; in the tree range, non-ancestors
-                    if (masked) {
-                        const uint64_t word = !tree ? ~0ull : i == 0 ? mrow[qb][0] : i == 1 ? mrow[qb][1]
-                                                                       : i == 2 ? mrow[qb][2] : mrow[qb][3];
+                    for (int qb = 0; qb < 2; ++qb) {
+                        f32x4 sc = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int ks = 0; ks < DK; ++ks)
+                            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[ks]),
+                                                                         __builtin_bit_cast(bf16x8, qf[qb][ks]), sc, 0,
+                                                                         0, 0);
+                        // mask: keys past the range; in the tree range, non-ancestors
+                        if (masked) {
+                            const uint64_t word = !tree ? ~0ull : i == 0 ? mrow[qb][0] : i == 1 ? mrow[qb][1]
+                                                                           : i == 2 ? mrow[qb][2] : mrow[qb][3];
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const bool vis = i * TK + kk0 + r < nkeys && ((word >> (kk0 + r)) & 1ull);
+                                sc[r] = vis ? sc[r] : -INFINITY;
+                            }
+                        }
+                        const float lm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+                        if (__any(lm * scale_log2 > Mq[qb] + MF_LAZY)) {
+                            // raise the reference of the queries that need it (the
+                            // block max over the query's 4 lanes decides, so they agree)
+                            float t = fmaxf(lm, __shfl_xor(lm, 16, 64));
+                            t = fmaxf(t, __shfl_xor(t, 32, 64));
+                            const float tc = t * scale_log2;
+                            const float Mn = tc > Mq[qb] + MF_LAZY ? tc : Mq[qb];
+                            const float alpha = __builtin_amdgcn_exp2f(Mq[qb] - Mn);  // exactly 1 when unchanged
+                            Mq[qb] = Mn;
+                            l[qb] *= alpha;
+#pragma unroll
+                            for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
+                        }
+                        // probabilities (bare v_exp_f32: arguments <= 8, masked
+                        // ones -inf) as head + remainder, both bf16 (17 significant
+                        // bits together): k-slots 0..3 of the lane's B fragment
+                        // carry the heads of its 4 keys, slots 4..7 the remainders,
+                        // and the A fragment repeats the 4 keys' V^T values in both
+                        // halves
+                        const float nm = -Mq[qb];
+                        float p4[4];
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            const bool vis = i * TK + kk0 + r < nkeys && ((word >> (kk0 + r)) & 1ull);
-                            sc[r] = vis ? sc[r] : -INFINITY;
+                            p4[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], scale_log2, nm));
+                            l[qb] += p4[r];
                         }
+                        const uint32_t h01 = pack_bf16x2(p4[0], p4[1]), h23 = pack_bf16x2(p4[2], p4[3]);
+                        const uint32_t r01 = pack_bf16x2(p4[0] - bf16_lo(h01), p4[1] - bf16_hi(h01));
+                        const uint32_t r23 = pack_bf16x2(p4[2] - bf16_lo(h23), p4[3] - bf16_hi(h23));
+                        pb[qb] = (u32x4){h01, h23, r01, r23};
                     }
-                    const float lm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-                    if (__any(lm * scale_log2 > Mq[qb] + MF_LAZY)) {
-                        // raise the reference of the queries that need it (the
-                        // tile max over the query's 4 lanes decides, so they agree)
-                        float t = fmaxf(lm, __shfl_xor(lm, 16, 64));
-                        t = fmaxf(t, __shfl_xor(t, 32, 64));
-                        const float tc = t * scale_log2;
-                        const float Mn = tc > Mq[qb] + MF_LAZY ? tc : Mq[qb];
-                        const float alpha = __builtin_amdgcn_exp2f(Mq[qb] - Mn);  // exactly 1 when unchanged
-                        Mq[qb] = Mn;
-                        l[qb] *= alpha;
+                    // O^T += V^T . P^T over the block's 16 keys
 #pragma unroll
-                        for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
+                    for (int db = 0; db < DB; ++db) {
+                        const uint2 v = __builtin_bit_cast(uint2, ds_read_tr16(st + voff[db] + kb * 16 * ROWB));
+                        const u32x4 va = (u32x4){v.x, v.y, v.x, v.y};  // the 4 keys' V^T values, twice
+#pragma unroll
+                        for (int qb = 0; qb < 2; ++qb)
+                            o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va),
+                                                                                __builtin_bit_cast(bf16x8, pb[qb]),
+                                                                                o[qb][db], 0, 0, 0);
                     }
-                    // probabilities (bare v_exp_f32: arguments <= 8, masked ones -inf)
-                    const float nm = -Mq[qb];
-                    float p4[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        p4[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], scale_log2, nm));
-                        l[qb] += p4[r];
-                    }
-                    // p = head + remainder, both bf16 (17 significant bits
-                    // together): k-slots 0..3 of the lane's B fragment carry the
-                    // heads of its 4 keys, slots 4..7 the remainders, and the A
-                    // fragment repeats the 4 keys' V^T values in both halves
-                    const uint32_t h01 = pack_bf16x2(p4[0], p4[1]), h23 = pack_bf16x2(p4[2], p4[3]);
-                    const uint32_t r01 = pack_bf16x2(p4[0] - bf16_lo(h01), p4[1] - bf16_hi(h01));
-                    const uint32_t r23 = pack_bf16x2(p4[2] - bf16_lo(h23), p4[3] - bf16_hi(h23));
-                    const u32x4 pb = (u32x4){h01, h23, r01, r23};
-#pragma unroll
-                    for (int db = 0; db < DB; ++db)
-                        o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va[db]),
-                                                                            __builtin_bit_cast(bf16x8, pb), o[qb][db],
-                                                                            0, 0, 0);
                 }
             }
         }
@@ -575,14 +620,13 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
     }
     // the stages become the merge area once no tile load is in flight
     mf_loads_landed();
-    // merge the key quarters: quarters 2, 3 into 0, 1, then 1 into 0 (the
-    // state of source slot k sits in stage k)
+    // merge the key groups: groups lo .. 2 lo - 1 into 0 .. lo - 1 for lo =
+    // KG / 2, .., 1 (the state of source slot k sits in stage k)
 #pragma unroll
-    for (int step = 0; step < 2; ++step) {
-        const int lo = step == 0 ? 2 : 1;   // source quarters lo .. 2 lo - 1 merge into quarters 0 .. lo - 1
+    for (int lo = KG / 2; lo >= 1; lo /= 2) {
         __syncthreads();                     // the stages (or the previous step's area) are free
         if (kq >= lo && kq < 2 * lo) {
-            float* w = (float*)stage_ptr((kq - lo) * 2 + qh);
+            float* w = (float*)stage_ptr((kq - lo) * QG + qh);
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
@@ -592,7 +636,7 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
         }
         __syncthreads();
         if (kq < lo) {
-            const float* w = (const float*)stage_ptr(kq * 2 + qh);
+            const float* w = (const float*)stage_ptr(kq * QG + qh);
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
                 const float2 ml = *(const float2*)(w + 2 * DB * 64 * 4 + (qb * 64 + lane) * 2);
@@ -606,7 +650,7 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
             }
         }
     }
-    // key quarter 0 writes the partial: O^T block db, lane holds
+    // key group 0 writes the partial: O^T block db, lane holds
     // d = db * 16 + 4 * lk + r of query column lr
     if (kq == 0) {
 #pragma unroll
@@ -657,7 +701,8 @@ static AttnPlan attn_plan(bool bf16, int B, int nH, int N, int max_cache_len, in
         // whole number of 64-key tiles (measured: 7 ranges of 320 keys for
         // 32 heads x 2048 keys, 2 of 2048 for 4 query blocks x 32 heads x
         // 4096 keys, 3 of 2752 for 8 x 32 heads up to 8192 keys)
-        p.QB = (N + MF_Q - 1) / MF_Q;
+        const int QW = 32 * mf_qg(N);
+        p.QB = (N + QW - 1) / QW;
         const int target = target_wg > 0 ? target_wg : ATT_MFMA_TARGET_WG;
         const int units = B * nH * p.QB;
         int Sp = target / units - 1;
@@ -698,11 +743,16 @@ void launch_tree_attention(const void* q, const void* k_tree, const void* v_tree
         bf16_t *KC = (bf16_t*)k_cache, *VC = (bf16_t*)v_cache;
         const int units = B * nH * pl.S;
         const dim3 grid((unsigned)(((units + 7) / 8) * 8 * pl.QB));
-#define MEDUSA_MF(DD)                                                                                        \
-    MEDUSA_LAUNCH("tree_attn_mfma", (tree_attn_mfma_kernel<DD>), grid, dim3(MF_THREADS), 0, s, Q, KT, VT,     \
+#define MEDUSA_MF(DD, QG)                                                                                    \
+    MEDUSA_LAUNCH("tree_attn_mfma", (tree_attn_mfma_kernel<DD, QG>), grid, dim3(MF_THREADS), 0, s, Q, KT, VT, \
                   KC, VC, cache_len, t.mask, N, t.W, nH, nKV, Lmax, max_cache_len, scale_log2, pl.KPS, pl.S,  \
                   pl.QB, B * nH, part_o, part_ml)
-        if (D == 64) MEDUSA_MF(64); else MEDUSA_MF(128);
+        const int qg = mf_qg(N);
+        if (D == 64) {
+            if (qg == 2) MEDUSA_MF(64, 2); else if (qg == 4) MEDUSA_MF(64, 4); else MEDUSA_MF(64, 8);
+        } else {
+            if (qg == 2) MEDUSA_MF(128, 2); else if (qg == 4) MEDUSA_MF(128, 4); else MEDUSA_MF(128, 8);
+        }
 #undef MEDUSA_MF
     } else {
         const dim3 grid(B * nH, pl.S, (N + ATT_QB - 1) / ATT_QB);

@@ -150,6 +150,11 @@ ATT_CASES = [
     ("bf16_sparse64_p0", lambda: _cfg("a6", "bf16", 1, 256, 10, 5, 4, mi.sparse_tree(64), 4, 4, 128, (0,), 206)),
     # four query blocks of 64 at D = 64, GQA, two sequences
     ("bf16_dense256_d64_gqa_b2", lambda: _cfg("a7", "bf16", 2, 256, 10, 5, 3, mi.dense_tree(256), 4, 2, 64, (70, 513), 207)),
+    # 65..128 nodes: one workgroup of 4 query groups x 2 key groups per head and range
+    ("bf16_sparse100_gqa_d128_b2", lambda: _cfg("a8", "bf16", 2, 256, 10, 5, 4, mi.sparse_tree(100), 4, 2, 128, (333, 1500), 208)),
+    # 129..256 nodes (padded queries): 8 query groups, every wave against whole tiles
+    ("bf16_sparse200_d64_p2100", lambda: _cfg("a9", "bf16", 1, 256, 10, 5, 5, mi.sparse_tree(200), 8, 8, 64, (2100,), 209)),
+    ("bf16_sparse129_d128_b2_p0", lambda: _cfg("a10", "bf16", 2, 256, 10, 5, 5, mi.sparse_tree(129), 2, 1, 128, (0, 64), 210)),
 ]
 
 
