@@ -63,6 +63,18 @@ def gate_up_traffic_bytes():
 METRIC = "Medusa steps/sec + tree-verify tokens/sec (64-node tree, 7B shape), % of HBM roofline"
 
 
+def tree_prior_tokens(parent, rank, alpha=0.8):
+    """Tokens per step if the heads' guesses were right with the synthetic
+    rank prior of the tree spec (rank r right with probability
+    alpha (1 - alpha)^r at any depth, independently): the root's bonus token
+    plus, for every candidate, the probability that its whole path is right."""
+    import medusa_inputs as mi
+    prob = [1.0] * len(parent)
+    for i in range(1, len(parent)):
+        prob[i] = prob[parent[i]] * mi.rank_prior(alpha, int(rank[i]))
+    return 1.0 + sum(prob[1:])
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -247,6 +259,7 @@ def main():
                 "bytes_per_launch": algo_bytes, "avg_us": round(vt_us, 2)}
 
     t_verify_us = st["tree_attention"]
+    prior_tokens = tree_prior_tokens(*cfg.tree.arrays())
     result = {
         "metric": METRIC,
         "value": round(1000.0 / ms_step, 2),
@@ -264,6 +277,8 @@ def main():
                    "tree_nodes": N, "attn_heads": cfg.nH, "head_dim": cfg.D, "kv_cache_len": list(cfg.P),
                    "graph": bool(args.graph)},
         "tree_verify_tokens_per_s": round(B * N / (t_verify_us * 1e-6), 1) if t_verify_us > 0 else None,
+        "tokens_per_step_under_tree_prior": round(prior_tokens, 3),
+        "tokens_per_s_under_tree_prior": round(B * prior_tokens * 1000.0 / ms_step, 1),
         "stages_us": {k: round(v, 2) for k, v in st.items()},
         "kernels_us": {k: round(v, 2) for k, v in kern_us.items()},
         "wall_ms_per_step": round(1e3 * wall / args.steps, 4),
@@ -541,15 +556,7 @@ def bench_loop(args, cfg):
     n_graph = loop.n_tokens.cpu().numpy()
     same = bool(np.array_equal(n_graph, n_eager) and np.array_equal(loop.tokens.cpu().numpy(), tokens_eager))
 
-    # tokens per round if the heads' guesses were right with the tree's prior
-    # (rank r at any depth right with probability 0.8 * 0.2^r): 1 + the sum
-    # over candidates of the product of the priors along their path
-    depth = np.zeros(N, dtype=int)
-    prob = np.ones(N)
-    for i in range(1, N):
-        depth[i] = depth[parent[i]] + 1
-        prob[i] = prob[parent[i]] * mi.rank_prior(0.8, int(rank[i]))
-    expected = 1.0 + float(prob[1:].sum())
+    expected = tree_prior_tokens(parent, rank)
     rounds_s = R / (graph_ms * 1e-3)
     result = {
         "metric": "Medusa generate rounds/sec (32-layer Llama-7B-shaped decoder, device-resident loop)",
