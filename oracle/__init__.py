@@ -38,3 +38,4 @@ from .medusa import *  # noqa: F401,F403
 from .cost import *    # noqa: F401,F403
 from .decoder import *  # noqa: F401,F403
 from .generate import *  # noqa: F401,F403
+from .typical import *  # noqa: F401,F403
