@@ -22,6 +22,7 @@ throughput on the host cores (cpu_baseline).
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -84,6 +85,9 @@ def parse():
                     help="workload index (2: 7B sparse-64, 3: dense-256, 4: batched, 5: 32-layer decoder verify)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay the step as a captured HIP graph")
+    ap.add_argument("--typical", action="store_true",
+                    help="sampling mode: the base greedy stage also writes the node rows' scores and "
+                         "medusa_typical_accept (temperature 0.7, eps 0.09, delta 0.3) replaces medusa_accept")
     ap.add_argument("--loop", type=int, default=0, metavar="ROUNDS",
                     help="with --config 5: time ROUNDS rounds of the device-resident generate loop (MedusaLoop), "
                          "eager and as one captured graph, and print that line instead")
@@ -177,6 +181,11 @@ def main():
     ot = torch.empty_like(an)
     ncl = torch.empty(B, dtype=torch.int32, device="cuda")
     maxP = max(cfg.P)
+    if args.typical:
+        lg = torch.empty(B * N, V, device="cuda")
+        u = dev(mi.uniform01((B,), cfg.seed, mi.S_TEST + 41).astype(np.float32))
+        ws_t = torch.empty(M._lib.medusa_typical_accept_workspace_size(tree.handle, B), dtype=torch.uint8,
+                           device="cuda")
 
     def step():
         M.medusa_resid_silu(d["h"], w1, d["b1"], z)
@@ -184,9 +193,14 @@ def main():
         M.medusa_build_tree(tree, ti, root_d, d["cache_len"], tok, pos)
         M.tree_attention_verify(d["q"], d["k_tree"], d["v_tree"], d["k_cache"], d["v_cache"], d["cache_len"], maxP,
                                 tree, o, ws=ws_a)
-        M.medusa_base_greedy(o, lm, g, ws=ws_g)
-        M.medusa_accept(tree, tok, g.view(B, N), al, an, ot, d["cache_len"], ncl, k_cache=d["k_cache"],
-                        v_cache=d["v_cache"])
+        if args.typical:
+            M.medusa_base_greedy(o, lm, g, logits=lg, ws=ws_g)
+            M.medusa_typical_accept(tree, tok, lg.view(B, N, V), u, al, an, ot, d["cache_len"], ncl, temperature=0.7,
+                                    epsilon=0.09, delta=0.3, k_cache=d["k_cache"], v_cache=d["v_cache"], ws=ws_t)
+        else:
+            M.medusa_base_greedy(o, lm, g, ws=ws_g)
+            M.medusa_accept(tree, tok, g.view(B, N), al, an, ot, d["cache_len"], ncl, k_cache=d["k_cache"],
+                            v_cache=d["v_cache"])
 
     run = step
     graph = None
@@ -198,8 +212,13 @@ def main():
                 step()
         torch.cuda.current_stream().wait_stream(s)
         graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
+        gc.collect()
+        gc.disable()  # no finalizer may free device memory while the graph is captured
+        try:
+            with torch.cuda.graph(graph):
+                step()
+        finally:
+            gc.enable()
         run = graph.replay
 
     for _ in range(args.warmup):
@@ -237,10 +256,10 @@ def main():
         "heads_vocab_topk": stage("vocab_proj_topk", "split_rows", "vocab_proj_topk_mfma", "topk_merge"),
         "build_tree": stage("build_tree"),
         "tree_attention": stage("tree_attn_split", "tree_attn_mfma", "tree_attn_merge"),
-        "base_greedy": stage("rmsnorm_rows", "lm_head_argmax", "argmax_merge") +
+        "base_greedy": stage("rmsnorm_rows", "row_rscale", "lm_head_argmax", "argmax_merge") +
         prof.get("lm_head_gemv", (0, 0.0))[1] * 1e3 / max(args.steps, 1) +
         prof.get("lm_head_gemv_merge", (0, 0.0))[1] * 1e3 / max(args.steps, 1),
-        "accept_compact": stage("accept_compact"),
+        "accept_compact": stage("accept_compact", "row_softmax_stats", "typical_accept_compact", "draw_extra"),
     }
 
     # roofline of the dominant kernel: the vocabulary projection of the heads
@@ -275,7 +294,7 @@ def main():
         "data": "synthetic (seeded Philox inputs, random-init weights)",
         "config": {"workload": cfg.name, "batch": B, "hidden": H, "vocab": V, "medusa_heads": K, "topk": topk,
                    "tree_nodes": N, "attn_heads": cfg.nH, "head_dim": cfg.D, "kv_cache_len": list(cfg.P),
-                   "graph": bool(args.graph)},
+                   "graph": bool(args.graph), "acceptance": "typical" if args.typical else "greedy"},
         "tree_verify_tokens_per_s": round(B * N / (t_verify_us * 1e-6), 1) if t_verify_us > 0 else None,
         "tokens_per_step_under_tree_prior": round(prior_tokens, 3),
         "tokens_per_s_under_tree_prior": round(B * prior_tokens * 1000.0 / ms_step, 1),
@@ -543,8 +562,13 @@ def bench_loop(args, cfg):
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=s):
-        loop.run(R)
+    gc.collect()
+    gc.disable()  # no finalizer may free device memory while the graph is captured
+    try:
+        with torch.cuda.graph(graph, stream=s):
+            loop.run(R)
+    finally:
+        gc.enable()
     torch.cuda.synchronize()
     restore()
     torch.cuda.synchronize()

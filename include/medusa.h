@@ -244,6 +244,35 @@ medusa_status medusa_accept(const medusa_tree* tree, const int32_t* node_tok, co
                             int nKV, int D, int Lmax, medusa_dtype dt, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Typical acceptance, the sampling-mode rule in place of steps a5 + a6 (tree
+ * section: under sampling a candidate is kept when its probability under the
+ * base model exceeds a threshold tied to the entropy of the distribution,
+ * accepting more tokens without matching the distribution exactly).  The
+ * page names the rule, not its form; the form taken:
+ *   p(. | node) = softmax(logits[b][node] / temperature), H its entropy (nats);
+ *   node i (depth >= 1) passes when p(node_tok[b][i] | parent(i)) >
+ *   min(epsilon, delta * exp(-H(parent(i)))), and is accepted when it and
+ *   every ancestor pass; L and the path as in medusa_accept (deepest accepted
+ *   node, lowest index among equally deep ones);
+ *   out_tokens[b][L] (the round's extra token) is drawn from p(. | path[L])
+ *   by inverse transform sampling with uniform[b] in [0, 1): the smallest
+ *   token index whose cumulative probability (index order) exceeds it.
+ *   logits [B][N][V] float32: the base model's scores after every node
+ *     (medusa_base_greedy's optional logits output);
+ *   the other arguments, the outputs and the compaction as medusa_accept;
+ *   workspace: medusa_typical_accept_workspace_size(tree, B) bytes.
+ * Limits: V <= 262144.  Three kernels: the per-node softmax statistics,
+ * acceptance with the compaction, then the draw of the extra token.
+ * ------------------------------------------------------------------------- */
+size_t medusa_typical_accept_workspace_size(const medusa_tree* tree, int B);
+medusa_status medusa_typical_accept(const medusa_tree* tree, const int32_t* node_tok, const float* logits, int B,
+                                    int V, float temperature, float epsilon, float delta, const float* uniform,
+                                    int32_t* accept_len, int32_t* accept_nodes, int32_t* out_tokens,
+                                    const int32_t* cache_len, int32_t* new_cache_len, void* k_cache, void* v_cache,
+                                    int n_layers, int64_t layer_stride_elems, int nKV, int D, int Lmax,
+                                    medusa_dtype dt, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * The loop around the step -- hand-off of the accepted branch to the next
  * round (tree section: the final state of the longest accepted branch feeds
  * the heads next round; e-book, section on why a round always yields k + 1

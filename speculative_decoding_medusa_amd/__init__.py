@@ -51,6 +51,9 @@ _SIGS = {
     "medusa_base_greedy": ([_vp, _vp, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
     "medusa_accept": ([_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32,
                        _vp], _i32),
+    "medusa_typical_accept_workspace_size": ([_vp, _i32], _sz),
+    "medusa_typical_accept": ([_vp, _vp, _vp, _i32, _i32, _f32, _f32, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                               _i32, _i64, _i32, _i32, _i32, _i32, _vp, _sz, _vp], _i32),
     "medusa_advance": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp], _i32),
     "medusa_decoder_workspace_size": ([_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32], _sz),
     "medusa_decoder_verify": ([_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
@@ -194,8 +197,19 @@ class Tree:
     def __del__(self):
         h = getattr(self, "handle", None)
         if h is not None and h.value and _lib is not None:  # _lib is gone at interpreter shutdown
-            _lib.medusa_tree_destroy(h)
             self.handle = None
+            # medusa_tree_destroy frees device memory, which would invalidate a
+            # HIP graph being captured on this thread (a collection can run a
+            # finalizer at any allocation): free it after the capture instead
+            if torch.cuda.is_available() and torch.cuda.is_current_stream_capturing():
+                _deferred_trees.append(h)
+                return
+            _lib.medusa_tree_destroy(h)
+            while _deferred_trees:
+                _lib.medusa_tree_destroy(_deferred_trees.pop())
+
+
+_deferred_trees = []  # tree handles released during a graph capture, freed at the next release outside one
 
 
 def medusa_build_tree(tree: Tree, topk_idx, root_tok, cache_len, node_tok, node_pos, anc_mask=None, stream=None):
@@ -339,6 +353,28 @@ def medusa_accept(tree: Tree, node_tok, greedy, accept_len, accept_nodes, out_to
     _check("medusa_accept", _lib.medusa_accept(
         tree.handle, _p(node_tok), _p(greedy), B, _p(accept_len), _p(accept_nodes), _p(out_tokens), _p(cache_len),
         _p(new_cache_len), _p(k_cache), _p(v_cache), n_layers, stride, nKV, D, Lmax, dt, _stream(stream)))
+    return accept_len
+
+
+def medusa_typical_accept(tree: Tree, node_tok, logits, uniform, accept_len, accept_nodes, out_tokens, cache_len,
+                          new_cache_len, temperature=0.7, epsilon=0.09, delta=0.3, k_cache=None, v_cache=None, ws=None,
+                          stream=None):
+    """Typical acceptance (sampling mode).  logits [B][N][V] float32 (the base
+    model's scores after every node); uniform [B] float32 in [0, 1).
+    k_cache / v_cache as medusa_accept."""
+    B, N, V = logits.shape
+    n_layers, nKV, D, Lmax, stride, dt = 0, 0, 0, 0, 0, F32
+    if k_cache is not None:
+        kc = k_cache if k_cache.dim() == 5 else k_cache.unsqueeze(0)
+        n_layers, _, nKV, Lmax, D = kc.shape
+        stride = kc.stride(0)
+        dt = _dt(kc)
+    need = _lib.medusa_typical_accept_workspace_size(tree.handle, B)
+    ws = _ws(need, logits.device, ws)
+    _check("medusa_typical_accept", _lib.medusa_typical_accept(
+        tree.handle, _p(node_tok), _p(logits), B, V, float(temperature), float(epsilon), float(delta), _p(uniform),
+        _p(accept_len), _p(accept_nodes), _p(out_tokens), _p(cache_len), _p(new_cache_len), _p(k_cache), _p(v_cache),
+        n_layers, stride, nKV, D, Lmax, dt, _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return accept_len
 
 

@@ -56,6 +56,13 @@ void launch_advance(const TreeDev& t, const int32_t* accept_len, const int32_t* 
                     const int32_t* out_tokens, const float* hidden, int B, int H, bool bf16, int32_t* root_tok,
                     void* h, int32_t* tokens, int32_t* n_tokens, int cap, const int32_t* new_cache_len,
                     int32_t* cache_len, hipStream_t s);
+size_t typical_accept_workspace_bytes(int B, int N);
+int typical_max_vocab();
+void launch_typical_accept(const TreeDev& t, const int32_t* node_tok, const float* logits, int B, int V,
+                           float temperature, float eps, float delta, const float* uniform, int32_t* accept_len,
+                           int32_t* accept_nodes, int32_t* out_tokens, const int32_t* cache_len,
+                           int32_t* new_cache_len, void* k_cache, void* v_cache, int n_layers, int64_t layer_stride,
+                           int nKV, int D, int Lmax, bool bf16, void* ws, hipStream_t s);
 size_t packed_elems(int rows, int K);
 void launch_pack_rows(const bf16_t* src, int rows, int K, bf16_t* dst, int dst_row0, int dst_rows, int inter,
                       hipStream_t s);
@@ -520,6 +527,43 @@ medusa_status medusa_accept(const medusa_tree* tree, const int32_t* node_tok, co
         launch_accept(tree->t, node_tok, greedy, B, accept_len, accept_nodes, out_tokens, cache_len, new_cache_len,
                       k_cache, v_cache, n_layers, layer_stride_elems, nKV, D, Lmax, dt == MEDUSA_BF16,
                       (hipStream_t)stream);
+    });
+}
+
+// ---------------------------------------------------------------------------
+// typical acceptance (sampling mode)
+// ---------------------------------------------------------------------------
+size_t medusa_typical_accept_workspace_size(const medusa_tree* tree, int B) {
+    if (!tree || B < 1) return 0;
+    return typical_accept_workspace_bytes(B, tree->t.N);
+}
+
+medusa_status medusa_typical_accept(const medusa_tree* tree, const int32_t* node_tok, const float* logits, int B,
+                                    int V, float temperature, float epsilon, float delta, const float* uniform,
+                                    int32_t* accept_len, int32_t* accept_nodes, int32_t* out_tokens,
+                                    const int32_t* cache_len, int32_t* new_cache_len, void* k_cache, void* v_cache,
+                                    int n_layers, int64_t layer_stride_elems, int nKV, int D, int Lmax,
+                                    medusa_dtype dt, void* ws, size_t ws_bytes, void* stream) {
+    return guarded("medusa_typical_accept", [&] {
+        REQUIRE(tree && node_tok && logits && uniform && accept_len && accept_nodes && out_tokens && cache_len &&
+                    new_cache_len && ws,
+                "null pointer argument");
+        REQUIRE(B >= 1 && V >= 1, "B and V must be positive (B=%d V=%d)", B, V);
+        SUPPORT(V <= typical_max_vocab(), "V=%d exceeds %d", V, typical_max_vocab());
+        REQUIRE(temperature > 0.f && epsilon > 0.f && delta > 0.f,
+                "temperature, epsilon and delta must be positive (%g %g %g)", temperature, epsilon, delta);
+        REQUIRE(ws_bytes >= typical_accept_workspace_bytes(B, tree->t.N), "workspace too small");
+        REQUIRE((k_cache == nullptr) == (v_cache == nullptr), "k_cache and v_cache must both be given or both NULL");
+        if (k_cache) {
+            REQUIRE(dt == MEDUSA_F32 || dt == MEDUSA_BF16, "bad dtype");
+            REQUIRE(n_layers >= 1 && nKV >= 1 && D >= 1 && Lmax >= tree->t.N, "bad cache shape");
+            SUPPORT(D <= 128, "D=%d exceeds 128", D);
+            REQUIRE(layer_stride_elems >= (int64_t)B * nKV * Lmax * D || n_layers == 1,
+                    "layer stride smaller than one layer's cache");
+        }
+        launch_typical_accept(tree->t, node_tok, logits, B, V, temperature, epsilon, delta, uniform, accept_len,
+                              accept_nodes, out_tokens, cache_len, new_cache_len, k_cache, v_cache, n_layers,
+                              layer_stride_elems, nKV, D, Lmax, dt == MEDUSA_BF16, ws, (hipStream_t)stream);
     });
 }
 

@@ -51,50 +51,173 @@ void launch_build_tree(const TreeDev& t, const int32_t* topk_idx, int K, int top
 }
 
 // ---------------------------------------------------------------------------
+// Typical acceptance needs the base distribution after every node at the
+// sampling temperature T: per logits row, with z = s / T, the maximum m, log Z
+// with Z = sum exp(z - m), and the entropy H = log Z - (1/Z) sum exp(z - m)
+// (z - m).  One block of 1024 threads per row, one pass: each thread keeps
+// (m, Z, A = sum exp(z - m)(z - m)) of the values it reads (16-byte loads,
+// four in flight), moving the reference to a larger maximum as it goes, and
+// the states are combined across the block.  stats[r] = (m, log Z, H, 0).
+// ---------------------------------------------------------------------------
+constexpr int STATS_THREADS = 1024;
+
+struct SoftStat {
+    float m, Z, A;  // reference, sum exp(z - m), sum exp(z - m)(z - m)
+};
+// the state of the union of two value sets (either may be empty: Z == 0)
+__device__ __forceinline__ SoftStat soft_combine(SoftStat x, SoftStat y) {
+    if (x.Z == 0.f) return y;
+    if (y.Z == 0.f) return x;
+    const float m = fmaxf(x.m, y.m);
+    const float fx = __expf(x.m - m), fy = __expf(y.m - m);
+    return SoftStat{m, x.Z * fx + y.Z * fy, (x.A + x.Z * (x.m - m)) * fx + (y.A + y.Z * (y.m - m)) * fy};
+}
+// add n values (-inf ones, the padding, contribute nothing)
+template <int NV>
+__device__ __forceinline__ void soft_add(SoftStat& st, const float (&z)[NV]) {
+    float mb = z[0];
+#pragma unroll
+    for (int i = 1; i < NV; ++i) mb = fmaxf(mb, z[i]);
+    if (mb == -INFINITY) return;
+    if (st.Z == 0.f) {
+        st = SoftStat{mb, 0.f, 0.f};
+    } else if (mb > st.m) {
+        const float f = __expf(st.m - mb);
+        st.A = (st.A + st.Z * (st.m - mb)) * f;
+        st.Z *= f;
+        st.m = mb;
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        if (z[i] == -INFINITY) continue;
+        const float d = z[i] - st.m;
+        const float e = __expf(d);
+        st.Z += e;
+        st.A = fmaf(e, d, st.A);
+    }
+}
+
+__global__ __launch_bounds__(STATS_THREADS) void row_softmax_stats_kernel(const float* __restrict__ logits, int V,
+                                                                          float inv_t, float4* __restrict__ stats) {
+    constexpr int U = 4;  // 16-byte loads in flight per thread
+    constexpr int WAVES = STATS_THREADS / 64;
+    __shared__ float red[3][WAVES];
+    const float* row = logits + (size_t)blockIdx.x * V;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    SoftStat st{0.f, 0.f, 0.f};
+    // 16-byte loads over the row's 16-byte-aligned body, scalars around it
+    const int head = (int)((4 - ((uintptr_t)row / 4) % 4) % 4) < V ? (int)((4 - ((uintptr_t)row / 4) % 4) % 4) : V;
+    const int n4 = (V - head) / 4;
+    const f32x4* row4 = (const f32x4*)(row + head);
+    for (int i0 = tid; i0 < n4; i0 += U * STATS_THREADS) {
+        f32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * STATS_THREADS;
+            v[u] = i < n4 ? row4[i] : (f32x4){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        }
+        float z[4 * U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) z[4 * u + c] = v[u][c] * inv_t;
+        soft_add(st, z);
+    }
+    // the scalars before and after the 16-byte body
+    const int tail0 = head + 4 * n4;
+    if (tid < head || (tid >= 4 && tail0 + tid - 4 < V)) {
+        const float z[1] = {row[tid < head ? tid : tail0 + tid - 4] * inv_t};
+        soft_add(st, z);
+    }
+    // combine across the wave, then across the waves
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const SoftStat other{__shfl_xor(st.m, o, 64), __shfl_xor(st.Z, o, 64), __shfl_xor(st.A, o, 64)};
+        st = soft_combine(st, other);
+    }
+    if (lane == 0) { red[0][wave] = st.m; red[1][wave] = st.Z; red[2][wave] = st.A; }
+    __syncthreads();
+    if (tid == 0) {
+        SoftStat t{red[0][0], red[1][0], red[2][0]};
+        for (int w = 1; w < WAVES; ++w) t = soft_combine(t, SoftStat{red[0][w], red[1][w], red[2][w]});
+        const float lz = __logf(t.Z);
+        stats[blockIdx.x] = make_float4(t.m, lz, lz - t.A / t.Z, 0.f);
+    }
+}
+
+// Arguments of the typical-acceptance rule (TYPICAL = true below).
+struct TypicalArgs {
+    const float* logits;  // [B][N][V]: base scores after every node
+    const float4* stats;  // [B][N]: row_softmax_stats_kernel's output
+    const float* uniform; // [B]: draws the extra token (draw_extra_kernel)
+    int V;
+    float inv_t, log_eps, log_delta;
+};
+
+// ---------------------------------------------------------------------------
 // Acceptance + compaction.  Grid (B, S): every block of row b recomputes the
 // acceptance of sequence b (N <= 256 nodes, one thread each: walk the chain
-// to the root and AND the matches), block (b, 0) writes the results, and
-// block (b, s) compacts slice s of the caches: slice = (layer, KV head).
+// to the root and AND the per-node tests), block (b, 0) writes the results,
+// and block (b, s) compacts slice s of the caches: slice = (layer, KV head).
 // Within a slice all source rows are read into registers before the barrier
 // that precedes any write, so an accepted node that moves onto a slot another
 // accepted node is read from cannot corrupt it; slices are disjoint.
+// Greedy (TYPICAL = false): node i passes when its token is its parent's
+// greedy choice; the extra token is the deepest node's greedy choice.
+// Typical: node i passes when log p(token | parent) = s / T - m - log Z of
+// the parent's row exceeds min(log eps, log delta - H) of that row; the extra
+// token is left to draw_extra_kernel.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, bool TYPICAL>
 __global__ __launch_bounds__(256) void accept_compact_kernel(
     const int* __restrict__ parent, const int* __restrict__ depth, int N, int Dmax,
     const int32_t* __restrict__ node_tok, const int32_t* __restrict__ greedy,
     int32_t* __restrict__ accept_len, int32_t* __restrict__ accept_nodes, int32_t* __restrict__ out_tokens,
     const int32_t* __restrict__ cache_len, int32_t* __restrict__ new_cache_len, T* __restrict__ k_cache,
-    T* __restrict__ v_cache, int nKV, int D, int Lmax, int64_t layer_stride, int n_slices) {
+    T* __restrict__ v_cache, int nKV, int D, int Lmax, int64_t layer_stride, int n_slices, TypicalArgs ta) {
     __shared__ int s_acc_depth[256];
     __shared__ int s_par[256], s_tok[256], s_g[256];
     __shared__ int s_path[MEDUSA_MAX_DEPTH_DEV + 1];
-    __shared__ int s_L, s_deepest;
+    __shared__ int s_L, s_deepest, s_extra;
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     const int32_t* tok = node_tok + (size_t)b * N;
-    const int32_t* g = greedy + (size_t)b * N;
     const int P = cache_len[b];
 
     // the sequence's nodes (N <= 256, one per thread) -> LDS in one round of
-    // loads, so the walks below read no global memory
+    // loads, so the walks below read no global memory; s_g holds the greedy
+    // choices (greedy) or the per-node test (typical)
     int dep = 0;
     if (tid < N) {
         s_par[tid] = parent[tid];
         s_tok[tid] = tok[tid];
-        s_g[tid] = g[tid];
         dep = depth[tid];
+        if constexpr (!TYPICAL) {
+            s_g[tid] = greedy[(size_t)b * N + tid];
+        } else {
+            int pass = 0;
+            if (tid > 0) {
+                const int a = parent[tid], x = tok[tid];
+                const size_t row = (size_t)b * N + a;
+                if (x >= 0 && x < ta.V) {
+                    const float4 st = ta.stats[row];
+                    const float lp = fmaf(ta.logits[row * ta.V + x], ta.inv_t, -st.x) - st.y;
+                    pass = lp > fminf(ta.log_eps, ta.log_delta - st.z);
+                }
+            }
+            s_g[tid] = pass;
+        }
     }
     if (tid == 0) { s_L = 0; s_deepest = 0; }
     __syncthreads();
-    // accepted iff every node on the chain to the root matches its parent's choice
+    // accepted iff every node on the chain to the root passes its test
     int my = -1;
     if (tid < N) {
         bool ok = true;
         int j = tid;
         while (j > 0) {
             const int p = s_par[j];
-            ok = ok && (s_tok[j] == s_g[p]);
+            ok = ok && (TYPICAL ? s_g[j] != 0 : s_tok[j] == s_g[p]);
             j = p;
         }
         my = ok ? dep : -1;
@@ -110,6 +233,7 @@ __global__ __launch_bounds__(256) void accept_compact_kernel(
         s_deepest = deepest;
         int j = deepest;
         for (int d = L; d >= 0; --d) { s_path[d] = j; j = d > 0 ? s_par[j] : 0; }
+        s_extra = TYPICAL ? -1 : s_g[deepest];  // typical: draw_extra_kernel writes the extra token
     }
     __syncthreads();
     const int L = s_L;
@@ -119,7 +243,7 @@ __global__ __launch_bounds__(256) void accept_compact_kernel(
         const size_t o = (size_t)b * (Dmax + 1) + d;
         if (d <= L) {
             accept_nodes[o] = s_path[d];
-            out_tokens[o] = d < L ? s_tok[s_path[d + 1]] : s_g[s_deepest];
+            out_tokens[o] = d < L ? s_tok[s_path[d + 1]] : s_extra;
         } else {
             accept_nodes[o] = -1;
             out_tokens[o] = -1;
@@ -164,20 +288,179 @@ __global__ __launch_bounds__(256) void accept_compact_kernel(
     }
 }
 
+// The extra token of typical acceptance: inverse transform sampling from the
+// deepest accepted node's row, out_tokens[b][L] = the smallest token index
+// whose cumulative weight exp(s / T - m) (index order) exceeds u[b] x the
+// row's total.  One block of 1024 threads per sequence; the row is taken in
+// chunks of 4096 tokens, thread t holding tokens 4t .. 4t + 3 of each chunk
+// (16-byte loads, eight chunks in flight).  The chunk totals come from one
+// block reduction per eight chunks; their prefix locates the chunk holding
+// the crossing, and one block scan of that chunk the thread and the token.
+constexpr int DRAW_THREADS = 1024;
+constexpr int DRAW_CHUNK = 4 * DRAW_THREADS;  // tokens per chunk
+constexpr int DRAW_GROUP = 8;                 // chunks loaded together
+constexpr int DRAW_MAX_CHUNKS = 64;           // rows of up to 64 x 4096 tokens
+
+// Block scan of one value per thread: the thread's exclusive and inclusive
+// prefixes and the block total.  Neighbouring threads' intervals [excl, incl)
+// meet exactly (the exclusive prefix is the previous lane's inclusive one),
+// so exactly one thread's interval holds any point of [0, total).
+__device__ __forceinline__ void block_scan(float x, float* wsum, float& excl, float& incl, float& total) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const float y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    float xp = __shfl_up(x, 1, 64);
+    if (lane == 0) xp = 0.f;
+    if (lane == 63) wsum[wv] = x;
+    __syncthreads();
+    float off = 0.f, tot = 0.f;
+    for (int w = 0; w < DRAW_THREADS / 64; ++w) {
+        const float v = wsum[w];
+        if (w < wv) off += v;
+        tot += v;
+    }
+    __syncthreads();  // wsum is reused by the next scan
+    excl = off + xp;
+    incl = off + x;
+    total = tot;
+}
+
+// the 4 weights of the thread's tokens j .. j + 3 (0 past the row)
+__device__ __forceinline__ f32x4 draw_weights(const float* lg, int j, int V, bool vec, float inv_t, float m) {
+    f32x4 v;
+    if (vec && j + 3 < V) {
+        v = *(const f32x4*)(lg + j);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = j + e < V ? lg[j + e] : -INFINITY;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = __expf(fmaf(v[e], inv_t, -m));  // exp(-inf) = 0
+    return v;
+}
+
+__global__ __launch_bounds__(DRAW_THREADS) void draw_extra_kernel(const float* __restrict__ logits,
+                                                                  const float4* __restrict__ stats, int N, int V,
+                                                                  float inv_t, const float* __restrict__ uniform,
+                                                                  const int32_t* __restrict__ accept_len,
+                                                                  const int32_t* __restrict__ accept_nodes, int Dmax,
+                                                                  int32_t* __restrict__ out_tokens) {
+    __shared__ float wsum[DRAW_THREADS / 64];
+    __shared__ float red[DRAW_THREADS / 64][DRAW_GROUP];
+    __shared__ float s_C[DRAW_MAX_CHUNKS];
+    __shared__ float s_base, s_target;
+    __shared__ int s_chunk, s_pick;
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int L = accept_len[b];
+    if (L < 0 || L > Dmax) return;
+    const int node = accept_nodes[(size_t)b * (Dmax + 1) + L];
+    if (node < 0 || node >= N) return;
+    const size_t row = (size_t)b * N + node;
+    const float* lg = logits + row * V;
+    const float m = stats[row].x;
+    const int nch = (V + DRAW_CHUNK - 1) / DRAW_CHUNK;  // <= DRAW_MAX_CHUNKS (checked on the host)
+    const bool vec = ((uintptr_t)lg & 15) == 0;
+    // the chunk totals
+    for (int g0 = 0; g0 < nch; g0 += DRAW_GROUP) {
+        f32x4 w[DRAW_GROUP];
+#pragma unroll
+        for (int q = 0; q < DRAW_GROUP; ++q) w[q] = draw_weights(lg, (g0 + q) * DRAW_CHUNK + 4 * tid, V, vec, inv_t, m);
+#pragma unroll
+        for (int q = 0; q < DRAW_GROUP; ++q) {
+            const float t = wave_sum((w[q][0] + w[q][1]) + (w[q][2] + w[q][3]));
+            if (lane == 0) red[wv][q] = t;
+        }
+        __syncthreads();
+        if (tid < DRAW_GROUP && g0 + tid < nch) {
+            float t = 0.f;
+            for (int w2 = 0; w2 < DRAW_THREADS / 64; ++w2) t += red[w2][tid];
+            s_C[g0 + tid] = t;
+        }
+        __syncthreads();
+    }
+    // the chunk holding the crossing and the weight before it
+    if (tid == 0) {
+        float total = 0.f;
+        for (int c = 0; c < nch; ++c) total += s_C[c];
+        const float target = uniform[b] * total;
+        float run = 0.f;
+        int cs = nch - 1;
+        for (int c = 0; c < nch; ++c) {
+            if (target < run + s_C[c]) { cs = c; break; }
+            if (c < nch - 1) run += s_C[c];
+        }
+        s_chunk = cs;
+        s_base = run;
+        s_target = target;
+        s_pick = min(V, (cs + 1) * DRAW_CHUNK) - 1;  // if rounding leaves the target past the scan
+    }
+    __syncthreads();
+    // the thread and the token inside that chunk
+    const int j = s_chunk * DRAW_CHUNK + 4 * tid;
+    const f32x4 w4 = draw_weights(lg, j, V, vec, inv_t, m);
+    float ex, in, tot;
+    block_scan((w4[0] + w4[1]) + (w4[2] + w4[3]), wsum, ex, in, tot);
+    const float base = s_base, target = s_target;
+    if (base + ex <= target && target < base + in) {
+        float run = base + ex;
+        int pick = min(j + 3, V - 1);
+        for (int e = 0; e < 4; ++e) {
+            run += w4[e];
+            if (j + e < V && run > target) { pick = j + e; break; }
+        }
+        s_pick = pick;
+    }
+    __syncthreads();
+    if (tid == 0) out_tokens[(size_t)b * (Dmax + 1) + L] = s_pick;
+}
+
+template <bool TYPICAL>
+static void launch_accept_t(const TreeDev& t, const int32_t* node_tok, const int32_t* greedy, int B,
+                            int32_t* accept_len, int32_t* accept_nodes, int32_t* out_tokens,
+                            const int32_t* cache_len, int32_t* new_cache_len, void* k_cache, void* v_cache,
+                            int n_layers, int64_t layer_stride, int nKV, int D, int Lmax, bool bf16,
+                            const TypicalArgs& ta, hipStream_t s) {
+    const int n_slices = k_cache ? n_layers * nKV : 1;
+    const dim3 grid(B, n_slices);
+    const char* name = TYPICAL ? "typical_accept_compact" : "accept_compact";
+    if (bf16)
+        MEDUSA_LAUNCH(name, (accept_compact_kernel<bf16_t, TYPICAL>), grid, dim3(256), 0, s, t.parent, t.depth,
+                      t.N, t.max_depth, node_tok, greedy, accept_len, accept_nodes, out_tokens, cache_len,
+                      new_cache_len, (bf16_t*)k_cache, (bf16_t*)v_cache, nKV, D, Lmax, layer_stride, n_slices, ta);
+    else
+        MEDUSA_LAUNCH(name, (accept_compact_kernel<float, TYPICAL>), grid, dim3(256), 0, s, t.parent, t.depth,
+                      t.N, t.max_depth, node_tok, greedy, accept_len, accept_nodes, out_tokens, cache_len,
+                      new_cache_len, (float*)k_cache, (float*)v_cache, nKV, D, Lmax, layer_stride, n_slices, ta);
+}
+
 void launch_accept(const TreeDev& t, const int32_t* node_tok, const int32_t* greedy, int B,
                    int32_t* accept_len, int32_t* accept_nodes, int32_t* out_tokens, const int32_t* cache_len,
                    int32_t* new_cache_len, void* k_cache, void* v_cache, int n_layers, int64_t layer_stride,
                    int nKV, int D, int Lmax, bool bf16, hipStream_t s) {
-    const int n_slices = k_cache ? n_layers * nKV : 1;
-    const dim3 grid(B, n_slices);
-    if (bf16)
-        MEDUSA_LAUNCH("accept_compact", accept_compact_kernel<bf16_t>, grid, dim3(256), 0, s, t.parent, t.depth,
-                      t.N, t.max_depth, node_tok, greedy, accept_len, accept_nodes, out_tokens, cache_len,
-                      new_cache_len, (bf16_t*)k_cache, (bf16_t*)v_cache, nKV, D, Lmax, layer_stride, n_slices);
-    else
-        MEDUSA_LAUNCH("accept_compact", accept_compact_kernel<float>, grid, dim3(256), 0, s, t.parent, t.depth,
-                      t.N, t.max_depth, node_tok, greedy, accept_len, accept_nodes, out_tokens, cache_len,
-                      new_cache_len, (float*)k_cache, (float*)v_cache, nKV, D, Lmax, layer_stride, n_slices);
+    launch_accept_t<false>(t, node_tok, greedy, B, accept_len, accept_nodes, out_tokens, cache_len, new_cache_len,
+                           k_cache, v_cache, n_layers, layer_stride, nKV, D, Lmax, bf16, TypicalArgs{}, s);
+}
+
+size_t typical_accept_workspace_bytes(int B, int N) { return (size_t)B * N * sizeof(float4); }
+int typical_max_vocab() { return DRAW_MAX_CHUNKS * DRAW_CHUNK; }
+
+void launch_typical_accept(const TreeDev& t, const int32_t* node_tok, const float* logits, int B, int V,
+                           float temperature, float eps, float delta, const float* uniform, int32_t* accept_len,
+                           int32_t* accept_nodes, int32_t* out_tokens, const int32_t* cache_len,
+                           int32_t* new_cache_len, void* k_cache, void* v_cache, int n_layers, int64_t layer_stride,
+                           int nKV, int D, int Lmax, bool bf16, void* ws, hipStream_t s) {
+    float4* stats = (float4*)ws;
+    const float inv_t = 1.0f / temperature;
+    MEDUSA_LAUNCH("row_softmax_stats", row_softmax_stats_kernel, dim3(B * t.N), dim3(STATS_THREADS), 0, s, logits, V,
+                  inv_t, stats);
+    const TypicalArgs ta{logits, stats, uniform, V, inv_t, logf(eps), logf(delta)};
+    launch_accept_t<true>(t, node_tok, nullptr, B, accept_len, accept_nodes, out_tokens, cache_len, new_cache_len,
+                          k_cache, v_cache, n_layers, layer_stride, nKV, D, Lmax, bf16, ta, s);
+    MEDUSA_LAUNCH("draw_extra", draw_extra_kernel, dim3(B), dim3(DRAW_THREADS), 0, s, logits, stats, t.N, V, inv_t,
+                  uniform, accept_len, accept_nodes, t.max_depth, out_tokens);
 }
 
 // ---------------------------------------------------------------------------

@@ -15,6 +15,7 @@ root, h as the bf16 rounding of the GPU's hidden row, tokens, lengths) and the
 caches (accepted slots within the float bound, the prefix untouched).  A
 captured run of rounds must replay bit for bit like the eager rounds.
 """
+import gc
 import sys
 
 import numpy as np
@@ -272,8 +273,13 @@ def test_loop_graph_replays_match_eager():
             getattr(loop, k).copy_(v)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    with torch.cuda.graph(graph):
-        loop.run(2)
+    gc.collect()
+    gc.disable()   # no finalizer may free device memory while the graph is captured
+    try:
+        with torch.cuda.graph(graph):
+            loop.run(2)
+    finally:
+        gc.enable()
     for rep in range(3):
         graph.replay()
         torch.cuda.synchronize()

@@ -1,6 +1,7 @@
 """The whole step captured in a HIP graph: every replay must reproduce the
 eager step bit for bit (the kernels are deterministic).  Replays are separated
 by eager work and synchronisations, and every replay is checked."""
+import gc
 import sys
 
 import numpy as np
@@ -80,8 +81,13 @@ def test_step_graph_replays_match_eager():
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step()
+    gc.collect()
+    gc.disable()   # no finalizer may free device memory while the graph is captured
+    try:
+        with torch.cuda.graph(graph):
+            step()
+    finally:
+        gc.enable()
     for rep in range(4):
         # clobber every output and restore the caches with eager work between replays
         for v in bufs.values():
