@@ -39,3 +39,4 @@ from .cost import *    # noqa: F401,F403
 from .decoder import *  # noqa: F401,F403
 from .generate import *  # noqa: F401,F403
 from .typical import *  # noqa: F401,F403
+from .specsample import *  # noqa: F401,F403
