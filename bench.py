@@ -91,6 +91,9 @@ def parse():
     ap.add_argument("--loop", type=int, default=0, metavar="ROUNDS",
                     help="with --config 5: time ROUNDS rounds of the device-resident generate loop (MedusaLoop), "
                          "eager and as one captured graph, and print that line instead")
+    ap.add_argument("--specsample", type=int, default=0, metavar="GAMMA",
+                    help="time the speculative-sampling rule alone (8 chains of GAMMA drafts over a "
+                         "32000-token vocabulary) and print that line instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device-to-device copies of MIB MiB (scale for HBM byte counters)")
     return ap.parse_args()
@@ -130,6 +133,8 @@ def main():
     import speculative_decoding_medusa_amd as M
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.specsample:
+        return bench_specsample(args)
     cfg = mi.config(args.config)
     if args.loop:
         assert cfg.layers, "--loop runs the decoder workload (--config 5)"
@@ -602,6 +607,45 @@ def bench_loop(args, cfg):
         "tokens_per_s_under_tree_prior": round(B * rounds_s * expected, 1),
     }
     print(json.dumps(result), flush=True)
+
+
+def bench_specsample(args):
+    """The speculative-sampling rule alone: 8 chains of GAMMA drafts over a
+    32000-token vocabulary (seeded target/draft rows, drafts and uniforms),
+    timed with HIP events over K calls; the bytes are the rows a call must
+    read at least (the draft tests' values and the stopping row's p and q)."""
+    import numpy as np
+    import torch
+
+    import medusa_inputs as mi
+    import speculative_decoding_medusa_amd as M
+    B, G, V, seed = 8, args.specsample, 32000, 905
+    lp = mi.normal((B, G + 1, V), seed, mi.S_TEST + 61, 1.5, "f32")
+    lq = lp[:, :G] + mi.normal((B, G, V), seed, mi.S_TEST + 62, 0.7, "f32")
+    sm = lambda x: np.exp(x - x.max(-1, keepdims=True)) / np.exp(x - x.max(-1, keepdims=True)).sum(-1, keepdims=True)
+    p = torch.from_numpy(sm(lp).astype(np.float32)).cuda()
+    q = torch.from_numpy(sm(lq).astype(np.float32)).cuda()
+    drafts = torch.from_numpy(mi.uniform_int((B, G), seed, mi.S_TEST + 63, 0, V - 1).astype(np.int32)).cuda()
+    ua = torch.from_numpy(mi.uniform01((B, G), seed, mi.S_TEST + 64)).cuda()
+    ur = torch.from_numpy(mi.uniform01((B, G + 1), seed, mi.S_TEST + 65)).cuda()
+    n = torch.empty(B, dtype=torch.int32, device="cuda")
+    out = torch.empty(B, G + 1, dtype=torch.int32, device="cuda")
+    for _ in range(args.warmup):
+        M.medusa_speculative_sample(p, q, drafts, ua, ur, n, out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        M.medusa_speculative_sample(p, q, drafts, ua, ur, n, out)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    nn = n.cpu().numpy()
+    row_bytes = int(sum(V * 4 * (2 if k < G else 1) for k in nn))
+    print(json.dumps({"metric": "speculative-sampling rule, us per call (8 chains, 32000-token rows)",
+                      "value": round(us, 2), "unit": "us", "higher_is_better": False, "gamma": G, "batch": B,
+                      "vocab": V, "accepted": nn.tolist(), "row_GBs": round(row_bytes / (us * 1e-6) / 1e9, 1),
+                      "data": "synthetic (seeded Philox rows, drafts and uniforms)"}), flush=True)
 
 
 def cpu_baseline_decoder(cfg, heads):

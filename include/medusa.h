@@ -273,6 +273,28 @@ medusa_status medusa_typical_accept(const medusa_tree* tree, const int32_t* node
                                     medusa_dtype dt, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Speculative sampling on a chain of drafts (draft-model speculative
+ * decoding; the speculative-decoding e-book, section on being faster with an
+ * unchanged output): draft i, drawn from q_i, is accepted with probability
+ * min(1, p_i(x) / q_i(x)); the round stops at the first rejection n and draws
+ * its token from max(0, p_n - q_n) normalised; if every draft passes, the
+ * extra token is drawn from p_gamma.  The output is then distributed exactly
+ * as p.  The random draws are inputs:
+ *   p [B][gamma+1][V], q [B][gamma][V] float32 probability rows (row i: after
+ *     the first i drafts); drafts [B][gamma] int32;
+ *   u_accept [B][gamma]: draft i passes when u_accept * q_i(x) < p_i(x);
+ *   u_resample [B][gamma+1] in [0, 1): the draw at the stopping position, by
+ *     inverse transform sampling (the smallest token index whose cumulative
+ *     weight, index order, exceeds u times the total);
+ *   n_accepted [B] (out); out_tokens [B][gamma+1] (out): the n accepted
+ *     drafts, the drawn token, then -1.
+ * Limits: gamma <= 64, V <= 262144.  One kernel; no workspace.
+ * ------------------------------------------------------------------------- */
+medusa_status medusa_speculative_sample(const float* p, const float* q, const int32_t* drafts, const float* u_accept,
+                                        const float* u_resample, int B, int gamma, int V, int32_t* n_accepted,
+                                        int32_t* out_tokens, void* stream);
+
+/* ---------------------------------------------------------------------------
  * The loop around the step -- hand-off of the accepted branch to the next
  * round (tree section: the final state of the longest accepted branch feeds
  * the heads next round; e-book, section on why a round always yields k + 1

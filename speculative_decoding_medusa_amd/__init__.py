@@ -54,6 +54,7 @@ _SIGS = {
     "medusa_typical_accept_workspace_size": ([_vp, _i32], _sz),
     "medusa_typical_accept": ([_vp, _vp, _vp, _i32, _i32, _f32, _f32, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                _i32, _i64, _i32, _i32, _i32, _i32, _vp, _sz, _vp], _i32),
+    "medusa_speculative_sample": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp], _i32),
     "medusa_advance": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp], _i32),
     "medusa_decoder_workspace_size": ([_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32], _sz),
     "medusa_decoder_verify": ([_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
@@ -376,6 +377,16 @@ def medusa_typical_accept(tree: Tree, node_tok, logits, uniform, accept_len, acc
         _p(accept_len), _p(accept_nodes), _p(out_tokens), _p(cache_len), _p(new_cache_len), _p(k_cache), _p(v_cache),
         n_layers, stride, nKV, D, Lmax, dt, _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return accept_len
+
+
+def medusa_speculative_sample(p, q, drafts, u_accept, u_resample, n_accepted, out_tokens, stream=None):
+    """p [B][gamma+1][V], q [B][gamma][V] float32; drafts [B][gamma] int32;
+    u_accept [B][gamma], u_resample [B][gamma+1] float32."""
+    B, g1, V = p.shape
+    _check("medusa_speculative_sample", _lib.medusa_speculative_sample(
+        _p(p), _p(q), _p(drafts), _p(u_accept), _p(u_resample), B, g1 - 1, V, _p(n_accepted), _p(out_tokens),
+        _stream(stream)))
+    return n_accepted
 
 
 def medusa_advance(tree: Tree, accept_len, accept_nodes, out_tokens, hidden, root_tok, h, tokens=None,

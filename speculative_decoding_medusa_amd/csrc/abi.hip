@@ -58,6 +58,9 @@ void launch_advance(const TreeDev& t, const int32_t* accept_len, const int32_t* 
                     int32_t* cache_len, hipStream_t s);
 size_t typical_accept_workspace_bytes(int B, int N);
 int typical_max_vocab();
+void launch_speculative_sample(const float* p, const float* q, const int32_t* drafts, const float* u_accept,
+                               const float* u_resample, int B, int gamma, int V, int32_t* n_accepted,
+                               int32_t* out_tokens, hipStream_t s);
 void launch_typical_accept(const TreeDev& t, const int32_t* node_tok, const float* logits, int B, int V,
                            float temperature, float eps, float delta, const float* uniform, int32_t* accept_len,
                            int32_t* accept_nodes, int32_t* out_tokens, const int32_t* cache_len,
@@ -564,6 +567,24 @@ medusa_status medusa_typical_accept(const medusa_tree* tree, const int32_t* node
         launch_typical_accept(tree->t, node_tok, logits, B, V, temperature, epsilon, delta, uniform, accept_len,
                               accept_nodes, out_tokens, cache_len, new_cache_len, k_cache, v_cache, n_layers,
                               layer_stride_elems, nKV, D, Lmax, dt == MEDUSA_BF16, ws, (hipStream_t)stream);
+    });
+}
+
+// ---------------------------------------------------------------------------
+// speculative sampling on a chain of drafts
+// ---------------------------------------------------------------------------
+medusa_status medusa_speculative_sample(const float* p, const float* q, const int32_t* drafts, const float* u_accept,
+                                        const float* u_resample, int B, int gamma, int V, int32_t* n_accepted,
+                                        int32_t* out_tokens, void* stream) {
+    return guarded("medusa_speculative_sample", [&] {
+        REQUIRE(p && u_resample && n_accepted && out_tokens, "null pointer argument");
+        REQUIRE(gamma == 0 || (q && drafts && u_accept), "null draft argument");
+        REQUIRE(B >= 1 && V >= 1 && gamma >= 0, "need B >= 1, V >= 1, gamma >= 0 (B=%d V=%d gamma=%d)", B, V,
+                gamma);
+        SUPPORT(gamma <= 64, "gamma=%d exceeds 64", gamma);
+        SUPPORT(V <= typical_max_vocab(), "V=%d exceeds %d", V, typical_max_vocab());
+        launch_speculative_sample(p, q, drafts, u_accept, u_resample, B, gamma, V, n_accepted, out_tokens,
+                                  (hipStream_t)stream);
     });
 }
 

@@ -328,46 +328,28 @@ __device__ __forceinline__ void block_scan(float x, float* wsum, float& excl, fl
     total = tot;
 }
 
-// the 4 weights of the thread's tokens j .. j + 3 (0 past the row)
-__device__ __forceinline__ f32x4 draw_weights(const float* lg, int j, int V, bool vec, float inv_t, float m) {
-    f32x4 v;
-    if (vec && j + 3 < V) {
-        v = *(const f32x4*)(lg + j);
-    } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = j + e < V ? lg[j + e] : -INFINITY;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = __expf(fmaf(v[e], inv_t, -m));  // exp(-inf) = 0
-    return v;
-}
-
-__global__ __launch_bounds__(DRAW_THREADS) void draw_extra_kernel(const float* __restrict__ logits,
-                                                                  const float4* __restrict__ stats, int N, int V,
-                                                                  float inv_t, const float* __restrict__ uniform,
-                                                                  const int32_t* __restrict__ accept_len,
-                                                                  const int32_t* __restrict__ accept_nodes, int Dmax,
-                                                                  int32_t* __restrict__ out_tokens) {
+// Inverse transform sampling over a row of V non-negative weights held by
+// the block (DRAW_THREADS threads): the smallest token index whose cumulative
+// weight (index order) exceeds u x the total; wt(j) returns the weights of
+// tokens j .. j + 3 (0 past the row).  Chunks of 4096 tokens, thread t holding
+// tokens 4t .. 4t + 3 of each: the chunk totals come from one block
+// reduction per eight chunks, their prefix locates the chunk holding the
+// crossing, one block scan of that chunk the thread and the token.  If float
+// rounding leaves u x total past that scan, the chunk's last token.  Every
+// thread returns the pick.  V <= DRAW_MAX_CHUNKS x 4096 (checked on the host).
+template <typename WF>
+__device__ int inverse_cdf_draw(const WF& wt, int V, float u) {
     __shared__ float wsum[DRAW_THREADS / 64];
     __shared__ float red[DRAW_THREADS / 64][DRAW_GROUP];
     __shared__ float s_C[DRAW_MAX_CHUNKS];
     __shared__ float s_base, s_target;
     __shared__ int s_chunk, s_pick;
-    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int L = accept_len[b];
-    if (L < 0 || L > Dmax) return;
-    const int node = accept_nodes[(size_t)b * (Dmax + 1) + L];
-    if (node < 0 || node >= N) return;
-    const size_t row = (size_t)b * N + node;
-    const float* lg = logits + row * V;
-    const float m = stats[row].x;
-    const int nch = (V + DRAW_CHUNK - 1) / DRAW_CHUNK;  // <= DRAW_MAX_CHUNKS (checked on the host)
-    const bool vec = ((uintptr_t)lg & 15) == 0;
-    // the chunk totals
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int nch = (V + DRAW_CHUNK - 1) / DRAW_CHUNK;
     for (int g0 = 0; g0 < nch; g0 += DRAW_GROUP) {
         f32x4 w[DRAW_GROUP];
 #pragma unroll
-        for (int q = 0; q < DRAW_GROUP; ++q) w[q] = draw_weights(lg, (g0 + q) * DRAW_CHUNK + 4 * tid, V, vec, inv_t, m);
+        for (int q = 0; q < DRAW_GROUP; ++q) w[q] = wt((g0 + q) * DRAW_CHUNK + 4 * tid);
 #pragma unroll
         for (int q = 0; q < DRAW_GROUP; ++q) {
             const float t = wave_sum((w[q][0] + w[q][1]) + (w[q][2] + w[q][3]));
@@ -381,11 +363,10 @@ __global__ __launch_bounds__(DRAW_THREADS) void draw_extra_kernel(const float* _
         }
         __syncthreads();
     }
-    // the chunk holding the crossing and the weight before it
     if (tid == 0) {
         float total = 0.f;
         for (int c = 0; c < nch; ++c) total += s_C[c];
-        const float target = uniform[b] * total;
+        const float target = u * total;
         float run = 0.f;
         int cs = nch - 1;
         for (int c = 0; c < nch; ++c) {
@@ -395,12 +376,11 @@ __global__ __launch_bounds__(DRAW_THREADS) void draw_extra_kernel(const float* _
         s_chunk = cs;
         s_base = run;
         s_target = target;
-        s_pick = min(V, (cs + 1) * DRAW_CHUNK) - 1;  // if rounding leaves the target past the scan
+        s_pick = min(V, (cs + 1) * DRAW_CHUNK) - 1;
     }
     __syncthreads();
-    // the thread and the token inside that chunk
     const int j = s_chunk * DRAW_CHUNK + 4 * tid;
-    const f32x4 w4 = draw_weights(lg, j, V, vec, inv_t, m);
+    const f32x4 w4 = wt(j);
     float ex, in, tot;
     block_scan((w4[0] + w4[1]) + (w4[2] + w4[3]), wsum, ex, in, tot);
     const float base = s_base, target = s_target;
@@ -414,7 +394,115 @@ __global__ __launch_bounds__(DRAW_THREADS) void draw_extra_kernel(const float* _
         s_pick = pick;
     }
     __syncthreads();
-    if (tid == 0) out_tokens[(size_t)b * (Dmax + 1) + L] = s_pick;
+    const int pick = s_pick;
+    __syncthreads();  // s_pick may be reused by a later draw
+    return pick;
+}
+
+// 16-byte or scalar loads of 4 consecutive floats of a row (-inf past V)
+__device__ __forceinline__ f32x4 load4(const float* row, int j, int V, bool vec, float pad) {
+    f32x4 v;
+    if (vec && j + 3 < V) {
+        v = *(const f32x4*)(row + j);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = j + e < V ? row[j + e] : pad;
+    }
+    return v;
+}
+
+// weights exp(s / T - m) of a scores row
+struct SoftmaxWeights {
+    const float* lg;
+    int V;
+    bool vec;
+    float inv_t, m;
+    __device__ f32x4 operator()(int j) const {
+        f32x4 v = load4(lg, j, V, vec, -INFINITY);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = __expf(fmaf(v[e], inv_t, -m));  // exp(-inf) = 0
+        return v;
+    }
+};
+
+// weights max(0, p - q) (the residual after a rejection), or p when q is null
+struct ResidualWeights {
+    const float *p, *q;
+    int V;
+    bool vec;
+    __device__ f32x4 operator()(int j) const {
+        f32x4 a = load4(p, j, V, vec, 0.f);
+        if (q != nullptr) {
+            const f32x4 c = load4(q, j, V, vec, 0.f);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[e] = fmaxf(0.f, a[e] - c[e]);
+        }
+        return a;
+    }
+};
+
+__global__ __launch_bounds__(DRAW_THREADS) void draw_extra_kernel(const float* __restrict__ logits,
+                                                                  const float4* __restrict__ stats, int N, int V,
+                                                                  float inv_t, const float* __restrict__ uniform,
+                                                                  const int32_t* __restrict__ accept_len,
+                                                                  const int32_t* __restrict__ accept_nodes, int Dmax,
+                                                                  int32_t* __restrict__ out_tokens) {
+    const int b = blockIdx.x;
+    const int L = accept_len[b];
+    if (L < 0 || L > Dmax) return;
+    const int node = accept_nodes[(size_t)b * (Dmax + 1) + L];
+    if (node < 0 || node >= N) return;
+    const size_t row = (size_t)b * N + node;
+    const float* lg = logits + row * V;
+    const SoftmaxWeights wt{lg, V, ((uintptr_t)lg & 15) == 0, inv_t, stats[row].x};
+    const int pick = inverse_cdf_draw(wt, V, uniform[b]);
+    if (threadIdx.x == 0) out_tokens[(size_t)b * (Dmax + 1) + L] = pick;
+}
+
+// ---------------------------------------------------------------------------
+// Speculative sampling on a chain of gamma drafts (draft-model speculative
+// decoding): draft i is accepted when u_accept q_i(x) < p_i(x), i.e. with
+// probability min(1, p/q); the round stops at the first rejection n and draws
+// its token from max(0, p_n - q_n) (normalised), or, when all gamma drafts
+// pass, the bonus token from p_gamma.  One block per sequence: thread 0
+// walks the drafts, then the block draws.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(DRAW_THREADS) void speculative_sample_kernel(
+    const float* __restrict__ p, const float* __restrict__ q, const int32_t* __restrict__ drafts,
+    const float* __restrict__ u_accept, const float* __restrict__ u_resample, int gamma, int V,
+    int32_t* __restrict__ n_accepted, int32_t* __restrict__ out_tokens) {
+    __shared__ int s_n;
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const float* pb = p + (size_t)b * (gamma + 1) * V;
+    const float* qb = q + (size_t)b * gamma * V;
+    if (tid == 0) {
+        int n = gamma;
+        for (int i = 0; i < gamma; ++i) {
+            const int x = drafts[(size_t)b * gamma + i];
+            const bool ok = x >= 0 && x < V && u_accept[(size_t)b * gamma + i] * qb[(size_t)i * V + x] <
+                                                   pb[(size_t)i * V + x];
+            if (!ok) { n = i; break; }
+        }
+        s_n = n;
+    }
+    __syncthreads();
+    const int n = s_n;
+    const float* pr = pb + (size_t)n * V;
+    const float* qr = n < gamma ? qb + (size_t)n * V : nullptr;
+    const bool vec = ((uintptr_t)pr & 15) == 0 && (qr == nullptr || ((uintptr_t)qr & 15) == 0);
+    const ResidualWeights wt{pr, qr, V, vec};
+    const int pick = inverse_cdf_draw(wt, V, u_resample[(size_t)b * (gamma + 1) + n]);
+    int32_t* out = out_tokens + (size_t)b * (gamma + 1);
+    for (int i = tid; i <= gamma; i += DRAW_THREADS)
+        out[i] = i < n ? drafts[(size_t)b * gamma + i] : i == n ? pick : -1;
+    if (tid == 0) n_accepted[b] = n;
+}
+
+void launch_speculative_sample(const float* p, const float* q, const int32_t* drafts, const float* u_accept,
+                               const float* u_resample, int B, int gamma, int V, int32_t* n_accepted,
+                               int32_t* out_tokens, hipStream_t s) {
+    MEDUSA_LAUNCH("speculative_sample", speculative_sample_kernel, dim3(B), dim3(DRAW_THREADS), 0, s, p, q, drafts,
+                  u_accept, u_resample, gamma, V, n_accepted, out_tokens);
 }
 
 template <bool TYPICAL>
