@@ -375,8 +375,11 @@ medusa_status medusa_decoder_verify(const medusa_layer_weights* layers, int n_la
 /* ---------------------------------------------------------------------------
  * Kernel timing: while enabled, every kernel launch of the library is
  * bracketed by HIP events on its stream.  medusa_profiler_collect waits for
- * the recorded events and folds them into per-kernel totals; ..._stat reads
- * entry i (0 <= i < count) of those totals.
+ * the recorded events and folds them into per-kernel totals and returns their
+ * count; ..._stat reads entry i (0 <= i < count) of those totals.  If creating,
+ * recording or reading a timing event failed since the last reset or collect,
+ * the launches concerned are missing from the totals and collect returns -1
+ * (medusa_last_error() names the HIP error); the totals stay readable.
  * ------------------------------------------------------------------------- */
 medusa_status medusa_profiler_enable(int on);
 medusa_status medusa_profiler_reset(void);

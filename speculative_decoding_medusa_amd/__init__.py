@@ -463,6 +463,8 @@ def profiler_reset():
 def profiler_collect() -> dict:
     """{kernel name: (launches, total milliseconds)} since the last reset."""
     n = _lib.medusa_profiler_collect()
+    if n < 0:
+        raise MedusaError("medusa_profiler_collect", EHIP)
     out = {}
     for i in range(n):
         name = ctypes.create_string_buffer(128)

@@ -145,6 +145,13 @@ static std::map<std::string, ProfStat> g_prof_stats;
 static std::vector<std::pair<std::string, ProfStat>> g_prof_snapshot;
 static thread_local const char* g_prof_name = nullptr;
 static thread_local hipEvent_t g_prof_a = nullptr;
+// the first HIP error of the timing events since the last collect; a launch
+// whose events fail is left untimed and the next collect reports the error
+static hipError_t g_prof_err = hipSuccess;
+
+static void prof_fail(hipError_t e) {
+    if (g_prof_err == hipSuccess) g_prof_err = e;
+}
 
 static hipEvent_t prof_event() {
     if (!g_prof_pool.empty()) {
@@ -153,7 +160,11 @@ static hipEvent_t prof_event() {
         return e;
     }
     hipEvent_t e = nullptr;
-    hipEventCreate(&e);
+    const hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) {
+        prof_fail(err);
+        return nullptr;
+    }
     return e;
 }
 
@@ -161,16 +172,32 @@ void prof_before(const char* name, hipStream_t s) {
     if (!g_prof_on) return;
     std::lock_guard<std::mutex> lk(g_prof_mu);
     g_prof_name = name;
-    g_prof_a = prof_event();
-    hipEventRecord(g_prof_a, s);
+    hipEvent_t a = prof_event();
+    if (a != nullptr) {
+        const hipError_t err = hipEventRecord(a, s);
+        if (err != hipSuccess) {
+            prof_fail(err);
+            g_prof_pool.push_back(a);
+            a = nullptr;
+        }
+    }
+    g_prof_a = a;
 }
 
 void prof_after(hipStream_t s) {
     if (!g_prof_on || g_prof_a == nullptr) return;
     std::lock_guard<std::mutex> lk(g_prof_mu);
     hipEvent_t b = prof_event();
-    hipEventRecord(b, s);
-    g_prof_pending.push_back({g_prof_name, g_prof_a, b});
+    const hipError_t err = b != nullptr ? hipEventRecord(b, s) : hipErrorOutOfMemory;
+    if (err != hipSuccess) {
+        if (b != nullptr) {
+            prof_fail(err);
+            g_prof_pool.push_back(b);
+        }
+        g_prof_pool.push_back(g_prof_a);
+    } else {
+        g_prof_pending.push_back({g_prof_name, g_prof_a, b});
+    }
     g_prof_a = nullptr;
 }
 
@@ -370,7 +397,8 @@ medusa_status medusa_tree_create(const int32_t* parent, const int32_t* rank, int
         up((void**)&t.rank, t.h_rank.data(), N * sizeof(int));
         up((void**)&t.mask, t.h_mask.data(), t.h_mask.size() * sizeof(uint64_t));
         if (e != hipSuccess) {
-            hipFree(t.parent); hipFree(t.depth); hipFree(t.rank); hipFree(t.mask);
+            // best-effort cleanup of what was allocated; the upload error is the one reported
+            (void)hipFree(t.parent); (void)hipFree(t.depth); (void)hipFree(t.rank); (void)hipFree(t.mask);
             set_error(std::string("medusa_tree_create: ") + hipGetErrorString(e));
             return MEDUSA_EHIP;
         }
@@ -385,10 +413,12 @@ medusa_status medusa_tree_create(const int32_t* parent, const int32_t* rank, int
 
 void medusa_tree_destroy(medusa_tree* tree) {
     if (!tree) return;
-    hipFree(tree->t.parent);
-    hipFree(tree->t.depth);
-    hipFree(tree->t.rank);
-    hipFree(tree->t.mask);
+    // no status to return: a failed free (only after an earlier sticky
+    // device error) leaks the four small arrays
+    (void)hipFree(tree->t.parent);
+    (void)hipFree(tree->t.depth);
+    (void)hipFree(tree->t.rank);
+    (void)hipFree(tree->t.mask);
     delete tree;
 }
 
@@ -668,30 +698,40 @@ medusa_status medusa_profiler_enable(int on) {
 medusa_status medusa_profiler_reset(void) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
     for (auto& r : g_prof_pending) {
-        hipEventSynchronize(r.b);
+        (void)hipEventSynchronize(r.b);  // discarded either way; only makes the events reusable
         g_prof_pool.push_back(r.a);
         g_prof_pool.push_back(r.b);
     }
     g_prof_pending.clear();
     g_prof_stats.clear();
     g_prof_snapshot.clear();
+    g_prof_err = hipSuccess;
     return MEDUSA_OK;
 }
 
 int medusa_profiler_collect(void) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
     for (auto& r : g_prof_pending) {
-        hipEventSynchronize(r.b);
         float ms = 0.f;
-        hipEventElapsedTime(&ms, r.a, r.b);
-        ProfStat& st = g_prof_stats[r.name];
-        st.calls += 1;
-        st.ms += ms;
+        hipError_t err = hipEventSynchronize(r.b);
+        if (err == hipSuccess) err = hipEventElapsedTime(&ms, r.a, r.b);
+        if (err == hipSuccess) {
+            ProfStat& st = g_prof_stats[r.name];
+            st.calls += 1;
+            st.ms += ms;
+        } else {
+            prof_fail(err);
+        }
         g_prof_pool.push_back(r.a);
         g_prof_pool.push_back(r.b);
     }
     g_prof_pending.clear();
     g_prof_snapshot.assign(g_prof_stats.begin(), g_prof_stats.end());
+    if (g_prof_err != hipSuccess) {
+        set_error(std::string("medusa_profiler_collect: timing events failed: ") + hipGetErrorString(g_prof_err));
+        g_prof_err = hipSuccess;
+        return -1;
+    }
     return (int)g_prof_snapshot.size();
 }
 
