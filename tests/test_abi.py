@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(M):
 def test_binding_names_match_the_abi(M):
     for n in ["medusa_resid_silu", "medusa_vocab_topk", "medusa_heads_forward", "medusa_build_tree",
               "tree_attention_verify", "medusa_base_greedy", "medusa_accept", "medusa_pack_rows",
-              "medusa_decoder_verify"]:
+              "medusa_decoder_verify", "medusa_advance", "medusa_typical_accept", "medusa_speculative_sample"]:
         assert callable(getattr(M, n))
 
 
@@ -102,6 +102,26 @@ def test_heads_argument_errors(M):
     assert st == M.EUNSUPPORTED and "multiple" in L.medusa_last_error().decode()
     st = L.medusa_vocab_topk(d, d, 7, 8, 4096, 1000, 5, 4, M.BF16, None, d, d, d, 1 << 30, None)
     assert st == M.EINVAL and "layout" in L.medusa_last_error().decode()
+
+
+def test_sampling_and_handoff_argument_errors(M):
+    """The sampling-mode and hand-off calls reject bad arguments on the host."""
+    L = M._lib
+    d = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    ss = L.medusa_speculative_sample
+    assert ss(None, d, d, d, d, 1, 4, 100, d, d, None) == M.EINVAL                  # no target rows
+    assert ss(d, None, d, d, d, 1, 4, 100, d, d, None) == M.EINVAL                  # drafts without q
+    assert "draft" in L.medusa_last_error().decode()
+    assert ss(d, d, d, d, d, 0, 4, 100, d, d, None) == M.EINVAL                     # B = 0
+    assert ss(d, d, d, d, d, 1, -1, 100, d, d, None) == M.EINVAL                    # gamma < 0
+    assert ss(d, d, d, d, d, 1, 65, 100, d, d, None) == M.EUNSUPPORTED              # gamma > 64
+    assert ss(d, d, d, d, d, 1, 4, 262145, d, d, None) == M.EUNSUPPORTED            # V over the draw's limit
+    ta = L.medusa_typical_accept
+    assert ta(None, d, d, 1, 100, 0.7, 0.09, 0.3, d, d, d, d, d, d, None, None, 0, 0, 0, 0, 0, M.BF16, d, 1 << 20,
+              None) == M.EINVAL and "null" in L.medusa_last_error().decode()
+    assert L.medusa_typical_accept_workspace_size(None, 1) == 0
+    adv = L.medusa_advance
+    assert adv(None, d, d, d, d, 1, 4096, M.BF16, d, d, None, None, 0, None, None, None) == M.EINVAL
 
 
 def test_workspace_sizes_are_positive(M):
