@@ -373,6 +373,47 @@ medusa_status medusa_decoder_verify(const medusa_layer_weights* layers, int n_la
                                     int32_t* greedy, float* hidden, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * The decoder layer's building blocks as calls of their own: the products,
+ * norms, rotations, gating and embedding that medusa_decoder_verify chains
+ * (the standard pre-norm Llama layer described above; the pages give no
+ * decoder internals), run by the same kernels.  Rows are the R = B*N tree
+ * tokens; the fp32 arrays are row-major and dense.  bf16 only.
+ *
+ * medusa_gemm_skinny: out [R][ncols] fp32 = n [R][K] (bf16) times the
+ *   transposed weight W [ncols][K], W packed by medusa_pack_rows
+ *   (dst_rows = ncols), fp32 accumulation.  The contraction is split over
+ *   whole rounds of workgroups as in the layer; the partial sums go to the
+ *   workspace (medusa_gemm_skinny_workspace_size bytes, 0 when unsplit: then
+ *   ws may be NULL) and are added in split order.  1 <= R <= 256, K a
+ *   multiple of 64; n, W, out and ws 16-byte aligned.
+ * medusa_rmsnorm: n [R][H] bf16 = x * rsqrt(mean(x^2) + eps) per row of the
+ *   fp32 x [R][H] (unit weight; bf16 rounding to nearest even).  H a
+ *   multiple of 4; x 16-byte, n 8-byte aligned.
+ * medusa_rope: from the fp32 product qkv [R][(nH + 2 nKV) D] (heads: nH of
+ *   q, nKV of k, nKV of v, D columns each), q [R][nH][D] and k [R][nKV][D]
+ *   rotated (pair (i, i + D/2) by the angle pos[r] * rope_base^(-2i/D),
+ *   angles in double, applied in fp32) and v [R][nKV][D], all bf16.
+ *   D even, <= 128; workspace medusa_rope_workspace_size(R, D) bytes
+ *   (the (cos, sin) table), 16-byte aligned.
+ * medusa_swiglu: a [R][F] bf16 = SiLU(g) * u from the fp32 product of a
+ *   gate|up matrix packed with interleave 2 ([R][2F]: column blocks of 16
+ *   alternate gate and up, gate column c at 32 (c / 16) + c % 16, its up
+ *   column 16 later).  F a multiple of 16.
+ * medusa_embed: x [R][H] fp32 = embedding [tok[r]] (bf16 [V][H], exact
+ *   widening); ids outside [0, V) read row 0.  H a multiple of 8; embedding
+ *   and x 16-byte aligned.
+ * ------------------------------------------------------------------------- */
+size_t medusa_gemm_skinny_workspace_size(int R, int K, int ncols);
+medusa_status medusa_gemm_skinny(const void* n, const void* w, int R, int K, int ncols, float* out, void* ws,
+                                 size_t ws_bytes, void* stream);
+medusa_status medusa_rmsnorm(const float* x, int R, int H, float eps, void* n, void* stream);
+size_t medusa_rope_workspace_size(int R, int D);
+medusa_status medusa_rope(const float* qkv, const int32_t* pos, int R, int nH, int nKV, int D, float rope_base,
+                          void* q, void* k, void* v, void* ws, size_t ws_bytes, void* stream);
+medusa_status medusa_swiglu(const float* gate_up, int R, int F, void* a, void* stream);
+medusa_status medusa_embed(const int32_t* tok, const void* embedding, int R, int H, int V, float* x, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Kernel timing: while enabled, every kernel launch of the library is
  * bracketed by HIP events on its stream.  medusa_profiler_collect waits for
  * the recorded events and folds them into per-kernel totals and returns their

@@ -59,6 +59,13 @@ _SIGS = {
     "medusa_decoder_workspace_size": ([_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32], _sz),
     "medusa_decoder_verify": ([_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
                                _i32, _i32, _i32, _i32, _f32, _f32, _vp, _vp, _vp, _sz, _vp], _i32),
+    "medusa_gemm_skinny_workspace_size": ([_i32, _i32, _i32], _sz),
+    "medusa_gemm_skinny": ([_vp, _vp, _i32, _i32, _i32, _vp, _vp, _sz, _vp], _i32),
+    "medusa_rmsnorm": ([_vp, _i32, _i32, _f32, _vp, _vp], _i32),
+    "medusa_rope_workspace_size": ([_i32, _i32], _sz),
+    "medusa_rope": ([_vp, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
+    "medusa_swiglu": ([_vp, _i32, _i32, _vp, _vp], _i32),
+    "medusa_embed": ([_vp, _vp, _i32, _i32, _i32, _vp, _vp], _i32),
     "medusa_profiler_enable": ([_i32], _i32),
     "medusa_profiler_reset": ([], _i32),
     "medusa_profiler_collect": ([], _i32),
@@ -451,6 +458,50 @@ def medusa_decoder_verify(layers, embedding, lm_head: Packed, tree: Tree, node_t
 # ---------------------------------------------------------------------------
 # kernel timing
 # ---------------------------------------------------------------------------
+
+def medusa_gemm_skinny(n, w: Packed, out, ws=None, stream=None):
+    """out [R][ncols] float32 = n [R][K] (bf16) times the packed W [ncols][K]^T."""
+    R, K = n.shape
+    need = _lib.medusa_gemm_skinny_workspace_size(R, K, w.rows)
+    ws = _ws(need, n.device, ws) if need else ws
+    _check("medusa_gemm_skinny", _lib.medusa_gemm_skinny(
+        _p(n), ctypes.c_void_p(w.data_ptr()), R, K, w.rows, _p(out), _p(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+    return out
+
+
+def medusa_rmsnorm(x, n, eps: float = 1e-6, stream=None):
+    """n [R][H] bf16 = RMSNorm(x [R][H] float32), unit weight."""
+    R, H = x.shape
+    _check("medusa_rmsnorm", _lib.medusa_rmsnorm(_p(x), R, H, float(eps), _p(n), _stream(stream)))
+    return n
+
+
+def medusa_rope(qkv, pos, nH: int, nKV: int, D: int, q, k, v, rope_base: float = 10000.0, ws=None, stream=None):
+    """qkv [R][(nH + 2 nKV) D] float32, pos [R] int32 -> q [R][nH][D], k, v
+    [R][nKV][D] bf16 (q and k rotated)."""
+    R = qkv.shape[0]
+    ws = _ws(_lib.medusa_rope_workspace_size(R, D), qkv.device, ws)
+    _check("medusa_rope", _lib.medusa_rope(_p(qkv), _p(pos), R, nH, nKV, D, float(rope_base), _p(q), _p(k), _p(v),
+                                           _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return q, k, v
+
+
+def medusa_swiglu(gate_up, a, stream=None):
+    """a [R][F] bf16 = SiLU(gate) * up from gate_up [R][2F] float32 (gate and
+    up columns alternating in blocks of 16)."""
+    R, F2 = gate_up.shape
+    _check("medusa_swiglu", _lib.medusa_swiglu(_p(gate_up), R, F2 // 2, _p(a), _stream(stream)))
+    return a
+
+
+def medusa_embed(tok, embedding, x, stream=None):
+    """x [R][H] float32 = embedding [V][H] (bf16) rows tok [R] (ids outside
+    [0, V) read row 0)."""
+    V, H = embedding.shape
+    _check("medusa_embed", _lib.medusa_embed(_p(tok), _p(embedding), tok.numel(), H, V, _p(x), _stream(stream)))
+    return x
+
 
 def profiler_enable(on: bool = True):
     _lib.medusa_profiler_enable(1 if on else 0)

@@ -75,6 +75,15 @@ void launch_decoder_verify(const LayerPtrs* layers, int n_layers, const bf16_t* 
                            const int32_t* cache_len, int max_cache_len, bf16_t* k_cache, bf16_t* v_cache,
                            int64_t layer_stride, int B, int H, int nH, int nKV, int D, int F, int V, int Lmax,
                            float eps, float rope_base, int32_t* greedy, float* hidden, void* ws, hipStream_t s);
+size_t skinny_gemm_workspace_bytes(int R, int K, int ncols);
+void launch_skinny_gemm(const bf16_t* n, const bf16_t* w, int R, int K, int ncols, float* out, void* ws,
+                        hipStream_t s);
+void launch_embed(const int32_t* tok, const bf16_t* E, int R, int H, int V, float* x, hipStream_t s);
+void launch_rmsnorm_f32_bf16(const float* x, int R, int H, float eps, bf16_t* n, hipStream_t s);
+size_t rope_workspace_bytes(int R, int D);
+void launch_rope(const float* qkv, const int32_t* pos, int R, int nH, int nKV, int D, float rope_base, bf16_t* q,
+                 bf16_t* k, bf16_t* v, void* ws, hipStream_t s);
+void launch_swiglu(const float* gate_up, int R, int F, bf16_t* a, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // errors
@@ -684,6 +693,82 @@ medusa_status medusa_decoder_verify(const medusa_layer_weights* layers, int n_la
                               node_pos, cache_len, max_cache_len, (bf16_t*)k_cache, (bf16_t*)v_cache,
                               layer_stride_elems, B, H, nH, nKV, D, F, V, Lmax, rms_eps, rope_base, greedy, hidden, ws,
                               (hipStream_t)stream);
+    });
+}
+
+// ---------------------------------------------------------------------------
+// the decoder layer's building blocks
+// ---------------------------------------------------------------------------
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+size_t medusa_gemm_skinny_workspace_size(int R, int K, int ncols) {
+    if (R < 1 || R > MEDUSA_MAX_TREE_NODES || K < 64 || K % 64 != 0 || ncols < 1) return 0;
+    return skinny_gemm_workspace_bytes(R, K, ncols);
+}
+
+medusa_status medusa_gemm_skinny(const void* n, const void* w, int R, int K, int ncols, float* out, void* ws,
+                                 size_t ws_bytes, void* stream) {
+    return guarded("medusa_gemm_skinny", [&] {
+        REQUIRE(n && w && out, "null pointer argument");
+        REQUIRE(R >= 1 && K >= 1 && ncols >= 1, "sizes must be positive (R=%d K=%d ncols=%d)", R, K, ncols);
+        SUPPORT(R <= MEDUSA_MAX_TREE_NODES, "R=%d exceeds %d", R, MEDUSA_MAX_TREE_NODES);
+        SUPPORT(K % 64 == 0, "K=%d must be a multiple of 64", K);
+        REQUIRE(aligned16(n) && aligned16(w) && aligned16(out), "n, w and out must be 16-byte aligned");
+        const size_t need = skinny_gemm_workspace_bytes(R, K, ncols);
+        REQUIRE(need == 0 || (ws != nullptr && ws_bytes >= need), "workspace too small: %zu < %zu", ws_bytes, need);
+        REQUIRE(need == 0 || aligned16(ws), "workspace must be 16-byte aligned");
+        launch_skinny_gemm((const bf16_t*)n, (const bf16_t*)w, R, K, ncols, out, ws, (hipStream_t)stream);
+    });
+}
+
+medusa_status medusa_embed(const int32_t* tok, const void* embedding, int R, int H, int V, float* x, void* stream) {
+    return guarded("medusa_embed", [&] {
+        REQUIRE(tok && embedding && x, "null pointer argument");
+        REQUIRE(R >= 1 && H >= 1 && V >= 1, "sizes must be positive (R=%d H=%d V=%d)", R, H, V);
+        SUPPORT(H % 8 == 0, "H=%d must be a multiple of 8", H);
+        REQUIRE(aligned16(embedding) && aligned16(x), "embedding and x must be 16-byte aligned");
+        launch_embed(tok, (const bf16_t*)embedding, R, H, V, x, (hipStream_t)stream);
+    });
+}
+
+medusa_status medusa_rmsnorm(const float* x, int R, int H, float eps, void* n, void* stream) {
+    return guarded("medusa_rmsnorm", [&] {
+        REQUIRE(x && n, "null pointer argument");
+        REQUIRE(R >= 1 && H >= 1, "sizes must be positive (R=%d H=%d)", R, H);
+        REQUIRE(eps >= 0.f, "eps must be >= 0");
+        SUPPORT(H % 4 == 0, "H=%d must be a multiple of 4", H);
+        REQUIRE(aligned16(x) && ((uintptr_t)n & 7) == 0, "x must be 16-byte and n 8-byte aligned");
+        launch_rmsnorm_f32_bf16(x, R, H, eps, (bf16_t*)n, (hipStream_t)stream);
+    });
+}
+
+size_t medusa_rope_workspace_size(int R, int D) {
+    if (R < 1 || D < 2 || D % 2 != 0 || D > 128) return 0;
+    return rope_workspace_bytes(R, D);
+}
+
+medusa_status medusa_rope(const float* qkv, const int32_t* pos, int R, int nH, int nKV, int D, float rope_base,
+                          void* q, void* k, void* v, void* ws, size_t ws_bytes, void* stream) {
+    return guarded("medusa_rope", [&] {
+        REQUIRE(qkv && pos && q && k && v && ws, "null pointer argument");
+        REQUIRE(R >= 1 && nH >= 1 && nKV >= 1 && D >= 2, "sizes must be positive (R=%d nH=%d nKV=%d D=%d)", R, nH,
+                nKV, D);
+        SUPPORT(D % 2 == 0 && D <= 128, "D=%d must be even and at most 128", D);
+        SUPPORT(R <= 65535 && nH + 2 * nKV <= 65535, "R=%d or nH + 2 nKV too large", R);
+        REQUIRE(rope_base > 1.f, "rope_base must exceed 1");
+        REQUIRE(ws_bytes >= rope_workspace_bytes(R, D), "workspace too small");
+        REQUIRE(aligned16(ws), "workspace must be 16-byte aligned");
+        launch_rope(qkv, pos, R, nH, nKV, D, rope_base, (bf16_t*)q, (bf16_t*)k, (bf16_t*)v, ws, (hipStream_t)stream);
+    });
+}
+
+medusa_status medusa_swiglu(const float* gate_up, int R, int F, void* a, void* stream) {
+    return guarded("medusa_swiglu", [&] {
+        REQUIRE(gate_up && a, "null pointer argument");
+        REQUIRE(R >= 1 && F >= 1, "sizes must be positive (R=%d F=%d)", R, F);
+        SUPPORT(F % 16 == 0, "F=%d must be a multiple of 16", F);
+        SUPPORT(R <= 65535, "R=%d exceeds 65535", R);
+        launch_swiglu(gate_up, R, F, (bf16_t*)a, (hipStream_t)stream);
     });
 }
 

@@ -391,4 +391,64 @@ void launch_decoder_verify(const LayerPtrs* layers, int n_layers, const bf16_t* 
     }
 }
 
+// ---------------------------------------------------------------------------
+// The layer's building blocks as calls of their own (same kernels as above;
+// shapes checked by the caller)
+// ---------------------------------------------------------------------------
+
+// out[e] = sum over the S splits of part[s][e], e < n
+__global__ __launch_bounds__(256) void sum_splits_kernel(const float* __restrict__ part, int S, size_t n,
+                                                         float* __restrict__ out) {
+    for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x)
+        out[e] = sum_splits(part, S, n, e);
+}
+
+// out [R][ncols] fp32 = n [R][K] (bf16) times the packed weights' rows; the
+// contraction is split as in the layer, the partial sums added by a second
+// kernel (workspace: the partials, none when the product is unsplit)
+size_t skinny_gemm_workspace_bytes(int R, int K, int ncols) {
+    const GemmSplit sp = gemm_split(R, K, ncols);
+    return sp.S > 1 ? (size_t)sp.S * R * ncols * sizeof(float) : 0;
+}
+
+void launch_skinny_gemm(const bf16_t* n, const bf16_t* w, int R, int K, int ncols, float* out, void* ws,
+                        hipStream_t s) {
+    const GemmSplit sp = gemm_split(R, K, ncols);
+    if (sp.S == 1) {
+        launch_skinny_partial(n, w, R, K, ncols, sp, out, s, "gemm_skinny");
+        return;
+    }
+    float* part = (float*)ws;
+    launch_skinny_partial(n, w, R, K, ncols, sp, part, s, "gemm_skinny");
+    const size_t total = (size_t)R * ncols;
+    const int blocks = (int)std::min<size_t>((total + 255) / 256, 4096);
+    MEDUSA_LAUNCH("sum_splits", sum_splits_kernel, dim3(blocks), dim3(256), 0, s, part, sp.S, total, out);
+}
+
+void launch_embed(const int32_t* tok, const bf16_t* E, int R, int H, int V, float* x, hipStream_t s) {
+    MEDUSA_LAUNCH("embed_rows", embed_rows_kernel, dim3(R), dim3(256), 0, s, tok, E, H, V, x);
+}
+
+void launch_rmsnorm_f32_bf16(const float* x, int R, int H, float eps, bf16_t* n, hipStream_t s) {
+    MEDUSA_LAUNCH("rmsnorm_f32", rmsnorm_f32_bf16_kernel, dim3(R), dim3(256), 0, s, x, H, eps, n);
+}
+
+size_t rope_workspace_bytes(int R, int D) { return (size_t)R * (D / 2) * sizeof(float2); }
+
+// q|k|v fp32 [R][(nH + 2 nKV) D] -> bf16 q [R][nH][D], k, v [R][nKV][D],
+// q and k rotated at pos[r] (the angle table in the workspace)
+void launch_rope(const float* qkv, const int32_t* pos, int R, int nH, int nKV, int D, float rope_base, bf16_t* q,
+                 bf16_t* k, bf16_t* v, void* ws, hipStream_t s) {
+    float2* cs = (float2*)ws;
+    MEDUSA_LAUNCH("rope_table", rope_table_kernel, dim3(R), dim3(64), 0, s, pos, D, log2((double)rope_base), cs);
+    MEDUSA_LAUNCH("qkv_rope", qkv_rope_kernel, dim3(R, nH + 2 * nKV), dim3(D / 2), 0, s, qkv, 1, R, nH, nKV, D, cs, q,
+                  k, v);
+}
+
+// a [R][F] bf16 = SiLU(gate) * up from the fp32 product [R][2F] whose columns
+// interleave gate and up in blocks of 16
+void launch_swiglu(const float* gate_up, int R, int F, bf16_t* a, hipStream_t s) {
+    MEDUSA_LAUNCH("swiglu", swiglu_kernel, dim3((F + 255) / 256, R), dim3(256), 0, s, gate_up, 1, R, F, a);
+}
+
 }  // namespace medusa

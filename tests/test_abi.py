@@ -40,7 +40,8 @@ def test_library_exports_every_declared_symbol(M):
 def test_binding_names_match_the_abi(M):
     for n in ["medusa_resid_silu", "medusa_vocab_topk", "medusa_heads_forward", "medusa_build_tree",
               "tree_attention_verify", "medusa_base_greedy", "medusa_accept", "medusa_pack_rows",
-              "medusa_decoder_verify", "medusa_advance", "medusa_typical_accept", "medusa_speculative_sample"]:
+              "medusa_decoder_verify", "medusa_advance", "medusa_typical_accept", "medusa_speculative_sample",
+              "medusa_gemm_skinny", "medusa_rmsnorm", "medusa_rope", "medusa_swiglu", "medusa_embed"]:
         assert callable(getattr(M, n))
 
 
@@ -122,6 +123,29 @@ def test_sampling_and_handoff_argument_errors(M):
     assert L.medusa_typical_accept_workspace_size(None, 1) == 0
     adv = L.medusa_advance
     assert adv(None, d, d, d, d, 1, 4096, M.BF16, d, d, None, None, 0, None, None, None) == M.EINVAL
+
+
+def test_layer_block_argument_errors(M):
+    """The decoder layer's building blocks reject bad shapes and misaligned
+    pointers on the host."""
+    L = M._lib
+    d = ctypes.c_void_p(256)   # aligned; never dereferenced: validation fails first
+    m = ctypes.c_void_p(264)   # 8-byte but not 16-byte aligned
+    assert L.medusa_gemm_skinny(None, d, 64, 4096, 4096, d, d, 1 << 30, None) == M.EINVAL
+    assert L.medusa_gemm_skinny(d, d, 64, 100, 4096, d, d, 1 << 30, None) == M.EUNSUPPORTED     # K % 64
+    assert L.medusa_gemm_skinny(d, d, 300, 4096, 4096, d, d, 1 << 30, None) == M.EUNSUPPORTED   # R > 256
+    assert L.medusa_gemm_skinny(m, d, 64, 4096, 4096, d, d, 1 << 30, None) == M.EINVAL          # alignment
+    assert L.medusa_gemm_skinny(d, d, 64, 4096, 4096, d, d, 16, None) == M.EINVAL               # workspace
+    assert "workspace" in L.medusa_last_error().decode()
+    assert L.medusa_gemm_skinny_workspace_size(64, 100, 4096) == 0
+    assert L.medusa_rmsnorm(d, 4, 6, 1e-6, d, None) == M.EUNSUPPORTED                           # H % 4
+    assert L.medusa_rmsnorm(d, 4, 8, -1.0, d, None) == M.EINVAL                                 # eps < 0
+    assert L.medusa_rope(d, d, 4, 2, 1, 130, 10000.0, d, d, d, d, 1 << 20, None) == M.EUNSUPPORTED  # D > 128
+    assert L.medusa_rope(d, d, 4, 2, 1, 64, 1.0, d, d, d, d, 1 << 20, None) == M.EINVAL             # base
+    assert L.medusa_rope(d, d, 4, 2, 1, 64, 10000.0, d, d, d, d, 8, None) == M.EINVAL               # workspace
+    assert L.medusa_swiglu(d, 4, 20, d, None) == M.EUNSUPPORTED                                 # F % 16
+    assert L.medusa_embed(d, d, 4, 12, 100, d, None) == M.EUNSUPPORTED                          # H % 8
+    assert L.medusa_embed(d, m, 4, 16, 100, d, None) == M.EINVAL                                # alignment
 
 
 def test_workspace_sizes_are_positive(M):
