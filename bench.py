@@ -261,7 +261,7 @@ def main():
         "heads_vocab_topk": stage("vocab_proj_topk", "split_rows", "vocab_proj_topk_mfma", "topk_merge"),
         "build_tree": stage("build_tree"),
         "tree_attention": stage("tree_attn_split", "tree_attn_mfma", "tree_attn_merge"),
-        "base_greedy": stage("rmsnorm_rows", "row_rscale", "lm_head_argmax", "argmax_merge") +
+        "base_greedy": stage("rmsnorm_rows", "lm_head_argmax", "argmax_merge") +
         prof.get("lm_head_gemv", (0, 0.0))[1] * 1e3 / max(args.steps, 1) +
         prof.get("lm_head_gemv_merge", (0, 0.0))[1] * 1e3 / max(args.steps, 1),
         "accept_compact": stage("accept_compact", "row_softmax_stats", "typical_accept_compact", "draw_extra"),

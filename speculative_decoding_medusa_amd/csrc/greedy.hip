@@ -37,23 +37,6 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const T* __restrict__
     for (int j = threadIdx.x; j < H; j += 256) n[(size_t)r * H + j] = Elem<T>::load(xr, j) * rs;
 }
 
-// rs[r] = rsqrt(mean(x_r^2) + eps): the RMSNorm factor of each row (for the
-// logits of the MFMA path).  One block of 256 threads per row.
-__global__ __launch_bounds__(256) void row_rscale_kernel(const bf16_t* __restrict__ x, int H, float eps,
-                                                         float* __restrict__ rs) {
-    __shared__ float red[4];
-    const bf16_t* xr = x + (size_t)blockIdx.x * H;
-    float ss = 0.f;
-    for (int j = threadIdx.x; j < H; j += 256) {
-        const float v = bf16_to_f32(xr[j]);
-        ss = fmaf(v, v, ss);
-    }
-    ss = wave_sum(ss);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    if (threadIdx.x == 0) rs[blockIdx.x] = rsqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)H + eps);
-}
-
 // greedy[r] = best of the G workgroup candidates of row r
 __global__ __launch_bounds__(64) void argmax_merge_kernel(const float* __restrict__ cand_val,
                                                           const int* __restrict__ cand_idx, int G,
@@ -126,7 +109,7 @@ size_t lm_head_greedy_workspace_bytes(int R, int H, int V) {
 }
 
 void launch_lm_head_greedy(const bf16_t* n, const bf16_t* lm_head, int R, int H, int V, int32_t* greedy,
-                           float* logits, const float* row_scale, void* ws, hipStream_t s) {
+                           float* logits, float rs_eps, void* ws, hipStream_t s) {
     const int G = lmh_groups(R, V);
     float* cv = (float*)ws;
     int* ci = (int*)((char*)ws + a256((size_t)R * G * 4));
@@ -135,7 +118,7 @@ void launch_lm_head_greedy(const bf16_t* n, const bf16_t* lm_head, int R, int H,
     const int nch = H / lmh_kc(nblk);
 #define LMH_LAUNCH(NB, WV, RBL)                                                                                 \
     MEDUSA_LAUNCH("lm_head_argmax", (skinny_mfma_kernel<NB, SKINNY_ARGMAX, WV, RBL>), grid, dim3(WV * 64), 0, s, \
-                  n, lm_head, R, H, V, nch, cv, ci, logits, row_scale)
+                  n, lm_head, R, H, V, nch, cv, ci, logits, rs_eps)
     if (lmh_shape(R, V).waves == 8) {
         if (nblk == 4) LMH_LAUNCH(4, 8, 1);
         else if (nblk == 8) LMH_LAUNCH(8, 8, 2);
@@ -151,11 +134,11 @@ void launch_lm_head_greedy(const bf16_t* n, const bf16_t* lm_head, int R, int H,
 
 void launch_lm_head_greedy(const bf16_t* n, const bf16_t* lm_head, int R, int H, int V, int32_t* greedy, void* ws,
                            hipStream_t s) {
-    launch_lm_head_greedy(n, lm_head, R, H, V, greedy, nullptr, nullptr, ws, s);
+    launch_lm_head_greedy(n, lm_head, R, H, V, greedy, nullptr, -1.f, ws, s);
 }
 
 size_t greedy_workspace_bytes(int R, int H, int V, bool packed) {
-    if (packed) return a256((size_t)R * 4) + lm_head_greedy_workspace_bytes(R, H, V);
+    if (packed) return lm_head_greedy_workspace_bytes(R, H, V);
     const int G = gemv_groups_max(V);
     return a256((size_t)R * H * 4) + a256((size_t)8 * G * 4) * 2 + a256((size_t)R * 4);
 }
@@ -166,13 +149,9 @@ void launch_base_greedy(const void* x, const void* lm_head, bool packed, int R, 
                         int32_t* greedy, float* logits, void* ws, hipStream_t s) {
     char* p = (char*)ws;
     if (packed) {
-        float* rs = nullptr;
-        if (logits != nullptr) {
-            rs = (float*)p;
-            MEDUSA_LAUNCH("row_rscale", row_rscale_kernel, dim3(R), dim3(256), 0, s, (const bf16_t*)x, H, eps, rs);
-        }
-        p += a256((size_t)R * 4);
-        launch_lm_head_greedy((const bf16_t*)x, (const bf16_t*)lm_head, R, H, V, greedy, logits, rs, p, s);
+        // the logits are the scores of the normalised rows: the product
+        // scales them by the RMSNorm factors it accumulates while staging x
+        launch_lm_head_greedy((const bf16_t*)x, (const bf16_t*)lm_head, R, H, V, greedy, logits, eps, p, s);
         return;
     }
     float* n = (float*)p;

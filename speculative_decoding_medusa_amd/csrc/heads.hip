@@ -470,7 +470,7 @@ void launch_vocab_topk_packed(const float* z, const void* w2p, int B, int H, int
     const long long w_stride = (long long)((V + PACK_ROWS - 1) / PACK_ROWS) * PACK_ROWS * H;
     MEDUSA_LAUNCH("vocab_proj_topk_mfma", (skinny_mfma_kernel<1, SKINNY_TOPK, VT_WAVES>), dim3(G, K),
                   dim3(VT_WAVES * 64), 0, s, zs, (const bf16_t*)w2p, 16, H, V, H / LmhCfg<1, VT_WAVES>::KC, cv, ci,
-                  logits, nullptr, topk, B, (long long)16 * H, w_stride);
+                  logits, -1.f, topk, B, (long long)16 * H, w_stride);
     launch_topk_merge(cv, ci, B * K, G * topk, topk, topk_idx, topk_val, s, "topk_merge");
 }
 
@@ -488,7 +488,7 @@ void launch_resid_silu_packed(const void* h, const void* w1p, const void* b1, in
     const long long w_stride = (long long)((H + PACK_ROWS - 1) / PACK_ROWS) * PACK_ROWS * H;
     MEDUSA_LAUNCH("resid_silu_mfma", (skinny_mfma_kernel<1, SKINNY_SILU, SILU_MF_WAVES>), dim3(G, K),
                   dim3(SILU_MF_WAVES * 64), 0, s, (const bf16_t*)h, (const bf16_t*)w1p, B, H, H,
-                  H / LmhCfg<1, SILU_MF_WAVES>::KC, nullptr, nullptr, z, nullptr, 0, 0, 0LL, w_stride,
+                  H / LmhCfg<1, SILU_MF_WAVES>::KC, nullptr, nullptr, z, -1.f, 0, 0, 0LL, w_stride,
                   (const bf16_t*)b1);
 }
 

@@ -82,13 +82,14 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
                                                           float* __restrict__ cand_val,
                                                           int* __restrict__ cand_idx,  // ARGMAX: [R][G]
                                                           float* __restrict__ out,
-                                                          const float* __restrict__ row_scale = nullptr,
+                                                          float rs_eps = -1.f,
                                                           int topk = 0, int nseq = 0, long long n_stride = 0,
                                                           long long w_stride = 0,
                                                           const bf16_t* __restrict__ bias = nullptr) {
-    // ARGMAX: out = optional logits [R][V], each node row's scores times
-    // row_scale[node] when given (a positive factor: the argmax is that of the
-    // unscaled scores);  PARTIAL: out = [splits][R][V];  SWIGLU: out = bf16 [R][V / 2];
+    // ARGMAX: out = optional logits [R][V]; with rs_eps >= 0 each node row's
+    // scores times its RMSNorm factor rsqrt(mean(n^2) + rs_eps), accumulated
+    // from the node rows as they are staged (a positive factor: the argmax is
+    // that of the unscaled scores);  PARTIAL: out = [splits][R][V];  SWIGLU: out = bf16 [R][V / 2];
     // TOPK: grid row y is matrix y (node rows at n + y n_stride, weights at
     // Wp + y w_stride); out = optional logits [nseq][gridDim.y][V];
     // candidates [nseq][gridDim.y][G][topk]
@@ -160,6 +161,25 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
         }
     };
 
+    // ARGMAX with logits: per-thread sums of squares of the node pieces it
+    // stages (each chunk once; pieces of one row per chunk lie in KC / 8
+    // consecutive threads)
+    const bool want_rs = EPI == SKINNY_ARGMAX && out != nullptr && rs_eps >= 0.f;
+    float rss[C::NPT];
+#pragma unroll
+    for (int e = 0; e < C::NPT; ++e) rss[e] = 0.f;
+    auto add_sq = [&](const u32x4(&src)[C::NPT]) {
+#pragma unroll
+        for (int e = 0; e < C::NPT; ++e) {
+            if (C::EVEN || tid + e * NT < C::PIECES) {
+                float v[8];
+                Elem<bf16_t>::expand(src[e], v);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) rss[e] = fmaf(v[j], v[j], rss[e]);
+            }
+        }
+    };
+
 #pragma unroll
     for (int u = 0; u < D - 1; ++u) {
         const int cu = min(u, nchunk - 1);
@@ -167,6 +187,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
         load_a(aring[u], cu);
     }
     store_n(nring[0], 0);
+    if (want_rs) add_sq(nring[0]);
     __syncthreads();
     for (int c0 = 0; c0 < nchunk; c0 += D) {
 #pragma unroll
@@ -191,6 +212,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
             }
             // the other stage was last read before the previous barrier
             store_n(nring[(u + 1) % D], (c + 1) & 1);
+            if (want_rs && c + 1 < nchunk) add_sq(nring[(u + 1) % D]);
             __syncthreads();
         }
     }
@@ -292,12 +314,27 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
         }
         return;
     }
+    // ARGMAX: the node rows' RMSNorm factors (rows past R: clamped copies, unused)
+    __shared__ float rs_l[EPI == SKINNY_ARGMAX ? C::NODES : 1];
+    if (EPI == SKINNY_ARGMAX && want_rs) {
+        constexpr int PPR = C::KC / 8;
+        static_assert(64 % PPR == 0 && NT % PPR == 0, "a row's pieces within one wave");
+#pragma unroll
+        for (int e = 0; e < C::NPT; ++e) {
+            float v = rss[e];
+#pragma unroll
+            for (int m = 1; m < PPR; m <<= 1) v += __shfl_xor(v, m, 64);
+            const int p = tid + e * NT;
+            if ((C::EVEN || p < C::PIECES) && p % PPR == 0) rs_l[p / PPR] = rsqrtf(v / (float)K + rs_eps);
+        }
+        __syncthreads();
+    }
 #pragma unroll
     for (int b = 0; b < NBLK; ++b) {
         float bv = -INFINITY;
         int bi = 0x7FFFFFFF;
         const int node = node0 + b * 16 + lr;
-        const float sc = (out != nullptr && row_scale != nullptr && node < R) ? row_scale[node] : 1.f;
+        const float sc = (want_rs && node < R) ? rs_l[b * 16 + lr] : 1.f;
 #pragma unroll
         for (int j = 0; j < RB; ++j)
 #pragma unroll
