@@ -550,6 +550,7 @@ def bench_loop(args, cfg):
         loop.h.copy_(state["h"])
         loop.root_tok.copy_(state["root_tok"])
         loop.n_tokens.zero_()
+        loop.restart(int(P0.max()))
 
     loop.run(min(R, 2))       # warm the launch paths
     restore()

@@ -147,6 +147,27 @@ medusa_status medusa_heads_forward(const void* h, const void* w1, const void* b1
 medusa_status medusa_tree_create(const int32_t* parent, const int32_t* rank, int N, int K, int topk,
                                  medusa_tree** out);
 void medusa_tree_destroy(medusa_tree* tree);
+
+/* ---------------------------------------------------------------------------
+ * Device-side status of a tree handle.  Sizes that live in device memory
+ * (cache_len[]) cannot be validated on the host before launch; when a kernel
+ * meets an invalid one it keeps every access in bounds, does what the call
+ * documents for that case, and sets a bit of the tree's status word (atomic
+ * OR; every call that takes the tree shares the word):
+ *   MEDUSA_STATUS_CACHE_LEN_CLAMPED: tree_attention_verify (or the decoder
+ *     pass) read a cache_len[b] outside [0, max_cache_len] and used the
+ *     clamped value;
+ *   MEDUSA_STATUS_CACHE_OVERFLOW: medusa_accept / medusa_typical_accept were
+ *     given caches and a cache_len[b] < 0 or cache_len[b] + N > Lmax: that
+ *     sequence's caches were not compacted and new_cache_len[b] = cache_len[b].
+ * medusa_tree_status waits for `stream`, copies the word into *flags (host)
+ * and, if clear != 0, resets it to 0.  Work of the tree on other streams must
+ * have finished (the caller synchronises them).  Not for use inside a graph
+ * capture.  Created trees start at 0.
+ * ------------------------------------------------------------------------- */
+#define MEDUSA_STATUS_CACHE_LEN_CLAMPED 1
+#define MEDUSA_STATUS_CACHE_OVERFLOW 2
+medusa_status medusa_tree_status(const medusa_tree* tree, int32_t* flags, int clear, void* stream);
 int medusa_tree_num_nodes(const medusa_tree* tree);
 int medusa_tree_max_depth(const medusa_tree* tree);
 /* host copy of the ancestor bitmask, [N][ceil(N/64)] */
@@ -166,8 +187,12 @@ medusa_status medusa_build_tree(const medusa_tree* tree, const int32_t* topk_idx
  *   out [B][N][nH][D] (dt): o = sum_j softmax_j(scale * q.k_j) v_j over the
  *     prefix and the node's ancestors-or-self; query head h reads KV head
  *     h / (nH / nKV).
- *   max_cache_len (host): an upper bound of cache_len[] (sizes the launch).
- * Limits: D in {64, 128}; nH % nKV == 0; cache_len[b] + N <= Lmax.
+ *   max_cache_len (host): an upper bound of cache_len[] (sizes the launch);
+ *     a cache_len[b] outside [0, max_cache_len] is clamped into it and
+ *     MEDUSA_STATUS_CACHE_LEN_CLAMPED is set in the tree's status word.
+ *   Cache slots at and past cache_len[b] are never part of the result,
+ *     whatever they hold (NaN included).
+ * Limits: D in {64, 128}; nH % nKV == 0; max_cache_len + N <= Lmax.
  * ------------------------------------------------------------------------- */
 size_t tree_attention_workspace_size(const medusa_tree* tree, int B, int nH, int D,
                                      int max_cache_len, medusa_dtype dt);
@@ -235,7 +260,10 @@ medusa_status medusa_base_greedy(const void* x, const void* lm_head, medusa_layo
  *   k_cache / v_cache (optional, both or neither): n_layers caches, layer l
  *     at base + l * layer_stride_elems, each [B][nKV][Lmax][D] (dt); for
  *     d = 1..L slot cache_len+d receives slot cache_len+path[d] (all sources
- *     read before any write).
+ *     read before any write).  A sequence whose cache_len[b] is negative or
+ *     whose tree slots would pass Lmax (cache_len[b] + N > Lmax) is not
+ *     compacted, gets new_cache_len[b] = cache_len[b], and sets
+ *     MEDUSA_STATUS_CACHE_OVERFLOW in the tree's status word.
  * ------------------------------------------------------------------------- */
 medusa_status medusa_accept(const medusa_tree* tree, const int32_t* node_tok, const int32_t* greedy,
                             int B, int32_t* accept_len, int32_t* accept_nodes, int32_t* out_tokens,

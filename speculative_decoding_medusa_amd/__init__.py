@@ -23,6 +23,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
+STATUS_CACHE_LEN_CLAMPED, STATUS_CACHE_OVERFLOW = 1, 2
 F32, BF16 = 0, 1
 ROW_MAJOR, PACKED = 0, 1
 
@@ -41,6 +42,7 @@ _SIGS = {
     "medusa_tree_num_nodes": ([_vp], _i32),
     "medusa_tree_max_depth": ([_vp], _i32),
     "medusa_tree_mask_host": ([_vp, _vp, _sz], _i32),
+    "medusa_tree_status": ([_vp, ctypes.POINTER(ctypes.c_int32), _i32, _vp], _i32),
     "medusa_build_tree": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp], _i32),
     "tree_attention_workspace_size": ([_vp, _i32, _i32, _i32, _i32, _i32], _sz),
     "tree_attention_verify": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
@@ -195,6 +197,15 @@ class Tree:
         self.N = _lib.medusa_tree_num_nodes(h)
         self.max_depth = _lib.medusa_tree_max_depth(h)
         self.W = (self.N + 63) // 64
+
+    def status(self, clear: bool = True, stream=None) -> int:
+        """The tree's device status word (STATUS_* bits set by kernels that
+        met an invalid cache length); waits for `stream` and, by default,
+        resets the word."""
+        v = ctypes.c_int32()
+        _check("medusa_tree_status", _lib.medusa_tree_status(self.handle, ctypes.byref(v), 1 if clear else 0,
+                                                             _stream(stream)))
+        return v.value
 
     def mask_host(self):
         import numpy as np

@@ -405,9 +405,12 @@ medusa_status medusa_tree_create(const int32_t* parent, const int32_t* rank, int
         up((void**)&t.depth, t.h_depth.data(), N * sizeof(int));
         up((void**)&t.rank, t.h_rank.data(), N * sizeof(int));
         up((void**)&t.mask, t.h_mask.data(), t.h_mask.size() * sizeof(uint64_t));
+        const int zero = 0;
+        up((void**)&t.status, &zero, sizeof(int));
         if (e != hipSuccess) {
             // best-effort cleanup of what was allocated; the upload error is the one reported
             (void)hipFree(t.parent); (void)hipFree(t.depth); (void)hipFree(t.rank); (void)hipFree(t.mask);
+            (void)hipFree(t.status);
             set_error(std::string("medusa_tree_create: ") + hipGetErrorString(e));
             return MEDUSA_EHIP;
         }
@@ -423,12 +426,31 @@ medusa_status medusa_tree_create(const int32_t* parent, const int32_t* rank, int
 void medusa_tree_destroy(medusa_tree* tree) {
     if (!tree) return;
     // no status to return: a failed free (only after an earlier sticky
-    // device error) leaks the four small arrays
+    // device error) leaks the five small arrays
     (void)hipFree(tree->t.parent);
     (void)hipFree(tree->t.depth);
     (void)hipFree(tree->t.rank);
     (void)hipFree(tree->t.mask);
+    (void)hipFree(tree->t.status);
     delete tree;
+}
+
+static_assert(MEDUSA_STATUS_CACHE_LEN_CLAMPED == STATUS_CACHE_LEN_CLAMPED &&
+                  MEDUSA_STATUS_CACHE_OVERFLOW == STATUS_CACHE_OVERFLOW,
+              "status bits of the header and the kernels");
+
+medusa_status medusa_tree_status(const medusa_tree* tree, int32_t* flags, int clear, void* stream) {
+    return guarded("medusa_tree_status", [&] {
+        REQUIRE(tree && flags, "null pointer argument");
+        hipStream_t s = (hipStream_t)stream;
+        hipError_t e = hipStreamSynchronize(s);
+        int32_t v = 0;
+        if (e == hipSuccess) e = hipMemcpy(&v, tree->t.status, sizeof(int32_t), hipMemcpyDeviceToHost);
+        if (e == hipSuccess && clear) e = hipMemsetAsync(tree->t.status, 0, sizeof(int32_t), s);
+        if (e == hipSuccess && clear) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) failf(MEDUSA_EHIP, "medusa_tree_status: %s", hipGetErrorString(e));
+        *flags = v;
+    });
 }
 
 int medusa_tree_num_nodes(const medusa_tree* tree) { return tree ? tree->t.N : 0; }

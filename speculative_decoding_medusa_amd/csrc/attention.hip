@@ -28,7 +28,7 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attn_valu_kernel(
     const T* __restrict__ q, const T* __restrict__ k_tree, const T* __restrict__ v_tree,
     T* __restrict__ k_cache, T* __restrict__ v_cache, const int32_t* __restrict__ cache_len,
     const uint64_t* __restrict__ mask, int N, int W, int nH, int nKV, int Lmax, int max_cache_len,
-    float scale_log2, int KPS, float* __restrict__ part_o, float* __restrict__ part_ml) {
+    float scale_log2, int KPS, float* __restrict__ part_o, float* __restrict__ part_ml, int* __restrict__ status) {
     constexpr int DE = D / 16;  // output columns per thread
     __shared__ float qs[ATT_QB][D];
     __shared__ float ks[ATT_TK][D + 1];
@@ -43,12 +43,15 @@ __global__ __launch_bounds__(ATT_THREADS) void tree_attn_valu_kernel(
     const int s = blockIdx.y;
     const int q0 = blockIdx.z * ATT_QB;
     const int tid = threadIdx.x;
-    // cache lengths above the host-declared bound are clamped (never read past Lmax)
-    const int P = max(0, min(cache_len[b], max_cache_len));
+    // cache lengths outside [0, max_cache_len] are clamped (never read past
+    // Lmax) and reported in the tree's status word
+    const int P_in = cache_len[b];
+    const int P = max(0, min(P_in, max_cache_len));
     const int total = P + N;
 
     // tree K/V -> cache slots P..P+N-1 (one writer per KV head)
     if (s == 0 && blockIdx.z == 0 && h % grp == 0) {
+        if (tid == 0 && P != P_in && status != nullptr) atomicOr(status, STATUS_CACHE_LEN_CLAMPED);
         for (int e = tid; e < N * D; e += ATT_THREADS) {
             const int t = e / D, c = e - t * D;
             const size_t src = (((size_t)b * N + t) * nKV + kvh) * D + c;
@@ -211,8 +214,13 @@ __global__ __launch_bounds__(ATT_MERGE_THREADS) void tree_attn_merge_kernel(cons
 // 32 QG of them) against one key range.  Ranges 0..S-2 each cover KPS
 // consecutive prefix keys (cache slots); range S-1 is the N tree keys, read
 // from k_tree / v_tree under the ancestor mask.  The tree range's workgroup of
-// query block 0 also copies the tree keys/values into cache slots P..P+N-1
-// (no other workgroup reads those slots).  With several query blocks per head
+// query block 0 also copies the tree keys/values into cache slots P..P+N-1.
+// The last tile of a prefix range may load slots at and past P (its rows are
+// clamped to the host bound max_cache_len, not to P, since the tiles are
+// requested before P is read), racing with that copy; those keys' scores are
+// masked and their V elements zeroed before the P.V product, so whatever the
+// slots hold (old data, the new tree keys, NaN) never reaches the output.
+// With several query blocks per head
 // the blocks of one key range get linear workgroup ids 8 apart: workgroups are
 // dealt to the 8 XCDs round-robin, so the blocks land on one XCD and read the
 // range's K/V through the same L2.
@@ -257,7 +265,7 @@ __global__ __launch_bounds__(ATT_MERGE_THREADS) void tree_attn_merge_kernel(cons
 // tiles in flight), then one barrier per tile publishes the tile and frees
 // the stage the next load overwrites.  No tile past the range is requested;
 // rows of the last tile past the range are clamped to its last row (their
-// scores are masked).  Within a
+// scores are masked and their V elements zeroed).  Within a
 // stage a row's 16-byte chunks are XOR-swizzled by a function of the row, so
 // the K fragment reads (16 rows, one chunk) and the transposing V reads (4
 // rows, two chunks) hit distinct LDS banks.  The first tiles are requested
@@ -333,7 +341,8 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_tree, const bf16_t* __restrict__ v_tree,
     bf16_t* __restrict__ k_cache, bf16_t* __restrict__ v_cache, const int32_t* __restrict__ cache_len,
     const uint64_t* __restrict__ mask, int N, int W, int nH, int nKV, int Lmax, int max_cache_len,
-    float scale_log2, int KPS, int S, int QB, int BH, float* __restrict__ part_o, float* __restrict__ part_ml) {
+    float scale_log2, int KPS, int S, int QB, int BH, float* __restrict__ part_o, float* __restrict__ part_ml,
+    int* __restrict__ status) {
     constexpr int TK = MF_TK;
     constexpr int KG = 8 / QG;                   // key groups
     constexpr int KW = TK / KG;                  // keys per wave per tile
@@ -459,8 +468,12 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
     if (nt_spec > 1) issue(1, 1);
     if (nt_spec > 2) issue(2, 2);
 
-    // the sequence's prefix length decides the range's true size
-    const int P = max(0, min(cache_len[b], max_cache_len));
+    // the sequence's prefix length decides the range's true size; a length
+    // outside [0, max_cache_len] is clamped and reported in the status word
+    const int P_in = cache_len[b];
+    const int P = max(0, min(P_in, max_cache_len));
+    if (tree && qblk == 0 && h % grp == 0 && tid == 0 && P != P_in && status != nullptr)
+        atomicOr(status, STATUS_CACHE_LEN_CLAMPED);
     const int nkeys = tree ? N : min(KPS, P - k0);
     if (nkeys <= 0) {  // a range past this sequence's prefix: empty partials
         if (tid < QW) {
@@ -596,10 +609,24 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
                         const uint32_t r23 = pack_bf16x2(p4[2] - bf16_lo(h23), p4[3] - bf16_hi(h23));
                         pb[qb] = (u32x4){h01, h23, r01, r23};
                     }
+                    // rows past the prefix in the last tile of a prefix range
+                    // hold whatever the cache slots hold (they were requested
+                    // before the prefix length was known): their probability is
+                    // 0, but 0 times a NaN or infinite V is NaN, so the lane's V
+                    // elements of keys past the range are zeroed (element e of
+                    // the transposed read is key kk0 + e)
+                    uint32_t vkeep_x = ~0u, vkeep_y = ~0u;
+                    if (!tree && masked) {
+                        const int nv = nkeys - (i * TK + kq * KW + kb * 16 + lk * 4);  // the lane's keys in range
+                        vkeep_x = nv >= 2 ? ~0u : nv == 1 ? 0x0000FFFFu : 0u;
+                        vkeep_y = nv >= 4 ? ~0u : nv == 3 ? 0x0000FFFFu : 0u;
+                    }
                     // O^T += V^T . P^T over the block's 16 keys
 #pragma unroll
                     for (int db = 0; db < DB; ++db) {
-                        const uint2 v = __builtin_bit_cast(uint2, ds_read_tr16(st + voff[db] + kb * 16 * ROWB));
+                        uint2 v = __builtin_bit_cast(uint2, ds_read_tr16(st + voff[db] + kb * 16 * ROWB));
+                        v.x &= vkeep_x;
+                        v.y &= vkeep_y;
                         const u32x4 va = (u32x4){v.x, v.y, v.x, v.y};  // the 4 keys' V^T values, twice
 #pragma unroll
                         for (int qb = 0; qb < 2; ++qb)
@@ -746,7 +773,7 @@ void launch_tree_attention(const void* q, const void* k_tree, const void* v_tree
 #define MEDUSA_MF(DD, QG)                                                                                    \
     MEDUSA_LAUNCH("tree_attn_mfma", (tree_attn_mfma_kernel<DD, QG>), grid, dim3(MF_THREADS), 0, s, Q, KT, VT, \
                   KC, VC, cache_len, t.mask, N, t.W, nH, nKV, Lmax, max_cache_len, scale_log2, pl.KPS, pl.S,  \
-                  pl.QB, B * nH, part_o, part_ml)
+                  pl.QB, B * nH, part_o, part_ml, t.status)
         const int qg = mf_qg(N);
         if (D == 64) {
             if (qg == 2) MEDUSA_MF(64, 2); else if (qg == 4) MEDUSA_MF(64, 4); else MEDUSA_MF(64, 8);
@@ -759,7 +786,7 @@ void launch_tree_attention(const void* q, const void* k_tree, const void* v_tree
 #define MEDUSA_ATT(T, DD)                                                                                   \
     MEDUSA_LAUNCH("tree_attn_split", (tree_attn_valu_kernel<T, DD>), grid, dim3(ATT_THREADS), 0, s,         \
                   (const T*)q, (const T*)k_tree, (const T*)v_tree, (T*)k_cache, (T*)v_cache, cache_len,     \
-                  t.mask, N, t.W, nH, nKV, Lmax, max_cache_len, scale_log2, pl.KPS, part_o, part_ml)
+                  t.mask, N, t.W, nH, nKV, Lmax, max_cache_len, scale_log2, pl.KPS, part_o, part_ml, t.status)
         if (bf16) {
             if (D == 64) MEDUSA_ATT(bf16_t, 64); else MEDUSA_ATT(bf16_t, 128);
         } else {

@@ -12,6 +12,11 @@ constexpr int MEDUSA_MAX_TOPK_DEV = 16;
 constexpr int MEDUSA_MAX_DEPTH_DEV = 16;
 constexpr int MEDUSA_MAX_NODES_DEV = 256;
 
+// Bits of a tree handle's status word (the MEDUSA_STATUS_* values of the C
+// header): an invalid device-side length was clamped or an operation skipped.
+constexpr int STATUS_CACHE_LEN_CLAMPED = 1;
+constexpr int STATUS_CACHE_OVERFLOW = 2;
+
 // ---------------------------------------------------------------------------
 // Storage types
 // ---------------------------------------------------------------------------

@@ -174,7 +174,8 @@ __global__ __launch_bounds__(256) void accept_compact_kernel(
     const int32_t* __restrict__ node_tok, const int32_t* __restrict__ greedy,
     int32_t* __restrict__ accept_len, int32_t* __restrict__ accept_nodes, int32_t* __restrict__ out_tokens,
     const int32_t* __restrict__ cache_len, int32_t* __restrict__ new_cache_len, T* __restrict__ k_cache,
-    T* __restrict__ v_cache, int nKV, int D, int Lmax, int64_t layer_stride, int n_slices, TypicalArgs ta) {
+    T* __restrict__ v_cache, int nKV, int D, int Lmax, int64_t layer_stride, int n_slices, TypicalArgs ta,
+    int* __restrict__ status) {
     __shared__ int s_acc_depth[256];
     __shared__ int s_par[256], s_tok[256], s_g[256];
     __shared__ int s_path[MEDUSA_MAX_DEPTH_DEV + 1];
@@ -237,6 +238,9 @@ __global__ __launch_bounds__(256) void accept_compact_kernel(
     }
     __syncthreads();
     const int L = s_L;
+    // caches whose tree slots P..P+N-1 would not fit: nothing is compacted,
+    // the length is not advanced, and the tree's status word says so
+    const bool overflow = k_cache != nullptr && (P < 0 || P + N > Lmax);
 
     if (blockIdx.y == 0 && tid <= Dmax) {
         const int d = tid;
@@ -250,12 +254,13 @@ __global__ __launch_bounds__(256) void accept_compact_kernel(
         }
         if (d == 0) {
             accept_len[b] = L;
-            new_cache_len[b] = P + L + 1;
+            new_cache_len[b] = overflow ? P : P + L + 1;
+            if (overflow && status != nullptr) atomicOr(status, STATUS_CACHE_OVERFLOW);
         }
     }
 
     // nothing to move, or a cache length that would address past Lmax
-    if (k_cache == nullptr || L == 0 || P < 0 || P + N > Lmax) return;
+    if (k_cache == nullptr || L == 0 || overflow) return;
     // slice s = layer * nKV + kv head
     const int s = blockIdx.y;
     if (s >= n_slices) return;
@@ -517,11 +522,13 @@ static void launch_accept_t(const TreeDev& t, const int32_t* node_tok, const int
     if (bf16)
         MEDUSA_LAUNCH(name, (accept_compact_kernel<bf16_t, TYPICAL>), grid, dim3(256), 0, s, t.parent, t.depth,
                       t.N, t.max_depth, node_tok, greedy, accept_len, accept_nodes, out_tokens, cache_len,
-                      new_cache_len, (bf16_t*)k_cache, (bf16_t*)v_cache, nKV, D, Lmax, layer_stride, n_slices, ta);
+                      new_cache_len, (bf16_t*)k_cache, (bf16_t*)v_cache, nKV, D, Lmax, layer_stride, n_slices, ta,
+                      t.status);
     else
         MEDUSA_LAUNCH(name, (accept_compact_kernel<float, TYPICAL>), grid, dim3(256), 0, s, t.parent, t.depth,
                       t.N, t.max_depth, node_tok, greedy, accept_len, accept_nodes, out_tokens, cache_len,
-                      new_cache_len, (float*)k_cache, (float*)v_cache, nKV, D, Lmax, layer_stride, n_slices, ta);
+                      new_cache_len, (float*)k_cache, (float*)v_cache, nKV, D, Lmax, layer_stride, n_slices, ta,
+                      t.status);
 }
 
 void launch_accept(const TreeDev& t, const int32_t* node_tok, const int32_t* greedy, int B,

@@ -17,6 +17,7 @@ struct TreeDev {
     int* depth = nullptr;      // device [N]
     int* rank = nullptr;       // device [N]
     uint64_t* mask = nullptr;  // device [N][W]
+    int* status = nullptr;     // device word: STATUS_* bits set by the kernels (atomic OR)
     std::vector<int> h_parent, h_depth, h_rank;
     std::vector<uint64_t> h_mask;
 };

@@ -31,11 +31,18 @@ class MedusaLoop:
     h [B][H] (the heads' dtype) and root_tok [B] int32: the state the first
     round starts from.  max_cache_len bounds every prefix length the rounds
     reach (default Lmax - N: any state the caches can hold).  tokens [B][cap]
-    collects every round's output; n_tokens [B] counts it."""
+    collects every round's output; n_tokens [B] counts it.
+
+    Capacity: a round grows a prefix by at most Dmax + 1 tokens (Dmax = the
+    tree's depth), so from the longest starting prefix P0 (start_len, or read
+    from cache_len once here) the loop can run (max_cache_len - P0) // (Dmax +
+    1) rounds before a prefix could pass max_cache_len.  round() and run()
+    refuse to enqueue a round beyond that (ValueError), since the device would
+    otherwise only clamp the length and flag it in the tree's status word."""
 
     def __init__(self, heads, layers, embedding, lm_head: Packed, tree: Tree, topk: int, k_cache, v_cache, nH: int,
                  cache_len, h, root_tok, max_cache_len: int | None = None, cap: int = 1024, rms_eps: float = 1e-6,
-                 rope_base: float = 10000.0):
+                 rope_base: float = 10000.0, start_len: int | None = None):
         dev = h.device
         self.heads, self.layers, self.embedding, self.lm_head, self.tree = heads, layers, embedding, lm_head, tree
         self.topk, self.nH, self.rms_eps, self.rope_base = topk, nH, rms_eps, rope_base
@@ -48,6 +55,9 @@ class MedusaLoop:
         K = w2.heads if isinstance(w2, Packed) else w2.shape[0]
         self.B, self.N, self.K = B, N, K
         self.max_cache_len = Lmax - N if max_cache_len is None else int(max_cache_len)
+        if self.max_cache_len + N > Lmax:
+            raise ValueError(f"max_cache_len + N = {self.max_cache_len + N} exceeds Lmax = {Lmax}")
+        self.restart(int(cache_len.max().item()) if start_len is None else int(start_len))
         i32 = dict(dtype=torch.int32, device=dev)
         self.topk_idx = torch.empty(B, K, topk, **i32)
         self.topk_val = torch.empty(B, K, topk, dtype=torch.float32, device=dev)
@@ -67,8 +77,25 @@ class MedusaLoop:
         F = layers[0]["w_gate_up"].rows // 2
         self.ws_dec = _ws(decoder_workspace_size(tree, B, H, nH, nKV, D, F, V, self.max_cache_len), dev, None)
 
+    def restart(self, start_len: int):
+        """Set the round budget from start_len, the longest prefix the
+        sequences now hold (after the caller restored or replaced the state)."""
+        if start_len > self.max_cache_len:
+            raise ValueError(f"a starting prefix of {start_len} tokens exceeds max_cache_len = {self.max_cache_len}")
+        self.rounds_left = (self.max_cache_len - int(start_len)) // (self.tree.max_depth + 1)
+
+    def _reserve(self, rounds: int):
+        if rounds > self.rounds_left:
+            raise ValueError(f"{rounds} more rounds could grow a prefix past max_cache_len = {self.max_cache_len}: "
+                             f"{self.rounds_left} fit")
+        self.rounds_left -= rounds
+
     def round(self, stream=None):
         """One round on `stream` (torch's current stream if None)."""
+        self._reserve(1)
+        self._enqueue(stream)
+
+    def _enqueue(self, stream):
         hd = self.heads
         medusa_heads_forward(self.h, hd.get("w1"), hd.get("b1"), hd["w2"], self.topk, self.topk_idx, self.topk_val,
                              ws=self.ws_heads, stream=stream)
@@ -85,5 +112,6 @@ class MedusaLoop:
                        cache_len=self.cache_len, stream=stream)
 
     def run(self, rounds: int, stream=None):
+        self._reserve(rounds)
         for _ in range(rounds):
-            self.round(stream)
+            self._enqueue(stream)

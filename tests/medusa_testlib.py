@@ -155,6 +155,42 @@ def tol(dtype_str):
     return 1e-4 if dtype_str == "f32" else 2e-2
 
 
+def bf16_step(x):
+    """One bf16 step (unit in the last place) at the magnitude of x."""
+    return 2.0 ** (np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126))) - 7)
+
+
+def pv_atol(v_cache, v_tree, cache_len):
+    """Absolute accuracy of the bf16 attention path before its output is
+    rounded: each probability enters the P.V product with 17 significant bits
+    (a bf16 head plus a bf16 remainder), so an output, a convex combination of
+    values, is off by at most 2^-17 max|v| (plus float32 accumulation, far
+    smaller); twice that.  Matters only for outputs near 0, where one bf16
+    step is smaller still."""
+    m = float(np.abs(v_tree).max())
+    for b, P in enumerate(np.asarray(cache_len)):
+        if P > 0:
+            m = max(m, float(np.abs(v_cache[b, :, :P]).max()))
+    return 2.0 ** -16 * m
+
+
+def assert_bf16_close(got, ref, min_exact=0.99, atol=1e-6, what=""):
+    """bf16 outputs against float64 oracle values: every element within one
+    bf16 step of the oracle value rounded to bf16 (a rounding flip at most;
+    atol covers values near 0), and at least ``min_exact`` of them equal to it.
+    Well inside 2e-2 everywhere, and tight enough that a wrong mask or scale
+    (moves of a few 1e-3 on outputs of size 0.04) fails."""
+    rb = oracle.round_bf16(ref)
+    err = np.abs(np.asarray(got, dtype=np.float64) - rb)
+    lim = bf16_step(ref) + atol
+    bad = err > lim
+    exact = float(np.mean(err == 0))
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} elements beyond one bf16 step; "
+                           f"worst {float((err - lim).max()):.3g} past it")
+    assert exact >= min_exact, f"{what}: only {exact:.4f} of the elements equal the rounded oracle"
+    return exact
+
+
 # ---------------------------------------------------------------------------
 # one whole step on the GPU, in the call sequence and launch shapes bench.py
 # times (the same C-ABI calls with the same arguments)

@@ -190,3 +190,50 @@ def test_profiler_without_launches(M):
     M.profiler_reset()
     assert M.profiler_collect() == {}
     M.profiler_enable(False)
+
+
+def test_tree_status_argument_errors(M):
+    L = M._lib
+    v = ctypes.c_int32(-1)
+    assert L.medusa_tree_status(None, ctypes.byref(v), 1, None) == M.EINVAL
+    assert "null" in L.medusa_last_error().decode()
+    assert v.value == -1            # nothing written on an error
+
+
+def test_status_bits_match_the_header(M):
+    src = open(HEADER).read()
+    bits = dict(re.findall(r"#define\s+MEDUSA_(STATUS_\w+)\s+(\d+)", src))
+    assert int(bits["STATUS_CACHE_LEN_CLAMPED"]) == M.STATUS_CACHE_LEN_CLAMPED
+    assert int(bits["STATUS_CACHE_OVERFLOW"]) == M.STATUS_CACHE_OVERFLOW
+
+
+class _StubTree:
+    def __init__(self, max_depth):
+        self.max_depth = max_depth
+
+
+def _loop_budget(M, max_cache_len, start_len, max_depth):
+    loop = M.MedusaLoop.__new__(M.MedusaLoop)     # the host-side budget only; no device buffers
+    loop.max_cache_len = max_cache_len
+    loop.tree = _StubTree(max_depth)
+    loop.restart(start_len)
+    return loop
+
+
+def test_loop_refuses_rounds_past_the_cache(M):
+    # a round grows a prefix by at most Dmax + 1 = 6 tokens: from 4000 under a
+    # bound of 4096, 16 rounds fit (4096 = 4000 + 16 * 6), the 17th could overrun
+    loop = _loop_budget(M, 4096, 4000, 5)
+    assert loop.rounds_left == 16
+    with pytest.raises(ValueError):
+        loop.run(17)
+    assert loop.rounds_left == 16        # a refused run reserves nothing
+    loop._reserve(10)
+    loop._reserve(6)
+    with pytest.raises(ValueError):
+        loop._reserve(1)
+    loop.restart(4096 - 6)
+    assert loop.rounds_left == 1
+    with pytest.raises(ValueError):
+        _loop_budget(M, 4096, 4097, 5)   # a start past the bound
+    assert _loop_budget(M, 100, 100, 5).rounds_left == 0

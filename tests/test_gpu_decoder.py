@@ -16,17 +16,26 @@ oracle alone, multiplying the attention output of one full-width layer by
 changes the residual stream by 0.3% of its RMS and the normalised rows by up
 to 0.031.  The float outputs of this multi-layer pass are therefore checked
 against max(4e-2, two bf16 steps) per element and 1% of the values' RMS for
-the RMS of the difference.  The same cascade moves the lm_head scores: at the
+the RMS of the difference; beyond that, the elements farther than 2e-2 (the
+bf16 tolerance of the step's single-layer outputs) from the oracle are
+counted, printed, and capped at 0.1% of the elements.  Through all 32
+layers the cascade is larger: the same 1.5e-4 perturbation of every layer's
+attention output, at hidden 512, moves the final normalised rows by up to
+0.078, by 1.5% of their RMS, and 16% of them by more than 2e-2 (keys and
+values of the last layer: 0.034 at most, 0.4% past 2e-2); the 32-layer case
+is checked against 0.1 per element (and two bf16 steps), 2% of the RMS, and at
+most 20% of the elements past 2e-2.  The same cascade moves
+the lm_head scores: at the
 full width over two layers, that 1.5e-4 noise moves them by 0.0069 RMS and
 0.038 at most (scores of RMS 1.28), so a 1e-2 margin between a node's best two
 scores is about one standard deviation of the noise on their difference.  The
-margin enforced for the full-width case is 0.1 (above twice the largest
-measured move); the narrow cases keep 1e-2.  The greedy choices must then
-match exactly.  Cases span the 64-, 128- and 256-row
+margin enforced for the full-width case and the 32-layer case is 0.1 (above
+twice the largest measured move); the other narrow cases keep 1e-2.  The
+greedy choices must then match exactly.  Cases span the 64-, 128- and 256-row
 tile shapes of the projections, GQA, ragged cache lengths, a gate|up product
-split over its contraction, and two layers at
-the full Llama-7B width (hidden 4096, 32 x 128 heads, MLP 11008, vocabulary
-32000, 4096-token caches, sparse 64-node tree).
+split over its contraction, two layers at the full Llama-7B width (hidden
+4096, 32 x 128 heads, MLP 11008, vocabulary 32000, 4096-token caches, sparse
+64-node tree), and all 32 layers of the 32-layer workload at hidden 512.
 """
 import sys
 
@@ -43,9 +52,22 @@ pytestmark = pytest.mark.gpu
 BF16_STEP = 2.0 ** -7
 
 
-def _close(got, ref):
-    np.testing.assert_allclose(got, ref, rtol=2 * BF16_STEP, atol=4e-2)
-    assert np.sqrt(np.mean((got - ref) ** 2)) <= 1e-2 * np.sqrt(np.mean(ref ** 2))
+# (per-element atol, RMS of the difference / RMS of the values, largest
+# fraction of elements past 2e-2): up to 3 layers, and for all 32 layers
+BOUNDS = {"shallow": (4e-2, 1e-2, 1e-3), "deep": (0.1, 2e-2, 0.2)}
+
+
+def _close(got, ref, what="", tally=None, depth="shallow"):
+    atol, rms_ratio, cap = BOUNDS[depth]
+    np.testing.assert_allclose(got, ref, rtol=2 * BF16_STEP, atol=atol)
+    assert np.sqrt(np.mean((got - ref) ** 2)) <= rms_ratio * np.sqrt(np.mean(ref ** 2))
+    beyond = int(np.count_nonzero(np.abs(got - ref) > 2e-2))
+    if tally is not None:
+        tally[0] += beyond
+        tally[1] += got.size
+    if beyond:
+        _say(what, beyond, "of", got.size, "elements beyond 2e-2, largest", float(np.abs(got - ref).max()))
+    assert beyond <= cap * got.size, (what, beyond, got.size)
 
 
 def _say(*a):
@@ -66,9 +88,12 @@ CASES = [
     # a narrow MLP under long rows: the gate|up product splits its contraction
     # (fp32 partial sums, then the separate SwiGLU kernel)
     ("split_gate_up_h2048_f128", lambda: _cfg("d6", 1, 2048, 1000, mi.sparse_tree(24), 16, 16, 128, (64,), 506, 1, 128)),
+    # the 32-layer workload's depth (layer strides of all 32 caches, the
+    # cascade through 32 layers) at a width the float64 oracle runs in seconds
+    ("depth32_h512_sparse64", lambda: _cfg("d7", 1, 512, 2000, mi.sparse_tree(64), 4, 4, 128, (300,), 507, 32, 1024)),
 ]
 # margin between each node's best two lm_head scores
-MARGIN = {"full_width_2layers": 0.1}
+MARGIN = {"full_width_2layers": 0.1, "depth32_h512_sparse64": 0.1}
 
 
 def _enforce_gap(cfg, lm_head, rows, gap=GAP, max_iter=1000):
@@ -135,17 +160,20 @@ def test_decoder_verify_parity(name, mk):
     torch.cuda.synchronize()
 
     assert np.array_equal(greedy.cpu().numpy(), g_ref)
-    _close(host_f64(hidden), ref["hidden"])
+    tally = [0, 0]
+    depth = "deep" if L > 3 else "shallow"
+    _close(host_f64(hidden), ref["hidden"], "hidden", tally, depth)
     kh, vh = host_f64(k_cache), host_f64(v_cache)
     for l in range(L):
         for b in range(B):
             got_k = kh[l, b, :, P[b]:P[b] + N].transpose(1, 0, 2)   # [N][nKV][D]
             got_v = vh[l, b, :, P[b]:P[b] + N].transpose(1, 0, 2)
-            _close(got_k, ref["k_tree"][l][b])
-            _close(got_v, ref["v_tree"][l][b])
+            _close(got_k, ref["k_tree"][l][b], f"layer {l} keys", tally, depth)
+            _close(got_v, ref["v_tree"][l][b], f"layer {l} values", tally, depth)
             # the prefix is never written
             assert np.array_equal(kh[l, b, :, :P[b]], kc[l][b, :, :P[b]])
-    _say("ok")
+            assert np.array_equal(vh[l, b, :, :P[b]], vc[l][b, :, :P[b]])
+    _say("ok;", tally[0], "of", tally[1], "checked elements beyond 2e-2")
 
 
 def test_decoder_argument_errors():

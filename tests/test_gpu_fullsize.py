@@ -19,7 +19,8 @@ import torch
 
 import medusa_inputs as mi
 import oracle
-from medusa_testlib import (enforce_greedy_gap, enforce_heads_gap, oracle_attention_seqs, run_step_gpu, tol)
+from medusa_testlib import (assert_bf16_close, enforce_greedy_gap, enforce_heads_gap, oracle_attention_seqs,
+                            pv_atol, run_step_gpu, tol)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +46,7 @@ def test_full_step(M, c):
     att = mi.gen_attention(cfg)
     root = mi.gen_root_tokens(cfg)
     ov = []
-    logits_ref, _ = enforce_heads_gap(cfg, heads, ov)                 # [K][V][B]
+    logits_ref, z_ref = enforce_heads_gap(cfg, heads, ov)             # [K][V][B], [B][K][H]
     idx_ref, val_ref = oracle.topk(np.transpose(logits_ref, (2, 0, 1)), cfg.topk)
     del logits_ref
     P = np.asarray(cfg.P)
@@ -57,6 +58,10 @@ def test_full_step(M, c):
 
     got = run_step_gpu(M, cfg, heads, att, root)
 
+    # the residual-SiLU block's float32 output, in the launch shape the step uses
+    z_err = float(np.abs(got["z"] - z_ref).max())
+    _say("z max abs error", z_err)
+    np.testing.assert_allclose(got["z"], z_ref, rtol=0, atol=tol(cfg.dtype))
     assert np.array_equal(got["topk_idx"], idx_ref)
     np.testing.assert_allclose(got["topk_val"], val_ref, rtol=0, atol=tol(cfg.dtype))
     parent, rank = cfg.tree.arrays()
@@ -65,7 +70,12 @@ def test_full_step(M, c):
     assert np.array_equal(got["node_pos"], pos_ref)
     lm = None
     for b in seqs:
-        np.testing.assert_allclose(got["o"][b], o_ref[b], rtol=0, atol=tol(cfg.dtype))
+        # o_ref is already rounded to bf16 (the boundary's output type)
+        vw = oracle.widen(att["v_tree"][b:b + 1], cfg.dtype)
+        vcw = oracle.widen(att["v_cache"][b:b + 1, :, :P[b]], cfg.dtype)
+        exact = assert_bf16_close(got["o"][b], o_ref[b], atol=pv_atol(vcw, vw, [P[b]]),
+                                  what=f"attention, sequence {b}")
+        _say("attention exactly rounded fraction", b, round(exact, 5))
         if lm is None:
             lm = oracle.widen(heads["lm_head"], cfg.dtype)
         g_ref, _ = oracle.base_greedy(o_ref[b].reshape(cfg.N, cfg.H), lm, 1e-6)

@@ -11,7 +11,8 @@ import torch
 
 import medusa_inputs as mi
 import oracle
-from medusa_testlib import dev, enforce_greedy_gap, enforce_heads_gap, host_f64, make_workload, tol
+from medusa_testlib import (assert_bf16_close, dev, enforce_greedy_gap, enforce_heads_gap, host_f64, make_workload,
+                            pv_atol, tol)
 
 pytestmark = pytest.mark.gpu
 
@@ -175,7 +176,12 @@ def test_tree_attention_parity(M, name, mk):
     scale = float(np.float32(1.0 / np.sqrt(cfg.D)))
     ref = oracle.tree_attention(w["q"], w["k_tree"], w["v_tree"], w["k_cache"], w["v_cache"], att["cache_len"],
                                 parent, scale)
-    np.testing.assert_allclose(host_f64(out), ref, rtol=0, atol=tol(cfg.dtype))
+    if cfg.dtype == "bf16":
+        exact = assert_bf16_close(host_f64(out), ref, atol=pv_atol(w["v_cache"], w["v_tree"], att["cache_len"]),
+                                  what=name)
+        _say("exactly rounded fraction", round(exact, 5))
+    else:
+        np.testing.assert_allclose(host_f64(out), ref, rtol=0, atol=tol(cfg.dtype))
     # the tree's keys/values now sit at slots P..P+N-1; every other slot is untouched
     kc_ref = kc0.clone()
     vc_ref = vc0.clone()
@@ -343,3 +349,251 @@ def test_accept_without_caches(M):
     assert al.item() == L and ncl.item() == 10 + L + 1
     assert an[0, :L + 1].cpu().numpy().tolist() == path.tolist()
     assert ot[0, :L + 1].cpu().numpy().tolist() == toks.tolist()
+
+
+# ---------------------------------------------------------------------------
+# cache slots past the prefix never reach the output
+# ---------------------------------------------------------------------------
+
+NAN_CASES = [
+    # ragged sequences under one host bound: every sequence but the longest has
+    # slots in [P_b, max_cache_len) that the last tile of a prefix range loads
+    ("bf16_sparse64_b3_ragged", lambda: _cfg("n1", "bf16", 3, 256, 10, 5, 4, mi.sparse_tree(64), 4, 2, 128,
+                                             (1, 777, 1000), 221), 2300),
+    ("bf16_dense256_d64_b2", lambda: _cfg("n2", "bf16", 2, 256, 10, 5, 3, mi.dense_tree(256), 2, 2, 64,
+                                          (70, 513), 222), 600),
+    ("bf16_sparse100_b2", lambda: _cfg("n3", "bf16", 2, 256, 10, 5, 4, mi.sparse_tree(100), 4, 4, 128,
+                                       (333, 100), 223), 700),
+    ("f32_tiny_b2", lambda: _cfg("n4", "f32", 2, 256, 10, 3, 3, mi.tiny_tree(), 4, 4, 64, (30, 97), 224), 200),
+]
+
+
+@pytest.mark.parametrize("name,mk,maxP", NAN_CASES, ids=[c[0] for c in NAN_CASES])
+def test_tree_attention_ignores_slots_past_prefix(M, name, mk, maxP):
+    """Slots at and past cache_len[b] hold NaN and infinities; the result must
+    equal the oracle's, which reads slots < cache_len[b] only."""
+    cfg = mk()
+    _say("attention, NaN past the prefix", name, "max_cache_len", maxP)
+    att = mi.gen_attention(cfg)
+    parent, rank = cfg.tree.arrays()
+    t = M.Tree(parent, rank, cfg.K, cfg.topk)
+    Lmax = maxP + cfg.N
+    B, nKV, D = cfg.B, cfg.nKV, cfg.D
+    kc_h = np.empty((B, nKV, Lmax, D), dtype=att["k_cache"].dtype)
+    vc_h = np.empty_like(kc_h)
+    nan, inf = (np.uint16(0x7FC0), np.uint16(0x7F80)) if cfg.dtype == "bf16" else (np.float32(np.nan),
+                                                                                     np.float32(np.inf))
+    kc_h[...] = nan
+    vc_h[...] = nan
+    vc_h[..., 1::3, :] = inf
+    for b, P in enumerate(cfg.P):
+        kc_h[b, :, :P] = att["k_cache"][b, :, :P]
+        vc_h[b, :, :P] = att["v_cache"][b, :, :P]
+    q, kt, vt = (dev(att[k]) for k in ("q", "k_tree", "v_tree"))
+    kc, vc = dev(kc_h), dev(vc_h)
+    out = torch.empty_like(q)
+    M.tree_attention_verify(q, kt, vt, kc, vc, dev(att["cache_len"]), maxP, t, out)
+    torch.cuda.synchronize()
+    got = host_f64(out)
+    assert np.isfinite(got).all()
+    w = {k: oracle.widen(att[k], cfg.dtype) for k in ("q", "k_tree", "v_tree", "k_cache", "v_cache")}
+    ref = oracle.tree_attention(w["q"], w["k_tree"], w["v_tree"], w["k_cache"], w["v_cache"], att["cache_len"],
+                                parent, float(np.float32(1.0 / np.sqrt(cfg.D))))
+    if cfg.dtype == "bf16":
+        assert_bf16_close(got, ref, atol=pv_atol(w["v_cache"], w["v_tree"], att["cache_len"]), what=name)
+    else:
+        np.testing.assert_allclose(got, ref, rtol=0, atol=tol(cfg.dtype))
+    assert t.status() == 0
+
+
+# ---------------------------------------------------------------------------
+# the tree's status word: invalid device-side lengths are reported
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_status_word_reports_clamped_cache_len(M, dtype):
+    cfg = _cfg("s1", dtype, 2, 256, 10, 5, 4, mi.sparse_tree(64), 2, 2, 128, (100, 100), 231)
+    _say("status: clamped cache_len", dtype)
+    att = mi.gen_attention(cfg)
+    parent, rank = cfg.tree.arrays()
+    t = M.Tree(parent, rank, cfg.K, cfg.topk)
+    maxP = 100
+    q, kt, vt, kc, vc = (dev(att[k]) for k in ("q", "k_tree", "v_tree", "k_cache", "v_cache"))
+    out = torch.empty_like(q)
+    assert t.status() == 0
+    M.tree_attention_verify(q, kt, vt, kc, vc, dev(np.array([100, 64], np.int32)), maxP, t, out)
+    assert t.status() == 0
+    # sequence 0 claims more than the host bound, sequence 1 a negative length:
+    # both are clamped into [0, max_cache_len] (all accesses stay in bounds)
+    M.tree_attention_verify(q, kt, vt, kc, vc, dev(np.array([maxP + 7, -5], np.int32)), maxP, t, out)
+    assert t.status(clear=False) == M.STATUS_CACHE_LEN_CLAMPED
+    assert t.status() == M.STATUS_CACHE_LEN_CLAMPED
+    assert t.status() == 0
+    # the clamped call computed attention at lengths maxP and 0
+    w = {k: oracle.widen(att[k], cfg.dtype) for k in ("q", "k_tree", "v_tree", "k_cache", "v_cache")}
+    ref = oracle.tree_attention(w["q"], w["k_tree"], w["v_tree"], w["k_cache"], w["v_cache"], [maxP, 0], parent,
+                                float(np.float32(1.0 / np.sqrt(cfg.D))))
+    np.testing.assert_allclose(host_f64(out), ref, rtol=0, atol=tol(cfg.dtype))
+
+
+def test_status_word_reports_cache_overflow(M):
+    tree = mi.sparse_tree(64)
+    parent, rank = tree.arrays()
+    _say("status: cache overflow in accept")
+    B, nKV, D, K, topk = 2, 2, 64, 5, 4
+    t = M.Tree(parent, rank, K, topk)
+    tk = np.arange(B * K * topk, dtype=np.int32).reshape(B, K, topk) + 100
+    Lmax = 200
+    P = np.array([50, Lmax - tree.n + 1], dtype=np.int32)     # sequence 1's tree slots would pass Lmax
+    tok, _, _ = oracle.build_tree(parent, rank, tk, np.array([1, 2]), P)
+    g = _planted_greedy(tree, tk, tok, np.zeros((B, K), dtype=np.int64))   # both accept the rank-0 chain
+    cache = mi.normal((1, B, nKV, Lmax, D), 60, mi.S_TEST + 7, 1.0, "bf16")
+    kc, vc = dev(cache), dev(cache)
+    al = torch.empty(B, dtype=torch.int32, device="cuda")
+    an = torch.empty(B, t.max_depth + 1, dtype=torch.int32, device="cuda")
+    ot = torch.empty_like(an)
+    ncl = torch.empty(B, dtype=torch.int32, device="cuda")
+    M.medusa_accept(t, dev(tok), dev(g), al, an, ot, dev(P), ncl, k_cache=kc, v_cache=vc)
+    torch.cuda.synchronize()
+    assert t.status() == M.STATUS_CACHE_OVERFLOW
+    assert al.cpu().numpy().tolist() == [t.max_depth, t.max_depth]
+    # sequence 0 compacted and advanced; sequence 1 untouched and not advanced
+    assert ncl.cpu().numpy().tolist() == [P[0] + t.max_depth + 1, P[1]]
+    L0, path0, _ = oracle.accept(parent, tok[0], g[0])
+    ref0, _ = oracle.compact_kv(cache[0, 0], int(P[0]), path0)
+    got = kc.cpu().view(torch.int16).numpy().view(np.uint16)[0]
+    assert np.array_equal(got[0], ref0)
+    assert np.array_equal(got[1], cache[0, 1])
+    # without caches nothing can overflow
+    M.medusa_accept(t, dev(tok), dev(g), al, an, ot, dev(P), ncl)
+    torch.cuda.synchronize()
+    assert t.status() == 0
+    assert ncl.cpu().numpy().tolist() == [P[0] + t.max_depth + 1, P[1] + t.max_depth + 1]
+
+
+# ---------------------------------------------------------------------------
+# the tie rule: among equal scores the lower vocabulary index ranks first
+# ---------------------------------------------------------------------------
+
+def _dup_positions(t, V, spread):
+    """Rows to copy the winning row t to: within the same 16-row fragment
+    ('near') or hundreds of rows away, in other workgroups ('far').  Returns
+    (rows holding a copy, expected order of the tied rows)."""
+    if spread == "near":
+        cands = [t - 1, t + 1, t + 5]
+    else:
+        cands = [t - 517, t - 1200, t + 733, t + 2100]
+    rows = sorted(set(c for c in cands if 0 <= c < V and c != t))
+    return rows, sorted(rows + [t])
+
+
+@pytest.mark.parametrize("spread", ["near", "far"])
+@pytest.mark.parametrize("layout", ["rows", "packed"])
+def test_topk_ties_keep_lower_index(M, layout, spread):
+    B = 1 if layout == "rows" else 4          # the step's layouts: GEMV at 1 sequence, MFMA from 4
+    cfg = _cfg("tie", "bf16", B, 1024, 5003, 3, 4, mi.tiny_tree(), seed=241)
+    _say("top-k ties", layout, spread)
+    heads = mi.gen_heads(cfg)
+    logits_ref, _ = enforce_heads_gap(cfg, heads, [])           # [K][V][B]
+    # each head: copy sequence 0's winning row of W2 to other rows; a copy
+    # scores exactly what the original scores, for every sequence
+    order = []
+    for k in range(cfg.K):
+        tw = int(np.lexsort((np.arange(cfg.V), -oracle.round_f32(logits_ref[k, :, 0])))[0])
+        rows, tied = _dup_positions(tw, cfg.V, spread)
+        heads["W2"][k, rows] = heads["W2"][k, tw]
+        logits_ref[k, rows] = logits_ref[k, tw]
+        order.append(tied)
+    idx_ref, _ = oracle.topk(np.transpose(logits_ref, (2, 0, 1)), cfg.topk)
+    for k in range(cfg.K):                                       # the oracle's rule: tied rows by index
+        n = min(len(order[k]), cfg.topk)
+        assert idx_ref[0, k, :n].tolist() == order[k][:n]
+    h, W1, b1, W2 = (dev(heads[k]) for k in ("h", "W1", "b1", "W2"))
+    if layout == "packed":
+        W1, W2 = M.pack_heads(W1), M.pack_heads(W2)
+    ti = torch.empty(B, cfg.K, cfg.topk, dtype=torch.int32, device="cuda")
+    tv = torch.empty(B, cfg.K, cfg.topk, device="cuda")
+    M.medusa_heads_forward(h, W1, b1, W2, cfg.topk, ti, tv)
+    torch.cuda.synchronize()
+    got, val = ti.cpu().numpy(), tv.cpu().numpy()
+    for k in range(cfg.K):                                       # the copies scored bit for bit alike
+        n = min(len(order[k]), cfg.topk)
+        assert len(set(val[0, k, :n].tolist())) == 1, (k, val[0, k])
+    assert np.array_equal(got, idx_ref)
+
+
+@pytest.mark.parametrize("spread", ["near", "far"])
+@pytest.mark.parametrize("layout", ["rows", "packed"])
+def test_greedy_ties_keep_lower_index(M, layout, spread):
+    R, H, V = 64, 1024, 5000
+    cfg = _cfg("gtie", "bf16", 1, H, V, 1, 1, mi.tiny_tree(), seed=251)
+    _say("argmax ties", layout, spread)
+    heads = {"lm_head": mi.normal((V, H), cfg.seed, mi.S_LM_HEAD, 0.02, "bf16")}
+    x = mi.normal((R, H), cfg.seed, mi.S_TEST, 1.0, "bf16")
+    xw = oracle.widen(x, "bf16")
+    enforce_greedy_gap(cfg, heads, xw, [])
+    g0, _ = oracle.base_greedy(xw, oracle.widen(heads["lm_head"], "bf16"), 1e-6)
+    # copy the winners of a few rows to other rows of lm_head
+    for r in (0, 17, 63):
+        rows, _ = _dup_positions(int(g0[r]), V, spread)
+        heads["lm_head"][rows] = heads["lm_head"][int(g0[r])]
+    g_ref, _ = oracle.base_greedy(xw, oracle.widen(heads["lm_head"], "bf16"), 1e-6)
+    for r in (0, 17, 63):
+        _, order = _dup_positions(int(g0[r]), V, spread)
+        assert g_ref[r] == order[0]       # the oracle's rule: the lowest of the tied rows
+    g = torch.empty(R, dtype=torch.int32, device="cuda")
+    lm = dev(heads["lm_head"])
+    if layout == "packed":
+        lm = M.pack(lm)
+    M.medusa_base_greedy(dev(x), lm, g, eps=1e-6)
+    torch.cuda.synchronize()
+    assert np.array_equal(g.cpu().numpy(), g_ref)
+
+
+# ---------------------------------------------------------------------------
+# compaction at the 32-layer workload's cache shape, deepest branches
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("tree,K,topk,nKV,D,layers", [
+    (mi.sparse_tree(64), 5, 4, 32, 128, 32),     # the 32-layer workload's caches: L = Dmax = 5, 640 elements a slice
+    (mi.chain_tree(16), 16, 1, 4, 128, 4),       # the deepest tree: L = 16, 2048 elements a slice
+    (mi.dense_tree(256), 5, 3, 8, 128, 6),
+], ids=["sparse64_nkv32_d128_32layers", "chain16_d128", "dense256_d128"])
+def test_deep_compaction_bench_shape(M, tree, K, topk, nKV, D, layers):
+    _say("deep compaction", tree.name, "nKV", nKV, "D", D, "layers", layers)
+    B = 2
+    parent, rank = tree.arrays()
+    r = np.random.default_rng(19)
+    tk = np.stack([np.stack([r.choice(30000, topk, replace=False) for _ in range(K)]) for _ in range(B)]).astype(np.int32)
+    root = r.integers(0, 30000, B).astype(np.int32)
+    P = np.array([300, 7], dtype=np.int32)
+    tok, _, _ = oracle.build_tree(parent, rank, tk, root, P)
+    truth = np.zeros((B, K), dtype=np.int64)                   # the rank-0 chain all the way down
+    if tree.name.startswith("dense"):
+        truth[1] = [1, 1, 2, 0, 1]                             # a depth-5 branch under the second child (the
+        #                                                        256-node cut keeps depth-5 tuples (0, ..) and (1, 0|1, ..))
+    g = _planted_greedy(tree, tk, tok, truth)
+    Lmax = int(P.max()) + tree.n + 3
+    cache_k = mi.normal((layers, B, nKV, Lmax, D), 70, mi.S_TEST + 11, 1.0, "bf16")
+    cache_v = mi.normal((layers, B, nKV, Lmax, D), 70, mi.S_TEST + 12, 1.0, "bf16")
+    t = M.Tree(parent, rank, K, topk)
+    kc, vc = dev(cache_k), dev(cache_v)
+    Dm = t.max_depth
+    al = torch.empty(B, dtype=torch.int32, device="cuda")
+    an = torch.empty(B, Dm + 1, dtype=torch.int32, device="cuda")
+    ot = torch.empty(B, Dm + 1, dtype=torch.int32, device="cuda")
+    ncl = torch.empty(B, dtype=torch.int32, device="cuda")
+    M.medusa_accept(t, dev(tok), dev(g), al, an, ot, dev(P), ncl, k_cache=kc, v_cache=vc)
+    torch.cuda.synchronize()
+    assert t.status() == 0
+    kh = kc.cpu().view(torch.int16).numpy().view(np.uint16)
+    vh = vc.cpu().view(torch.int16).numpy().view(np.uint16)
+    for b in range(B):
+        L, path, toks = oracle.accept(parent, tok[b], g[b])
+        assert L == Dm
+        assert al[b].item() == L and ncl[b].item() == P[b] + L + 1
+        assert an[b].cpu().numpy().tolist() == path.tolist()
+        assert ot[b].cpu().numpy().tolist() == toks.tolist()
+        for src, got in ((cache_k, kh), (cache_v, vh)):
+            ref, _ = oracle.compact_kv(src[:, b], int(P[b]), path)     # bit patterns, every layer and head
+            assert np.array_equal(got[:, b], ref)
