@@ -130,6 +130,27 @@ medusa_status medusa_heads_forward(const void* h, const void* w1, const void* b1
                                    void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * medusa_heads_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and arguments without a workspace.  z
+ * and the top-k partials live in a library-owned device array of
+ * MEDUSA_STATIC_SCRATCH_BYTES on each GPU the library runs on (held until the
+ * process ends).  Nothing in it needs to start at zero: every call writes what
+ * it reads.  Calls that overlap on one GPU (several streams or threads) race
+ * on the array; serialise them.  The first call on each device looks up the
+ * array's device address (make it outside a graph capture).  Returns
+ * MEDUSA_EUNSUPPORTED, enqueuing nothing, when
+ * medusa_heads_workspace_size(...) exceeds MEDUSA_STATIC_SCRATCH_BYTES
+ * (8 sequences x 5 heads x hidden 4096 x vocabulary 128256 need about 3.9
+ * MB).  Allocates nothing: no hipMalloc, no allocating library call.
+ * ------------------------------------------------------------------------- */
+#define MEDUSA_STATIC_SCRATCH_BYTES (8u << 20)
+medusa_status medusa_heads_forward_static(const void* h, const void* w1, const void* b1, const void* w2,
+                                          medusa_layout layout,
+                                          int B, int H, int V, int K, int topk, medusa_dtype dt,
+                                          float* logits, int32_t* topk_idx, float* topk_val, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Step a3 -- candidate tree (tree section: Cartesian product of the heads'
  * top guesses, sharing prefixes).
  *

@@ -37,6 +37,8 @@ _SIGS = {
     "medusa_heads_workspace_size": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32], _sz),
     "medusa_heads_forward": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz,
                               _vp], _i32),
+    "medusa_heads_forward_static": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
+                                     _vp], _i32),
     "medusa_tree_create": ([_vp, _vp, _i32, _i32, _i32, ctypes.POINTER(_vp)], _i32),
     "medusa_tree_destroy": ([_vp], None),
     "medusa_tree_num_nodes": ([_vp], _i32),
@@ -176,6 +178,23 @@ def medusa_heads_forward(h, w1, b1, w2, topk, topk_idx, topk_val, logits=None, w
     _check("medusa_heads_forward", _lib.medusa_heads_forward(
         _p(h), _p(w1), _p(b1), _p(w2), layout, B, H, V, K, topk, dt, _p(logits), _p(topk_idx), _p(topk_val),
         _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return topk_idx, topk_val
+
+
+STATIC_SCRATCH_BYTES = 8 << 20
+
+
+def medusa_heads_forward_static(h, w1, b1, w2, topk, topk_idx, topk_val, logits=None, stream=None):
+    """medusa_heads_forward without a workspace: the library's static device
+    scratch array holds z and the top-k partials (nothing is allocated)."""
+    K, V, H = w2.shape
+    B = h.shape[0]
+    if w1 is not None:
+        assert isinstance(w1, Packed) == isinstance(w2, Packed), "w1 and w2 must share one layout"
+    layout, dt = _w_args(w2)
+    _check("medusa_heads_forward_static", _lib.medusa_heads_forward_static(
+        _p(h), _p(w1), _p(b1), _p(w2), layout, B, H, V, K, topk, dt, _p(logits), _p(topk_idx), _p(topk_val),
+        _stream(stream)))
     return topk_idx, topk_val
 
 

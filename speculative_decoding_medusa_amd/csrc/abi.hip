@@ -356,6 +356,64 @@ medusa_status medusa_heads_forward(const void* h, const void* w1, const void* b1
 }
 
 // ---------------------------------------------------------------------------
+// medusa_heads_forward without a caller workspace: z and the top-k partials
+// go to `scratch`, a file-scope device array of MEDUSA_STATIC_SCRATCH_BYTES.
+// In host code `scratch` names a host-side stand-in, not the device array, so
+// its device address is looked up once per device (hipGetSymbolAddress, with
+// that device current) and only that address is handed to kernels.
+// ---------------------------------------------------------------------------
+}  // extern "C"
+
+static __device__ __align__(256) char scratch[MEDUSA_STATIC_SCRATCH_BYTES];
+static std::mutex g_scratch_mu;
+static std::vector<void*> g_scratch_dev;  // per device: scratch's device address (null until looked up)
+
+static void* scratch_on_current_device() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) failf(MEDUSA_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if ((int)g_scratch_dev.size() <= dev) g_scratch_dev.resize((size_t)dev + 1, nullptr);
+    if (g_scratch_dev[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            failf(MEDUSA_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_dev[dev] = p;
+    }
+    return g_scratch_dev[dev];
+}
+
+extern "C" {
+
+medusa_status medusa_heads_forward_static(const void* h, const void* w1, const void* b1, const void* w2,
+                                          medusa_layout layout, int B, int H, int V, int K, int topk,
+                                          medusa_dtype dt, float* logits, int32_t* topk_idx, float* topk_val,
+                                          void* stream) {
+    return guarded("medusa_heads_forward_static", [&] {
+        // the same argument checks as medusa_heads_forward, then the size limit
+        check_vocab(B, H, V, K, topk, dt, layout);
+        if (w1) check_w1_layout(H, dt, layout);
+        REQUIRE(h && w2 && topk_idx && topk_val, "null pointer argument");
+        REQUIRE((w1 == nullptr) == (b1 == nullptr), "w1 and b1 must both be given or both be NULL");
+        const size_t need = medusa_heads_workspace_size(B, H, V, K, topk, dt, layout);
+        SUPPORT(need <= MEDUSA_STATIC_SCRATCH_BYTES,
+                "these sizes need %zu bytes of scratch; the static array holds %zu (use medusa_heads_forward)",
+                need, (size_t)MEDUSA_STATIC_SCRATCH_BYTES);
+        void* ws = scratch_on_current_device();
+        float* z = (float*)ws;
+        void* vws = (char*)ws + align256((size_t)B * K * H * 4);
+        hipStream_t s = (hipStream_t)stream;
+        if (w1)
+            run_resid_silu(h, w1, layout, b1, B, H, K, dt, z, s);
+        else
+            MEDUSA_LAUNCH("broadcast_h", broadcast_h_kernel, dim3(64), dim3(256), 0, s, h, B, H, K,
+                          dt == MEDUSA_BF16 ? 1 : 0, z);
+        run_vocab_topk(z, w2, layout, B, H, V, K, topk, dt, logits, topk_idx, topk_val, vws, s);
+    });
+}
+
+// ---------------------------------------------------------------------------
 // a3 tree
 // ---------------------------------------------------------------------------
 medusa_status medusa_tree_create(const int32_t* parent, const int32_t* rank, int N, int K, int topk,
