@@ -18,6 +18,11 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
     # packed fp32 instructions are disabled for the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the first kernel arguments arrive in SGPRs at wave launch instead of
+    # through a dependent scalar load from the kernarg segment (gfx950 kernel
+    # argument preloading; code objects keep a compatibility prologue that
+    # loads them where the firmware does not preload)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-I", os.path.join(ROOT, "include"),
 ]
 

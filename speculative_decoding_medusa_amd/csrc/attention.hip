@@ -226,15 +226,18 @@ __global__ __launch_bounds__(ATT_MERGE_THREADS) void tree_attn_merge_kernel(cons
 // range's K/V through the same L2.
 //
 // Inside the workgroup, 8 waves = QG query groups x KG = 8 / QG key groups:
-// wave w takes queries 32 (w % QG) .. +31 (two 16-query blocks) against the
+// wave w takes QBW blocks of 16 queries, 16 QBW (w % QG) .., against the
 // KW = 64 / KG keys 16 (w / QG) NKB .. of every 64-key tile (NKB = KW / 16
 // blocks of 16 keys), keeps its own online-softmax state, and the key groups
-// are merged through LDS at the end.  Up to 64 tree nodes QG = 2 (64 queries,
-// 4 key groups of 16 keys); up to 128 QG = 4; up to 256 QG = 8 (every wave
-// against the whole tile, no merge): a wide tree then shares each K/V tile,
-// its barrier and its loads among all its queries instead of re-streaming
-// the range once per 64 queries, and each wave has 4x the independent
-// products per tile.
+// are merged through LDS at the end.  Up to 64 tree nodes 4 x 2 with one
+// query block per wave: a single merge step of half-size states (2 query
+// groups of two blocks x 4 key groups read the tiles from LDS half as often,
+// but their two merge steps measured 2 us, more than the LDS reads save while
+// the loop waits on HBM anyway); up to 128 nodes 4 x 2 with two blocks; up to
+// 256 QG = 8 (every wave against the whole tile, no merge): a wide tree then
+// shares each K/V tile, its barrier and its loads among all its queries
+// instead of re-streaming the range once per 64 queries, and each wave has
+// 4x the independent products per tile.
 //
 // Contractions, in transposed form so that no register data moves between
 // lanes:
@@ -272,11 +275,16 @@ __global__ __launch_bounds__(ATT_MERGE_THREADS) void tree_attn_merge_kernel(cons
 // before the sequence's cache length is read (clamped to the host bound
 // max_cache_len, so they stay in bounds).  The 64-query variant stages its
 // queries in LDS with the same loads; the wider ones load each wave's query
-// fragments straight into registers once the first tiles are requested.
+// fragments straight into registers right after tile 0 is requested and
+// wait for both before requesting tiles 1 and 2.
 // ---------------------------------------------------------------------------
 constexpr int MF_TK = 64;       // keys per tile
-// query groups of a workgroup (32 queries each) for an N-node tree
-__host__ __device__ constexpr int mf_qg(int N) { return N <= 64 ? 2 : N <= 128 ? 4 : 8; }
+// query groups of a workgroup and 16-query blocks per wave for an N-node
+// tree: up to 64 nodes 4 groups of one block (two key groups), up to 128 4
+// groups of two blocks (two key groups), up to 256 8 groups of two blocks
+// (one key group)
+__host__ __device__ constexpr int mf_qg(int N) { return N <= 128 ? 4 : 8; }
+__host__ __device__ constexpr int mf_qbw(int N) { return N <= 64 ? 1 : 2; }
 constexpr int MF_THREADS = 512;
 constexpr int MF_STAGES = 4;
 constexpr float MF_LAZY = 8.f;  // log2 of the largest probability before a rescale
@@ -336,7 +344,7 @@ __device__ __forceinline__ void mf_loads_landed() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <int D, int QG>
+template <int D, int QG, int QBW>
 __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_tree, const bf16_t* __restrict__ v_tree,
     bf16_t* __restrict__ k_cache, bf16_t* __restrict__ v_cache, const int32_t* __restrict__ cache_len,
@@ -347,8 +355,8 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
     constexpr int KG = 8 / QG;                   // key groups
     constexpr int KW = TK / KG;                  // keys per wave per tile
     constexpr int NKB = KW / 16;                 // 16-key blocks per wave per tile
-    constexpr int QW = 32 * QG;                  // queries per workgroup
-    constexpr bool QLDS = QG == 2;               // queries staged in LDS (else straight into registers)
+    constexpr int QW = 16 * QBW * QG;            // queries per workgroup
+    constexpr bool QLDS = QW <= 64;              // queries staged in LDS (else straight into registers)
     constexpr int DK = D / 32;                   // k-steps of S^T over the head dimension
     constexpr int DB = D / 16;                   // 16-row blocks of O^T
     constexpr int DC = D / 8;                    // 16-byte chunks per key row
@@ -357,14 +365,14 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
     constexpr int STAGE_B = 2 * TILE_B;          // K tile, then V tile
     constexpr int BLKS = 2 * TILE_B / 1024;      // 1 KB load blocks per stage
     constexpr int NLD = BLKS / (MF_THREADS / 64);  // loads per wave per tile
-    static_assert(QG == 2 || QG == 4 || QG == 8, "query groups");
+    static_assert((QG == 2 || QG == 4 || QG == 8) && (QBW == 1 || QBW == 2), "query groups");
     static_assert(NLD >= 1 && NLD * (MF_THREADS / 64) == BLKS && (BLKS / 2) % NLD == 0, "load split");
     constexpr int QBLKS = QLDS ? QW * ROWB / 1024 : 8;  // 1 KB load blocks of the query block
     constexpr int NQLD = QBLKS / (MF_THREADS / 64);     // query loads per wave
     static_assert(NQLD >= 1 && NQLD * (MF_THREADS / 64) == QBLKS, "query load split");
     // after the key loop the stages hold the states of the key groups' waves
     // for their merge: O^T fragments + (M, l) per lane, one wave per stage
-    constexpr int MERGE_WAVE_F = 2 * DB * 64 * 4 + 2 * 64 * 2;
+    constexpr int MERGE_WAVE_F = QBW * DB * 64 * 4 + QBW * 64 * 2;
     static_assert(MERGE_WAVE_F * 4 <= STAGE_B && MF_STAGES == 4 && (KG / 2) * QG <= MF_STAGES,
                   "merge area: one wave state per stage");
     // four separate arrays, so the compiler can tell a stage being read from
@@ -413,17 +421,21 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
 
     // the lane's queries (a padded query, qi >= N, computes with the last
     // query's data and is never written)
-    int qidx[2];
+    int qidx[QBW];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) qidx[qb] = qblk * QW + qh * 32 + qb * 16 + lr;
-    u32x4 qf[2][DK];  // QLDS: read from LDS after the first tile barrier; else loaded below
+    for (int qb = 0; qb < QBW; ++qb) qidx[qb] = qblk * QW + qh * 16 * QBW + qb * 16 + lr;
+    u32x4 qf[QBW][DK];  // QLDS: read from LDS after the first tile barrier; else loaded below
     // in the tree range, the queries' ancestor rows (words past W are never
     // used: the range has W tiles), waited for before any load into LDS is
     // issued
-    uint64_t mrow[2][4] = {{~0ull, ~0ull, ~0ull, ~0ull}, {~0ull, ~0ull, ~0ull, ~0ull}};
+    uint64_t mrow[QBW][4];
+#pragma unroll
+    for (int qb = 0; qb < QBW; ++qb)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) mrow[qb][w] = ~0ull;
     if (tree) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < QBW; ++qb)
 #pragma unroll
             for (int w = 0; w < 4; ++w) mrow[qb][w] = mask[(size_t)min(qidx[qb], N - 1) * W + min(w, W - 1)];
         mf_loads_landed();
@@ -465,6 +477,20 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
     // size is known only after the cache length is read)
     const int nt_spec = (nspec + TK - 1) / TK;
     issue(0, 0);
+    if constexpr (!QLDS) {
+        // the wave's query fragments straight into registers, right behind
+        // tile 0's loads: one full wait covers both, and tile 0 is needed
+        // first anyway; tiles 1 and 2 are requested after it, so the wait
+        // leaves them in flight (and no compiler-placed wait for these
+        // loads remains after it)
+#pragma unroll
+        for (int qb = 0; qb < QBW; ++qb) {
+            const bf16_t* qrow = q + (((size_t)b * N + min(qidx[qb], N - 1)) * nH + h) * D;
+#pragma unroll
+            for (int ks = 0; ks < DK; ++ks) qf[qb][ks] = *(const u32x4*)(qrow + (ks * 4 + lk) * 8);
+        }
+        mf_loads_landed();
+    }
     if (nt_spec > 1) issue(1, 1);
     if (nt_spec > 2) issue(2, 2);
 
@@ -486,19 +512,6 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
         mf_loads_landed();  // no load into LDS outlives the workgroup
         return;
     }
-    if constexpr (!QLDS) {
-        // the wave's query fragments straight into registers, behind the
-        // first tiles' loads; waiting for all of them costs little more
-        // than the wait for tile 0 that follows anyway, and after a full
-        // vmcnt wait no compiler-placed wait for these loads remains
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            const bf16_t* qrow = q + (((size_t)b * N + min(qidx[qb], N - 1)) * nH + h) * D;
-#pragma unroll
-            for (int ks = 0; ks < DK; ++ks) qf[qb][ks] = *(const u32x4*)(qrow + (ks * 4 + lk) * 8);
-        }
-        mf_loads_landed();
-    }
     const int ntiles = (nkeys + TK - 1) / TK;
     // tile t has been requested iff t < ntiles, or t < 3 and t < nt_spec
     auto requested = [&](int t) { return t < ntiles || (t < 3 && t < nt_spec); };
@@ -516,10 +529,10 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
     for (int db = 0; db < DB; ++db)
         voff[db] = TILE_B + vrow * ROWB + (((db * 2 + ((lr & 3) >> 1)) ^ mf_swz<DC>(vrow)) * 16) + (lr & 1) * 8;
 
-    f32x4 o[2][DB];
-    float Mq[2], l[2];
+    f32x4 o[QBW][DB];
+    float Mq[QBW], l[QBW];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QBW; ++qb) {
         Mq[qb] = -3.402823466e38f;  // reference (scaled, base 2); finite so that M - M' never is inf - inf
         l[qb] = 0.f;                // this lane's share of the query's sum
 #pragma unroll
@@ -539,8 +552,8 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
                 if constexpr (QLDS) {
                     if (i == 0) {
 #pragma unroll
-                        for (int qb = 0; qb < 2; ++qb) {
-                            const int r = qh * 32 + qb * 16 + lr;
+                        for (int qb = 0; qb < QBW; ++qb) {
+                            const int r = qh * 16 * QBW + qb * 16 + lr;
 #pragma unroll
                             for (int ks = 0; ks < DK; ++ks)
                                 qf[qb][ks] = *(const u32x4*)(qlds + r * ROWB + (((ks * 4 + lk) ^ mf_swz<DC>(r)) * 16));
@@ -558,9 +571,9 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
 #pragma unroll
                     for (int ks = 0; ks < DK; ++ks) ka[ks] = *(const u32x4*)(st + koff[ks] + kb * 16 * ROWB);
                     const int kk0 = kq * KW + kb * 16 + lk * 4;  // the lane's first key of the block
-                    u32x4 pb[2];
+                    u32x4 pb[QBW];
 #pragma unroll
-                    for (int qb = 0; qb < 2; ++qb) {
+                    for (int qb = 0; qb < QBW; ++qb) {
                         f32x4 sc = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int ks = 0; ks < DK; ++ks)
@@ -629,7 +642,7 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
                         v.y &= vkeep_y;
                         const u32x4 va = (u32x4){v.x, v.y, v.x, v.y};  // the 4 keys' V^T values, twice
 #pragma unroll
-                        for (int qb = 0; qb < 2; ++qb)
+                        for (int qb = 0; qb < QBW; ++qb)
                             o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va),
                                                                                 __builtin_bit_cast(bf16x8, pb[qb]),
                                                                                 o[qb][db], 0, 0, 0);
@@ -641,7 +654,7 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
 
     // per-query sums over the 4 lanes of the query
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QBW; ++qb) {
         l[qb] += __shfl_xor(l[qb], 16, 64);
         l[qb] += __shfl_xor(l[qb], 32, 64);
     }
@@ -655,18 +668,18 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
         if (kq >= lo && kq < 2 * lo) {
             float* w = (float*)stage_ptr((kq - lo) * QG + qh);
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
+            for (int qb = 0; qb < QBW; ++qb) {
 #pragma unroll
                 for (int db = 0; db < DB; ++db) *(f32x4*)(w + ((qb * DB + db) * 64 + lane) * 4) = o[qb][db];
-                *(float2*)(w + 2 * DB * 64 * 4 + (qb * 64 + lane) * 2) = (float2){Mq[qb], l[qb]};
+                *(float2*)(w + QBW * DB * 64 * 4 + (qb * 64 + lane) * 2) = (float2){Mq[qb], l[qb]};
             }
         }
         __syncthreads();
         if (kq < lo) {
             const float* w = (const float*)stage_ptr(kq * QG + qh);
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const float2 ml = *(const float2*)(w + 2 * DB * 64 * 4 + (qb * 64 + lane) * 2);
+            for (int qb = 0; qb < QBW; ++qb) {
+                const float2 ml = *(const float2*)(w + QBW * DB * 64 * 4 + (qb * 64 + lane) * 2);
                 const float Mn = fmaxf(Mq[qb], ml.x);
                 const float fa = __builtin_amdgcn_exp2f(Mq[qb] - Mn), fb = __builtin_amdgcn_exp2f(ml.x - Mn);
                 Mq[qb] = Mn;
@@ -681,7 +694,7 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
     // d = db * 16 + 4 * lk + r of query column lr
     if (kq == 0) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < QBW; ++qb) {
             if (qidx[qb] < N) {
                 const size_t r = prow + qidx[qb];
 #pragma unroll
@@ -728,7 +741,7 @@ static AttnPlan attn_plan(bool bf16, int B, int nH, int N, int max_cache_len, in
         // whole number of 64-key tiles (measured: 7 ranges of 320 keys for
         // 32 heads x 2048 keys, 2 of 2048 for 4 query blocks x 32 heads x
         // 4096 keys, 3 of 2752 for 8 x 32 heads up to 8192 keys)
-        const int QW = 32 * mf_qg(N);
+        const int QW = 16 * mf_qbw(N) * mf_qg(N);
         p.QB = (N + QW - 1) / QW;
         const int target = target_wg > 0 ? target_wg : ATT_MFMA_TARGET_WG;
         const int units = B * nH * p.QB;
@@ -770,15 +783,15 @@ void launch_tree_attention(const void* q, const void* k_tree, const void* v_tree
         bf16_t *KC = (bf16_t*)k_cache, *VC = (bf16_t*)v_cache;
         const int units = B * nH * pl.S;
         const dim3 grid((unsigned)(((units + 7) / 8) * 8 * pl.QB));
-#define MEDUSA_MF(DD, QG)                                                                                    \
-    MEDUSA_LAUNCH("tree_attn_mfma", (tree_attn_mfma_kernel<DD, QG>), grid, dim3(MF_THREADS), 0, s, Q, KT, VT, \
-                  KC, VC, cache_len, t.mask, N, t.W, nH, nKV, Lmax, max_cache_len, scale_log2, pl.KPS, pl.S,  \
+#define MEDUSA_MF(DD, QG, QBW)                                                                                \
+    MEDUSA_LAUNCH("tree_attn_mfma", (tree_attn_mfma_kernel<DD, QG, QBW>), grid, dim3(MF_THREADS), 0, s, Q, KT,  \
+                  VT, KC, VC, cache_len, t.mask, N, t.W, nH, nKV, Lmax, max_cache_len, scale_log2, pl.KPS, pl.S, \
                   pl.QB, B * nH, part_o, part_ml, t.status)
-        const int qg = mf_qg(N);
+        const int qg = mf_qg(N), qbw = mf_qbw(N);
         if (D == 64) {
-            if (qg == 2) MEDUSA_MF(64, 2); else if (qg == 4) MEDUSA_MF(64, 4); else MEDUSA_MF(64, 8);
+            if (qbw == 1) MEDUSA_MF(64, 4, 1); else if (qg == 4) MEDUSA_MF(64, 4, 2); else MEDUSA_MF(64, 8, 2);
         } else {
-            if (qg == 2) MEDUSA_MF(128, 2); else if (qg == 4) MEDUSA_MF(128, 4); else MEDUSA_MF(128, 8);
+            if (qbw == 1) MEDUSA_MF(128, 4, 1); else if (qg == 4) MEDUSA_MF(128, 4, 2); else MEDUSA_MF(128, 8, 2);
         }
 #undef MEDUSA_MF
     } else {
