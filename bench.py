@@ -88,6 +88,8 @@ def parse():
     ap.add_argument("--typical", action="store_true",
                     help="sampling mode: the base greedy stage also writes the node rows' scores and "
                          "medusa_typical_accept (temperature 0.7, eps 0.09, delta 0.3) replaces medusa_accept")
+    ap.add_argument("--planted", type=float, default=None, metavar="ALPHA",
+                    help="with --loop: plant the base model's choices from the rank prior ALPHA (1-ALPHA)^r")
     ap.add_argument("--loop", type=int, default=0, metavar="ROUNDS",
                     help="with --config 5: time ROUNDS rounds of the device-resident generate loop (MedusaLoop), "
                          "eager and as one captured graph, and print that line instead")
@@ -498,11 +500,27 @@ def bench_decoder(args, cfg):
 
 def bench_loop(args, cfg):
     """ROUNDS rounds of the generate loop on the 32-layer workload: heads ->
-    tree -> decoder verify -> accept with compaction -> hand-off, nothing
-    waiting for the host.  The caches are the workload's; the rounds start
-    (Dmax + 1) * ROUNDS tokens before the workload's prefix length, so every
-    round fits the caches.  Timed eagerly and as one captured graph of all
-    ROUNDS rounds, each from the same initial state."""
+    tree -> decoder verify -> [planted choices] -> accept with compaction ->
+    hand-off, nothing waiting for the host.  The caches are the workload's;
+    the rounds start (Dmax + 1) * ROUNDS tokens before the workload's prefix
+    length, so every round fits the caches.  Timed eagerly and as one captured
+    graph of all ROUNDS rounds, each from the same initial state.
+
+    With --planted ALPHA the base model's choices are replaced after every
+    verify pass by a continuation drawn from the rank prior ALPHA (1 - ALPHA)^r
+    (medusa_plant_greedy), so the random-weight model accepts candidates the
+    way a trained one would: rounds accept deep branches and compact them in
+    all 32 layer caches, and the tokens per round are measured, not modelled.
+
+    The cost reading (the speculative-decoding e-book's accounting: a round
+    costs the drafting plus the verify pass, in units of one plain decoding
+    step, and yields E tokens): each stage of a round is timed with HIP events
+    in an eager pass, and a plain decoding step -- the same decoder pass over
+    a one-node tree, the root alone, plus its greedy choice -- is timed the
+    same way.  c_draft = heads / plain step, c_verify = verify / plain step,
+    c_rest = (tree + accept + hand-off) / plain step; modelled speedup =
+    E / (c_draft + c_verify + c_rest) with E the tokens per round, against the
+    measured speedup = tokens per round x plain step / round time."""
     import numpy as np
     import torch
 
@@ -538,8 +556,9 @@ def bench_loop(args, cfg):
     state = dict(cache_len=dev(P0), h=d["h"].clone(), root_tok=dev(mi.gen_root_tokens(cfg)))
     loop = M.MedusaLoop({"w1": d["W1"], "b1": d["b1"], "w2": d["W2"]}, layers, emb, lm_head, tree, topk, k_cache,
                         v_cache, cfg.nH, state["cache_len"].clone(), state["h"].clone(), state["root_tok"].clone(),
-                        max_cache_len=int(max(cfg.P)), cap=(tree.max_depth + 1) * R)
-    # only the accepted slots [P0, P0 + R (Dmax + 1)) change: keep them to restore the initial state
+                        max_cache_len=int(max(cfg.P)), cap=(tree.max_depth + 1) * R, planted=args.planted,
+                        plant_seed=2024)
+    # only the slots [P0, max P + N) change: keep them to restore the initial state
     lo, hi = int(P0.min()), int(max(cfg.P)) + N
     keep_k, keep_v = k_cache[..., lo:hi, :].clone(), v_cache[..., lo:hi, :].clone()
 
@@ -585,9 +604,70 @@ def bench_loop(args, cfg):
     graph_ms = e0.elapsed_time(e1)
     n_graph = loop.n_tokens.cpu().numpy()
     same = bool(np.array_equal(n_graph, n_eager) and np.array_equal(loop.tokens.cpu().numpy(), tokens_eager))
+    status = tree.status()
+
+    # --- the cost reading: every stage of a round timed with events (eager)
+    restore()
+    torch.cuda.synchronize()
+    stages = ("heads", "tree", "verify", "plant", "accept", "handoff")
+    acc_ms = dict.fromkeys(stages, 0.0)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+    hd = loop.heads
+    for _ in range(R):
+        ev[0].record()
+        M.medusa_heads_forward(loop.h, hd.get("w1"), hd.get("b1"), hd["w2"], loop.topk, loop.topk_idx, loop.topk_val,
+                               ws=loop.ws_heads)
+        ev[1].record()
+        M.medusa_build_tree(tree, loop.topk_idx, loop.root_tok, loop.cache_len, loop.node_tok, loop.node_pos)
+        ev[2].record()
+        M.medusa_decoder_verify(layers, emb, lm_head, tree, loop.node_tok, loop.node_pos, loop.cache_len,
+                                loop.max_cache_len, k_cache, v_cache, cfg.nH, loop.greedy, hidden=loop.hidden,
+                                ws=loop.ws_dec)
+        ev[3].record()
+        if args.planted is not None:
+            M.medusa_plant_greedy(tree, loop.topk_idx, loop.cache_len, loop.greedy, cfg.V, args.planted, 2024)
+        ev[4].record()
+        M.medusa_accept(tree, loop.node_tok, loop.greedy, loop.accept_len, loop.accept_nodes, loop.out_tokens,
+                        loop.cache_len, loop.new_cache_len, k_cache=k_cache, v_cache=v_cache)
+        ev[5].record()
+        M.medusa_advance(tree, loop.accept_len, loop.accept_nodes, loop.out_tokens, loop.hidden, loop.root_tok, loop.h,
+                         tokens=loop.tokens, n_tokens=loop.n_tokens, new_cache_len=loop.new_cache_len,
+                         cache_len=loop.cache_len)
+        ev[6].record()
+        torch.cuda.synchronize()
+        for j, st in enumerate(stages):
+            acc_ms[st] += ev[j].elapsed_time(ev[j + 1])
+    stage_us = {k: round(v * 1e3 / R, 2) for k, v in acc_ms.items()}
+
+    # --- a plain decoding step: the root alone through the same decoder, its greedy choice
+    restore()
+    one = M.Tree(np.array([-1], dtype=np.int32), np.array([0], dtype=np.int32), K, topk)
+    tok1 = loop.root_tok.view(B, 1).clone()
+    pos1 = loop.cache_len.view(B, 1).clone()
+    g1 = torch.empty(B, 1, dtype=torch.int32, device="cuda")
+    ws1 = M._ws(M.decoder_workspace_size(one, B, H, cfg.nH, cfg.nKV, cfg.D, cfg.ffn, cfg.V, loop.max_cache_len),
+                "cuda", None)
+    for _ in range(3):
+        M.medusa_decoder_verify(layers, emb, lm_head, one, tok1, pos1, loop.cache_len, loop.max_cache_len, k_cache,
+                                v_cache, cfg.nH, g1, ws=ws1)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(R):
+        M.medusa_decoder_verify(layers, emb, lm_head, one, tok1, pos1, loop.cache_len, loop.max_cache_len, k_cache,
+                                v_cache, cfg.nH, g1, ws=ws1)
+    e1.record()
+    torch.cuda.synchronize()
+    plain_us = e0.elapsed_time(e1) * 1e3 / R
+    restore()
+    torch.cuda.synchronize()
 
     expected = tree_prior_tokens(parent, rank)
     rounds_s = R / (graph_ms * 1e-3)
+    tpr = float(n_graph.sum()) / (B * R)
+    round_us = graph_ms * 1e3 / R
+    c_draft = stage_us["heads"] / plain_us
+    c_verify = stage_us["verify"] / plain_us
+    c_rest = (stage_us["tree"] + stage_us["accept"] + stage_us["handoff"]) / plain_us
     result = {
         "metric": "Medusa generate rounds/sec (32-layer Llama-7B-shaped decoder, device-resident loop)",
         "value": round(rounds_s, 2),
@@ -596,16 +676,28 @@ def bench_loop(args, cfg):
         "rounds": R,
         "higher_is_better": True,
         "dtype": "bf16",
-        "data": "synthetic (seeded Philox inputs, random-init weights)",
+        "data": "synthetic (seeded Philox inputs, random-init weights)" +
+                (f"; base-model choices planted from the rank prior alpha={args.planted}" if args.planted is not None
+                 else ""),
         "config": {"workload": cfg.name + "_loop", "batch": B, "tree_nodes": N, "decoder_layers": L,
-                   "start_prefix": P0.tolist(), "max_prefix": [int(p) for p in cfg.P]},
+                   "start_prefix": P0.tolist(), "max_prefix": [int(p) for p in cfg.P],
+                   "acceptance": "planted" if args.planted is not None else "model"},
         "ms_per_round_graph": round(graph_ms / R, 4),
         "ms_per_round_eager": round(eager_ms / R, 4),
         "graph_replay_matches_eager": same,
-        "tokens_per_round_measured": round(float(n_graph.sum()) / (B * R), 3),
+        "tree_status_word": status,
+        "tokens_per_round_measured": round(tpr, 3),
         "tokens_per_s_measured": round(float(n_graph.sum()) / (graph_ms * 1e-3), 1),
         "tokens_per_round_under_tree_prior": round(expected, 3),
-        "tokens_per_s_under_tree_prior": round(B * rounds_s * expected, 1),
+        "cost_reading": {
+            "stage_us": stage_us,
+            "plain_decode_step_us": round(plain_us, 2),
+            "plain_decode_tokens_per_s": round(B * 1e6 / plain_us, 1),
+            "c_draft": round(c_draft, 4), "c_verify": round(c_verify, 4), "c_rest": round(c_rest, 4),
+            "speedup_modelled": round(tpr / (c_draft + c_verify + c_rest), 3),
+            "speedup_modelled_prior": round(expected / (c_draft + c_verify + c_rest), 3),
+            "speedup_measured": round(tpr * plain_us / round_us, 3),
+        },
     }
     print(json.dumps(result), flush=True)
 

@@ -370,6 +370,25 @@ medusa_status medusa_advance(const medusa_tree* tree, const int32_t* accept_len,
                              const int32_t* new_cache_len, int32_t* cache_len, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Measurement aid, not a step of the method.  With random weights the base
+ * model's choices never match the heads' guesses, so every round accepts
+ * nothing.  medusa_plant_greedy overwrites greedy [B][N] (the base model's
+ * choice after every node, as medusa_base_greedy or medusa_decoder_verify
+ * wrote it) with a planted continuation: for sequence b and depth d, the
+ * token after every depth-d node is head (d + 1)'s rank-r guess
+ * topk_idx[b][d][r] with probability alpha (1 - alpha)^r (r < topk), else a
+ * token outside that head's top-k (at depth K: any token), drawn with the
+ * counter hash of (seed, b, cache_len[b], d) -- a new prefix length draws a new
+ * continuation, so a captured loop draws anew every round.  A round then
+ * accepts the ranks drawn as far as the tree holds them: 1 + sum over nodes of
+ * the product of alpha (1 - alpha)^rank along their path tokens per round on
+ * average (the rank prior the sparse tree was chosen under, with alpha =
+ * 0.8).  One kernel; no workspace.  Limits: tree depth <= 16, K >= depth.
+ * ------------------------------------------------------------------------- */
+medusa_status medusa_plant_greedy(const medusa_tree* tree, const int32_t* topk_idx, const int32_t* cache_len, int B,
+                                  int K, int topk, int V, float alpha, uint64_t seed, int32_t* greedy, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Step a8 -- the tree-verify forward pass through a Llama-shaped decoder
  * ("Medusa Heads" glossary, section on tree attention and acceptance: every
  * candidate is appended to the input of one forward pass of the base model,

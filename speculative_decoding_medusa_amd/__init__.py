@@ -60,6 +60,7 @@ _SIGS = {
                                _i32, _i64, _i32, _i32, _i32, _i32, _vp, _sz, _vp], _i32),
     "medusa_speculative_sample": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp], _i32),
     "medusa_advance": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp], _i32),
+    "medusa_plant_greedy": ([_vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, ctypes.c_uint64, _vp, _vp], _i32),
     "medusa_decoder_workspace_size": ([_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32], _sz),
     "medusa_decoder_verify": ([_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
                                _i32, _i32, _i32, _i32, _f32, _f32, _vp, _vp, _vp, _sz, _vp], _i32),
@@ -438,6 +439,17 @@ def medusa_advance(tree: Tree, accept_len, accept_nodes, out_tokens, hidden, roo
         tree.handle, _p(accept_len), _p(accept_nodes), _p(out_tokens), _p(hidden), B, H, _dt(h), _p(root_tok),
         _p(h), _p(tokens), _p(n_tokens), cap, _p(new_cache_len), _p(cache_len), _stream(stream)))
     return root_tok
+
+
+def medusa_plant_greedy(tree: Tree, topk_idx, cache_len, greedy, V: int, alpha: float = 0.8, seed: int = 0,
+                        stream=None):
+    """Measurement aid: overwrite greedy [B][N] with a continuation drawn
+    from the rank prior alpha (1 - alpha)^r (see include/medusa.h)."""
+    B, K, topk = topk_idx.shape
+    _check("medusa_plant_greedy", _lib.medusa_plant_greedy(
+        tree.handle, _p(topk_idx), _p(cache_len), B, K, topk, int(V), float(alpha), ctypes.c_uint64(seed),
+        _p(greedy), _stream(stream)))
+    return greedy
 
 
 # ---------------------------------------------------------------------------

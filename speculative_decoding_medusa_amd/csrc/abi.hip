@@ -52,6 +52,9 @@ void launch_accept(const TreeDev& t, const int32_t* node_tok, const int32_t* gre
 struct LayerPtrs {
     const bf16_t *wqkv, *wo, *w_gate_up, *w_down;
 };
+void launch_plant_greedy(const TreeDev& t, const int32_t* topk_idx, int B, int K, int topk,
+                         const int32_t* cache_len, float alpha, uint64_t seed, int V, int32_t* greedy,
+                         hipStream_t s);
 void launch_advance(const TreeDev& t, const int32_t* accept_len, const int32_t* accept_nodes,
                     const int32_t* out_tokens, const float* hidden, int B, int H, bool bf16, int32_t* root_tok,
                     void* h, int32_t* tokens, int32_t* n_tokens, int cap, const int32_t* new_cache_len,
@@ -724,6 +727,23 @@ medusa_status medusa_advance(const medusa_tree* tree, const int32_t* accept_len,
                 "new_cache_len and cache_len must both be given or both NULL");
         launch_advance(tree->t, accept_len, accept_nodes, out_tokens, hidden, B, H, dt == MEDUSA_BF16, root_tok, h,
                        tokens, n_tokens, cap, new_cache_len, cache_len, (hipStream_t)stream);
+    });
+}
+
+// ---------------------------------------------------------------------------
+// measurement aid: planted base-model choices
+// ---------------------------------------------------------------------------
+medusa_status medusa_plant_greedy(const medusa_tree* tree, const int32_t* topk_idx, const int32_t* cache_len, int B,
+                                  int K, int topk, int V, float alpha, uint64_t seed, int32_t* greedy, void* stream) {
+    return guarded("medusa_plant_greedy", [&] {
+        REQUIRE(tree && topk_idx && cache_len && greedy, "null pointer argument");
+        REQUIRE(B >= 1 && V >= 1, "B and V must be positive (B=%d V=%d)", B, V);
+        REQUIRE(K >= tree->t.max_depth, "K=%d is smaller than the tree depth %d", K, tree->t.max_depth);
+        REQUIRE(topk >= 1 && topk > tree->t.max_rank, "topk=%d does not cover rank %d", topk, tree->t.max_rank);
+        SUPPORT(tree->t.max_depth <= MEDUSA_MAX_DEPTH, "tree depth %d exceeds %d", tree->t.max_depth,
+                MEDUSA_MAX_DEPTH);
+        REQUIRE(alpha >= 0.f && alpha <= 1.f, "alpha=%g must be in [0, 1]", alpha);
+        launch_plant_greedy(tree->t, topk_idx, B, K, topk, cache_len, alpha, seed, V, greedy, (hipStream_t)stream);
     });
 }
 

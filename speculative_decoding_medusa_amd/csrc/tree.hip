@@ -559,6 +559,68 @@ void launch_typical_accept(const TreeDev& t, const int32_t* node_tok, const floa
 }
 
 // ---------------------------------------------------------------------------
+// Measurement aid, not a step of the method: with random weights the base
+// model never agrees with the heads, so every round would accept nothing.
+// This replaces the base model's choice after every node by a continuation
+// drawn per sequence and depth from a rank prior -- the token after a depth-d
+// node is head (d + 1)'s rank-r guess with probability alpha (1 - alpha)^r, or
+// a token outside its top-k with the remaining probability -- so a round
+// accepts the branch of ranks drawn, as far as the tree holds it.  The draw
+// for (sequence b, depth d) is a counter hash of (seed, b, cache_len[b], d):
+// a new prefix length gives a new continuation, and graph replays draw anew.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t mix64(uint64_t z) {
+    z += 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+__global__ __launch_bounds__(256) void plant_greedy_kernel(const int* __restrict__ depth, int N, int max_depth,
+                                                           const int32_t* __restrict__ topk_idx, int K, int topk,
+                                                           const int32_t* __restrict__ cache_len, float alpha,
+                                                           uint64_t seed, int V, int32_t* __restrict__ greedy) {
+    __shared__ int s_next[MEDUSA_MAX_DEPTH_DEV + 1];  // the token after a node of depth d
+    const int b = blockIdx.x, tid = threadIdx.x;
+    if (tid <= max_depth) {
+        const int d = tid;
+        const uint64_t z = mix64(mix64(mix64(seed ^ (uint64_t)b) ^ (uint64_t)(uint32_t)cache_len[b]) ^ (uint64_t)d);
+        const float u = (float)(z >> 40) * (1.0f / 16777216.0f);
+        const int32_t* cand = topk_idx + ((size_t)b * K + min(d, K - 1)) * topk;
+        // the rank drawn: the first r with u < sum_{j <= r} alpha (1 - alpha)^j
+        int r = topk;
+        float cum = 0.f, pr = alpha;
+        for (int j = 0; j < topk && d < K; ++j) {
+            cum += pr;
+            if (u < cum) { r = j; break; }
+            pr *= 1.f - alpha;
+        }
+        int tok;
+        if (r < topk) {
+            tok = cand[r];
+        } else {  // a token outside the head's top-k (at depth K: any token)
+            tok = (int)((mix64(z) >> 33) % (uint64_t)V);
+            for (int it = 0; it <= topk && d < K; ++it) {
+                bool hit = false;
+                for (int j = 0; j < topk; ++j) hit = hit || cand[j] == tok;
+                if (!hit) break;
+                tok = tok + 1 < V ? tok + 1 : 0;
+            }
+        }
+        s_next[d] = tok;
+    }
+    __syncthreads();
+    for (int i = tid; i < N; i += blockDim.x) greedy[(size_t)b * N + i] = s_next[depth[i]];
+}
+
+void launch_plant_greedy(const TreeDev& t, const int32_t* topk_idx, int B, int K, int topk,
+                         const int32_t* cache_len, float alpha, uint64_t seed, int V, int32_t* greedy,
+                         hipStream_t s) {
+    MEDUSA_LAUNCH("plant_greedy", plant_greedy_kernel, dim3(B), dim3(256), 0, s, t.depth, t.N, t.max_depth, topk_idx,
+                  K, topk, cache_len, alpha, seed, V, greedy);
+}
+
+// ---------------------------------------------------------------------------
 // Hand-off to the next round.  Block b reads sequence b's L and deepest
 // accepted node (uniform over the block), gathers that node's final
 // normalised row into h[b] (converted to T), sets the next root to the bonus

@@ -18,7 +18,8 @@ from __future__ import annotations
 import torch
 
 from . import (Packed, Tree, _ws, decoder_workspace_size, heads_workspace_size, medusa_accept, medusa_advance,
-               medusa_build_tree, medusa_decoder_verify, medusa_heads_forward, ROW_MAJOR, PACKED, BF16, F32)
+               medusa_build_tree, medusa_decoder_verify, medusa_heads_forward, medusa_plant_greedy, ROW_MAJOR, PACKED,
+               BF16, F32)
 
 
 class MedusaLoop:
@@ -38,14 +39,22 @@ class MedusaLoop:
     from cache_len once here) the loop can run (max_cache_len - P0) // (Dmax +
     1) rounds before a prefix could pass max_cache_len.  round() and run()
     refuse to enqueue a round beyond that (ValueError), since the device would
-    otherwise only clamp the length and flag it in the tree's status word."""
+    otherwise only clamp the length and flag it in the tree's status word.
+
+    planted (measurement aid): None, or the alpha of a rank prior; then after
+    the verify pass the base model's choices are replaced by a continuation
+    drawn from that prior (medusa_plant_greedy, keyed by plant_seed and each
+    sequence's prefix length), so that random weights accept candidates the
+    way a trained model would and the rounds compact deep branches."""
 
     def __init__(self, heads, layers, embedding, lm_head: Packed, tree: Tree, topk: int, k_cache, v_cache, nH: int,
                  cache_len, h, root_tok, max_cache_len: int | None = None, cap: int = 1024, rms_eps: float = 1e-6,
-                 rope_base: float = 10000.0, start_len: int | None = None):
+                 rope_base: float = 10000.0, start_len: int | None = None, planted: float | None = None,
+                 plant_seed: int = 0):
         dev = h.device
         self.heads, self.layers, self.embedding, self.lm_head, self.tree = heads, layers, embedding, lm_head, tree
         self.topk, self.nH, self.rms_eps, self.rope_base = topk, nH, rms_eps, rope_base
+        self.planted, self.plant_seed = planted, plant_seed
         self.k_cache, self.v_cache = k_cache, v_cache
         self.cache_len, self.h, self.root_tok = cache_len, h, root_tok
         n_layers, B, nKV, Lmax, D = k_cache.shape
@@ -53,7 +62,7 @@ class MedusaLoop:
         V, H = embedding.shape
         w2 = heads["w2"]
         K = w2.heads if isinstance(w2, Packed) else w2.shape[0]
-        self.B, self.N, self.K = B, N, K
+        self.B, self.N, self.K, self.V = B, N, K, V
         self.max_cache_len = Lmax - N if max_cache_len is None else int(max_cache_len)
         if self.max_cache_len + N > Lmax:
             raise ValueError(f"max_cache_len + N = {self.max_cache_len + N} exceeds Lmax = {Lmax}")
@@ -105,6 +114,9 @@ class MedusaLoop:
                               self.cache_len, self.max_cache_len, self.k_cache, self.v_cache, self.nH, self.greedy,
                               hidden=self.hidden, rms_eps=self.rms_eps, rope_base=self.rope_base, ws=self.ws_dec,
                               stream=stream)
+        if self.planted is not None:
+            medusa_plant_greedy(self.tree, self.topk_idx, self.cache_len, self.greedy, self.V, self.planted,
+                                self.plant_seed, stream=stream)
         medusa_accept(self.tree, self.node_tok, self.greedy, self.accept_len, self.accept_nodes, self.out_tokens,
                       self.cache_len, self.new_cache_len, k_cache=self.k_cache, v_cache=self.v_cache, stream=stream)
         medusa_advance(self.tree, self.accept_len, self.accept_nodes, self.out_tokens, self.hidden, self.root_tok,

@@ -277,3 +277,59 @@ def oracle_attention_seqs(cfg, att, seqs):
                                   np.asarray(att["cache_len"])[sl], parent, scale)[0]
         res[b] = oracle.round_bf16(o) if dt == "bf16" else o
     return res
+
+
+# ---------------------------------------------------------------------------
+# host reference of medusa_plant_greedy (a measurement aid: the planted
+# continuation drawn from the rank prior with a counter hash)
+# ---------------------------------------------------------------------------
+
+_M64 = (1 << 64) - 1
+
+
+def mix64(z: int) -> int:
+    """The 64-bit finaliser of SplitMix64 (Steele, Lea and Flood, OOPSLA'14)."""
+    z = (z + 0x9E3779B97F4A7C15) & _M64
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _M64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _M64
+    return z ^ (z >> 31)
+
+
+def planted_next_tokens(topk_idx_b, K, topk, P, max_depth, alpha, seed, b, V):
+    """Token after a node of depth d = 0..max_depth for one sequence."""
+    out = []
+    for d in range(max_depth + 1):
+        z = mix64(mix64(mix64((seed ^ b) & _M64) ^ (P & 0xFFFFFFFF)) ^ d)
+        u = np.float32(z >> 40) * np.float32(1.0 / 16777216.0)
+        cand = [int(x) for x in topk_idx_b[min(d, K - 1)]]
+        r = topk
+        if d < K:
+            cum, pr = np.float32(0), np.float32(alpha)
+            for j in range(topk):
+                cum = np.float32(cum + pr)
+                if u < cum:
+                    r = j
+                    break
+                pr = np.float32(pr * np.float32(1.0 - np.float32(alpha)))
+        if r < topk:
+            tok = cand[r]
+        else:
+            tok = (mix64(z) >> 33) % V
+            if d < K:
+                for _ in range(topk + 1):
+                    if tok not in cand:
+                        break
+                    tok = tok + 1 if tok + 1 < V else 0
+        out.append(int(tok))
+    return out
+
+
+def planted_greedy_ref(depth, topk_idx, cache_len, alpha, seed, V):
+    """greedy [B][N] as medusa_plant_greedy writes it."""
+    depth = np.asarray(depth)
+    B, K, topk = topk_idx.shape
+    g = np.empty((B, len(depth)), dtype=np.int32)
+    for b in range(B):
+        nxt = planted_next_tokens(topk_idx[b], K, topk, int(cache_len[b]), int(depth.max()), alpha, seed, b, V)
+        g[b] = [nxt[d] for d in depth]
+    return g

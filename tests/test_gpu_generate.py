@@ -24,7 +24,7 @@ import torch
 
 import medusa_inputs as mi
 import oracle
-from medusa_testlib import dev, host_f64
+from medusa_testlib import dev, host_f64, planted_greedy_ref
 
 pytestmark = pytest.mark.gpu
 
@@ -157,9 +157,10 @@ def _loop_setup(M, P_start, seed):
     return cfg, g, o, parent, rank
 
 
-def _make_loop(M, cfg, g, cap=64):
+def _make_loop(M, cfg, g, cap=64, planted=None):
     return M.MedusaLoop(g["heads"], g["layers"], g["embedding"], g["lm_head"], g["tree"], cfg.topk, g["k_cache"],
-                        g["v_cache"], cfg.nH, g["cache_len"], g["h"], g["root_tok"], cap=cap)
+                        g["v_cache"], cfg.nH, g["cache_len"], g["h"], g["root_tok"], cap=cap, planted=planted,
+                        plant_seed=99)
 
 
 def _check_topk(gpu_idx, logits, k):
@@ -176,11 +177,12 @@ def _check_topk(gpu_idx, logits, k):
             np.testing.assert_allclose(logits[b, j, got], ref_val[b, j], rtol=0, atol=TOPK_TIE)
 
 
-def test_loop_rounds_replay_against_oracle():
+@pytest.mark.parametrize("planted", [None, 0.8], ids=["model_choices", "planted_alpha0.8"])
+def test_loop_rounds_replay_against_oracle(planted):
     import speculative_decoding_medusa_amd as M
     P_start = (40, 77)
     cfg, g, o, parent, rank = _loop_setup(M, P_start, 611)
-    loop = _make_loop(M, cfg, g)
+    loop = _make_loop(M, cfg, g, planted=planted)
     B, N, Dmax = cfg.B, cfg.N, g["tree"].max_depth
     n_prev = np.zeros(B, dtype=np.int64)
     tokens_ref = [[] for _ in range(B)]
@@ -207,12 +209,16 @@ def test_loop_rounds_replay_against_oracle():
         hid = host_f64(loop.hidden)
         _close(hid, ref["hidden"])
         g_gpu = loop.greedy.cpu().numpy()
-        lg = oracle.round_f32(ref["logits"])
-        for b in range(B):
-            for i in range(N):
-                best = lg[b, i].max()
-                if g_gpu[b, i] != ref["greedy"][b, i]:
-                    assert lg[b, i, g_gpu[b, i]] >= best - GREEDY_TIE, (t, b, i)
+        if planted is None:
+            lg = oracle.round_f32(ref["logits"])
+            for b in range(B):
+                for i in range(N):
+                    best = lg[b, i].max()
+                    if g_gpu[b, i] != ref["greedy"][b, i]:
+                        assert lg[b, i, g_gpu[b, i]] >= best - GREEDY_TIE, (t, b, i)
+        else:
+            # the planted continuation, exactly as the host reference draws it
+            assert np.array_equal(g_gpu, planted_greedy_ref(cfg.tree.depth, ti, s["cache_len"], planted, 99, cfg.V))
         # acceptance on the GPU's own choices, then the hand-off
         al, an, ot = loop.accept_len.cpu().numpy(), loop.accept_nodes.cpu().numpy(), loop.out_tokens.cpu().numpy()
         kh, vh = host_f64(loop.k_cache), host_f64(loop.v_cache)
@@ -241,6 +247,8 @@ def test_loop_rounds_replay_against_oracle():
         assert got_tokens[b, :len(tokens_ref[b])].tolist() == tokens_ref[b]
     _say("ok, accepted candidates over the rounds:", accepted)
     assert accepted >= 1   # the accepted-path hand-off and compaction were exercised
+    if planted is not None:
+        assert accepted >= 10   # deep branches (about 2.9 per sequence and round under the prior)
 
 
 def test_loop_graph_replays_match_eager():
@@ -288,3 +296,23 @@ def test_loop_graph_replays_match_eager():
         for k, v in snaps[rep].items():
             assert torch.equal(getattr(loop, k), v), (rep, k)
     _say("ok")
+
+
+@pytest.mark.parametrize("alpha,tree_name", [(0.8, "sparse64"), (0.3, "sparse64"), (0.8, "dense256"),
+                                              (1.0, "chain7")])
+def test_plant_greedy_matches_host_reference(alpha, tree_name):
+    import speculative_decoding_medusa_amd as M
+    _say("plant_greedy", alpha, tree_name)
+    tree = {"sparse64": mi.sparse_tree(64), "dense256": mi.dense_tree(256), "chain7": mi.chain_tree(7)}[tree_name]
+    parent, rank = tree.arrays()
+    K = max(tree.depth)
+    topk = int(max(rank)) + 1
+    B, V = 37, 32000
+    r = np.random.default_rng(21)
+    tk = np.stack([np.stack([r.choice(V, topk, replace=False) for _ in range(K)]) for _ in range(B)]).astype(np.int32)
+    P = r.integers(0, 1 << 20, B).astype(np.int32)
+    t = M.Tree(parent, rank, K, topk)
+    g = torch.full((B, tree.n), -7, dtype=torch.int32, device="cuda")
+    M.medusa_plant_greedy(t, dev(tk), dev(P), g, V, alpha, seed=0xC0FFEE)
+    torch.cuda.synchronize()
+    assert np.array_equal(g.cpu().numpy(), planted_greedy_ref(tree.depth, tk, P, alpha, 0xC0FFEE, V))
