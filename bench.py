@@ -88,6 +88,8 @@ def parse():
     ap.add_argument("--typical", action="store_true",
                     help="sampling mode: the base greedy stage also writes the node rows' scores and "
                          "medusa_typical_accept (temperature 0.7, eps 0.09, delta 0.3) replaces medusa_accept")
+    ap.add_argument("--prefill-tokens", type=int, default=1024, metavar="T",
+                    help="with --loop: also time the prefill of a T-token prompt (0: skip)")
     ap.add_argument("--planted", type=float, default=None, metavar="ALPHA",
                     help="with --loop: plant the base model's choices from the rank prior ALPHA (1-ALPHA)^r")
     ap.add_argument("--loop", type=int, default=0, metavar="ROUNDS",
@@ -661,6 +663,36 @@ def bench_loop(args, cfg):
     restore()
     torch.cuda.synchronize()
 
+    # --- prefill: a TP-token prompt through the 32 layers in chain passes of
+    # 256 // B tokens, ending where the rounds start (slots below P0 are
+    # overwritten: this runs last)
+    TP = args.prefill_tokens
+    pf = {}
+    if TP > 0 and int(P0.min()) >= TP:
+        prompt = torch.from_numpy(mi.uniform_int((B, TP), cfg.seed, mi.S_TEST + 77, 0, cfg.V - 1).astype(np.int32)).cuda()
+        start = torch.from_numpy((P0 - TP).astype(np.int32)).cuda()
+        C = max(1, min(256 // B, TP))
+        chain = M.chain_tree(C)
+        ws_pf = M._ws(M._lib.medusa_prefill_workspace_size(chain.handle, B, H, cfg.nH, cfg.nKV, cfg.D, cfg.ffn, cfg.V,
+                                                           TP, int(P0.max()) - TP), "cuda", None)
+        nt = torch.empty(B, dtype=torch.int32, device="cuda")
+        hpf = torch.empty(B, H, dtype=torch.bfloat16, device="cuda")
+        times = []
+        for rep_ in range(4):
+            loop.cache_len.copy_(start)
+            torch.cuda.synchronize()
+            e0.record()
+            M.medusa_prefill(layers, emb, lm_head, chain, prompt, loop.cache_len, int(P0.max()) - TP, k_cache, v_cache,
+                             cfg.nH, nt, hpf, ws=ws_pf)
+            e1.record()
+            torch.cuda.synchronize()
+            if rep_ > 0:
+                times.append(e0.elapsed_time(e1))
+        ok = bool(np.array_equal(loop.cache_len.cpu().numpy(), P0))
+        ms = sum(times) / len(times)
+        pf = {"prompt_tokens": TP, "tokens_per_pass": C, "passes": -(-TP // C), "ms": round(ms, 3),
+              "tokens_per_s": round(B * TP / (ms * 1e-3), 1), "cache_len_advanced": ok}
+
     expected = tree_prior_tokens(parent, rank)
     rounds_s = R / (graph_ms * 1e-3)
     tpr = float(n_graph.sum()) / (B * R)
@@ -689,6 +721,7 @@ def bench_loop(args, cfg):
         "tokens_per_round_measured": round(tpr, 3),
         "tokens_per_s_measured": round(float(n_graph.sum()) / (graph_ms * 1e-3), 1),
         "tokens_per_round_under_tree_prior": round(expected, 3),
+        "prefill": pf,
         "cost_reading": {
             "stage_us": stage_us,
             "plain_decode_step_us": round(plain_us, 2),

@@ -160,6 +160,11 @@ medusa_status medusa_heads_forward_static(const void* h, const void* w1, const v
  *   (0 <= rank[i] < topk) of head depth(i) (1 <= depth(i) <= K).  Siblings
  *   must have distinct ranks.  1 <= N <= 256.  Uploads the spec and the
  *   ancestor bitmask to the current device (allocates; not for hot loops).
+ *   Candidate trees are at most 16 deep (medusa_build_tree, medusa_accept,
+ *   medusa_typical_accept, medusa_advance and medusa_plant_greedy refuse
+ *   deeper ones with MEDUSA_EUNSUPPORTED; medusa_build_tree also needs depth x
+ *   (largest rank + 1) <= 256); a deeper chain (parent[i] = i - 1, rank 0,
+ *   K = N - 1) serves the verify pass and medusa_prefill.
  * medusa_build_tree: node_tok[b][i] = root_tok[b] for i = 0, else
  *   topk_idx[b][depth(i)-1][rank[i]];  node_pos[b][i] = cache_len[b] + depth(i);
  *   anc_mask (optional) [N][W] uint64, W = ceil(N/64): bit j of word j/64 of
@@ -439,6 +444,38 @@ medusa_status medusa_decoder_verify(const medusa_layer_weights* layers, int n_la
                                     void* k_cache, void* v_cache, int64_t layer_stride_elems, int B, int H, int nH,
                                     int nKV, int D, int F, int V, int Lmax, float rms_eps, float rope_base,
                                     int32_t* greedy, float* hidden, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Prefill of a prompt before the first round (the state a round starts from:
+ * the prompt's keys/values in every layer's cache, the base model's greedy
+ * choice after the prompt -- the first root token -- and the final
+ * normalised row that chose it -- the heads' first input).  The prompt goes
+ * through the same decoder pass as medusa_decoder_verify, C tokens at a time
+ * with `chain` a chain tree of C nodes (parent[i] = i - 1, rank 0, created
+ * with K = C - 1): every token sees the cache prefix and the chunk's earlier
+ * tokens, i.e. causal attention, and writes its keys/values at slot
+ * cache_len[b] + its index.  The last pass is padded with copies of the last
+ * token, whose keys/values land in slots past the new length that no prompt
+ * token sees (they are overwritten later).
+ *   tokens [B][T] int32 (ids outside [0, V) read row 0 of the embedding);
+ *   cache_len [B] (in: the prefix before the prompt; out: + T);
+ *   max_cache_len (host): an upper bound of cache_len[] on entry;
+ *   next_tok [B] (out): greedy choice after the last prompt token;
+ *   hidden [B][H] (out, hidden_dt: MEDUSA_F32 or MEDUSA_BF16, exact either way:
+ *     the values are bf16): that token's final normalised row, the heads'
+ *     first input;
+ *   the other arguments as medusa_decoder_verify.
+ * Limits: max_cache_len + ceil(T / C) * C <= Lmax; B * C <= 256; the
+ * decoder's limits.  Workspace: medusa_prefill_workspace_size bytes.
+ * ------------------------------------------------------------------------- */
+size_t medusa_prefill_workspace_size(const medusa_tree* chain, int B, int H, int nH, int nKV, int D, int F, int V,
+                                     int T, int max_cache_len);
+medusa_status medusa_prefill(const medusa_layer_weights* layers, int n_layers, const void* embedding,
+                             const void* lm_head, const medusa_tree* chain, const int32_t* tokens, int T,
+                             int32_t* cache_len, int max_cache_len, void* k_cache, void* v_cache,
+                             int64_t layer_stride_elems, int B, int H, int nH, int nKV, int D, int F, int V, int Lmax,
+                             float rms_eps, float rope_base, int32_t* next_tok, void* hidden,
+                             medusa_dtype hidden_dt, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * The decoder layer's building blocks as calls of their own: the products,

@@ -14,7 +14,9 @@ Readings taken (the pages print no loop):
 * the next tree's root is the extra token; after a round the cache holds the
   round's root and its L accepted tokens, so the prefix grows by L + 1;
 * a prompt and its prefill lie outside the loop: a round starts from a cache,
-  a root token and a hidden state.
+  a root token and a hidden state; ``prefill`` produces that state from a
+  prompt (every prompt token's keys/values in the cache, the greedy choice
+  after the prompt as the first root, the row that chose it as the first h).
 
 Pins (tests/test_oracle_generate.py): greedy speculative decoding is lossless
 -- the rounds must emit exactly the tokens of plain autoregressive greedy
@@ -29,7 +31,7 @@ import numpy as np
 from .decoder import decoder_verify
 from .medusa import accept, build_tree, compact_kv, medusa_heads, round_bf16, topk, write_tree_kv
 
-__all__ = ["advance", "medusa_round", "greedy_decode"]
+__all__ = ["advance", "medusa_round", "greedy_decode", "prefill"]
 
 
 def advance(L, path, out_tokens, hidden_b, bf16):
@@ -109,3 +111,30 @@ def greedy_decode(root_tok, cache_len, k_caches, v_caches, dec, n_tokens, bf16=T
         hid.append(r["hidden"][:, 0])
     return dict(tokens=np.stack(toks, axis=1), hidden=np.stack(hid, axis=1), k_caches=kcs, v_caches=vcs,
                 cache_len=P)
+
+
+def prefill(tokens, cache_len, k_caches, v_caches, dec, bf16=True, eps=1e-6, rope_base=10000.0):
+    """The prompt before the first round, the plain causal way: one base-model
+    pass per prompt token (a one-node tree: it sees the cache and itself),
+    its keys/values appended to the cache.
+
+    tokens [B][T] (every sequence's prompt), cache_len [B] (the prefix before
+    it).  -> dict(next_tok [B] (the greedy choice after the last prompt
+    token: the first round's root), hidden [B][H] (the final normalised row
+    that chose it: the heads' first input), hidden_all [B][T][H], k_caches,
+    v_caches, cache_len (+ T))"""
+    parent = np.array([-1])
+    tokens = np.asarray(tokens, dtype=np.int64)
+    P = np.asarray(cache_len, dtype=np.int64).copy()
+    kcs = [k.copy() for k in k_caches]
+    vcs = [v.copy() for v in v_caches]
+    hid = []
+    for t in range(tokens.shape[1]):
+        r = decoder_verify(tokens[:, t:t + 1], P, parent, dec["embedding"], dec["layers"], dec["lm_head"], kcs, vcs,
+                           dec["nH"], dec["nKV"], eps, rope_base, bf16)
+        for l in range(len(kcs)):
+            kcs[l], vcs[l] = write_tree_kv(kcs[l], vcs[l], r["k_tree"][l], r["v_tree"][l], P)
+        P = P + 1
+        hid.append(r["hidden"][:, 0])
+    return dict(next_tok=r["greedy"][:, 0].astype(np.int64), hidden=hid[-1], hidden_all=np.stack(hid, axis=1),
+                k_caches=kcs, v_caches=vcs, cache_len=P)

@@ -64,6 +64,9 @@ _SIGS = {
     "medusa_decoder_workspace_size": ([_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32], _sz),
     "medusa_decoder_verify": ([_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
                                _i32, _i32, _i32, _i32, _f32, _f32, _vp, _vp, _vp, _sz, _vp], _i32),
+    "medusa_prefill_workspace_size": ([_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32], _sz),
+    "medusa_prefill": ([_vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32,
+                        _i32, _i32, _i32, _f32, _f32, _vp, _vp, _i32, _vp, _sz, _vp], _i32),
     "medusa_gemm_skinny_workspace_size": ([_i32, _i32, _i32], _sz),
     "medusa_gemm_skinny": ([_vp, _vp, _i32, _i32, _i32, _vp, _vp, _sz, _vp], _i32),
     "medusa_rmsnorm": ([_vp, _i32, _i32, _f32, _vp, _vp], _i32),
@@ -495,6 +498,36 @@ def medusa_decoder_verify(layers, embedding, lm_head: Packed, tree: Tree, node_t
         k_cache.stride(0), B, H, nH, nKV, D, F, V, Lmax, float(rms_eps), float(rope_base), _p(greedy), _p(hidden),
         _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return greedy
+
+
+def chain_tree(C: int) -> Tree:
+    """A chain of C nodes (each node's parent is the previous one): the tree
+    medusa_prefill runs its passes on."""
+    import numpy as np
+    return Tree(np.arange(-1, C - 1, dtype=np.int32), np.zeros(C, dtype=np.int32), max(C - 1, 1), 1)
+
+
+def medusa_prefill(layers, embedding, lm_head: Packed, chain: Tree, tokens, cache_len, max_cache_len: int, k_cache,
+                   v_cache, nH: int, next_tok, hidden, rms_eps=1e-6, rope_base=10000.0, ws=None, stream=None):
+    """Prefill the prompt tokens [B][T] (int32) in passes of chain.N tokens:
+    their keys/values go to the caches at cache_len.., cache_len grows by T,
+    next_tok [B] gets the greedy choice after the prompt and hidden [B][H]
+    (float32 or bf16) its final normalised row."""
+    n_layers, B, nKV, Lmax, D = k_cache.shape
+    V, H = embedding.shape
+    T = tokens.shape[1]
+    F = layers[0]["w_gate_up"].rows // 2
+    arr = (LayerWeights * len(layers))()
+    for i, W in enumerate(layers):
+        arr[i] = LayerWeights(*[W[n].data_ptr() for n in LAYER_MATRICES])
+    need = _lib.medusa_prefill_workspace_size(chain.handle, B, H, nH, nKV, D, F, V, T, int(max_cache_len))
+    ws = _ws(need, embedding.device, ws)
+    _check("medusa_prefill", _lib.medusa_prefill(
+        ctypes.cast(arr, ctypes.c_void_p), len(layers), _p(embedding), ctypes.c_void_p(lm_head.data_ptr()),
+        chain.handle, _p(tokens), T, _p(cache_len), int(max_cache_len), _p(k_cache), _p(v_cache), k_cache.stride(0),
+        B, H, nH, nKV, D, F, V, Lmax, float(rms_eps), float(rope_base), _p(next_tok), _p(hidden), _dt(hidden), _p(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
+    return next_tok
 
 
 # ---------------------------------------------------------------------------

@@ -73,6 +73,12 @@ size_t packed_elems(int rows, int K);
 void launch_pack_rows(const bf16_t* src, int rows, int K, bf16_t* dst, int dst_row0, int dst_rows, int inter,
                       hipStream_t s);
 size_t decoder_workspace_bytes(int B, int N, int H, int nH, int nKV, int D, int F, int V, int max_cache_len);
+size_t prefill_workspace_bytes(int B, int C, int H, int nH, int nKV, int D, int F, int V, int T, int max_cache_len);
+void launch_prefill(const LayerPtrs* layers, int n_layers, const bf16_t* E, const bf16_t* lm_head, const TreeDev& chain,
+                    const int32_t* tokens, int T, int32_t* cache_len, int max_cache_len, bf16_t* k_cache,
+                    bf16_t* v_cache, int64_t layer_stride, int B, int H, int nH, int nKV, int D, int F, int V,
+                    int Lmax, float eps, float rope_base, int32_t* next_tok, void* h_out, bool h_bf16, void* ws,
+                    hipStream_t s);
 void launch_decoder_verify(const LayerPtrs* layers, int n_layers, const bf16_t* E, const bf16_t* lm_head,
                            const TreeDev& t, const int32_t* node_tok, const int32_t* node_pos,
                            const int32_t* cache_len, int max_cache_len, bf16_t* k_cache, bf16_t* v_cache,
@@ -445,7 +451,6 @@ medusa_status medusa_tree_create(const int32_t* parent, const int32_t* rank, int
             t.h_depth[i] = t.h_depth[p] + 1;
             t.h_rank[i] = rank[i];
             REQUIRE(t.h_depth[i] <= K, "node %d has depth %d > K=%d", i, t.h_depth[i], K);
-            SUPPORT(t.h_depth[i] <= MEDUSA_MAX_DEPTH, "node %d depth exceeds %d", i, MEDUSA_MAX_DEPTH);
             uint32_t& w = seen[(size_t)p * ((topk + 31) / 32) + rank[i] / 32];
             REQUIRE(!(w & (1u << (rank[i] % 32))), "node %d repeats rank %d under parent %d", i, rank[i], p);
             w |= 1u << (rank[i] % 32);
@@ -533,6 +538,9 @@ medusa_status medusa_build_tree(const medusa_tree* tree, const int32_t* topk_idx
         REQUIRE(B >= 1, "B must be >= 1");
         REQUIRE(K >= tree->t.max_depth, "K=%d is smaller than the tree depth %d", K, tree->t.max_depth);
         REQUIRE(topk > tree->t.max_rank, "topk=%d does not cover rank %d", topk, tree->t.max_rank);
+        SUPPORT(tree->t.max_depth * (tree->t.max_rank + 1) <= MEDUSA_MAX_DEPTH * MEDUSA_MAX_TOPK,
+                "tree depth %d x ranks %d: more than %d candidates", tree->t.max_depth, tree->t.max_rank + 1,
+                MEDUSA_MAX_DEPTH * MEDUSA_MAX_TOPK);
         launch_build_tree(tree->t, topk_idx, K, topk, root_tok, cache_len, B, node_tok, node_pos, anc_mask,
                           (hipStream_t)stream);
     });
@@ -641,6 +649,8 @@ medusa_status medusa_accept(const medusa_tree* tree, const int32_t* node_tok, co
                     new_cache_len,
                 "null pointer argument");
         REQUIRE(B >= 1, "B must be >= 1");
+        SUPPORT(tree->t.max_depth <= MEDUSA_MAX_DEPTH, "tree depth %d exceeds %d", tree->t.max_depth,
+                MEDUSA_MAX_DEPTH);
         REQUIRE((k_cache == nullptr) == (v_cache == nullptr), "k_cache and v_cache must both be given or both NULL");
         if (k_cache) {
             REQUIRE(dt == MEDUSA_F32 || dt == MEDUSA_BF16, "bad dtype");
@@ -675,6 +685,8 @@ medusa_status medusa_typical_accept(const medusa_tree* tree, const int32_t* node
                 "null pointer argument");
         REQUIRE(B >= 1 && V >= 1, "B and V must be positive (B=%d V=%d)", B, V);
         SUPPORT(V <= typical_max_vocab(), "V=%d exceeds %d", V, typical_max_vocab());
+        SUPPORT(tree->t.max_depth <= MEDUSA_MAX_DEPTH, "tree depth %d exceeds %d", tree->t.max_depth,
+                MEDUSA_MAX_DEPTH);
         REQUIRE(temperature > 0.f && epsilon > 0.f && delta > 0.f,
                 "temperature, epsilon and delta must be positive (%g %g %g)", temperature, epsilon, delta);
         REQUIRE(ws_bytes >= typical_accept_workspace_bytes(B, tree->t.N), "workspace too small");
@@ -720,6 +732,8 @@ medusa_status medusa_advance(const medusa_tree* tree, const int32_t* accept_len,
     return guarded("medusa_advance", [&] {
         REQUIRE(tree && accept_len && accept_nodes && out_tokens && hidden && root_tok && h, "null pointer argument");
         REQUIRE(B >= 1 && H >= 1, "B and H must be positive (B=%d H=%d)", B, H);
+        SUPPORT(tree->t.max_depth <= MEDUSA_MAX_DEPTH, "tree depth %d exceeds %d", tree->t.max_depth,
+                MEDUSA_MAX_DEPTH);
         REQUIRE(dt == MEDUSA_F32 || dt == MEDUSA_BF16, "bad dtype");
         REQUIRE((tokens == nullptr) == (n_tokens == nullptr), "tokens and n_tokens must both be given or both NULL");
         REQUIRE(tokens == nullptr || cap >= 1, "cap=%d must be >= 1 when tokens are appended", cap);
@@ -793,6 +807,67 @@ medusa_status medusa_decoder_verify(const medusa_layer_weights* layers, int n_la
                               node_pos, cache_len, max_cache_len, (bf16_t*)k_cache, (bf16_t*)v_cache,
                               layer_stride_elems, B, H, nH, nKV, D, F, V, Lmax, rms_eps, rope_base, greedy, hidden, ws,
                               (hipStream_t)stream);
+    });
+}
+
+// ---------------------------------------------------------------------------
+// prefill: a prompt through the decoder in chain-tree passes
+// ---------------------------------------------------------------------------
+static bool is_chain(const TreeDev& t) {
+    for (int i = 1; i < t.N; ++i)
+        if (t.h_parent[i] != i - 1) return false;
+    return true;
+}
+
+size_t medusa_prefill_workspace_size(const medusa_tree* chain, int B, int H, int nH, int nKV, int D, int F, int V,
+                                     int T, int max_cache_len) {
+    if (!chain || B < 1 || H < 1 || nH < 1 || nKV < 1 || D < 1 || F < 1 || V < 1 || T < 1 || max_cache_len < 0)
+        return 0;
+    return prefill_workspace_bytes(B, chain->t.N, H, nH, nKV, D, F, V, T, max_cache_len);
+}
+
+medusa_status medusa_prefill(const medusa_layer_weights* layers, int n_layers, const void* embedding,
+                             const void* lm_head, const medusa_tree* chain, const int32_t* tokens, int T,
+                             int32_t* cache_len, int max_cache_len, void* k_cache, void* v_cache,
+                             int64_t layer_stride_elems, int B, int H, int nH, int nKV, int D, int F, int V, int Lmax,
+                             float rms_eps, float rope_base, int32_t* next_tok, void* hidden,
+                             medusa_dtype hidden_dt, void* ws, size_t ws_bytes, void* stream) {
+    return guarded("medusa_prefill", [&] {
+        REQUIRE(hidden_dt == MEDUSA_F32 || hidden_dt == MEDUSA_BF16, "bad hidden dtype");
+        REQUIRE(layers && embedding && lm_head && chain && tokens && cache_len && k_cache && v_cache && next_tok &&
+                    hidden && ws,
+                "null pointer argument");
+        REQUIRE(is_chain(chain->t), "the tree handle must be a chain (parent[i] = i - 1)");
+        REQUIRE(T >= 1, "T=%d must be positive", T);
+        REQUIRE(n_layers >= 1 && B >= 1 && H >= 1 && nH >= 1 && nKV >= 1 && D >= 1 && F >= 1 && V >= 1,
+                "sizes must be positive");
+        REQUIRE(nH % nKV == 0, "need nH %% nKV == 0 (nH=%d nKV=%d)", nH, nKV);
+        SUPPORT(H == nH * D, "H=%d must equal nH*D=%d", H, nH * D);
+        SUPPORT(D == 64 || D == 128, "D=%d not in {64, 128}", D);
+        const int C = chain->t.N;
+        SUPPORT(B * C <= MEDUSA_MAX_TREE_NODES, "B*C=%d exceeds %d", B * C, MEDUSA_MAX_TREE_NODES);
+        SUPPORT(H % 64 == 0 && F % 64 == 0, "H=%d and F=%d must be multiples of 64", H, F);
+        SUPPORT(H <= 16384, "H=%d exceeds 16384", H);
+        REQUIRE(rms_eps >= 0.f && rope_base > 1.f, "need rms_eps >= 0 and rope_base > 1");
+        const int passes = (T + C - 1) / C;
+        REQUIRE(max_cache_len >= 0 && (int64_t)max_cache_len + (int64_t)passes * C <= Lmax,
+                "max_cache_len + %d passes x %d = %lld exceeds Lmax = %d", passes, C,
+                (long long)max_cache_len + (long long)passes * C, Lmax);
+        REQUIRE(layer_stride_elems >= (int64_t)B * nKV * Lmax * D || n_layers == 1,
+                "layer stride smaller than one layer's cache");
+        std::vector<LayerPtrs> L((size_t)n_layers);
+        for (int l = 0; l < n_layers; ++l) {
+            const medusa_layer_weights& w = layers[l];
+            REQUIRE(w.wqkv && w.wo && w.w_gate_up && w.w_down, "layer %d: null weight", l);
+            L[l] = LayerPtrs{(const bf16_t*)w.wqkv, (const bf16_t*)w.wo, (const bf16_t*)w.w_gate_up,
+                             (const bf16_t*)w.w_down};
+        }
+        const size_t need = medusa_prefill_workspace_size(chain, B, H, nH, nKV, D, F, V, T, max_cache_len);
+        REQUIRE(ws_bytes >= need, "workspace too small: %zu < %zu", ws_bytes, need);
+        launch_prefill(L.data(), n_layers, (const bf16_t*)embedding, (const bf16_t*)lm_head, chain->t, tokens, T,
+                       cache_len, max_cache_len, (bf16_t*)k_cache, (bf16_t*)v_cache, layer_stride_elems, B, H, nH,
+                       nKV, D, F, V, Lmax, rms_eps, rope_base, next_tok, hidden, hidden_dt == MEDUSA_BF16, ws,
+                       (hipStream_t)stream);
     });
 }
 

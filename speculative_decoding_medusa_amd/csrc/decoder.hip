@@ -392,6 +392,92 @@ void launch_decoder_verify(const LayerPtrs* layers, int n_layers, const bf16_t* 
 }
 
 // ---------------------------------------------------------------------------
+// Prefill: a prompt of T tokens through the same pass, C tokens at a time,
+// the tree a chain of C nodes (each token sees the prefix and the chunk's
+// earlier tokens: causal attention).  Pass j covers prompt tokens jC ..
+// jC + C - 1 at prefix length cache_len + jC; the last pass is padded with
+// copies of the last token, whose keys/values land past the new cache
+// length, where no prompt token can see them.  After the last pass the
+// greedy choice and final normalised row of the last prompt token are the
+// first round's root and heads input, and the cache length grows by T.
+// ---------------------------------------------------------------------------
+
+// node_tok / node_pos / prefix length of pass j (one block per sequence)
+__global__ __launch_bounds__(256) void prefill_chunk_kernel(const int32_t* __restrict__ tokens, int T, int C, int j,
+                                                            const int32_t* __restrict__ cache_len,
+                                                            int32_t* __restrict__ node_tok,
+                                                            int32_t* __restrict__ node_pos,
+                                                            int32_t* __restrict__ prefix) {
+    const int b = blockIdx.x;
+    const int P = cache_len[b] + j * C;
+    for (int i = threadIdx.x; i < C; i += blockDim.x) {
+        const int t = min(j * C + i, T - 1);
+        node_tok[(size_t)b * C + i] = tokens[(size_t)b * T + t];
+        node_pos[(size_t)b * C + i] = P + i;
+    }
+    if (threadIdx.x == 0) prefix[b] = P;
+}
+
+// after the last pass (row = the last prompt token's node): the next token,
+// the heads' input (in T's storage; the row's values are bf16, so exact), the
+// new cache length
+template <typename TO>
+__global__ __launch_bounds__(256) void prefill_finish_kernel(const int32_t* __restrict__ greedy,
+                                                             const float* __restrict__ hidden, int C, int H, int row,
+                                                             int T, int32_t* __restrict__ next_tok,
+                                                             TO* __restrict__ h_out,
+                                                             int32_t* __restrict__ cache_len) {
+    const int b = blockIdx.x;
+    const float* src = hidden + ((size_t)b * C + row) * H;
+    for (int c = threadIdx.x; c < H; c += blockDim.x) Elem<TO>::store(h_out, (size_t)b * H + c, src[c]);
+    if (threadIdx.x == 0) {
+        next_tok[b] = greedy[(size_t)b * C + row];
+        cache_len[b] += T;
+    }
+}
+
+size_t prefill_workspace_bytes(int B, int C, int H, int nH, int nKV, int D, int F, int V, int T, int max_cache_len) {
+    const int passes = (T + C - 1) / C;
+    const size_t BC = (size_t)B * C;
+    return 3 * a256(BC * 4) + a256((size_t)B * 4) + a256(BC * H * 4) +
+           decoder_workspace_bytes(B, C, H, nH, nKV, D, F, V, max_cache_len + (passes - 1) * C);
+}
+
+void launch_prefill(const LayerPtrs* layers, int n_layers, const bf16_t* E, const bf16_t* lm_head, const TreeDev& chain,
+                    const int32_t* tokens, int T, int32_t* cache_len, int max_cache_len, bf16_t* k_cache,
+                    bf16_t* v_cache, int64_t layer_stride, int B, int H, int nH, int nKV, int D, int F, int V,
+                    int Lmax, float eps, float rope_base, int32_t* next_tok, void* h_out, bool h_bf16, void* ws,
+                    hipStream_t s) {
+    const int C = chain.N;
+    const int passes = (T + C - 1) / C;
+    const size_t BC = (size_t)B * C;
+    char* p = (char*)ws;
+    int32_t* node_tok = (int32_t*)p; p += a256(BC * 4);
+    int32_t* node_pos = (int32_t*)p; p += a256(BC * 4);
+    int32_t* greedy = (int32_t*)p; p += a256(BC * 4);
+    int32_t* prefix = (int32_t*)p; p += a256((size_t)B * 4);
+    float* hidden = (float*)p; p += a256(BC * H * 4);
+    void* dws = p;  // sized for the largest prefix bound of any pass
+    const int max_len_last = max_cache_len + (passes - 1) * C;
+    for (int j = 0; j < passes; ++j) {
+        MEDUSA_LAUNCH("prefill_chunk", prefill_chunk_kernel, dim3(B), dim3(256), 0, s, tokens, T, C, j, cache_len,
+                      node_tok, node_pos, prefix);
+        // every pass carves the workspace for the last pass's bound, so the
+        // carving is the same in all passes
+        launch_decoder_verify(layers, n_layers, E, lm_head, chain, node_tok, node_pos, prefix, max_len_last, k_cache,
+                              v_cache, layer_stride, B, H, nH, nKV, D, F, V, Lmax, eps, rope_base, greedy,
+                              j == passes - 1 ? hidden : nullptr, dws, s);
+    }
+    const int row = T - 1 - (passes - 1) * C;
+    if (h_bf16)
+        MEDUSA_LAUNCH("prefill_finish", prefill_finish_kernel<bf16_t>, dim3(B), dim3(256), 0, s, greedy, hidden, C, H,
+                      row, T, next_tok, (bf16_t*)h_out, cache_len);
+    else
+        MEDUSA_LAUNCH("prefill_finish", prefill_finish_kernel<float>, dim3(B), dim3(256), 0, s, greedy, hidden, C, H,
+                      row, T, next_tok, (float*)h_out, cache_len);
+}
+
+// ---------------------------------------------------------------------------
 // The layer's building blocks as calls of their own (same kernels as above;
 // shapes checked by the caller)
 // ---------------------------------------------------------------------------

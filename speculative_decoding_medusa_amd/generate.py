@@ -17,9 +17,9 @@ from __future__ import annotations
 
 import torch
 
-from . import (Packed, Tree, _ws, decoder_workspace_size, heads_workspace_size, medusa_accept, medusa_advance,
-               medusa_build_tree, medusa_decoder_verify, medusa_heads_forward, medusa_plant_greedy, ROW_MAJOR, PACKED,
-               BF16, F32)
+from . import (Packed, Tree, _ws, chain_tree, decoder_workspace_size, heads_workspace_size, medusa_accept,
+               medusa_advance, medusa_build_tree, medusa_decoder_verify, medusa_heads_forward, medusa_plant_greedy,
+               medusa_prefill, ROW_MAJOR, PACKED, BF16, F32)
 
 
 class MedusaLoop:
@@ -85,6 +85,26 @@ class MedusaLoop:
         self.ws_heads = _ws(heads_workspace_size(B, H, V, K, topk, dt, layout), dev, None)
         F = layers[0]["w_gate_up"].rows // 2
         self.ws_dec = _ws(decoder_workspace_size(tree, B, H, nH, nKV, D, F, V, self.max_cache_len), dev, None)
+
+    def prefill(self, tokens, start_len: int, chunk: int = 0, stream=None):
+        """Run the prompts tokens [B][T] (int32, device) through the decoder
+        from the current caches (medusa_prefill): afterwards the caches hold
+        their keys/values, root_tok is the greedy choice after each prompt and
+        h the row that chose it -- the state the first round starts from.
+        start_len: the longest prefix before the prompts (host bound).  chunk:
+        tokens per pass (default: as many as 256 rows allow)."""
+        B, T = tokens.shape
+        C = chunk or max(1, min(256 // B, T))
+        key = ("chain", C)
+        if getattr(self, "_chain", None) is None or self._chain[0] != key:
+            self._chain = (key, chain_tree(C))
+        passes = -(-T // C)
+        if start_len + passes * C > self.k_cache.shape[3]:
+            raise ValueError(f"prompts of {T} tokens in passes of {C} do not fit the caches after {start_len}")
+        medusa_prefill(self.layers, self.embedding, self.lm_head, self._chain[1], tokens, self.cache_len, start_len,
+                       self.k_cache, self.v_cache, self.nH, self.root_tok, self.h, rms_eps=self.rms_eps,
+                       rope_base=self.rope_base, stream=stream)
+        self.restart(start_len + T)
 
     def restart(self, start_len: int):
         """Set the round budget from start_len, the longest prefix the

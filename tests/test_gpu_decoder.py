@@ -190,3 +190,78 @@ def test_decoder_argument_errors():
         M.medusa_decoder_verify([W], emb, M.pack(emb), tree, tok, tok, torch.zeros(1, dtype=torch.int32, device="cuda"), 5,
                                 kc, kc.clone(), 4, g)
     assert e.value.status == M.EUNSUPPORTED
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("C,T,T2", [(32, 70, 5), (64, 64, 17)], ids=["c32_t70_ragged", "c64_t64_exact"])
+def test_prefill_parity(C, T, T2):
+    """medusa_prefill (chain-tree passes of C tokens, the last one padded)
+    against the oracle's token-by-token causal prefill: the next token
+    (exact), the last row, every prompt token's keys/values in every layer,
+    the new cache length; then a second prompt continues from that state."""
+    import speculative_decoding_medusa_amd as M
+    from oracle.generate import prefill
+    cfg = _cfg("pf", 2, 256, 1000, mi.sparse_tree(24), 4, 2, 64, (37, 5), 520, 2, 384)
+    _say("prefill", "C", C, "T", T, "then", T2)
+    L, B = cfg.layers, cfg.B
+    Lmax = max(cfg.P) + 2 * ((T + C - 1) // C) * C + 2 * C
+    layers = [mi.gen_layer(cfg, l) for l in range(L)]
+    caches = []
+    for l in range(L):
+        kc = mi.normal((B, cfg.nKV, Lmax, cfg.D), cfg.seed, mi.S_LAYER + 16 * l + 7, 1.0, "bf16")
+        vc = mi.normal((B, cfg.nKV, Lmax, cfg.D), cfg.seed, mi.S_LAYER + 16 * l + 8, 1.0, "bf16")
+        caches.append((kc, vc))
+    emb = mi.gen_embedding(cfg)
+    lm_head = mi.normal((cfg.V, cfg.H), cfg.seed, mi.S_LM_HEAD, mi.WEIGHT_SIGMA, "bf16")
+    prompt = mi.uniform_int((B, T), cfg.seed, mi.S_TEST + 30, 0, cfg.V - 1).astype(np.int32)
+    prompt2 = mi.uniform_int((B, T2), cfg.seed, mi.S_TEST + 31, 0, cfg.V - 1).astype(np.int32)
+    P0 = np.asarray(cfg.P, dtype=np.int64)
+
+    dec = dict(embedding=oracle.widen(emb, "bf16"), layers=[{m: oracle.widen(W[m], "bf16") for m in W} for W in layers],
+               lm_head=None, nH=cfg.nH, nKV=cfg.nKV)
+    kc0 = [oracle.widen(c[0], "bf16") for c in caches]
+    vc0 = [oracle.widen(c[1], "bf16") for c in caches]
+    # lm_head margin for the two next-token choices (final rows do not depend on lm_head)
+    dec["lm_head"] = oracle.widen(lm_head, "bf16")
+    ref1 = prefill(prompt, P0, kc0, vc0, dec)
+    ref2 = prefill(prompt2, ref1["cache_len"], ref1["k_caches"], ref1["v_caches"], dec)
+    ov = _enforce_gap(cfg, lm_head, np.concatenate([ref1["hidden"], ref2["hidden"]]))
+    dec["lm_head"] = oracle.widen(lm_head, "bf16")
+    nt1 = np.argmax(oracle.round_f32(ref1["hidden"] @ dec["lm_head"].T), axis=1)
+    nt2 = np.argmax(oracle.round_f32(ref2["hidden"] @ dec["lm_head"].T), axis=1)
+    _say("oracle done,", len(ov), "lm_head overrides")
+
+    d_layers = [M.pack_layer({m: dev(W[m]) for m in W}) for W in layers]
+    k_cache = torch.stack([dev(c[0]) for c in caches])
+    v_cache = torch.stack([dev(c[1]) for c in caches])
+    chain = M.chain_tree(C)
+    cl = dev(P0.astype(np.int32))
+    nt = torch.empty(B, dtype=torch.int32, device="cuda")
+    hid = torch.empty(B, cfg.H, device="cuda")
+    E, LM = dev(emb), M.pack(dev(lm_head))
+    M.medusa_prefill(d_layers, E, LM, chain, dev(prompt), cl, int(P0.max()), k_cache, v_cache, cfg.nH, nt, hid)
+    torch.cuda.synchronize()
+    assert np.array_equal(cl.cpu().numpy(), P0 + T)
+    assert np.array_equal(nt.cpu().numpy(), nt1)
+    _close(host_f64(hid), ref1["hidden"], "last row")
+    kh, vh = host_f64(k_cache), host_f64(v_cache)
+    for l in range(L):
+        for b in range(B):
+            P = int(P0[b])
+            _close(kh[l, b, :, P:P + T], ref1["k_caches"][l][b, :, P:P + T], f"layer {l} keys")
+            _close(vh[l, b, :, P:P + T], ref1["v_caches"][l][b, :, P:P + T], f"layer {l} values")
+            assert np.array_equal(kh[l, b, :, :P], kc0[l][b, :, :P])
+    # a second prompt continues from the prefilled state
+    M.medusa_prefill(d_layers, E, LM, chain, dev(prompt2), cl, int(P0.max()) + T, k_cache, v_cache, cfg.nH, nt, hid)
+    torch.cuda.synchronize()
+    assert np.array_equal(cl.cpu().numpy(), P0 + T + T2)
+    assert np.array_equal(nt.cpu().numpy(), nt2)
+    _close(host_f64(hid), ref2["hidden"], "last row, second prompt")
+    assert chain.status() == 0
+    # bf16 output of the row (the heads' dtype): the same values
+    hid16 = torch.empty(B, cfg.H, dtype=torch.bfloat16, device="cuda")
+    M.medusa_prefill(d_layers, E, LM, chain, dev(prompt2), cl, int(P0.max()) + T + T2, k_cache, v_cache, cfg.nH, nt,
+                     hid16)
+    torch.cuda.synchronize()
+    assert np.array_equal(cl.cpu().numpy(), P0 + T + 2 * T2)
+    _say("ok")

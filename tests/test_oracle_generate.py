@@ -107,3 +107,51 @@ def test_advance_takes_the_deepest_accepted_row_and_the_bonus():
     # bf16: nearest-even rounding of the row (1 + 2^-8 is a tie between 1 and 1 + 2^-7: even mantissa wins)
     _, h, _ = advance(0, np.array([0]), np.array([0]), np.array([[1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8]]), bf16=True)
     assert np.array_equal(h, [1.0, 1 + 2.0 ** -6])
+
+
+# ----------------------------------------------------------------------------
+# prefill
+# ----------------------------------------------------------------------------
+
+def test_prefill_equals_one_chain_tree_pass():
+    # the causal token-by-token prefill equals one verify pass over the whole
+    # prompt as a chain tree (every token sees the prefix and its earlier tokens)
+    from oracle.decoder import decoder_verify
+    from oracle.generate import prefill
+    dec, _, state = _model(31)
+    T = 7
+    r = np.random.default_rng(5)
+    prompt = r.integers(0, V, (2, T))
+    pre = prefill(prompt, state["cache_len"], state["k_caches"], state["v_caches"], dec, bf16=False)
+    chain = np.arange(-1, T - 1)
+    one = decoder_verify(prompt, state["cache_len"], chain, dec["embedding"], dec["layers"], dec["lm_head"],
+                         state["k_caches"], state["v_caches"], NH, NKV, bf16=False)
+    np.testing.assert_allclose(pre["hidden_all"], one["hidden"], rtol=1e-11, atol=1e-11)
+    assert np.array_equal(pre["next_tok"], one["greedy"][:, -1])
+    for b in range(2):
+        P = int(state["cache_len"][b])
+        for l in range(LAYERS):
+            np.testing.assert_allclose(pre["k_caches"][l][b, :, P:P + T], one["k_tree"][l][b].transpose(1, 0, 2),
+                                       rtol=1e-11, atol=1e-11)
+            np.testing.assert_allclose(pre["v_caches"][l][b, :, P:P + T], one["v_tree"][l][b].transpose(1, 0, 2),
+                                       rtol=1e-11, atol=1e-11)
+            assert np.array_equal(pre["k_caches"][l][b, :, :P], state["k_caches"][l][b, :, :P])
+    assert np.array_equal(pre["cache_len"], state["cache_len"] + T)
+
+
+def test_prefill_hands_greedy_decoding_the_same_state():
+    # prefilling the whole prompt gives the token and caches that prefilling
+    # all but its last token and then taking one greedy step from that token
+    # gives
+    from oracle.generate import greedy_decode, prefill
+    dec, _, state = _model(32)
+    r = np.random.default_rng(6)
+    prompt = r.integers(0, V, (2, 6))
+    full = prefill(prompt, state["cache_len"], state["k_caches"], state["v_caches"], dec, bf16=False)
+    part = prefill(prompt[:, :-1], state["cache_len"], state["k_caches"], state["v_caches"], dec, bf16=False)
+    step = greedy_decode(prompt[:, -1], part["cache_len"], part["k_caches"], part["v_caches"], dec, 1, bf16=False)
+    assert np.array_equal(full["next_tok"], step["tokens"][:, 0])
+    np.testing.assert_allclose(full["hidden"], step["hidden"][:, 0], rtol=1e-12, atol=1e-12)
+    assert np.array_equal(full["cache_len"], step["cache_len"])
+    for l in range(LAYERS):
+        np.testing.assert_allclose(full["k_caches"][l], step["k_caches"][l], rtol=1e-12, atol=1e-12)
