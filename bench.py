@@ -90,6 +90,11 @@ def parse():
                          "medusa_typical_accept (temperature 0.7, eps 0.09, delta 0.3) replaces medusa_accept")
     ap.add_argument("--prefill-tokens", type=int, default=1024, metavar="T",
                     help="with --loop: also time the prefill of a T-token prompt (0: skip)")
+    ap.add_argument("--dynamic", type=int, default=0, metavar="T",
+                    help="with --config 5 --loop R: the tree topology study -- static sparse tree vs one re-chosen "
+                         "every T rounds from measured acceptance (needs --planted-depths)")
+    ap.add_argument("--planted-depths", type=str, default="0.8,0.7,0.6,0.5,0.4", metavar="A1,A2,..",
+                    help="per-depth alphas of the planted truth for --dynamic")
     ap.add_argument("--planted", type=float, default=None, metavar="ALPHA",
                     help="with --loop: plant the base model's choices from the rank prior ALPHA (1-ALPHA)^r")
     ap.add_argument("--loop", type=int, default=0, metavar="ROUNDS",
@@ -142,7 +147,7 @@ def main():
     cfg = mi.config(args.config)
     if args.loop:
         assert cfg.layers, "--loop runs the decoder workload (--config 5)"
-        return bench_loop(args, cfg)
+        return bench_topology(args, cfg) if args.dynamic else bench_loop(args, cfg)
     if cfg.layers:
         return bench_decoder(args, cfg)
     dt_str = cfg.dtype
@@ -500,6 +505,62 @@ def bench_decoder(args, cfg):
     print(json.dumps(result), flush=True)
 
 
+def _loop_state(args, cfg, R, planted=None):
+    """Weights, caches and a MedusaLoop for R rounds of the 32-layer workload,
+    starting (Dmax + 1) R tokens before its prefix length; restore() puts the
+    caches and the loop's state back to that start."""
+    import numpy as np
+    import torch
+
+    import medusa_inputs as mi
+    import speculative_decoding_medusa_amd as M
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16 else torch.from_numpy(a)
+        return t.cuda()
+
+    B, K, H, N, topk, L = cfg.B, cfg.K, cfg.H, cfg.N, cfg.topk, cfg.layers
+    parent, rank = cfg.tree.arrays()
+    tree = M.Tree(parent, rank, K, topk)
+    P0 = np.asarray(cfg.P, dtype=np.int32) - (tree.max_depth + 1) * R
+    assert P0.min() >= 0, "too many rounds for the workload's prefix"
+    heads = mi.gen_heads(cfg)
+    d = {k: dev(v) for k, v in heads.items()}
+    layers = []
+    k_cache = torch.empty(L, B, cfg.nKV, cfg.Lmax, cfg.D, dtype=torch.bfloat16, device="cuda")
+    v_cache = torch.empty_like(k_cache)
+    for l in range(L):
+        W = mi.gen_layer(cfg, l)
+        layers.append(M.pack_layer({m: dev(W[m]) for m in W}))
+        del W
+        kc, vc = mi.gen_layer_cache(cfg, l)
+        k_cache[l].copy_(dev(kc))
+        v_cache[l].copy_(dev(vc))
+        del kc, vc
+    emb = dev(mi.gen_embedding(cfg))
+    lm_head = M.pack(d.pop("lm_head"))
+    state = dict(cache_len=dev(P0), h=d["h"].clone(), root_tok=dev(mi.gen_root_tokens(cfg)))
+    loop = M.MedusaLoop({"w1": d["W1"], "b1": d["b1"], "w2": d["W2"]}, layers, emb, lm_head, tree, topk, k_cache,
+                        v_cache, cfg.nH, state["cache_len"].clone(), state["h"].clone(), state["root_tok"].clone(),
+                        max_cache_len=int(max(cfg.P)), cap=(tree.max_depth + 1) * R, planted=args.planted if planted is None else planted,
+                        plant_seed=2024)
+    # only the slots [P0, max P + N) change: keep them to restore the initial state
+    lo, hi = int(P0.min()), int(max(cfg.P)) + N
+    keep_k, keep_v = k_cache[..., lo:hi, :].clone(), v_cache[..., lo:hi, :].clone()
+
+    def restore():
+        k_cache[..., lo:hi, :].copy_(keep_k)
+        v_cache[..., lo:hi, :].copy_(keep_v)
+        loop.cache_len.copy_(state["cache_len"])
+        loop.h.copy_(state["h"])
+        loop.root_tok.copy_(state["root_tok"])
+        loop.n_tokens.zero_()
+        loop.restart(int(P0.max()))
+
+    return tree, loop, layers, emb, lm_head, k_cache, v_cache, P0, restore
+
+
 def bench_loop(args, cfg):
     """ROUNDS rounds of the generate loop on the 32-layer workload: heads ->
     tree -> decoder verify -> [planted choices] -> accept with compaction ->
@@ -537,42 +598,7 @@ def bench_loop(args, cfg):
     R = args.loop
     B, K, H, N, topk, L = cfg.B, cfg.K, cfg.H, cfg.N, cfg.topk, cfg.layers
     parent, rank = cfg.tree.arrays()
-    tree = M.Tree(parent, rank, K, topk)
-    P0 = np.asarray(cfg.P, dtype=np.int32) - (tree.max_depth + 1) * R
-    assert P0.min() >= 0, "too many rounds for the workload's prefix"
-    heads = mi.gen_heads(cfg)
-    d = {k: dev(v) for k, v in heads.items()}
-    layers = []
-    k_cache = torch.empty(L, B, cfg.nKV, cfg.Lmax, cfg.D, dtype=torch.bfloat16, device="cuda")
-    v_cache = torch.empty_like(k_cache)
-    for l in range(L):
-        W = mi.gen_layer(cfg, l)
-        layers.append(M.pack_layer({m: dev(W[m]) for m in W}))
-        del W
-        kc, vc = mi.gen_layer_cache(cfg, l)
-        k_cache[l].copy_(dev(kc))
-        v_cache[l].copy_(dev(vc))
-        del kc, vc
-    emb = dev(mi.gen_embedding(cfg))
-    lm_head = M.pack(d.pop("lm_head"))
-    state = dict(cache_len=dev(P0), h=d["h"].clone(), root_tok=dev(mi.gen_root_tokens(cfg)))
-    loop = M.MedusaLoop({"w1": d["W1"], "b1": d["b1"], "w2": d["W2"]}, layers, emb, lm_head, tree, topk, k_cache,
-                        v_cache, cfg.nH, state["cache_len"].clone(), state["h"].clone(), state["root_tok"].clone(),
-                        max_cache_len=int(max(cfg.P)), cap=(tree.max_depth + 1) * R, planted=args.planted,
-                        plant_seed=2024)
-    # only the slots [P0, max P + N) change: keep them to restore the initial state
-    lo, hi = int(P0.min()), int(max(cfg.P)) + N
-    keep_k, keep_v = k_cache[..., lo:hi, :].clone(), v_cache[..., lo:hi, :].clone()
-
-    def restore():
-        k_cache[..., lo:hi, :].copy_(keep_k)
-        v_cache[..., lo:hi, :].copy_(keep_v)
-        loop.cache_len.copy_(state["cache_len"])
-        loop.h.copy_(state["h"])
-        loop.root_tok.copy_(state["root_tok"])
-        loop.n_tokens.zero_()
-        loop.restart(int(P0.max()))
-
+    tree, loop, layers, emb, lm_head, k_cache, v_cache, P0, restore = _loop_state(args, cfg, R)
     loop.run(min(R, 2))       # warm the launch paths
     restore()
     torch.cuda.synchronize()
@@ -731,6 +757,125 @@ def bench_loop(args, cfg):
             "speedup_modelled_prior": round(expected / (c_draft + c_verify + c_rest), 3),
             "speedup_measured": round(tpr * plain_us / round_us, 3),
         },
+    }
+    print(json.dumps(result), flush=True)
+
+
+def bench_topology(args, cfg):
+    """The tree topology study, dynamic variant: the same 32-layer loop on the
+    same planted truth -- base-model choices drawn with per-depth alphas that
+    fall with depth (the e-book's caveat: once a guess slips, later positions
+    slip more) -- run twice from the same state, R rounds each: with the
+    static sparse 64-node tree (chosen for 0.8 at every depth), and with a
+    64-node tree re-chosen every T rounds from the acceptance counts the
+    rounds gathered so far (medusa_accept_stats -> per-depth rank estimates ->
+    medusa_tree_select).  Reports tokens per round and tokens/s of both (wall
+    time including the re-selections), and the expected tokens per round of
+    the static tree, the final dynamic tree and the best 64-node tree under
+    the true prior."""
+    import numpy as np
+    import torch
+
+    import medusa_inputs as mi
+    import speculative_decoding_medusa_amd as M
+
+    R, T = args.loop, args.dynamic
+    alphas = [float(a) for a in args.planted_depths.split(",")]
+    B, K, topk, N = cfg.B, cfg.K, cfg.topk, cfg.N
+    tree, loop, layers, emb, lm_head, k_cache, v_cache, P0, restore = _loop_state(args, cfg, R, planted=alphas)
+    static = tree
+
+    def prior_matrix(al):
+        return np.array([[mi.rank_prior(al[min(d, len(al) - 1)], r) for r in range(topk)] for d in range(K)])
+
+    def expected(parent, rank, acc):
+        e = 1.0
+        depth = np.zeros(len(parent), int)
+        prod = np.ones(len(parent))
+        for i in range(1, len(parent)):
+            depth[i] = depth[parent[i]] + 1
+            prod[i] = prod[parent[i]] * acc[depth[i] - 1][rank[i]]
+            e += prod[i]
+        return e
+
+    truth = prior_matrix(alphas)
+    assumed = prior_matrix([0.8])
+    best = M.tree_select(truth, N)
+
+    def run(dynamic):
+        restore()
+        loop.set_tree(static)
+        loop.stats = torch.zeros(K, topk + 1, dtype=torch.int32, device="cuda") if dynamic else None
+        loop.run(2)                       # warm the launch paths
+        restore()
+        if dynamic:
+            loop.stats.zero_()
+        torch.cuda.synchronize()
+        trees, history = [static], []
+        t0 = time.perf_counter()
+        done = 0
+        while done < R:
+            n = min(T if dynamic else R, R - done)
+            loop.run(n)
+            done += n
+            if dynamic and done < R:
+                c = loop.stats.cpu().numpy().astype(np.float64)        # waits for the rounds
+                a0 = 4.0                                               # pseudo-observations of the assumed prior
+                tot = c.sum(axis=1, keepdims=True)
+                acc = (c[:, :topk] + a0 * assumed) / (tot + a0)
+                parent, rank = M.tree_select(acc, N)
+                nt = M.Tree(parent, rank, K, topk)
+                loop.set_tree(nt)
+                trees.append(nt)
+                history.append(round(expected(parent, rank, truth), 3))
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ntok = int(loop.n_tokens.sum().item())
+        last = trees[-1]
+        res = {"tokens_per_round": round(ntok / (B * R), 3), "tokens_per_s": round(ntok / wall, 1),
+               "ms_per_round_wall": round(wall * 1e3 / R, 4), "tree_status_word": last.status(),
+               "expected_tokens_final_tree": None}
+        if dynamic:
+            res["reselections"] = len(history)
+            res["expected_tokens_per_reselection"] = history
+        return res, trees
+
+    # alternate the two (static, dynamic, static, dynamic) so both see the same
+    # warm state; the figures are the means of the two runs of each
+    runs = {False: [], True: []}
+    trees = None
+    for dynamic in (False, True, False, True):
+        res, tr = run(dynamic)
+        runs[dynamic].append(res)
+        if dynamic:
+            trees = tr
+
+    def mean_of(rs):
+        out = dict(rs[-1])
+        for k in ("tokens_per_round", "tokens_per_s", "ms_per_round_wall"):
+            out[k] = round(sum(r[k] for r in rs) / len(rs), 4)
+        out["runs_tokens_per_s"] = [r["tokens_per_s"] for r in rs]
+        return out
+
+    st, dy = mean_of(runs[False]), mean_of(runs[True])
+    restore()
+    loop.set_tree(static)
+    sp, sr = cfg.tree.arrays()
+    st["expected_tokens_final_tree"] = round(expected(sp, sr, truth), 3)
+    if len(trees) > 1:
+        dy["expected_tokens_final_tree"] = dy["expected_tokens_per_reselection"][-1]
+    result = {
+        "metric": "tree topology study: tokens/s of the 32-layer loop, static sparse 64-node tree vs a 64-node tree "
+                  "re-chosen from measured acceptance",
+        "value": dy["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "rounds": R, "reselect_every": T,
+        "higher_is_better": True, "dtype": "bf16",
+        "data": f"synthetic; base-model choices planted with per-depth alphas {alphas}",
+        "config": {"workload": cfg.name + "_topology", "batch": B, "tree_nodes": N, "decoder_layers": cfg.layers},
+        "static_sparse64": st, "dynamic": dy,
+        "expected_tokens_static_tree_under_truth": st["expected_tokens_final_tree"],
+        "expected_tokens_best_tree_under_truth": round(expected(best[0], best[1], truth), 3),
+        "expected_tokens_static_tree_as_assumed": round(expected(sp, sr, assumed), 3),
+        "dynamic_over_static_tokens_per_s": round(dy["tokens_per_s"] / st["tokens_per_s"], 4),
     }
     print(json.dumps(result), flush=True)
 

@@ -381,7 +381,8 @@ medusa_status medusa_advance(const medusa_tree* tree, const int32_t* accept_len,
  * choice after every node, as medusa_base_greedy or medusa_decoder_verify
  * wrote it) with a planted continuation: for sequence b and depth d, the
  * token after every depth-d node is head (d + 1)'s rank-r guess
- * topk_idx[b][d][r] with probability alpha (1 - alpha)^r (r < topk), else a
+ * topk_idx[b][d][r] with probability a (1 - a)^r (r < topk), a =
+ * alpha[min(d, n_alpha - 1)] (host array: one alpha, or one per depth), else a
  * token outside that head's top-k (at depth K: any token), drawn with the
  * counter hash of (seed, b, cache_len[b], d) -- a new prefix length draws a new
  * continuation, so a captured loop draws anew every round.  A round then
@@ -391,7 +392,34 @@ medusa_status medusa_advance(const medusa_tree* tree, const int32_t* accept_len,
  * 0.8).  One kernel; no workspace.  Limits: tree depth <= 16, K >= depth.
  * ------------------------------------------------------------------------- */
 medusa_status medusa_plant_greedy(const medusa_tree* tree, const int32_t* topk_idx, const int32_t* cache_len, int B,
-                                  int K, int topk, int V, float alpha, uint64_t seed, int32_t* greedy, void* stream);
+                                  int K, int topk, int V, const float* alpha, int n_alpha, uint64_t seed,
+                                  int32_t* greedy, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Choosing the candidate tree from measured acceptance (tree section: the
+ * sparse tree is built from the combinations of head guesses most likely to
+ * be accepted).
+ *
+ * medusa_accept_stats adds what one round of medusa_accept revealed to
+ * counts [K][topk + 1] (int32, device, accumulated with atomic adds): for
+ * sequence b with L = accept_len[b], the base model's choice at depth
+ * d <= L was the rank-rank[path[d]] candidate (counts[d - 1][rank]++), and
+ * at depth L + 1 <= K it was the extra token out_tokens[b][L], found at rank
+ * r of head L + 1's top-k topk_idx[b][L] (counts[L][r]++) or among none of
+ * them (counts[L][topk]++); deeper depths are not observed.  One kernel.
+ *
+ * medusa_tree_select (host only, no device work): the N-node tree with the
+ * largest expected tokens per round, 1 + sum over nodes of the product along
+ * the node's path of acc[d][r] -- the probability that head d + 1's rank-r
+ * guess is the base model's choice given the path so far (host [K][topk]
+ * doubles) -- chosen best-first: larger product, then shallower, then the
+ * lexicographically smaller rank tuple.  Writes parent[N], rank[N] (host) in
+ * breadth-first order, ready for medusa_tree_create.
+ * ------------------------------------------------------------------------- */
+medusa_status medusa_accept_stats(const medusa_tree* tree, const int32_t* accept_len, const int32_t* accept_nodes,
+                                  const int32_t* out_tokens, const int32_t* topk_idx, int B, int K, int topk,
+                                  int32_t* counts, void* stream);
+medusa_status medusa_tree_select(const double* acc, int K, int topk, int N, int32_t* parent, int32_t* rank);
 
 /* ---------------------------------------------------------------------------
  * Step a8 -- the tree-verify forward pass through a Llama-shaped decoder

@@ -60,7 +60,9 @@ _SIGS = {
                                _i32, _i64, _i32, _i32, _i32, _i32, _vp, _sz, _vp], _i32),
     "medusa_speculative_sample": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp], _i32),
     "medusa_advance": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp], _i32),
-    "medusa_plant_greedy": ([_vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, ctypes.c_uint64, _vp, _vp], _i32),
+    "medusa_plant_greedy": ([_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, ctypes.c_uint64, _vp, _vp], _i32),
+    "medusa_accept_stats": ([_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp], _i32),
+    "medusa_tree_select": ([_vp, _i32, _i32, _i32, _vp, _vp], _i32),
     "medusa_decoder_workspace_size": ([_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32], _sz),
     "medusa_decoder_verify": ([_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
                                _i32, _i32, _i32, _i32, _f32, _f32, _vp, _vp, _vp, _sz, _vp], _i32),
@@ -444,15 +446,40 @@ def medusa_advance(tree: Tree, accept_len, accept_nodes, out_tokens, hidden, roo
     return root_tok
 
 
-def medusa_plant_greedy(tree: Tree, topk_idx, cache_len, greedy, V: int, alpha: float = 0.8, seed: int = 0,
+def medusa_plant_greedy(tree: Tree, topk_idx, cache_len, greedy, V: int, alpha=0.8, seed: int = 0,
                         stream=None):
     """Measurement aid: overwrite greedy [B][N] with a continuation drawn
-    from the rank prior alpha (1 - alpha)^r (see include/medusa.h)."""
+    from the rank prior a (1 - a)^r (see include/medusa.h); alpha: one value
+    or one per depth."""
     B, K, topk = topk_idx.shape
+    a = (ctypes.c_float * 16)(*([float(x) for x in alpha] if hasattr(alpha, "__len__") else [float(alpha)]))
+    n = len(alpha) if hasattr(alpha, "__len__") else 1
     _check("medusa_plant_greedy", _lib.medusa_plant_greedy(
-        tree.handle, _p(topk_idx), _p(cache_len), B, K, topk, int(V), float(alpha), ctypes.c_uint64(seed),
-        _p(greedy), _stream(stream)))
+        tree.handle, _p(topk_idx), _p(cache_len), B, K, topk, int(V), ctypes.cast(a, ctypes.c_void_p), n,
+        ctypes.c_uint64(seed), _p(greedy), _stream(stream)))
     return greedy
+
+
+def medusa_accept_stats(tree: Tree, accept_len, accept_nodes, out_tokens, topk_idx, counts, stream=None):
+    """Add one round's acceptance observations to counts [K][topk + 1] (int32)."""
+    B, K, topk = topk_idx.shape
+    _check("medusa_accept_stats", _lib.medusa_accept_stats(
+        tree.handle, _p(accept_len), _p(accept_nodes), _p(out_tokens), _p(topk_idx), B, K, topk, _p(counts),
+        _stream(stream)))
+    return counts
+
+
+def tree_select(acc, N: int):
+    """(parent, rank) of the N-node tree chosen best-first under acc
+    [K][topk] (per-depth probability that each rank's guess is right)."""
+    import numpy as np
+    a = np.ascontiguousarray(acc, dtype=np.float64)
+    K, topk = a.shape
+    parent = np.empty(N, dtype=np.int32)
+    rank = np.empty(N, dtype=np.int32)
+    _check("medusa_tree_select", _lib.medusa_tree_select(a.ctypes.data, K, topk, N, parent.ctypes.data,
+                                                         rank.ctypes.data))
+    return parent, rank
 
 
 # ---------------------------------------------------------------------------

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <string>
@@ -53,7 +54,10 @@ struct LayerPtrs {
     const bf16_t *wqkv, *wo, *w_gate_up, *w_down;
 };
 void launch_plant_greedy(const TreeDev& t, const int32_t* topk_idx, int B, int K, int topk,
-                         const int32_t* cache_len, float alpha, uint64_t seed, int V, int32_t* greedy,
+                         const int32_t* cache_len, const PlantAlphas& pa, uint64_t seed, int V, int32_t* greedy,
+                         hipStream_t s);
+void launch_accept_stats(const TreeDev& t, const int32_t* accept_len, const int32_t* accept_nodes,
+                         const int32_t* out_tokens, const int32_t* topk_idx, int B, int K, int topk, int32_t* counts,
                          hipStream_t s);
 void launch_advance(const TreeDev& t, const int32_t* accept_len, const int32_t* accept_nodes,
                     const int32_t* out_tokens, const float* hidden, int B, int H, bool bf16, int32_t* root_tok,
@@ -748,17 +752,105 @@ medusa_status medusa_advance(const medusa_tree* tree, const int32_t* accept_len,
 // measurement aid: planted base-model choices
 // ---------------------------------------------------------------------------
 medusa_status medusa_plant_greedy(const medusa_tree* tree, const int32_t* topk_idx, const int32_t* cache_len, int B,
-                                  int K, int topk, int V, float alpha, uint64_t seed, int32_t* greedy, void* stream) {
+                                  int K, int topk, int V, const float* alpha, int n_alpha, uint64_t seed,
+                                  int32_t* greedy, void* stream) {
     return guarded("medusa_plant_greedy", [&] {
+        REQUIRE(alpha && n_alpha >= 1, "need at least one alpha");
         REQUIRE(tree && topk_idx && cache_len && greedy, "null pointer argument");
         REQUIRE(B >= 1 && V >= 1, "B and V must be positive (B=%d V=%d)", B, V);
         REQUIRE(K >= tree->t.max_depth, "K=%d is smaller than the tree depth %d", K, tree->t.max_depth);
         REQUIRE(topk >= 1 && topk > tree->t.max_rank, "topk=%d does not cover rank %d", topk, tree->t.max_rank);
         SUPPORT(tree->t.max_depth <= MEDUSA_MAX_DEPTH, "tree depth %d exceeds %d", tree->t.max_depth,
                 MEDUSA_MAX_DEPTH);
-        REQUIRE(alpha >= 0.f && alpha <= 1.f, "alpha=%g must be in [0, 1]", alpha);
-        launch_plant_greedy(tree->t, topk_idx, B, K, topk, cache_len, alpha, seed, V, greedy, (hipStream_t)stream);
+        PlantAlphas pa;
+        for (int d = 0; d < 16; ++d) {
+            pa.a[d] = alpha[d < n_alpha ? d : n_alpha - 1];
+            REQUIRE(pa.a[d] >= 0.f && pa.a[d] <= 1.f, "alpha=%g must be in [0, 1]", pa.a[d]);
+        }
+        launch_plant_greedy(tree->t, topk_idx, B, K, topk, cache_len, pa, seed, V, greedy, (hipStream_t)stream);
     });
+}
+
+medusa_status medusa_accept_stats(const medusa_tree* tree, const int32_t* accept_len, const int32_t* accept_nodes,
+                                  const int32_t* out_tokens, const int32_t* topk_idx, int B, int K, int topk,
+                                  int32_t* counts, void* stream) {
+    return guarded("medusa_accept_stats", [&] {
+        REQUIRE(tree && accept_len && accept_nodes && out_tokens && topk_idx && counts, "null pointer argument");
+        REQUIRE(B >= 1 && topk >= 1, "B and topk must be positive");
+        REQUIRE(K >= tree->t.max_depth && K >= 1, "K=%d is smaller than the tree depth %d", K, tree->t.max_depth);
+        SUPPORT(K <= 64 && tree->t.max_depth <= MEDUSA_MAX_DEPTH, "K=%d or the tree depth exceeds the limits", K);
+        launch_accept_stats(tree->t, accept_len, accept_nodes, out_tokens, topk_idx, B, K, topk, counts,
+                            (hipStream_t)stream);
+    });
+}
+
+// ---------------------------------------------------------------------------
+// choosing a tree: the N rank tuples with the largest product of per-depth
+// acceptance probabilities, best first
+// ---------------------------------------------------------------------------
+medusa_status medusa_tree_select(const double* acc, int K, int topk, int N, int32_t* parent, int32_t* rank) {
+    g_err.clear();
+    try {
+        REQUIRE(acc && parent && rank, "null pointer argument");
+        REQUIRE(K >= 1 && topk >= 1 && N >= 1, "K, topk and N must be positive");
+        SUPPORT(N <= MEDUSA_MAX_TREE_NODES && topk <= MEDUSA_MAX_TOPK && K <= MEDUSA_MAX_DEPTH,
+                "N=%d, topk=%d or K=%d exceeds the limits", N, topk, K);
+        for (int i = 0; i < K * topk; ++i) REQUIRE(acc[i] >= 0.0 && acc[i] <= 1.0, "acc[%d]=%g not in [0, 1]", i, acc[i]);
+        // a candidate: (product, rank tuple); best = larger product, then
+        // shallower, then the lexicographically smaller tuple
+        struct Cand {
+            double prod;
+            std::vector<int> path;
+        };
+        auto worse = [](const Cand& a, const Cand& b) {  // a ranks after b
+            if (a.prod != b.prod) return a.prod < b.prod;
+            if (a.path.size() != b.path.size()) return a.path.size() > b.path.size();
+            return b.path < a.path;
+        };
+        std::vector<Cand> heap;
+        auto push = [&](std::vector<int> p) {
+            double prod = 1.0;
+            for (size_t d = 0; d < p.size(); ++d) prod *= acc[d * topk + p[d]];
+            heap.push_back(Cand{prod, std::move(p)});
+            std::push_heap(heap.begin(), heap.end(), worse);
+        };
+        std::vector<std::vector<int>> chosen{{}};
+        for (int r = 0; r < topk; ++r) push({r});
+        while ((int)chosen.size() < N && !heap.empty()) {
+            std::pop_heap(heap.begin(), heap.end(), worse);
+            Cand c = std::move(heap.back());
+            heap.pop_back();
+            if ((int)c.path.size() < K)
+                for (int r = 0; r < topk; ++r) {
+                    std::vector<int> q = c.path;
+                    q.push_back(r);
+                    push(std::move(q));
+                }
+            chosen.push_back(std::move(c.path));
+        }
+        REQUIRE((int)chosen.size() == N, "only %zu candidates exist for N=%d", chosen.size(), N);
+        // breadth-first order: by depth, then rank tuple
+        std::sort(chosen.begin(), chosen.end(), [](const std::vector<int>& a, const std::vector<int>& b) {
+            return a.size() != b.size() ? a.size() < b.size() : a < b;
+        });
+        std::map<std::vector<int>, int> index;
+        for (int i = 0; i < N; ++i) index[chosen[i]] = i;
+        parent[0] = -1;
+        rank[0] = 0;
+        for (int i = 1; i < N; ++i) {
+            std::vector<int> up(chosen[i].begin(), chosen[i].end() - 1);
+            auto it = index.find(up);
+            // products of probabilities <= 1 never grow along a path, so the
+            // best-first set is prefix-closed; equal products keep the order
+            // above (a parent is shallower than its child)
+            REQUIRE(it != index.end(), "internal: chosen set not prefix-closed");
+            parent[i] = it->second;
+            rank[i] = chosen[i].back();
+        }
+    } catch (const Fail& x) {
+        return x.st;
+    }
+    return MEDUSA_OK;
 }
 
 // ---------------------------------------------------------------------------

@@ -578,7 +578,7 @@ __device__ __forceinline__ uint64_t mix64(uint64_t z) {
 
 __global__ __launch_bounds__(256) void plant_greedy_kernel(const int* __restrict__ depth, int N, int max_depth,
                                                            const int32_t* __restrict__ topk_idx, int K, int topk,
-                                                           const int32_t* __restrict__ cache_len, float alpha,
+                                                           const int32_t* __restrict__ cache_len, PlantAlphas pa,
                                                            uint64_t seed, int V, int32_t* __restrict__ greedy) {
     __shared__ int s_next[MEDUSA_MAX_DEPTH_DEV + 1];  // the token after a node of depth d
     const int b = blockIdx.x, tid = threadIdx.x;
@@ -588,6 +588,7 @@ __global__ __launch_bounds__(256) void plant_greedy_kernel(const int* __restrict
         const float u = (float)(z >> 40) * (1.0f / 16777216.0f);
         const int32_t* cand = topk_idx + ((size_t)b * K + min(d, K - 1)) * topk;
         // the rank drawn: the first r with u < sum_{j <= r} alpha (1 - alpha)^j
+        const float alpha = pa.a[min(d, MEDUSA_MAX_DEPTH_DEV - 1)];
         int r = topk;
         float cum = 0.f, pr = alpha;
         for (int j = 0; j < topk && d < K; ++j) {
@@ -614,10 +615,49 @@ __global__ __launch_bounds__(256) void plant_greedy_kernel(const int* __restrict
 }
 
 void launch_plant_greedy(const TreeDev& t, const int32_t* topk_idx, int B, int K, int topk,
-                         const int32_t* cache_len, float alpha, uint64_t seed, int V, int32_t* greedy,
+                         const int32_t* cache_len, const PlantAlphas& pa, uint64_t seed, int V, int32_t* greedy,
                          hipStream_t s) {
     MEDUSA_LAUNCH("plant_greedy", plant_greedy_kernel, dim3(B), dim3(256), 0, s, t.depth, t.N, t.max_depth, topk_idx,
-                  K, topk, cache_len, alpha, seed, V, greedy);
+                  K, topk, cache_len, pa, seed, V, greedy);
+}
+
+// ---------------------------------------------------------------------------
+// Acceptance statistics for choosing the tree from what rounds accept.  What
+// a round reveals about sequence b: the base model's choice at every depth
+// d <= L was the candidate on the accepted path (its rank is the node's
+// rank), and at depth L + 1 <= K it was the bonus token, whose rank among
+// head L + 1's guesses is found in topk_idx (or it is none of them: bucket
+// topk); deeper depths are not observed.  counts [K][topk + 1] gathers them
+// (atomic adds; one block per sequence).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void accept_stats_kernel(const int* __restrict__ rank, int Dmax,
+                                                          const int32_t* __restrict__ accept_len,
+                                                          const int32_t* __restrict__ accept_nodes,
+                                                          const int32_t* __restrict__ out_tokens,
+                                                          const int32_t* __restrict__ topk_idx, int K, int topk,
+                                                          int32_t* __restrict__ counts) {
+    const int b = blockIdx.x, d = threadIdx.x + 1;  // depth observed by this thread
+    const int L = accept_len[b];
+    if (L < 0 || L > Dmax || d > K) return;
+    int r = -1;
+    if (d <= L) {
+        const int node = accept_nodes[(size_t)b * (Dmax + 1) + d];
+        if (node >= 0) r = rank[node];
+    } else if (d == L + 1) {
+        const int tok = out_tokens[(size_t)b * (Dmax + 1) + L];
+        const int32_t* cand = topk_idx + ((size_t)b * K + (d - 1)) * topk;
+        r = topk;
+        for (int j = 0; j < topk; ++j)
+            if (cand[j] == tok) { r = j; break; }
+    }
+    if (r >= 0) atomicAdd(&counts[(d - 1) * (topk + 1) + r], 1);
+}
+
+void launch_accept_stats(const TreeDev& t, const int32_t* accept_len, const int32_t* accept_nodes,
+                         const int32_t* out_tokens, const int32_t* topk_idx, int B, int K, int topk, int32_t* counts,
+                         hipStream_t s) {
+    MEDUSA_LAUNCH("accept_stats", accept_stats_kernel, dim3(B), dim3(64), 0, s, t.rank, t.max_depth, accept_len,
+                  accept_nodes, out_tokens, topk_idx, K, topk, counts);
 }
 
 // ---------------------------------------------------------------------------

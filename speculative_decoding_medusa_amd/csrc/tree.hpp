@@ -22,4 +22,9 @@ struct TreeDev {
     std::vector<uint64_t> h_mask;
 };
 
+// per-depth alphas of the planted continuation (depth d uses a[min(d, 15)])
+struct PlantAlphas {
+    float a[16];
+};
+
 }  // namespace medusa

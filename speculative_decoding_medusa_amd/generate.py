@@ -18,8 +18,8 @@ from __future__ import annotations
 import torch
 
 from . import (Packed, Tree, _ws, chain_tree, decoder_workspace_size, heads_workspace_size, medusa_accept,
-               medusa_advance, medusa_build_tree, medusa_decoder_verify, medusa_heads_forward, medusa_plant_greedy,
-               medusa_prefill, ROW_MAJOR, PACKED, BF16, F32)
+               medusa_accept_stats, medusa_advance, medusa_build_tree, medusa_decoder_verify, medusa_heads_forward,
+               medusa_plant_greedy, medusa_prefill, ROW_MAJOR, PACKED, BF16, F32)
 
 
 class MedusaLoop:
@@ -55,6 +55,7 @@ class MedusaLoop:
         self.heads, self.layers, self.embedding, self.lm_head, self.tree = heads, layers, embedding, lm_head, tree
         self.topk, self.nH, self.rms_eps, self.rope_base = topk, nH, rms_eps, rope_base
         self.planted, self.plant_seed = planted, plant_seed
+        self.stats = None   # counts [K][topk + 1] of medusa_accept_stats, when gathered
         self.k_cache, self.v_cache = k_cache, v_cache
         self.cache_len, self.h, self.root_tok = cache_len, h, root_tok
         n_layers, B, nKV, Lmax, D = k_cache.shape
@@ -106,6 +107,27 @@ class MedusaLoop:
                        rope_base=self.rope_base, stream=stream)
         self.restart(start_len + T)
 
+    def set_tree(self, tree: Tree):
+        """Use another candidate tree from the next round on (a host call
+        between rounds; buffers that depend on the tree are reallocated when
+        its size or depth differs)."""
+        dev = self.h.device
+        B, H = self.h.shape
+        i32 = dict(dtype=torch.int32, device=dev)
+        if tree.N != self.N:
+            self.node_tok = torch.empty(B, tree.N, **i32)
+            self.node_pos = torch.empty(B, tree.N, **i32)
+            self.greedy = torch.empty(B, tree.N, **i32)
+            self.hidden = torch.empty(B, tree.N, H, dtype=torch.float32, device=dev)
+            n_layers, _, nKV, Lmax, D = self.k_cache.shape
+            V = self.embedding.shape[0]
+            F = self.layers[0]["w_gate_up"].rows // 2
+            self.ws_dec = _ws(decoder_workspace_size(tree, B, H, self.nH, nKV, D, F, V, self.max_cache_len), dev, None)
+        if tree.max_depth != self.tree.max_depth:
+            self.accept_nodes = torch.empty(B, tree.max_depth + 1, **i32)
+            self.out_tokens = torch.empty(B, tree.max_depth + 1, **i32)
+        self.tree, self.N = tree, tree.N
+
     def restart(self, start_len: int):
         """Set the round budget from start_len, the longest prefix the
         sequences now hold (after the caller restored or replaced the state)."""
@@ -139,6 +161,9 @@ class MedusaLoop:
                                 self.plant_seed, stream=stream)
         medusa_accept(self.tree, self.node_tok, self.greedy, self.accept_len, self.accept_nodes, self.out_tokens,
                       self.cache_len, self.new_cache_len, k_cache=self.k_cache, v_cache=self.v_cache, stream=stream)
+        if self.stats is not None:
+            medusa_accept_stats(self.tree, self.accept_len, self.accept_nodes, self.out_tokens, self.topk_idx,
+                                self.stats, stream=stream)
         medusa_advance(self.tree, self.accept_len, self.accept_nodes, self.out_tokens, self.hidden, self.root_tok,
                        self.h, tokens=self.tokens, n_tokens=self.n_tokens, new_cache_len=self.new_cache_len,
                        cache_len=self.cache_len, stream=stream)

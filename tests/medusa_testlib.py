@@ -302,15 +302,16 @@ def planted_next_tokens(topk_idx_b, K, topk, P, max_depth, alpha, seed, b, V):
         z = mix64(mix64(mix64((seed ^ b) & _M64) ^ (P & 0xFFFFFFFF)) ^ d)
         u = np.float32(z >> 40) * np.float32(1.0 / 16777216.0)
         cand = [int(x) for x in topk_idx_b[min(d, K - 1)]]
+        a = alpha[min(d, len(alpha) - 1, 15)] if hasattr(alpha, "__len__") else alpha
         r = topk
         if d < K:
-            cum, pr = np.float32(0), np.float32(alpha)
+            cum, pr = np.float32(0), np.float32(a)
             for j in range(topk):
                 cum = np.float32(cum + pr)
                 if u < cum:
                     r = j
                     break
-                pr = np.float32(pr * np.float32(1.0 - np.float32(alpha)))
+                pr = np.float32(pr * np.float32(1.0 - np.float32(a)))
         if r < topk:
             tok = cand[r]
         else:
@@ -333,3 +334,18 @@ def planted_greedy_ref(depth, topk_idx, cache_len, alpha, seed, V):
         nxt = planted_next_tokens(topk_idx[b], K, topk, int(cache_len[b]), int(depth.max()), alpha, seed, b, V)
         g[b] = [nxt[d] for d in depth]
     return g
+
+
+def accept_stats_ref(rank, Dmax, accept_len, accept_nodes, out_tokens, topk_idx):
+    """counts [K][topk + 1] that one round of medusa_accept_stats adds."""
+    B, K, topk = topk_idx.shape
+    c = np.zeros((K, topk + 1), dtype=np.int64)
+    for b in range(B):
+        L = int(accept_len[b])
+        for d in range(1, L + 1):
+            c[d - 1, rank[accept_nodes[b, d]]] += 1
+        if L + 1 <= K:
+            cand = list(topk_idx[b, L])
+            tok = int(out_tokens[b, L])
+            c[L, cand.index(tok) if tok in cand else topk] += 1
+    return c

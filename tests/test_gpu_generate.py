@@ -316,3 +316,40 @@ def test_plant_greedy_matches_host_reference(alpha, tree_name):
     M.medusa_plant_greedy(t, dev(tk), dev(P), g, V, alpha, seed=0xC0FFEE)
     torch.cuda.synchronize()
     assert np.array_equal(g.cpu().numpy(), planted_greedy_ref(tree.depth, tk, P, alpha, 0xC0FFEE, V))
+
+
+@pytest.mark.parametrize("tree_name", ["sparse64", "dense256", "tiny"])
+def test_accept_stats_matches_host_reference(tree_name):
+    """medusa_accept_stats over three rounds of planted acceptance (per-depth
+    alphas falling with depth) against the host count of what each round
+    revealed."""
+    import speculative_decoding_medusa_amd as M
+    from medusa_testlib import accept_stats_ref
+    _say("accept_stats", tree_name)
+    tree = {"sparse64": mi.sparse_tree(64), "dense256": mi.dense_tree(256), "tiny": mi.tiny_tree()}[tree_name]
+    parent, rank = tree.arrays()
+    K = max(tree.depth) + (1 if tree_name == "tiny" else 0)    # tiny: a head beyond the tree's depth
+    topk = int(max(rank)) + 1
+    B, V = 29, 5000
+    t = M.Tree(parent, rank, K, topk)
+    counts = torch.zeros(K, topk + 1, dtype=torch.int32, device="cuda")
+    want = np.zeros((K, topk + 1), dtype=np.int64)
+    r = np.random.default_rng(31)
+    Dm = t.max_depth
+    for rnd in range(3):
+        tk = np.stack([np.stack([r.choice(V, topk, replace=False) for _ in range(K)]) for _ in range(B)]).astype(np.int32)
+        P = r.integers(0, 1 << 20, B).astype(np.int32)
+        root = r.integers(0, V, B).astype(np.int32)
+        tok, _, _ = oracle.build_tree(parent, rank, tk, root, P)
+        g = torch.empty(B, tree.n, dtype=torch.int32, device="cuda")
+        M.medusa_plant_greedy(t, dev(tk), dev(P), g, V, [0.9, 0.7, 0.5, 0.4, 0.3], seed=rnd)
+        al = torch.empty(B, dtype=torch.int32, device="cuda")
+        an = torch.empty(B, Dm + 1, dtype=torch.int32, device="cuda")
+        ot = torch.empty(B, Dm + 1, dtype=torch.int32, device="cuda")
+        ncl = torch.empty(B, dtype=torch.int32, device="cuda")
+        M.medusa_accept(t, dev(tok), g, al, an, ot, dev(P), ncl)
+        M.medusa_accept_stats(t, al, an, ot, dev(tk), counts)
+        torch.cuda.synchronize()
+        want += accept_stats_ref(rank, Dm, al.cpu().numpy(), an.cpu().numpy(), ot.cpu().numpy(), tk)
+        assert np.array_equal(counts.cpu().numpy(), want), rnd
+    assert want.sum() > 3 * B
