@@ -108,6 +108,33 @@ def parse():
     return ap.parse_args()
 
 
+def read_ceiling(gib: int = 1, reps: int = 10):
+    """The achievable HBM read rate for the weight streams' access pattern:
+    medusa_stream_read (16-byte non-temporal loads, 4 in flight per thread,
+    16,384 workgroups) over `gib` GiB, timed with HIP events on the launch
+    stream."""
+    import torch
+
+    import speculative_decoding_medusa_amd as M
+    n = gib << 30
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    buf.fill_(3)
+    sink = torch.empty(16384, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        M.medusa_stream_read(buf, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        M.medusa_stream_read(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf
+    return {"GBs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "kernel": "stream_read",
+            "bytes": n, "workgroups": 16384, "reps": reps}
+
+
 def copy_calibration(mib: int):
     """Three plain copies of a known size: the HBM byte counters of these
     dispatches convert counter units into bytes."""
@@ -286,10 +313,12 @@ def main():
     vt_name = "vocab_proj_topk" if w2_layout == M.ROW_MAJOR else "vocab_proj_topk_mfma"
     vt_us = kern_us[vt_name]
     achieved = algo_bytes / (vt_us * 1e-6) / 1e9
+    ceiling = read_ceiling()
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": vocab_traffic_bytes() if w2_layout == M.ROW_MAJOR else None, "kernel": vt_name,
-                "bytes_per_launch": algo_bytes, "avg_us": round(vt_us, 2)}
+                "bytes_per_launch": algo_bytes, "avg_us": round(vt_us, 2),
+                "frac_of_read_ceiling": round(achieved / ceiling["GBs"], 4)}
 
     t_verify_us = st["tree_attention"]
     prior_tokens = tree_prior_tokens(*cfg.tree.arrays())
@@ -316,6 +345,7 @@ def main():
         "kernels_us": {k: round(v, 2) for k, v in kern_us.items()},
         "wall_ms_per_step": round(1e3 * wall / args.steps, 4),
         "roofline": roofline,
+        "hbm_read_ceiling": ceiling,
         "input_gen_s": round(gen_s, 2),
     }
     if not args.no_cpu_baseline:
@@ -367,10 +397,25 @@ def cpu_baseline(cfg, heads, att, root):
     t["accept"] = time.perf_counter() - t0
     total = sum(t.values())
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    # the whole heads stage (every head, nothing scaled) on one thread: the
+    # bf16 -> float64 widening, the residual-SiLU block, the projection and
+    # the per-head top-k, one head at a time so one head's weights are resident
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        h = oracle.widen(heads["h"], dt)
+        for k in range(cfg.K):
+            lg, _ = oracle.medusa_heads(h, oracle.widen(heads["W1"][k:k + 1], dt),
+                                        oracle.widen(heads["b1"][k:k + 1], dt), oracle.widen(heads["W2"][k:k + 1], dt))
+            oracle.topk(lg, cfg.topk)
+        heads_1t = time.perf_counter() - t0
     return {"value": round(1.0 / total, 5), "unit": "steps/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"float64 NumPy oracle: 1 of {cfg.K} heads, {nh} of {cfg.nH} attention heads, 8 of "
-                      f"{cfg.B * cfg.N} greedy rows, each stage timed and scaled linearly to the full step",
+            "sample": f"estimate: float64 NumPy oracle on {int(threads)} threads over 1 of {cfg.K} heads, {nh} of "
+                      f"{cfg.nH} attention heads and 8 of {cfg.B * cfg.N} greedy rows, each stage timed and scaled "
+                      f"linearly to the full step",
             "stage_s": {k: round(v, 3) for k, v in t.items()},
+            "heads_stage_single_thread": {"s": round(heads_1t, 3), "cores": 1, "scaled": False,
+                                          "what": f"all {cfg.K} heads: widening, residual-SiLU, projection, top-k"},
             "host_cpus": len(os.sched_getaffinity(0))}
 
 

@@ -547,6 +547,16 @@ medusa_status medusa_swiglu(const float* gate_up, int R, int F, void* a, void* s
 medusa_status medusa_embed(const int32_t* tok, const void* embedding, int R, int H, int V, float* x, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Measurement aid: reads `bytes` (a multiple of 16; src 16-byte aligned) once
+ * with 16-byte non-temporal loads, 4 in flight per thread, n_wg workgroups of
+ * 256 threads each taking a contiguous slice, and writes the XOR of what
+ * each workgroup read to sink[n_wg] (uint32).  Its rate is the achievable
+ * HBM read ceiling for the weight streams' access pattern (bench.py times it
+ * over 1 GiB with 16,384 workgroups).
+ * ------------------------------------------------------------------------- */
+medusa_status medusa_stream_read(const void* src, size_t bytes, uint32_t* sink, int n_wg, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Kernel timing: while enabled, every kernel launch of the library is
  * bracketed by HIP events on its stream.  medusa_profiler_collect waits for
  * the recorded events and folds them into per-kernel totals and returns their

@@ -76,6 +76,7 @@ _SIGS = {
     "medusa_rope": ([_vp, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
     "medusa_swiglu": ([_vp, _i32, _i32, _vp, _vp], _i32),
     "medusa_embed": ([_vp, _vp, _i32, _i32, _i32, _vp, _vp], _i32),
+    "medusa_stream_read": ([_vp, _sz, _vp, _i32, _vp], _i32),
     "medusa_profiler_enable": ([_i32], _i32),
     "medusa_profiler_reset": ([], _i32),
     "medusa_profiler_collect": ([], _i32),
@@ -603,6 +604,14 @@ def medusa_embed(tok, embedding, x, stream=None):
     V, H = embedding.shape
     _check("medusa_embed", _lib.medusa_embed(_p(tok), _p(embedding), tok.numel(), H, V, _p(x), _stream(stream)))
     return x
+
+
+def medusa_stream_read(src, sink, n_wg: int = 16384, stream=None):
+    """Measurement aid: read src (a device tensor) once as the weight streams
+    read (see include/medusa.h); sink: [n_wg] int32 device tensor."""
+    nbytes = src.numel() * src.element_size()
+    _check("medusa_stream_read", _lib.medusa_stream_read(_p(src), nbytes, _p(sink), int(n_wg), _stream(stream)))
+    return sink
 
 
 def profiler_enable(on: bool = True):

@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libmedusa.so")
-SOURCES = ["abi.hip", "heads.hip", "tree.hip", "attention.hip", "greedy.hip", "decoder.hip", "pack.hip"]
+SOURCES = ["abi.hip", "heads.hip", "tree.hip", "attention.hip", "greedy.hip", "decoder.hip", "pack.hip", "measure.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -53,6 +53,7 @@ void launch_accept(const TreeDev& t, const int32_t* node_tok, const int32_t* gre
 struct LayerPtrs {
     const bf16_t *wqkv, *wo, *w_gate_up, *w_down;
 };
+void launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int n_wg, hipStream_t s);
 void launch_plant_greedy(const TreeDev& t, const int32_t* topk_idx, int B, int K, int topk,
                          const int32_t* cache_len, const PlantAlphas& pa, uint64_t seed, int V, int32_t* greedy,
                          hipStream_t s);
@@ -768,6 +769,16 @@ medusa_status medusa_plant_greedy(const medusa_tree* tree, const int32_t* topk_i
             REQUIRE(pa.a[d] >= 0.f && pa.a[d] <= 1.f, "alpha=%g must be in [0, 1]", pa.a[d]);
         }
         launch_plant_greedy(tree->t, topk_idx, B, K, topk, cache_len, pa, seed, V, greedy, (hipStream_t)stream);
+    });
+}
+
+medusa_status medusa_stream_read(const void* src, size_t bytes, uint32_t* sink, int n_wg, void* stream) {
+    return guarded("medusa_stream_read", [&] {
+        REQUIRE(src && sink, "null pointer argument");
+        REQUIRE(bytes >= 16 && bytes % 16 == 0, "bytes=%zu must be a positive multiple of 16", bytes);
+        REQUIRE(((uintptr_t)src & 15) == 0, "src must be 16-byte aligned");
+        REQUIRE(n_wg >= 1 && n_wg <= (1 << 20), "n_wg=%d must be in [1, 2^20]", n_wg);
+        launch_stream_read(src, bytes, sink, n_wg, (hipStream_t)stream);
     });
 }
 
