@@ -87,19 +87,28 @@ static size_t a256(size_t x) { return (x + 255) / 256 * 256; }
 // each wave takes two weight blocks (a fragment read feeds two products):
 // 256 x 128256 in 280 us against 363, 512 x 128256 in 574 against 717; 8
 // waves unless that leaves fewer than 256 workgroups (256 x 32000: 4 waves,
-// 110 us against 126).
+// 110 us against 126).  256-row node tiles that would get fewer than 256
+// workgroups split the node blocks over two waves instead of dropping to 4
+// waves (8 waves: 4 row groups x 2 node halves, 128 weight rows per
+// workgroup): each wave then reads 8 node fragments a chunk, and two waves
+// per SIMD hide each other's latencies (256 x 32000: 104 us against 125).
+// With enough workgroups the unsplit 8-wave tile stays faster (512 x 128256:
+// 620 us against 780): the split doubles the workgroups that stage each node
+// row.
 struct LmhShape {
-    int waves, rb;
+    int waves, rb, ns;
 };
 static LmhShape lmh_shape(int R, int V) {
     const int nblk = lmh_nblk(R);
-    if (nblk < 8) return {V >= 8192 ? 8 : 4, 1};
+    if (nblk < 8) return {V >= 8192 ? 8 : 4, 1, 1};
     const int tiles = (R + nblk * 16 - 1) / (nblk * 16);
-    return {(V + 255) / 256 * tiles >= 256 ? 8 : 4, 2};
+    const bool many = (V + 255) / 256 * tiles >= 256;
+    if (nblk == 16) return {8, 2, many ? 1 : 2};
+    return {many ? 8 : 4, 2, 1};
 }
 static int lmh_groups(int R, int V) {
     const LmhShape sh = lmh_shape(R, V);
-    const int rows = 16 * sh.waves * sh.rb;
+    const int rows = 16 * sh.waves / sh.ns * sh.rb;
     return (V + rows - 1) / rows;
 }
 
@@ -116,17 +125,19 @@ void launch_lm_head_greedy(const bf16_t* n, const bf16_t* lm_head, int R, int H,
     const int nblk = lmh_nblk(R);
     const dim3 grid(G, (R + nblk * 16 - 1) / (nblk * 16));
     const int nch = H / lmh_kc(nblk);
-#define LMH_LAUNCH(NB, WV, RBL)                                                                                 \
-    MEDUSA_LAUNCH("lm_head_argmax", (skinny_mfma_kernel<NB, SKINNY_ARGMAX, WV, RBL>), grid, dim3(WV * 64), 0, s, \
-                  n, lm_head, R, H, V, nch, cv, ci, logits, rs_eps)
-    if (lmh_shape(R, V).waves == 8) {
-        if (nblk == 4) LMH_LAUNCH(4, 8, 1);
-        else if (nblk == 8) LMH_LAUNCH(8, 8, 2);
-        else LMH_LAUNCH(16, 8, 2);
+#define LMH_LAUNCH(NB, WV, RBL, NSP)                                                                   \
+    MEDUSA_LAUNCH("lm_head_argmax", (skinny_mfma_kernel<NB, SKINNY_ARGMAX, WV, RBL, NSP>), grid, dim3(WV * 64), 0, \
+                  s, n, lm_head, R, H, V, nch, cv, ci, logits, rs_eps)
+    const LmhShape sh = lmh_shape(R, V);
+    if (nblk == 16) {
+        if (sh.ns == 2) LMH_LAUNCH(16, 8, 2, 2);
+        else LMH_LAUNCH(16, 8, 2, 1);
+    } else if (sh.waves == 8) {
+        if (nblk == 4) LMH_LAUNCH(4, 8, 1, 1);
+        else LMH_LAUNCH(8, 8, 2, 1);
     } else {
-        if (nblk == 4) LMH_LAUNCH(4, 4, 1);
-        else if (nblk == 8) LMH_LAUNCH(8, 4, 2);
-        else LMH_LAUNCH(16, 4, 2);
+        if (nblk == 4) LMH_LAUNCH(4, 4, 1, 1);
+        else LMH_LAUNCH(8, 4, 2, 1);
     }
 #undef LMH_LAUNCH
     MEDUSA_LAUNCH("argmax_merge", argmax_merge_kernel, dim3(R), dim3(64), 0, s, cv, ci, G, greedy);

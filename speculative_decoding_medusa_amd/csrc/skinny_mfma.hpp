@@ -58,7 +58,15 @@ struct LmhCfg {
     // use chunks wide enough that every thread stages one 16-byte piece
     static constexpr int KC = NBLK == 1 ? NT / 2 : NBLK <= 8 ? 64 : 32;
     static constexpr int KS = KC / PACK_K;             // MFMA k-steps per chunk
-    static constexpr int LDW = KC + 8;                 // padded LDS row (bf16): conflict-free B reads
+    // LDS rows of the node tile.  Tiles of >= 64 rows: unpadded rows whose
+    // 16-byte column c sits at c ^ swz(row) -- measured with the LDS
+    // bank-conflict counter on gfx950, both the MFMA fragment reads (16 rows x
+    // 4 columns a wave) and the staging writes (KC / 8 pieces a row) are then
+    // conflict-free, where padded rows cost twice the cycles on the reads.
+    // 16-row tiles (wide chunks, little LDS traffic) keep padded rows.
+    static constexpr bool SWZ = NBLK > 1;
+    static constexpr int LDW = SWZ ? KC : KC + 8;
+    static __device__ __forceinline__ int swz(int row) { return SWZ ? (row >> 1) & (KC / 8 - 1) : 0; }
     static constexpr int PIECES = NODES * KC / 8;           // 16-byte node pieces per chunk
     static constexpr int NPT = (PIECES + NT - 1) / NT;     // per thread (the last round may be partial)
     static constexpr bool EVEN = NPT * NT == PIECES;
@@ -75,7 +83,13 @@ struct LmhCfg {
 // RB (ARGMAX only): 16-row weight blocks per wave; every node fragment read
 // from LDS then feeds RB products, which halves the LDS traffic per product
 // at RB = 2 (the bound of the 128- and 256-node tiles).
-template <int NBLK, int EPI, int WAVES = LMH_WAVES, int RB = 1>
+// NS (ARGMAX only): the waves split the node blocks into NS groups -- wave w
+// takes row group w / NS and node blocks (w % NS) NBLK / NS .. -- so each wave
+// reads 1/NS of the node fragments per chunk; the NS waves of a row group
+// load the same weight fragments (the second load hits the caches), and a
+// workgroup has NS times as many waves for the same weight rows, which hide
+// each other's LDS and MFMA latencies.
+template <int NBLK, int EPI, int WAVES = LMH_WAVES, int RB = 1, int NS = 1>
 __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* __restrict__ n,   // [R][K] node rows
                                                           const bf16_t* __restrict__ Wp,  // packed, V rows of K
                                                           int R, int K, int V, int chunks_per_split,
@@ -97,12 +111,15 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
     constexpr int D = C::D;
     constexpr int NT = C::NT;
     __shared__ __attribute__((aligned(16))) bf16_t ns[2][C::NODES][C::LDW];
-    __shared__ float red_v[WAVES][EPI == SKINNY_ARGMAX ? C::NODES : 1];
-    __shared__ int red_i[WAVES][EPI == SKINNY_ARGMAX ? C::NODES : 1];
+    constexpr int RG = WAVES / NS;      // row groups of a workgroup
+    constexpr int NBW = NBLK / NS;      // node blocks per wave
+    __shared__ float red_v[RG][EPI == SKINNY_ARGMAX ? C::NODES : 1];
+    __shared__ int red_i[RG][EPI == SKINNY_ARGMAX ? C::NODES : 1];
     __shared__ f32x4 xup[EPI == SKINNY_SWIGLU ? WAVES / 2 : 1][EPI == SKINNY_SWIGLU ? NBLK : 1][64];
     __shared__ float tkv[EPI == SKINNY_TOPK ? WAVES * PACK_ROWS : 1][8];  // TOPK: the workgroup's rows x sequences
     static_assert((EPI != SKINNY_TOPK && EPI != SKINNY_SILU) || NBLK == 1, "top-k / SiLU epilogue: 16 node rows");
     static_assert(RB == 1 || EPI == SKINNY_ARGMAX, "several row blocks per wave: argmax epilogue only");
+    static_assert(NS == 1 || (EPI == SKINNY_ARGMAX && NBLK % NS == 0 && WAVES % NS == 0), "node split: argmax only");
     if (EPI == SKINNY_TOPK || EPI == SKINNY_SILU) {
         n += (size_t)blockIdx.y * n_stride;
         Wp += (size_t)blockIdx.y * w_stride;
@@ -112,14 +129,15 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
     const int lane = tid & 63, wave = tid >> 6;
     const int G = gridDim.x;
     const int node0 = (EPI == SKINNY_TOPK || EPI == SKINNY_SILU) ? 0 : blockIdx.y * C::NODES;
-    const int rb = (blockIdx.x * WAVES + wave) * RB;  // this wave's first 16-row block
+    const int rgw = wave / NS, ngw = wave % NS;        // this wave's row group and node group
+    const int rb = (blockIdx.x * RG + rgw) * RB;       // this wave's first 16-row block
     const int vw = rb * PACK_ROWS;                    // its first weight row
     const int lr = lane & 15, lk = lane >> 4;         // row / k-group within a 16x16x32 tile
     const int nrb = (V + PACK_ROWS - 1) / PACK_ROWS;
 
-    f32x4 acc[RB * NBLK];  // row block j, node block b: acc[j * NBLK + b]
+    f32x4 acc[RB * NBW];  // row block j, the wave's node block b: acc[j * NBW + b]
 #pragma unroll
-    for (int b = 0; b < RB * NBLK; ++b) acc[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < RB * NBW; ++b) acc[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
     const bf16_t* wb[RB];
 #pragma unroll
@@ -157,7 +175,8 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
 #pragma unroll
         for (int e = 0; e < C::NPT; ++e) {
             const int p = tid + e * NT;
-            if (C::EVEN || p < C::PIECES) *(u32x4*)(&ns[stage][p / (C::KC / 8)][k8p[e] * 8]) = src[e];
+            const int r = p / (C::KC / 8);
+            if (C::EVEN || p < C::PIECES) *(u32x4*)(&ns[stage][r][(k8p[e] ^ C::swz(r)) * 8]) = src[e];
         }
     };
 
@@ -201,13 +220,14 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
 #pragma unroll
                 for (int s = 0; s < C::KS; ++s)
 #pragma unroll
-                    for (int b = 0; b < NBLK; ++b) {
-                        const u32x4 bv = *(const u32x4*)(&ns[stage][b * 16 + lr][s * 32 + lk * 8]);
+                    for (int b = 0; b < NBW; ++b) {
+                        const u32x4 bv = *(const u32x4*)(
+                            &ns[stage][(ngw * NBW + b) * 16 + lr][((s * 4 + lk) ^ C::swz(lr)) * 8]);
 #pragma unroll
                         for (int j = 0; j < RB; ++j)
-                            acc[j * NBLK + b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            acc[j * NBW + b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                                 __builtin_bit_cast(bf16x8, aring[u][s * RB + j]), __builtin_bit_cast(bf16x8, bv),
-                                acc[j * NBLK + b], 0, 0, 0);
+                                acc[j * NBW + b], 0, 0, 0);
                     }
             }
             // the other stage was last read before the previous barrier
@@ -330,17 +350,18 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
         __syncthreads();
     }
 #pragma unroll
-    for (int b = 0; b < NBLK; ++b) {
+    for (int b = 0; b < NBW; ++b) {
         float bv = -INFINITY;
         int bi = 0x7FFFFFFF;
-        const int node = node0 + b * 16 + lr;
-        const float sc = (want_rs && node < R) ? rs_l[b * 16 + lr] : 1.f;
+        const int nb = ngw * NBW + b;  // node block within the workgroup's tile
+        const int node = node0 + nb * 16 + lr;
+        const float sc = (want_rs && node < R) ? rs_l[nb * 16 + lr] : 1.f;
 #pragma unroll
         for (int j = 0; j < RB; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int v = vw + j * PACK_ROWS + lk * 4 + r;
-                const float x = acc[j * NBLK + b][r];
+                const float x = acc[j * NBW + b][r];
                 if (v < V) {
                     if (out != nullptr && node < R) out[(size_t)node * V + v] = x * sc;
                     if (better(x, v, bv, bi)) { bv = x; bi = v; }
@@ -352,14 +373,14 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
             const int oi = __shfl_xor(bi, m, 64);
             if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
         }
-        if (lane < 16) { red_v[wave][b * 16 + lane] = bv; red_i[wave][b * 16 + lane] = bi; }
+        if (lane < 16) { red_v[rgw][nb * 16 + lane] = bv; red_i[rgw][nb * 16 + lane] = bi; }
     }
     __syncthreads();
     for (int j = tid; j < C::NODES; j += NT) {
         float bv = red_v[0][j];
         int bi = red_i[0][j];
 #pragma unroll
-        for (int w = 1; w < WAVES; ++w)
+        for (int w = 1; w < RG; ++w)
             if (better(red_v[w][j], red_i[w][j], bv, bi)) { bv = red_v[w][j]; bi = red_i[w][j]; }
         const int node = node0 + j;
         if (node < R) {

@@ -477,10 +477,14 @@ def test_status_word_reports_cache_overflow(M):
 
 def _dup_positions(t, V, spread):
     """Rows to copy the winning row t to: within the same 16-row fragment
-    ('near') or hundreds of rows away, in other workgroups ('far').  Returns
-    (rows holding a copy, expected order of the tied rows)."""
+    ('near'), in other 16-row blocks tens of rows away, within one workgroup's
+    weight rows but other waves' ('mid'), or hundreds of rows away, in other
+    workgroups ('far').  Returns (rows holding a copy, expected order of the
+    tied rows)."""
     if spread == "near":
         cands = [t - 1, t + 1, t + 5]
+    elif spread == "mid":
+        cands = [t - 37, t + 20, t + 45]
     else:
         cands = [t - 517, t - 1200, t + 733, t + 2100]
     rows = sorted(set(c for c in cands if 0 <= c < V and c != t))
@@ -522,23 +526,25 @@ def test_topk_ties_keep_lower_index(M, layout, spread):
     assert np.array_equal(got, idx_ref)
 
 
-@pytest.mark.parametrize("spread", ["near", "far"])
+@pytest.mark.parametrize("R", [64, 256], ids=["r64", "r256"])     # 256: node blocks split over two waves
+@pytest.mark.parametrize("spread", ["near", "mid", "far"])
 @pytest.mark.parametrize("layout", ["rows", "packed"])
-def test_greedy_ties_keep_lower_index(M, layout, spread):
-    R, H, V = 64, 1024, 5000
+def test_greedy_ties_keep_lower_index(M, layout, spread, R):
+    H, V = 1024, 5000
     cfg = _cfg("gtie", "bf16", 1, H, V, 1, 1, mi.tiny_tree(), seed=251)
-    _say("argmax ties", layout, spread)
+    _say("argmax ties", layout, spread, R)
+    tied = (0, 17, R // 2 + 3, R - 1)
     heads = {"lm_head": mi.normal((V, H), cfg.seed, mi.S_LM_HEAD, 0.02, "bf16")}
     x = mi.normal((R, H), cfg.seed, mi.S_TEST, 1.0, "bf16")
     xw = oracle.widen(x, "bf16")
     enforce_greedy_gap(cfg, heads, xw, [])
     g0, _ = oracle.base_greedy(xw, oracle.widen(heads["lm_head"], "bf16"), 1e-6)
     # copy the winners of a few rows to other rows of lm_head
-    for r in (0, 17, 63):
+    for r in tied:
         rows, _ = _dup_positions(int(g0[r]), V, spread)
         heads["lm_head"][rows] = heads["lm_head"][int(g0[r])]
     g_ref, _ = oracle.base_greedy(xw, oracle.widen(heads["lm_head"], "bf16"), 1e-6)
-    for r in (0, 17, 63):
+    for r in tied:
         _, order = _dup_positions(int(g0[r]), V, spread)
         assert g_ref[r] == order[0]       # the oracle's rule: the lowest of the tied rows
     g = torch.empty(R, dtype=torch.int32, device="cuda")
