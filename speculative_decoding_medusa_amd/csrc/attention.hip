@@ -14,6 +14,8 @@
 // blocks of 16); range s covers keys [s * KPS, (s+1) * KPS) of the key space;
 // split 0 / query block 0 writes the cache slots.  The bf16 MFMA variant
 // follows the merge kernel.
+#include <type_traits>
+
 #include "common.hpp"
 #include "tree.hpp"
 
@@ -539,6 +541,114 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
         for (int db = 0; db < DB; ++db) o[qb][db] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
 
+    // (One query block per wave.)  Keys kb * 16 .. kb * 16 + 31 of the
+    // wave's share of tile i (stage st): S^T of each 16-key block (the lane
+    // holds keys 4 lk .. 4 lk + 3 of both blocks), the mask, the reference,
+    // then O^T += V^T . P^T with the lane's 8 keys of the pair as one 32-deep
+    // contraction, once over the probabilities' bf16 heads and once over
+    // their bf16 remainders (17 significant bits together); A = those 8 keys'
+    // V^T values, 4 from each block's transposing read, so no register is
+    // copied to build it.
+    auto key_pair = [&](auto masked_tag, const char* st, int i, int kb) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+        static_assert(NKB % 2 == 0, "16-key blocks are taken in pairs");
+        f32x4 sc[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            u32x4 ka[DK];
+#pragma unroll
+            for (int ks = 0; ks < DK; ++ks) ka[ks] = *(const u32x4*)(st + koff[ks] + (kb + h) * 16 * ROWB);
+            f32x4 a = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < DK; ++ks)
+                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[ks]),
+                                                            __builtin_bit_cast(bf16x8, qf[0][ks]), a, 0, 0, 0);
+            sc[h] = a;
+        }
+        const int kk0 = kq * KW + kb * 16 + lk * 4;  // the lane's first key of block kb (block kb + 1: 16 on)
+        if constexpr (MASKED) {
+            // keys past the range; in the tree range, non-ancestors
+            const uint64_t word = !tree ? ~0ull : i == 0 ? mrow[0][0] : i == 1 ? mrow[0][1]
+                                               : i == 2 ? mrow[0][2] : mrow[0][3];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int kk = kk0 + h * 16 + r;
+                    const bool vis = i * TK + kk < nkeys && ((word >> kk) & 1ull);
+                    sc[h][r] = vis ? sc[h][r] : -INFINITY;
+                }
+        }
+        const float lm = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                               fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+        if (__any(lm * scale_log2 > Mq[0] + MF_LAZY)) {
+            // raise the reference of the queries that need it (the pair's max
+            // over the query's 4 lanes decides, so they agree)
+            float t = fmaxf(lm, __shfl_xor(lm, 16, 64));
+            t = fmaxf(t, __shfl_xor(t, 32, 64));
+            const float tc = t * scale_log2;
+            const float Mn = tc > Mq[0] + MF_LAZY ? tc : Mq[0];
+            const float alpha = __builtin_amdgcn_exp2f(Mq[0] - Mn);  // exactly 1 when unchanged
+            Mq[0] = Mn;
+            l[0] *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) o[0][db] *= alpha;
+        }
+        // probabilities (bare v_exp_f32: arguments <= 8, masked ones -inf);
+        // k-slots 4 h .. 4 h + 3 of the lane's B fragments are keys
+        // 4 lk .. 4 lk + 3 of block kb + h
+        const float nm = -Mq[0];
+        float pv[8];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                pv[h * 4 + r] = __builtin_amdgcn_exp2f(fmaf(sc[h][r], scale_log2, nm));
+                l[0] += pv[h * 4 + r];
+            }
+        uint32_t hw[4], rw[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            hw[w] = pack_bf16x2(pv[2 * w], pv[2 * w + 1]);
+            rw[w] = pack_bf16x2(pv[2 * w] - bf16_lo(hw[w]), pv[2 * w + 1] - bf16_hi(hw[w]));
+        }
+        const u32x4 ph = (u32x4){hw[0], hw[1], hw[2], hw[3]};
+        const u32x4 pr = (u32x4){rw[0], rw[1], rw[2], rw[3]};
+        // rows past the prefix in the last tile of a prefix range hold
+        // whatever the cache slots hold (they were requested before the
+        // prefix length was known): their probability is 0, but 0 times a
+        // NaN or infinite V is NaN, so the lane's V elements of keys past the
+        // range are zeroed (element e of a transposed read is key 4 lk + e of
+        // its block)
+        uint32_t keep[2][2] = {{~0u, ~0u}, {~0u, ~0u}};
+        if constexpr (MASKED) {
+            if (!tree) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int nv = nkeys - (i * TK + kk0 + h * 16);  // the lane's keys of block kb + h in range
+                    keep[h][0] = nv >= 2 ? ~0u : nv == 1 ? 0x0000FFFFu : 0u;
+                    keep[h][1] = nv >= 4 ? ~0u : nv == 3 ? 0x0000FFFFu : 0u;
+                }
+            }
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            uint2 v0 = __builtin_bit_cast(uint2, ds_read_tr16(st + voff[db] + kb * 16 * ROWB));
+            uint2 v1 = __builtin_bit_cast(uint2, ds_read_tr16(st + voff[db] + (kb + 1) * 16 * ROWB));
+            if constexpr (MASKED) {
+                v0.x &= keep[0][0];
+                v0.y &= keep[0][1];
+                v1.x &= keep[1][0];
+                v1.y &= keep[1][1];
+            }
+            const u32x4 va = (u32x4){v0.x, v0.y, v1.x, v1.y};
+            o[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va),
+                                                               __builtin_bit_cast(bf16x8, ph), o[0][db], 0, 0, 0);
+            o[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va),
+                                                               __builtin_bit_cast(bf16x8, pr), o[0][db], 0, 0, 0);
+        }
+    };
+
     for (int tb = 0; tb < ntiles; tb += MF_STAGES) {
 #pragma unroll
         for (int u = 0; u < MF_STAGES; ++u) {
@@ -562,9 +672,20 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
                 }
                 const char* st = stage_ptr(u);
                 const bool masked = tree || (i + 1) * TK > nkeys;
+                if constexpr (QBW == 1) {
+                    // two 16-key blocks at a time; a tile whose keys are all
+                    // visible runs the body compiled without mask work; not
+                    // unrolled, so the pairs do not compete for registers
+#pragma unroll 1
+                    for (int kb = 0; kb < NKB; kb += 2) {
+                        if (masked) key_pair(std::true_type{}, st, i, kb);
+                        else key_pair(std::false_type{}, st, i, kb);
+                    }
+                } else {
                 // one 16-key block at a time: S^T, mask, reference, then O^T
                 // (the online softmax takes its keys in any grouping); not
-                // unrolled, so the blocks do not compete for registers
+                // unrolled, so the blocks do not compete for registers (two
+                // query blocks per wave leave no room for the pairs)
 #pragma unroll 1
                 for (int kb = 0; kb < NKB; ++kb) {
                     u32x4 ka[DK];
@@ -647,6 +768,7 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
                                                                                 __builtin_bit_cast(bf16x8, pb[qb]),
                                                                                 o[qb][db], 0, 0, 0);
                     }
+                }
                 }
             }
         }
