@@ -427,21 +427,20 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
 #pragma unroll
     for (int qb = 0; qb < QBW; ++qb) qidx[qb] = qblk * QW + qh * 16 * QBW + qb * 16 + lr;
     u32x4 qf[QBW][DK];  // QLDS: read from LDS after the first tile barrier; else loaded below
-    // in the tree range, the queries' ancestor rows (words past W are never
-    // used: the range has W tiles), waited for before any load into LDS is
-    // issued
-    uint64_t mrow[QBW][4];
-#pragma unroll
-    for (int qb = 0; qb < QBW; ++qb)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) mrow[qb][w] = ~0ull;
+    // in the tree range, the block's ancestor rows in LDS (row r: query
+    // min(qblk * QW + r, N - 1); words past W are never used: the range has W
+    // tiles), loaded and waited for before any load into LDS is issued, read
+    // after the first tile's barrier
+    __shared__ uint64_t mlds[QW][4];
     if (tree) {
-#pragma unroll
-        for (int qb = 0; qb < QBW; ++qb)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) mrow[qb][w] = mask[(size_t)min(qidx[qb], N - 1) * W + min(w, W - 1)];
+        for (int t = tid; t < QW * 4; t += MF_THREADS) {
+            const int r = t >> 2, w = t & 3;
+            mlds[r][w] = mask[(size_t)min(qblk * QW + r, N - 1) * W + min(w, W - 1)];
+        }
         mf_loads_landed();
     }
+    // the lane's row of the block's ancestor rows for its query block qb
+    auto mword = [&](int qb, int i) -> uint64_t { return mlds[qh * 16 * QBW + qb * 16 + lr][i]; };
     // the query block -> LDS: row r is query min(qblk * QW + r, N - 1)
     if constexpr (QLDS) {
 #pragma unroll
@@ -541,79 +540,84 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
         for (int db = 0; db < DB; ++db) o[qb][db] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
 
-    // (One query block per wave.)  Keys kb * 16 .. kb * 16 + 31 of the
-    // wave's share of tile i (stage st): S^T of each 16-key block (the lane
-    // holds keys 4 lk .. 4 lk + 3 of both blocks), the mask, the reference,
-    // then O^T += V^T . P^T with the lane's 8 keys of the pair as one 32-deep
-    // contraction, once over the probabilities' bf16 heads and once over
-    // their bf16 remainders (17 significant bits together); A = those 8 keys'
-    // V^T values, 4 from each block's transposing read, so no register is
-    // copied to build it.
+    // Keys kb * 16 .. kb * 16 + 31 of the wave's share of tile i (stage st):
+    // S^T of each 16-key block (the lane holds keys 4 lk .. 4 lk + 3 of both
+    // blocks), the mask, the reference, then O^T += V^T . P^T with the lane's
+    // 8 keys of the pair as one 32-deep contraction, once over the
+    // probabilities' bf16 heads and once over their bf16 remainders (17
+    // significant bits together); A = those 8 keys' V^T values, 4 from each
+    // block's transposing read, so no register is copied to build it.
     auto key_pair = [&](auto masked_tag, const char* st, int i, int kb) {
         constexpr bool MASKED = decltype(masked_tag)::value;
         static_assert(NKB % 2 == 0, "16-key blocks are taken in pairs");
-        f32x4 sc[2];
+        f32x4 sc[QBW][2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             u32x4 ka[DK];
 #pragma unroll
             for (int ks = 0; ks < DK; ++ks) ka[ks] = *(const u32x4*)(st + koff[ks] + (kb + h) * 16 * ROWB);
-            f32x4 a = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < DK; ++ks)
-                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[ks]),
-                                                            __builtin_bit_cast(bf16x8, qf[0][ks]), a, 0, 0, 0);
-            sc[h] = a;
+            for (int qb = 0; qb < QBW; ++qb) {
+                f32x4 a = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < DK; ++ks)
+                    a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[ks]),
+                                                                __builtin_bit_cast(bf16x8, qf[qb][ks]), a, 0, 0, 0);
+                sc[qb][h] = a;
+            }
         }
         const int kk0 = kq * KW + kb * 16 + lk * 4;  // the lane's first key of block kb (block kb + 1: 16 on)
-        if constexpr (MASKED) {
-            // keys past the range; in the tree range, non-ancestors
-            const uint64_t word = !tree ? ~0ull : i == 0 ? mrow[0][0] : i == 1 ? mrow[0][1]
-                                               : i == 2 ? mrow[0][2] : mrow[0][3];
+        u32x4 ph[QBW], pr[QBW];  // the probabilities' bf16 heads and remainders
+#pragma unroll
+        for (int qb = 0; qb < QBW; ++qb) {
+            if constexpr (MASKED) {
+                // keys past the range; in the tree range, non-ancestors
+                const uint64_t word = !tree ? ~0ull : mword(qb, i);
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int kk = kk0 + h * 16 + r;
+                        const bool vis = i * TK + kk < nkeys && ((word >> kk) & 1ull);
+                        sc[qb][h][r] = vis ? sc[qb][h][r] : -INFINITY;
+                    }
+            }
+            const float lm = fmaxf(fmaxf(fmaxf(sc[qb][0][0], sc[qb][0][1]), fmaxf(sc[qb][0][2], sc[qb][0][3])),
+                                   fmaxf(fmaxf(sc[qb][1][0], sc[qb][1][1]), fmaxf(sc[qb][1][2], sc[qb][1][3])));
+            if (__any(lm * scale_log2 > Mq[qb] + MF_LAZY)) {
+                // raise the reference of the queries that need it (the pair's
+                // max over the query's 4 lanes decides, so they agree)
+                float t = fmaxf(lm, __shfl_xor(lm, 16, 64));
+                t = fmaxf(t, __shfl_xor(t, 32, 64));
+                const float tc = t * scale_log2;
+                const float Mn = tc > Mq[qb] + MF_LAZY ? tc : Mq[qb];
+                const float alpha = __builtin_amdgcn_exp2f(Mq[qb] - Mn);  // exactly 1 when unchanged
+                Mq[qb] = Mn;
+                l[qb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
+            }
+            // probabilities (bare v_exp_f32: arguments <= 8, masked ones
+            // -inf); k-slots 4 h .. 4 h + 3 of the lane's B fragments are
+            // keys 4 lk .. 4 lk + 3 of block kb + h
+            const float nm = -Mq[qb];
+            float pv[8];
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int kk = kk0 + h * 16 + r;
-                    const bool vis = i * TK + kk < nkeys && ((word >> kk) & 1ull);
-                    sc[h][r] = vis ? sc[h][r] : -INFINITY;
+                    pv[h * 4 + r] = __builtin_amdgcn_exp2f(fmaf(sc[qb][h][r], scale_log2, nm));
+                    l[qb] += pv[h * 4 + r];
                 }
-        }
-        const float lm = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                               fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-        if (__any(lm * scale_log2 > Mq[0] + MF_LAZY)) {
-            // raise the reference of the queries that need it (the pair's max
-            // over the query's 4 lanes decides, so they agree)
-            float t = fmaxf(lm, __shfl_xor(lm, 16, 64));
-            t = fmaxf(t, __shfl_xor(t, 32, 64));
-            const float tc = t * scale_log2;
-            const float Mn = tc > Mq[0] + MF_LAZY ? tc : Mq[0];
-            const float alpha = __builtin_amdgcn_exp2f(Mq[0] - Mn);  // exactly 1 when unchanged
-            Mq[0] = Mn;
-            l[0] *= alpha;
+            uint32_t hw[4], rw[4];
 #pragma unroll
-            for (int db = 0; db < DB; ++db) o[0][db] *= alpha;
-        }
-        // probabilities (bare v_exp_f32: arguments <= 8, masked ones -inf);
-        // k-slots 4 h .. 4 h + 3 of the lane's B fragments are keys
-        // 4 lk .. 4 lk + 3 of block kb + h
-        const float nm = -Mq[0];
-        float pv[8];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                pv[h * 4 + r] = __builtin_amdgcn_exp2f(fmaf(sc[h][r], scale_log2, nm));
-                l[0] += pv[h * 4 + r];
+            for (int w = 0; w < 4; ++w) {
+                hw[w] = pack_bf16x2(pv[2 * w], pv[2 * w + 1]);
+                rw[w] = pack_bf16x2(pv[2 * w] - bf16_lo(hw[w]), pv[2 * w + 1] - bf16_hi(hw[w]));
             }
-        uint32_t hw[4], rw[4];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            hw[w] = pack_bf16x2(pv[2 * w], pv[2 * w + 1]);
-            rw[w] = pack_bf16x2(pv[2 * w] - bf16_lo(hw[w]), pv[2 * w + 1] - bf16_hi(hw[w]));
+            ph[qb] = (u32x4){hw[0], hw[1], hw[2], hw[3]};
+            pr[qb] = (u32x4){rw[0], rw[1], rw[2], rw[3]};
         }
-        const u32x4 ph = (u32x4){hw[0], hw[1], hw[2], hw[3]};
-        const u32x4 pr = (u32x4){rw[0], rw[1], rw[2], rw[3]};
         // rows past the prefix in the last tile of a prefix range hold
         // whatever the cache slots hold (they were requested before the
         // prefix length was known): their probability is 0, but 0 times a
@@ -642,10 +646,16 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
                 v1.y &= keep[1][1];
             }
             const u32x4 va = (u32x4){v0.x, v0.y, v1.x, v1.y};
-            o[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va),
-                                                               __builtin_bit_cast(bf16x8, ph), o[0][db], 0, 0, 0);
-            o[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va),
-                                                               __builtin_bit_cast(bf16x8, pr), o[0][db], 0, 0, 0);
+#pragma unroll
+            for (int qb = 0; qb < QBW; ++qb)
+                o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va),
+                                                                    __builtin_bit_cast(bf16x8, ph[qb]), o[qb][db], 0,
+                                                                    0, 0);
+#pragma unroll
+            for (int qb = 0; qb < QBW; ++qb)
+                o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va),
+                                                                    __builtin_bit_cast(bf16x8, pr[qb]), o[qb][db], 0,
+                                                                    0, 0);
         }
     };
 
@@ -703,8 +713,7 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
                                                                          0, 0);
                         // mask: keys past the range; in the tree range, non-ancestors
                         if (masked) {
-                            const uint64_t word = !tree ? ~0ull : i == 0 ? mrow[qb][0] : i == 1 ? mrow[qb][1]
-                                                                           : i == 2 ? mrow[qb][2] : mrow[qb][3];
+                            const uint64_t word = !tree ? ~0ull : mword(qb, i);
 #pragma unroll
                             for (int r = 0; r < 4; ++r) {
                                 const bool vis = i * TK + kk0 + r < nkeys && ((word >> (kk0 + r)) & 1ull);
