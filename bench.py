@@ -38,11 +38,11 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 # calibration (profiles/medusa_step_hbm_counters__vicuna7b_sparse64.txt).
 # Valid only for the kernel sources they were taken on (sha256 prefix of
 # heads.hip + common.hpp); reported as null after any change to them.
-VOCAB_TRAFFIC = {"sources_sha256_16": "f7831c55680f463e", "read_bytes": 1311544807, "write_bytes": 128034}
+VOCAB_TRAFFIC = {"sources_sha256_16": "f96627411038c3da", "read_bytes": 1311534503, "write_bytes": 128013}
 # the same for the gate|up projection of the 32-layer workload (one layer's
 # launch: 64 x 4096 node rows against 22016 packed weight rows, unsplit, the
 # SwiGLU product written in bf16)
-GATE_UP_TRAFFIC = {"sources_sha256_16": "e5edf799b48dc441", "read_bytes": 185348838, "write_bytes": 1409024}
+GATE_UP_TRAFFIC = {"sources_sha256_16": "47fc8fa70a26af65", "read_bytes": 185387324, "write_bytes": 1409024}
 
 
 def _traffic_bytes(rec, sources):
