@@ -353,6 +353,18 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def _cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, heads, att, root):
     """The float64 oracle on the host cores, on a bounded sample of the same
     step, scaled to steps/s: one of the K heads (x K), 4 of the attention
@@ -416,7 +428,7 @@ def cpu_baseline(cfg, heads, att, root):
             "stage_s": {k: round(v, 3) for k, v in t.items()},
             "heads_stage_single_thread": {"s": round(heads_1t, 3), "cores": 1, "scaled": False,
                                           "what": f"all {cfg.K} heads: widening, residual-SiLU, projection, top-k"},
-            "host_cpus": len(os.sched_getaffinity(0))}
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": _cpu_model()}
 
 
 def bench_decoder(args, cfg):
@@ -1017,7 +1029,8 @@ def cpu_baseline_decoder(cfg, heads):
             "sample": f"float64 NumPy oracle: 1 of {cfg.K} heads; one full-width decoder layer (4 of {cfg.nH} "
                       f"attention heads exact) scaled to {cfg.layers} layers; 8 of {cfg.B * cfg.N} lm_head rows; "
                       "each part timed and scaled linearly",
-            "stage_s": {k: round(v, 3) for k, v in t.items()}, "host_cpus": len(os.sched_getaffinity(0))}
+            "stage_s": {k: round(v, 3) for k, v in t.items()}, "host_cpus": len(os.sched_getaffinity(0)),
+            "cpu_model": _cpu_model()}
 
 
 if __name__ == "__main__":
