@@ -8,11 +8,14 @@
 // vocabulary gives 250 8-wave workgroups).  RMSNorm with unit weight is a
 // positive factor per row, so the product runs on the bf16 rows x themselves
 // and the argmax is that of lm_head . x; the factor is applied only to the
-// logits when they are asked for.  Each workgroup writes, per node, its best
-// (value, index); a merge kernel reduces them.
+// logits when they are asked for.  A 256-row node tile over a vocabulary too
+// small to give that product 256 workgroups runs instead on the 32 x 32 x 16
+// kernel with loader waves of lm_head_wide.hpp.  Each workgroup writes, per
+// node, its best (value, index); a merge kernel reduces them.
 // Row-major lm_head (float32 or bf16): the vector-ALU GEMV of the heads on the
 // float32 normalised rows, one pass per 8 rows.
 #include "common.hpp"
+#include "lm_head_wide.hpp"
 #include "skinny_mfma.hpp"
 
 namespace medusa {
@@ -112,13 +115,31 @@ static int lmh_groups(int R, int V) {
     return (V + rows - 1) / rows;
 }
 
+// Node tiles that would split their node blocks (too few workgroups), without
+// logits: the 32 x 32 x 16 kernel of lm_head_wide.hpp with loader waves
+// (ring depth LMW_D chunks), 92 us against 99 us at 256 x 4096 x 32000.
+constexpr int LMW_D = 4;
+static bool lmw_use(int R, int H, int V, bool logits) {
+    return lmh_nblk(R) == 16 && lmh_shape(R, V).ns == 2 && !logits && H % LMW_KC == 0;
+}
+
 size_t lm_head_greedy_workspace_bytes(int R, int H, int V) {
+    const int G = lmh_groups(R, V) > lmw_groups(V) ? lmh_groups(R, V) : lmw_groups(V);
     (void)H;
-    return a256((size_t)R * lmh_groups(R, V) * 4) * 2;
+    return a256((size_t)R * G * 4) * 2;
 }
 
 void launch_lm_head_greedy(const bf16_t* n, const bf16_t* lm_head, int R, int H, int V, int32_t* greedy,
                            float* logits, float rs_eps, void* ws, hipStream_t s) {
+    if (lmw_use(R, H, V, logits != nullptr)) {
+        const int G = lmw_groups(V), T = lmw_tiles(R);
+        float* cv = (float*)ws;
+        int* ci = (int*)((char*)ws + a256((size_t)R * G * 4));
+        MEDUSA_LAUNCH("lm_head_argmax", lm_head_argmax_wide_kernel<LMW_D>, dim3((G + 7) / 8 * 8 * T), dim3(512), 0, s, n,
+                      lm_head, R, H, V, T, G, cv, ci);
+        MEDUSA_LAUNCH("argmax_merge", argmax_merge_kernel, dim3(R), dim3(64), 0, s, cv, ci, G, greedy);
+        return;
+    }
     const int G = lmh_groups(R, V);
     float* cv = (float*)ws;
     int* ci = (int*)((char*)ws + a256((size_t)R * G * 4));

@@ -1,0 +1,232 @@
+// Wide-tree lm_head argmax for one 256-row node tile and a vocabulary too
+// small to give the skinny product enough workgroups: the node rows against
+// the packed bf16 lm_head on v_mfma_f32_32x32x16_bf16, the argmax over the
+// workgroup's weight rows fused into the epilogue.  The per-workgroup
+// candidates have the layout of skinny_mfma_kernel's argmax epilogue
+// ([R][G]) and go to the same merge.
+//
+// Workgroup: 128 weight rows against one 256-row node tile, 8 waves in two
+// roles.  Waves 0-3 (one per SIMD) are matrix waves: wave w owns weight rows
+// 32 w .. +31 against all 256 node rows (8 accumulator tiles of 32 x 32) and
+// reads both operands from LDS -- it issues no global load, so no product
+// ever waits behind a weight fragment still on its way from HBM.  Waves 4-7
+// are loader waves: they stream each 64-wide k-chunk's weight pieces and
+// node rows into register rings D chunks ahead and publish chunk c + 1 into
+// the idle one of two LDS stages while the matrix waves work on chunk c (one
+// barrier per chunk for all 8 waves).
+//
+// Operands (lane l of a matrix wave, k-step s of 16 within a chunk):
+//   A, weights: row l % 32 of the wave's 32, k = 16 s + 8 (l / 32) .. +7 --
+//     in the packed fragment order one 16-byte piece of the fragment of
+//     16-row block 2 (32-row block) + (l % 32) / 16; LDS keeps the pieces in
+//     lane order, [stage][wave][s][lane], so the matrix waves read them
+//     linearly.
+//   B, nodes: node row 32 t + l % 32, the same k, from the LDS node tile.
+//   D: element r of lane l is weight row 8 (r / 4) + 4 (l / 32) + r % 4,
+//     node l % 32 of tile t.
+// LDS node tile: 128-byte rows without padding, 16-byte column c of row r at
+// c ^ ((r >> 1) & 7): measured with the LDS bank-conflict counter on gfx950,
+// both the B-fragment reads (32 rows x 2 columns a wave) and the staging
+// writes (8 rows x 8 columns a wave) are then conflict-free.
+// The last k-step of every chunk has its node fragments read before the
+// chunk's barrier and its products issued after it, so the matrix pipe has
+// 8 products queued while the waves meet.
+//
+// Measured (256 x 4096 x 32000, random bf16 data): 92 us against 99 us for
+// the 8-wave 16 x 16 x 32 node-split product.  The loader waves alone take
+// 85 us: the bound is the CU's vector-memory path, which carries 3 MB per
+// workgroup (its 1 MB of weights from HBM and the 2 MB node tile from L2) at
+// about 45 GB/s; the products alone take 65 us (random bf16 operands keep
+// the matrix cores at about 1.4 PFLOP/s, well under the constant-data rate).
+// With two node tiles and enough workgroups the 256-row skinny tile, which
+// stages each node row for twice the weight rows, stays faster.
+//
+// Grid: ceil(G / 8) * 8 * T workgroups for G = ceil(V / 128) row tiles and T
+// node tiles.  Workgroup L runs on XCD L % 8 (round-robin dispatch); the T
+// node tiles of one row tile are consecutive workgroups of one XCD, so they
+// run together and the second reads the weights from that XCD's L2.
+#pragma once
+
+#include "common.hpp"
+#include "skinny_mfma.hpp"
+
+namespace medusa {
+
+constexpr int LMW_NODES = 256;  // node rows per tile
+constexpr int LMW_ROWS = 128;   // weight rows per workgroup
+constexpr int LMW_KC = 64;      // contraction elements per chunk
+
+inline int lmw_groups(int V) { return (V + LMW_ROWS - 1) / LMW_ROWS; }
+inline int lmw_tiles(int R) { return (R + LMW_NODES - 1) / LMW_NODES; }
+
+template <int D>
+__global__ __launch_bounds__(512) void lm_head_argmax_wide_kernel(const bf16_t* __restrict__ n,   // [R][K]
+                                                                  const bf16_t* __restrict__ Wp,  // packed [V][K]
+                                                                  int R, int K, int V, int T, int G,
+                                                                  float* __restrict__ cand_val,  // [R][G]
+                                                                  int* __restrict__ cand_idx) {
+    constexpr int KC = LMW_KC;
+    constexpr int KS = KC / 16;                   // 32 x 32 x 16 k-steps per chunk
+    constexpr int NTL = LMW_NODES / 32;           // accumulator tiles per matrix wave
+    constexpr int NPL = LMW_NODES * (KC / 8) / 256;  // node pieces per loader thread per chunk
+    constexpr int APL = 4 * KS * 64 / 256;           // weight pieces per loader thread per chunk
+    static_assert(KC == 64 && NPL == 8 && APL == 4, "the swizzle and the loader split assume 64-wide chunks");
+    __shared__ __attribute__((aligned(16))) bf16_t ns[2][LMW_NODES][KC];  // node tile, swizzled columns
+    __shared__ u32x4 as[2][4][KS][64];  // weight pieces in the lane order of the A operand
+    __shared__ float red_v[4][LMW_NODES];
+    __shared__ int red_i[4][LMW_NODES];
+
+    const int L = blockIdx.x, j = L >> 3;
+    const int y = j % T, x = (j / T) * 8 + (L & 7);  // node tile, row tile
+    if (x >= G) return;                               // padding of the grid to whole XCD rounds
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int node0 = y * LMW_NODES;
+    const int nrb = (V + PACK_ROWS - 1) / PACK_ROWS;
+    const int nchunk = K / KC;  // host guarantees K % KC == 0
+
+    if (wave >= 4) {
+        // ---- loader waves: chunk j's weight and node pieces into registers
+        // D chunks ahead, published into LDS stage j & 1 one step before use
+        const int lt = tid - 256;
+        // weight pieces e = 0..3: matrix wave e, k-step s = lt / 64, lane l = lt % 64
+        const int s = lt >> 6, l = lt & 63;
+        const bf16_t* wa[APL];
+#pragma unroll
+        for (int e = 0; e < APL; ++e) {
+            const int pb = min((x * 4 + e) * 2 + ((l & 31) >> 4), nrb - 1);  // past the end: clamped, discarded
+            wa[e] = Wp + ((size_t)(s >> 1) * nrb + pb) * PACK_FRAG + ((2 * (s & 1) + (l >> 5)) * PACK_ROWS + (l & 15)) * 8;
+        }
+        const size_t cstride = (size_t)(KC / 32) * nrb * PACK_FRAG;  // one chunk of the packed matrix
+        // node pieces e = 0..7: row (lt >> 3) + 32 e, 16-byte column lt & 7 (the
+        // swizzle term (row >> 1) & 7 is the same for every e)
+        const int col = lt & 7, row0 = lt >> 3;
+        const int wcol = (col ^ ((row0 >> 1) & 7)) * 8;
+        const bf16_t* nrow[NPL];
+#pragma unroll
+        for (int e = 0; e < NPL; ++e) nrow[e] = n + (size_t)min(node0 + row0 + 32 * e, R - 1) * K + col * 8;
+
+        u32x4 nr[D][NPL], ar[D][APL];
+        auto load = [&](int slot, int c) {
+            c = min(c, nchunk - 1);  // past the end: the last chunk again, never published
+#pragma unroll
+            for (int e = 0; e < NPL; ++e) nr[slot][e] = *(const u32x4*)(nrow[e] + (size_t)c * KC);
+#pragma unroll
+            for (int e = 0; e < APL; ++e) ar[slot][e] = ld_stream(wa[e] + (size_t)c * cstride);
+        };
+        auto publish = [&](int slot, int st) {
+#pragma unroll
+            for (int e = 0; e < NPL; ++e) *(u32x4*)(&ns[st][row0 + 32 * e][wcol]) = nr[slot][e];
+#pragma unroll
+            for (int e = 0; e < APL; ++e) as[st][e][s][l] = ar[slot][e];
+        };
+#pragma unroll
+        for (int u = 0; u < D; ++u) load(u, u);
+        publish(0, 0);
+        load(0, D);
+        __syncthreads();
+        // step c: chunk c + 1 into the idle stage (last read before the previous
+        // barrier), then chunk c + 1 + D into the freed slot
+        for (int c0 = 0; c0 < nchunk; c0 += D) {
+#pragma unroll
+            for (int u = 0; u < D; ++u) {
+                const int c = c0 + u;
+                if (c < nchunk) {
+                    publish((u + 1) % D, (c + 1) & 1);
+                    load((u + 1) % D, c + 1 + D);
+                    __syncthreads();
+                }
+            }
+        }
+    } else {
+        // ---- matrix waves: wave w owns weight rows 32 w .. +31 of the workgroup
+        const int l32 = lane & 31, hi = lane >> 5;
+        const int rsw = (l32 >> 1) & 7;  // swizzle of this lane's B-fragment row
+        f32x16 acc[NTL];
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) acc[t] = (f32x16){};
+        auto read_b = [&](int st, int s, int t) {
+            return __builtin_bit_cast(bf16x8, *(const u32x4*)(&ns[st][t * 32 + l32][((2 * s + hi) ^ rsw) * 8]));
+        };
+        auto read_a = [&](int st, int s) { return __builtin_bit_cast(bf16x8, as[st][wave][s][lane]); };
+        auto mfma = [&](bf16x8 a, bf16x8 b, f32x16& d) {
+            d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, d, 0, 0, 0);
+        };
+        // the previous chunk's last k-step (zeros before the first chunk): its
+        // products are issued after the barrier that ends the chunk, so the
+        // matrix pipe has 8 products queued while the waves meet
+        bf16x8 bl[NTL], al = (bf16x8){};
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) bl[t] = (bf16x8){};
+        __syncthreads();
+        // scheduling fences keep every phase in place: the operands of a k-step
+        // are read one whole k-step (8 products) before their use
+        for (int c = 0; c < nchunk; ++c) {
+            const int st = c & 1;
+            bf16x8 bc[NTL], ac = read_a(st, 0);
+#pragma unroll
+            for (int t = 0; t < NTL; ++t) bc[t] = read_b(st, 0, t);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < NTL; ++t) mfma(al, bl[t], acc[t]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                if (s + 1 < KS) {
+                    bf16x8 bn[NTL], an = read_a(st, s + 1);
+#pragma unroll
+                    for (int t = 0; t < NTL; ++t) bn[t] = read_b(st, s + 1, t);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int t = 0; t < NTL; ++t) mfma(ac, bc[t], acc[t]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    ac = an;
+#pragma unroll
+                    for (int t = 0; t < NTL; ++t) bc[t] = bn[t];
+                } else {
+                    al = ac;
+#pragma unroll
+                    for (int t = 0; t < NTL; ++t) bl[t] = bc[t];
+                }
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) mfma(al, bl[t], acc[t]);
+
+        // best (value, lower index) per node over the wave's 32 rows, then over
+        // the lane pair l, l ^ 32
+        const int vw = (x * 4 + wave) * 32;
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) {
+            float bv = -INFINITY;
+            int bi = 0x7FFFFFFF;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int v = vw + 8 * (r >> 2) + 4 * hi + (r & 3);
+                const float sc = acc[t][r];
+                if (v < V && better(sc, v, bv, bi)) { bv = sc; bi = v; }
+            }
+            const float ov = __shfl_xor(bv, 32, 64);
+            const int oi = __shfl_xor(bi, 32, 64);
+            if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+            if (hi == 0) { red_v[wave][t * 32 + l32] = bv; red_i[wave][t * 32 + l32] = bi; }
+        }
+    }
+    __syncthreads();
+    // over the 4 matrix waves: one node per thread of the first 256
+    if (tid < LMW_NODES) {
+        float bv = red_v[0][tid];
+        int bi = red_i[0][tid];
+#pragma unroll
+        for (int w = 1; w < 4; ++w)
+            if (better(red_v[w][tid], red_i[w][tid], bv, bi)) { bv = red_v[w][tid]; bi = red_i[w][tid]; }
+        const int node = node0 + tid;
+        if (node < R) {
+            cand_val[(size_t)node * G + x] = bv;
+            cand_idx[(size_t)node * G + x] = bi;
+        }
+    }
+}
+
+}  // namespace medusa

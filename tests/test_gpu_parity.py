@@ -224,6 +224,37 @@ def test_base_greedy_parity(M, name, dtype, R, H, V, layout):
     assert np.array_equal(g.cpu().numpy(), g_ref)
 
 
+# Trees of more than 128 nodes without logits over a vocabulary too small to
+# give the skinny product 256 workgroups take the 32 x 32 x 16 product with
+# loader waves (256-node tiles, 128 weight rows a workgroup, 64-wide k-chunks,
+# loader rings four chunks deep): one chunk, two, three, a whole ring round
+# and two rounds; ragged node tiles, two node tiles, ragged row tiles and a
+# vocabulary under one row tile.
+WIDE_GREEDY_CASES = [
+    ("r129_h64_v200", 129, 64, 200),        # one chunk, 2 row tiles (the second ragged), one node past 128
+    ("r200_h512_v1537", 200, 512, 1537),    # two ring rounds, ragged node tile
+    ("r256_h256_v5000", 256, 256, 5000),    # one ring round, the last chunk on its final slot
+    ("r300_h128_v1000", 300, 128, 1000),    # two node tiles, the second ragged, two chunks
+    ("r512_h1024_v4099", 512, 1024, 4099),  # two full node tiles
+    ("r160_h192_v100", 160, 192, 100),      # three chunks, a vocabulary under one row tile
+]
+
+
+@pytest.mark.parametrize("name,R,H,V", WIDE_GREEDY_CASES, ids=[c[0] for c in WIDE_GREEDY_CASES])
+def test_base_greedy_wide_tree_parity(M, name, R, H, V):
+    _say("base_greedy wide", name)
+    cfg = _cfg("gw", "bf16", 1, H, V, 1, 1, mi.tiny_tree(), seed=700 + R)
+    heads = {"lm_head": mi.normal((V, H), cfg.seed, mi.S_LM_HEAD, 0.02, "bf16")}
+    x = mi.normal((R, H), cfg.seed, mi.S_TEST, 1.0, "bf16")
+    xw = oracle.widen(x, "bf16")
+    enforce_greedy_gap(cfg, heads, xw, [])
+    g_ref, _ = oracle.base_greedy(xw, oracle.widen(heads["lm_head"], "bf16"), 1e-6)
+    g = torch.full((R,), -1, dtype=torch.int32, device="cuda")
+    M.medusa_base_greedy(dev(x), M.pack(dev(heads["lm_head"])), g, eps=1e-6)
+    torch.cuda.synchronize()
+    assert np.array_equal(g.cpu().numpy(), g_ref)
+
+
 def _pack_layout(W):
     """Row r, column k of a [rows][K] matrix of NRB = ceil(rows / 16) row blocks
     -> element ((k // 32) * NRB + r // 16) * 512 + ((k % 32) // 8 * 16 + r % 16) * 8 + k % 8
@@ -526,7 +557,7 @@ def test_topk_ties_keep_lower_index(M, layout, spread):
     assert np.array_equal(got, idx_ref)
 
 
-@pytest.mark.parametrize("R", [64, 256], ids=["r64", "r256"])     # 256: node blocks split over two waves
+@pytest.mark.parametrize("R", [64, 256, 512], ids=["r64", "r256", "r512"])  # 256, 512: 32 x 32 x 16 with loader waves
 @pytest.mark.parametrize("spread", ["near", "mid", "far"])
 @pytest.mark.parametrize("layout", ["rows", "packed"])
 def test_greedy_ties_keep_lower_index(M, layout, spread, R):
