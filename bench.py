@@ -343,6 +343,9 @@ def main():
         "tokens_per_s_under_tree_prior": round(B * prior_tokens * 1000.0 / ms_step, 1),
         "stages_us": {k: round(v, 2) for k, v in st.items()},
         "kernels_us": {k: round(v, 2) for k, v in kern_us.items()},
+        "stages_timing": "second pass, every launch between two HIP events: each time includes its launch's "
+                         "dispatch (about 2 us more than the kernel trace for the short kernels), which the "
+                         "unbracketed step overlaps with the previous kernel, so the stages sum above ms_per_step",
         "wall_ms_per_step": round(1e3 * wall / args.steps, 4),
         "roofline": roofline,
         "hbm_read_ceiling": ceiling,
