@@ -103,6 +103,10 @@ def parse():
     ap.add_argument("--specsample", type=int, default=0, metavar="GAMMA",
                     help="time the speculative-sampling rule alone (8 chains of GAMMA drafts over a "
                          "32000-token vocabulary) and print that line instead")
+    ap.add_argument("--probes", action="store_true",
+                    help="only measure the memory path and the matrix cores (per-CU read rates from an "
+                         "L2-resident window, from HBM and mixed; the wide lm_head's matrix loop on constant "
+                         "and random operands) and print that line instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device-to-device copies of MIB MiB (scale for HBM byte counters)")
     return ap.parse_args()
@@ -150,6 +154,60 @@ def copy_calibration(mib: int):
     print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "copies": 3}), flush=True)
 
 
+def probes():
+    """Per-CU read rates and the matrix loop's rate, one workgroup per CU
+    (256 workgroups), each timed over 5 launches with HIP events.
+
+    Reads: a 2 MiB window every workgroup shares (plain loads: it stays in
+    L2), a private 4 MiB slice of a 1 GiB buffer per workgroup (non-temporal
+    loads from HBM), and 2 : 1 mixes of the two in the same waves with 6 and
+    12 loads in flight per thread (the wide lm_head's node-row to weight
+    bytes).  Matrix loop: 2000 iterations of 32 products of 32 x 32 x 16 per
+    wave with the node fragments read from LDS, constant against random bf16
+    operands."""
+    import torch
+
+    import speculative_decoding_medusa_amd as M
+    n_wg = 256
+    win = torch.empty(2 << 20, dtype=torch.uint8, device="cuda")
+    win.fill_(1)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    src.fill_(2)
+    sink = torch.empty(n_wg, dtype=torch.int32, device="cuda")
+
+    def timed(fn, reps=5):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps  # us per launch
+
+    reads = {}
+    for name, (wp, sp, rounds) in {"l2_window": (8, 0, 256), "hbm_slice": (0, 8, 128),
+                                   "mix_2to1_6_in_flight": (4, 2, 512), "mix_2to1_12_in_flight": (8, 4, 256)}.items():
+        us = timed(lambda: M.medusa_read_mix(win if wp else None, src if sp else None, wp, sp, rounds, sink, n_wg))
+        per_wg = rounds * (wp + sp) * 4096
+        reads[name] = {"us": round(us, 1), "GBs_per_cu": round(per_wg / (us * 1e3), 1),
+                       "TBs_total": round(per_wg * n_wg / (us * 1e6), 2),
+                       "hbm_TBs": round(rounds * sp * 4096 * n_wg / (us * 1e6), 2)}
+    del src, win
+    out = torch.empty(n_wg * 256, device="cuda")
+    iters = 2000
+    flops = n_wg * 4 * iters * 32 * 32768.0
+    mfma = {}
+    for name, rnd in (("constant_operands", False), ("random_operands", True)):
+        us = timed(lambda: M.medusa_mfma_rate(rnd, iters, out, n_wg))
+        mfma[name] = {"us": round(us, 1), "TFLOPs": round(flops / (us * 1e-6) / 1e12, 1),
+                      "ns_per_32_products": round(us * 1e3 / iters, 1)}
+    print(json.dumps({"metric": "memory path and matrix-core probes, one workgroup per CU", "n_wg": n_wg,
+                      "read_ceiling": read_ceiling(), "reads": reads, "mfma_32x32x16_lds_loop": mfma,
+                      "mfma_peak_TFLOPs": 2500.0}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -161,6 +219,9 @@ def main():
     import numpy as np
     import torch
 
+    if args.probes:
+        probes()
+        return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return

@@ -557,6 +557,42 @@ medusa_status medusa_embed(const int32_t* tok, const void* embedding, int R, int
 medusa_status medusa_stream_read(const void* src, size_t bytes, uint32_t* sink, int n_wg, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Measurement aid: the rate at which one workgroup per CU pulls data through
+ * its vector-memory path.  n_wg workgroups of 256 threads run `rounds`
+ * rounds; in each, every thread issues window_parts 16-byte loads of the
+ * shared `window` (plain loads, so the window stays in L2: 4 KB blocks read
+ * consecutively from offset 0, wrapping at window_bytes) and stream_parts
+ * 16-byte non-temporal loads of its workgroup's own slice of `src`
+ * (workgroup g reads bytes [g, g + 1) x rounds x stream_parts x 4096, in
+ * order), then XORs them.  (window_parts, stream_parts) is one of (8, 0)
+ * (window only), (0, 8) (HBM only), (4, 2) and (8, 4) (2 : 1 mixes, the
+ * wide lm_head's ratio of node-row to weight bytes).  sink[g] (uint32) =
+ * the XOR of every word workgroup g loaded.  Pointers of a part that is 0
+ * are not read.  Errors: EINVAL for another pair, rounds or n_wg outside
+ * [1, 2^20] / [1, 2^16], misaligned or null pointers, or src_bytes below
+ * rounds x stream_parts x 4096 x n_wg.
+ * ------------------------------------------------------------------------- */
+medusa_status medusa_read_mix(const void* window, size_t window_bytes, const void* src, size_t src_bytes,
+                              int window_parts, int stream_parts, int rounds, uint32_t* sink, int n_wg,
+                              void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Measurement aid: the matrix-wave loop of the wide lm_head product on its
+ * own.  n_wg workgroups of 4 waves (one per SIMD); each wave keeps 8
+ * independent 32 x 32 x 16 bf16 accumulators and runs `iters` iterations of
+ * 4 k-steps, each reading the 8 node fragments of the next k-step from a
+ * 64 KB LDS tile (the lm_head's swizzled layout) while the current 8
+ * products run, and one workgroup barrier per iteration: 32 products (1 MFLOP
+ * a wave) per iteration.  random_operands = 0: every operand element is 1.0,
+ * so out[g * 256 + t] = iters x 64 x 128 exactly; 1: bf16 values of random
+ * sign and magnitude in [0.25, 2) (the data-dependent power of real
+ * operands).  out: n_wg x 256 floats, the sum of each thread's accumulator
+ * elements.  Errors: EINVAL for random_operands not 0 / 1, iters outside
+ * [1, 2^20], n_wg outside [1, 2^16] or a null out.
+ * ------------------------------------------------------------------------- */
+medusa_status medusa_mfma_rate(int random_operands, int iters, float* out, int n_wg, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Kernel timing: while enabled, every kernel launch of the library is
  * bracketed by HIP events on its stream.  medusa_profiler_collect waits for
  * the recorded events and folds them into per-kernel totals and returns their

@@ -77,6 +77,8 @@ _SIGS = {
     "medusa_swiglu": ([_vp, _i32, _i32, _vp, _vp], _i32),
     "medusa_embed": ([_vp, _vp, _i32, _i32, _i32, _vp, _vp], _i32),
     "medusa_stream_read": ([_vp, _sz, _vp, _i32, _vp], _i32),
+    "medusa_read_mix": ([_vp, _sz, _vp, _sz, _i32, _i32, _i32, _vp, _i32, _vp], _i32),
+    "medusa_mfma_rate": ([_i32, _i32, _vp, _i32, _vp], _i32),
     "medusa_profiler_enable": ([_i32], _i32),
     "medusa_profiler_reset": ([], _i32),
     "medusa_profiler_collect": ([], _i32),
@@ -612,6 +614,26 @@ def medusa_stream_read(src, sink, n_wg: int = 16384, stream=None):
     nbytes = src.numel() * src.element_size()
     _check("medusa_stream_read", _lib.medusa_stream_read(_p(src), nbytes, _p(sink), int(n_wg), _stream(stream)))
     return sink
+
+
+def medusa_read_mix(window, src, window_parts: int, stream_parts: int, rounds: int, sink, n_wg: int = 256,
+                    stream=None):
+    """Measurement aid: per-CU read rate from a shared L2-resident window and
+    private HBM slices (see include/medusa.h).  window / src: device tensors
+    (or None where their part is 0); sink: [n_wg] int32 device tensor."""
+    wb = 0 if window is None else window.numel() * window.element_size()
+    sb = 0 if src is None else src.numel() * src.element_size()
+    _check("medusa_read_mix", _lib.medusa_read_mix(_p(window), wb, _p(src), sb, int(window_parts), int(stream_parts),
+                                                   int(rounds), _p(sink), int(n_wg), _stream(stream)))
+    return sink
+
+
+def medusa_mfma_rate(random_operands: bool, iters: int, out, n_wg: int = 256, stream=None):
+    """Measurement aid: the wide lm_head's matrix loop alone (see
+    include/medusa.h); out: [n_wg * 256] float32 device tensor."""
+    _check("medusa_mfma_rate", _lib.medusa_mfma_rate(int(bool(random_operands)), int(iters), _p(out), int(n_wg),
+                                                     _stream(stream)))
+    return out
 
 
 def profiler_enable(on: bool = True):

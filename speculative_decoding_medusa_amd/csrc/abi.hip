@@ -54,6 +54,10 @@ struct LayerPtrs {
     const bf16_t *wqkv, *wo, *w_gate_up, *w_down;
 };
 void launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int n_wg, hipStream_t s);
+bool read_mix_supported(int wp, int sp);
+void launch_read_mix(const void* win, size_t win_bytes, const void* src, int wp, int sp, int rounds, uint32_t* sink,
+                     int n_wg, hipStream_t s);
+void launch_mfma_rate(int random_operands, int iters, float* out, int n_wg, hipStream_t s);
 void launch_plant_greedy(const TreeDev& t, const int32_t* topk_idx, int B, int K, int topk,
                          const int32_t* cache_len, const PlantAlphas& pa, uint64_t seed, int V, int32_t* greedy,
                          hipStream_t s);
@@ -779,6 +783,42 @@ medusa_status medusa_stream_read(const void* src, size_t bytes, uint32_t* sink, 
         REQUIRE(((uintptr_t)src & 15) == 0, "src must be 16-byte aligned");
         REQUIRE(n_wg >= 1 && n_wg <= (1 << 20), "n_wg=%d must be in [1, 2^20]", n_wg);
         launch_stream_read(src, bytes, sink, n_wg, (hipStream_t)stream);
+    });
+}
+
+medusa_status medusa_read_mix(const void* window, size_t window_bytes, const void* src, size_t src_bytes,
+                              int window_parts, int stream_parts, int rounds, uint32_t* sink, int n_wg, void* stream) {
+    return guarded("medusa_read_mix", [&] {
+        REQUIRE(sink, "null pointer argument");
+        REQUIRE(read_mix_supported(window_parts, stream_parts),
+                "(window_parts, stream_parts) = (%d, %d) must be (8, 0), (0, 8), (4, 2) or (8, 4)", window_parts,
+                stream_parts);
+        REQUIRE(rounds >= 1 && rounds <= (1 << 20), "rounds=%d must be in [1, 2^20]", rounds);
+        REQUIRE(n_wg >= 1 && n_wg <= (1 << 16), "n_wg=%d must be in [1, 2^16]", n_wg);
+        if (window_parts > 0) {
+            REQUIRE(window, "null window");
+            REQUIRE(window_bytes >= 16 && window_bytes % 16 == 0, "window_bytes=%zu must be a positive multiple of 16",
+                    window_bytes);
+            REQUIRE(((uintptr_t)window & 15) == 0, "window must be 16-byte aligned");
+        }
+        if (stream_parts > 0) {
+            REQUIRE(src, "null src");
+            REQUIRE(((uintptr_t)src & 15) == 0, "src must be 16-byte aligned");
+            const size_t need = (size_t)rounds * stream_parts * 4096 * n_wg;
+            REQUIRE(src_bytes >= need, "src_bytes=%zu < %zu (rounds x stream_parts x 4096 x n_wg)", src_bytes, need);
+        }
+        launch_read_mix(window, window_bytes, src, window_parts, stream_parts, rounds, sink, n_wg,
+                        (hipStream_t)stream);
+    });
+}
+
+medusa_status medusa_mfma_rate(int random_operands, int iters, float* out, int n_wg, void* stream) {
+    return guarded("medusa_mfma_rate", [&] {
+        REQUIRE(out, "null pointer argument");
+        REQUIRE(random_operands == 0 || random_operands == 1, "random_operands must be 0 or 1");
+        REQUIRE(iters >= 1 && iters <= (1 << 20), "iters=%d must be in [1, 2^20]", iters);
+        REQUIRE(n_wg >= 1 && n_wg <= (1 << 16), "n_wg=%d must be in [1, 2^16]", n_wg);
+        launch_mfma_rate(random_operands, iters, out, n_wg, (hipStream_t)stream);
     });
 }
 

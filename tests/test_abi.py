@@ -237,3 +237,18 @@ def test_loop_refuses_rounds_past_the_cache(M):
     with pytest.raises(ValueError):
         _loop_budget(M, 4096, 4097, 5)   # a start past the bound
     assert _loop_budget(M, 100, 100, 5).rounds_left == 0
+
+
+def test_measurement_aid_argument_errors(M):
+    L = M._lib
+    d = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    st = L.medusa_read_mix(d, 4096, d, 1 << 20, 3, 1, 1, d, 1, None)
+    assert st == M.EINVAL and "window_parts" in L.medusa_last_error().decode()
+    st = L.medusa_read_mix(d, 4096, d, 4096, 0, 8, 1, d, 1, None)      # needs 8 x 4096 bytes of src
+    assert st == M.EINVAL and "src_bytes" in L.medusa_last_error().decode()
+    st = L.medusa_read_mix(ctypes.c_void_p(24), 4096, None, 0, 8, 0, 1, d, 1, None)
+    assert st == M.EINVAL and "aligned" in L.medusa_last_error().decode()
+    st = L.medusa_mfma_rate(2, 10, d, 1, None)
+    assert st == M.EINVAL and "random_operands" in L.medusa_last_error().decode()
+    st = L.medusa_mfma_rate(0, 0, d, 1, None)
+    assert st == M.EINVAL and "iters" in L.medusa_last_error().decode()
