@@ -255,6 +255,28 @@ def test_base_greedy_wide_tree_parity(M, name, R, H, V):
     assert np.array_equal(g.cpu().numpy(), g_ref)
 
 
+def _random_wide_shapes(n, seed=4242):
+    """n seeded (R, H, V): 129-512 node rows, H a multiple of 64 up to 512,
+    ragged vocabularies up to 3000 rows."""
+    r = np.random.default_rng(seed)
+    return [(int(r.integers(129, 513)), 64 * int(r.integers(1, 9)), int(r.integers(100, 3001))) for _ in range(n)]
+
+
+@pytest.mark.parametrize("R,H,V", _random_wide_shapes(10), ids=lambda v: str(v))
+def test_base_greedy_wide_tree_random_shapes(M, R, H, V):
+    _say("base_greedy wide random", R, H, V)
+    cfg = _cfg("gwr", "bf16", 1, H, V, 1, 1, mi.tiny_tree(), seed=900 + R + H + V)
+    heads = {"lm_head": mi.normal((V, H), cfg.seed, mi.S_LM_HEAD, 0.02, "bf16")}
+    x = mi.normal((R, H), cfg.seed, mi.S_TEST, 1.0, "bf16")
+    xw = oracle.widen(x, "bf16")
+    enforce_greedy_gap(cfg, heads, xw, [])
+    g_ref, _ = oracle.base_greedy(xw, oracle.widen(heads["lm_head"], "bf16"), 1e-6)
+    g = torch.full((R,), -1, dtype=torch.int32, device="cuda")
+    M.medusa_base_greedy(dev(x), M.pack(dev(heads["lm_head"])), g, eps=1e-6)
+    torch.cuda.synchronize()
+    assert np.array_equal(g.cpu().numpy(), g_ref)
+
+
 def _pack_layout(W):
     """Row r, column k of a [rows][K] matrix of NRB = ceil(rows / 16) row blocks
     -> element ((k // 32) * NRB + r // 16) * 512 + ((k % 32) // 8 * 16 + r % 16) * 8 + k % 8
