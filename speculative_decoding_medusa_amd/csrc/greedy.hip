@@ -117,8 +117,9 @@ static int lmh_groups(int R, int V) {
 
 // Node tiles that would split their node blocks (too few workgroups), without
 // logits: the 32 x 32 x 16 kernel of lm_head_wide.hpp with loader waves
-// (ring depth LMW_D chunks), 92 us against 99 us at 256 x 4096 x 32000.
-constexpr int LMW_D = 4;
+// (register ring LMW_D chunks deep: measured at 256 x 4096 x 32000, 79 us
+// with 1, 82 with 2, 85 with 4, against 90 for the 16 x 16 x 32 product).
+constexpr int LMW_D = 1;
 static bool lmw_use(int R, int H, int V, bool logits) {
     return lmh_nblk(R) == 16 && lmh_shape(R, V).ns == 2 && !logits && H % LMW_KC == 0;
 }

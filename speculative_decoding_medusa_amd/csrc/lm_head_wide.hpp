@@ -6,21 +6,26 @@
 // ([R][G]) and go to the same merge.
 //
 // Workgroup: 128 weight rows against one 256-row node tile, 8 waves in two
-// roles.  Waves 0-3 (one per SIMD) are matrix waves: wave w owns weight rows
-// 32 w .. +31 against all 256 node rows (8 accumulator tiles of 32 x 32) and
-// reads both operands from LDS -- it issues no global load, so no product
-// ever waits behind a weight fragment still on its way from HBM.  Waves 4-7
-// are loader waves: they stream each 64-wide k-chunk's weight pieces and
-// node rows into register rings D chunks ahead and publish chunk c + 1 into
-// the idle one of two LDS stages while the matrix waves work on chunk c (one
-// barrier per chunk for all 8 waves).
+// roles.  Waves 0-3 (one per SIMD) are matrix waves: wave w owns the 32-row
+// weight blocks 2 (w / 2) and 2 (w / 2) + 1 against node rows 128 (w % 2) ..
+// + 127 (2 x 4 accumulator tiles of 32 x 32), so every k-step reads 2 weight
+// and 4 node fragments from LDS for 8 products (with one weight block
+// against all 256 nodes it read 1 + 8: LDS time was the tighter bound).
+// They issue no global load, so no product ever waits behind a weight
+// fragment still on its way from HBM.  Waves 4-7 are loader waves: they
+// stream each 64-wide k-chunk's weight pieces and node rows into a register
+// ring D chunks deep and publish chunk c + 1 into the idle one of two LDS
+// stages while the matrix waves work on chunk c (one barrier per chunk for
+// all 8 waves).  One chunk ahead measured fastest: 79 us against 82 with two
+// and 85 with four at 256 x 4096 x 32000 (each workgroup then keeps about
+// 48 KB of loads in flight instead of up to 192 KB).
 //
 // Operands (lane l of a matrix wave, k-step s of 16 within a chunk):
-//   A, weights: row l % 32 of the wave's 32, k = 16 s + 8 (l / 32) .. +7 --
+//   A, weights: row l % 32 of a 32-row block, k = 16 s + 8 (l / 32) .. +7 --
 //     in the packed fragment order one 16-byte piece of the fragment of
 //     16-row block 2 (32-row block) + (l % 32) / 16; LDS keeps the pieces in
-//     lane order, [stage][wave][s][lane], so the matrix waves read them
-//     linearly.
+//     lane order, [stage][32-row block][s][lane], so the matrix waves read
+//     them linearly.
 //   B, nodes: node row 32 t + l % 32, the same k, from the LDS node tile.
 //   D: element r of lane l is weight row 8 (r / 4) + 4 (l / 32) + r % 4,
 //     node l % 32 of tile t.
@@ -28,18 +33,19 @@
 // c ^ ((r >> 1) & 7): measured with the LDS bank-conflict counter on gfx950,
 // both the B-fragment reads (32 rows x 2 columns a wave) and the staging
 // writes (8 rows x 8 columns a wave) are then conflict-free.
-// The last k-step of every chunk has its node fragments read before the
-// chunk's barrier and its products issued after it, so the matrix pipe has
-// 8 products queued while the waves meet.
+// The last k-step of every chunk has its operands read before the chunk's
+// barrier and its products issued after it, so the matrix pipe has 8
+// products queued while the waves meet.
 //
-// Measured (256 x 4096 x 32000, random bf16 data): 92 us against 99 us for
-// the 8-wave 16 x 16 x 32 node-split product.  The loader waves alone take
-// 85 us: the bound is the CU's vector-memory path, which carries 3 MB per
-// workgroup (its 1 MB of weights from HBM and the 2 MB node tile from L2) at
-// about 45 GB/s; the products alone take 65 us (random bf16 operands keep
-// the matrix cores at about 1.4 PFLOP/s, well under the constant-data rate).
-// With two node tiles and enough workgroups the 256-row skinny tile, which
-// stages each node row for twice the weight rows, stays faster.
+// Measured (256 x 4096 x 32000, random bf16 data): 79 us against 90 us for
+// the 8-wave 16 x 16 x 32 node-split product.  Each workgroup carries 3 MB
+// through its CU's vector-memory path (its 1 MB of weights from HBM, the
+// 2 MB node tile from L2) and its LDS carries 96 KB of operand reads and
+// 48 KB of loader writes per chunk; the products alone take 65 us (random
+// bf16 operands keep the matrix cores at about 1.4 PFLOP/s, well under the
+// constant-data rate).  With two node tiles and enough workgroups the
+// 256-row skinny tile, which stages each node row for twice the weight rows,
+// stays faster.
 //
 // Grid: ceil(G / 8) * 8 * T workgroups for G = ceil(V / 128) row tiles and T
 // node tiles.  Workgroup L runs on XCD L % 8 (round-robin dispatch); the T
@@ -73,8 +79,8 @@ __global__ __launch_bounds__(512) void lm_head_argmax_wide_kernel(const bf16_t* 
     static_assert(KC == 64 && NPL == 8 && APL == 4, "the swizzle and the loader split assume 64-wide chunks");
     __shared__ __attribute__((aligned(16))) bf16_t ns[2][LMW_NODES][KC];  // node tile, swizzled columns
     __shared__ u32x4 as[2][4][KS][64];  // weight pieces in the lane order of the A operand
-    __shared__ float red_v[4][LMW_NODES];
-    __shared__ int red_i[4][LMW_NODES];
+    __shared__ float red_v[2][LMW_NODES];  // per row group of the matrix waves
+    __shared__ int red_i[2][LMW_NODES];
 
     const int L = blockIdx.x, j = L >> 3;
     const int y = j % T, x = (j / T) * 8 + (L & 7);  // node tile, row tile
@@ -139,88 +145,110 @@ __global__ __launch_bounds__(512) void lm_head_argmax_wide_kernel(const bf16_t* 
             }
         }
     } else {
-        // ---- matrix waves: wave w owns weight rows 32 w .. +31 of the workgroup
+        // ---- matrix waves: wave w owns the workgroup's 32-row weight blocks
+        // 2 (w / 2) and 2 (w / 2) + 1 against its 32-node tiles 4 (w % 2) .. + 3
+        constexpr int WB = 2;         // 32-row weight blocks per matrix wave
+        constexpr int WT = NTL / 2;   // 32-node tiles per matrix wave
+        const int rg = wave >> 1, nh = wave & 1;
         const int l32 = lane & 31, hi = lane >> 5;
         const int rsw = (l32 >> 1) & 7;  // swizzle of this lane's B-fragment row
-        f32x16 acc[NTL];
+        f32x16 acc[WB * WT];             // weight block j, node tile t: acc[j * WT + t]
 #pragma unroll
-        for (int t = 0; t < NTL; ++t) acc[t] = (f32x16){};
+        for (int t = 0; t < WB * WT; ++t) acc[t] = (f32x16){};
         auto read_b = [&](int st, int s, int t) {
-            return __builtin_bit_cast(bf16x8, *(const u32x4*)(&ns[st][t * 32 + l32][((2 * s + hi) ^ rsw) * 8]));
+            return __builtin_bit_cast(bf16x8,
+                                      *(const u32x4*)(&ns[st][(nh * WT + t) * 32 + l32][((2 * s + hi) ^ rsw) * 8]));
         };
-        auto read_a = [&](int st, int s) { return __builtin_bit_cast(bf16x8, as[st][wave][s][lane]); };
+        auto read_a = [&](int st, int s, int j) { return __builtin_bit_cast(bf16x8, as[st][2 * rg + j][s][lane]); };
         auto mfma = [&](bf16x8 a, bf16x8 b, f32x16& d) {
             d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, d, 0, 0, 0);
         };
         // the previous chunk's last k-step (zeros before the first chunk): its
         // products are issued after the barrier that ends the chunk, so the
         // matrix pipe has 8 products queued while the waves meet
-        bf16x8 bl[NTL], al = (bf16x8){};
+        bf16x8 bl[WT], al[WB];
 #pragma unroll
-        for (int t = 0; t < NTL; ++t) bl[t] = (bf16x8){};
+        for (int t = 0; t < WT; ++t) bl[t] = (bf16x8){};
+#pragma unroll
+        for (int j = 0; j < WB; ++j) al[j] = (bf16x8){};
         __syncthreads();
         // scheduling fences keep every phase in place: the operands of a k-step
-        // are read one whole k-step (8 products) before their use
+        // (2 weight and 4 node fragments for 8 products) are read one whole
+        // k-step before their use
         for (int c = 0; c < nchunk; ++c) {
             const int st = c & 1;
-            bf16x8 bc[NTL], ac = read_a(st, 0);
+            bf16x8 bc[WT], ac[WB];
 #pragma unroll
-            for (int t = 0; t < NTL; ++t) bc[t] = read_b(st, 0, t);
+            for (int j = 0; j < WB; ++j) ac[j] = read_a(st, 0, j);
+#pragma unroll
+            for (int t = 0; t < WT; ++t) bc[t] = read_b(st, 0, t);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int t = 0; t < NTL; ++t) mfma(al, bl[t], acc[t]);
+            for (int j = 0; j < WB; ++j)
+#pragma unroll
+                for (int t = 0; t < WT; ++t) mfma(al[j], bl[t], acc[j * WT + t]);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 if (s + 1 < KS) {
-                    bf16x8 bn[NTL], an = read_a(st, s + 1);
+                    bf16x8 bn[WT], an[WB];
 #pragma unroll
-                    for (int t = 0; t < NTL; ++t) bn[t] = read_b(st, s + 1, t);
+                    for (int j = 0; j < WB; ++j) an[j] = read_a(st, s + 1, j);
+#pragma unroll
+                    for (int t = 0; t < WT; ++t) bn[t] = read_b(st, s + 1, t);
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int t = 0; t < NTL; ++t) mfma(ac, bc[t], acc[t]);
-                    __builtin_amdgcn_sched_barrier(0);
-                    ac = an;
+                    for (int j = 0; j < WB; ++j)
 #pragma unroll
-                    for (int t = 0; t < NTL; ++t) bc[t] = bn[t];
+                        for (int t = 0; t < WT; ++t) mfma(ac[j], bc[t], acc[j * WT + t]);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int j = 0; j < WB; ++j) ac[j] = an[j];
+#pragma unroll
+                    for (int t = 0; t < WT; ++t) bc[t] = bn[t];
                 } else {
-                    al = ac;
 #pragma unroll
-                    for (int t = 0; t < NTL; ++t) bl[t] = bc[t];
+                    for (int j = 0; j < WB; ++j) al[j] = ac[j];
+#pragma unroll
+                    for (int t = 0; t < WT; ++t) bl[t] = bc[t];
                 }
             }
             __syncthreads();
         }
 #pragma unroll
-        for (int t = 0; t < NTL; ++t) mfma(al, bl[t], acc[t]);
-
-        // best (value, lower index) per node over the wave's 32 rows, then over
-        // the lane pair l, l ^ 32
-        const int vw = (x * 4 + wave) * 32;
+        for (int j = 0; j < WB; ++j)
 #pragma unroll
-        for (int t = 0; t < NTL; ++t) {
+            for (int t = 0; t < WT; ++t) mfma(al[j], bl[t], acc[j * WT + t]);
+
+        // best (value, lower index) per node over the wave's 64 rows, then over
+        // the lane pair l, l ^ 32
+#pragma unroll
+        for (int t = 0; t < WT; ++t) {
             float bv = -INFINITY;
             int bi = 0x7FFFFFFF;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int v = vw + 8 * (r >> 2) + 4 * hi + (r & 3);
-                const float sc = acc[t][r];
-                if (v < V && better(sc, v, bv, bi)) { bv = sc; bi = v; }
+            for (int j = 0; j < WB; ++j) {
+                const int vw = (x * 4 + 2 * rg + j) * 32;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int v = vw + 8 * (r >> 2) + 4 * hi + (r & 3);
+                    const float sc = acc[j * WT + t][r];
+                    if (v < V && better(sc, v, bv, bi)) { bv = sc; bi = v; }
+                }
             }
             const float ov = __shfl_xor(bv, 32, 64);
             const int oi = __shfl_xor(bi, 32, 64);
             if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-            if (hi == 0) { red_v[wave][t * 32 + l32] = bv; red_i[wave][t * 32 + l32] = bi; }
+            const int node = (nh * WT + t) * 32 + l32;
+            if (hi == 0) { red_v[rg][node] = bv; red_i[rg][node] = bi; }
         }
     }
     __syncthreads();
-    // over the 4 matrix waves: one node per thread of the first 256
+    // over the 2 row groups: one node per thread of the first 256
     if (tid < LMW_NODES) {
         float bv = red_v[0][tid];
         int bi = red_i[0][tid];
-#pragma unroll
-        for (int w = 1; w < 4; ++w)
-            if (better(red_v[w][tid], red_i[w][tid], bv, bi)) { bv = red_v[w][tid]; bi = red_i[w][tid]; }
+        if (better(red_v[1][tid], red_i[1][tid], bv, bi)) { bv = red_v[1][tid]; bi = red_i[1][tid]; }
         const int node = node0 + tid;
         if (node < R) {
             cand_val[(size_t)node * G + x] = bv;
