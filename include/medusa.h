@@ -561,15 +561,17 @@ medusa_status medusa_stream_read(const void* src, size_t bytes, uint32_t* sink, 
  * its vector-memory path.  n_wg workgroups of 256 threads run `rounds`
  * rounds; in each, every thread issues window_parts 16-byte loads of the
  * shared `window` (plain loads, so the window stays in L2: 4 KB blocks read
- * consecutively from offset 0, wrapping at window_bytes) and stream_parts
+ * consecutively from offset 0, wrapping at window_bytes, which must be a
+ * multiple of window_parts x 4096) and stream_parts
  * 16-byte non-temporal loads of its workgroup's own slice of `src`
  * (workgroup g reads bytes [g, g + 1) x rounds x stream_parts x 4096, in
- * order), then XORs them.  (window_parts, stream_parts) is one of (8, 0)
+ * order), all in flight together, then XORs them.  (window_parts, stream_parts) is one of (8, 0)
  * (window only), (0, 8) (HBM only), (4, 2) and (8, 4) (2 : 1 mixes, the
  * wide lm_head's ratio of node-row to weight bytes).  sink[g] (uint32) =
  * the XOR of every word workgroup g loaded.  Pointers of a part that is 0
  * are not read.  Errors: EINVAL for another pair, rounds or n_wg outside
- * [1, 2^20] / [1, 2^16], misaligned or null pointers, or src_bytes below
+ * [1, 2^20] / [1, 2^16], misaligned or null pointers, a window size that is
+ * not a whole number of rounds, or src_bytes below
  * rounds x stream_parts x 4096 x n_wg.
  * ------------------------------------------------------------------------- */
 medusa_status medusa_read_mix(const void* window, size_t window_bytes, const void* src, size_t src_bytes,

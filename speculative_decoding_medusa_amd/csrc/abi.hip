@@ -797,8 +797,8 @@ medusa_status medusa_read_mix(const void* window, size_t window_bytes, const voi
         REQUIRE(n_wg >= 1 && n_wg <= (1 << 16), "n_wg=%d must be in [1, 2^16]", n_wg);
         if (window_parts > 0) {
             REQUIRE(window, "null window");
-            REQUIRE(window_bytes >= 16 && window_bytes % 16 == 0, "window_bytes=%zu must be a positive multiple of 16",
-                    window_bytes);
+            REQUIRE(window_bytes >= 1 && window_bytes % ((size_t)window_parts * 4096) == 0,
+                    "window_bytes=%zu must be a positive multiple of window_parts x 4096", window_bytes);
             REQUIRE(((uintptr_t)window & 15) == 0, "window must be 16-byte aligned");
         }
         if (stream_parts > 0) {

@@ -50,8 +50,8 @@ void launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int n_wg,
 }
 
 // One round: every thread issues WP window loads (plain: the window stays in
-// L2) and SP loads of its workgroup's slice of `src` (non-temporal), then
-// XORs them.  The window is read in 4 KB blocks (256 threads x 16 bytes),
+// L2) and SP loads of its workgroup's slice of `src` (non-temporal), all in
+// flight together, then XORs them.  The window is read in 4 KB blocks (256 threads x 16 bytes),
 // consecutive per round and wrapping at its end; the slice of workgroup g is
 // rounds x SP x 4 KB starting at g times that.
 template <int WP, int SP>
@@ -65,16 +65,18 @@ __global__ __launch_bounds__(READ_THREADS) void read_mix_kernel(const u32x4* __r
     for (int r = 0; r < rounds; ++r) {
         u32x4 v[WP + SP];
 #pragma unroll
-        for (int u = 0; u < WP; ++u) {
-            size_t i = wpos + (size_t)u * READ_THREADS + tid;
-            i = i < w16 ? i : i % w16;
-            v[u] = win[i];
-        }
+        for (int u = 0; u < WP; ++u) v[u] = win[wpos + (size_t)u * READ_THREADS + tid];
 #pragma unroll
         for (int u = 0; u < SP; ++u) v[WP + u] = ld_stream(slice + ((size_t)r * SP + u) * READ_THREADS + tid);
+        // every load of the round is issued before the first is consumed (left
+        // to itself the compiler interleaves the XORs and waits after three)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < WP + SP; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
-        if constexpr (WP > 0) wpos = (wpos + (size_t)WP * READ_THREADS) % w16;
+        if constexpr (WP > 0) {
+            wpos += (size_t)WP * READ_THREADS;
+            if (wpos == w16) wpos = 0;  // the window is a whole number of rounds
+        }
     }
     __shared__ uint32_t red[READ_THREADS / 64];
 #pragma unroll

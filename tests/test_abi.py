@@ -246,8 +246,10 @@ def test_measurement_aid_argument_errors(M):
     assert st == M.EINVAL and "window_parts" in L.medusa_last_error().decode()
     st = L.medusa_read_mix(d, 4096, d, 4096, 0, 8, 1, d, 1, None)      # needs 8 x 4096 bytes of src
     assert st == M.EINVAL and "src_bytes" in L.medusa_last_error().decode()
-    st = L.medusa_read_mix(ctypes.c_void_p(24), 4096, None, 0, 8, 0, 1, d, 1, None)
+    st = L.medusa_read_mix(ctypes.c_void_p(24), 8 * 4096, None, 0, 8, 0, 1, d, 1, None)
     assert st == M.EINVAL and "aligned" in L.medusa_last_error().decode()
+    st = L.medusa_read_mix(d, 4096, None, 0, 8, 0, 1, d, 1, None)      # not a whole round of 8 x 4 KB
+    assert st == M.EINVAL and "window_bytes" in L.medusa_last_error().decode()
     st = L.medusa_mfma_rate(2, 10, d, 1, None)
     assert st == M.EINVAL and "random_operands" in L.medusa_last_error().decode()
     st = L.medusa_mfma_rate(0, 0, d, 1, None)

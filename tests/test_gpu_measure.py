@@ -28,10 +28,10 @@ def test_stream_read_covers_every_byte(nbytes, n_wg):
 
 
 @pytest.mark.parametrize("wp,sp,rounds,n_wg,w16", [
-    (8, 0, 3, 5, 3000),     # window only; rounds wrap inside a round and across rounds
-    (0, 8, 2, 7, 0),        # private slices only
-    (4, 2, 5, 3, 1000),     # 2 : 1 mix
-    (8, 4, 2, 4, 4096),
+    (8, 0, 5, 5, 3 * 2048),     # window only (3 rounds' worth): reads wrap at its end
+    (0, 8, 2, 7, 0),            # private slices only
+    (4, 2, 5, 3, 3 * 1024),     # 2 : 1 mix
+    (8, 4, 3, 4, 2 * 2048),
 ], ids=["window", "stream", "mix42", "mix84"])
 def test_read_mix_covers_every_load(wp, sp, rounds, n_wg, w16):
     import speculative_decoding_medusa_amd as M
