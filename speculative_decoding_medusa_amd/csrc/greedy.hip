@@ -123,6 +123,12 @@ constexpr int LMW_D = 1;
 static bool lmw_use(int R, int H, int V, bool logits) {
     return lmh_nblk(R) == 16 && lmh_shape(R, V).ns == 2 && !logits && H % LMW_KC == 0;
 }
+// Node tiles with enough workgroups at 256 weight rows, without logits: the
+// 256-row variant of lm_head_wide.hpp (512 x 4096 x 128256: 555 us against
+// 628 for the 16 x 16 x 32 product; 256 x 4096 x 128256: 292 against 302).
+static bool lmw256_use(int R, int H, int V, bool logits) {
+    return lmh_nblk(R) == 16 && lmh_shape(R, V).ns == 1 && !logits && H % LMW_KC == 0;
+}
 
 size_t lm_head_greedy_workspace_bytes(int R, int H, int V) {
     const int G = lmh_groups(R, V) > lmw_groups(V) ? lmh_groups(R, V) : lmw_groups(V);
@@ -132,6 +138,15 @@ size_t lm_head_greedy_workspace_bytes(int R, int H, int V) {
 
 void launch_lm_head_greedy(const bf16_t* n, const bf16_t* lm_head, int R, int H, int V, int32_t* greedy,
                            float* logits, float rs_eps, void* ws, hipStream_t s) {
+    if (lmw256_use(R, H, V, logits != nullptr)) {
+        const int G = lmw256_groups(V), T = lmw_tiles(R);
+        float* cv = (float*)ws;
+        int* ci = (int*)((char*)ws + a256((size_t)R * G * 4));
+        MEDUSA_LAUNCH("lm_head_argmax", lm_head_argmax_wide256_kernel, dim3((G + 7) / 8 * 8 * T), dim3(512), 0, s, n,
+                      lm_head, R, H, V, T, G, cv, ci);
+        MEDUSA_LAUNCH("argmax_merge", argmax_merge_kernel, dim3(R), dim3(64), 0, s, cv, ci, G, greedy);
+        return;
+    }
     if (lmw_use(R, H, V, logits != nullptr)) {
         const int G = lmw_groups(V), T = lmw_tiles(R);
         float* cv = (float*)ws;

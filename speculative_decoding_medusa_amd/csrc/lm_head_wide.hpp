@@ -257,4 +257,189 @@ __global__ __launch_bounds__(512) void lm_head_argmax_wide_kernel(const bf16_t* 
     }
 }
 
+// The same product for vocabularies that give 256-row weight tiles enough
+// workgroups (two node tiles of a 128,256-row vocabulary): each workgroup
+// holds 256 weight rows against one 256-row node tile, so every node row it
+// stages from L2 feeds twice the weight rows of the 128-row tile above (that
+// tile moved 4 GB of node rows at 512 x 128,256 and was bound by it).  8
+// waves, two per SIMD; wave w owns the 32-row weight blocks 2 (w / 2) and
+// 2 (w / 2) + 1 against node rows 128 (w % 2) .. + 127, the operands of each
+// k-step read from LDS as above.  No wave role split (two matrix waves per
+// SIMD leave no registers for loader waves): every thread loads a quarter of
+// a chunk's 2,048 weight pieces and 2,048 node pieces into a register ring
+// one chunk deep and publishes them into the idle LDS stage while the
+// chunk before is computed.  Measured at 512 x 4096 x 128256: 555 us against
+// 628 for the 16 x 16 x 32 product; without its loads it takes 426 us and
+// without its products 404 us (each workgroup then has about 64 KB of loads
+// in flight; a second chunk of registers would not fit beside the
+// accumulators, and a third LDS stage would not fit either).
+inline int lmw256_groups(int V) { return (V + 255) / 256; }
+
+__global__ __launch_bounds__(512) void lm_head_argmax_wide256_kernel(const bf16_t* __restrict__ n,   // [R][K]
+                                                                     const bf16_t* __restrict__ Wp,  // packed [V][K]
+                                                                     int R, int K, int V, int T, int G,
+                                                                     float* __restrict__ cand_val,  // [R][G]
+                                                                     int* __restrict__ cand_idx) {
+    constexpr int KC = LMW_KC;
+    constexpr int KS = KC / 16;                 // 32 x 32 x 16 k-steps per chunk
+    constexpr int NB = 8;                       // 32-row weight blocks per workgroup
+    constexpr int PPT = 4;                      // weight pieces and node pieces per thread per chunk
+    constexpr int WB = 2, WT = 4;               // per wave: 32-row weight blocks, 32-node tiles
+    static_assert(KC == 64 && NB * KS * 64 == 512 * PPT && LMW_NODES * (KC / 8) == 512 * PPT, "piece split");
+    __shared__ __attribute__((aligned(16))) bf16_t ns[2][LMW_NODES][KC];  // node tile, swizzled columns
+    __shared__ u32x4 as[2][NB][KS][64];  // weight pieces in the lane order of the A operand
+    __shared__ float red_v[4][LMW_NODES];  // per row group of waves
+    __shared__ int red_i[4][LMW_NODES];
+
+    const int L = blockIdx.x, j0 = L >> 3;
+    const int y = j0 % T, x = (j0 / T) * 8 + (L & 7);  // node tile, row tile (256 rows)
+    if (x >= G) return;                                 // padding of the grid to whole XCD rounds
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int node0 = y * LMW_NODES;
+    const int nrb = (V + PACK_ROWS - 1) / PACK_ROWS;
+    const int nchunk = K / KC;  // host guarantees K % KC == 0
+
+    // this thread's pieces e = 0..3: weight block 2 e + tid / 256, k-step
+    // (tid / 64) % 4, lane tid % 64; node row tid / 8 + 64 e, column tid % 8
+    const int ps = (tid >> 6) & 3, pl = tid & 63, pbh = tid >> 8;
+    const bf16_t* wa[PPT];
+#pragma unroll
+    for (int e = 0; e < PPT; ++e) {
+        const int pb = min((x * NB + 2 * e + pbh) * 2 + ((pl & 31) >> 4), nrb - 1);  // past the end: clamped
+        wa[e] = Wp + ((size_t)(ps >> 1) * nrb + pb) * PACK_FRAG + ((2 * (ps & 1) + (pl >> 5)) * PACK_ROWS + (pl & 15)) * 8;
+    }
+    const size_t cstride = (size_t)(KC / 32) * nrb * PACK_FRAG;
+    const int col = tid & 7, row0 = tid >> 3;
+    const int wcol = (col ^ ((row0 >> 1) & 7)) * 8;
+    const bf16_t* nrow[PPT];
+#pragma unroll
+    for (int e = 0; e < PPT; ++e) nrow[e] = n + (size_t)min(node0 + row0 + 64 * e, R - 1) * K + col * 8;
+    u32x4 nr[PPT], ar[PPT];
+    auto load = [&](int c) {
+        c = min(c, nchunk - 1);  // past the end: the last chunk again, never published
+#pragma unroll
+        for (int e = 0; e < PPT; ++e) nr[e] = *(const u32x4*)(nrow[e] + (size_t)c * KC);
+#pragma unroll
+        for (int e = 0; e < PPT; ++e) ar[e] = ld_stream(wa[e] + (size_t)c * cstride);
+    };
+    auto publish = [&](int st) {
+#pragma unroll
+        for (int e = 0; e < PPT; ++e) *(u32x4*)(&ns[st][row0 + 64 * e][wcol]) = nr[e];
+#pragma unroll
+        for (int e = 0; e < PPT; ++e) as[st][2 * e + pbh][ps][pl] = ar[e];
+    };
+
+    const int rg = wave >> 1, nh = wave & 1;
+    const int l32 = lane & 31, hi = lane >> 5;
+    const int rsw = (l32 >> 1) & 7;
+    f32x16 acc[WB * WT];
+#pragma unroll
+    for (int t = 0; t < WB * WT; ++t) acc[t] = (f32x16){};
+    auto read_b = [&](int st, int s, int t) {
+        return __builtin_bit_cast(bf16x8,
+                                  *(const u32x4*)(&ns[st][(nh * WT + t) * 32 + l32][((2 * s + hi) ^ rsw) * 8]));
+    };
+    auto read_a = [&](int st, int s, int jb) { return __builtin_bit_cast(bf16x8, as[st][2 * rg + jb][s][lane]); };
+    auto mfma = [&](bf16x8 a, bf16x8 b, f32x16& d) {
+        d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, d, 0, 0, 0);
+    };
+
+    load(0);
+    publish(0);
+    load(1);
+    bf16x8 bl[WT], al[WB];
+#pragma unroll
+    for (int t = 0; t < WT; ++t) bl[t] = (bf16x8){};
+#pragma unroll
+    for (int jb = 0; jb < WB; ++jb) al[jb] = (bf16x8){};
+    __syncthreads();
+    for (int c = 0; c < nchunk; ++c) {
+        const int st = c & 1;
+        bf16x8 bc[WT], ac[WB];
+#pragma unroll
+        for (int jb = 0; jb < WB; ++jb) ac[jb] = read_a(st, 0, jb);
+#pragma unroll
+        for (int t = 0; t < WT; ++t) bc[t] = read_b(st, 0, t);
+        __builtin_amdgcn_sched_barrier(0);
+        // the previous chunk's last k-step, after the barrier that ended it
+#pragma unroll
+        for (int jb = 0; jb < WB; ++jb)
+#pragma unroll
+            for (int t = 0; t < WT; ++t) mfma(al[jb], bl[t], acc[jb * WT + t]);
+        __builtin_amdgcn_sched_barrier(0);
+        // chunk c + 1 into the idle stage (last read before the previous
+        // barrier), then chunk c + 2 into the registers just freed
+        publish(st ^ 1);
+        load(c + 2);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            if (s + 1 < KS) {
+                bf16x8 bn[WT], an[WB];
+#pragma unroll
+                for (int jb = 0; jb < WB; ++jb) an[jb] = read_a(st, s + 1, jb);
+#pragma unroll
+                for (int t = 0; t < WT; ++t) bn[t] = read_b(st, s + 1, t);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int jb = 0; jb < WB; ++jb)
+#pragma unroll
+                    for (int t = 0; t < WT; ++t) mfma(ac[jb], bc[t], acc[jb * WT + t]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int jb = 0; jb < WB; ++jb) ac[jb] = an[jb];
+#pragma unroll
+                for (int t = 0; t < WT; ++t) bc[t] = bn[t];
+            } else {
+#pragma unroll
+                for (int jb = 0; jb < WB; ++jb) al[jb] = ac[jb];
+#pragma unroll
+                for (int t = 0; t < WT; ++t) bl[t] = bc[t];
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int jb = 0; jb < WB; ++jb)
+#pragma unroll
+        for (int t = 0; t < WT; ++t) mfma(al[jb], bl[t], acc[jb * WT + t]);
+
+    // best (value, lower index) per node over the wave's 64 rows, then over
+    // the lane pair l, l ^ 32, then over the 4 row groups
+#pragma unroll
+    for (int t = 0; t < WT; ++t) {
+        float bv = -INFINITY;
+        int bi = 0x7FFFFFFF;
+#pragma unroll
+        for (int jb = 0; jb < WB; ++jb) {
+            const int vw = (x * NB + 2 * rg + jb) * 32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int v = vw + 8 * (r >> 2) + 4 * hi + (r & 3);
+                const float sc = acc[jb * WT + t][r];
+                if (v < V && better(sc, v, bv, bi)) { bv = sc; bi = v; }
+            }
+        }
+        const float ov = __shfl_xor(bv, 32, 64);
+        const int oi = __shfl_xor(bi, 32, 64);
+        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+        const int node = (nh * WT + t) * 32 + l32;
+        if (hi == 0) { red_v[rg][node] = bv; red_i[rg][node] = bi; }
+    }
+    __syncthreads();
+    if (tid < LMW_NODES) {
+        float bv = red_v[0][tid];
+        int bi = red_i[0][tid];
+#pragma unroll
+        for (int g = 1; g < 4; ++g)
+            if (better(red_v[g][tid], red_i[g][tid], bv, bi)) { bv = red_v[g][tid]; bi = red_i[g][tid]; }
+        const int node = node0 + tid;
+        if (node < R) {
+            cand_val[(size_t)node * G + x] = bv;
+            cand_idx[(size_t)node * G + x] = bi;
+        }
+    }
+}
+
 }  // namespace medusa

@@ -255,6 +255,32 @@ def test_base_greedy_wide_tree_parity(M, name, R, H, V):
     assert np.array_equal(g.cpu().numpy(), g_ref)
 
 
+# Node tiles whose vocabulary gives 256-row weight tiles at least 256
+# workgroups take the 256-row variant (8 waves loading and multiplying,
+# 64-wide chunks): two ragged node tiles, one full, and a vocabulary whose
+# last row tile is ragged.
+WIDE256_GREEDY_CASES = [
+    ("r300_h128_v32513", 300, 128, 32513),   # two node tiles, 128 x 2 workgroups, ragged last row tile
+    ("r256_h192_v65600", 256, 192, 65600),   # one node tile, 257 workgroups, three chunks
+    ("r512_h64_v33000", 512, 64, 33000),     # two full node tiles, one chunk
+]
+
+
+@pytest.mark.parametrize("name,R,H,V", WIDE256_GREEDY_CASES, ids=[c[0] for c in WIDE256_GREEDY_CASES])
+def test_base_greedy_wide256_parity(M, name, R, H, V):
+    _say("base_greedy wide256", name)
+    cfg = _cfg("gw2", "bf16", 1, H, V, 1, 1, mi.tiny_tree(), seed=800 + R)
+    heads = {"lm_head": mi.normal((V, H), cfg.seed, mi.S_LM_HEAD, 0.02, "bf16")}
+    x = mi.normal((R, H), cfg.seed, mi.S_TEST, 1.0, "bf16")
+    xw = oracle.widen(x, "bf16")
+    enforce_greedy_gap(cfg, heads, xw, [])
+    g_ref, _ = oracle.base_greedy(xw, oracle.widen(heads["lm_head"], "bf16"), 1e-6)
+    g = torch.full((R,), -1, dtype=torch.int32, device="cuda")
+    M.medusa_base_greedy(dev(x), M.pack(dev(heads["lm_head"])), g, eps=1e-6)
+    torch.cuda.synchronize()
+    assert np.array_equal(g.cpu().numpy(), g_ref)
+
+
 def _random_wide_shapes(n, seed=4242):
     """n seeded (R, H, V): 129-512 node rows, H a multiple of 64 up to 512,
     ragged vocabularies up to 3000 rows."""
