@@ -1,11 +1,14 @@
-// Wide-tree lm_head argmax for one 256-row node tile and a vocabulary too
-// small to give the skinny product enough workgroups: the node rows against
-// the packed bf16 lm_head on v_mfma_f32_32x32x16_bf16, the argmax over the
-// workgroup's weight rows fused into the epilogue.  The per-workgroup
-// candidates have the layout of skinny_mfma_kernel's argmax epilogue
-// ([R][G]) and go to the same merge.
+// Wide-tree lm_head argmax: 256-row node tiles against the packed bf16
+// lm_head on v_mfma_f32_32x32x16_bf16, the argmax over the workgroup's
+// weight rows fused into the epilogue.  The per-workgroup candidates have
+// the layout of skinny_mfma_kernel's argmax epilogue ([R][G]) and go to the
+// same merge.  Two kernels: lm_head_argmax_wide_kernel (128 weight rows a
+// workgroup, loader waves) for vocabularies too small to give 256-row weight
+// tiles 256 workgroups (32,000 rows), and lm_head_argmax_wide256_kernel
+// (256 weight rows a workgroup, below) for the others.
 //
-// Workgroup: 128 weight rows against one 256-row node tile, 8 waves in two
+// lm_head_argmax_wide_kernel.  Workgroup: 128 weight rows against one
+// 256-row node tile, 8 waves in two
 // roles.  Waves 0-3 (one per SIMD) are matrix waves: wave w owns the 32-row
 // weight blocks 2 (w / 2) and 2 (w / 2) + 1 against node rows 128 (w % 2) ..
 // + 127 (2 x 4 accumulator tiles of 32 x 32), so every k-step reads 2 weight
@@ -43,9 +46,9 @@
 // 2 MB node tile from L2) and its LDS carries 96 KB of operand reads and
 // 48 KB of loader writes per chunk; the products alone take 65 us (random
 // bf16 operands keep the matrix cores at about 1.4 PFLOP/s, well under the
-// constant-data rate).  With two node tiles and enough workgroups the
-// 256-row skinny tile, which stages each node row for twice the weight rows,
-// stays faster.
+// constant-data rate).  Where there are enough workgroups the 256-row
+// kernel below, which stages each node row for twice the weight rows, is
+// faster (this one: 635 us at 512 x 4096 x 128256, that one 555).
 //
 // Grid: ceil(G / 8) * 8 * T workgroups for G = ceil(V / 128) row tiles and T
 // node tiles.  Workgroup L runs on XCD L % 8 (round-robin dispatch); the T
@@ -95,7 +98,7 @@ __global__ __launch_bounds__(512) void lm_head_argmax_wide_kernel(const bf16_t* 
         // ---- loader waves: chunk j's weight and node pieces into registers
         // D chunks ahead, published into LDS stage j & 1 one step before use
         const int lt = tid - 256;
-        // weight pieces e = 0..3: matrix wave e, k-step s = lt / 64, lane l = lt % 64
+        // weight pieces e = 0..3: 32-row block e, k-step s = lt / 64, lane l = lt % 64
         const int s = lt >> 6, l = lt & 63;
         const bf16_t* wa[APL];
 #pragma unroll
