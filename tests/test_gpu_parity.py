@@ -281,6 +281,35 @@ def test_base_greedy_wide256_parity(M, name, R, H, V):
     assert np.array_equal(g.cpu().numpy(), g_ref)
 
 
+def test_base_greedy_wide_tree_tiny_vocabulary(M):
+    """17 vocabulary rows (one packed block and one row of the next; every
+    other weight block of the workgroup clamped) against 140 nodes.  Too few
+    rows to enforce a gap between every node's best two scores, so: where the
+    float64 scores' best two differ by more than the products' error bound
+    the ids match; elsewhere the chosen row scores within that bound of the
+    best."""
+    R, H, V = 140, 64, 17
+    _say("base_greedy wide tiny vocabulary", R, H, V)
+    cfg = _cfg("gwt", "bf16", 1, H, V, 1, 1, mi.tiny_tree(), seed=913)
+    lm = mi.normal((V, H), cfg.seed, mi.S_LM_HEAD, 0.02, "bf16")
+    x = mi.normal((R, H), cfg.seed, mi.S_TEST, 1.0, "bf16")
+    lmw, xw = oracle.widen(lm, "bf16"), oracle.widen(x, "bf16")
+    g_ref, _ = oracle.base_greedy(xw, lmw, 1e-6)
+    scores = xw @ lmw.T                     # unnormalised: same argmax (positive row factors)
+    g = torch.full((R,), -1, dtype=torch.int32, device="cuda")
+    M.medusa_base_greedy(dev(x), M.pack(dev(lm)), g, eps=1e-6)
+    torch.cuda.synchronize()
+    got = g.cpu().numpy()
+    bound = 1e-4 * np.abs(xw) @ np.abs(lmw).T  # fp32 accumulation of bf16 products, with margin
+    top2 = np.sort(scores, axis=1)[:, -2:]
+    clear = top2[:, 1] - top2[:, 0] > 2 * bound.max(axis=1)
+    assert clear.sum() > R // 2
+    assert np.array_equal(got[clear], g_ref[clear])
+    rows = np.arange(R)
+    assert np.all((got >= 0) & (got < V))
+    assert np.all(scores[rows, got] >= scores[rows, g_ref] - 2 * bound[rows, g_ref])
+
+
 def _random_wide_shapes(n, seed=4242):
     """n seeded (R, H, V): 129-512 node rows, H a multiple of 64 up to 512,
     ragged vocabularies up to 3000 rows."""
