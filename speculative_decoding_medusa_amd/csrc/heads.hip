@@ -433,7 +433,15 @@ void launch_vocab_topk_named(const float* z, const void* w2, int B, int H, int V
 // of sequences 0..7, rows 8..15 the remainders (absent sequences zero), and
 // the epilogue adds the two columns of a sequence.
 // ---------------------------------------------------------------------------
-constexpr int VT_WAVES = 4;  // waves per workgroup: 64 weight rows
+// Launch shape, measured at 8 sequences x 5 heads x 128,256 x 4,096 (per
+// call, with the row split and the top-k merge): 4 waves of 4 16-row blocks
+// each (256 weight rows a workgroup) with a two-chunk weight ring take 835
+// us, against 913 for one block a wave with a four-chunk ring, 869 for two
+// blocks, 840 for eight, and 866 for 2 waves of 4 blocks.  More rows a
+// workgroup stage the 16 node rows for more weight bytes; a shallower ring
+// keeps fewer bytes in flight.
+constexpr int VT_WAVES = 4;  // waves per workgroup
+constexpr int VT_RB = 4;     // 16-row weight blocks per wave: 256 weight rows a workgroup
 
 // z [B][K][H] fp32 -> zs [K][16][H] bf16
 __global__ __launch_bounds__(256) void split_rows_kernel(const float* __restrict__ z, int B, int K, int H,
@@ -450,7 +458,7 @@ __global__ __launch_bounds__(256) void split_rows_kernel(const float* __restrict
     }
 }
 
-int vocab_topk_packed_groups(int V) { return (V + 16 * VT_WAVES - 1) / (16 * VT_WAVES); }
+int vocab_topk_packed_groups(int V) { return (V + 16 * VT_WAVES * VT_RB - 1) / (16 * VT_WAVES * VT_RB); }
 int vocab_topk_packed_kc() { return LmhCfg<1, VT_WAVES>::KC; }
 
 static size_t a256h(size_t n) { return (n + 255) / 256 * 256; }
@@ -468,7 +476,7 @@ void launch_vocab_topk_packed(const float* z, const void* w2p, int B, int H, int
     int* ci = (int*)((char*)cv + a256h(cand * 4));
     MEDUSA_LAUNCH("split_rows", split_rows_kernel, dim3(256), dim3(256), 0, s, z, B, K, H, zs);
     const long long w_stride = (long long)((V + PACK_ROWS - 1) / PACK_ROWS) * PACK_ROWS * H;
-    MEDUSA_LAUNCH("vocab_proj_topk_mfma", (skinny_mfma_kernel<1, SKINNY_TOPK, VT_WAVES>), dim3(G, K),
+    MEDUSA_LAUNCH("vocab_proj_topk_mfma", (skinny_mfma_kernel<1, SKINNY_TOPK, VT_WAVES, VT_RB>), dim3(G, K),
                   dim3(VT_WAVES * 64), 0, s, zs, (const bf16_t*)w2p, 16, H, V, H / LmhCfg<1, VT_WAVES>::KC, cv, ci,
                   logits, -1.f, topk, B, (long long)16 * H, w_stride);
     launch_topk_merge(cv, ci, B * K, G * topk, topk, topk_idx, topk_val, s, "topk_merge");

@@ -13,8 +13,8 @@
 // fragments of one k-step lie side by side over all row blocks, so a wave's
 // consecutive fragments are one k-step of the whole matrix apart.
 //
-// Grid (ceil(V / (16 WAVES)), ceil(R / NODES), splits); WAVES waves per
-// workgroup, each owning one 16-row block against NODES node rows.  Weight fragments stream
+// Grid (ceil(V / (16 WAVES RB)), ceil(R / NODES), splits); WAVES waves per
+// workgroup, each owning RB 16-row blocks against NODES node rows.  Weight fragments stream
 // into registers (non-temporal) up to D - 1 k-chunks ahead; the node rows are
 // staged in LDS in k-chunks shared by the waves (double-buffered, one
 // barrier per chunk).  Every load is issued unconditionally -- rows past the
@@ -80,9 +80,13 @@ struct LmhCfg {
 // loads go out before the weight loads of the same step: vector-memory loads
 // complete in issue order, so waiting for a chunk's node rows never waits for
 // younger weight fragments.
-// RB (ARGMAX only): 16-row weight blocks per wave; every node fragment read
-// from LDS then feeds RB products, which halves the LDS traffic per product
-// at RB = 2 (the bound of the 128- and 256-node tiles).
+// RB (ARGMAX and TOPK): 16-row weight blocks per wave; every node fragment
+// read from LDS then feeds RB products, which halves the LDS traffic per
+// product at RB = 2 (the bound of the 128- and 256-node tiles), and a
+// workgroup stages its node rows once for RB times the weight rows.  With
+// TOPK and RB > 1 the weight ring is two chunks deep (each chunk already
+// holds RB times the fragments): fewer bytes in flight per CU measured
+// faster (see the packed vocabulary projection in heads.hip).
 // NS (ARGMAX only): the waves split the node blocks into NS groups -- wave w
 // takes row group w / NS and node blocks (w % NS) NBLK / NS .. -- so each wave
 // reads 1/NS of the node fragments per chunk; the NS waves of a row group
@@ -108,7 +112,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
     // Wp + y w_stride); out = optional logits [nseq][gridDim.y][V];
     // candidates [nseq][gridDim.y][G][topk]
     using C = LmhCfg<NBLK, WAVES>;
-    constexpr int D = C::D;
+    constexpr int D = EPI == SKINNY_TOPK && RB > 1 ? 2 : C::D;
     constexpr int NT = C::NT;
     __shared__ __attribute__((aligned(16))) bf16_t ns[2][C::NODES][C::LDW];
     constexpr int RG = WAVES / NS;      // row groups of a workgroup
@@ -116,9 +120,10 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
     __shared__ float red_v[RG][EPI == SKINNY_ARGMAX ? C::NODES : 1];
     __shared__ int red_i[RG][EPI == SKINNY_ARGMAX ? C::NODES : 1];
     __shared__ f32x4 xup[EPI == SKINNY_SWIGLU ? WAVES / 2 : 1][EPI == SKINNY_SWIGLU ? NBLK : 1][64];
-    __shared__ float tkv[EPI == SKINNY_TOPK ? WAVES * PACK_ROWS : 1][8];  // TOPK: the workgroup's rows x sequences
+    __shared__ float tkv[EPI == SKINNY_TOPK ? WAVES * PACK_ROWS * RB : 1][8];  // TOPK: the workgroup's rows x sequences
     static_assert((EPI != SKINNY_TOPK && EPI != SKINNY_SILU) || NBLK == 1, "top-k / SiLU epilogue: 16 node rows");
-    static_assert(RB == 1 || EPI == SKINNY_ARGMAX, "several row blocks per wave: argmax epilogue only");
+    static_assert(RB == 1 || EPI == SKINNY_ARGMAX || EPI == SKINNY_TOPK,
+                  "several row blocks per wave: argmax and top-k epilogues only");
     static_assert(NS == 1 || (EPI == SKINNY_ARGMAX && NBLK % NS == 0 && WAVES % NS == 0), "node split: argmax only");
     if (EPI == SKINNY_TOPK || EPI == SKINNY_SILU) {
         n += (size_t)blockIdx.y * n_stride;
@@ -281,22 +286,24 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_mfma_kernel(const bf16_t* _
         return;
     }
     if (EPI == SKINNY_TOPK) {
-        // lane (lr, lk) holds rows vw + 4 lk + r of node column lr; sequence
-        // b's score adds its remainder column b + 8, held by lane lr ^ 8
+        // lane (lr, lk) holds rows vw + 16 j + 4 lk + r of node column lr;
+        // sequence b's score adds its remainder column b + 8, held by lane lr ^ 8
         const int nm = gridDim.y, m = blockIdx.y;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float x = acc[0][r] + __shfl_xor(acc[0][r], 8, 64);
-            const int v = vw + lk * 4 + r;
-            if (lr < 8) {
-                tkv[wave * PACK_ROWS + lk * 4 + r][lr] = v < V ? x : -INFINITY;
-                if (out != nullptr && lr < nseq && v < V) out[((size_t)lr * nm + m) * V + v] = x;
+        for (int j = 0; j < RB; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float x = acc[j * NBW][r] + __shfl_xor(acc[j * NBW][r], 8, 64);
+                const int v = vw + j * PACK_ROWS + lk * 4 + r;
+                if (lr < 8) {
+                    tkv[(wave * RB + j) * PACK_ROWS + lk * 4 + r][lr] = v < V ? x : -INFINITY;
+                    if (out != nullptr && lr < nseq && v < V) out[((size_t)lr * nm + m) * V + v] = x;
+                }
             }
-        }
         __syncthreads();
         // each wave takes sequences wave, wave + WAVES, ...: every lane keeps a
         // sorted list of the rows it scans, then the wave extracts the winners
-        constexpr int ROWS = WAVES * PACK_ROWS;
+        constexpr int ROWS = WAVES * PACK_ROWS * RB;
         for (int b = wave; b < nseq; b += WAVES) {
             float lv[MEDUSA_MAX_TOPK_DEV];
             int li[MEDUSA_MAX_TOPK_DEV];

@@ -152,9 +152,10 @@ def test_workspace_sizes_are_positive(M):
     L = M._lib
     assert L.medusa_heads_workspace_size(1, 4096, 32000, 5, 4, M.BF16, M.ROW_MAJOR) >= 5 * 4096 * 4
     assert L.medusa_vocab_topk_workspace_size(8, 4096, 128256, 5, 4, M.BF16, M.ROW_MAJOR) > 0
-    # packed: the bf16 head/remainder rows of every head + per-workgroup top-k candidates
+    # packed: the bf16 head/remainder rows of every head + the top-k candidates
+    # of every 256-row workgroup (501 of them per head)
     assert (L.medusa_vocab_topk_workspace_size(8, 4096, 128256, 5, 4, M.BF16, M.PACKED)
-            >= 5 * 16 * 4096 * 2 + 2 * 8 * 5 * 1002 * 4 * 4)
+            >= 5 * 16 * 4096 * 2 + 2 * 8 * 5 * 501 * 4 * 4)
     # packed: per-workgroup (value, index) candidates of every row
     assert L.medusa_base_greedy_workspace_size(64, 4096, 32000, M.BF16, M.PACKED) >= 2 * 64 * 250 * 4
     assert L.medusa_base_greedy_workspace_size(9, 256, 1000, M.F32, M.ROW_MAJOR) >= 9 * 256 * 4
