@@ -483,10 +483,15 @@ void launch_vocab_topk_packed(const float* z, const void* w2p, int B, int H, int
 }
 
 // Residual-SiLU block over packed W1 on MFMA (several sequences): the bf16
-// hidden states are the node rows (exact, no split), grid (H / 64, K), one
+// hidden states are the node rows (exact, no split), grid (H / 32, K), one
 // packed H x H matrix per grid row; the epilogue adds the bias, applies SiLU
-// and the residual.
-constexpr int SILU_MF_WAVES = 4;
+// and the residual.  Two-wave workgroups (32 weight rows): at 5 x 4096 x 4096
+// the 4-wave grid has 320 workgroups, so a quarter of the CUs stream two
+// while the rest stream one (39.4 us); 640 two-wave workgroups spread the
+// rows more evenly (33.6 us; one-wave workgroups with six chunks in flight
+// 33.1, four blocks a wave 38.1, with the weights evicted from the caches
+// between calls).
+constexpr int SILU_MF_WAVES = 2;
 
 int resid_silu_packed_kc() { return LmhCfg<1, SILU_MF_WAVES>::KC; }
 
