@@ -42,7 +42,7 @@ VOCAB_TRAFFIC = {"sources_sha256_16": "73b4ac2fd7b4d9f3", "read_bytes": 13115281
 # the same for the gate|up projection of the 32-layer workload (one layer's
 # launch: 64 x 4096 node rows against 22016 packed weight rows, unsplit, the
 # SwiGLU product written in bf16)
-GATE_UP_TRAFFIC = {"sources_sha256_16": "114b8eb7854cb4ee", "read_bytes": 185335404, "write_bytes": 1409024}
+GATE_UP_TRAFFIC = {"sources_sha256_16": "4ffb806ed700d70e", "read_bytes": 185331073, "write_bytes": 1409024}
 
 
 def _traffic_bytes(rec, sources):
