@@ -220,8 +220,10 @@ __global__ __launch_bounds__(ATT_MERGE_THREADS) void tree_attn_merge_kernel(cons
 // The last tile of a prefix range may load slots at and past P (its rows are
 // clamped to the host bound max_cache_len, not to P, since the tiles are
 // requested before P is read), racing with that copy; those keys' scores are
-// masked and their V elements zeroed before the P.V product, so whatever the
-// slots hold (old data, the new tree keys, NaN) never reaches the output.
+// masked and their V values zeroed (per key pair in masked tiles with one
+// query block a wave; with two, the V rows in LDS once the tile has landed,
+// one extra barrier on that tile alone), so whatever the slots hold (old
+// data, the new tree keys, NaN) never reaches the output.
 // With several query blocks per head
 // the blocks of one key range get linear workgroup ids 8 apart: workgroups are
 // dealt to the 8 XCDs round-robin, so the blocks land on one XCD and read the
@@ -270,7 +272,7 @@ __global__ __launch_bounds__(ATT_MERGE_THREADS) void tree_attn_merge_kernel(cons
 // tiles in flight), then one barrier per tile publishes the tile and frees
 // the stage the next load overwrites.  No tile past the range is requested;
 // rows of the last tile past the range are clamped to its last row (their
-// scores are masked and their V elements zeroed).  Within a
+// scores are masked and their V values zeroed).  Within a
 // stage a row's 16-byte chunks are XOR-swizzled by a function of the row, so
 // the K fragment reads (16 rows, one chunk) and the transposing V reads (4
 // rows, two chunks) hit distinct LDS banks.  The first tiles are requested
@@ -336,6 +338,14 @@ template <int younger> __device__ __forceinline__ void mf_tile_barrier() {
     static_assert(younger < 16, "vmcnt field");
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0x70 | younger);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// This wave's LDS accesses are done (lgkmcnt = 0; loads into LDS still in
+// flight are not waited for: vmcnt = 63), then the workgroup barrier.
+__device__ __forceinline__ void mf_lds_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
@@ -623,7 +633,7 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
         // prefix length was known): their probability is 0, but 0 times a
         // NaN or infinite V is NaN, so the lane's V elements of keys past the
         // range are zeroed (element e of a transposed read is key 4 lk + e of
-        // its block)
+        // its block); only masked pairs pay for this
         uint32_t keep[2][2] = {{~0u, ~0u}, {~0u, ~0u}};
         if constexpr (MASKED) {
             if (!tree) {
@@ -682,6 +692,21 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
                 }
                 const char* st = stage_ptr(u);
                 const bool masked = tree || (i + 1) * TK > nkeys;
+                if (QBW == 2 && !tree && masked) {
+                    // two query blocks a wave (no separate body for full
+                    // tiles): the last tile of a prefix range that ends inside
+                    // it has rows past the range that hold whatever the cache
+                    // slots hold (requested before the prefix length was
+                    // known, or slots the tree range is writing); their scores
+                    // are masked, but 0 times a NaN or infinite V is NaN, so
+                    // those V rows are zeroed here, once, instead of masking V
+                    // in every key block of every tile
+                    const int r0 = nkeys - i * TK;  // the first row past the range, 1 .. TK - 1
+                    for (int e = tid; e < (TK - r0) * DC; e += MF_THREADS)
+                        *(u32x4*)(stage_ptr(u) + TILE_B + (r0 + e / DC) * ROWB + (e % DC) * 16) =
+                            (u32x4){0u, 0u, 0u, 0u};
+                    mf_lds_barrier();
+                }
                 if constexpr (QBW == 1) {
                     // two 16-key blocks at a time; a tile whose keys are all
                     // visible runs the body compiled without mask work; not
@@ -752,24 +777,11 @@ __global__ __launch_bounds__(MF_THREADS) void tree_attn_mfma_kernel(
                         const uint32_t r23 = pack_bf16x2(p4[2] - bf16_lo(h23), p4[3] - bf16_hi(h23));
                         pb[qb] = (u32x4){h01, h23, r01, r23};
                     }
-                    // rows past the prefix in the last tile of a prefix range
-                    // hold whatever the cache slots hold (they were requested
-                    // before the prefix length was known): their probability is
-                    // 0, but 0 times a NaN or infinite V is NaN, so the lane's V
-                    // elements of keys past the range are zeroed (element e of
-                    // the transposed read is key kk0 + e)
-                    uint32_t vkeep_x = ~0u, vkeep_y = ~0u;
-                    if (!tree && masked) {
-                        const int nv = nkeys - (i * TK + kq * KW + kb * 16 + lk * 4);  // the lane's keys in range
-                        vkeep_x = nv >= 2 ? ~0u : nv == 1 ? 0x0000FFFFu : 0u;
-                        vkeep_y = nv >= 4 ? ~0u : nv == 3 ? 0x0000FFFFu : 0u;
-                    }
-                    // O^T += V^T . P^T over the block's 16 keys
+                    // O^T += V^T . P^T over the block's 16 keys (V rows past a
+                    // prefix range were zeroed in LDS when the tile landed)
 #pragma unroll
                     for (int db = 0; db < DB; ++db) {
-                        uint2 v = __builtin_bit_cast(uint2, ds_read_tr16(st + voff[db] + kb * 16 * ROWB));
-                        v.x &= vkeep_x;
-                        v.y &= vkeep_y;
+                        const uint2 v = __builtin_bit_cast(uint2, ds_read_tr16(st + voff[db] + kb * 16 * ROWB));
                         const u32x4 va = (u32x4){v.x, v.y, v.x, v.y};  // the 4 keys' V^T values, twice
 #pragma unroll
                         for (int qb = 0; qb < QBW; ++qb)
