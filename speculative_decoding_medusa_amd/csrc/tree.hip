@@ -176,7 +176,7 @@ __global__ __launch_bounds__(256) void accept_compact_kernel(
     const int32_t* __restrict__ cache_len, int32_t* __restrict__ new_cache_len, T* __restrict__ k_cache,
     T* __restrict__ v_cache, int nKV, int D, int Lmax, int64_t layer_stride, int n_slices, TypicalArgs ta,
     int* __restrict__ status) {
-    __shared__ int s_acc_depth[256];
+    __shared__ int s_best[256 / 64];
     __shared__ int s_par[256], s_tok[256], s_g[256];
     __shared__ int s_path[MEDUSA_MAX_DEPTH_DEV + 1];
     __shared__ int s_L, s_deepest, s_extra;
@@ -209,7 +209,6 @@ __global__ __launch_bounds__(256) void accept_compact_kernel(
             s_g[tid] = pass;
         }
     }
-    if (tid == 0) { s_L = 0; s_deepest = 0; }
     __syncthreads();
     // accepted iff every node on the chain to the root passes its test
     int my = -1;
@@ -223,13 +222,20 @@ __global__ __launch_bounds__(256) void accept_compact_kernel(
         }
         my = ok ? dep : -1;
     }
-    s_acc_depth[tid] = my;
+    // deepest accepted depth, then the lowest node index at that depth: the
+    // largest key depth * 2^16 + (2^16 - 1 - index) over the block (the root
+    // is always accepted at depth 0; nodes not accepted, and threads past N,
+    // hold -1)
+    int key = my >= 0 ? (my << 16) | (0xFFFF - tid) : -1;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) key = max(key, __shfl_xor(key, m, 64));
+    if ((tid & 63) == 0) s_best[tid >> 6] = key;
     __syncthreads();
-    // deepest accepted depth, then the lowest node index at that depth
     if (tid == 0) {
-        int L = 0, deepest = 0;
-        for (int i = 0; i < N; ++i)
-            if (s_acc_depth[i] > L) { L = s_acc_depth[i]; deepest = i; }
+        int best = s_best[0];
+#pragma unroll
+        for (int w = 1; w < 256 / 64; ++w) best = max(best, s_best[w]);
+        const int L = best >> 16, deepest = 0xFFFF - (best & 0xFFFF);
         s_L = L;
         s_deepest = deepest;
         int j = deepest;
