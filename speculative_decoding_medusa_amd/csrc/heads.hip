@@ -204,17 +204,20 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_rows_kernel(
 
 // Final merge: per (b, k) the top-k of the G * topk workgroup candidates.
 // Each thread keeps a sorted register list of the best TK candidates it reads
-// (loads issued eight at a time: one round for up to 2048 candidates); the block then extracts the winners one rank
-// at a time: block-wide argmax of the threads' list heads, the winning thread
-// pops its head.  Candidate rows are distinct (padding entries rank last), so
-// the (value desc, index asc) order is total.
+// (loads issued eight at a time: one round for up to 2048 candidates); each
+// wave then extracts its own top-k rank by rank (wave-wide argmax of the lane
+// list heads, the winning lane pops its head: no workgroup barrier), and wave
+// 0 takes the top-k of the 4 waves' lists, one candidate a lane.  Candidate
+// rows are distinct (padding entries rank last), so the (value desc, index
+// asc) order is total.
 template <int TK>
 __global__ __launch_bounds__(256) void topk_merge_kernel(const float* __restrict__ cand_val,
                                                          const int* __restrict__ cand_idx, int M, int topk,
                                                          int32_t* __restrict__ topk_idx,
                                                          float* __restrict__ topk_val) {
-    __shared__ float wv_s[4];
-    __shared__ int wi_s[4];
+    static_assert(4 * TK <= 64, "the waves' lists fit one wave, a candidate a lane");
+    __shared__ float wv_s[4 * TK];
+    __shared__ int wi_s[4 * TK];
     const int bk = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float* cv = cand_val + (size_t)bk * M;
@@ -239,19 +242,23 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(const float* __restrict
         float bv = lv[0];
         int bi = li[0];
         wave_argmax(bv, bi);
-        if (lane == 0) { wv_s[wave] = bv; wi_s[wave] = bi; }
-        __syncthreads();
-        float gv = wv_s[0];
-        int gi = wi_s[0];
-#pragma unroll
-        for (int w = 1; w < 4; ++w)
-            if (better(wv_s[w], wi_s[w], gv, gi)) { gv = wv_s[w]; gi = wi_s[w]; }
-        if (tid == 0) {
-            topk_idx[(size_t)bk * topk + t] = gi;
-            topk_val[(size_t)bk * topk + t] = gv;
+        if (lane == 0) { wv_s[wave * TK + t] = bv; wi_s[wave * TK + t] = bi; }
+        if (lv[0] == bv && li[0] == bi) sorted_pop<TK>(lv, li);  // the owner pops its head
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    float v = -INFINITY;
+    int i = 0x7FFFFFFF;
+    if (lane < 4 * TK && lane % TK < topk) { v = wv_s[lane]; i = wi_s[lane]; }
+    for (int t = 0; t < topk; ++t) {
+        float bv = v;
+        int bi = i;
+        wave_argmax(bv, bi);
+        if (lane == 0) {
+            topk_idx[(size_t)bk * topk + t] = bi;
+            topk_val[(size_t)bk * topk + t] = bv;
         }
-        if (lv[0] == gv && li[0] == gi) sorted_pop<TK>(lv, li);  // the owner pops its head
-        __syncthreads();
+        if (v == bv && i == bi) { v = -INFINITY; i = 0x7FFFFFFF; }  // the owner drops it
     }
 }
 
