@@ -38,7 +38,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 # calibration (profiles/medusa_step_hbm_counters__vicuna7b_sparse64.txt).
 # Valid only for the kernel sources they were taken on (sha256 prefix of
 # heads.hip + common.hpp); reported as null after any change to them.
-VOCAB_TRAFFIC = {"sources_sha256_16": "73b4ac2fd7b4d9f3", "read_bytes": 1311528142, "write_bytes": 128029}
+VOCAB_TRAFFIC = {"sources_sha256_16": "1f82b2dd370675b9", "read_bytes": 1311538974, "write_bytes": 128027}
 # the same for the gate|up projection of the 32-layer workload (one layer's
 # launch: 64 x 4096 node rows against 22016 packed weight rows, unsplit, the
 # SwiGLU product written in bf16)
