@@ -41,7 +41,7 @@ HEAD_CASES = [
     ("f32_h256_v777_b2_k5", lambda: _cfg("m3", "f32", 2, 256, 777, 3, 5, mi.tiny_tree(), seed=103), "rows"),
     ("bf16_h2048_v4000_b8", lambda: _cfg("m4", "bf16", 8, 2048, 4000, 2, 4, mi.tiny_tree(), seed=104), "rows"),
     # packed W2 (MFMA): 8, 3 and 1 sequences; vocabularies not a multiple of
-    # the 128 rows of a workgroup; top-16
+    # the 256 rows of a workgroup; top-16
     ("packed_h2048_v4000_b8", lambda: _cfg("m4", "bf16", 8, 2048, 4000, 2, 4, mi.tiny_tree(), seed=104), "packed"),
     ("packed_h512_v3001_b3_k6", lambda: _cfg("m2", "bf16", 3, 512, 3001, 2, 6, mi.tiny_tree(), seed=102), "packed"),
     ("packed_h1024_v5003_b1_k16", lambda: _cfg("m5", "bf16", 1, 1024, 5003, 3, 16, mi.tiny_tree(), seed=106),
@@ -470,6 +470,10 @@ NAN_CASES = [
                                              (1, 777, 1000), 221), 2300),
     ("bf16_dense256_d64_b2", lambda: _cfg("n2", "bf16", 2, 256, 10, 5, 3, mi.dense_tree(256), 2, 2, 64,
                                           (70, 513), 222), 600),
+    # the 256-node kernel at head size 128 (two query blocks a wave): the
+    # partial last tiles of both sequences' ranges get their V rows zeroed
+    ("bf16_dense256_d128_b2", lambda: _cfg("n5", "bf16", 2, 256, 10, 5, 3, mi.dense_tree(256), 2, 2, 128,
+                                           (70, 700), 225), 800),
     ("bf16_sparse100_b2", lambda: _cfg("n3", "bf16", 2, 256, 10, 5, 4, mi.sparse_tree(100), 4, 4, 128,
                                        (333, 100), 223), 700),
     ("f32_tiny_b2", lambda: _cfg("n4", "f32", 2, 256, 10, 3, 3, mi.tiny_tree(), 4, 4, 64, (30, 97), 224), 200),
