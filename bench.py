@@ -262,7 +262,7 @@ def main():
     # from 4 sequences on, W1 and W2 in the packed layout of the MFMA head
     # products (packed once, like a weight load); fewer sequences stream the
     # row-major weights through the vector-ALU GEMVs
-    w2_layout = M.PACKED if B >= 4 and wdt == M.BF16 and H % 256 == 0 else M.ROW_MAJOR
+    w2_layout = M.PACKED if B >= 4 and wdt == M.BF16 and H % 128 == 0 else M.ROW_MAJOR
     w1 = M.pack_heads(d.pop("W1")) if w2_layout == M.PACKED else d["W1"]
     w2 = M.pack_heads(d.pop("W2")) if w2_layout == M.PACKED else d["W2"]
     ws_v = torch.empty(M.vocab_topk_workspace_size(B, H, V, K, topk, wdt, w2_layout), dtype=torch.uint8,

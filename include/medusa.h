@@ -78,7 +78,7 @@ const char* medusa_version(void);
  *   h  [B][H] (dt), b1 [K][H] (dt)
  *   w1 head k's square matrix ([out][in]), laid out as w1_layout says:
  *      MEDUSA_ROW_MAJOR: [K][H][H] (dt), streamed by a vector-ALU GEMV;
- *      MEDUSA_PACKED (bf16 only, H a multiple of 128): K packed H x H
+ *      MEDUSA_PACKED (bf16 only, H a multiple of 64): K packed H x H
  *      matrices back to back (head k at byte offset k * medusa_packed_size(H,
  *      H)), streamed through MFMA with the bf16 h rows as exact operands;
  *      the faster choice from B = 4 on.
@@ -96,7 +96,7 @@ medusa_status medusa_resid_silu(const void* h, const void* w1, medusa_layout w1_
  *   w2       head k's projection (no bias), laid out as w2_layout says:
  *            MEDUSA_ROW_MAJOR: [K][V][H] (dt), streamed by a vector-ALU GEMV
  *            (every weight byte meets B <= 8 inputs);
- *            MEDUSA_PACKED (bf16 only, H a multiple of 256): K packed
+ *            MEDUSA_PACKED (bf16 only, H a multiple of 128): K packed
  *            matrices of V rows x H columns back to back, each
  *            medusa_packed_size(V, H) bytes (medusa_pack_rows of head k at
  *            byte offset k * medusa_packed_size(V, H)), streamed through
@@ -141,7 +141,7 @@ medusa_status medusa_heads_forward(const void* h, const void* w1, const void* b1
  * array's device address (make it outside a graph capture).  Returns
  * MEDUSA_EUNSUPPORTED, enqueuing nothing, when
  * medusa_heads_workspace_size(...) exceeds MEDUSA_STATIC_SCRATCH_BYTES
- * (8 sequences x 5 heads x hidden 4096 x vocabulary 128256 need about 3.9
+ * (8 sequences x 5 heads x hidden 4096 x vocabulary 128256 need about 2.0
  * MB).  Allocates nothing: no hipMalloc, no allocating library call.
  * ------------------------------------------------------------------------- */
 #define MEDUSA_STATIC_SCRATCH_BYTES (8u << 20)

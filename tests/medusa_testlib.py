@@ -208,10 +208,10 @@ def lm_head_arg(M, lm_head):
 
 def head_weights_arg(M, W1, W2, B):
     """The heads' W1 and W2 as a step passes them: packed for the MFMA
-    products from 4 sequences on (bf16, H % 256 == 0), else the row-major
+    products from 4 sequences on (bf16, H % 128 == 0), else the row-major
     tensors (vector-ALU GEMVs)."""
     import torch
-    if B >= 4 and W2.dtype == torch.bfloat16 and W2.shape[2] % 256 == 0:
+    if B >= 4 and W2.dtype == torch.bfloat16 and W2.shape[2] % 128 == 0:
         return M.pack_heads(W1), M.pack_heads(W2)
     return W1, W2
 

@@ -96,7 +96,7 @@ def test_heads_argument_errors(M):
     assert st == M.EUNSUPPORTED and "multiple" in L.medusa_last_error().decode()
     st = L.medusa_resid_silu(d, d, M.PACKED, d, 8, 4096, 5, M.F32, d, None)
     assert st == M.EUNSUPPORTED and "bf16" in L.medusa_last_error().decode()
-    # packed w2: bf16 only, H a multiple of 256, a known layout
+    # packed w2: bf16 only, H a multiple of 128, a known layout
     st = L.medusa_vocab_topk(d, d, M.PACKED, 8, 256, 1000, 5, 4, M.F32, None, d, d, d, 1 << 30, None)
     assert st == M.EUNSUPPORTED and "bf16" in L.medusa_last_error().decode()
     st = L.medusa_vocab_topk(d, d, M.PACKED, 8, 4104, 1000, 5, 4, M.BF16, None, d, d, d, 1 << 30, None)
