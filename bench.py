@@ -39,6 +39,10 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 # Valid only for the kernel sources they were taken on (sha256 prefix of
 # heads.hip + common.hpp); reported as null after any change to them.
 VOCAB_TRAFFIC = {"sources_sha256_16": "1f82b2dd370675b9", "read_bytes": 1311538974, "write_bytes": 128027}
+# the same for the packed vocabulary projection of 8 sequences (5 heads x
+# 128256 rows over 4096, the 16 bf16 head/remainder node rows per head)
+# (heads.hip + skinny_mfma.hpp + common.hpp)
+VOCAB_PACKED_TRAFFIC = {"sources_sha256_16": "650c92d5fe0fbada", "read_bytes": 5397281081, "write_bytes": 1286731}
 # the same for the gate|up projection of the 32-layer workload (one layer's
 # launch: 64 x 4096 node rows against 22016 packed weight rows, unsplit, the
 # SwiGLU product written in bf16)
@@ -57,6 +61,10 @@ def _traffic_bytes(rec, sources):
 
 def vocab_traffic_bytes():
     return _traffic_bytes(VOCAB_TRAFFIC, ("heads.hip", "common.hpp"))
+
+
+def vocab_packed_traffic_bytes():
+    return _traffic_bytes(VOCAB_PACKED_TRAFFIC, ("heads.hip", "skinny_mfma.hpp", "common.hpp"))
 
 
 def gate_up_traffic_bytes():
@@ -402,7 +410,8 @@ def main():
     ceiling = read_ceiling()
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": vocab_traffic_bytes() if w2_layout == M.ROW_MAJOR else None, "kernel": vt_name,
+                "traffic": vocab_traffic_bytes() if w2_layout == M.ROW_MAJOR else vocab_packed_traffic_bytes(),
+                "kernel": vt_name,
                 "bytes_per_launch": algo_bytes, "avg_us": round(vt_us, 2),
                 "frac_of_read_ceiling": round(achieved / ceiling["GBs"], 4)}
 
