@@ -38,11 +38,11 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 # calibration (profiles/medusa_step_hbm_counters__vicuna7b_sparse64.txt).
 # Valid only for the kernel sources they were taken on (sha256 prefix of
 # heads.hip + common.hpp); reported as null after any change to them.
-VOCAB_TRAFFIC = {"sources_sha256_16": "1f82b2dd370675b9", "read_bytes": 1311538974, "write_bytes": 128027}
+VOCAB_TRAFFIC = {"sources_sha256_16": "9253b7a5430e4316", "read_bytes": 1311531009, "write_bytes": 128028}
 # the same for the packed vocabulary projection of 8 sequences (5 heads x
 # 128256 rows over 4096, the 16 bf16 head/remainder node rows per head)
 # (heads.hip + skinny_mfma.hpp + common.hpp)
-VOCAB_PACKED_TRAFFIC = {"sources_sha256_16": "650c92d5fe0fbada", "read_bytes": 5397281081, "write_bytes": 1286731}
+VOCAB_PACKED_TRAFFIC = {"sources_sha256_16": "c257469e44fa4189", "read_bytes": 5397341044, "write_bytes": 1286784}
 # the same for the gate|up projection of the 32-layer workload (one layer's
 # launch: 64 x 4096 node rows against 22016 packed weight rows, unsplit, the
 # SwiGLU product written in bf16)
@@ -273,7 +273,7 @@ def main():
     w2_layout = M.PACKED if B >= 4 and wdt == M.BF16 and H % 128 == 0 else M.ROW_MAJOR
     w1 = M.pack_heads(d.pop("W1")) if w2_layout == M.PACKED else d["W1"]
     w2 = M.pack_heads(d.pop("W2")) if w2_layout == M.PACKED else d["W2"]
-    ws_v = torch.empty(M.vocab_topk_workspace_size(B, H, V, K, topk, wdt, w2_layout), dtype=torch.uint8,
+    ws_h = torch.empty(M.heads_workspace_size(B, H, V, K, topk, wdt, w2_layout), dtype=torch.uint8,
                        device="cuda")
     tok = torch.empty(B, N, dtype=torch.int32, device="cuda")
     pos = torch.empty_like(tok)
@@ -298,9 +298,8 @@ def main():
                            device="cuda")
 
     def step():
-        M.medusa_resid_silu(d["h"], w1, d["b1"], z)
-        M.medusa_vocab_topk(z, w2, topk, ti, tv, ws=ws_v)
-        M.medusa_build_tree(tree, ti, root_d, d["cache_len"], tok, pos)
+        M.medusa_heads_forward_tree(d["h"], w1, d["b1"], w2, topk, ti, tv, tree, root_d, d["cache_len"], tok, pos,
+                                    ws=ws_h)
         M.tree_attention_verify(d["q"], d["k_tree"], d["v_tree"], d["k_cache"], d["v_cache"], d["cache_len"], maxP,
                                 tree, o, ws=ws_a)
         if args.typical:
@@ -388,7 +387,7 @@ def main():
 
     st = {
         "heads_resid_silu": stage("resid_silu_gemv", "resid_silu_mfma"),
-        "heads_vocab_topk": stage("vocab_proj_topk", "split_rows", "vocab_proj_topk_mfma", "topk_merge"),
+        "heads_vocab_topk": stage("vocab_proj_topk", "split_rows", "vocab_proj_topk_mfma", "topk_merge", "topk_tree"),
         "build_tree": stage("build_tree"),
         "tree_attention": stage("tree_attn_split", "tree_attn_mfma", "tree_attn_merge"),
         "base_greedy": stage("rmsnorm_rows", "lm_head_argmax", "argmax_merge") +
@@ -440,7 +439,9 @@ def main():
         "kernels_us": {k: round(v, 2) for k, v in kern_us.items()},
         "stages_timing": "second pass, every launch between two HIP events: each time includes its launch's "
                          "dispatch (about 2 us more than the kernel trace for the short kernels), which the "
-                         "unbracketed step overlaps with the previous kernel, so the stages sum above ms_per_step",
+                         "unbracketed step overlaps with the previous kernel, so the stages sum above ms_per_step; "
+                         "the tree is built by the heads' top-k merge workgroups (topk_tree, counted under "
+                         "heads_vocab_topk)",
         "wall_ms_per_step": round(1e3 * wall / args.steps, 4),
         "step_modes": modes,
         "roofline": roofline,
@@ -593,7 +594,7 @@ def bench_decoder(args, cfg):
     z = torch.empty(B, K, H, device="cuda")
     ti = torch.empty(B, K, topk, dtype=torch.int32, device="cuda")
     tv = torch.empty(B, K, topk, device="cuda")
-    ws_v = torch.empty(M.vocab_topk_workspace_size(B, H, V, K, topk, wdt), dtype=torch.uint8, device="cuda")
+    ws_h = torch.empty(M.heads_workspace_size(B, H, V, K, topk, wdt), dtype=torch.uint8, device="cuda")
     tok = torch.empty(B, N, dtype=torch.int32, device="cuda")
     pos = torch.empty_like(tok)
     maxP = max(cfg.P)
@@ -606,9 +607,8 @@ def bench_decoder(args, cfg):
     ncl = torch.empty(B, dtype=torch.int32, device="cuda")
 
     def step():
-        M.medusa_resid_silu(d["h"], d["W1"], d["b1"], z)
-        M.medusa_vocab_topk(z, d["W2"], topk, ti, tv, ws=ws_v)
-        M.medusa_build_tree(tree, ti, root, cache_len, tok, pos)
+        M.medusa_heads_forward_tree(d["h"], d["W1"], d["b1"], d["W2"], topk, ti, tv, tree, root, cache_len, tok, pos,
+                                    ws=ws_h)
         M.medusa_decoder_verify(layers, emb, lm_head, tree, tok, pos, cache_len, maxP, k_cache, v_cache, cfg.nH, g,
                                 ws=ws_d)
         M.medusa_accept(tree, tok, g, al, an, ot, cache_len, ncl, k_cache=k_cache, v_cache=v_cache)
@@ -661,7 +661,7 @@ def bench_decoder(args, cfg):
     kv_bytes = L * B * cfg.nKV * (2 * maxP * cfg.D * 2)
     verify_bytes = L * w_layer + kv_bytes + V * H * 2
     verify_us = sum(v for k, v in per_step_us.items() if k not in ("resid_silu_gemv", "vocab_proj_topk", "topk_merge",
-                                                                    "build_tree", "accept_compact"))
+                                                                    "topk_tree", "build_tree", "accept_compact"))
     result = {
         "metric": METRIC,
         "value": round(1000.0 / ms_graph, 2),

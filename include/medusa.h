@@ -204,6 +204,26 @@ medusa_status medusa_build_tree(const medusa_tree* tree, const int32_t* topk_idx
                                 int32_t* node_tok, int32_t* node_pos, uint64_t* anc_mask, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Steps a1 + a2 + a3 in one call (heads page; tree section: the tree is the
+ * Cartesian product of the heads' top guesses): medusa_heads_forward, then
+ * medusa_build_tree on the top-k it chose, without the tree build's own
+ * launch: the merge workgroup of head k (one per sequence and head) also
+ * writes the tree nodes at depth k + 1, whose tokens are that head's
+ * choices, and head 0's the root.  Arguments as medusa_heads_forward (the
+ * same workspace size) and as medusa_build_tree (the tree, root_tok,
+ * cache_len, node_tok, node_pos and the optional anc_mask); every output
+ * equals what those two calls write.  Errors: those of either call; on
+ * error nothing is enqueued.
+ * ------------------------------------------------------------------------- */
+medusa_status medusa_heads_forward_tree(const void* h, const void* w1, const void* b1, const void* w2,
+                                        medusa_layout layout,
+                                        int B, int H, int V, int K, int topk, medusa_dtype dt,
+                                        float* logits, int32_t* topk_idx, float* topk_val,
+                                        const medusa_tree* tree, const int32_t* root_tok,
+                                        const int32_t* cache_len, int32_t* node_tok, int32_t* node_pos,
+                                        uint64_t* anc_mask, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Step a4 -- tree-masked attention (tree section: all candidates appended in
  * one pass; each token sees only its ancestors -- and itself).
  *   q [B][N][nH][D], k_tree / v_tree [B][N][nKV][D] (dt)

@@ -46,6 +46,8 @@ _SIGS = {
     "medusa_tree_mask_host": ([_vp, _vp, _sz], _i32),
     "medusa_tree_status": ([_vp, ctypes.POINTER(ctypes.c_int32), _i32, _vp], _i32),
     "medusa_build_tree": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp], _i32),
+    "medusa_heads_forward_tree": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
+                                   _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
     "tree_attention_workspace_size": ([_vp, _i32, _i32, _i32, _i32, _i32], _sz),
     "tree_attention_verify": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                                _vp, _vp, _sz, _vp], _i32),
@@ -257,6 +259,24 @@ class Tree:
 
 
 _deferred_trees = []  # tree handles released during a graph capture, freed at the next release outside one
+
+
+def medusa_heads_forward_tree(h, w1, b1, w2, topk, topk_idx, topk_val, tree: Tree, root_tok, cache_len, node_tok,
+                              node_pos, anc_mask=None, logits=None, ws=None, stream=None):
+    """medusa_heads_forward and medusa_build_tree in one call (the tree built by
+    the top-k merge's workgroups); arguments as those two."""
+    K, V, H = w2.shape
+    B = h.shape[0]
+    if w1 is not None:
+        assert isinstance(w1, Packed) == isinstance(w2, Packed), "w1 and w2 must share one layout"
+    layout, dt = _w_args(w2)
+    need = heads_workspace_size(B, H, V, K, topk, dt, layout)
+    ws = _ws(need, h.device, ws)
+    _check("medusa_heads_forward_tree", _lib.medusa_heads_forward_tree(
+        _p(h), _p(w1), _p(b1), _p(w2), layout, B, H, V, K, topk, dt, _p(logits), _p(topk_idx), _p(topk_val),
+        tree.handle, _p(root_tok), _p(cache_len), _p(node_tok), _p(node_pos), _p(anc_mask), _p(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
+    return node_tok, node_pos
 
 
 def medusa_build_tree(tree: Tree, topk_idx, root_tok, cache_len, node_tok, node_pos, anc_mask=None, stream=None):

@@ -31,6 +31,12 @@ void launch_resid_silu_packed(const void* h, const void* w1p, const void* b1, in
 size_t vocab_topk_packed_ws_bytes(int B, int H, int V, int K, int topk);
 void launch_vocab_topk_packed(const float* z, const void* w2p, int B, int H, int V, int K, int topk, float* logits,
                               int32_t* topk_idx, float* topk_val, void* ws, hipStream_t s);
+void launch_vocab_topk_tree(const float* z, const void* w2, int B, int H, int V, int K, int topk, bool bf16,
+                            float* logits, int32_t* topk_idx, float* topk_val, float* cv, int* ci,
+                            const TreeBuild& tb, hipStream_t s);
+void launch_vocab_topk_packed_tree(const float* z, const void* w2p, int B, int H, int V, int K, int topk,
+                                   float* logits, int32_t* topk_idx, float* topk_val, void* ws, const TreeBuild& tb,
+                                   hipStream_t s);
 size_t resid_silu_lds_bytes(int B, int H);
 void launch_build_tree(const TreeDev& t, const int32_t* topk_idx, int K, int topk, const int32_t* root_tok,
                        const int32_t* cache_len, int B, int32_t* node_tok, int32_t* node_pos, uint64_t* anc_mask,
@@ -310,17 +316,22 @@ static void check_vocab(int B, int H, int V, int K, int topk, medusa_dtype dt, m
     }
 }
 
+// tb: build the candidate tree in the merge's launch (null: the merge alone)
 static void run_vocab_topk(const float* z, const void* w2, medusa_layout w2_layout, int B, int H, int V, int K,
                            int topk, medusa_dtype dt, float* logits, int32_t* topk_idx, float* topk_val, void* ws,
-                           hipStream_t s) {
+                           hipStream_t s, const TreeBuild* tb = nullptr) {
     if (w2_layout == MEDUSA_PACKED) {
-        launch_vocab_topk_packed(z, w2, B, H, V, K, topk, logits, topk_idx, topk_val, ws, s);
+        if (tb) launch_vocab_topk_packed_tree(z, w2, B, H, V, K, topk, logits, topk_idx, topk_val, ws, *tb, s);
+        else launch_vocab_topk_packed(z, w2, B, H, V, K, topk, logits, topk_idx, topk_val, ws, s);
         return;
     }
     float* cv;
     int* ci;
     carve_vocab_ws(ws, B, V, K, topk, &cv, &ci);
-    launch_vocab_topk(z, w2, B, H, V, K, topk, dt == MEDUSA_BF16, logits, topk_idx, topk_val, cv, ci, s);
+    if (tb)
+        launch_vocab_topk_tree(z, w2, B, H, V, K, topk, dt == MEDUSA_BF16, logits, topk_idx, topk_val, cv, ci, *tb, s);
+    else
+        launch_vocab_topk(z, w2, B, H, V, K, topk, dt == MEDUSA_BF16, logits, topk_idx, topk_val, cv, ci, s);
 }
 
 medusa_status medusa_vocab_topk(const float* z, const void* w2, medusa_layout w2_layout, int B, int H, int V, int K,
@@ -370,6 +381,50 @@ medusa_status medusa_heads_forward(const void* h, const void* w1, const void* b1
             MEDUSA_LAUNCH("broadcast_h", broadcast_h_kernel, dim3(64), dim3(256), 0, s, h, B, H, K,
                           dt == MEDUSA_BF16 ? 1 : 0, z);
         run_vocab_topk(z, w2, w2_layout, B, H, V, K, topk, dt, logits, topk_idx, topk_val, vws, s);
+    });
+}
+
+// the checks medusa_build_tree makes of a tree against K and topk
+static void check_tree_for_heads(const medusa_tree* tree, int K, int topk) {
+    REQUIRE(K >= tree->t.max_depth, "K=%d is smaller than the tree depth %d", K, tree->t.max_depth);
+    REQUIRE(topk > tree->t.max_rank, "topk=%d does not cover rank %d", topk, tree->t.max_rank);
+    SUPPORT(tree->t.max_depth * (tree->t.max_rank + 1) <= MEDUSA_MAX_DEPTH * MEDUSA_MAX_TOPK,
+            "tree depth %d x ranks %d: more than %d candidates", tree->t.max_depth, tree->t.max_rank + 1,
+            MEDUSA_MAX_DEPTH * MEDUSA_MAX_TOPK);
+}
+
+medusa_status medusa_heads_forward_tree(const void* h, const void* w1, const void* b1, const void* w2,
+                                        medusa_layout layout, int B, int H, int V, int K, int topk, medusa_dtype dt,
+                                        float* logits, int32_t* topk_idx, float* topk_val, const medusa_tree* tree,
+                                        const int32_t* root_tok, const int32_t* cache_len, int32_t* node_tok,
+                                        int32_t* node_pos, uint64_t* anc_mask, void* ws, size_t ws_bytes,
+                                        void* stream) {
+    const medusa_layout w2_layout = layout;
+    return guarded("medusa_heads_forward_tree", [&] {
+        check_vocab(B, H, V, K, topk, dt, w2_layout);
+        if (w1) check_w1_layout(H, dt, layout);
+        REQUIRE(h && w2 && topk_idx && topk_val && ws, "null pointer argument");
+        REQUIRE(tree && root_tok && cache_len && node_tok && node_pos, "null pointer argument");
+        REQUIRE((w1 == nullptr) == (b1 == nullptr), "w1 and b1 must both be given or both be NULL");
+        check_tree_for_heads(tree, K, topk);
+        const size_t need = medusa_heads_workspace_size(B, H, V, K, topk, dt, w2_layout);
+        REQUIRE(ws_bytes >= need, "workspace too small: %zu < %zu", ws_bytes, need);
+        float* z = (float*)ws;
+        void* vws = (char*)ws + align256((size_t)B * K * H * 4);
+        hipStream_t s = (hipStream_t)stream;
+        if (w1)
+            run_resid_silu(h, w1, layout, b1, B, H, K, dt, z, s);
+        else
+            MEDUSA_LAUNCH("broadcast_h", broadcast_h_kernel, dim3(64), dim3(256), 0, s, h, B, H, K,
+                          dt == MEDUSA_BF16 ? 1 : 0, z);
+        TreeBuild tb;
+        tb.t = &tree->t;
+        tb.root_tok = root_tok;
+        tb.cache_len = cache_len;
+        tb.node_tok = node_tok;
+        tb.node_pos = node_pos;
+        tb.anc_mask = anc_mask;
+        run_vocab_topk(z, w2, w2_layout, B, H, V, K, topk, dt, logits, topk_idx, topk_val, vws, s, &tb);
     });
 }
 
@@ -545,11 +600,7 @@ medusa_status medusa_build_tree(const medusa_tree* tree, const int32_t* topk_idx
     return guarded("medusa_build_tree", [&] {
         REQUIRE(tree && topk_idx && root_tok && cache_len && node_tok && node_pos, "null pointer argument");
         REQUIRE(B >= 1, "B must be >= 1");
-        REQUIRE(K >= tree->t.max_depth, "K=%d is smaller than the tree depth %d", K, tree->t.max_depth);
-        REQUIRE(topk > tree->t.max_rank, "topk=%d does not cover rank %d", topk, tree->t.max_rank);
-        SUPPORT(tree->t.max_depth * (tree->t.max_rank + 1) <= MEDUSA_MAX_DEPTH * MEDUSA_MAX_TOPK,
-                "tree depth %d x ranks %d: more than %d candidates", tree->t.max_depth, tree->t.max_rank + 1,
-                MEDUSA_MAX_DEPTH * MEDUSA_MAX_TOPK);
+        check_tree_for_heads(tree, K, topk);
         launch_build_tree(tree->t, topk_idx, K, topk, root_tok, cache_len, B, node_tok, node_pos, anc_mask,
                           (hipStream_t)stream);
     });

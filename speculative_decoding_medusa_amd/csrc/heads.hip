@@ -21,6 +21,7 @@
 
 #include "common.hpp"
 #include "skinny_mfma.hpp"
+#include "tree.hpp"
 
 namespace medusa {
 
@@ -210,11 +211,26 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_rows_kernel(
 // 0 takes the top-k of the 4 waves' lists, one candidate a lane.  Candidate
 // rows are distinct (padding entries rank last), so the (value desc, index
 // asc) order is total.
+// With a tree (node_tok not null) the workgroup of (b, k) also writes the
+// tree nodes that take their token from head k, those at depth k + 1
+// (node_tok = its rank-th choice, node_pos = P + depth), and the workgroup of
+// head 0 the root (node_tok = root_tok[b], node_pos = P); (0, 0) copies the
+// ancestor mask.  No node depends on another head, so the tree build needs no
+// launch of its own.
 template <int TK>
 __global__ __launch_bounds__(256) void topk_merge_kernel(const float* __restrict__ cand_val,
                                                          const int* __restrict__ cand_idx, int M, int topk,
                                                          int32_t* __restrict__ topk_idx,
-                                                         float* __restrict__ topk_val) {
+                                                         float* __restrict__ topk_val, int K = 1,
+                                                         const int* __restrict__ depth = nullptr,
+                                                         const int* __restrict__ rank = nullptr,
+                                                         const uint64_t* __restrict__ mask = nullptr, int N = 0,
+                                                         int W = 0, const int32_t* __restrict__ root_tok = nullptr,
+                                                         const int32_t* __restrict__ cache_len = nullptr,
+                                                         int32_t* __restrict__ node_tok = nullptr,
+                                                         int32_t* __restrict__ node_pos = nullptr,
+                                                         uint64_t* __restrict__ anc_mask = nullptr) {
+    __shared__ int top_s[TK];
     static_assert(4 * TK <= 64, "the waves' lists fit one wave, a candidate a lane");
     __shared__ float wv_s[4 * TK];
     __shared__ int wi_s[4 * TK];
@@ -246,20 +262,60 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(const float* __restrict
         if (lv[0] == bv && li[0] == bi) sorted_pop<TK>(lv, li);  // the owner pops its head
     }
     __syncthreads();
-    if (wave != 0) return;
-    float v = -INFINITY;
-    int i = 0x7FFFFFFF;
-    if (lane < 4 * TK && lane % TK < topk) { v = wv_s[lane]; i = wi_s[lane]; }
-    for (int t = 0; t < topk; ++t) {
-        float bv = v;
-        int bi = i;
-        wave_argmax(bv, bi);
-        if (lane == 0) {
-            topk_idx[(size_t)bk * topk + t] = bi;
-            topk_val[(size_t)bk * topk + t] = bv;
+    if (wave == 0) {
+        float v = -INFINITY;
+        int i = 0x7FFFFFFF;
+        if (lane < 4 * TK && lane % TK < topk) { v = wv_s[lane]; i = wi_s[lane]; }
+        for (int t = 0; t < topk; ++t) {
+            float bv = v;
+            int bi = i;
+            wave_argmax(bv, bi);
+            if (lane == 0) {
+                topk_idx[(size_t)bk * topk + t] = bi;
+                topk_val[(size_t)bk * topk + t] = bv;
+                top_s[t] = bi;
+            }
+            if (v == bv && i == bi) { v = -INFINITY; i = 0x7FFFFFFF; }  // the owner drops it
         }
-        if (v == bv && i == bi) { v = -INFINITY; i = 0x7FFFFFFF; }  // the owner drops it
     }
+    if (node_tok == nullptr) return;
+    // the tree nodes of head k (see above)
+    const int b = bk / K, k = bk - b * K;
+    if (bk == 0 && anc_mask != nullptr)
+        for (int e = tid; e < N * W; e += 256) anc_mask[e] = mask[e];
+    __syncthreads();
+    const int P = cache_len[b];
+    for (int n = tid; n < N; n += 256) {
+        const int d = depth[n];
+        if (d == k + 1) {
+            node_tok[(size_t)b * N + n] = top_s[rank[n]];
+            node_pos[(size_t)b * N + n] = P + d;
+        } else if (d == 0 && k == 0) {
+            node_tok[(size_t)b * N + n] = root_tok[b];
+            node_pos[(size_t)b * N + n] = P;
+        }
+    }
+}
+
+void launch_topk_merge(const float* cv, const int* ci, int BK, int M, int topk, int32_t* topk_idx,
+                       float* topk_val, hipStream_t s, const char* merge_name);
+
+// the per-head merge of the workgroup candidates, alone or with the tree build
+static void launch_merge(const float* cv, const int* ci, int B, int K, int M, int topk, int32_t* topk_idx,
+                         float* topk_val, const TreeBuild* tb, hipStream_t s, const char* merge_name) {
+    if (tb == nullptr) {
+        launch_topk_merge(cv, ci, B * K, M, topk, topk_idx, topk_val, s, merge_name);
+        return;
+    }
+    const TreeDev& t = *tb->t;
+#define MEDUSA_TOPK_TREE(TK)                                                                                    \
+    MEDUSA_LAUNCH("topk_tree", topk_merge_kernel<TK>, dim3(B * K), dim3(256), 0, s, cv, ci, M, topk, topk_idx, \
+                  topk_val, K, t.depth, t.rank, t.mask, t.N, t.W, tb->root_tok, tb->cache_len, tb->node_tok,   \
+                  tb->node_pos, tb->anc_mask)
+    if (topk <= 4) MEDUSA_TOPK_TREE(4);
+    else if (topk <= 8) MEDUSA_TOPK_TREE(8);
+    else MEDUSA_TOPK_TREE(16);
+#undef MEDUSA_TOPK_TREE
 }
 
 // ---------------------------------------------------------------------------
@@ -409,9 +465,9 @@ void launch_topk_merge(const float* cv, const int* ci, int BK, int M, int topk, 
                       topk_val);
 }
 
-void launch_vocab_topk_named(const float* z, const void* w2, int B, int H, int V, int K, int topk, bool bf16,
-                             float* logits, int32_t* topk_idx, float* topk_val, float* cv, int* ci, hipStream_t s,
-                             const char* gemv_name, const char* merge_name) {
+static void vocab_topk_impl(const float* z, const void* w2, int B, int H, int V, int K, int topk, bool bf16,
+                            float* logits, int32_t* topk_idx, float* topk_val, float* cv, int* ci, hipStream_t s,
+                            const char* gemv_name, const char* merge_name, const TreeBuild* tb) {
     const int PER = bf16 ? 8 : 4;
     const int NB = pick_nb(B), CPL = pick_cpl(H / PER);
     const GemvShape sh = topk_shape(NB);
@@ -427,7 +483,21 @@ void launch_vocab_topk_named(const float* z, const void* w2, int B, int H, int V
     } while (0)
     if (sh.R == 2) MEDUSA_TOPK_GO(2, 8, 1, 2); else if (sh.R == 4) MEDUSA_TOPK_GO(4, 4, 4); else MEDUSA_TOPK_GO(8, 4, 8);
 #undef MEDUSA_TOPK_GO
-    launch_topk_merge(cv, ci, B * K, pl.G * topk, topk, topk_idx, topk_val, s, merge_name);
+    launch_merge(cv, ci, B, K, pl.G * topk, topk, topk_idx, topk_val, tb, s, merge_name);
+}
+
+void launch_vocab_topk_named(const float* z, const void* w2, int B, int H, int V, int K, int topk, bool bf16,
+                             float* logits, int32_t* topk_idx, float* topk_val, float* cv, int* ci, hipStream_t s,
+                             const char* gemv_name, const char* merge_name) {
+    vocab_topk_impl(z, w2, B, H, V, K, topk, bf16, logits, topk_idx, topk_val, cv, ci, s, gemv_name, merge_name,
+                    nullptr);
+}
+
+void launch_vocab_topk_tree(const float* z, const void* w2, int B, int H, int V, int K, int topk, bool bf16,
+                            float* logits, int32_t* topk_idx, float* topk_val, float* cv, int* ci,
+                            const TreeBuild& tb, hipStream_t s) {
+    vocab_topk_impl(z, w2, B, H, V, K, topk, bf16, logits, topk_idx, topk_val, cv, ci, s, "vocab_proj_topk",
+                    "topk_merge", &tb);
 }
 
 // ---------------------------------------------------------------------------
@@ -474,8 +544,9 @@ size_t vocab_topk_packed_ws_bytes(int B, int H, int V, int K, int topk) {
     return a256h((size_t)K * 16 * H * 2) + 2 * a256h(cand * 4);
 }
 
-void launch_vocab_topk_packed(const float* z, const void* w2p, int B, int H, int V, int K, int topk, float* logits,
-                              int32_t* topk_idx, float* topk_val, void* ws, hipStream_t s) {
+static void vocab_topk_packed_impl(const float* z, const void* w2p, int B, int H, int V, int K, int topk,
+                                   float* logits, int32_t* topk_idx, float* topk_val, void* ws, const TreeBuild* tb,
+                                   hipStream_t s) {
     const int G = vocab_topk_packed_groups(V);
     const size_t cand = (size_t)B * K * G * topk;
     bf16_t* zs = (bf16_t*)ws;
@@ -486,7 +557,18 @@ void launch_vocab_topk_packed(const float* z, const void* w2p, int B, int H, int
     MEDUSA_LAUNCH("vocab_proj_topk_mfma", (skinny_mfma_kernel<1, SKINNY_TOPK, VT_WAVES, VT_RB>), dim3(G, K),
                   dim3(VT_WAVES * 64), 0, s, zs, (const bf16_t*)w2p, 16, H, V, H / LmhCfg<1, VT_WAVES>::KC, cv, ci,
                   logits, -1.f, topk, B, (long long)16 * H, w_stride);
-    launch_topk_merge(cv, ci, B * K, G * topk, topk, topk_idx, topk_val, s, "topk_merge");
+    launch_merge(cv, ci, B, K, G * topk, topk, topk_idx, topk_val, tb, s, "topk_merge");
+}
+
+void launch_vocab_topk_packed(const float* z, const void* w2p, int B, int H, int V, int K, int topk, float* logits,
+                              int32_t* topk_idx, float* topk_val, void* ws, hipStream_t s) {
+    vocab_topk_packed_impl(z, w2p, B, H, V, K, topk, logits, topk_idx, topk_val, ws, nullptr, s);
+}
+
+void launch_vocab_topk_packed_tree(const float* z, const void* w2p, int B, int H, int V, int K, int topk,
+                                   float* logits, int32_t* topk_idx, float* topk_val, void* ws, const TreeBuild& tb,
+                                   hipStream_t s) {
+    vocab_topk_packed_impl(z, w2p, B, H, V, K, topk, logits, topk_idx, topk_val, ws, &tb, s);
 }
 
 // Residual-SiLU block over packed W1 on MFMA (several sequences): the bf16

@@ -22,6 +22,18 @@ struct TreeDev {
     std::vector<uint64_t> h_mask;
 };
 
+// What the per-head top-k merge needs to build the candidate tree in the same
+// launch (medusa_heads_forward_tree): the tree, the sequences' root tokens and
+// prefix lengths, and the outputs of the tree build.
+struct TreeBuild {
+    const TreeDev* t = nullptr;
+    const int32_t* root_tok = nullptr;   // [B]
+    const int32_t* cache_len = nullptr;  // [B]
+    int32_t* node_tok = nullptr;         // [B][N]
+    int32_t* node_pos = nullptr;         // [B][N]
+    uint64_t* anc_mask = nullptr;        // [N][W], may be null
+};
+
 // per-depth alphas of the planted continuation (depth d uses a[min(d, 15)])
 struct PlantAlphas {
     float a[16];

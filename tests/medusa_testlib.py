@@ -217,9 +217,10 @@ def head_weights_arg(M, W1, W2, B):
 
 
 def run_step_gpu(M, cfg, heads, att, root):
-    """Upload the workload, run resid_silu -> vocab_topk -> build_tree ->
-    tree_attention_verify -> base_greedy -> accept (with compaction) once and
-    return host copies of every output."""
+    """Upload the workload, run the heads with the tree build (the one call
+    bench.py times) -> tree_attention_verify -> base_greedy -> accept (with
+    compaction) once and return host copies of every output; z comes from a
+    separate medusa_resid_silu call on the same inputs."""
     import torch
     d = {k: dev(v) for k, v in {**heads, **att}.items()}
     B, K, H, V, N, topk = cfg.B, cfg.K, cfg.H, cfg.V, cfg.N, cfg.topk
@@ -231,8 +232,7 @@ def run_step_gpu(M, cfg, heads, att, root):
     tv = torch.empty(B, K, topk, device="cuda")
     w1, w2 = head_weights_arg(M, d["W1"], d["W2"], B)
     w2_layout = M.PACKED if isinstance(w2, M.Packed) else M.ROW_MAJOR
-    ws_v = torch.empty(M.vocab_topk_workspace_size(B, H, V, K, topk, wdt, w2_layout), dtype=torch.uint8,
-                       device="cuda")
+    ws_h = torch.empty(M.heads_workspace_size(B, H, V, K, topk, wdt, w2_layout), dtype=torch.uint8, device="cuda")
     tok = torch.empty(B, N, dtype=torch.int32, device="cuda")
     pos = torch.empty_like(tok)
     o = torch.empty_like(d["q"])
@@ -247,8 +247,8 @@ def run_step_gpu(M, cfg, heads, att, root):
     ot = torch.empty_like(an)
     ncl = torch.empty(B, dtype=torch.int32, device="cuda")
     M.medusa_resid_silu(d["h"], w1, d["b1"], z)
-    M.medusa_vocab_topk(z, w2, topk, ti, tv, ws=ws_v)
-    M.medusa_build_tree(tree, ti, dev(root), d["cache_len"], tok, pos)
+    M.medusa_heads_forward_tree(d["h"], w1, d["b1"], w2, topk, ti, tv, tree, dev(root), d["cache_len"], tok, pos,
+                                ws=ws_h)
     M.tree_attention_verify(d["q"], d["k_tree"], d["v_tree"], d["k_cache"], d["v_cache"], d["cache_len"], maxP, tree, o,
                             ws=ws_a)
     M.medusa_base_greedy(o, lm, g, ws=ws_g)

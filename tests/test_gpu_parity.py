@@ -82,6 +82,56 @@ def test_heads_parity(M, name, mk, layout):
     assert torch.equal(ti, ti2) and torch.equal(tv, tv2)
 
 
+# heads and tree build in one call (the merge workgroup of head k writes the
+# nodes at depth k + 1): the same top-k bits as medusa_heads_forward and the
+# same tree as medusa_build_tree on it; several sequences, both layouts, top-k
+# up to 16
+HEADS_TREE_CASES = [
+    ("rows_b1_sparse64", "rows", 1, 1024, 5003, 5, 4, lambda: mi.sparse_tree(64)),
+    ("rows_b3_dense256_k3", "rows", 3, 512, 3001, 5, 3, lambda: mi.dense_tree(256)),
+    ("packed_b8_sparse64", "packed", 8, 1024, 4000, 5, 4, lambda: mi.sparse_tree(64)),
+    ("packed_b4_tiny_k16", "packed", 4, 512, 2000, 3, 16, lambda: mi.tiny_tree()),
+    ("rows_b2_tiny_k3", "rows", 2, 256, 777, 3, 3, lambda: mi.tiny_tree()),
+]
+
+
+@pytest.mark.parametrize("name,layout,B,H,V,K,k,tree_fn", HEADS_TREE_CASES, ids=[c[0] for c in HEADS_TREE_CASES])
+def test_heads_forward_tree_matches_two_calls(M, name, layout, B, H, V, K, k, tree_fn):
+    cfg = _cfg("ht", "bf16", B, H, V, K, k, tree_fn(), seed=261)
+    _say("heads + tree in one call", name)
+    heads = mi.gen_heads(cfg)
+    h, W1, b1, W2 = (dev(heads[x]) for x in ("h", "W1", "b1", "W2"))
+    if layout == "packed":
+        W1, W2 = M.pack_heads(W1), M.pack_heads(W2)
+    parent, rank = cfg.tree.arrays()
+    t = M.Tree(parent, rank, K, k)
+    g = np.random.default_rng(262)
+    root = dev(g.integers(0, V, B).astype(np.int32))
+    cache_len = dev(g.integers(0, 1000, B).astype(np.int32))
+    N, W = t.N, (t.N + 63) // 64
+    ti = torch.empty(B, K, k, dtype=torch.int32, device="cuda")
+    tv = torch.empty(B, K, k, device="cuda")
+    M.medusa_heads_forward(h, W1, b1, W2, k, ti, tv)
+    tok = torch.empty(B, N, dtype=torch.int32, device="cuda")
+    pos = torch.empty_like(tok)
+    mask = torch.zeros(N * W, dtype=torch.int64, device="cuda")
+    M.medusa_build_tree(t, ti, root, cache_len, tok, pos, mask)
+    ti2 = torch.full_like(ti, -7)
+    tv2 = torch.full_like(tv, -7.0)
+    tok2 = torch.full_like(tok, -7)
+    pos2 = torch.full_like(pos, -7)
+    mask2 = torch.full_like(mask, -7)
+    M.medusa_heads_forward_tree(h, W1, b1, W2, k, ti2, tv2, t, root, cache_len, tok2, pos2, mask2)
+    torch.cuda.synchronize()
+    assert torch.equal(ti, ti2) and torch.equal(tv, tv2)
+    assert torch.equal(tok, tok2) and torch.equal(pos, pos2) and torch.equal(mask, mask2)
+    # and without the mask output
+    tok3 = torch.full_like(tok, -7)
+    M.medusa_heads_forward_tree(h, W1, b1, W2, k, ti2, tv2, t, root, cache_len, tok3, pos2)
+    torch.cuda.synchronize()
+    assert torch.equal(tok, tok3)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "bf16_packed"])
 def test_zero_init_heads_reproduce_lm_head_bitwise(M, dtype):
     # heads page sketch: W1 = 0, b1 = 0, W2 = copy of lm_head => every head's
@@ -636,6 +686,15 @@ def test_topk_ties_keep_lower_index(M, layout, spread):
         n = min(len(order[k]), cfg.topk)
         assert len(set(val[0, k, :n].tolist())) == 1, (k, val[0, k])
     assert np.array_equal(got, idx_ref)
+    # the merge that also builds the tree keeps the same rule
+    parent, rank = cfg.tree.arrays()
+    t = M.Tree(parent, rank, cfg.K, cfg.topk)
+    tok = torch.empty(B, t.N, dtype=torch.int32, device="cuda")
+    pos = torch.empty_like(tok)
+    zero = dev(np.zeros(B, np.int32))
+    M.medusa_heads_forward_tree(h, W1, b1, W2, cfg.topk, ti, tv, t, zero, zero, tok, pos)
+    torch.cuda.synchronize()
+    assert np.array_equal(ti.cpu().numpy(), idx_ref)
 
 
 @pytest.mark.parametrize("R", [64, 256, 512], ids=["r64", "r256", "r512"])  # 256, 512: 32 x 32 x 16 with loader waves
