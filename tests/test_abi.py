@@ -90,6 +90,17 @@ def test_heads_argument_errors(M):
     assert st == M.EINVAL and "workspace" in L.medusa_last_error().decode()
     st = L.medusa_heads_forward(d, d, None, d, M.ROW_MAJOR, 1, 4096, 32000, 5, 4, M.BF16, None, d, d, d, 1 << 30, None)
     assert st == M.EINVAL and "both" in L.medusa_last_error().decode()
+    # the heads with the tree build: the tree and its outputs are required,
+    # and the heads' checks come first
+    st = L.medusa_heads_forward_tree(d, d, d, d, M.ROW_MAJOR, 1, 4096, 32000, 5, 4, M.BF16, None, d, d, None, d, d,
+                                     d, d, None, d, 1 << 30, None)
+    assert st == M.EINVAL and "null" in L.medusa_last_error().decode()
+    st = L.medusa_heads_forward_tree(d, d, d, d, M.ROW_MAJOR, 1, 4096, 32000, 5, 4, M.BF16, None, d, d, d, d, d,
+                                     None, d, None, d, 1 << 30, None)
+    assert st == M.EINVAL and "null" in L.medusa_last_error().decode()
+    st = L.medusa_heads_forward_tree(d, d, d, d, M.ROW_MAJOR, 1, 4096, 32000, 5, 17, M.BF16, None, d, d, d, d, d,
+                                     d, d, None, d, 1 << 30, None)
+    assert st == M.EUNSUPPORTED
     st = L.medusa_resid_silu(d, d, M.ROW_MAJOR, d, 1, 4096, 5, 7, d, None)
     assert st == M.EINVAL
     st = L.medusa_resid_silu(d, d, M.PACKED, d, 8, 4104, 5, M.BF16, d, None)
