@@ -18,7 +18,7 @@ from __future__ import annotations
 import torch
 
 from . import (Packed, Tree, _ws, chain_tree, decoder_workspace_size, heads_workspace_size, medusa_accept,
-               medusa_accept_stats, medusa_advance, medusa_build_tree, medusa_decoder_verify, medusa_heads_forward,
+               medusa_accept_stats, medusa_advance, medusa_decoder_verify, medusa_heads_forward_tree,
                medusa_plant_greedy, medusa_prefill, ROW_MAJOR, PACKED, BF16, F32)
 
 
@@ -148,10 +148,9 @@ class MedusaLoop:
 
     def _enqueue(self, stream):
         hd = self.heads
-        medusa_heads_forward(self.h, hd.get("w1"), hd.get("b1"), hd["w2"], self.topk, self.topk_idx, self.topk_val,
-                             ws=self.ws_heads, stream=stream)
-        medusa_build_tree(self.tree, self.topk_idx, self.root_tok, self.cache_len, self.node_tok, self.node_pos,
-                          stream=stream)
+        medusa_heads_forward_tree(self.h, hd.get("w1"), hd.get("b1"), hd["w2"], self.topk, self.topk_idx,
+                                  self.topk_val, self.tree, self.root_tok, self.cache_len, self.node_tok, self.node_pos,
+                                  ws=self.ws_heads, stream=stream)
         medusa_decoder_verify(self.layers, self.embedding, self.lm_head, self.tree, self.node_tok, self.node_pos,
                               self.cache_len, self.max_cache_len, self.k_cache, self.v_cache, self.nH, self.greedy,
                               hidden=self.hidden, rms_eps=self.rms_eps, rope_base=self.rope_base, ws=self.ws_dec,
