@@ -76,6 +76,51 @@ __global__ __launch_bounds__(256) void rmsnorm_f32_bf16_kernel(const float* __re
     }
 }
 
+// The pass's first per-row work in one launch, one block per node row r:
+// x[r] = embedding[tok[r]] (fp32; ids outside [0, V) read row 0), n[r] =
+// bf16(x[r] * rsqrt(mean(x[r]^2) + eps)) with the sum taken in the order of
+// rmsnorm_f32_bf16_kernel (so n is bitwise that kernel's), and the row's
+// angle table cs[r][i] = (cos, sin) of pos[r] * base^(-2i/D) in double, as
+// rope_table_kernel computes it.
+__global__ __launch_bounds__(256) void embed_norm_rope_kernel(const int32_t* __restrict__ tok,
+                                                              const bf16_t* __restrict__ E, int H, int V, float eps,
+                                                              const int32_t* __restrict__ pos, int D,
+                                                              double log2_base, float* __restrict__ x,
+                                                              bf16_t* __restrict__ n, float2* __restrict__ cs) {
+    __shared__ float red[4];
+    const int r = blockIdx.x;
+    int t = tok[r];
+    if (t < 0 || t >= V) t = 0;
+    const bf16_t* e = E + (size_t)t * H;
+    float* xr = x + (size_t)r * H;
+    float ss = 0.f;
+    for (int j = threadIdx.x * 4; j < H; j += 256 * 4) {
+        const uint2 w = *(const uint2*)(e + j);
+        const f32x4 v = (f32x4){bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
+        *(f32x4*)(xr + j) = v;
+        ss = fmaf(v.x, v.x, ss);
+        ss = fmaf(v.y, v.y, ss);
+        ss = fmaf(v.z, v.z, ss);
+        ss = fmaf(v.w, v.w, ss);
+    }
+    const int half = D / 2;
+    for (int i = threadIdx.x; i < half; i += 256) {
+        const double ang = (double)pos[r] * exp2(-2.0 * (double)i / (double)D * log2_base);
+        double sn, c;
+        sincos(ang, &sn, &c);
+        cs[(size_t)r * half + i] = make_float2((float)c, (float)sn);
+    }
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float rs = rsqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)H + eps);
+    for (int j = threadIdx.x * 4; j < H; j += 256 * 4) {
+        const f32x4 v = *(const f32x4*)(xr + j);
+        *(uint2*)(n + (size_t)r * H + j) = (uint2){(uint32_t)f32_to_bf16(v.x * rs) | ((uint32_t)f32_to_bf16(v.y * rs) << 16),
+                                                   (uint32_t)f32_to_bf16(v.z * rs) | ((uint32_t)f32_to_bf16(v.w * rs) << 16)};
+    }
+}
+
 // out[e] = float(in[e])
 __global__ __launch_bounds__(256) void widen_bf16_kernel(const bf16_t* __restrict__ in, size_t n, float* __restrict__ out) {
     for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x)
@@ -396,9 +441,8 @@ void launch_decoder_verify(const LayerPtrs* layers, int n_layers, const bf16_t* 
     const double log2_base = log2((double)rope_base);
     const int ew_blocks = 1024;
 
-    MEDUSA_LAUNCH("embed_rows", embed_rows_kernel, dim3(R), dim3(256), 0, s, node_tok, E, H, V, w.x);
-    MEDUSA_LAUNCH("rope_table", rope_table_kernel, dim3(R), dim3(64), 0, s, node_pos, D, log2_base, w.rope);
-    MEDUSA_LAUNCH("rmsnorm_f32", rmsnorm_f32_bf16_kernel, dim3(R), dim3(256), 0, s, w.x, H, eps, w.n);
+    MEDUSA_LAUNCH("embed_norm_rope", embed_norm_rope_kernel, dim3(R), dim3(256), 0, s, node_tok, E, H, V, eps,
+                  node_pos, D, log2_base, w.x, w.n, w.rope);
     for (int l = 0; l < n_layers; ++l) {
         // w.n holds bf16(RMSNorm(x)) of the layer input
         const LayerPtrs& L = layers[l];
