@@ -38,11 +38,11 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 # calibration (profiles/medusa_step_hbm_counters__vicuna7b_sparse64.txt).
 # Valid only for the kernel sources they were taken on (sha256 prefix of
 # heads.hip + common.hpp); reported as null after any change to them.
-VOCAB_TRAFFIC = {"sources_sha256_16": "9253b7a5430e4316", "read_bytes": 1311531009, "write_bytes": 128028}
+VOCAB_TRAFFIC = {"sources_sha256_16": "7571114b7ffd3c93", "read_bytes": 1311530849, "write_bytes": 128027}
 # the same for the packed vocabulary projection of 8 sequences (5 heads x
 # 128256 rows over 4096, the 16 bf16 head/remainder node rows per head)
 # (heads.hip + skinny_mfma.hpp + common.hpp)
-VOCAB_PACKED_TRAFFIC = {"sources_sha256_16": "c257469e44fa4189", "read_bytes": 5397341044, "write_bytes": 1286784}
+VOCAB_PACKED_TRAFFIC = {"sources_sha256_16": "7501fdf35a183e01", "read_bytes": 5397545134, "write_bytes": 1286601}
 # the same for the gate|up projection of the 32-layer workload (one layer's
 # launch: 64 x 4096 node rows against 22016 packed weight rows, unsplit, the
 # SwiGLU product written in bf16)

@@ -238,6 +238,17 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(const float* __restrict
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float* cv = cand_val + (size_t)bk * M;
     const int* ci = cand_idx + (size_t)bk * M;
+    // the tree's inputs for this thread's first node (and the first mask
+    // word), loaded before the candidates: their round trip to memory
+    // overlaps the merge instead of following it
+    const int b = bk / K, k = bk - b * K;
+    int P = 0, d0 = -1, r0 = 0;
+    uint64_t m0 = 0;
+    if (node_tok != nullptr) {
+        P = cache_len[b];
+        if (tid < N) { d0 = depth[tid]; r0 = rank[tid]; }
+        if (bk == 0 && anc_mask != nullptr && tid < N * W) m0 = mask[tid];
+    }
     float lv[TK];
     int li[TK];
 #pragma unroll
@@ -280,15 +291,13 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(const float* __restrict
     }
     if (node_tok == nullptr) return;
     // the tree nodes of head k (see above)
-    const int b = bk / K, k = bk - b * K;
     if (bk == 0 && anc_mask != nullptr)
-        for (int e = tid; e < N * W; e += 256) anc_mask[e] = mask[e];
+        for (int e = tid; e < N * W; e += 256) anc_mask[e] = e == tid ? m0 : mask[e];
     __syncthreads();
-    const int P = cache_len[b];
     for (int n = tid; n < N; n += 256) {
-        const int d = depth[n];
+        const int d = n == tid ? d0 : depth[n];
         if (d == k + 1) {
-            node_tok[(size_t)b * N + n] = top_s[rank[n]];
+            node_tok[(size_t)b * N + n] = top_s[n == tid ? r0 : rank[n]];
             node_pos[(size_t)b * N + n] = P + d;
         } else if (d == 0 && k == 0) {
             node_tok[(size_t)b * N + n] = root_tok[b];
