@@ -46,7 +46,7 @@ VOCAB_PACKED_TRAFFIC = {"sources_sha256_16": "7501fdf35a183e01", "read_bytes": 5
 # the same for the gate|up projection of the 32-layer workload (one layer's
 # launch: 64 x 4096 node rows against 22016 packed weight rows, unsplit, the
 # SwiGLU product written in bf16)
-GATE_UP_TRAFFIC = {"sources_sha256_16": "ba7c9a36223094f4", "read_bytes": 185369405, "write_bytes": 1409024}
+GATE_UP_TRAFFIC = {"sources_sha256_16": "94c592ef53006fda", "read_bytes": 185374649, "write_bytes": 1409024}
 
 
 def _traffic_bytes(rec, sources):

@@ -152,7 +152,9 @@ __device__ __forceinline__ void sum_splits2(const float* __restrict__ part, int 
 }
 
 // cs[r][i] = (cos, sin) of the angle pos[r] * base^(-2i/D), computed in double
-// once per verify call (every layer rotates at the same positions).
+// (the RoPE building-block call; the verify pass takes the same table from
+// embed_norm_rope_kernel, once per call, since every layer rotates at the
+// same positions).
 __global__ void rope_table_kernel(const int32_t* __restrict__ pos, int D, double log2_base, float2* __restrict__ cs) {
     const int r = blockIdx.x, half = D / 2;
     for (int i = threadIdx.x; i < half; i += blockDim.x) {
